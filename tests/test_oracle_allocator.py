@@ -1,0 +1,147 @@
+"""Pins for the oracle's allocator model: hand-worked examples (tables and
+slots worked out by hand from the stated rules) and invariants checked after
+every operation of long seeded random operation streams."""
+import numpy as np
+import pytest
+
+from oracle.allocator import AllocError, BlockAllocatorModel
+
+
+def test_hand_worked_four_sequences():
+    a = BlockAllocatorModel(8, 4)
+    a.set_free_order([5, 3, 6, 0, 7, 1, 2, 4])
+    for s in range(4):
+        a.create(s)
+    assert a.append_slots(0, 1) == ([80], [])
+    assert a.append_slots(1, 16) == (list(range(48, 64)), [])
+    assert a.append_slots(2, 17) == (list(range(96, 112)) + [0], [])
+    assert a.append_slots(3, 40) == (list(range(112, 128)) + list(range(16, 32)) + list(range(32, 40)), [])
+    tables, lens = a.block_tables(range(4), 4)
+    assert tables == [[5, 0, 0, 0], [3, 0, 0, 0], [6, 0, 0, 0], [7, 1, 2, 0]]
+    assert lens == [1, 16, 17, 40]
+    # one appended token each; only sequence 1 crosses into a new block
+    assert a.append_slots(0, 1) == ([81], [])
+    assert a.append_slots(1, 1) == ([64], [])          # takes block 4, the last free one
+    assert a.append_slots(2, 1) == ([1], [])
+    assert a.append_slots(3, 1) == ([40], [])
+    assert a.stats()["free_blocks"] == 0
+    # a block-crossing append with no free block fails and changes nothing
+    before = (dict(a.tables), dict(a.lens), list(a.free), list(a.ref))
+    with pytest.raises(AllocError) as e:
+        a.append_slots(0, 15)
+    assert e.value.kind == "no_free_blocks"
+    assert before == (dict(a.tables), dict(a.lens), list(a.free), list(a.ref))
+    # freeing sequence 2 releases blocks 6 then 0: block 0 is reused first
+    a.free_seq(2)
+    assert a.append_slots(0, 15) == (list(range(82, 96)) + [0], [])
+    assert a.tables[0] == [5, 0]
+
+
+def test_hand_worked_fork_and_copy_on_write():
+    a = BlockAllocatorModel(6, 8)
+    a.create(0)
+    assert a.append_slots(0, 20) == (list(range(0, 20)), [])
+    a.fork(0, 1)
+    assert a.ref[:2] == [2, 2]
+    # seq 1 writes into the shared partial block 1: copy to block 2 first
+    assert a.append_slots(1, 1) == ([36], [(1, 2)])
+    assert a.tables[1] == [0, 2] and a.ref[1] == 1
+    # seq 0 is now the only holder of block 1: written in place
+    assert a.append_slots(0, 1) == ([20], [])
+    a.fork(0, 2)
+    assert a.ref[0] == 3 and a.ref[1] == 2
+    assert a.append_slots(2, 12) == (list(range(53, 64)) + [64], [(1, 3)])
+    assert a.tables[2] == [0, 3, 4]
+    st = a.stats()
+    assert st["used_blocks"] == 5 and st["free_blocks"] == 1 and st["shared_blocks"] == 1
+    assert st["cow_copies"] == 2 and st["cached_tokens"] == 21 + 21 + 33
+    assert st["stored_tokens"] == 16 + 5 + 5 + 16 + 1
+    assert st["utilisation"] == pytest.approx(43 / 80)
+
+
+def test_full_shared_block_is_never_copied():
+    a = BlockAllocatorModel(5, 8)
+    a.create(0)
+    a.append_slots(0, 32)
+    a.fork(0, 1)
+    slots, pairs = a.append_slots(1, 1)
+    assert pairs == [] and slots == [32] and a.tables[1] == [0, 1, 2]
+    assert a.ref[:3] == [2, 2, 1]
+
+
+def test_errors():
+    a = BlockAllocatorModel(4, 2)
+    a.create(0)
+    with pytest.raises(AllocError) as e:
+        a.append_slots(0, 33)                         # needs 3 > max_blocks_per_seq
+    assert e.value.kind == "invalid_arg"
+    with pytest.raises(AllocError) as e:
+        a.append_slots(9, 1)
+    assert e.value.kind == "unknown_seq"
+    with pytest.raises(AllocError):
+        a.create(0)
+    with pytest.raises(AllocError):
+        a.set_free_order([0, 1, 2, 2])
+    a.append_slots(0, 1)
+    with pytest.raises(AllocError):
+        a.set_free_order([0, 1, 2, 3])                # pool not idle
+
+
+def _check_invariants(a: BlockAllocatorModel):
+    # reference counts equal the number of table entries naming each block
+    counts = [0] * a.num_blocks
+    for t in a.tables.values():
+        for blk in t:
+            counts[blk] += 1
+    assert counts == a.ref
+    # sum of counts = sum over sequences of ceil(L/16)
+    assert sum(a.ref) == sum(-(-L // 16) for L in a.lens.values())
+    # free + distinct used = pool, and the free list holds no duplicates
+    assert len(set(a.free)) == len(a.free)
+    used = {b for b in range(a.num_blocks) if a.ref[b] > 0}
+    assert used.isdisjoint(a.free) and len(used) + len(a.free) == a.num_blocks
+    for s, t in a.tables.items():
+        assert len(t) == -(-a.lens[s] // 16)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_random_streams_keep_invariants(seed):
+    rng = np.random.default_rng(seed)
+    a = BlockAllocatorModel(64, 16)
+    a.set_free_order(rng.permutation(64))
+    live, next_id = [], 0
+    for _ in range(1500):
+        r = rng.random()
+        if r < 0.15 or not live:
+            a.create(next_id)
+            live.append(next_id)
+            next_id += 1
+        elif r < 0.30:
+            a.free_seq(live.pop(int(rng.integers(len(live)))))
+        elif r < 0.40:
+            parent = live[int(rng.integers(len(live)))]
+            a.fork(parent, next_id)
+            live.append(next_id)
+            next_id += 1
+        else:
+            s = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(0, 40))
+            snapshot = (dict((k, list(v)) for k, v in a.tables.items()), dict(a.lens), list(a.free), list(a.ref))
+            try:
+                slots, pairs = a.append_slots(s, n)
+            except AllocError as e:
+                assert e.kind in ("no_free_blocks", "invalid_arg")
+                assert snapshot == (dict((k, list(v)) for k, v in a.tables.items()), dict(a.lens), list(a.free), list(a.ref))
+                continue
+            assert len(slots) == n and len(pairs) <= 1
+            # every written slot belongs to a block this sequence alone holds
+            for sl in slots:
+                assert a.ref[sl // 16] == 1
+            # slots are the sequence's positions L-n..L-1 through its table
+            L = a.lens[s]
+            for i, sl in enumerate(slots):
+                p = L - n + i
+                assert sl == 16 * a.tables[s][p // 16] + p % 16
+            for old, new in pairs:
+                assert a.ref[old] >= 1 and a.ref[new] == 1
+        _check_invariants(a)
