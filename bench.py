@@ -1,0 +1,336 @@
+#!/usr/bin/env python3
+"""Paged decode attention throughput on one MI355X.
+
+One step = one decode step of a model's attention over every rotated layer:
+  host   the native allocator reserves one new slot per sequence (taking a
+         block when a sequence's last block is full) and rebuilds the block
+         tables; slots and tables go to the GPU (pinned host buffers, async);
+  GPU    per layer: copy-on-write copies (if any), the cache-write kernel
+         appends the new token's K/V, then paged_attention_decode (main
+         kernel + partition merge) attends over the whole cache.
+Every layer has its own pool, so the K/V read each step is far larger than
+the 256 MB Infinity Cache (reads come from HBM).
+
+value    = KV tokens attended per second = sum over timed steps and layers of
+           sum_b L_b, divided by the timed wall time.
+roofline = the decode call's algorithmic bytes (K/V [+ fp8 scales] of every
+           attended token, q, out, block-table entries, lengths) divided by
+           its average duration from HIP events on the launch stream.
+cpu_baseline = the fp64 oracle (test infrastructure) timed on the host over a
+           bounded sample of the same workload.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention KV tokens/s and achieved HBM GB/s (% of peak), 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 * 2 ** 20
+ES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: Llama-3-8B shape, bf16)")
+    ap.add_argument("--layers", type=int, default=0, help="pools to rotate (0 = 32, or enough for 4x the MALL)")
+    ap.add_argument("--partition-size", type=int, default=0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for name in ("decode.hip", "device_common.h", "launch.h"):
+        with open(os.path.join(ROOT, "paged_kv_cache_160_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_name: str):
+    """HBM bytes per decode launch from a committed rocprofv3 counter summary,
+    if it was taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload_name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(sharding by sequence or KV head needs no exchange; see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    import paged_kv_cache_160_amd as pkv
+    from paged_kv_cache_160_amd.cache import PagedKVCache
+    from paged_kv_cache_160_amd.workload_runner import TORCH_DTYPES, to_device
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = wl.make_workload(args.config)
+    B, hq, hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
+    ces = ES[w.cache_dtype]
+    per_layer_bytes = 2 * w.num_blocks * hkv * 16 * D * ces
+    layers = args.layers or (32 if args.config == 2 else max(1, math.ceil(4 * MALL_BYTES / per_layer_bytes)))
+    log(f"[bench] workload {args.config} {w.name}: B={B} Hq={hq} Hkv={hkv} D={D} cache={w.cache_dtype} "
+        f"layers={layers} pool={w.num_blocks} blocks/layer ({per_layer_bytes / 2**30:.2f} GiB/layer)")
+
+    cache = PagedKVCache(layers, w.num_blocks, hkv, D, TORCH_DTYPES[w.cache_dtype], w.max_blocks_per_seq,
+                         device=dev)
+    gen = torch.Generator(device=dev)
+    src_t = TORCH_DTYPES[w.src_dtype]
+
+    def gpu_rows(n, seed):
+        gen.manual_seed(seed)
+        return torch.randn((n, hkv, D), generator=gen, device=dev, dtype=torch.float32).to(src_t)
+
+    # ---- setup: the workload's allocator script; layer 0 holds the seeded
+    # workload rows, the other layers seeded device-generated rows of the same
+    # distribution
+    t0 = time.perf_counter()
+    for op in wl.setup_ops(w):
+        kind = op[0]
+        if kind == "free_order":
+            cache.set_free_order(op[1])
+        elif kind == "create":
+            cache.create(op[1])
+        elif kind == "fork":
+            cache.fork(op[1], op[2])
+        elif kind == "free":
+            cache.free(op[1])
+        elif kind == "append":
+            seq, n = op[1], op[2]
+            if seq >= wl.CHURN_ID_BASE:
+                cache.alloc.append_slots(seq, n)
+                continue
+            start = cache.seq_len(seq)
+            k0 = to_device(wl.kv_rows(w, seq, "k")[start:start + n], w.src_dtype, dev)
+            v0 = to_device(wl.kv_rows(w, seq, "v")[start:start + n], w.src_dtype, dev)
+            ks = [k0] + [gpu_rows(n, 7919 * (l + 1) + 2 * seq) for l in range(1, layers)]
+            vs = [v0] + [gpu_rows(n, 7919 * (l + 1) + 2 * seq + 1) for l in range(1, layers)]
+            cache.append(seq, ks, vs)
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.perf_counter() - t0:.1f}s; stats {cache.alloc.stats()}")
+
+    seqs = list(range(B))
+    n_steps = args.warmup + args.steps
+    qt = TORCH_DTYPES[w.q_dtype]
+    gen.manual_seed(12345)
+    qs = torch.randn((n_steps, layers, B, hq, D), generator=gen, device=dev).to(qt)
+    knew = torch.randn((n_steps, layers, B, hkv, D), generator=gen, device=dev).to(src_t)
+    vnew = torch.randn((n_steps, layers, B, hkv, D), generator=gen, device=dev).to(src_t)
+    outs = torch.empty((layers, B, hq, D), dtype=qt, device=dev)
+
+    mb = w.max_blocks_per_seq
+    # one set of pinned host buffers per step: an async copy may still be
+    # queued behind the previous step's kernels when the host moves on
+    h_tables = [torch.zeros((B, mb), dtype=torch.int32).pin_memory() for _ in range(n_steps)]
+    h_lens = [torch.zeros(B, dtype=torch.int32).pin_memory() for _ in range(n_steps)]
+    h_slots = [torch.zeros(B, dtype=torch.int64).pin_memory() for _ in range(n_steps)]
+    d_tables = torch.zeros((B, mb), dtype=torch.int32, device=dev)
+    d_lens = torch.zeros(B, dtype=torch.int32, device=dev)
+    d_slots = torch.zeros(B, dtype=torch.int64, device=dev)
+    max_possible = max(w.context_lens) + n_steps
+    ws = torch.empty(max(1, pkv.workspace_size(B, hq, hkv, D, max_possible, args.partition_size,
+                                               pkv.dtype_code(cache.cache_dtype))), dtype=torch.uint8, device=dev)
+    ps_used, np_used = pkv.decode_partition_size(B, hq, hkv, D, max(w.context_lens) + 1,
+                                                 pkv.dtype_code(cache.cache_dtype))
+    if args.partition_size:
+        ps_used = args.partition_size
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps * layers)]
+    tokens_timed = 0
+    bytes_timed = 0
+
+    # Raw C-ABI calls with precomputed arguments: the timed loop enqueues
+    # 2 * layers launches per step and Python must stay ahead of the GPU.
+    lib = pkv._lib.lib()
+    sp = stream.cuda_stream
+    src_code = pkv.dtype_code(src_t)
+    cache_code = pkv.dtype_code(cache.cache_dtype)
+    q_code = pkv.dtype_code(qt)
+    scale = 1.0 / math.sqrt(D)
+    kv_stride = knew[0, 0].numel() * knew.element_size()
+    q_stride = qs[0, 0].numel() * qs.element_size()
+    out_stride = outs[0].numel() * outs.element_size()
+    ptr = lambda t: None if t is None else t.data_ptr()
+    pools = [(ptr(cache.k[l]), ptr(cache.v[l]), ptr(cache.k_scale[l]), ptr(cache.v_scale[l]))
+             for l in range(layers)]
+    ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
+
+    def step(s, timed):
+        nonlocal tokens_timed, bytes_timed
+        slots, pairs = cache.alloc.batch_append_one(seqs)
+        h_slots[s].copy_(torch.tensor(slots, dtype=torch.int64))
+        cache.alloc.block_tables(seqs, mb, out_tables=h_tables[s], out_lens=h_lens[s])
+        d_slots.copy_(h_slots[s], non_blocking=True)
+        d_tables.copy_(h_tables[s], non_blocking=True)
+        d_lens.copy_(h_lens[s], non_blocking=True)
+        if pairs:
+            cache._apply_cow(pairs)
+        lens = h_lens[s].tolist()
+        max_len = max(lens)
+        sum_l = sum(lens)
+        kbase = knew.data_ptr() + s * layers * kv_stride
+        vbase = vnew.data_ptr() + s * layers * kv_stride
+        qbase = qs.data_ptr() + s * layers * q_stride
+        for l in range(layers):
+            kp, vp, ksp, vsp = pools[l]
+            rc = lib.kv_cache_append(kbase + l * kv_stride, vbase + l * kv_stride, kp, vp, ksp, vsp,
+                                     d_slots.data_ptr(), B, hkv, D, w.num_blocks, src_code, cache_code, sp)
+            if rc:
+                raise pkv.PagedKVError(rc, "kv_cache_append")
+            if timed:
+                ev[(s - args.warmup) * layers + l][0].record(stream)
+            rc = lib.paged_attention_decode(outs.data_ptr() + l * out_stride, qbase + l * q_stride, kp, vp,
+                                            ksp, vsp, d_tables.data_ptr(), d_lens.data_ptr(), B, hq, hkv, D,
+                                            w.num_blocks, mb, max_len, scale, q_code, cache_code,
+                                            args.partition_size, ws_ptr, ws_bytes, sp)
+            if rc:
+                raise pkv.PagedKVError(rc, "paged_attention_decode")
+            if timed:
+                ev[(s - args.warmup) * layers + l][1].record(stream)
+        if timed:
+            tokens_timed += sum_l * layers
+            kv_bytes = sum_l * hkv * D * 2 * ces
+            if w.cache_dtype == "fp8_e4m3":
+                kv_bytes += sum_l * hkv * 2 * 4
+            qo_bytes = 2 * B * hq * D * ES[w.q_dtype]
+            table_bytes = sum(-(-L // 16) for L in lens) * 4 + B * 4
+            bytes_timed += (kv_bytes + qo_bytes + table_bytes) * layers
+
+    for s in range(args.warmup):
+        step(s, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, n_steps):
+        step(s, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    dec_ms = [a.elapsed_time(b) for a, b in ev]
+    avg_dec_s = sum(dec_ms) / len(dec_ms) / 1e3
+    calls = args.steps * layers
+    bytes_per_call = bytes_timed / calls
+    achieved = bytes_per_call / avg_dec_s / 1e9
+    value = tokens_timed / elapsed
+    log(f"[bench] {args.steps} steps in {elapsed * 1e3:.2f} ms; decode call avg {avg_dec_s * 1e6:.2f} us; "
+        f"{achieved:.0f} GB/s algorithmic; {value / 1e9:.3f} G KV tokens/s")
+    traffic = load_traffic(w.name)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds)
+
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.cache_dtype,
+        "data": "synthetic (seeded N(0,1) K/V/q; no weights or datasets)",
+        "config": {
+            "workload": f"{w.name} (paged decode, one layer per call)",
+            "batch": B, "context_len_first_timed_step": max(w.context_lens) + args.warmup + 1,
+            "q_heads": hq, "kv_heads": hkv, "head_dim": D, "block_size": 16, "kv_dtype": w.cache_dtype,
+            "q_dtype": w.q_dtype, "layers_rotated": layers, "pool_blocks_per_layer": w.num_blocks,
+            "partition_size": ps_used, "parallelism": "none (1 GPU)",
+        },
+        "achieved_hbm_gbps": achieved,
+        "pct_of_peak": 100.0 * achieved / HBM_PEAK_GBPS,
+        "decode_call_us": avg_dec_s * 1e6,
+        "roofline": {
+            "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+            "kernel": "paged_attention_decode (main kernel + partition merge)",
+            "bytes_per_launch": bytes_per_call,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(w, budget_s: float):
+    """The fp64 oracle on the host: whole sequences of layer 0, rows generated
+    beforehand (not timed), attention timed until the budget is spent."""
+    import numpy as np
+    import psutil
+    from threadpoolctl import threadpool_info
+
+    import workloads as wl
+    from oracle import attention
+
+    scale = 1.0 / math.sqrt(w.head_dim)
+    q = wl.queries(w, 0)
+    n_pre = min(w.num_seqs, 4)
+    pre = []
+    for b in range(n_pre):
+        L = w.context_lens[b]
+        K, V = attention.rows_as_cached(wl.kv_rows(w, b, "k", L), wl.kv_rows(w, b, "v", L), w.cache_dtype)
+        pre.append((b, K, V))
+    proc = psutil.Process()
+    c0 = proc.cpu_times()
+    t0 = time.perf_counter()
+    tokens = 0
+    seqs_done = 0
+    while True:
+        b, K, V = pre[seqs_done % n_pre]
+        attention.attend(q[b], K, V, scale)
+        tokens += K.shape[0]
+        seqs_done += 1
+        if time.perf_counter() - t0 >= budget_s and seqs_done >= n_pre:
+            break
+    wall = time.perf_counter() - t0
+    c1 = proc.cpu_times()
+    busy = (c1.user - c0.user + c1.system - c0.system) / wall
+    blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
+    allowed = len(os.sched_getaffinity(0))
+    log(f"[cpu] oracle: {seqs_done} sequence decodes, {tokens} KV tokens in {wall:.1f}s "
+        f"({tokens / wall / 1e6:.2f} M KV tokens/s), {busy:.1f} cores busy on average")
+    return {
+        "value": tokens / wall, "unit": "KV tokens/s", "cores": max(1, round(busy)),
+        "kind": "oracle",
+        "sample": (f"{seqs_done} single-sequence decodes (all {w.num_q_heads} query heads, "
+                   f"L={w.context_lens[0]}) cycling over the first {n_pre} sequences of layer 0 of "
+                   f"{w.name}; fp64 numpy; rows generated and dequantised before timing; "
+                   f"{busy:.2f} cores busy on average, {allowed} allowed, BLAS threads {blas}"),
+    }
+
+
+if __name__ == "__main__":
+    main()

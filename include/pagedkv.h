@@ -1,0 +1,265 @@
+/*
+ * pagedkv.h - C ABI of libpagedkv.so: single-token decode attention over a
+ * paged KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages: "KV Cache 和 vLLM" §1.2-1.3, §3.1-3.3; "KV Cache优化实战"
+ * §2.1, §3.2-3.3, §4.2; "企业官网建设流程全解析" §1.2-1.3, §2.2, §3.2):
+ *   - each layer keeps its K and V in a pool of fixed 16-token physical blocks;
+ *   - each sequence has a block table mapping logical block i (tokens
+ *     16i..16i+15) to a physical block, so a sequence is logically contiguous
+ *     and physically scattered;
+ *   - a decode step appends the new token's K and V to the cache, then the new
+ *     query attends over every cached token, itself included:
+ *       out[h] = softmax(q[h] . K^T * scale) V,  scale = 1/sqrt(head_dim),
+ *     with query head h reading KV head h / (Hq/Hkv) (grouped-query attention);
+ *   - KV may be stored as fp8 e4m3 with one scale per token and per head.
+ *
+ * Conventions for every call:
+ *   - Return value: PKV_OK (0) or a negative PKV_ERR_* code; pkv_strerror()
+ *     names it.  No C++ exception crosses this interface.
+ *   - Device pointers are owned by the caller (for example PyTorch tensors).
+ *     The library never allocates, frees or keeps device memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every device call only enqueues work on it and returns; none
+ *     synchronises.  Argument checks are done on the host before anything is
+ *     enqueued; a failed check enqueues nothing.  A launch failure reported by
+ *     the HIP runtime is returned as PKV_ERR_HIP.
+ *   - Kernels never read or write outside the buffers described below, for
+ *     any contents of slot_mapping, block_tables, context_lens or pairs:
+ *     out-of-range entries are skipped.  Outputs are defined only when those
+ *     contents meet the stated preconditions.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKV_BLOCK_SIZE 16   /* tokens per physical block ("KV Cache 和 vLLM" §3.1) */
+#define PKV_ABI_VERSION 1
+
+typedef enum {
+  PKV_F32 = 0,
+  PKV_F16 = 1,
+  PKV_BF16 = 2,
+  PKV_FP8_E4M3 = 3   /* OCP E4M3FN: bias 7, max 448, no infinities */
+} pkv_dtype;
+
+enum {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = -1,    /* null pointer, bad size, Hq % Hkv != 0, ... */
+  PKV_ERR_UNSUPPORTED = -2,    /* dtype pair, head_dim or group size not built */
+  PKV_ERR_WORKSPACE = -3,      /* workspace missing or smaller than required */
+  PKV_ERR_HIP = -4,            /* the HIP runtime reported an error */
+  PKV_ERR_NO_FREE_BLOCKS = -5, /* allocator: not enough free blocks; nothing changed */
+  PKV_ERR_UNKNOWN_SEQ = -6     /* allocator: no such sequence id */
+};
+
+/* Library ABI version (PKV_ABI_VERSION). */
+int pkv_abi_version(void);
+
+/* Static text for a return code. */
+const char* pkv_strerror(int code);
+
+/* ------------------------------------------------------------------------ */
+/* Device layouts (row-major, contiguous):                                   */
+/*   k_pool, v_pool   [num_blocks][num_kv_heads][16][head_dim] of cache dtype */
+/*   k_scale, v_scale [num_blocks][num_kv_heads][16] float32 (fp8 only)       */
+/*   slot = physical_block * 16 + (position % 16)                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * kv_cache_append - write new K/V token rows into their slots.
+ * Pages: "KV Cache 和 vLLM" §1.3 (each step computes the new token's K and V
+ * and appends them to the layer's cache) and §3.1 (16-token blocks);
+ * "KV Cache优化实战" §3.2-3.3 (fp8 KV with per-token / per-head scales).
+ *
+ *   k_new, v_new  device, [num_tokens][num_kv_heads][head_dim] of src_dtype
+ *   k_pool, v_pool device pools (layout above) of cache_dtype
+ *   k_scale, v_scale device [num_blocks][num_kv_heads][16] float32; required
+ *                 when cache_dtype is PKV_FP8_E4M3, ignored (may be NULL)
+ *                 otherwise
+ *   slot_mapping  device int64 [num_tokens]: row i goes to slot_mapping[i];
+ *                 a negative entry skips the row; entries >= 16*num_blocks
+ *                 are skipped as well
+ * Same dtype (f32/f16/bf16): an exact bit copy of each row.
+ * fp8 (src f32, f16 or bf16): per (token, head) row, a = max|x| (fp32),
+ *   s = a / 448 (fp32, correctly rounded; s = 1 when a == 0), code =
+ *   e4m3 round-to-nearest-even of clamp(x / s, -448, 448) with x / s a
+ *   correctly rounded fp32 division; codes go to the pool and s to the scale
+ *   array at the same (block, head, offset).
+ * Slots must be distinct within one call.  num_tokens == 0 is a no-op.
+ * head_dim: 64 or 128.
+ */
+int kv_cache_append(const void* k_new, const void* v_new,
+                    void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                    const int64_t* slot_mapping,
+                    int num_tokens, int num_kv_heads, int head_dim, int num_blocks,
+                    pkv_dtype src_dtype, pkv_dtype cache_dtype, void* stream);
+
+/*
+ * pkv_copy_blocks - copy whole physical blocks (K, V and, for fp8, the
+ * scales) from src to dst, for the copy-on-write of a shared block that one
+ * sequence is about to write ("KV Cache 和 vLLM" §3.3).
+ *   pairs  device int32 [n_pairs][2] = {src, dst}; pairs with an entry
+ *          outside [0, num_blocks) are skipped.  dst blocks must be distinct
+ *          and no dst may be a src of the same call.
+ */
+int pkv_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                    const int32_t* pairs, int n_pairs,
+                    int num_kv_heads, int head_dim, int num_blocks, pkv_dtype cache_dtype,
+                    void* stream);
+
+/*
+ * pkv_decode_partition_size - the partition length (tokens, a multiple of 16)
+ * paged_attention_decode uses when called with partition_size == 0, and the
+ * resulting partitions per sequence for max_context_len.  Host only.
+ */
+int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                              int max_context_len, pkv_dtype cache_dtype,
+                              int* partition_size_out, int* num_partitions_out);
+
+/*
+ * paged_attention_workspace_size - bytes of device workspace
+ * paged_attention_decode needs for these sizes (0 when every sequence fits
+ * in one partition).  partition_size: 0 = automatic, else a multiple of 16.
+ * Returns 0 as well for invalid sizes (the decode call then reports them).
+ */
+size_t paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                      int head_dim, int max_context_len, int partition_size,
+                                      pkv_dtype cache_dtype);
+
+/*
+ * paged_attention_decode - one decode step of attention for a batch.
+ * Pages: "企业官网建设流程全解析" §1.2 (softmax(Q K^T / sqrt(d_k)) V), §2.2
+ * (several query heads share one KV head), §3.2 (the query attends to the
+ * whole cache, its own token included); "KV Cache 和 vLLM" §3.2 (block-table
+ * translation: only the sequence's own blocks are read).
+ *
+ *   out           device [num_seqs][num_q_heads][head_dim] of q_dtype (written)
+ *   q             device [num_seqs][num_q_heads][head_dim] of q_dtype
+ *   k_pool, v_pool, k_scale, v_scale  as for kv_cache_append (scales: fp8 only)
+ *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entry i of row
+ *                 b is the physical block of sequence b's logical block i
+ *   context_lens  device int32 [num_seqs]; L_b, the tokens sequence b attends
+ *                 to (positions 0..L_b-1)
+ *   max_context_len  host bound with L_b <= max_context_len <=
+ *                 16 * max_blocks_per_seq; it sizes the launch
+ *   scale         the caller passes 1/sqrt(head_dim)
+ *   partition_size 0 = automatic; else tokens per partition, a multiple of 16.
+ *                 Sequences longer than one partition are split; partitions
+ *                 are merged exactly by a log-sum-exp reduction.
+ *   workspace     device scratch of at least paged_attention_workspace_size()
+ *                 bytes (may be NULL when that is 0); contents on entry are
+ *                 ignored
+ * Query head h reads KV head h / (num_q_heads / num_kv_heads).  L_b == 0 gives
+ * an all-zero output row.  Entries of the used part of a block-table row must
+ * lie in [0, num_blocks); a block outside that range contributes no tokens.
+ * Tokens at or beyond max_context_len (or 16*max_blocks_per_seq) are ignored.
+ * dtype pairs (q / cache): f32/f32, f16/f16, bf16/bf16, bf16/fp8_e4m3,
+ * f16/fp8_e4m3.  head_dim: 64 or 128.  num_q_heads/num_kv_heads: 1..16.
+ * Accumulation is fp32; the output is rounded to q_dtype (round to nearest
+ * even).  The result for a given (sequence, head) depends only on the values
+ * at its logical positions, not on where the blocks lie or who shares them.
+ */
+int paged_attention_decode(void* out, const void* q,
+                           const void* k_pool, const void* v_pool,
+                           const float* k_scale, const float* v_scale,
+                           const int32_t* block_tables, const int32_t* context_lens,
+                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                           int num_blocks, int max_blocks_per_seq, int max_context_len,
+                           float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                           int partition_size, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host block allocator.  Opaque handle, not thread-safe, no device memory.  */
+/*                                                                          */
+/* Pages: blocks are taken on demand when a sequence's current block is full */
+/* and appended to its block table ("KV Cache 和 vLLM" §3.1); finished        */
+/* sequences return their blocks for reuse ("KV Cache优化实战" §4.2);          */
+/* sequences with a common prefix point at the same physical blocks, and      */
+/* copy-on-write handles writes to shared blocks ("KV Cache 和 vLLM" §3.3);   */
+/* running out of cache must degrade rather than crash ("企业官网建设流程全解析" */
+/* §6.4): every failing call leaves the allocator unchanged.                  */
+/*                                                                          */
+/* Rules: blocks carry reference counts.  The free list is a stack:          */
+/* pkv_alloc_set_free_order(order) makes order[0] the next block handed out,  */
+/* and a released block goes on top.  A sequence's blocks are released in     */
+/* logical order.  Appending n tokens to a sequence of length L: if L % 16 != */
+/* 0 and its last block is shared, that block is copied first (one fresh      */
+/* block, one {old, new} pair reported, old count decremented, table entry    */
+/* repointed); then a fresh block is taken for each position p in [L, L+n)    */
+/* with p % 16 == 0.  A full shared block is never written, never copied.     */
+/* ------------------------------------------------------------------------ */
+
+typedef struct pkv_alloc pkv_alloc;
+
+typedef struct {
+  int64_t num_blocks;
+  int64_t free_blocks;
+  int64_t used_blocks;     /* blocks with reference count > 0 */
+  int64_t shared_blocks;   /* blocks with reference count > 1 */
+  int64_t cow_copies;      /* copy pairs reported so far */
+  int64_t cached_tokens;   /* sum over live sequences of their length */
+  int64_t stored_tokens;   /* filled physical slots, a shared slot counted once */
+  double utilisation;      /* stored_tokens / (16 * used_blocks), 0 if none used */
+} pkv_alloc_stats_t;
+
+/* New allocator with every block free (block 0 handed out first).
+   Returns NULL if num_blocks <= 0 or max_blocks_per_seq <= 0. */
+pkv_alloc* pkv_alloc_create(int num_blocks, int max_blocks_per_seq);
+void pkv_alloc_destroy(pkv_alloc* a);
+
+/* Reorder the free list of an idle allocator (no live sequence): order is a
+   host permutation of 0..num_blocks-1 and order[0] is handed out first. */
+int pkv_alloc_set_free_order(pkv_alloc* a, const int32_t* order, int n);
+
+int pkv_seq_create(pkv_alloc* a, int64_t seq_id);
+/* child shares every block of parent (counts incremented) and its length. */
+int pkv_seq_fork(pkv_alloc* a, int64_t parent, int64_t child);
+/* Drop a sequence: counts decremented, blocks at zero return to the list. */
+int pkv_seq_free(pkv_alloc* a, int64_t seq_id);
+/* Length of a sequence (>= 0) or a negative error code. */
+int pkv_seq_len(pkv_alloc* a, int64_t seq_id);
+
+/*
+ * pkv_seq_append_slots - reserve the next n_tokens positions of a sequence.
+ *   slots_out      host int64 [n_tokens]: the slot of each new position
+ *   cow_pairs_out  host int32 [2]: the {src, dst} copy to apply before
+ *                  writing, when *n_cow_out == 1
+ *   n_cow_out      host: 0 or 1
+ * Fails with PKV_ERR_NO_FREE_BLOCKS when the free list is too short and with
+ * PKV_ERR_INVALID_ARG when the table would exceed max_blocks_per_seq; then
+ * nothing changes.
+ */
+int pkv_seq_append_slots(pkv_alloc* a, int64_t seq_id, int n_tokens,
+                         int64_t* slots_out, int32_t* cow_pairs_out, int* n_cow_out);
+
+/*
+ * pkv_batch_append_one - one new position for each of n sequences (a decode
+ * step), in the given order, all or nothing.
+ *   slots_out      host int64 [n]
+ *   cow_pairs_out  host int32 [n][2]; the first *n_cow_out rows are filled
+ */
+int pkv_batch_append_one(pkv_alloc* a, const int64_t* seq_ids, int n,
+                         int64_t* slots_out, int32_t* cow_pairs_out, int* n_cow_out);
+
+/*
+ * pkv_build_block_tables - host int32 tables [n][max_blocks_per_seq] (unused
+ * entries 0) and lengths [n] for the given sequences.
+ */
+int pkv_build_block_tables(pkv_alloc* a, const int64_t* seq_ids, int n, int max_blocks_per_seq,
+                           int32_t* tables_out, int32_t* lens_out);
+
+int pkv_alloc_stats(pkv_alloc* a, pkv_alloc_stats_t* out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

@@ -1,0 +1,233 @@
+"""Paged KV cache decode attention for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over libpagedkv.so (include/pagedkv.h): argument
+marshalling only.  Every step of the path - block allocation, cache writes,
+copy-on-write, decode attention and the partition merge - runs in the native
+library (C++ on the host, HIP kernels on the GPU).  PyTorch tensors supply the
+device memory and the current stream.  There is no CPU fallback: if the
+library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Iterable, List, Optional, Sequence, Tuple
+
+import torch
+
+from . import _lib
+
+__all__ = [
+    "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3", "BLOCK_SIZE", "PagedKVError",
+    "kv_cache_append", "copy_blocks", "paged_attention_decode", "workspace_size",
+    "decode_partition_size", "BlockAllocator", "dtype_code", "abi_version",
+]
+
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
+BLOCK_SIZE = 16
+
+_TORCH_TO_CODE = {
+    torch.float32: PKV_F32,
+    torch.float16: PKV_F16,
+    torch.bfloat16: PKV_BF16,
+    torch.float8_e4m3fn: PKV_FP8_E4M3,
+    torch.uint8: PKV_FP8_E4M3,      # raw e4m3 codes
+}
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        msg = _lib.lib().pkv_strerror(code).decode()
+        super().__init__(f"{where}: {msg} ({code})")
+        self.code = code
+
+
+def _check(code: int, where: str) -> None:
+    if code != 0:
+        raise PagedKVError(code, where)
+
+
+def dtype_code(t: torch.dtype) -> int:
+    try:
+        return _TORCH_TO_CODE[t]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t}") from None
+
+
+def abi_version() -> int:
+    return _lib.lib().pkv_abi_version()
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libpagedkv must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _pool_geometry(k_pool: torch.Tensor) -> Tuple[int, int, int]:
+    if k_pool.dim() != 4 or k_pool.shape[2] != BLOCK_SIZE:
+        raise ValueError("pools are [num_blocks, num_kv_heads, 16, head_dim]")
+    return int(k_pool.shape[0]), int(k_pool.shape[1]), int(k_pool.shape[3])
+
+
+def kv_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor,
+                    v_pool: torch.Tensor, slot_mapping: torch.Tensor,
+                    k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                    stream=None) -> None:
+    """Write rows ``k_new, v_new [T, Hkv, D]`` to ``slot_mapping [T]`` (int64) of the pools."""
+    nb, hkv, d = _pool_geometry(k_pool)
+    if k_new.shape[1:] != (hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [T, Hkv, D] matching the pool")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != k_new.shape[0]:
+        raise ValueError("slot_mapping must be int64 [T]")
+    _check(_lib.lib().kv_cache_append(
+        _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+        _ptr(slot_mapping), int(k_new.shape[0]), hkv, d, nb, dtype_code(k_new.dtype),
+        dtype_code(k_pool.dtype), _stream(stream)), "kv_cache_append")
+
+
+def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torch.Tensor,
+                k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                stream=None) -> None:
+    """Copy whole blocks ``pairs [n, 2] = (src, dst)`` (int32, device)."""
+    nb, hkv, d = _pool_geometry(k_pool)
+    if pairs.dtype != torch.int32 or (pairs.numel() and pairs.shape[-1] != 2):
+        raise ValueError("pairs must be int32 [n, 2]")
+    _check(_lib.lib().pkv_copy_blocks(
+        _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(pairs),
+        int(pairs.numel() // 2), hkv, d, nb, dtype_code(k_pool.dtype), _stream(stream)),
+        "pkv_copy_blocks")
+
+
+def decode_partition_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          max_context_len: int, cache_dtype: int) -> Tuple[int, int]:
+    ps, npart = ctypes.c_int(), ctypes.c_int()
+    _check(_lib.lib().pkv_decode_partition_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                max_context_len, cache_dtype, ctypes.byref(ps),
+                                                ctypes.byref(npart)), "pkv_decode_partition_size")
+    return ps.value, npart.value
+
+
+def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                   max_context_len: int, partition_size: int = 0, cache_dtype: int = PKV_BF16) -> int:
+    return int(_lib.lib().paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                         max_context_len, partition_size, cache_dtype))
+
+
+def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
+                           v_pool: torch.Tensor, block_tables: torch.Tensor,
+                           context_lens: torch.Tensor, max_context_len: int,
+                           scale: Optional[float] = None, k_scale: Optional[torch.Tensor] = None,
+                           v_scale: Optional[torch.Tensor] = None, partition_size: int = 0,
+                           workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step: ``out[b, h] = softmax(q[b, h] . K_b^T * scale) V_b`` over
+    each sequence's first ``context_lens[b]`` cached tokens."""
+    nb, hkv, d = _pool_geometry(k_pool)
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must be [B, Hq, D] of one dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    B, hq = int(q.shape[0]), int(q.shape[1])
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables must be [B, max_blocks], context_lens [B]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    cdt = dtype_code(k_pool.dtype)
+    need = workspace_size(B, hq, hkv, d, max_context_len, partition_size, cdt)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.lib().paged_attention_decode(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
+        _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb, int(block_tables.shape[1]),
+        int(max_context_len), float(scale), dtype_code(q.dtype), cdt, int(partition_size),
+        _ptr(workspace), ws_bytes, _stream(stream)), "paged_attention_decode")
+    return out
+
+
+class BlockAllocator:
+    """Host block allocator (refcounts, fork, copy-on-write planning)."""
+
+    def __init__(self, num_blocks: int, max_blocks_per_seq: int):
+        self._lib = _lib.lib()
+        self._h = self._lib.pkv_alloc_create(num_blocks, max_blocks_per_seq)
+        if not self._h:
+            raise PagedKVError(-1, "pkv_alloc_create")
+        self.num_blocks = num_blocks
+        self.max_blocks_per_seq = max_blocks_per_seq
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h:
+            self._lib.pkv_alloc_destroy(h)
+            self._h = None
+
+    def set_free_order(self, order: Sequence[int]) -> None:
+        arr = (ctypes.c_int32 * len(order))(*[int(x) for x in order])
+        _check(self._lib.pkv_alloc_set_free_order(self._h, arr, len(order)), "set_free_order")
+
+    def create(self, seq_id: int) -> None:
+        _check(self._lib.pkv_seq_create(self._h, seq_id), "pkv_seq_create")
+
+    def fork(self, parent: int, child: int) -> None:
+        _check(self._lib.pkv_seq_fork(self._h, parent, child), "pkv_seq_fork")
+
+    def free(self, seq_id: int) -> None:
+        _check(self._lib.pkv_seq_free(self._h, seq_id), "pkv_seq_free")
+
+    def seq_len(self, seq_id: int) -> int:
+        r = self._lib.pkv_seq_len(self._h, seq_id)
+        if r < 0:
+            raise PagedKVError(r, "pkv_seq_len")
+        return r
+
+    def append_slots(self, seq_id: int, n: int) -> Tuple[List[int], List[Tuple[int, int]]]:
+        slots = (ctypes.c_int64 * max(n, 1))()
+        pair = (ctypes.c_int32 * 2)()
+        ncow = ctypes.c_int()
+        _check(self._lib.pkv_seq_append_slots(self._h, seq_id, n, slots, pair, ctypes.byref(ncow)),
+               "pkv_seq_append_slots")
+        return list(slots[:n]), ([(pair[0], pair[1])] if ncow.value else [])
+
+    def batch_append_one(self, seq_ids: Sequence[int]) -> Tuple[List[int], List[Tuple[int, int]]]:
+        n = len(seq_ids)
+        ids = (ctypes.c_int64 * max(n, 1))(*seq_ids)
+        slots = (ctypes.c_int64 * max(n, 1))()
+        pairs = (ctypes.c_int32 * (2 * max(n, 1)))()
+        ncow = ctypes.c_int()
+        _check(self._lib.pkv_batch_append_one(self._h, ids, n, slots, pairs, ctypes.byref(ncow)),
+               "pkv_batch_append_one")
+        return list(slots[:n]), [(pairs[2 * i], pairs[2 * i + 1]) for i in range(ncow.value)]
+
+    def block_tables(self, seq_ids: Sequence[int], max_blocks: Optional[int] = None,
+                     out_tables: Optional[torch.Tensor] = None, out_lens: Optional[torch.Tensor] = None):
+        """(tables int32 [n, max_blocks], lens int32 [n]) as CPU tensors, written
+        into ``out_tables`` / ``out_lens`` (for example pinned buffers) when given."""
+        n = len(seq_ids)
+        mb = self.max_blocks_per_seq if max_blocks is None else max_blocks
+        ids = (ctypes.c_int64 * max(n, 1))(*seq_ids)
+        tables = torch.zeros((n, mb), dtype=torch.int32) if out_tables is None else out_tables
+        lens = torch.zeros(n, dtype=torch.int32) if out_lens is None else out_lens
+        if (tables.device.type != "cpu" or lens.device.type != "cpu" or tables.dtype != torch.int32
+                or lens.dtype != torch.int32 or tables.shape != (n, mb) or lens.shape != (n,)
+                or not tables.is_contiguous()):
+            raise ValueError("block table buffers must be contiguous int32 CPU [n, max_blocks] and [n]")
+        _check(self._lib.pkv_build_block_tables(
+            self._h, ids, n, mb, ctypes.cast(tables.data_ptr(), _lib.P_i32),
+            ctypes.cast(lens.data_ptr(), _lib.P_i32)), "pkv_build_block_tables")
+        return tables, lens
+
+    def stats(self) -> dict:
+        st = _lib.AllocStats()
+        _check(self._lib.pkv_alloc_stats(self._h, ctypes.byref(st)), "pkv_alloc_stats")
+        return {name: getattr(st, name) for name, _ in _lib.AllocStats._fields_}

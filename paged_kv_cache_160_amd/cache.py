@@ -1,0 +1,125 @@
+"""Per-layer paged K/V pools driven by the native block allocator.
+
+Marshalling only: the allocator decides slots and copy-on-write pairs (C++),
+the HIP kernels copy blocks, write rows and run decode attention.  PyTorch
+owns the device memory.
+"""
+from __future__ import annotations
+
+from typing import List, Optional, Sequence, Union
+
+import torch
+
+from . import (BLOCK_SIZE, BlockAllocator, copy_blocks, kv_cache_append, paged_attention_decode,
+               workspace_size, dtype_code)
+
+Rows = Union[torch.Tensor, Sequence[torch.Tensor]]
+
+
+class PagedKVCache:
+    """``num_layers`` pools of ``num_blocks`` 16-token blocks sharing one block
+    table per sequence (every layer stores a token at the same slot)."""
+
+    def __init__(self, num_layers: int, num_blocks: int, num_kv_heads: int, head_dim: int,
+                 cache_dtype: torch.dtype, max_blocks_per_seq: int, device="cuda"):
+        self.num_layers = num_layers
+        self.num_blocks = num_blocks
+        self.num_kv_heads = num_kv_heads
+        self.head_dim = head_dim
+        self.max_blocks_per_seq = max_blocks_per_seq
+        self.device = torch.device(device)
+        self.fp8 = cache_dtype in (torch.uint8, torch.float8_e4m3fn)
+        self.cache_dtype = torch.uint8 if self.fp8 else cache_dtype
+        shape = (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim)
+        self.k = [torch.empty(shape, dtype=self.cache_dtype, device=self.device) for _ in range(num_layers)]
+        self.v = [torch.empty(shape, dtype=self.cache_dtype, device=self.device) for _ in range(num_layers)]
+        if self.fp8:
+            sshape = (num_blocks, num_kv_heads, BLOCK_SIZE)
+            self.k_scale = [torch.empty(sshape, dtype=torch.float32, device=self.device) for _ in range(num_layers)]
+            self.v_scale = [torch.empty(sshape, dtype=torch.float32, device=self.device) for _ in range(num_layers)]
+        else:
+            self.k_scale = [None] * num_layers
+            self.v_scale = [None] * num_layers
+        self.alloc = BlockAllocator(num_blocks, max_blocks_per_seq)
+        self.cow_pairs_applied: List[tuple] = []
+        self._ws: Optional[torch.Tensor] = None
+
+    # -- allocator passthroughs ----------------------------------------------
+    def set_free_order(self, order) -> None:
+        self.alloc.set_free_order(order)
+
+    def create(self, seq_id: int) -> None:
+        self.alloc.create(seq_id)
+
+    def fork(self, parent: int, child: int) -> None:
+        self.alloc.fork(parent, child)
+
+    def free(self, seq_id: int) -> None:
+        self.alloc.free(seq_id)
+
+    def seq_len(self, seq_id: int) -> int:
+        return self.alloc.seq_len(seq_id)
+
+    # -- writes ---------------------------------------------------------------
+    def _layer_rows(self, rows: Rows, layer: int) -> torch.Tensor:
+        if isinstance(rows, torch.Tensor):
+            return rows
+        return rows[layer]
+
+    def _apply_cow(self, pairs) -> None:
+        if not pairs:
+            return
+        t = torch.tensor(pairs, dtype=torch.int32).to(self.device)
+        for layer in range(self.num_layers):
+            copy_blocks(self.k[layer], self.v[layer], t, self.k_scale[layer], self.v_scale[layer])
+        self.cow_pairs_applied.extend(pairs)
+
+    def _write(self, slots: torch.Tensor, k_rows: Rows, v_rows: Rows) -> None:
+        for layer in range(self.num_layers):
+            kv_cache_append(self._layer_rows(k_rows, layer), self._layer_rows(v_rows, layer),
+                            self.k[layer], self.v[layer], slots,
+                            self.k_scale[layer], self.v_scale[layer])
+
+    def append(self, seq_id: int, k_rows: Rows, v_rows: Rows) -> List[int]:
+        """Append n token rows ``[n, Hkv, D]`` (device tensors; one tensor for
+        every layer or a list per layer) to one sequence."""
+        n = int(self._layer_rows(k_rows, 0).shape[0])
+        slots, pairs = self.alloc.append_slots(seq_id, n)
+        self._apply_cow(pairs)
+        if n:
+            self._write(torch.tensor(slots, dtype=torch.int64).to(self.device), k_rows, v_rows)
+        return slots
+
+    def append_one_each(self, seq_ids: Sequence[int], k_rows: Rows, v_rows: Rows) -> List[int]:
+        """One decode step's append: row i of ``k_rows [B, Hkv, D]`` goes to
+        sequence ``seq_ids[i]``."""
+        slots, pairs = self.alloc.batch_append_one(list(seq_ids))
+        self._apply_cow(pairs)
+        self._write(torch.tensor(slots, dtype=torch.int64).to(self.device), k_rows, v_rows)
+        return slots
+
+    # -- reads ----------------------------------------------------------------
+    def block_tables(self, seq_ids: Sequence[int]):
+        """Device (tables int32 [B, max_blocks_per_seq], lens int32 [B]) and the
+        host max context length."""
+        tables, lens = self.alloc.block_tables(list(seq_ids), self.max_blocks_per_seq)
+        max_len = int(lens.max()) if len(seq_ids) else 0
+        return tables.to(self.device), lens.to(self.device), max_len
+
+    def decode(self, q: torch.Tensor, layer: int, seq_ids: Optional[Sequence[int]] = None,
+               tables=None, partition_size: int = 0, out: Optional[torch.Tensor] = None,
+               max_context_len: Optional[int] = None) -> torch.Tensor:
+        if tables is None:
+            tables = self.block_tables(seq_ids)
+        bt, lens, max_len = tables
+        if max_context_len is not None:
+            max_len = max_context_len
+        if out is None:
+            out = torch.empty_like(q)
+        need = workspace_size(q.shape[0], q.shape[1], self.num_kv_heads, self.head_dim, max_len,
+                              partition_size, dtype_code(self.cache_dtype))
+        if need and (self._ws is None or self._ws.numel() < need):
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return paged_attention_decode(out, q, self.k[layer], self.v[layer], bt, lens, max_len,
+                                      k_scale=self.k_scale[layer], v_scale=self.v_scale[layer],
+                                      partition_size=partition_size, workspace=self._ws)

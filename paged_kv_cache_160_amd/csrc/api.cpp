@@ -1,0 +1,196 @@
+// C-ABI shim: host-side argument checks, workspace sizing and kernel
+// dispatch.  Nothing here allocates device memory or synchronises.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "launch.h"
+#include "pagedkv.h"
+
+namespace {
+
+constexpr int kBlock = PKV_BLOCK_SIZE;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int d) { return d >= PKV_F32 && d <= PKV_FP8_E4M3; }
+
+bool supported_head_dim(int d) { return d == 64 || d == 128; }
+
+// (q dtype, cache dtype) pairs the decode kernels are built for.
+bool decode_pair_ok(pkv_dtype q, pkv_dtype c) {
+  if (c == PKV_FP8_E4M3) return q == PKV_BF16 || q == PKV_F16;
+  return q == c;
+}
+
+int resolve_partitions(int num_seqs, int num_kv_heads, int max_context_len, int partition_size,
+                       int* ps_out, int* np_out) {
+  int ps = partition_size;
+  if (ps == 0) ps = pkv::choose_partition_size(num_seqs, num_kv_heads, max_context_len);
+  if (ps <= 0 || ps % kBlock != 0) return PKV_ERR_INVALID_ARG;
+  int64_t np = (static_cast<int64_t>(max_context_len) + ps - 1) / ps;
+  if (np < 1) np = 1;
+  if (np > (1 << 20)) return PKV_ERR_UNSUPPORTED;
+  *ps_out = ps;
+  *np_out = static_cast<int>(np);
+  return PKV_OK;
+}
+
+size_t workspace_bytes_for(int num_seqs, int num_q_heads, int head_dim, int np) {
+  if (np <= 1) return 0;
+  const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * np;
+  // (m, l) pairs, then the unnormalised outputs; the second part starts on a
+  // 256-byte boundary.
+  size_t ml = rows * 2 * sizeof(float);
+  ml = (ml + 255) & ~static_cast<size_t>(255);
+  return ml + rows * head_dim * sizeof(float);
+}
+
+bool decode_sizes_ok(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                     int max_context_len) {
+  return num_seqs >= 0 && num_kv_heads > 0 && num_q_heads > 0 && num_q_heads % num_kv_heads == 0 &&
+         max_context_len >= 0 && head_dim > 0;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_abi_version(void) { return PKV_ABI_VERSION; }
+
+const char* pkv_strerror(int code) {
+  switch (code) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_INVALID_ARG: return "invalid argument";
+    case PKV_ERR_UNSUPPORTED: return "unsupported dtype, head_dim or group size";
+    case PKV_ERR_WORKSPACE: return "workspace missing or too small";
+    case PKV_ERR_HIP: return "HIP runtime error";
+    case PKV_ERR_NO_FREE_BLOCKS: return "no free blocks";
+    case PKV_ERR_UNKNOWN_SEQ: return "unknown sequence id";
+    default: return "unknown error code";
+  }
+}
+
+int kv_cache_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                    float* k_scale, float* v_scale, const int64_t* slot_mapping, int num_tokens,
+                    int num_kv_heads, int head_dim, int num_blocks, pkv_dtype src_dtype,
+                    pkv_dtype cache_dtype, void* stream) {
+  if (!valid_dtype(src_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PKV_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (src_dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
+  if (cache_dtype != PKV_FP8_E4M3 && src_dtype != cache_dtype) return PKV_ERR_UNSUPPORTED;
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping) return PKV_ERR_INVALID_ARG;
+  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
+    return PKV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(num_tokens) * num_kv_heads > (static_cast<int64_t>(1) << 31))
+    return PKV_ERR_UNSUPPORTED;
+  return pkv::launch_append(k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, num_tokens,
+                            num_kv_heads, head_dim, num_blocks, src_dtype, cache_dtype,
+                            static_cast<hipStream_t>(stream));
+}
+
+int pkv_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                    const int32_t* pairs, int n_pairs, int num_kv_heads, int head_dim,
+                    int num_blocks, pkv_dtype cache_dtype, void* stream) {
+  if (!valid_dtype(cache_dtype) || n_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (n_pairs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !pairs) return PKV_ERR_INVALID_ARG;
+  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_INVALID_ARG;
+  if (n_pairs > 65535 || num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
+  return pkv::launch_copy_blocks(k_pool, v_pool, k_scale, v_scale, pairs, n_pairs, num_kv_heads,
+                                 head_dim, num_blocks, cache_dtype, static_cast<hipStream_t>(stream));
+}
+
+int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                              int max_context_len, pkv_dtype cache_dtype, int* partition_size_out,
+                              int* num_partitions_out) {
+  (void)head_dim;
+  (void)cache_dtype;
+  if (!partition_size_out || !num_partitions_out) return PKV_ERR_INVALID_ARG;
+  if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, 64, max_context_len))
+    return PKV_ERR_INVALID_ARG;
+  return resolve_partitions(num_seqs, num_kv_heads, max_context_len, 0, partition_size_out,
+                            num_partitions_out);
+}
+
+size_t paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
+                                      int head_dim, int max_context_len, int partition_size,
+                                      pkv_dtype cache_dtype) {
+  (void)cache_dtype;
+  if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len)) return 0;
+  int ps, np;
+  if (resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, &ps, &np) != PKV_OK)
+    return 0;
+  return workspace_bytes_for(num_seqs, num_q_heads, head_dim, np);
+}
+
+int paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                           const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                           const int32_t* context_lens, int num_seqs, int num_q_heads,
+                           int num_kv_heads, int head_dim, int num_blocks, int max_blocks_per_seq,
+                           int max_context_len, float scale, pkv_dtype q_dtype,
+                           pkv_dtype cache_dtype, int partition_size, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
+  if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len))
+    return PKV_ERR_INVALID_ARG;
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBlock)
+    return PKV_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (!decode_pair_ok(q_dtype, cache_dtype)) return PKV_ERR_UNSUPPORTED;
+  if (num_q_heads / num_kv_heads > 16) return PKV_ERR_UNSUPPORTED;
+  if (partition_size < 0 || partition_size % kBlock != 0) return PKV_ERR_INVALID_ARG;
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_INVALID_ARG;
+  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
+    return PKV_ERR_INVALID_ARG;
+  if (cache_dtype == PKV_FP8_E4M3 && (!aligned16(k_scale) || !aligned16(v_scale)))
+    return PKV_ERR_INVALID_ARG;
+
+  int ps, np;
+  int rc = resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, &ps, &np);
+  if (rc != PKV_OK) return rc;
+  const size_t need = workspace_bytes_for(num_seqs, num_q_heads, head_dim, np);
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return PKV_ERR_WORKSPACE;
+
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.scale = scale;
+  a.q_dtype = q_dtype;
+  a.cache_dtype = cache_dtype;
+  a.partition_size = ps;
+  a.num_partitions = np;
+  if (np > 1) {
+    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * np;
+    size_t ml = (rows * 2 * sizeof(float) + 255) & ~static_cast<size_t>(255);
+    a.part_ml = static_cast<float*>(workspace);
+    a.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml);
+  }
+  return pkv::launch_decode(a, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

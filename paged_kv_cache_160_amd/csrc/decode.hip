@@ -1,0 +1,518 @@
+// Paged decode attention for gfx950: one query token per sequence attends
+// over its cached K/V, read through the block table.
+//
+// Pages: softmax(Q K^T / sqrt(d_k)) V ("企业官网建设流程全解析" §1.2); the query
+// attends to every cached token, its own included (§3.2-3.3 of the same
+// page); several query heads share one KV head (§2.2 of the same page); the
+// block table translates logical blocks to physical blocks and only the
+// sequence's own blocks are read ("KV Cache 和 vLLM" §3.2); decode time goes
+// to moving the cached K/V out of device memory, so bandwidth sets the speed
+// ("KV Cache 和 vLLM" §2.3).
+//
+// Design (MI355X / CDNA4):
+//  * Workgroup = 4 waves for one (sequence, KV head, partition).  A partition
+//    is a run of logical positions; wave w takes the partition's blocks w,
+//    w+4, w+8, ...  Each wave streams its blocks straight from HBM into
+//    registers with 16-byte loads, two blocks in flight, and keeps its own
+//    online-softmax state; the 4 states merge through LDS at the end.
+//  * The whole GQA group is served from one read of each K/V tile: the
+//    group's query heads are the 16 columns of an MFMA tile (columns >= G are
+//    zero), so one 16x16 MFMA output holds 16 tokens x 16 heads.
+//      S^T = K_tile (16 tok x D) * Q^T (D x 16 heads)    [16x16x32 MFMA]
+//      O  += P (16 heads x 16 tok) * V_tile (16 tok x D) [16x16x16 MFMA]
+//    The S^T accumulator layout (lane = head + 16*(token/4), reg = token%4)
+//    is exactly the A-operand layout P needs, so no transpose is done.  The
+//    contraction index of each MFMA may be permuted freely as long as both
+//    operands use the same permutation: each lane loads a contiguous 1/4 of
+//    a K row, and 4 V rows x D/16 contiguous columns.
+//  * fp8 e4m3 codes convert exactly to bf16/f16 in hardware; the per-token
+//    scales multiply the scores (k) and the probabilities (v), never each
+//    element.
+//  * Probabilities enter the P*V MFMA as a hi + lo pair of 16-bit values, so
+//    P carries ~16 significant bits while the MFMA still accumulates in fp32.
+//  * Long sequences split into partitions whose (max, sum, unnormalised
+//    output) are merged by a second kernel with the log-sum-exp formula.
+
+#include <math.h>
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace pkv {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * kWave;
+constexpr int kMaxGroup = 16;
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- raw register loads -------------------------------------------------------
+
+template <int N>
+struct Words {
+  uint32_t w[N];
+};
+
+template <int N>
+__device__ __forceinline__ void load_words(Words<N>& dst, const uint8_t* p) {
+  if constexpr (N % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < N / 4; ++i) {
+      uint4 v = reinterpret_cast<const uint4*>(p)[i];
+      dst.w[4 * i + 0] = v.x;
+      dst.w[4 * i + 1] = v.y;
+      dst.w[4 * i + 2] = v.z;
+      dst.w[4 * i + 3] = v.w;
+    }
+  } else if constexpr (N == 2) {
+    uint2 v = *reinterpret_cast<const uint2*>(p);
+    dst.w[0] = v.x;
+    dst.w[1] = v.y;
+  } else {
+    static_assert(N == 1, "unsupported load width");
+    dst.w[0] = *reinterpret_cast<const uint32_t*>(p);
+  }
+}
+
+// ---- per-flavour geometry -------------------------------------------------------
+//   QT: query/output type (F32, F16, BF16); CT: cache type (same, or FP8).
+template <typename QT, typename CT, int D>
+struct Geo {
+  static constexpr int ces = CT::bytes;
+  static constexpr int qes = QT::bytes;
+  static constexpr int kWords = D / 4 * ces / 4;    // K words per lane (1/4 of a row)
+  static constexpr int qWords = D / 4 * qes / 4;    // Q words per lane
+  static constexpr int DC = D / 16;                 // V columns per lane = P*V tiles
+  static constexpr int vWords = DC * ces / 4;       // V words per lane per row
+  static constexpr int tileBytes = kBlockTokens * D * ces;
+};
+
+template <typename QT, typename CT, int D>
+struct BlockRegs {
+  using G = Geo<QT, CT, D>;
+  Words<G::kWords> k;
+  Words<G::vWords> v[4];      // rows 4j..4j+3
+  float4 ks, vs;              // fp8 scales of tokens 4j..4j+3
+};
+
+// ---- QK^T on MFMA -----------------------------------------------------------------
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ float4_t qk_tile(const Words<Geo<QT, CT, D>::kWords>& k,
+                                            const Words<Geo<QT, CT, D>::qWords>& q) {
+  float4_t s = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (std::is_same<CT, F32>::value) {
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i)
+      s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.w[i]), __uint_as_float(q.w[i]), s, 0, 0, 0);
+  } else if constexpr (std::is_same<CT, FP8>::value) {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      uint32_t a[4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint32_t src = k.w[2 * i + h];
+        if constexpr (std::is_same<QT, BF16>::value) {
+          a[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, false));
+          a[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, true));
+        } else {
+          a[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, false));
+          a[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, true));
+        }
+      }
+      uint4 av = make_uint4(a[0], a[1], a[2], a[3]);
+      uint4 bv = make_uint4(q.w[4 * i], q.w[4 * i + 1], q.w[4 * i + 2], q.w[4 * i + 3]);
+      if constexpr (std::is_same<QT, BF16>::value)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                    __builtin_bit_cast(bf16x8_t, bv), s, 0, 0, 0);
+      else
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av),
+                                                   __builtin_bit_cast(half8_t, bv), s, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      uint4 av = make_uint4(k.w[4 * i], k.w[4 * i + 1], k.w[4 * i + 2], k.w[4 * i + 3]);
+      uint4 bv = make_uint4(q.w[4 * i], q.w[4 * i + 1], q.w[4 * i + 2], q.w[4 * i + 3]);
+      if constexpr (std::is_same<CT, BF16>::value)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                    __builtin_bit_cast(bf16x8_t, bv), s, 0, 0, 0);
+      else
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av),
+                                                   __builtin_bit_cast(half8_t, bv), s, 0, 0, 0);
+    }
+  }
+  return s;
+}
+
+// Pack two fp32 values into a word of two 16-bit values of type QT (RNE).
+template <typename QT>
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  if constexpr (std::is_same<QT, BF16>::value) {
+    bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    half2_t v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+template <typename QT>
+__device__ __forceinline__ float lo16_to_f32(uint32_t w) {
+  if constexpr (std::is_same<QT, BF16>::value) return __uint_as_float(w << 16);
+  else return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w & 0xffffu)));
+}
+template <typename QT>
+__device__ __forceinline__ float hi16_to_f32(uint32_t w) {
+  if constexpr (std::is_same<QT, BF16>::value) return __uint_as_float(w & 0xffff0000u);
+  else return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+template <typename QT>
+__device__ __forceinline__ float4_t mfma16(uint2 a, uint2 b, float4_t c) {
+  if constexpr (std::is_same<QT, BF16>::value)
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(short4_t, a),
+                                                      __builtin_bit_cast(short4_t, b), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(half4_t, a),
+                                                 __builtin_bit_cast(half4_t, b), c, 0, 0, 0);
+}
+
+// ---- P*V on MFMA -----------------------------------------------------------------
+// p[r]: probability (times the fp8 V scale) of token 4j+r for head column c.
+template <typename QT, typename CT, int D>
+__device__ __forceinline__ void pv_tile(const float (&p)[4], const Words<Geo<QT, CT, D>::vWords> (&v)[4],
+                                        float4_t (&o)[D / 16]) {
+  using G = Geo<QT, CT, D>;
+  if constexpr (std::is_same<CT, F32>::value) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int nt = 0; nt < G::DC; ++nt)
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[r], __uint_as_float(v[r].w[nt]), o[nt], 0, 0, 0);
+  } else {
+    // hi/lo split of the probabilities
+    uint32_t h01 = pack2<QT>(p[0], p[1]);
+    uint32_t h23 = pack2<QT>(p[2], p[3]);
+    uint32_t l01 = pack2<QT>(p[0] - lo16_to_f32<QT>(h01), p[1] - hi16_to_f32<QT>(h01));
+    uint32_t l23 = pack2<QT>(p[2] - lo16_to_f32<QT>(h23), p[3] - hi16_to_f32<QT>(h23));
+    const uint2 phi = make_uint2(h01, h23);
+    const uint2 plo = make_uint2(l01, l23);
+    // 16-bit words of the 4 V rows: element nt of row e sits in word nt/2.
+    uint32_t w16[4][G::DC / 2];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if constexpr (std::is_same<CT, FP8>::value) {
+#pragma unroll
+        for (int i = 0; i < G::vWords; ++i) {
+          uint32_t src = v[e].w[i];
+          if constexpr (std::is_same<QT, BF16>::value) {
+            w16[e][2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, false));
+            w16[e][2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, true));
+          } else {
+            w16[e][2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, false));
+            w16[e][2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, true));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < G::vWords; ++i) w16[e][i] = v[e].w[i];
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < G::DC; ++nt) {
+      const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
+      const int wi = nt >> 1;
+      uint2 b;
+      b.x = __builtin_amdgcn_perm(w16[1][wi], w16[0][wi], sel);
+      b.y = __builtin_amdgcn_perm(w16[3][wi], w16[2][wi], sel);
+      o[nt] = mfma16<QT>(phi, b, o[nt]);
+      o[nt] = mfma16<QT>(plo, b, o[nt]);
+    }
+  }
+}
+
+// ---- the main kernel ------------------------------------------------------------
+
+template <typename QT, typename CT, int D>
+__global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a) {
+  using G = Geo<QT, CT, D>;
+  constexpr bool kFp8 = std::is_same<CT, FP8>::value;
+  constexpr float kNegInf = -INFINITY;
+
+  __shared__ float sm_m[kWaves][kMaxGroup];
+  __shared__ float sm_l[kWaves][kMaxGroup];
+  __shared__ float sm_o[kWaves][kMaxGroup][D];
+
+  const int P = a.num_partitions;
+  const int part = blockIdx.x % P;
+  const int g = (blockIdx.x / P) % a.num_kv_heads;
+  const int b = blockIdx.x / (P * a.num_kv_heads);
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+
+  int L = a.context_lens[b];
+  L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * kBlockTokens)));
+  const int tok0 = part * a.partition_size;
+  const int64_t out_row0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(g) * group;
+
+  if (tok0 >= L) {
+    // Nothing to attend to in this partition.  With a single partition the
+    // output row is defined as zero; with several, the reduce kernel only
+    // reads partitions below ceil(L / partition_size).
+    if (P == 1) {
+      for (int i = tid; i < group * D; i += kThreads)
+        store_from_f32<QT>(a.out, out_row0 * D + i, 0.0f);
+    }
+    return;
+  }
+  const int tok1 = min(L, tok0 + a.partition_size);
+  const int blk0 = tok0 / kBlockTokens;
+  const int nblk = (tok1 - tok0 + kBlockTokens - 1) / kBlockTokens;
+  const int32_t* table = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq + blk0;
+
+  // Q^T operand: lane (head column c, k-group j) holds q[head c][j*D/4 ...).
+  Words<G::qWords> qop;
+  {
+    const bool valid = c < group;
+    const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
+                        ((out_row0 + (valid ? c : 0)) * D + j * (D / 4)) * G::qes;
+    load_words(qop, qp);
+    if (!valid) {
+#pragma unroll
+      for (int i = 0; i < G::qWords; ++i) qop.w[i] = 0u;
+    }
+  }
+  const float qk_scale = a.scale * kLog2e;   // scores in log2 units
+
+  const uint8_t* kbase = static_cast<const uint8_t*>(a.k_pool);
+  const uint8_t* vbase = static_cast<const uint8_t*>(a.v_pool);
+  const int64_t k_lane = static_cast<int64_t>(c * D + j * (D / 4)) * G::ces;
+  const int64_t v_lane = static_cast<int64_t>((4 * j) * D + G::DC * c) * G::ces;
+
+  // Load one block's K/V (and scales) for this lane.  Blocks whose physical
+  // id lies outside the pool are read from block 0 and fully masked.
+  auto load_block = [&](BlockRegs<QT, CT, D>& r, int i, bool& ok) {
+    int phys = __builtin_amdgcn_readfirstlane(table[i]);
+    ok = phys >= 0 && phys < a.num_blocks;
+    if (!ok) phys = 0;
+    const int64_t tile = static_cast<int64_t>(phys) * a.num_kv_heads + g;
+    const uint8_t* kt = kbase + tile * G::tileBytes;
+    const uint8_t* vt = vbase + tile * G::tileBytes;
+    load_words(r.k, kt + k_lane);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) load_words(r.v[e], vt + v_lane + static_cast<int64_t>(e) * D * G::ces);
+    if constexpr (kFp8) {
+      r.ks = *reinterpret_cast<const float4*>(a.k_scale + tile * kBlockTokens + 4 * j);
+      r.vs = *reinterpret_cast<const float4*>(a.v_scale + tile * kBlockTokens + 4 * j);
+    }
+  };
+
+  float m = kNegInf;          // running max of head column c (log2 units)
+  float l = 0.0f;             // this lane's share of the running sum
+  float4_t o[G::DC];
+#pragma unroll
+  for (int nt = 0; nt < G::DC; ++nt) o[nt] = {0.f, 0.f, 0.f, 0.f};
+
+  auto compute_block = [&](BlockRegs<QT, CT, D>& r, int i, bool ok) {
+    const int base = tok0 + i * kBlockTokens;   // logical position of the block's token 0
+    float4_t s = qk_tile<QT, CT, D>(r.k, qop);
+    float sc[4] = {s[0], s[1], s[2], s[3]};
+    float ksc[4] = {1.f, 1.f, 1.f, 1.f};
+    float vsc[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (kFp8) {
+      ksc[0] = r.ks.x; ksc[1] = r.ks.y; ksc[2] = r.ks.z; ksc[3] = r.ks.w;
+      vsc[0] = r.vs.x; vsc[1] = r.vs.y; vsc[2] = r.vs.z; vsc[3] = r.vs.w;
+    }
+    bool valid[4];
+    const bool partial = !ok || base + kBlockTokens > tok1;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      valid[t] = ok && (base + 4 * j + t < tok1);
+      float x = sc[t] * ksc[t] * qk_scale;
+      sc[t] = valid[t] ? x : kNegInf;
+    }
+    if (partial) {
+      // zero V rows of masked tokens (their slots may hold any bits)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (!valid[e]) {
+#pragma unroll
+          for (int w = 0; w < G::vWords; ++w) r.v[e].w[w] = 0u;
+          vsc[e] = 0.f;
+        }
+      }
+    }
+    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
+    bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+    const float m_new = fmaxf(m, bm);
+    const float alpha = (m_new == kNegInf) ? 1.0f : exp2f(m - m_new);
+    float p[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float e = valid[t] ? exp2f(sc[t] - m_new) : 0.0f;
+      psum += e;
+      p[t] = e * vsc[t];
+    }
+    l = l * alpha + psum;
+    m = m_new;
+    // rescale O: lane (c, j) reg r holds head row 4j+r; alpha of head h sits
+    // in lane h (all lanes of column h agree).
+    float ar[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) ar[rr] = __shfl(alpha, 4 * j + rr, kWave);
+#pragma unroll
+    for (int nt = 0; nt < G::DC; ++nt) {
+      o[nt][0] *= ar[0];
+      o[nt][1] *= ar[1];
+      o[nt][2] *= ar[2];
+      o[nt][3] *= ar[3];
+    }
+    pv_tile<QT, CT, D>(p, r.v, o);
+  };
+
+  // Two blocks in flight per wave.
+  BlockRegs<QT, CT, D> r0, r1;
+  bool ok0 = true, ok1 = true;
+  int i = wave;
+  if (i < nblk) load_block(r0, i, ok0);
+  if (i + kWaves < nblk) load_block(r1, i + kWaves, ok1);
+  for (; i < nblk; i += 2 * kWaves) {
+    compute_block(r0, i, ok0);
+    if (i + 2 * kWaves < nblk) load_block(r0, i + 2 * kWaves, ok0);
+    if (i + kWaves < nblk) {
+      compute_block(r1, i + kWaves, ok1);
+      if (i + 3 * kWaves < nblk) load_block(r1, i + 3 * kWaves, ok1);
+    }
+  }
+
+  // ---- merge the waves' states ----
+  l += __shfl_xor(l, 16, kWave);
+  l += __shfl_xor(l, 32, kWave);
+  if (j == 0 && c < group) {
+    sm_m[wave][c] = m;
+    sm_l[wave][c] = l;
+  }
+#pragma unroll
+  for (int rr = 0; rr < 4; ++rr) {
+    const int h = 4 * j + rr;
+    if (h < group) {
+#pragma unroll
+      for (int nt = 0; nt < G::DC; ++nt) sm_o[wave][h][G::DC * c + nt] = o[nt][rr];
+    }
+  }
+  __syncthreads();
+
+  for (int idx = tid; idx < group * D; idx += kThreads) {
+    const int h = idx / D;
+    const int d = idx % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+    float acc = 0.f, lsum = 0.f;
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm_m[w][h];
+        if (mw != kNegInf) {
+          const float f = exp2f(mw - M);
+          acc += f * sm_o[w][h][d];
+          lsum += f * sm_l[w][h];
+        }
+      }
+    }
+    const int64_t row = out_row0 + h;
+    if (P == 1) {
+      store_from_f32<QT>(a.out, row * D + d, lsum > 0.f ? acc / lsum : 0.f);
+    } else {
+      const int64_t prow = row * P + part;
+      a.part_acc[prow * D + d] = acc;
+      if (d == 0) {
+        a.part_ml[2 * prow] = M;
+        a.part_ml[2 * prow + 1] = lsum;
+      }
+    }
+  }
+}
+
+// ---- log-sum-exp merge of partitions ------------------------------------------------
+// One workgroup of D threads per (sequence, query head).
+template <typename QT, int D>
+__global__ void __launch_bounds__(D) partition_reduce_kernel(DecodeArgs a) {
+  const int row = blockIdx.x;                 // b * Hq + h
+  const int b = row / a.num_q_heads;
+  const int d = threadIdx.x;
+  const int P = a.num_partitions;
+  int L = a.context_lens[b];
+  L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * kBlockTokens)));
+  const int np = (L + a.partition_size - 1) / a.partition_size;
+  const float* ml = a.part_ml + static_cast<int64_t>(row) * P * 2;
+  const float* acc = a.part_acc + static_cast<int64_t>(row) * P * D;
+  float M = -INFINITY;
+  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
+  float num = 0.f, den = 0.f;
+  if (M != -INFINITY) {
+    for (int p = 0; p < np; ++p) {
+      const float mp = ml[2 * p];
+      if (mp == -INFINITY) continue;
+      const float f = exp2f(mp - M);
+      num += f * acc[static_cast<int64_t>(p) * D + d];
+      den += f * ml[2 * p + 1];
+    }
+  }
+  store_from_f32<QT>(a.out, static_cast<int64_t>(row) * D + d, den > 0.f ? num / den : 0.f);
+}
+
+// ---- host side -------------------------------------------------------------------------
+
+int choose_partition_size(int num_seqs, int num_kv_heads, int max_context_len) {
+  // Aim for about 2048 resident waves (2 per SIMD on 256 CUs) with at least
+  // 4 blocks per wave; a partition is a multiple of 16 * waves-per-group.
+  const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads;
+  const int64_t blocks = units * ((max_context_len + kBlockTokens - 1) / kBlockTokens);
+  int64_t per_wave = (blocks + 2047) / 2048;
+  if (per_wave < 4) per_wave = 4;
+  int64_t ps = per_wave * kWaves * kBlockTokens;
+  const int64_t cap = ((static_cast<int64_t>(max_context_len) + kBlockTokens - 1) / kBlockTokens) * kBlockTokens;
+  if (ps > cap) ps = cap > 0 ? cap : kBlockTokens;
+  if (ps > (1 << 30)) ps = 1 << 30;
+  return static_cast<int>(ps);
+}
+
+template <typename QT, typename CT, int D>
+static int launch_typed(const DecodeArgs& a, hipStream_t stream) {
+  const int64_t grid = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.num_partitions;
+  if (grid > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL((paged_decode_kernel<QT, CT, D>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
+                     0, stream, a);
+  int rc = check_launch();
+  if (rc != PKV_OK || a.num_partitions == 1) return rc;
+  hipLaunchKernelGGL((partition_reduce_kernel<QT, D>), dim3(a.num_seqs * a.num_q_heads), dim3(D), 0,
+                     stream, a);
+  return check_launch();
+}
+
+template <typename QT, typename CT>
+static int launch_dim(const DecodeArgs& a, hipStream_t stream) {
+  if (a.head_dim == 128) return launch_typed<QT, CT, 128>(a, stream);
+  return launch_typed<QT, CT, 64>(a, stream);
+}
+
+int launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  switch (a.cache_dtype) {
+    case PKV_F32: return launch_dim<F32, F32>(a, stream);
+    case PKV_F16: return launch_dim<F16, F16>(a, stream);
+    case PKV_BF16: return launch_dim<BF16, BF16>(a, stream);
+    case PKV_FP8_E4M3:
+      if (a.q_dtype == PKV_BF16) return launch_dim<BF16, FP8>(a, stream);
+      return launch_dim<F16, FP8>(a, stream);
+  }
+  return PKV_ERR_UNSUPPORTED;
+}
+
+}  // namespace pkv

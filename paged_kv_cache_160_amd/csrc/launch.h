@@ -1,0 +1,49 @@
+// Host-side declarations shared by the C-ABI shim and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "pagedkv.h"
+
+namespace pkv {
+
+// Map the runtime's last error after a launch to a return code.
+inline int check_launch() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int launch_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                  float* k_scale, float* v_scale, const int64_t* slot_mapping, int num_tokens,
+                  int num_kv_heads, int head_dim, int num_blocks, pkv_dtype src_dtype,
+                  pkv_dtype cache_dtype, hipStream_t stream);
+
+int launch_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                       const int32_t* pairs, int n_pairs, int num_kv_heads, int head_dim,
+                       int num_blocks, pkv_dtype cache_dtype, hipStream_t stream);
+
+struct DecodeArgs {
+  void* out;
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int num_seqs, num_q_heads, num_kv_heads, head_dim;
+  int num_blocks, max_blocks_per_seq, max_context_len;
+  float scale;
+  pkv_dtype q_dtype, cache_dtype;
+  int partition_size;      // tokens, multiple of 16 (resolved, never 0)
+  int num_partitions;      // ceil(max_context_len / partition_size), >= 1
+  float* part_ml;          // [num_seqs][num_q_heads][num_partitions][2]  (m, l)
+  float* part_acc;         // [num_seqs][num_q_heads][num_partitions][head_dim]
+};
+
+int launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Automatic partition length for a decode launch (tokens, multiple of 16).
+int choose_partition_size(int num_seqs, int num_kv_heads, int max_context_len);
+
+}  // namespace pkv

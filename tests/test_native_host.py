@@ -1,0 +1,246 @@
+"""Host-side checks of libpagedkv.so that need no GPU: every declared symbol
+is exported, the C++ allocator matches the oracle's allocator model
+bit-exactly on every workload's setup and on random operation streams, and
+invalid arguments are rejected on the host before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_cache_160_amd as pkv
+from paged_kv_cache_160_amd import _lib
+import workloads as wl
+from oracle.allocator import AllocError, BlockAllocatorModel
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "pagedkv.h")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "sizeof")))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("kv_cache_append", "paged_attention_decode", "paged_attention_workspace_size",
+                     "pkv_copy_blocks", "pkv_alloc_create", "pkv_seq_append_slots"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    # and the binding declares a signature for each of them
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_strerror_and_version():
+    lib = _lib.lib()
+    assert lib.pkv_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.pkv_strerror(code)
+    assert lib.pkv_strerror(-99) == b"unknown error code"
+
+
+# ---- allocator: C++ vs the oracle model ------------------------------------------
+
+def _run_both(w, ops):
+    model = BlockAllocatorModel(w.num_blocks, w.max_blocks_per_seq)
+    native = pkv.BlockAllocator(w.num_blocks, w.max_blocks_per_seq)
+    for op in ops:
+        kind = op[0]
+        if kind == "free_order":
+            model.set_free_order(op[1])
+            native.set_free_order(op[1])
+        elif kind == "create":
+            model.create(op[1]); native.create(op[1])
+        elif kind == "fork":
+            model.fork(op[1], op[2]); native.fork(op[1], op[2])
+        elif kind == "free":
+            model.free_seq(op[1]); native.free(op[1])
+        elif kind == "append":
+            a = model.append_slots(op[1], op[2])
+            b = native.append_slots(op[1], op[2])
+            assert a == b, op
+    return model, native
+
+
+@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
+def test_allocator_matches_model_on_workload_setup(cid):
+    w = wl.make_workload(cid)
+    model, native = _run_both(w, wl.setup_ops(w))
+    seqs = list(range(w.num_seqs))
+    mt, ml = model.block_tables(seqs, w.max_blocks_per_seq)
+    nt, nl = native.block_tables(seqs)
+    assert np.array_equal(np.array(mt, dtype=np.int32), nt.numpy())
+    assert ml == nl.tolist() == w.context_lens
+    ms, ns = model.stats(), native.stats()
+    for k in ms:
+        assert ms[k] == pytest.approx(ns[k]), k
+    # with long sequences the last-block waste is small: utilisation > 90%
+    # ("KV Cache 和 vLLM" §3.1 reports above 90% for paged storage)
+    if cid >= 2:
+        assert ns["utilisation"] > 0.9
+
+
+def test_workload4_copy_on_write_pairs():
+    w = wl.make_workload(4)
+    model, native = _run_both(w, wl.setup_ops(w))
+    st = native.stats()
+    # 8 holders of the partial prefix block: the first 7 appenders copy it
+    assert st["cow_copies"] == 7
+    assert st["shared_blocks"] == 1500 // 16
+
+
+def test_batch_append_matches_sequential_model():
+    w = wl.make_workload(4)
+    model, native = _run_both(w, wl.setup_ops(w))
+    seqs = list(range(w.num_seqs))
+    for _ in range(40):
+        exp_slots, exp_pairs = [], []
+        for s in seqs:
+            sl, pr = model.append_slots(s, 1)
+            exp_slots += sl
+            exp_pairs += pr
+        got_slots, got_pairs = native.batch_append_one(seqs)
+        assert got_slots == exp_slots and got_pairs == exp_pairs
+
+
+def test_batch_append_shared_block_counts_exact():
+    # 3 forks of a 5-token sequence share its partial block: a batch step
+    # copies for the first three holders and writes in place for the last,
+    # so exactly 3 fresh blocks are needed: a pool of 4 is just enough.
+    native = pkv.BlockAllocator(4, 4)
+    native.create(0)
+    native.append_slots(0, 5)
+    for c in (1, 2, 3):
+        native.fork(0, c)
+    slots, pairs = native.batch_append_one([0, 1, 2, 3])
+    assert len(pairs) == 3 and native.stats()["free_blocks"] == 0
+    assert [s % 16 for s in slots] == [5, 5, 5, 5]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_allocator_random_streams_match_model(seed):
+    rng = np.random.default_rng(100 + seed)
+    nb, mb = 48, 12
+    model = BlockAllocatorModel(nb, mb)
+    native = pkv.BlockAllocator(nb, mb)
+    order = rng.permutation(nb)
+    model.set_free_order(order)
+    native.set_free_order(order)
+    live, nxt = [], 0
+    for _ in range(2000):
+        r = rng.random()
+        if r < 0.15 or not live:
+            model.create(nxt); native.create(nxt); live.append(nxt); nxt += 1
+        elif r < 0.3:
+            s = live.pop(int(rng.integers(len(live))))
+            model.free_seq(s); native.free(s)
+        elif r < 0.4:
+            p = live[int(rng.integers(len(live)))]
+            model.fork(p, nxt); native.fork(p, nxt); live.append(nxt); nxt += 1
+        else:
+            s = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(0, 40))
+            try:
+                exp = model.append_slots(s, n)
+            except AllocError as e:
+                with pytest.raises(pkv.PagedKVError) as got:
+                    native.append_slots(s, n)
+                assert got.value.code == {"no_free_blocks": -5, "invalid_arg": -1}[e.kind]
+                continue
+            assert native.append_slots(s, n) == exp
+        assert model.stats() == pytest.approx(native.stats())
+
+
+def test_allocator_errors_leave_state_unchanged():
+    a = pkv.BlockAllocator(2, 8)
+    a.create(1)
+    a.append_slots(1, 20)
+    before = (a.block_tables([1]), a.stats())
+    with pytest.raises(pkv.PagedKVError) as e:
+        a.append_slots(1, 13)           # needs a third block
+    assert e.value.code == -5
+    after = (a.block_tables([1]), a.stats())
+    assert before[1] == after[1] and np.array_equal(before[0][0], after[0][0])
+    with pytest.raises(pkv.PagedKVError) as e:
+        a.append_slots(7, 1)
+    assert e.value.code == -6
+    with pytest.raises(pkv.PagedKVError) as e:
+        a.create(1)
+    assert e.value.code == -1
+    with pytest.raises(pkv.PagedKVError):
+        a.batch_append_one([1, 1])
+    assert _lib.lib().pkv_alloc_create(0, 4) is None
+
+
+# ---- argument validation of the device calls (host side only) ---------------------
+
+FAKE = 1 << 20          # an aligned non-null address; never dereferenced here
+
+
+def _decode(**kw):
+    args = dict(out=FAKE, q=FAKE, k_pool=FAKE, v_pool=FAKE, k_scale=None, v_scale=None,
+                block_tables=FAKE, context_lens=FAKE, num_seqs=4, num_q_heads=32, num_kv_heads=8,
+                head_dim=128, num_blocks=64, max_blocks_per_seq=8, max_context_len=128, scale=0.1,
+                q_dtype=pkv.PKV_BF16, cache_dtype=pkv.PKV_BF16, partition_size=0,
+                workspace=None, workspace_bytes=0, stream=None)
+    args.update(kw)
+    return _lib.lib().paged_attention_decode(*args.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(head_dim=96), -2),
+    (dict(num_q_heads=30), -1),
+    (dict(num_q_heads=8 * 17), -2),
+    (dict(q_dtype=pkv.PKV_F16), -2),
+    (dict(q_dtype=pkv.PKV_F32, cache_dtype=pkv.PKV_FP8_E4M3), -2),
+    (dict(cache_dtype=pkv.PKV_FP8_E4M3), -1),             # fp8 without scales
+    (dict(max_context_len=8 * 16 + 1), -1),
+    (dict(partition_size=24), -1),
+    (dict(q=FAKE + 4), -1),
+    (dict(q=None), -1),
+    (dict(q_dtype=7), -1),
+    (dict(max_context_len=4096, max_blocks_per_seq=256, partition_size=512), -3),
+])
+def test_decode_rejects_bad_arguments(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_decode_empty_batch_is_noop():
+    assert _decode(num_seqs=0) == 0
+
+
+def test_append_and_copy_reject_bad_arguments():
+    L = _lib.lib()
+    # dtype mismatch, unsupported head_dim, fp8 without scales
+    assert L.kv_cache_append(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 4, 8, 128, 64,
+                             pkv.PKV_F16, pkv.PKV_BF16, None) == -2
+    assert L.kv_cache_append(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 4, 8, 80, 64,
+                             pkv.PKV_BF16, pkv.PKV_BF16, None) == -2
+    assert L.kv_cache_append(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 4, 8, 128, 64,
+                             pkv.PKV_F32, pkv.PKV_FP8_E4M3, None) == -1
+    assert L.kv_cache_append(FAKE, FAKE, FAKE, FAKE, None, None, FAKE, 0, 8, 128, 64,
+                             pkv.PKV_BF16, pkv.PKV_BF16, None) == 0
+    assert L.pkv_copy_blocks(FAKE, FAKE, None, None, FAKE, 2, 8, 128, 64,
+                             pkv.PKV_FP8_E4M3, None) == -1
+    assert L.pkv_copy_blocks(FAKE, FAKE, None, None, FAKE, 0, 8, 128, 64,
+                             pkv.PKV_BF16, None) == 0
+
+
+def test_partition_plan_and_workspace():
+    for (B, hq, hkv, L) in [(16, 32, 8, 4096), (32, 32, 8, 32768), (64, 32, 32, 2048), (4, 4, 2, 41)]:
+        ps, npart = pkv.decode_partition_size(B, hq, hkv, 128, L, pkv.PKV_BF16)
+        assert ps % 16 == 0 and ps > 0 and npart == -(-L // ps)
+        ws = pkv.workspace_size(B, hq, hkv, 128, L, 0, pkv.PKV_BF16)
+        if npart == 1:
+            assert ws == 0
+        else:
+            assert ws >= B * hq * npart * (128 + 2) * 4
+    assert pkv.workspace_size(16, 32, 8, 128, 4096, 16, pkv.PKV_BF16) >= 16 * 32 * 256 * 130 * 4

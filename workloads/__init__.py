@@ -220,3 +220,53 @@ def queries(w: Workload, step: int = 0) -> np.ndarray:
 def random_rows(seed: int, tag: int, shape, dtype: str) -> np.ndarray:
     """Free-form N(0,1) rows rounded to ``dtype`` (tests that build their own cases)."""
     return round_to_dtype(_normal(_rng(seed, 100 + tag), shape), dtype)
+
+
+# ----------------------------------------------------------------------------
+# Setup scripts
+# ----------------------------------------------------------------------------
+
+CHURN_ID_BASE = 1_000_000
+
+
+def setup_ops(w: Workload, share_prefix: bool = True) -> list:
+    """The allocator operations that build the workload's cache state, as a
+    list of tuples for whichever allocator runs them:
+
+      ("free_order", order)   reorder the free list of the idle pool
+      ("create", seq)         new empty sequence
+      ("append", seq, n)      next n positions of seq (rows: the next n rows
+                              of seq's stream, see kv_rows)
+      ("fork", parent, child) child shares parent's blocks
+      ("free", seq)           drop a sequence
+
+    Churn sequences (workload 3) use ids from CHURN_ID_BASE and write no rows.
+    With share_prefix=False, workload 4's sequences each append the prefix
+    privately instead of forking it (the unshared twin of the same values)."""
+    ops: list = [("free_order", w.free_order)]
+    if w.churn_ops:
+        live: List[int] = []
+        nxt = CHURN_ID_BASE
+        for op, arg in w.churn_ops:
+            if op == "alloc":
+                ops.append(("create", nxt))
+                ops.append(("append", nxt, BLOCK_TOKENS * arg))
+                live.append(nxt)
+                nxt += 1
+            else:
+                ops.append(("free", live.pop(arg)))
+        for k in w.churn_release:
+            ops.append(("free", live[int(k)]))
+    if w.prefix_len and share_prefix:
+        ops.append(("create", 0))
+        ops.append(("append", 0, w.prefix_len))
+        for b in range(1, w.num_seqs):
+            ops.append(("fork", 0, b))
+        for b in range(w.num_seqs):
+            ops.append(("append", b, w.context_lens[b] - w.prefix_len))
+        return ops
+    for b in range(w.num_seqs):
+        ops.append(("create", b))
+    for b in range(w.num_seqs):
+        ops.append(("append", b, w.context_lens[b]))
+    return ops
