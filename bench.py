@@ -7,15 +7,16 @@ One step = one decode step of a model's attention over every rotated layer:
          tables; slots and tables go to the GPU (pinned host buffers, async);
   GPU    per layer: copy-on-write copies (if any), the cache-write kernel
          appends the new token's K/V, then paged_attention_decode (main
-         kernel + partition merge) attends over the whole cache.
+         kernel; the partition merge runs in the same launch) attends over the whole cache.
 Every layer has its own pool, so the K/V read each step is far larger than
 the 256 MB Infinity Cache (reads come from HBM).
 
 value    = KV tokens attended per second = sum over timed steps and layers of
            sum_b L_b, divided by the timed wall time.
 roofline = the decode call's algorithmic bytes (K/V [+ fp8 scales] of every
-           attended token, q, out, block-table entries, lengths) divided by
-           its average duration from HIP events on the launch stream.
+           attended token, q, out, block-table entries, lengths, and the
+           appended K/V row) divided by its average duration from HIP events
+           on the launch stream.
 cpu_baseline = the fp64 oracle (test infrastructure) timed on the host over a
            bounded sample of the same workload.
 
@@ -55,6 +56,13 @@ def parse():
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (counter calibration) and exit")
+    ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                    help="from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of this bench and of "
+                         "--calibrate-copy, write profiles/decode_<workload>_traffic.json and exit")
+    ap.add_argument("--unfused", action="store_true",
+                    help="append with kv_cache_append, then paged_attention_decode (default: one fused call)")
     return ap.parse_args()
 
 
@@ -79,8 +87,51 @@ def load_traffic(workload_name: str):
     return rec.get("bytes_per_launch")
 
 
+def write_traffic(args):
+    """HBM bytes per decode call from counter CSVs, each counter scaled by what
+    it reads for a 1 GiB device copy (reads 1 GiB, writes 1 GiB)."""
+    import csv
+    import statistics
+
+    import workloads as wl
+
+    def rows(path):
+        with open(path) as f:
+            return list(csv.DictReader(f))
+
+    def per_kernel(path, key):
+        vals = [float(r["Counter_Value"]) for r in rows(path) if key in r["Kernel_Name"]]
+        return statistics.median(vals) if vals else 0.0, len(vals)
+
+    fetch_csv, write_csv, cal_fetch_csv, cal_write_csv = args.write_traffic
+    gib_kib = float(2 ** 20)
+    # the device-to-device copy runs as the runtime's copyBuffer kernel
+    cal_f = statistics.median(float(r["Counter_Value"]) for r in rows(cal_fetch_csv)
+                              if "copyBuffer" in r["Kernel_Name"])
+    cal_w = statistics.median(float(r["Counter_Value"]) for r in rows(cal_write_csv)
+                              if "copyBuffer" in r["Kernel_Name"])
+    f_scale, w_scale = gib_kib / cal_f, gib_kib / cal_w
+    rec = {"workload": wl.make_workload(args.config).name, "source_digest": source_digest(),
+           "fetch_scale": f_scale, "write_scale": w_scale, "kernels": {}}
+    total = 0.0
+    for key in ("paged_decode_kernel", "partition_merge_kernel"):
+        fk, n = per_kernel(fetch_csv, key)
+        wk, _ = per_kernel(write_csv, key)
+        b = (fk * f_scale + wk * w_scale) * 1024.0
+        rec["kernels"][key] = {"dispatches": n, "fetch_kib_raw": fk, "write_kib_raw": wk, "hbm_bytes": b}
+        total += b
+    rec["bytes_per_launch"] = total
+    out = os.path.join(ROOT, "profiles", f"decode_{rec['workload']}_traffic.json")
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=2)
+    print(json.dumps(rec))
+
+
 def main():
     args = parse()
+    if args.write_traffic:
+        write_traffic(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(sharding by sequence or KV head needs no exchange; see DESIGN.md)", file=sys.stderr)
@@ -88,6 +139,18 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.calibrate_copy:
+        # HBM-counter calibration: a copy of known size (reads and writes
+        # 1 GiB per launch); FETCH_SIZE / WRITE_SIZE per dispatch of this
+        # kernel divided by 1 GiB gives the counters' scale.
+        src = torch.ones(2 ** 30, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] calibration copies done: 5 x 1 GiB")
+        return
 
     import workloads as wl
     import paged_kv_cache_160_amd as pkv
@@ -160,7 +223,7 @@ def main():
     d_lens = torch.zeros(B, dtype=torch.int32, device=dev)
     d_slots = torch.zeros(B, dtype=torch.int64, device=dev)
     max_possible = max(w.context_lens) + n_steps
-    ws = torch.empty(max(1, pkv.workspace_size(B, hq, hkv, D, max_possible, args.partition_size,
+    ws = torch.zeros(max(1, pkv.workspace_size(B, hq, hkv, D, max_possible, args.partition_size,
                                                pkv.dtype_code(cache.cache_dtype))), dtype=torch.uint8, device=dev)
     ps_used, np_used = pkv.decode_partition_size(B, hq, hkv, D, max(w.context_lens) + 1,
                                                  pkv.dtype_code(cache.cache_dtype))
@@ -206,18 +269,27 @@ def main():
         qbase = qs.data_ptr() + s * layers * q_stride
         for l in range(layers):
             kp, vp, ksp, vsp = pools[l]
-            rc = lib.kv_cache_append(kbase + l * kv_stride, vbase + l * kv_stride, kp, vp, ksp, vsp,
-                                     d_slots.data_ptr(), B, hkv, D, w.num_blocks, src_code, cache_code, sp)
-            if rc:
-                raise pkv.PagedKVError(rc, "kv_cache_append")
+            kl, vl = kbase + l * kv_stride, vbase + l * kv_stride
+            if args.unfused:
+                rc = lib.kv_cache_append(kl, vl, kp, vp, ksp, vsp, d_slots.data_ptr(), B, hkv, D, w.num_blocks,
+                                         src_code, cache_code, sp)
+                if rc:
+                    raise pkv.PagedKVError(rc, "kv_cache_append")
             if timed:
                 ev[(s - args.warmup) * layers + l][0].record(stream)
-            rc = lib.paged_attention_decode(outs.data_ptr() + l * out_stride, qbase + l * q_stride, kp, vp,
-                                            ksp, vsp, d_tables.data_ptr(), d_lens.data_ptr(), B, hq, hkv, D,
-                                            w.num_blocks, mb, max_len, scale, q_code, cache_code,
-                                            args.partition_size, ws_ptr, ws_bytes, sp)
+            if args.unfused:
+                rc = lib.paged_attention_decode(outs.data_ptr() + l * out_stride, qbase + l * q_stride, kp, vp,
+                                                ksp, vsp, d_tables.data_ptr(), d_lens.data_ptr(), B, hq, hkv, D,
+                                                w.num_blocks, mb, max_len, scale, q_code, cache_code,
+                                                args.partition_size, ws_ptr, ws_bytes, sp)
+            else:
+                rc = lib.paged_attention_decode_append(outs.data_ptr() + l * out_stride, qbase + l * q_stride,
+                                                       kl, vl, kp, vp, ksp, vsp, d_slots.data_ptr(),
+                                                       d_tables.data_ptr(), d_lens.data_ptr(), B, hq, hkv, D,
+                                                       w.num_blocks, mb, max_len, scale, q_code, src_code,
+                                                       cache_code, args.partition_size, ws_ptr, ws_bytes, sp)
             if rc:
-                raise pkv.PagedKVError(rc, "paged_attention_decode")
+                raise pkv.PagedKVError(rc, "decode")
             if timed:
                 ev[(s - args.warmup) * layers + l][1].record(stream)
         if timed:
@@ -227,7 +299,10 @@ def main():
                 kv_bytes += sum_l * hkv * 2 * 4
             qo_bytes = 2 * B * hq * D * ES[w.q_dtype]
             table_bytes = sum(-(-L // 16) for L in lens) * 4 + B * 4
-            bytes_timed += (kv_bytes + qo_bytes + table_bytes) * layers
+            # the fused call also reads the new rows and slots (its writes are
+            # inside the K/V bytes already counted)
+            new_bytes = 0 if args.unfused else B * hkv * D * 2 * ES[w.src_dtype] + B * 8
+            bytes_timed += (kv_bytes + qo_bytes + table_bytes + new_bytes) * layers
 
     for s in range(args.warmup):
         step(s, False)
@@ -277,7 +352,8 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-            "kernel": "paged_attention_decode (main kernel + partition merge)",
+            "kernel": ("paged_attention_decode" if args.unfused else "paged_attention_decode_append")
+                      + " call (paged_decode_kernel + partition_merge_kernel when split)",
             "bytes_per_launch": bytes_per_call,
         },
         "cpu_baseline": cpu,

@@ -41,6 +41,7 @@ extern "C" {
 
 #define PKV_BLOCK_SIZE 16   /* tokens per physical block ("KV Cache 和 vLLM" §3.1) */
 #define PKV_ABI_VERSION 1
+#define PKV_MAX_PARTITION_TOKENS 32768   /* largest decode partition (tokens) */
 
 typedef enum {
   PKV_F32 = 0,
@@ -126,7 +127,8 @@ int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, i
 /*
  * paged_attention_workspace_size - bytes of device workspace
  * paged_attention_decode needs for these sizes (0 when every sequence fits
- * in one partition).  partition_size: 0 = automatic, else a multiple of 16.
+ * in one partition).  partition_size: 0 = automatic, else a multiple of 16
+ * no larger than PKV_MAX_PARTITION_TOKENS.
  * Returns 0 as well for invalid sizes (the decode call then reports them).
  */
 size_t paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
@@ -150,12 +152,18 @@ size_t paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_
  *   max_context_len  host bound with L_b <= max_context_len <=
  *                 16 * max_blocks_per_seq; it sizes the launch
  *   scale         the caller passes 1/sqrt(head_dim)
- *   partition_size 0 = automatic; else tokens per partition, a multiple of 16.
- *                 Sequences longer than one partition are split; partitions
- *                 are merged exactly by a log-sum-exp reduction.
+ *   partition_size 0 = automatic; else tokens per partition, a multiple of 16
+ *                 and at most PKV_MAX_PARTITION_TOKENS.
+ *                 Sequences longer than one partition are split; the
+ *                 partitions are merged exactly (log-sum-exp) in the same
+ *                 launch by whichever workgroup of a (sequence, KV head)
+ *                 finishes last.
  *   workspace     device scratch of at least paged_attention_workspace_size()
- *                 bytes (may be NULL when that is 0); contents on entry are
- *                 ignored
+ *                 bytes (may be NULL when that is 0).  Its first part holds
+ *                 arrival counters: the whole workspace must be zero before
+ *                 its first use (for example allocated with torch.zeros), and
+ *                 every call leaves the counters zero again.  Calls that may
+ *                 run concurrently must not share a workspace.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).  L_b == 0 gives
  * an all-zero output row.  Entries of the used part of a block-table row must
  * lie in [0, num_blocks); a block outside that range contributes no tokens.
@@ -175,6 +183,36 @@ int paged_attention_decode(void* out, const void* q,
                            float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
                            int partition_size, void* workspace, size_t workspace_bytes,
                            void* stream);
+
+/*
+ * paged_attention_decode_append - one decode step with its cache write fused
+ * in: the same result, pool bytes and scales as kv_cache_append(k_new, v_new,
+ * ..., slot_mapping, num_tokens = num_seqs) followed by
+ * paged_attention_decode(...), in one launch (plus the partition merge when a
+ * sequence spans several partitions).  Pages: the new token's K and V are
+ * appended to the cache and the new query then attends over the whole cache,
+ * itself included ("KV Cache 和 vLLM" §1.2-1.3; "企业官网建设流程全解析" §3.2).
+ *
+ *   k_new, v_new  device [num_seqs][num_kv_heads][head_dim] of src_dtype: the
+ *                 step's K and V row of each sequence
+ *   slot_mapping  device int64 [num_seqs]: slot of sequence b's newest
+ *                 position context_lens[b] - 1 (the slot the allocator handed
+ *                 out for it); a negative entry writes nothing for b
+ *   all other arguments as for paged_attention_decode; src_dtype as for
+ *   kv_cache_append (equal to cache_dtype, or f32/f16/bf16 for an fp8 cache).
+ * The row of sequence b is written by the workgroup whose partition holds
+ * position context_lens[b] - 1, before any K/V is read, so sequences with
+ * context_lens[b] == 0 write nothing.
+ */
+int paged_attention_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                                  void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                  const int64_t* slot_mapping,
+                                  const int32_t* block_tables, const int32_t* context_lens,
+                                  int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                  int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                  float scale, pkv_dtype q_dtype, pkv_dtype src_dtype,
+                                  pkv_dtype cache_dtype, int partition_size, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Host block allocator.  Opaque handle, not thread-safe, no device memory.  */

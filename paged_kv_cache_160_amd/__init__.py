@@ -19,7 +19,8 @@ from . import _lib
 
 __all__ = [
     "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3", "BLOCK_SIZE", "PagedKVError",
-    "kv_cache_append", "copy_blocks", "paged_attention_decode", "workspace_size",
+    "kv_cache_append", "copy_blocks", "paged_attention_decode", "paged_attention_decode_append",
+    "workspace_size",
     "decode_partition_size", "BlockAllocator", "dtype_code", "abi_version",
 ]
 
@@ -145,13 +146,50 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
     cdt = dtype_code(k_pool.dtype)
     need = workspace_size(B, hq, hkv, d, max_context_len, partition_size, cdt)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        # zeroed once: the library keeps its counters zero between calls
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.lib().paged_attention_decode(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
         _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb, int(block_tables.shape[1]),
         int(max_context_len), float(scale), dtype_code(q.dtype), cdt, int(partition_size),
         _ptr(workspace), ws_bytes, _stream(stream)), "paged_attention_decode")
+    return out
+
+
+def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                                  v_new: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                  slot_mapping: torch.Tensor, block_tables: torch.Tensor,
+                                  context_lens: torch.Tensor, max_context_len: int,
+                                  scale: Optional[float] = None, k_scale: Optional[torch.Tensor] = None,
+                                  v_scale: Optional[torch.Tensor] = None, partition_size: int = 0,
+                                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """A decode step with the cache write fused in: row b of ``k_new, v_new
+    [B, Hkv, D]`` goes to ``slot_mapping[b]`` (the slot of position
+    ``context_lens[b] - 1``), then ``out`` = attention over the whole cache."""
+    nb, hkv, d = _pool_geometry(k_pool)
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must be [B, Hq, D] of one dtype")
+    B, hq = int(q.shape[0]), int(q.shape[1])
+    if k_new.shape != (B, hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [B, Hkv, D]")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != B:
+        raise ValueError("slot_mapping must be int64 [B]")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    cdt = dtype_code(k_pool.dtype)
+    need = workspace_size(B, hq, hkv, d, max_context_len, partition_size, cdt)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.lib().paged_attention_decode_append(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+        _ptr(v_scale), _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb,
+        int(block_tables.shape[1]), int(max_context_len), float(scale), dtype_code(q.dtype),
+        dtype_code(k_new.dtype), cdt, int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)),
+        "paged_attention_decode_append")
     return out
 
 

@@ -11,7 +11,7 @@ from typing import List, Optional, Sequence, Union
 import torch
 
 from . import (BLOCK_SIZE, BlockAllocator, copy_blocks, kv_cache_append, paged_attention_decode,
-               workspace_size, dtype_code)
+               paged_attention_decode_append, workspace_size, dtype_code)
 
 Rows = Union[torch.Tensor, Sequence[torch.Tensor]]
 
@@ -119,7 +119,33 @@ class PagedKVCache:
         need = workspace_size(q.shape[0], q.shape[1], self.num_kv_heads, self.head_dim, max_len,
                               partition_size, dtype_code(self.cache_dtype))
         if need and (self._ws is None or self._ws.numel() < need):
-            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+            self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
         return paged_attention_decode(out, q, self.k[layer], self.v[layer], bt, lens, max_len,
                                       k_scale=self.k_scale[layer], v_scale=self.v_scale[layer],
                                       partition_size=partition_size, workspace=self._ws)
+
+    def decode_step(self, q: Rows, seq_ids: Sequence[int], k_rows: Rows, v_rows: Rows,
+                    partition_size: int = 0, out: Optional[List[torch.Tensor]] = None) -> List[torch.Tensor]:
+        """One decode step over every layer: the allocator reserves one slot
+        per sequence (copy-on-write pairs applied first), then per layer one
+        fused launch writes the step's K/V rows and attends over the cache.
+        ``q``, ``k_rows``, ``v_rows``: one tensor for every layer or a list."""
+        seq_ids = list(seq_ids)
+        slots, pairs = self.alloc.batch_append_one(seq_ids)
+        self._apply_cow(pairs)
+        slot_t = torch.tensor(slots, dtype=torch.int64).to(self.device)
+        bt, lens, max_len = self.block_tables(seq_ids)
+        outs = []
+        for layer in range(self.num_layers):
+            ql = self._layer_rows(q, layer)
+            o = out[layer] if out is not None else torch.empty_like(ql)
+            need = workspace_size(ql.shape[0], ql.shape[1], self.num_kv_heads, self.head_dim, max_len,
+                                  partition_size, dtype_code(self.cache_dtype))
+            if need and (self._ws is None or self._ws.numel() < need):
+                self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
+            paged_attention_decode_append(o, ql, self._layer_rows(k_rows, layer), self._layer_rows(v_rows, layer),
+                                          self.k[layer], self.v[layer], slot_t, bt, lens, max_len,
+                                          k_scale=self.k_scale[layer], v_scale=self.v_scale[layer],
+                                          partition_size=partition_size, workspace=self._ws)
+            outs.append(o)
+        return outs

@@ -28,7 +28,7 @@ int resolve_partitions(int num_seqs, int num_kv_heads, int max_context_len, int 
                        int* ps_out, int* np_out) {
   int ps = partition_size;
   if (ps == 0) ps = pkv::choose_partition_size(num_seqs, num_kv_heads, max_context_len);
-  if (ps <= 0 || ps % kBlock != 0) return PKV_ERR_INVALID_ARG;
+  if (ps <= 0 || ps % kBlock != 0 || ps > PKV_MAX_PARTITION_TOKENS) return PKV_ERR_INVALID_ARG;
   int64_t np = (static_cast<int64_t>(max_context_len) + ps - 1) / ps;
   if (np < 1) np = 1;
   if (np > (1 << 20)) return PKV_ERR_UNSUPPORTED;
@@ -37,14 +37,23 @@ int resolve_partitions(int num_seqs, int num_kv_heads, int max_context_len, int 
   return PKV_OK;
 }
 
-size_t workspace_bytes_for(int num_seqs, int num_q_heads, int head_dim, int np) {
-  if (np <= 1) return 0;
+// Workspace layout: per (sequence, KV head) arrival counters (int32), then
+// per (sequence, query head, partition) (m, l) pairs, then the unnormalised
+// partition outputs; each part starts on a 256-byte boundary.
+struct WorkspaceLayout {
+  size_t counters = 0, ml = 0, acc = 0, total = 0;
+};
+
+WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int np) {
+  WorkspaceLayout w;
+  if (np <= 1) return w;
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * np;
-  // (m, l) pairs, then the unnormalised outputs; the second part starts on a
-  // 256-byte boundary.
-  size_t ml = rows * 2 * sizeof(float);
-  ml = (ml + 255) & ~static_cast<size_t>(255);
-  return ml + rows * head_dim * sizeof(float);
+  w.counters = 0;
+  w.ml = up(static_cast<size_t>(num_seqs) * num_kv_heads * sizeof(int32_t));
+  w.acc = w.ml + up(rows * 2 * sizeof(float));
+  w.total = w.acc + rows * head_dim * sizeof(float);
+  return w;
 }
 
 bool decode_sizes_ok(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
@@ -128,17 +137,20 @@ size_t paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_
   int ps, np;
   if (resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, &ps, &np) != PKV_OK)
     return 0;
-  return workspace_bytes_for(num_seqs, num_q_heads, head_dim, np);
+  return workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, np).total;
 }
 
-int paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
-                           const float* k_scale, const float* v_scale, const int32_t* block_tables,
-                           const int32_t* context_lens, int num_seqs, int num_q_heads,
-                           int num_kv_heads, int head_dim, int num_blocks, int max_blocks_per_seq,
-                           int max_context_len, float scale, pkv_dtype q_dtype,
-                           pkv_dtype cache_dtype, int partition_size, void* workspace,
-                           size_t workspace_bytes, void* stream) {
-  if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
+}  // extern "C"
+
+namespace {
+
+int decode_impl(void* out, const void* q, const void* k_new, const void* v_new, const void* k_pool,
+                const void* v_pool, const float* k_scale, const float* v_scale, const int64_t* slot_mapping,
+                const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
+                int num_kv_heads, int head_dim, int num_blocks, int max_blocks_per_seq, int max_context_len,
+                float scale, pkv_dtype q_dtype, pkv_dtype src_dtype, pkv_dtype cache_dtype, int partition_size,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype) || !valid_dtype(src_dtype)) return PKV_ERR_INVALID_ARG;
   if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len))
     return PKV_ERR_INVALID_ARG;
   if (num_blocks <= 0 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
@@ -146,8 +158,13 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
     return PKV_ERR_INVALID_ARG;
   if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
   if (!decode_pair_ok(q_dtype, cache_dtype)) return PKV_ERR_UNSUPPORTED;
+  if (slot_mapping) {
+    if (src_dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
+    if (cache_dtype != PKV_FP8_E4M3 && src_dtype != cache_dtype) return PKV_ERR_UNSUPPORTED;
+  }
   if (num_q_heads / num_kv_heads > 16) return PKV_ERR_UNSUPPORTED;
-  if (partition_size < 0 || partition_size % kBlock != 0) return PKV_ERR_INVALID_ARG;
+  if (partition_size < 0 || partition_size % kBlock != 0 || partition_size > PKV_MAX_PARTITION_TOKENS)
+    return PKV_ERR_INVALID_ARG;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_INVALID_ARG;
   if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
@@ -155,12 +172,13 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
     return PKV_ERR_INVALID_ARG;
   if (cache_dtype == PKV_FP8_E4M3 && (!aligned16(k_scale) || !aligned16(v_scale)))
     return PKV_ERR_INVALID_ARG;
+  if (slot_mapping && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_INVALID_ARG;
 
   int ps, np;
   int rc = resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, &ps, &np);
   if (rc != PKV_OK) return rc;
-  const size_t need = workspace_bytes_for(num_seqs, num_q_heads, head_dim, np);
-  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+  const WorkspaceLayout ws = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, np);
+  if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || !aligned16(workspace)))
     return PKV_ERR_WORKSPACE;
 
   pkv::DecodeArgs a{};
@@ -184,13 +202,49 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
   a.cache_dtype = cache_dtype;
   a.partition_size = ps;
   a.num_partitions = np;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slot_mapping = slot_mapping;
+  a.src_dtype = src_dtype;
   if (np > 1) {
-    const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * np;
-    size_t ml = (rows * 2 * sizeof(float) + 255) & ~static_cast<size_t>(255);
-    a.part_ml = static_cast<float*>(workspace);
-    a.part_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ml);
+    char* base = static_cast<char*>(workspace);
+    a.counters = reinterpret_cast<int*>(base + ws.counters);
+    a.part_ml = reinterpret_cast<float*>(base + ws.ml);
+    a.part_acc = reinterpret_cast<float*>(base + ws.acc);
   }
   return pkv::launch_decode(a, static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
+                           const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                           const int32_t* context_lens, int num_seqs, int num_q_heads,
+                           int num_kv_heads, int head_dim, int num_blocks, int max_blocks_per_seq,
+                           int max_context_len, float scale, pkv_dtype q_dtype,
+                           pkv_dtype cache_dtype, int partition_size, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, nullptr, nullptr, k_pool, v_pool, k_scale, v_scale, nullptr, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, q_dtype, q_dtype, cache_dtype,
+                     partition_size, workspace, workspace_bytes, stream);
+}
+
+int paged_attention_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                                  void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                  const int64_t* slot_mapping, const int32_t* block_tables,
+                                  const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                  int num_kv_heads, int head_dim, int num_blocks, int max_blocks_per_seq,
+                                  int max_context_len, float scale, pkv_dtype q_dtype, pkv_dtype src_dtype,
+                                  pkv_dtype cache_dtype, int partition_size, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (!slot_mapping) return PKV_ERR_INVALID_ARG;
+  return decode_impl(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, q_dtype, src_dtype, cache_dtype,
+                     partition_size, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

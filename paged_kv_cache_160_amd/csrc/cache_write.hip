@@ -50,7 +50,6 @@ __global__ void __launch_bounds__(256) append_fp8_kernel(
     float* __restrict__ k_scale, float* __restrict__ v_scale,
     const int64_t* __restrict__ slot_mapping, int num_tokens, int num_kv_heads,
     int64_t num_slots) {
-  constexpr int kPer = D / kWave;   // 1 or 2 elements per lane
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t row = static_cast<int64_t>(blockIdx.x) * (blockDim.x / kWave) + (threadIdx.x / kWave);
   const int64_t rows = static_cast<int64_t>(num_tokens) * num_kv_heads;
@@ -64,34 +63,10 @@ __global__ void __launch_bounds__(256) append_fp8_kernel(
   const int64_t slot = slot_mapping[tok];
   if (slot < 0 || slot >= num_slots) return;
 
-  float x[kPer];
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    x[i] = load_as_f32<Src>(src, row * D + lane * kPer + i);
-    amax = fmaxf(amax, fabsf(x[i]));
-  }
-  amax = wave_max(amax);
-  float s = __fdiv_rn(amax, 448.0f);
-  if (amax == 0.0f) s = 1.0f;
-
   const int64_t blk = slot / kBlockTokens;
   const int64_t off = slot % kBlockTokens;
   const int64_t dst_row = (blk * num_kv_heads + head) * kBlockTokens + off;
-  uint32_t packed = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    float y = __fdiv_rn(x[i], s);
-    y = fminf(fmaxf(y, -448.0f), 448.0f);
-    packed |= e4m3_encode_rne(y) << (8 * i);
-  }
-  uint8_t* dst = pool + dst_row * D + lane * kPer;
-  if constexpr (kPer == 2) {
-    *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(packed);
-  } else {
-    *dst = static_cast<uint8_t>(packed);
-  }
-  if (lane == 0) scales[dst_row] = s;
+  write_row_fp8<Src, D>(src, row, pool, scales, dst_row, lane);
 }
 
 // Copy-on-write: one workgroup per (pair, head, tensor); 16-byte chunks.

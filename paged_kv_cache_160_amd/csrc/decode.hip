@@ -13,7 +13,7 @@
 //  * Workgroup = 4 waves for one (sequence, KV head, partition).  A partition
 //    is a run of logical positions; wave w takes the partition's blocks w,
 //    w+4, w+8, ...  Each wave streams its blocks straight from HBM into
-//    registers with 16-byte loads, two blocks in flight, and keeps its own
+//    registers with 16-byte loads, several blocks in flight, and keeps its own
 //    online-softmax state; the 4 states merge through LDS at the end.
 //  * The whole GQA group is served from one read of each K/V tile: the
 //    group's query heads are the 16 columns of an MFMA tile (columns >= G are
@@ -30,8 +30,10 @@
 //    element.
 //  * Probabilities enter the P*V MFMA as a hi + lo pair of 16-bit values, so
 //    P carries ~16 significant bits while the MFMA still accumulates in fp32.
-//  * Long sequences split into partitions whose (max, sum, unnormalised
-//    output) are merged by a second kernel with the log-sum-exp formula.
+//  * Long sequences split into partitions; each partition's (max, sum,
+//    unnormalised output) goes to the workspace, and the workgroup that
+//    finishes last for a (sequence, KV head) merges them with the
+//    log-sum-exp formula in the same launch.
 
 #include <math.h>
 
@@ -42,9 +44,13 @@
 
 namespace pkv {
 
-constexpr int kWaves = 4;
+#ifndef PKV_DECODE_WAVES
+#define PKV_DECODE_WAVES 4     // waves per workgroup
+#endif
+constexpr int kWaves = PKV_DECODE_WAVES;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxGroup = 16;
+constexpr int kMaxPartitionBlocks = PKV_MAX_PARTITION_TOKENS / kBlockTokens;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---- raw register loads -------------------------------------------------------
@@ -54,25 +60,51 @@ struct Words {
   uint32_t w[N];
 };
 
-template <int N>
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+template <typename T, bool NT>
+__device__ __forceinline__ T load_vec(const uint8_t* p) {
+  const T* src = reinterpret_cast<const T*>(p);
+  if constexpr (NT) return __builtin_nontemporal_load(src);
+  else return *src;
+}
+
+template <int N, bool NT>
 __device__ __forceinline__ void load_words(Words<N>& dst, const uint8_t* p) {
   if constexpr (N % 4 == 0) {
 #pragma unroll
     for (int i = 0; i < N / 4; ++i) {
-      uint4 v = reinterpret_cast<const uint4*>(p)[i];
-      dst.w[4 * i + 0] = v.x;
-      dst.w[4 * i + 1] = v.y;
-      dst.w[4 * i + 2] = v.z;
-      dst.w[4 * i + 3] = v.w;
+      u32x4_t v = load_vec<u32x4_t, NT>(p + 16 * i);
+      dst.w[4 * i + 0] = v[0];
+      dst.w[4 * i + 1] = v[1];
+      dst.w[4 * i + 2] = v[2];
+      dst.w[4 * i + 3] = v[3];
     }
   } else if constexpr (N == 2) {
-    uint2 v = *reinterpret_cast<const uint2*>(p);
-    dst.w[0] = v.x;
-    dst.w[1] = v.y;
+    u32x2_t v = load_vec<u32x2_t, NT>(p);
+    dst.w[0] = v[0];
+    dst.w[1] = v[1];
   } else {
     static_assert(N == 1, "unsupported load width");
-    dst.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    dst.w[0] = load_vec<uint32_t, NT>(p);
   }
+}
+
+// ---- cross-row reductions (a "row" is 16 lanes) ------------------------------------
+// Max / sum over the 4 lanes c, c+16, c+32, c+48 of each column c, with the
+// gfx950 row-swap permutes (VALU, no LDS round trip).
+__device__ __forceinline__ float col_max4(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float col_sum4(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // ---- per-flavour geometry -------------------------------------------------------
@@ -233,7 +265,17 @@ __device__ __forceinline__ void pv_tile(const float (&p)[4], const Words<Geo<QT,
 
 // ---- the main kernel ------------------------------------------------------------
 
-template <typename QT, typename CT, int D>
+#ifndef PKV_DECODE_PIPE
+#define PKV_DECODE_PIPE 3      // blocks in flight per wave
+#endif
+#ifndef PKV_DECODE_NT
+#define PKV_DECODE_NT 0        // non-temporal K/V loads (measured slower: off)
+#endif
+#ifndef PKV_DECODE_MERGE
+#define PKV_DECODE_MERGE 0     // 0: merge kernel; 1: last workgroup merges (release fences)
+#endif
+
+template <typename QT, typename CT, int D, int PIPE>
 __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a) {
   using G = Geo<QT, CT, D>;
   constexpr bool kFp8 = std::is_same<CT, FP8>::value;
@@ -242,6 +284,8 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
   __shared__ float sm_m[kWaves][kMaxGroup];
   __shared__ float sm_l[kWaves][kMaxGroup];
   __shared__ float sm_o[kWaves][kMaxGroup][D];
+  __shared__ int sm_last;
+  __shared__ int sm_ids[kMaxPartitionBlocks];
 
   const int P = a.num_partitions;
   const int part = blockIdx.x % P;
@@ -256,20 +300,20 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
 
   int L = a.context_lens[b];
   L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * kBlockTokens)));
-  const int tok0 = part * a.partition_size;
+  const int PS = a.partition_size;
+  const int np_b = (L + PS - 1) / PS;         // non-empty partitions of this sequence
+  const int tok0 = part * PS;
   const int64_t out_row0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(g) * group;
 
-  if (tok0 >= L) {
-    // Nothing to attend to in this partition.  With a single partition the
-    // output row is defined as zero; with several, the reduce kernel only
-    // reads partitions below ceil(L / partition_size).
-    if (P == 1) {
-      for (int i = tid; i < group * D; i += kThreads)
-        store_from_f32<QT>(a.out, out_row0 * D + i, 0.0f);
+  if (L == 0) {
+    // an empty context gives a zero output row (written once)
+    if (part == 0) {
+      for (int i = tid; i < group * D; i += kThreads) store_from_f32<QT>(a.out, out_row0 * D + i, 0.0f);
     }
     return;
   }
-  const int tok1 = min(L, tok0 + a.partition_size);
+  if (part >= np_b) return;
+  const int tok1 = min(L, tok0 + PS);
   const int blk0 = tok0 / kBlockTokens;
   const int nblk = (tok1 - tok0 + kBlockTokens - 1) / kBlockTokens;
   const int32_t* table = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq + blk0;
@@ -280,7 +324,7 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
     const bool valid = c < group;
     const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
                         ((out_row0 + (valid ? c : 0)) * D + j * (D / 4)) * G::qes;
-    load_words(qop, qp);
+    load_words<G::qWords, false>(qop, qp);
     if (!valid) {
 #pragma unroll
       for (int i = 0; i < G::qWords; ++i) qop.w[i] = 0u;
@@ -293,18 +337,49 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
   const int64_t k_lane = static_cast<int64_t>(c * D + j * (D / 4)) * G::ces;
   const int64_t v_lane = static_cast<int64_t>((4 * j) * D + G::DC * c) * G::ces;
 
+  // Fused cache write: the workgroup whose partition holds the sequence's
+  // last position writes this step's K and V rows for its KV head (wave 0:
+  // K, wave 1: V) before anything is read; the barrier below makes the rows
+  // visible to every wave of the workgroup.
+  if (a.slot_mapping != nullptr && part == (L - 1) / PS && wave < 2) {
+    const int64_t slot = a.slot_mapping[b];
+    if (slot >= 0 && slot < static_cast<int64_t>(a.num_blocks) * kBlockTokens) {
+      const int64_t dst_row = ((slot / kBlockTokens) * a.num_kv_heads + g) * kBlockTokens + slot % kBlockTokens;
+      const int64_t src_row = static_cast<int64_t>(b) * a.num_kv_heads + g;
+      const void* src = wave == 0 ? a.k_new : a.v_new;
+      void* pool = const_cast<void*>(wave == 0 ? a.k_pool : a.v_pool);
+      if constexpr (kFp8) {
+        float* scales = const_cast<float*>(wave == 0 ? a.k_scale : a.v_scale);
+        auto* p8 = static_cast<uint8_t*>(pool);
+        if (a.src_dtype == PKV_F32) write_row_fp8<F32, D>(src, src_row, p8, scales, dst_row, lane);
+        else if (a.src_dtype == PKV_F16) write_row_fp8<F16, D>(src, src_row, p8, scales, dst_row, lane);
+        else write_row_fp8<BF16, D>(src, src_row, p8, scales, dst_row, lane);
+      } else {
+        write_row_copy(src, src_row, pool, dst_row, D * G::ces, lane);
+      }
+    }
+  }
+
+  // The partition's physical block ids, staged in LDS once: a per-block
+  // table read from global memory in front of the K/V loads would make the
+  // wave wait for every load already in flight (vmcnt is in order), while
+  // LDS reads are counted separately.
+  for (int i = tid; i < nblk; i += kThreads) sm_ids[i] = table[i];
+  __syncthreads();
+
   // Load one block's K/V (and scales) for this lane.  Blocks whose physical
   // id lies outside the pool are read from block 0 and fully masked.
   auto load_block = [&](BlockRegs<QT, CT, D>& r, int i, bool& ok) {
-    int phys = __builtin_amdgcn_readfirstlane(table[i]);
+    int phys = __builtin_amdgcn_readfirstlane(sm_ids[i]);
     ok = phys >= 0 && phys < a.num_blocks;
     if (!ok) phys = 0;
     const int64_t tile = static_cast<int64_t>(phys) * a.num_kv_heads + g;
     const uint8_t* kt = kbase + tile * G::tileBytes;
     const uint8_t* vt = vbase + tile * G::tileBytes;
-    load_words(r.k, kt + k_lane);
+    load_words<G::kWords, PKV_DECODE_NT>(r.k, kt + k_lane);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) load_words(r.v[e], vt + v_lane + static_cast<int64_t>(e) * D * G::ces);
+    for (int e = 0; e < 4; ++e)
+      load_words<G::vWords, PKV_DECODE_NT>(r.v[e], vt + v_lane + static_cast<int64_t>(e) * D * G::ces);
     if constexpr (kFp8) {
       r.ks = *reinterpret_cast<const float4*>(a.k_scale + tile * kBlockTokens + 4 * j);
       r.vs = *reinterpret_cast<const float4*>(a.v_scale + tile * kBlockTokens + 4 * j);
@@ -346,26 +421,31 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
         }
       }
     }
-    float bm = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16, kWave));
-    bm = fmaxf(bm, __shfl_xor(bm, 32, kWave));
+    const float bm = col_max4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
     const float m_new = fmaxf(m, bm);
-    const float alpha = (m_new == kNegInf) ? 1.0f : exp2f(m - m_new);
+    const float alpha = (m_new == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
     float p[4];
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      float e = valid[t] ? exp2f(sc[t] - m_new) : 0.0f;
+      float e = valid[t] ? __builtin_amdgcn_exp2f(sc[t] - m_new) : 0.0f;
       psum += e;
       p[t] = e * vsc[t];
     }
     l = l * alpha + psum;
     m = m_new;
     // rescale O: lane (c, j) reg r holds head row 4j+r; alpha of head h sits
-    // in lane h (all lanes of column h agree).
+    // in lane h (all lanes of column h agree).  With at most 4 heads per
+    // group only rows 0..3 (lanes j == 0) matter, and the four factors are
+    // wave-uniform: read them into scalar registers.
     float ar[4];
+    if (group <= 4) {
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) ar[rr] = __shfl(alpha, 4 * j + rr, kWave);
+      for (int rr = 0; rr < 4; ++rr) ar[rr] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(alpha), rr));
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) ar[rr] = __shfl(alpha, 4 * j + rr, kWave);
+    }
 #pragma unroll
     for (int nt = 0; nt < G::DC; ++nt) {
       o[nt][0] *= ar[0];
@@ -376,24 +456,29 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
     pv_tile<QT, CT, D>(p, r.v, o);
   };
 
-  // Two blocks in flight per wave.
-  BlockRegs<QT, CT, D> r0, r1;
-  bool ok0 = true, ok1 = true;
-  int i = wave;
-  if (i < nblk) load_block(r0, i, ok0);
-  if (i + kWaves < nblk) load_block(r1, i + kWaves, ok1);
-  for (; i < nblk; i += 2 * kWaves) {
-    compute_block(r0, i, ok0);
-    if (i + 2 * kWaves < nblk) load_block(r0, i + 2 * kWaves, ok0);
-    if (i + kWaves < nblk) {
-      compute_block(r1, i + kWaves, ok1);
-      if (i + 3 * kWaves < nblk) load_block(r1, i + 3 * kWaves, ok1);
+  // PIPE blocks in flight per wave: block i is computed while blocks
+  // i+4, ..., i+4*(PIPE-1) are being loaded.  Every stage issues its load
+  // unconditionally (past the end it re-reads the wave's last block, an L2
+  // hit) so that all paths through the loop carry the same loads in the same
+  // order and each wait covers only the block about to be used.
+  if (wave < nblk) {
+    const int last = wave + kWaves * ((nblk - 1 - wave) / kWaves);
+    BlockRegs<QT, CT, D> r[PIPE];
+    bool ok[PIPE];
+#pragma unroll
+    for (int st = 0; st < PIPE; ++st) load_block(r[st], min(wave + st * kWaves, last), ok[st]);
+    for (int i = wave; i < nblk; i += PIPE * kWaves) {
+#pragma unroll
+      for (int st = 0; st < PIPE; ++st) {
+        const int blk = i + st * kWaves;
+        if (blk < nblk) compute_block(r[st], blk, ok[st]);
+        load_block(r[st], min(blk + PIPE * kWaves, last), ok[st]);
+      }
     }
   }
 
   // ---- merge the waves' states ----
-  l += __shfl_xor(l, 16, kWave);
-  l += __shfl_xor(l, 32, kWave);
+  l = col_sum4(l);
   if (j == 0 && c < group) {
     sm_m[wave][c] = m;
     sm_l[wave][c] = l;
@@ -408,6 +493,7 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
   }
   __syncthreads();
 
+  const bool single = np_b == 1;
   for (int idx = tid; idx < group * D; idx += kThreads) {
     const int h = idx / D;
     const int d = idx % D;
@@ -420,14 +506,14 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
       for (int w = 0; w < kWaves; ++w) {
         const float mw = sm_m[w][h];
         if (mw != kNegInf) {
-          const float f = exp2f(mw - M);
+          const float f = __builtin_amdgcn_exp2f(mw - M);
           acc += f * sm_o[w][h][d];
           lsum += f * sm_l[w][h];
         }
       }
     }
     const int64_t row = out_row0 + h;
-    if (P == 1) {
+    if (single) {
       store_from_f32<QT>(a.out, row * D + d, lsum > 0.f ? acc / lsum : 0.f);
     } else {
       const int64_t prow = row * P + part;
@@ -438,12 +524,48 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
       }
     }
   }
+  if (single || PKV_DECODE_MERGE == 0) return;
+
+  // ---- log-sum-exp merge of the sequence's partitions, by the workgroup of
+  // this (sequence, KV head) that finishes last.  Each workgroup releases its
+  // partials device-wide (every XCD's L2) before counting in; the last
+  // arriver acquires before reading them and resets the count, so the
+  // counters stay zero between calls.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  __syncthreads();
+  int* counter = a.counters + static_cast<int64_t>(b) * a.num_kv_heads + g;
+  if (tid == 0) sm_last = (atomicAdd(counter, 1) == np_b - 1);
+  __syncthreads();
+  if (!sm_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  for (int idx = tid; idx < group * D; idx += kThreads) {
+    const int h = idx / D;
+    const int d = idx % D;
+    const int64_t row = out_row0 + h;
+    const float* ml = a.part_ml + row * P * 2;
+    const float* acc = a.part_acc + row * P * D;
+    float M = kNegInf;
+    for (int pp = 0; pp < np_b; ++pp) M = fmaxf(M, ml[2 * pp]);
+    float num = 0.f, den = 0.f;
+    if (M != kNegInf) {
+      for (int pp = 0; pp < np_b; ++pp) {
+        const float mp = ml[2 * pp];
+        if (mp == kNegInf) continue;
+        const float f = __builtin_amdgcn_exp2f(mp - M);
+        num += f * acc[static_cast<int64_t>(pp) * D + d];
+        den += f * ml[2 * pp + 1];
+      }
+    }
+    store_from_f32<QT>(a.out, row * D + d, den > 0.f ? num / den : 0.f);
+  }
+  if (tid == 0) atomicExch(counter, 0);
 }
 
-// ---- log-sum-exp merge of partitions ------------------------------------------------
-// One workgroup of D threads per (sequence, query head).
+// ---- log-sum-exp merge of partitions (second launch) --------------------------------
+// One workgroup of D threads per (sequence, query head); rows whose sequence
+// fit in one partition (or was empty) were written by the main kernel.
 template <typename QT, int D>
-__global__ void __launch_bounds__(D) partition_reduce_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(D) partition_merge_kernel(DecodeArgs a) {
   const int row = blockIdx.x;                 // b * Hq + h
   const int b = row / a.num_q_heads;
   const int d = threadIdx.x;
@@ -451,6 +573,7 @@ __global__ void __launch_bounds__(D) partition_reduce_kernel(DecodeArgs a) {
   int L = a.context_lens[b];
   L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * kBlockTokens)));
   const int np = (L + a.partition_size - 1) / a.partition_size;
+  if (np <= 1) return;
   const float* ml = a.part_ml + static_cast<int64_t>(row) * P * 2;
   const float* acc = a.part_acc + static_cast<int64_t>(row) * P * D;
   float M = -INFINITY;
@@ -460,7 +583,7 @@ __global__ void __launch_bounds__(D) partition_reduce_kernel(DecodeArgs a) {
     for (int p = 0; p < np; ++p) {
       const float mp = ml[2 * p];
       if (mp == -INFINITY) continue;
-      const float f = exp2f(mp - M);
+      const float f = __builtin_amdgcn_exp2f(mp - M);
       num += f * acc[static_cast<int64_t>(p) * D + d];
       den += f * ml[2 * p + 1];
     }
@@ -471,29 +594,45 @@ __global__ void __launch_bounds__(D) partition_reduce_kernel(DecodeArgs a) {
 // ---- host side -------------------------------------------------------------------------
 
 int choose_partition_size(int num_seqs, int num_kv_heads, int max_context_len) {
-  // Aim for about 2048 resident waves (2 per SIMD on 256 CUs) with at least
-  // 4 blocks per wave; a partition is a multiple of 16 * waves-per-group.
+  // Pick the number of partitions per sequence, np, as the smallest value
+  // for which the launch fills the chip evenly and no wave streams more than
+  // 64 blocks: units * np workgroups should be at least one per CU (256) and
+  // either a whole number of CU rounds or at least four rounds (then the
+  // dispatcher balances the remainder).  Each partition keeps >= 4 blocks per
+  // wave.  Partitions of one sequence are made as even as a 16-token granule
+  // allows.
+  constexpr int64_t kCUs = 256;
   const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads;
-  const int64_t blocks = units * ((max_context_len + kBlockTokens - 1) / kBlockTokens);
-  int64_t per_wave = (blocks + 2047) / 2048;
-  if (per_wave < 4) per_wave = 4;
-  int64_t ps = per_wave * kWaves * kBlockTokens;
-  const int64_t cap = ((static_cast<int64_t>(max_context_len) + kBlockTokens - 1) / kBlockTokens) * kBlockTokens;
-  if (ps > cap) ps = cap > 0 ? cap : kBlockTokens;
-  if (ps > (1 << 30)) ps = 1 << 30;
-  return static_cast<int>(ps);
+  const int64_t seq_blocks = (static_cast<int64_t>(max_context_len) + kBlockTokens - 1) / kBlockTokens;
+  if (seq_blocks <= 0 || units <= 0) return kBlockTokens;
+  const int64_t np_min = (seq_blocks + kMaxPartitionBlocks - 1) / kMaxPartitionBlocks;
+  int64_t np_max = seq_blocks / (4 * kWaves);
+  if (np_max < np_min) np_max = np_min;
+  int64_t np = np_max;
+  for (int64_t cand = np_min; cand <= np_max; ++cand) {
+    const int64_t wgs = units * cand;
+    const int64_t per_wave = (seq_blocks + cand * kWaves - 1) / (cand * kWaves);
+    if (per_wave <= 64 && wgs >= kCUs && (wgs % kCUs == 0 || wgs >= 4 * kCUs)) {
+      np = cand;
+      break;
+    }
+  }
+  if (np < 1) np = 1;
+  const int64_t blocks = (seq_blocks + np - 1) / np;
+  return static_cast<int>(blocks * kBlockTokens);
 }
 
 template <typename QT, typename CT, int D>
 static int launch_typed(const DecodeArgs& a, hipStream_t stream) {
   const int64_t grid = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.num_partitions;
   if (grid > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL((paged_decode_kernel<QT, CT, D>), dim3(static_cast<unsigned>(grid)), dim3(kThreads),
-                     0, stream, a);
+  // fp32 tiles are twice as large: two in flight keep them in registers
+  constexpr int pipe = std::is_same<CT, F32>::value ? 2 : PKV_DECODE_PIPE;
+  hipLaunchKernelGGL((paged_decode_kernel<QT, CT, D, pipe>), dim3(static_cast<unsigned>(grid)),
+                     dim3(kThreads), 0, stream, a);
   int rc = check_launch();
-  if (rc != PKV_OK || a.num_partitions == 1) return rc;
-  hipLaunchKernelGGL((partition_reduce_kernel<QT, D>), dim3(a.num_seqs * a.num_q_heads), dim3(D), 0,
-                     stream, a);
+  if (rc != PKV_OK || PKV_DECODE_MERGE != 0 || a.num_partitions == 1) return rc;
+  hipLaunchKernelGGL((partition_merge_kernel<QT, D>), dim3(a.num_seqs * a.num_q_heads), dim3(D), 0, stream, a);
   return check_launch();
 }
 

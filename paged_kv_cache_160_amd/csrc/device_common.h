@@ -109,4 +109,50 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// ---- cache-row writes ------------------------------------------------------------
+// One wave writes one (token, head) row of D elements to its pool row
+// (`dst_row` counts rows of D elements).  Same dtype: a bit copy in 16-byte
+// chunks.  fp8: a = max|x| over the row, s = a / 448 (s = 1 if a == 0),
+// codes = e4m3 RNE of clamp(x / s, -448, 448), with both divisions correctly
+// rounded in fp32; the scale goes to scales[dst_row].
+template <typename Src, int D>
+__device__ __forceinline__ void write_row_fp8(const void* src, int64_t src_row, uint8_t* pool,
+                                              float* scales, int64_t dst_row, int lane) {
+  constexpr int kPer = D / kWave;   // 1 or 2 elements per lane
+  float x[kPer];
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    x[i] = load_as_f32<Src>(src, src_row * D + lane * kPer + i);
+    amax = fmaxf(amax, fabsf(x[i]));
+  }
+  amax = wave_max(amax);
+  float s = __fdiv_rn(amax, 448.0f);
+  if (amax == 0.0f) s = 1.0f;
+  uint32_t packed = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    float y = __fdiv_rn(x[i], s);
+    y = fminf(fmaxf(y, -448.0f), 448.0f);
+    packed |= e4m3_encode_rne(y) << (8 * i);
+  }
+  uint8_t* dst = pool + dst_row * D + lane * kPer;
+  if constexpr (kPer == 2) {
+    *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(packed);
+  } else {
+    *dst = static_cast<uint8_t>(packed);
+  }
+  if (lane == 0) scales[dst_row] = s;
+}
+
+__device__ __forceinline__ void write_row_copy(const void* src, int64_t src_row, void* pool, int64_t dst_row,
+                                               int row_bytes, int lane) {
+  const int chunks = row_bytes / 16;
+  if (lane < chunks) {
+    const uint4* s = reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(src) + src_row * row_bytes);
+    uint4* d = reinterpret_cast<uint4*>(static_cast<uint8_t*>(pool) + dst_row * row_bytes);
+    d[lane] = s[lane];
+  }
+}
+
 }  // namespace pkv

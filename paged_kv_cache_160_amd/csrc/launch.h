@@ -37,6 +37,12 @@ struct DecodeArgs {
   pkv_dtype q_dtype, cache_dtype;
   int partition_size;      // tokens, multiple of 16 (resolved, never 0)
   int num_partitions;      // ceil(max_context_len / partition_size), >= 1
+  // fused cache write of this step's token (slot_mapping == nullptr: none)
+  const void* k_new;       // [num_seqs][num_kv_heads][head_dim] of src_dtype
+  const void* v_new;
+  const int64_t* slot_mapping;   // [num_seqs]: slot of position context_lens[b] - 1
+  pkv_dtype src_dtype;
+  int* counters;           // [num_seqs][num_kv_heads], zero between calls
   float* part_ml;          // [num_seqs][num_q_heads][num_partitions][2]  (m, l)
   float* part_acc;         // [num_seqs][num_q_heads][num_partitions][head_dim]
 };

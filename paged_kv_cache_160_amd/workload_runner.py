@@ -90,5 +90,22 @@ class GpuWorkload:
         vd = to_device(np.stack(vs), self.w.src_dtype, self.device)
         return c.append_one_each(list(seqs), kd, vd)
 
+    def step_rows(self, seqs):
+        """Each sequence's next K/V row (position = its current length)."""
+        c = self.cache
+        ks, vs = [], []
+        for s in seqs:
+            k, v = self.rows(s)
+            L = c.seq_len(s)
+            ks.append(k[L])
+            vs.append(v[L])
+        return (to_device(np.stack(ks), self.w.src_dtype, self.device),
+                to_device(np.stack(vs), self.w.src_dtype, self.device))
+
+    def decode_step(self, seqs, step: int, partition_size: int = 0) -> torch.Tensor:
+        """Fused decode step (append the next row of each sequence, attend)."""
+        kd, vd = self.step_rows(seqs)
+        return self.cache.decode_step(self.queries(step), list(seqs), kd, vd, partition_size=partition_size)[0]
+
     def queries(self, step: int = 0) -> torch.Tensor:
         return to_device(wl.queries(self.w, step), self.w.q_dtype, self.device)
