@@ -15,8 +15,9 @@ value    = KV tokens attended per second = sum over timed steps and layers of
            sum_b L_b, divided by the timed wall time.
 roofline = the decode call's algorithmic bytes (K/V [+ fp8 scales] of every
            attended token, q, out, block-table entries, lengths, and the
-           appended K/V row) divided by its average duration from HIP events
-           on the launch stream.
+           appended K/V row) divided by the attention kernel's average
+           duration from HIP events on the launch stream (every 8th layer by
+           default); the whole call (with the merge) is reported beside it.
 cpu_baseline = the fp64 oracle (test infrastructure) timed on the host over a
            bounded sample of the same workload.
 
@@ -61,8 +62,17 @@ def parse():
     ap.add_argument("--write-traffic", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
                     help="from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of this bench and of "
                          "--calibrate-copy, write profiles/decode_<workload>_traffic.json and exit")
+    ap.add_argument("--probe-read", action="store_true",
+                    help="only measure a cold read-bandwidth reference (a torch sum over 256 MiB per launch, "
+                         "rotating through 4 GiB) and exit")
+    ap.add_argument("--event-every", type=int, default=8,
+                    help="bracket every Nth layer's decode call with HIP events (default 8: each event pair "
+                         "adds a few microseconds of GPU time, so the calls in between run undisturbed)")
     ap.add_argument("--unfused", action="store_true",
-                    help="append with kv_cache_append, then paged_attention_decode (default: one fused call)")
+                    help="write the step's rows with kv_cache_append, then attend (default: the write is fused "
+                         "into the attention kernel)")
+    ap.add_argument("--one-call", action="store_true",
+                    help="use the one-call paged_attention_decode_append (events then bracket both launches)")
     return ap.parse_args()
 
 
@@ -152,6 +162,28 @@ def main():
         log("[bench] calibration copies done: 5 x 1 GiB")
         return
 
+    if args.probe_read:
+        # Reference for the per-launch cold HBM rate of this GPU at the size of
+        # one 8B-shape decode layer: device-to-device copies of 128 MiB
+        # (256 MiB of traffic per launch) rotating through 16 slices of a
+        # 2 GiB source, so no slice is cache-resident.
+        n = 2 ** 27
+        src = torch.ones(16 * n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+        res = []
+        for r in range(48):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dst.copy_(src[(r % 16) * n:(r % 16 + 1) * n])
+            e1.record()
+            res.append((e0, e1))
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) * 1e3 for a, b in res[16:])
+        med = t[len(t) // 2]
+        log(f"[bench] cold 128 MiB copy (256 MiB traffic): median {med:.1f} us -> {2 * n / med / 1e3:.0f} GB/s")
+        print(json.dumps({"probe": "cold_copy_128MiB", "median_us": med, "gbps": 2 * n / med / 1e3}))
+        return
+
     import workloads as wl
     import paged_kv_cache_160_amd as pkv
     from paged_kv_cache_160_amd.cache import PagedKVCache
@@ -230,8 +262,11 @@ def main():
     if args.partition_size:
         ps_used = args.partition_size
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps * layers)]
+    timed_layers = [l for l in range(layers) if l % max(1, args.event_every) == 0]
+    # per sampled call: before the attention kernel, after it (= before the
+    # merge kernel), after the merge
+    ev = {(s_, l): tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+          for s_ in range(args.warmup, n_steps) for l in timed_layers}
     tokens_timed = 0
     bytes_timed = 0
 
@@ -275,23 +310,39 @@ def main():
                                          src_code, cache_code, sp)
                 if rc:
                     raise pkv.PagedKVError(rc, "kv_cache_append")
-            if timed:
-                ev[(s - args.warmup) * layers + l][0].record(stream)
-            if args.unfused:
-                rc = lib.paged_attention_decode(outs.data_ptr() + l * out_stride, qbase + l * q_stride, kp, vp,
-                                                ksp, vsp, d_tables.data_ptr(), d_lens.data_ptr(), B, hq, hkv, D,
-                                                w.num_blocks, mb, max_len, scale, q_code, cache_code,
-                                                args.partition_size, ws_ptr, ws_bytes, sp)
-            else:
-                rc = lib.paged_attention_decode_append(outs.data_ptr() + l * out_stride, qbase + l * q_stride,
-                                                       kl, vl, kp, vp, ksp, vsp, d_slots.data_ptr(),
+            e = ev.get((s, l)) if timed else None
+            if e:
+                e[0].record(stream)
+            o_ptr, q_ptr = outs.data_ptr() + l * out_stride, qbase + l * q_stride
+            if args.one_call:
+                rc = lib.paged_attention_decode_append(o_ptr, q_ptr, kl, vl, kp, vp, ksp, vsp, d_slots.data_ptr(),
                                                        d_tables.data_ptr(), d_lens.data_ptr(), B, hq, hkv, D,
                                                        w.num_blocks, mb, max_len, scale, q_code, src_code,
                                                        cache_code, args.partition_size, ws_ptr, ws_bytes, sp)
+                if rc:
+                    raise pkv.PagedKVError(rc, "paged_attention_decode_append")
+                if e:
+                    e[1].record(stream)
+                    e[2].record(stream)
+                continue
+            # split form: the attention kernel (with the cache write fused in,
+            # unless --unfused wrote it already), then the partition merge
+            slot_ptr = None if args.unfused else d_slots.data_ptr()
+            rc = lib.paged_attention_decode_append_partials(o_ptr, q_ptr, kl, vl, kp, vp, ksp, vsp, slot_ptr,
+                                                            d_tables.data_ptr(), d_lens.data_ptr(), B, hq, hkv,
+                                                            D, w.num_blocks, mb, max_len, scale, q_code,
+                                                            src_code, cache_code, args.partition_size, ws_ptr,
+                                                            ws_bytes, sp)
             if rc:
-                raise pkv.PagedKVError(rc, "decode")
-            if timed:
-                ev[(s - args.warmup) * layers + l][1].record(stream)
+                raise pkv.PagedKVError(rc, "paged_attention_decode_append_partials")
+            if e:
+                e[1].record(stream)
+            rc = lib.paged_attention_merge_partials(o_ptr, d_lens.data_ptr(), B, hq, hkv, D, mb, max_len, q_code,
+                                                    args.partition_size, ws_ptr, ws_bytes, sp)
+            if rc:
+                raise pkv.PagedKVError(rc, "paged_attention_merge_partials")
+            if e:
+                e[2].record(stream)
         if timed:
             tokens_timed += sum_l * layers
             kv_bytes = sum_l * hkv * D * 2 * ces
@@ -312,14 +363,15 @@ def main():
         step(s, True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    dec_ms = [a.elapsed_time(b) for a, b in ev]
-    avg_dec_s = sum(dec_ms) / len(dec_ms) / 1e3
+    kern_s = sum(a.elapsed_time(b) for a, b, _ in ev.values()) / len(ev) / 1e3
+    call_s = sum(a.elapsed_time(c) for a, _, c in ev.values()) / len(ev) / 1e3
     calls = args.steps * layers
     bytes_per_call = bytes_timed / calls
-    achieved = bytes_per_call / avg_dec_s / 1e9
+    achieved = bytes_per_call / kern_s / 1e9
     value = tokens_timed / elapsed
-    log(f"[bench] {args.steps} steps in {elapsed * 1e3:.2f} ms; decode call avg {avg_dec_s * 1e6:.2f} us; "
-        f"{achieved:.0f} GB/s algorithmic; {value / 1e9:.3f} G KV tokens/s")
+    log(f"[bench] {args.steps} steps in {elapsed * 1e3:.2f} ms; attention kernel avg {kern_s * 1e6:.2f} us "
+        f"({achieved:.0f} GB/s algorithmic); whole decode call {call_s * 1e6:.2f} us "
+        f"({bytes_per_call / call_s / 1e9:.0f} GB/s); {value / 1e9:.3f} G KV tokens/s")
     traffic = load_traffic(w.name)
 
     cpu = None
@@ -348,12 +400,14 @@ def main():
         },
         "achieved_hbm_gbps": achieved,
         "pct_of_peak": 100.0 * achieved / HBM_PEAK_GBPS,
-        "decode_call_us": avg_dec_s * 1e6,
+        "attention_kernel_us": kern_s * 1e6,
+        "decode_call_us": call_s * 1e6,
+        "decode_call_hbm_gbps": bytes_per_call / call_s / 1e9,
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-            "kernel": ("paged_attention_decode" if args.unfused else "paged_attention_decode_append")
-                      + " call (paged_decode_kernel + partition_merge_kernel when split)",
+            "kernel": "paged_decode_kernel" + ("" if args.unfused else " (cache write fused)")
+                      + ("; timed with the partition merge (one call)" if args.one_call else ""),
             "bytes_per_launch": bytes_per_call,
         },
         "cpu_baseline": cpu,

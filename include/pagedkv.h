@@ -214,6 +214,35 @@ int paged_attention_decode_append(void* out, const void* q, const void* k_new, c
                                   pkv_dtype cache_dtype, int partition_size, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/*
+ * Split form of paged_attention_decode_append, for callers that schedule or
+ * time its two launches separately.  paged_attention_decode_append_partials
+ * takes the same arguments (slot_mapping may be NULL: no cache write, as in
+ * paged_attention_decode) and launches only the attention kernel: it writes
+ * the output rows of sequences that fit in one partition and the partition
+ * states of the others into the workspace.  paged_attention_merge_partials
+ * then merges those states into the remaining output rows (log-sum-exp); it
+ * must get the same num_seqs, head counts, head_dim, max_context_len,
+ * partition_size and workspace, on the same stream.  The pair gives exactly
+ * the bytes of the one-call form.  When nothing is split, the merge call
+ * does nothing.
+ */
+int paged_attention_decode_append_partials(void* out, const void* q, const void* k_new, const void* v_new,
+                                           void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                           const int64_t* slot_mapping,
+                                           const int32_t* block_tables, const int32_t* context_lens,
+                                           int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                           int num_blocks, int max_blocks_per_seq, int max_context_len,
+                                           float scale, pkv_dtype q_dtype, pkv_dtype src_dtype,
+                                           pkv_dtype cache_dtype, int partition_size, void* workspace,
+                                           size_t workspace_bytes, void* stream);
+
+int paged_attention_merge_partials(void* out, const int32_t* context_lens,
+                                   int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                   int max_blocks_per_seq, int max_context_len, pkv_dtype q_dtype,
+                                   int partition_size, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host block allocator.  Opaque handle, not thread-safe, no device memory.  */
 /*                                                                          */

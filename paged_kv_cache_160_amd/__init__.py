@@ -20,6 +20,7 @@ from . import _lib
 __all__ = [
     "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3", "BLOCK_SIZE", "PagedKVError",
     "kv_cache_append", "copy_blocks", "paged_attention_decode", "paged_attention_decode_append",
+    "paged_attention_decode_append_partials", "paged_attention_merge_partials",
     "workspace_size",
     "decode_partition_size", "BlockAllocator", "dtype_code", "abi_version",
 ]
@@ -157,6 +158,36 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
     return out
 
 
+def _decode_append_call(fn_name, out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables,
+                        context_lens, max_context_len, scale, k_scale, v_scale, partition_size, workspace,
+                        stream):
+    nb, hkv, d = _pool_geometry(k_pool)
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must be [B, Hq, D] of one dtype")
+    B, hq = int(q.shape[0]), int(q.shape[1])
+    if slot_mapping is not None:
+        if k_new.shape != (B, hkv, d) or v_new.shape != k_new.shape:
+            raise ValueError("k_new/v_new must be [B, Hkv, D]")
+        if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != B:
+            raise ValueError("slot_mapping must be int64 [B]")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    cdt = dtype_code(k_pool.dtype)
+    need = workspace_size(B, hq, hkv, d, max_context_len, partition_size, cdt)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    src_code = dtype_code(k_new.dtype) if k_new is not None else dtype_code(q.dtype)
+    _check(getattr(_lib.lib(), fn_name)(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+        _ptr(v_scale), _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb,
+        int(block_tables.shape[1]), int(max_context_len), float(scale), dtype_code(q.dtype),
+        src_code, cdt, int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)), fn_name)
+    return out, workspace
+
+
 def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
                                   v_new: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
                                   slot_mapping: torch.Tensor, block_tables: torch.Tensor,
@@ -167,29 +198,34 @@ def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: tor
     """A decode step with the cache write fused in: row b of ``k_new, v_new
     [B, Hkv, D]`` goes to ``slot_mapping[b]`` (the slot of position
     ``context_lens[b] - 1``), then ``out`` = attention over the whole cache."""
-    nb, hkv, d = _pool_geometry(k_pool)
-    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape or out.dtype != q.dtype:
-        raise ValueError("q and out must be [B, Hq, D] of one dtype")
-    B, hq = int(q.shape[0]), int(q.shape[1])
-    if k_new.shape != (B, hkv, d) or v_new.shape != k_new.shape:
-        raise ValueError("k_new/v_new must be [B, Hkv, D]")
-    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != B:
-        raise ValueError("slot_mapping must be int64 [B]")
-    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
-        raise ValueError("block_tables and context_lens must be int32")
-    if scale is None:
-        scale = 1.0 / math.sqrt(d)
-    cdt = dtype_code(k_pool.dtype)
-    need = workspace_size(B, hq, hkv, d, max_context_len, partition_size, cdt)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    if slot_mapping is None:
+        raise ValueError("slot_mapping is required")
+    return _decode_append_call("paged_attention_decode_append", out, q, k_new, v_new, k_pool, v_pool,
+                               slot_mapping, block_tables, context_lens, max_context_len, scale, k_scale,
+                               v_scale, partition_size, workspace, stream)[0]
+
+
+def paged_attention_decode_append_partials(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables,
+                                           context_lens, max_context_len, scale=None, k_scale=None,
+                                           v_scale=None, partition_size=0, workspace=None, stream=None):
+    """First launch of the split form (attention kernel only); returns
+    ``(out, workspace)`` for :func:`paged_attention_merge_partials`.
+    ``slot_mapping`` may be None (no cache write)."""
+    return _decode_append_call("paged_attention_decode_append_partials", out, q, k_new, v_new, k_pool, v_pool,
+                               slot_mapping, block_tables, context_lens, max_context_len, scale, k_scale,
+                               v_scale, partition_size, workspace, stream)
+
+
+def paged_attention_merge_partials(out: torch.Tensor, context_lens: torch.Tensor, num_kv_heads: int,
+                                   max_blocks_per_seq: int, max_context_len: int, partition_size: int = 0,
+                                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Second launch of the split form: merge the partition states."""
+    B, hq, d = (int(x) for x in out.shape)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib.lib().paged_attention_decode_append(
-        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
-        _ptr(v_scale), _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb,
-        int(block_tables.shape[1]), int(max_context_len), float(scale), dtype_code(q.dtype),
-        dtype_code(k_new.dtype), cdt, int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)),
-        "paged_attention_decode_append")
+    _check(_lib.lib().paged_attention_merge_partials(
+        _ptr(out), _ptr(context_lens), B, hq, num_kv_heads, d, max_blocks_per_seq, int(max_context_len),
+        dtype_code(out.dtype), int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)),
+        "paged_attention_merge_partials")
     return out
 
 

@@ -149,7 +149,7 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new, 
                 const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
                 int num_kv_heads, int head_dim, int num_blocks, int max_blocks_per_seq, int max_context_len,
                 float scale, pkv_dtype q_dtype, pkv_dtype src_dtype, pkv_dtype cache_dtype, int partition_size,
-                void* workspace, size_t workspace_bytes, void* stream) {
+                void* workspace, size_t workspace_bytes, void* stream, int stages) {
   if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype) || !valid_dtype(src_dtype)) return PKV_ERR_INVALID_ARG;
   if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len))
     return PKV_ERR_INVALID_ARG;
@@ -212,7 +212,7 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new, 
     a.part_ml = reinterpret_cast<float*>(base + ws.ml);
     a.part_acc = reinterpret_cast<float*>(base + ws.acc);
   }
-  return pkv::launch_decode(a, static_cast<hipStream_t>(stream));
+  return pkv::launch_decode(a, static_cast<hipStream_t>(stream), stages);
 }
 
 }  // namespace
@@ -229,7 +229,7 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
   return decode_impl(out, q, nullptr, nullptr, k_pool, v_pool, k_scale, v_scale, nullptr, block_tables,
                      context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
                      max_blocks_per_seq, max_context_len, scale, q_dtype, q_dtype, cache_dtype,
-                     partition_size, workspace, workspace_bytes, stream);
+                     partition_size, workspace, workspace_bytes, stream, pkv::kStageBoth);
 }
 
 int paged_attention_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
@@ -244,7 +244,64 @@ int paged_attention_decode_append(void* out, const void* q, const void* k_new, c
   return decode_impl(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, block_tables,
                      context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
                      max_blocks_per_seq, max_context_len, scale, q_dtype, src_dtype, cache_dtype,
-                     partition_size, workspace, workspace_bytes, stream);
+                     partition_size, workspace, workspace_bytes, stream, pkv::kStageBoth);
+}
+
+int paged_attention_decode_append_partials(void* out, const void* q, const void* k_new, const void* v_new,
+                                           void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                           const int64_t* slot_mapping, const int32_t* block_tables,
+                                           const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                           int num_kv_heads, int head_dim, int num_blocks,
+                                           int max_blocks_per_seq, int max_context_len, float scale,
+                                           pkv_dtype q_dtype, pkv_dtype src_dtype, pkv_dtype cache_dtype,
+                                           int partition_size, void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  return decode_impl(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                     max_blocks_per_seq, max_context_len, scale, q_dtype, src_dtype, cache_dtype,
+                     partition_size, workspace, workspace_bytes, stream, pkv::kStageAttend);
+}
+
+int paged_attention_merge_partials(void* out, const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int max_blocks_per_seq, int max_context_len,
+                                   pkv_dtype q_dtype, int partition_size, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(q_dtype) || q_dtype == PKV_FP8_E4M3) return PKV_ERR_INVALID_ARG;
+  if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len))
+    return PKV_ERR_INVALID_ARG;
+  if (max_blocks_per_seq <= 0 ||
+      static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBlock)
+    return PKV_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (partition_size < 0 || partition_size % kBlock != 0 || partition_size > PKV_MAX_PARTITION_TOKENS)
+    return PKV_ERR_INVALID_ARG;
+  int ps, np;
+  int rc = resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, &ps, &np);
+  if (rc != PKV_OK) return rc;
+  if (num_seqs == 0 || np == 1) return PKV_OK;       // nothing was split
+  if (!out || !context_lens || !aligned16(out)) return PKV_ERR_INVALID_ARG;
+  const WorkspaceLayout ws = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, np);
+  if (!workspace || workspace_bytes < ws.total || !aligned16(workspace)) return PKV_ERR_WORKSPACE;
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.context_lens = context_lens;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.q_dtype = q_dtype;
+  // the merge kernel is instantiated per output dtype; any cache dtype that
+  // pairs with q_dtype selects the same one
+  a.cache_dtype = q_dtype;
+  a.partition_size = ps;
+  a.num_partitions = np;
+  char* base = static_cast<char*>(workspace);
+  a.counters = reinterpret_cast<int*>(base + ws.counters);
+  a.part_ml = reinterpret_cast<float*>(base + ws.ml);
+  a.part_acc = reinterpret_cast<float*>(base + ws.acc);
+  return pkv::launch_decode(a, static_cast<hipStream_t>(stream), pkv::kStageMerge);
 }
 
 }  // extern "C"

@@ -566,6 +566,7 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
 // fit in one partition (or was empty) were written by the main kernel.
 template <typename QT, int D>
 __global__ void __launch_bounds__(D) partition_merge_kernel(DecodeArgs a) {
+  constexpr int kChunk = 8;                   // partitions whose loads are in flight together
   const int row = blockIdx.x;                 // b * Hq + h
   const int b = row / a.num_q_heads;
   const int d = threadIdx.x;
@@ -576,17 +577,36 @@ __global__ void __launch_bounds__(D) partition_merge_kernel(DecodeArgs a) {
   if (np <= 1) return;
   const float* ml = a.part_ml + static_cast<int64_t>(row) * P * 2;
   const float* acc = a.part_acc + static_cast<int64_t>(row) * P * D;
-  float M = -INFINITY;
-  for (int p = 0; p < np; ++p) M = fmaxf(M, ml[2 * p]);
-  float num = 0.f, den = 0.f;
-  if (M != -INFINITY) {
-    for (int p = 0; p < np; ++p) {
-      const float mp = ml[2 * p];
-      if (mp == -INFINITY) continue;
-      const float f = __builtin_amdgcn_exp2f(mp - M);
-      num += f * acc[static_cast<int64_t>(p) * D + d];
-      den += f * ml[2 * p + 1];
+  // Running merge over chunks of partitions; within a chunk every load is
+  // issued before any of them is used.
+  float M = -INFINITY, num = 0.f, den = 0.f;
+  for (int p0 = 0; p0 < np; p0 += kChunk) {
+    float mp[kChunk], lp[kChunk], ap[kChunk];
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      const int p = min(p0 + i, np - 1);
+      mp[i] = ml[2 * p];
+      lp[i] = ml[2 * p + 1];
+      ap[i] = acc[static_cast<int64_t>(p) * D + d];
     }
+    float cm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i)
+      if (p0 + i < np) cm = fmaxf(cm, mp[i]);
+    const float M_new = fmaxf(M, cm);
+    if (M_new == -INFINITY) continue;
+    const float r = __builtin_amdgcn_exp2f(M - M_new);   // 0 while M is still -inf
+    num *= r;
+    den *= r;
+#pragma unroll
+    for (int i = 0; i < kChunk; ++i) {
+      if (p0 + i < np && mp[i] != -INFINITY) {
+        const float f = __builtin_amdgcn_exp2f(mp[i] - M_new);
+        num += f * ap[i];
+        den += f * lp[i];
+      }
+    }
+    M = M_new;
   }
   store_from_f32<QT>(a.out, static_cast<int64_t>(row) * D + d, den > 0.f ? num / den : 0.f);
 }
@@ -623,33 +643,36 @@ int choose_partition_size(int num_seqs, int num_kv_heads, int max_context_len) {
 }
 
 template <typename QT, typename CT, int D>
-static int launch_typed(const DecodeArgs& a, hipStream_t stream) {
+static int launch_typed(const DecodeArgs& a, hipStream_t stream, int stages) {
   const int64_t grid = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.num_partitions;
   if (grid > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
-  // fp32 tiles are twice as large: two in flight keep them in registers
-  constexpr int pipe = std::is_same<CT, F32>::value ? 2 : PKV_DECODE_PIPE;
-  hipLaunchKernelGGL((paged_decode_kernel<QT, CT, D, pipe>), dim3(static_cast<unsigned>(grid)),
-                     dim3(kThreads), 0, stream, a);
-  int rc = check_launch();
-  if (rc != PKV_OK || PKV_DECODE_MERGE != 0 || a.num_partitions == 1) return rc;
+  int rc = PKV_OK;
+  if (stages & kStageAttend) {
+    // fp32 tiles are twice as large: two in flight keep them in registers
+    constexpr int pipe = std::is_same<CT, F32>::value ? 2 : PKV_DECODE_PIPE;
+    hipLaunchKernelGGL((paged_decode_kernel<QT, CT, D, pipe>), dim3(static_cast<unsigned>(grid)),
+                       dim3(kThreads), 0, stream, a);
+    rc = check_launch();
+  }
+  if (rc != PKV_OK || !(stages & kStageMerge) || PKV_DECODE_MERGE != 0 || a.num_partitions == 1) return rc;
   hipLaunchKernelGGL((partition_merge_kernel<QT, D>), dim3(a.num_seqs * a.num_q_heads), dim3(D), 0, stream, a);
   return check_launch();
 }
 
 template <typename QT, typename CT>
-static int launch_dim(const DecodeArgs& a, hipStream_t stream) {
-  if (a.head_dim == 128) return launch_typed<QT, CT, 128>(a, stream);
-  return launch_typed<QT, CT, 64>(a, stream);
+static int launch_dim(const DecodeArgs& a, hipStream_t stream, int stages) {
+  if (a.head_dim == 128) return launch_typed<QT, CT, 128>(a, stream, stages);
+  return launch_typed<QT, CT, 64>(a, stream, stages);
 }
 
-int launch_decode(const DecodeArgs& a, hipStream_t stream) {
+int launch_decode(const DecodeArgs& a, hipStream_t stream, int stages) {
   switch (a.cache_dtype) {
-    case PKV_F32: return launch_dim<F32, F32>(a, stream);
-    case PKV_F16: return launch_dim<F16, F16>(a, stream);
-    case PKV_BF16: return launch_dim<BF16, BF16>(a, stream);
+    case PKV_F32: return launch_dim<F32, F32>(a, stream, stages);
+    case PKV_F16: return launch_dim<F16, F16>(a, stream, stages);
+    case PKV_BF16: return launch_dim<BF16, BF16>(a, stream, stages);
     case PKV_FP8_E4M3:
-      if (a.q_dtype == PKV_BF16) return launch_dim<BF16, FP8>(a, stream);
-      return launch_dim<F16, FP8>(a, stream);
+      if (a.q_dtype == PKV_BF16) return launch_dim<BF16, FP8>(a, stream, stages);
+      return launch_dim<F16, FP8>(a, stream, stages);
   }
   return PKV_ERR_UNSUPPORTED;
 }

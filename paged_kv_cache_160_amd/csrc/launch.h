@@ -47,7 +47,11 @@ struct DecodeArgs {
   float* part_acc;         // [num_seqs][num_q_heads][num_partitions][head_dim]
 };
 
-int launch_decode(const DecodeArgs& a, hipStream_t stream);
+// What a decode call launches: the attention kernel and, when sequences are
+// split into partitions, the merge kernel after it (or only one of them).
+enum DecodeStages { kStageAttend = 1, kStageMerge = 2, kStageBoth = 3 };
+
+int launch_decode(const DecodeArgs& a, hipStream_t stream, int stages);
 
 // Automatic partition length for a decode launch (tokens, multiple of 16).
 int choose_partition_size(int num_seqs, int num_kv_heads, int max_context_len);

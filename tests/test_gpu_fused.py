@@ -100,3 +100,36 @@ def test_fused_step_with_copy_on_write():
         check_cache_rows(w, g.cache, 0, b, ot[b], 1501)
     exp = scenario.expected_decode_rows(w, wl.queries(w, 0), seqs, [1501] * 8)
     assert max_err(out, exp) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("ps", [0, 64])
+def test_split_form_equals_one_call(ps):
+    # paged_attention_decode_append_partials + paged_attention_merge_partials
+    # gives the bytes of paged_attention_decode_append (split and unsplit rows)
+    import paged_kv_cache_160_amd as pkv
+    case = ([700, 9, 1300, 64], 32, 8, 128, "bf16", None, None, ps)
+    say(f"[split] ps={ps}")
+    w = _make(case, seed=23)
+    ops = wl.setup_ops(w)
+    one = GpuWorkload(w).run(ops)
+    two = GpuWorkload(w).run(ops)
+    seqs = list(range(w.num_seqs))
+    for step in range(3):
+        out_a = one.decode_step(seqs, step, partition_size=ps)
+        c = two.cache
+        kd, vd = two.step_rows(seqs)
+        slots, pairs = c.alloc.batch_append_one(seqs)
+        assert not pairs
+        slot_t = torch.tensor(slots, dtype=torch.int64, device="cuda")
+        bt, lens, max_len = c.block_tables(seqs)
+        q = two.queries(step)
+        out_b = torch.empty_like(q)
+        out_b, ws = pkv.paged_attention_decode_append_partials(out_b, q, kd, vd, c.k[0], c.v[0], slot_t, bt, lens,
+                                                               max_len, partition_size=ps)
+        pkv.paged_attention_merge_partials(out_b, lens, w.num_kv_heads, w.max_blocks_per_seq, max_len,
+                                           partition_size=ps, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(out_a.cpu(), out_b.cpu()), f"step {step}"
+    for b in seqs:
+        tb, lb = two.cache.alloc.block_tables(seqs)
+        check_cache_rows(w, two.cache, 0, b, tb[b].numpy(), int(lb[b]))
