@@ -33,6 +33,7 @@ the benchmark use this module.
 """
 from __future__ import annotations
 
+import copy
 from typing import Dict, List, Tuple
 
 BLOCK_TOKENS = 16
@@ -64,6 +65,9 @@ class BlockAllocatorModel:
         if sorted(order) != list(range(self.num_blocks)):
             raise AllocError("invalid_arg")
         self.free = order[::-1]
+
+    def _available(self) -> int:
+        return len(self.free)
 
     def _take(self) -> int:
         blk = self.free.pop()
@@ -112,7 +116,7 @@ class BlockAllocatorModel:
         new_blocks = -(-(L + n) // BLOCK_TOKENS) - -(-L // BLOCK_TOKENS)
         if len(table) + new_blocks > self.max_blocks_per_seq:
             raise AllocError("invalid_arg")
-        if int(needs_cow) + new_blocks > len(self.free):
+        if int(needs_cow) + new_blocks > self._available():
             raise AllocError("no_free_blocks")
         pairs: List[Tuple[int, int]] = []
         if needs_cow:
@@ -174,3 +178,164 @@ class BlockAllocatorModel:
             "stored_tokens": stored,
             "utilisation": (stored / (BLOCK_TOKENS * used)) if used else 0.0,
         }
+
+
+class PrefixCachingAllocatorModel(BlockAllocatorModel):
+    """The allocator with prefix caching; keys are whole token prefixes.
+
+    What the pages fix ("KV Cache优化实战" §5.2-5.3; "企业官网建设流程全解析"
+    §6.2-6.3): cached KV blocks are found by their content, keyed by the
+    model identity together with the token ids; a new request walks its
+    prefix block by block, reuses every block that matches exactly and stops
+    at the first that does not; the cache is finite, and what is evicted
+    must follow the prefix tree (a block whose prefix is gone is useless), not
+    plain access order.
+
+    Readings (the pages leave these open):
+      * only full 16-token blocks are indexed; the key of a sequence's block i
+        is (model key, tokens 0 .. 16*i+15), the whole prefix it ends;
+      * a block is indexed when an append that names its tokens fills it,
+        unless its key is indexed already (the block then stays private), and
+        for i > 0 only if the sequence's block i-1 is the one indexed under
+        the shorter key - so whoever holds an indexed block holds its parent;
+      * ``create``, ``create_cached`` and ``fork`` of a tracked sequence give
+        tracked sequences; an append without tokens (``append_slots``) stops
+        tracking the sequence, since the keys of its later blocks are unknown;
+      * a lookup matches at most (n_tokens - 1) // 16 blocks, so the last
+        prompt token is always computed, and takes a reference on each match;
+      * an indexed block whose count drops to zero stays indexed and becomes
+        evictable, stamped with a counter that rises at each such release;
+      * a fresh block comes from the free list while it has any; otherwise
+        the evictable block with the smallest stamp among those with no
+        indexed child is evicted and reused (leaf first: a chain shrinks from
+        its tail, and its head, shared by the most requests, goes last);
+      * capacity for an append counts free and evictable blocks.
+    """
+
+    def __init__(self, num_blocks: int, max_blocks_per_seq: int, model_key: int = 0):
+        super().__init__(num_blocks, max_blocks_per_seq)
+        self.model_key = int(model_key)
+        self.index: Dict[tuple, int] = {}          # prefix key -> block
+        self.key_of: Dict[int, tuple] = {}         # indexed block -> its key
+        self.evictable: Dict[int, int] = {}        # block (count 0, indexed) -> stamp
+        self.clock = 0
+        self.tokens: Dict[int, List[int]] = {}     # tracked sequences' tokens
+        self.lookup_blocks = self.hit_blocks = self.evictions = 0
+
+    def _key(self, toks, nblocks: int) -> tuple:
+        return (self.model_key,) + tuple(toks[:BLOCK_TOKENS * nblocks])
+
+    def _children(self, blk: int) -> int:
+        key = self.key_of[blk]
+        return sum(1 for k in self.index if len(k) == len(key) + BLOCK_TOKENS and k[:len(key)] == key)
+
+    # -- free list with eviction --------------------------------------------
+    def _available(self) -> int:
+        return len(self.free) + len(self.evictable)
+
+    def _take(self) -> int:
+        if self.free:
+            return super()._take()
+        _, blk = min((st, b) for b, st in self.evictable.items() if self._children(b) == 0)
+        del self.evictable[blk]
+        del self.index[self.key_of.pop(blk)]
+        self.evictions += 1
+        self.ref[blk] = 1
+        return blk
+
+    def _release(self, blk: int) -> None:
+        self.ref[blk] -= 1
+        if self.ref[blk] == 0:
+            if blk in self.key_of:
+                self.clock += 1
+                self.evictable[blk] = self.clock
+            else:
+                self.free.append(blk)
+
+    # -- sequences ----------------------------------------------------------
+    def create(self, seq: int) -> None:
+        super().create(seq)
+        self.tokens[seq] = []
+
+    def create_cached(self, seq: int, tokens) -> int:
+        """New tracked sequence holding the longest indexed prefix of
+        ``tokens``; returns its length (a multiple of 16)."""
+        if seq in self.tables:
+            raise AllocError("invalid_arg")
+        tokens = [int(t) for t in tokens]
+        most = min(max(len(tokens) - 1, 0) // BLOCK_TOKENS, self.max_blocks_per_seq)
+        hits = []
+        for i in range(most):
+            blk = self.index.get(self._key(tokens, i + 1))
+            if blk is None:
+                break
+            hits.append(blk)
+        self.lookup_blocks += most
+        self.hit_blocks += len(hits)
+        for blk in hits:
+            if self.ref[blk] == 0:
+                del self.evictable[blk]
+            self.ref[blk] += 1
+        n = BLOCK_TOKENS * len(hits)
+        self.tables[seq] = hits
+        self.lens[seq] = n
+        self.tokens[seq] = tokens[:n]
+        return n
+
+    def fork(self, parent: int, child: int) -> None:
+        super().fork(parent, child)
+        if parent in self.tokens:
+            self.tokens[child] = list(self.tokens[parent])
+
+    def free_seq(self, seq: int) -> None:
+        super().free_seq(seq)
+        self.tokens.pop(seq, None)
+
+    def append_slots(self, seq: int, n: int):
+        slots, pairs = super().append_slots(seq, n)
+        if n > 0:
+            self.tokens.pop(seq, None)
+        return slots, pairs
+
+    def append_tokens(self, seq: int, tokens):
+        tokens = [int(t) for t in tokens]
+        slots, pairs = super().append_slots(seq, len(tokens))
+        if seq in self.tokens:
+            toks = self.tokens[seq]
+            done = len(toks) // BLOCK_TOKENS
+            toks.extend(tokens)
+            for i in range(done, len(toks) // BLOCK_TOKENS):
+                self._index_block(seq, i)
+        return slots, pairs
+
+    def batch_append_tokens(self, seqs, tokens):
+        """One token for each sequence, in order; all or nothing."""
+        seqs = [int(s) for s in seqs]
+        if len(set(seqs)) != len(seqs):
+            raise AllocError("invalid_arg")
+        saved = copy.deepcopy(self.__dict__)
+        slots, pairs = [], []
+        try:
+            for s, t in zip(seqs, tokens):
+                sl, pr = self.append_tokens(s, [t])
+                slots += sl
+                pairs += pr
+        except AllocError:
+            self.__dict__.update(saved)
+            raise
+        return slots, pairs
+
+    def _index_block(self, seq: int, i: int) -> None:
+        key = self._key(self.tokens[seq], i + 1)
+        if key in self.index:
+            return
+        table = self.tables[seq]
+        if i > 0 and self.index.get(key[:-BLOCK_TOKENS]) != table[i - 1]:
+            return
+        self.index[key] = table[i]
+        self.key_of[table[i]] = key
+
+    def prefix_stats(self) -> dict:
+        return {"cached_blocks": len(self.index), "evictable_blocks": len(self.evictable),
+                "lookup_blocks": self.lookup_blocks, "hit_blocks": self.hit_blocks,
+                "evictions": self.evictions}

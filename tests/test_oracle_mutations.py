@@ -3,16 +3,20 @@ or halved 1/sqrt(d), a wrong GQA index, K and V swapped, a partition merge
 without the exp(m_p - M) rescale, round-half-up instead of ties-to-even, a
 wrong fp8 exponent bias, a scale from the mean instead of the max, an
 off-by-one position, a reversed free order, a copy-on-write that skips the
-copy - must make at least one of the pins fail.  This shows the pins are
+copy, a prefix cache that evicts by plain recency, keys a block by its own
+tokens only, lets a lookup cover the last prompt token or forgets released
+blocks - must make at least one of the pins fail.  This shows the pins are
 sharp enough to catch the mistakes they are meant to catch."""
 import numpy as np
 import pytest
 
 from oracle import allocator as alloc_mod
 from oracle import attention, cache, fp8_e4m3
+from oracle.allocator import BLOCK_TOKENS as BLOCK
 from tests import test_oracle_allocator as pins_alloc
 from tests import test_oracle_attention as pins_attn
 from tests import test_oracle_fp8 as pins_fp8
+from tests import test_oracle_prefix_cache as pins_prefix
 
 
 def _fails(fn, *args):
@@ -139,3 +143,49 @@ def test_cow_without_copy_is_caught(monkeypatch):
         return orig(self, seq, n)
     monkeypatch.setattr(alloc_mod.BlockAllocatorModel, "append_slots", no_cow)
     _fails(pins_alloc.test_hand_worked_fork_and_copy_on_write)
+
+
+# ---- prefix-cache mutants -------------------------------------------------------------
+
+PCM = alloc_mod.PrefixCachingAllocatorModel
+
+
+def test_plain_lru_eviction_is_caught(monkeypatch):
+    def lru_take(self):
+        if self.free:
+            return alloc_mod.BlockAllocatorModel._take(self)
+        _, blk = min((st, b) for b, st in self.evictable.items())     # ignores children
+        del self.evictable[blk]
+        del self.index[self.key_of.pop(blk)]
+        self.evictions += 1
+        self.ref[blk] = 1
+        return blk
+    monkeypatch.setattr(PCM, "_take", lru_take)
+    _fails(pins_prefix.test_hand_worked_leaf_first_eviction)
+
+
+def test_block_only_key_is_caught(monkeypatch):
+    # keying a block by its own 16 tokens, forgetting the prefix before it
+    monkeypatch.setattr(PCM, "_key", lambda self, toks, nb: (self.model_key,) + tuple(
+        toks[BLOCK * (nb - 1):BLOCK * nb]))
+    _fails(pins_prefix.test_hits_hold_the_right_content_under_pressure, 0)
+
+
+def test_lookup_bound_off_by_one_is_caught(monkeypatch):
+    orig = PCM.create_cached
+
+    def greedy(self, seq, tokens):
+        return orig(self, seq, list(tokens) + [0])      # as if the bound were n // 16
+    monkeypatch.setattr(PCM, "create_cached", greedy)
+    _fails(pins_prefix.test_lookup_never_covers_the_last_prompt_token)
+
+
+def test_forgetting_released_blocks_is_caught(monkeypatch):
+    def forget(self, blk):
+        self.ref[blk] -= 1
+        if self.ref[blk] == 0:
+            if blk in self.key_of:                      # dropped from the index at once
+                del self.index[self.key_of.pop(blk)]
+            self.free.append(blk)
+    monkeypatch.setattr(PCM, "_release", forget)
+    _fails(pins_prefix.test_hits_equal_brute_force_longest_shared_prefix, 0)

@@ -1,0 +1,321 @@
+"""Pins of the prefix-caching allocator model (CPU only).
+
+The model keys blocks by whole token prefixes ("KV Cache优化实战" §5.2-5.3;
+"企业官网建设流程全解析" §6.2-6.3).  These tests pin it to things other
+than itself:
+  * a hand-worked request sequence whose tables, hits and evictions were
+    worked out on paper, in which leaf-first eviction and plain
+    least-recently-used eviction pick different blocks;
+  * a shadow of every physical slot holding the prefix its K/V row stands
+    for: a cache hit must hand out only slots whose shadow equals the new
+    prompt's prefix (a key that forgot the earlier blocks, or eviction of a
+    block still in use, breaks this);
+  * brute force: with no eviction and requests served one at a time, the hit
+    count is the longest run of leading full blocks shared with any earlier
+    request's token stream;
+  * the structural invariants the eviction rule guarantees.
+"""
+import numpy as np
+import pytest
+
+from oracle.allocator import BLOCK_TOKENS, AllocError, PrefixCachingAllocatorModel
+
+B = BLOCK_TOKENS
+
+
+def blk(v):
+    return [v] * B
+
+
+# ---- hand-worked example ------------------------------------------------------
+
+def hand_worked(alloc):
+    """Runs the paper example on ``alloc`` (model or native) and returns what
+    each step observed.  Pool of 5 blocks, block 0 handed out first.
+
+    r1 = a b c x: no hit; blocks 0,1,2 indexed (a, ab, abc), 3 partial.
+    free r1: 0,1,2 evictable with stamps 1,2,3; 3 back on the free list.
+    r2 = a b d y: hits blocks 0,1; takes 3 (free) for d and 4 for y; 3 is
+    indexed as abd.  Free list now empty, evictable {2}.
+    r3 = e f z while r2 lives: needs 3 blocks, 1 available -> refused.
+    free r2: 0,1,3 evictable with stamps 4,5,6; 4 free.  Leaves: 2 (abc,
+    stamp 3) and 3 (abd, stamp 6); 0 and 1 have indexed children.
+    r3 again: takes 4 (free), then evicts 2, then 3 - plain LRU would have
+    evicted 2 and then 0, the root both chains hang from.
+    r4 = a b c w: abc is gone, a and ab remain -> 2 blocks hit.
+    """
+    a, b, c, d, e, f = (blk(v) for v in (11, 12, 13, 14, 15, 16))
+    seen = {}
+    p1 = a + b + c + [1]
+    seen["r1_hit"] = alloc.create_cached(1, p1)
+    seen["r1_slots"] = alloc.append_tokens(1, p1)[0]
+    alloc.free_seq(1) if hasattr(alloc, "free_seq") else alloc.free(1)
+    p2 = a + b + d + [2]
+    seen["r2_hit"] = alloc.create_cached(2, p2)
+    seen["r2_slots"] = alloc.append_tokens(2, p2[seen["r2_hit"]:])[0]
+    p3 = e + f + [3]
+    assert alloc.create_cached(3, p3) == 0
+    try:
+        alloc.append_tokens(3, p3)
+        seen["r3_refused"] = False
+    except Exception as err:          # AllocError or PagedKVError
+        seen["r3_refused"] = getattr(err, "kind", getattr(err, "code", None))
+    alloc.free_seq(2) if hasattr(alloc, "free_seq") else alloc.free(2)
+    seen["r3_slots"] = alloc.append_tokens(3, p3)[0]
+    p4 = a + b + c + [4]
+    seen["r4_hit"] = alloc.create_cached(4, p4)
+    seen["prefix"] = alloc.prefix_stats()
+    return seen
+
+
+EXPECTED_HAND = {
+    "r1_hit": 0,
+    "r1_slots": list(range(0, 49)),                       # blocks 0,1,2,3
+    "r2_hit": 32,
+    "r2_slots": list(range(48, 64)) + [64],               # block 3 then block 4
+    "r3_slots": list(range(64, 80)) + list(range(32, 48)) + [48],   # blocks 4, 2, 3
+    "r4_hit": 32,
+}
+
+
+def test_hand_worked_leaf_first_eviction():
+    m = PrefixCachingAllocatorModel(5, 8)
+    seen = hand_worked(m)
+    for k, v in EXPECTED_HAND.items():
+        assert seen[k] == v, k
+    assert seen["r3_refused"] == "no_free_blocks"
+    assert m.tables[3] == [4, 2, 3] and m.tables[4] == [0, 1]
+    assert seen["prefix"] == {"cached_blocks": 4, "evictable_blocks": 0, "lookup_blocks": 3 + 3 + 2 + 3,
+                              "hit_blocks": 4, "evictions": 2}
+
+
+def test_lookup_never_covers_the_last_prompt_token():
+    m = PrefixCachingAllocatorModel(8, 8)
+    p = blk(1) + blk(2)
+    m.create_cached(0, p)
+    m.append_tokens(0, p)
+    assert m.create_cached(1, p) == 16           # (32 - 1) // 16 = 1 block
+    assert m.create_cached(2, p + [5]) == 32
+    assert m.create_cached(3, blk(1)) == 0       # a one-block prompt never hits
+    assert m.create_cached(4, []) == 0
+
+
+def test_model_key_separates_caches():
+    # same tokens under a different key is a different prefix
+    m = PrefixCachingAllocatorModel(8, 8, model_key=7)
+    p = blk(1) + blk(2) + [3]
+    m.create_cached(0, p)
+    m.append_tokens(0, p)
+    assert m.create_cached(1, p) == 32
+    assert all(k[0] == 7 for k in m.index)
+
+
+def test_append_without_tokens_stops_indexing():
+    m = PrefixCachingAllocatorModel(8, 8)
+    m.create(0)
+    m.append_tokens(0, blk(1))
+    m.append_slots(0, 20)                        # untracked from here on
+    m.append_tokens(0, [9] * 12)
+    assert len(m.index) == 1
+
+
+# ---- shadow content over random streams -------------------------------------------
+
+def _stream(seed, n_ops=600, pool=40, sys_prompts=3, vocab=3):
+    """Random request stream: prompts start with one of a few system prompts
+    and go on with tokens from a tiny vocabulary, so equal blocks at
+    different depths are common; sequences grow, fork and finish under pool
+    pressure.  Yields ops; the model and the native allocator replay them."""
+    rng = np.random.default_rng(seed)
+    systems = [list(rng.integers(100, 100 + vocab, size=int(rng.integers(20, 70)))) for _ in range(sys_prompts)]
+    live, nxt = [], 0
+    for _ in range(n_ops):
+        r = rng.random()
+        if r < 0.3 or not live:
+            sysp = systems[int(rng.integers(sys_prompts))]
+            prompt = sysp + list(rng.integers(0, vocab, size=int(rng.integers(1, 40))))
+            yield ("request", nxt, [int(t) for t in prompt])
+            live.append(nxt)
+            nxt += 1
+        elif r < 0.5:
+            yield ("free", live.pop(int(rng.integers(len(live)))))
+        elif r < 0.56:
+            p = live[int(rng.integers(len(live)))]
+            yield ("fork", p, nxt)
+            live.append(nxt)
+            nxt += 1
+        elif r < 0.62:
+            s = live[int(rng.integers(len(live)))]
+            yield ("append_slots", s, int(rng.integers(1, 20)))
+        elif r < 0.8:
+            ids = [live[i] for i in rng.permutation(len(live))[:int(rng.integers(1, len(live) + 1))]]
+            yield ("batch", ids, [int(t) for t in rng.integers(0, vocab, size=len(ids))])
+        else:
+            s = live[int(rng.integers(len(live)))]
+            yield ("generate", s, [int(t) for t in rng.integers(0, vocab, size=int(rng.integers(1, 24)))])
+
+
+class Shadow:
+    """slot -> the token prefix whose last position's K/V the slot holds."""
+
+    def __init__(self):
+        self.slot = {}
+        self.stream = {}
+
+    def wrote(self, seq, slots):
+        toks = self.stream[seq]
+        base = len(toks) - len(slots)
+        for i, s in enumerate(slots):
+            self.slot[s] = tuple(toks[:base + i + 1])
+
+    def copied(self, pairs):
+        for src, dst in pairs:
+            for o in range(B):
+                if B * src + o in self.slot:
+                    self.slot[B * dst + o] = self.slot[B * src + o]
+
+
+_CODES = {-1: "invalid_arg", -5: "no_free_blocks", -6: "unknown_seq"}
+
+
+def error_kind(e):
+    if isinstance(e, AllocError):
+        return e.kind
+    code = getattr(e, "code", None)
+    if code in _CODES:
+        return _CODES[code]
+    raise e
+
+
+def replay(alloc, ops, shadow=None, check=None):
+    """Applies ops to ``alloc``; returns the observed results (for comparing
+    the model and the native allocator) and keeps ``shadow`` up to date."""
+    out = []
+    free = alloc.free_seq if hasattr(alloc, "free_seq") else alloc.free
+    for op in ops:
+        kind = op[0]
+        try:
+            if kind == "request":
+                _, s, prompt = op
+                n = alloc.create_cached(s, prompt)
+                if shadow is not None:
+                    shadow.stream[s] = list(prompt[:n])
+                    if check:
+                        check(alloc, s, prompt, n)
+                slots, pairs = alloc.append_tokens(s, prompt[n:])
+                if shadow is not None:
+                    shadow.stream[s] = list(prompt)
+                    shadow.copied(pairs)
+                    shadow.wrote(s, slots)
+                out.append((kind, n, slots, pairs))
+            elif kind == "free":
+                free(op[1])
+                out.append((kind,))
+            elif kind == "fork":
+                alloc.fork(op[1], op[2])
+                if shadow is not None:
+                    shadow.stream[op[2]] = list(shadow.stream[op[1]])
+                out.append((kind,))
+            elif kind == "append_slots":
+                slots, pairs = alloc.append_slots(op[1], op[2])
+                if shadow is not None:
+                    shadow.copied(pairs)
+                    shadow.stream[op[1]] += [None] * op[2]
+                    shadow.wrote(op[1], slots)
+                out.append((kind, slots, pairs))
+            elif kind == "batch":
+                ids, toks = op[1], op[2]
+                slots, pairs = alloc.batch_append_tokens(ids, toks)
+                if shadow is not None:
+                    shadow.copied(pairs)
+                    for s, t, sl in zip(ids, toks, slots):
+                        shadow.stream[s].append(t)
+                        shadow.wrote(s, [sl])
+                out.append((kind, slots, pairs))
+            elif kind == "generate":
+                slots, pairs = alloc.append_tokens(op[1], op[2])
+                if shadow is not None:
+                    shadow.copied(pairs)
+                    shadow.stream[op[1]] += op[2]
+                    shadow.wrote(op[1], slots)
+                out.append((kind, slots, pairs))
+        except Exception as e:             # the model's AllocError or the library's error
+            out.append((kind, "error", error_kind(e)))
+        if kind == "free" and shadow is not None:
+            shadow.stream.pop(op[1], None)
+    return out
+
+
+def _hit_check(shadow):
+    def check(m, s, prompt, n):
+        assert n % B == 0 and n <= max(len(prompt) - 1, 0)
+        for p in range(n):
+            slot = B * m.tables[s][p // B] + p % B
+            assert shadow.slot.get(slot) == tuple(prompt[:p + 1]), (s, p)
+    return check
+
+
+def _invariants(m):
+    for key, b in m.index.items():
+        assert m.key_of[b] == key
+        if len(key) > 1 + B:
+            assert key[:-B] in m.index                          # parents stay indexed
+    for b in m.evictable:
+        assert m.ref[b] == 0 and b in m.key_of
+    assert len(m.free) + len(m.evictable) + sum(1 for r in m.ref if r > 0) == m.num_blocks
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_hits_hold_the_right_content_under_pressure(seed):
+    m = PrefixCachingAllocatorModel(40, 12)
+    shadow = Shadow()
+    ops = list(_stream(seed))
+    res = replay(m, ops, shadow, _hit_check(shadow))
+    _invariants(m)
+    st = m.prefix_stats()
+    assert st["hit_blocks"] > 20 and st["evictions"] > 20, st       # the stream exercises both
+    assert any(r[1:2] == ("error",) for r in res)
+
+
+# ---- brute force with no eviction ---------------------------------------------------
+
+@pytest.mark.parametrize("seed", range(4))
+def test_hits_equal_brute_force_longest_shared_prefix(seed):
+    rng = np.random.default_rng(50 + seed)
+    m = PrefixCachingAllocatorModel(4096, 64)
+    systems = [list(rng.integers(0, 4, size=int(rng.integers(10, 60)))) for _ in range(4)]
+    done = []                                    # full token streams of finished requests
+    for r in range(120):
+        prompt = systems[int(rng.integers(4))] + list(rng.integers(0, 4, size=int(rng.integers(1, 50))))
+        if len(prompt) % B == 0:
+            prompt.append(1)                     # keep the bound from cutting a cached block
+        prompt = [int(t) for t in prompt]
+        best = 0
+        for stream in done:
+            full = len(stream) // B
+            k = 0
+            while k < min(full, (len(prompt) - 1) // B) and stream[B * k:B * k + B] == prompt[B * k:B * k + B]:
+                k += 1
+            best = max(best, k)
+        n = m.create_cached(r, prompt)
+        assert n == B * best, r
+        m.append_tokens(r, prompt[n:])
+        gen = [int(t) for t in rng.integers(0, 4, size=int(rng.integers(0, 40)))]
+        m.append_tokens(r, gen)
+        done.append(prompt + gen)
+        m.free_seq(r)
+    assert m.evictions == 0
+
+
+def test_refused_batch_changes_nothing():
+    # pool of 2: sequence 0 holds both blocks; in the batch its token fits
+    # in place but sequence 1 needs a block, so the whole batch is refused
+    m = PrefixCachingAllocatorModel(2, 8)
+    m.create(0)
+    m.create(1)
+    m.append_tokens(0, blk(1) + [2])
+    before = (dict(m.lens), m.prefix_stats(), m.stats(), list(m.tokens[0]))
+    with pytest.raises(AllocError) as e:
+        m.batch_append_tokens([0, 1], [4, 5])
+    assert e.value.kind == "no_free_blocks"
+    assert (dict(m.lens), m.prefix_stats(), m.stats(), list(m.tokens[0])) == before
