@@ -300,7 +300,8 @@ int pkv_seq_len(pkv_alloc* a, int64_t seq_id);
  *   cow_pairs_out  host int32 [2]: the {src, dst} copy to apply before
  *                  writing, when *n_cow_out == 1
  *   n_cow_out      host: 0 or 1
- * Fails with PKV_ERR_NO_FREE_BLOCKS when the free list is too short and with
+ * Fails with PKV_ERR_NO_FREE_BLOCKS when the free list (with prefix caching:
+ * free plus evictable blocks) is too short and with
  * PKV_ERR_INVALID_ARG when the table would exceed max_blocks_per_seq; then
  * nothing changes.
  */
@@ -324,6 +325,83 @@ int pkv_build_block_tables(pkv_alloc* a, const int64_t* seq_ids, int n, int max_
                            int32_t* tables_out, int32_t* lens_out);
 
 int pkv_alloc_stats(pkv_alloc* a, pkv_alloc_stats_t* out);
+
+/* ------------------------------------------------------------------------ */
+/* Prefix caching.                                                          */
+/*                                                                          */
+/* Pages: cached KV is looked up by its content - the token ids together    */
+/* with a model identifier - block by block from the start of the prompt,   */
+/* reusing every block that matches exactly and stopping at the first that  */
+/* does not ("KV Cache优化实战" §5.2-5.3; "企业官网建设流程全解析" §6.2);     */
+/* the cache is finite and eviction follows the prefix tree, not plain       */
+/* access order ("KV Cache优化实战" §5.3; "企业官网建设流程全解析" §6.3).     */
+/*                                                                          */
+/* Rules: only full blocks are indexed.  Block i of a tracked sequence is    */
+/* indexed when an append that names its tokens fills it, unless the same   */
+/* prefix (model key and tokens 0 .. 16i+15) is indexed already, and for    */
+/* i > 0 only if block i-1 of the sequence is the indexed block of the      */
+/* shorter prefix.  Sequences made by pkv_seq_create (with caching on),     */
+/* pkv_seq_create_cached or a fork of a tracked sequence are tracked; an    */
+/* append without tokens (pkv_seq_append_slots, pkv_batch_append_one)      */
+/* untracks a sequence for good.  An indexed block whose count drops to     */
+/* zero stays indexed and becomes evictable, stamped in release order.  A   */
+/* fresh block comes from the free list while it is not empty, otherwise   */
+/* the evictable block with the smallest stamp among those with no indexed  */
+/* child is evicted and reused.  Appends count free plus evictable blocks   */
+/* as capacity.  Block contents are the caller's: a hit means the K/V rows  */
+/* written for those positions are still in the pool.                       */
+/* ------------------------------------------------------------------------ */
+
+typedef struct {
+  int64_t cached_blocks;     /* indexed blocks (in use or evictable) */
+  int64_t evictable_blocks;  /* indexed blocks with count 0 */
+  int64_t lookup_blocks;     /* full blocks offered to lookups so far */
+  int64_t hit_blocks;        /* of those, blocks found in the cache */
+  int64_t evictions;         /* evictable blocks reused so far */
+} pkv_prefix_stats_t;
+
+/*
+ * pkv_prefix_cache_enable - turn prefix caching on for an idle allocator
+ * (no sequence, every block free).  model_key seeds the content hash, so
+ * caches of different models never match.  hash_bits (1..64) is how many
+ * bits of the hash pick a bucket: 64 in use; fewer force collisions, which
+ * cost comparisons but never a wrong match (entries are compared in full).
+ * PKV_ERR_INVALID_ARG if already enabled, not idle or hash_bits is out of
+ * range.
+ */
+int pkv_prefix_cache_enable(pkv_alloc* a, uint64_t model_key, int hash_bits);
+
+/*
+ * pkv_seq_create_cached - new tracked sequence that starts with the longest
+ * run of indexed blocks matching tokens[0 .. n_tokens) from the start, at
+ * most (n_tokens - 1) / 16 blocks (the last prompt token is always
+ * computed).  Each matched block gains a reference.
+ *   tokens        host int32 [n_tokens]: the prompt's token ids
+ *   n_cached_out  host: the new sequence's length, 16 x matched blocks; the
+ *                 caller appends tokens[*n_cached_out ..] with
+ *                 pkv_seq_append_tokens and writes their K/V rows
+ * PKV_ERR_INVALID_ARG if caching is off or the id is live.
+ */
+int pkv_seq_create_cached(pkv_alloc* a, int64_t seq_id, const int32_t* tokens, int n_tokens,
+                          int* n_cached_out);
+
+/*
+ * pkv_seq_append_tokens - pkv_seq_append_slots for positions whose token ids
+ * are known (tokens: host int32 [n_tokens]); on a tracked sequence, indexes
+ * every block the append fills.  Same outputs and errors.
+ */
+int pkv_seq_append_tokens(pkv_alloc* a, int64_t seq_id, const int32_t* tokens, int n_tokens,
+                          int64_t* slots_out, int32_t* cow_pairs_out, int* n_cow_out);
+
+/*
+ * pkv_batch_append_tokens - pkv_batch_append_one with the new token of each
+ * sequence (tokens: host int32 [n]), indexing the blocks it fills; in order,
+ * all or nothing.
+ */
+int pkv_batch_append_tokens(pkv_alloc* a, const int64_t* seq_ids, const int32_t* tokens, int n,
+                            int64_t* slots_out, int32_t* cow_pairs_out, int* n_cow_out);
+
+int pkv_prefix_stats(pkv_alloc* a, pkv_prefix_stats_t* out);
 
 #ifdef __cplusplus
 }

@@ -230,7 +230,8 @@ def paged_attention_merge_partials(out: torch.Tensor, context_lens: torch.Tensor
 
 
 class BlockAllocator:
-    """Host block allocator (refcounts, fork, copy-on-write planning)."""
+    """Host block allocator (refcounts, fork, copy-on-write planning and,
+    once ``enable_prefix_cache`` is called, prefix caching)."""
 
     def __init__(self, num_blocks: int, max_blocks_per_seq: int):
         self._lib = _lib.lib()
@@ -282,6 +283,50 @@ class BlockAllocator:
         _check(self._lib.pkv_batch_append_one(self._h, ids, n, slots, pairs, ctypes.byref(ncow)),
                "pkv_batch_append_one")
         return list(slots[:n]), [(pairs[2 * i], pairs[2 * i + 1]) for i in range(ncow.value)]
+
+    # -- prefix caching --------------------------------------------------------
+    def enable_prefix_cache(self, model_key: int = 0, hash_bits: int = 64) -> None:
+        _check(self._lib.pkv_prefix_cache_enable(self._h, int(model_key) & (2 ** 64 - 1), hash_bits),
+               "pkv_prefix_cache_enable")
+
+    def create_cached(self, seq_id: int, tokens: Sequence[int]) -> int:
+        """New sequence holding the longest cached prefix of ``tokens``; returns
+        its length (the number of prompt tokens whose K/V is already cached)."""
+        n = len(tokens)
+        toks = (ctypes.c_int32 * max(n, 1))(*[int(t) for t in tokens])
+        got = ctypes.c_int()
+        _check(self._lib.pkv_seq_create_cached(self._h, seq_id, toks, n, ctypes.byref(got)),
+               "pkv_seq_create_cached")
+        return got.value
+
+    def append_tokens(self, seq_id: int, tokens: Sequence[int]) -> Tuple[List[int], List[Tuple[int, int]]]:
+        n = len(tokens)
+        toks = (ctypes.c_int32 * max(n, 1))(*[int(t) for t in tokens])
+        slots = (ctypes.c_int64 * max(n, 1))()
+        pair = (ctypes.c_int32 * 2)()
+        ncow = ctypes.c_int()
+        _check(self._lib.pkv_seq_append_tokens(self._h, seq_id, toks, n, slots, pair, ctypes.byref(ncow)),
+               "pkv_seq_append_tokens")
+        return list(slots[:n]), ([(pair[0], pair[1])] if ncow.value else [])
+
+    def batch_append_tokens(self, seq_ids: Sequence[int], tokens: Sequence[int]
+                            ) -> Tuple[List[int], List[Tuple[int, int]]]:
+        n = len(seq_ids)
+        if len(tokens) != n:
+            raise ValueError("one token per sequence")
+        ids = (ctypes.c_int64 * max(n, 1))(*seq_ids)
+        toks = (ctypes.c_int32 * max(n, 1))(*[int(t) for t in tokens])
+        slots = (ctypes.c_int64 * max(n, 1))()
+        pairs = (ctypes.c_int32 * (2 * max(n, 1)))()
+        ncow = ctypes.c_int()
+        _check(self._lib.pkv_batch_append_tokens(self._h, ids, toks, n, slots, pairs, ctypes.byref(ncow)),
+               "pkv_batch_append_tokens")
+        return list(slots[:n]), [(pairs[2 * i], pairs[2 * i + 1]) for i in range(ncow.value)]
+
+    def prefix_stats(self) -> dict:
+        st = _lib.PrefixStats()
+        _check(self._lib.pkv_prefix_stats(self._h, ctypes.byref(st)), "pkv_prefix_stats")
+        return {name: getattr(st, name) for name, _ in _lib.PrefixStats._fields_}
 
     def block_tables(self, seq_ids: Sequence[int], max_blocks: Optional[int] = None,
                      out_tables: Optional[torch.Tensor] = None, out_lens: Optional[torch.Tensor] = None):

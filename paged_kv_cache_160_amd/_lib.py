@@ -29,6 +29,16 @@ class AllocStats(ctypes.Structure):
     ]
 
 
+class PrefixStats(ctypes.Structure):
+    _fields_ = [
+        ("cached_blocks", c_int64),
+        ("evictable_blocks", c_int64),
+        ("lookup_blocks", c_int64),
+        ("hit_blocks", c_int64),
+        ("evictions", c_int64),
+    ]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "pkv_abi_version": (c_int, []),
@@ -65,6 +75,11 @@ SIGNATURES = {
     "pkv_batch_append_one": (c_int, [c_void_p, P_i64, c_int, P_i64, P_i32, P_int]),
     "pkv_build_block_tables": (c_int, [c_void_p, P_i64, c_int, c_int, P_i32, P_i32]),
     "pkv_alloc_stats": (c_int, [c_void_p, ctypes.POINTER(AllocStats)]),
+    "pkv_prefix_cache_enable": (c_int, [c_void_p, ctypes.c_uint64, c_int]),
+    "pkv_seq_create_cached": (c_int, [c_void_p, c_int64, P_i32, c_int, P_int]),
+    "pkv_seq_append_tokens": (c_int, [c_void_p, c_int64, P_i32, c_int, P_i64, P_i32, P_int]),
+    "pkv_batch_append_tokens": (c_int, [c_void_p, P_i64, P_i32, c_int, P_i64, P_i32, P_int]),
+    "pkv_prefix_stats": (c_int, [c_void_p, ctypes.POINTER(PrefixStats)]),
 }
 
 _lib = None
