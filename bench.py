@@ -71,6 +71,8 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="write the step's rows with kv_cache_append, then attend (default: the write is fused "
                          "into the attention kernel)")
+    ap.add_argument("--row", choices=["decode", "prefix"], default="decode",
+                    help="decode (default): the hot path; prefix: host prefix-cache replay of agent sessions")
     ap.add_argument("--one-call", action="store_true",
                     help="use the one-call paged_attention_decode_append (events then bracket both launches)")
     return ap.parse_args()
@@ -146,6 +148,10 @@ def main():
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(sharding by sequence or KV head needs no exchange; see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+
+    if args.row == "prefix":
+        run_prefix_row(args)
+        return
 
     import numpy as np
     import torch
@@ -460,6 +466,151 @@ def cpu_baseline(w, budget_s: float):
                    f"{w.name}; fp64 numpy; rows generated and dequantised before timing; "
                    f"{busy:.2f} cores busy on average, {allowed} allowed, BLAS threads {blas}"),
     }
+
+
+# ---- prefix caching row --------------------------------------------------------------
+
+PREFIX_SHAPE = dict(n_sessions=32, turns=11, system_len=1000, user_len=400, output_len=100, vocab=32000)
+
+
+def run_prefix_row(args):
+    """Host prefix cache on agent sessions ("KV Cache优化实战" §5.1, §5.3).
+
+    32 sessions on one 1000-token system prompt; every turn appends 400 user
+    tokens to the session's history and generates 100, so the eleventh turn's
+    prompt is 6400 tokens of which 5900 were seen the turn before (the pages'
+    log: 6000-token requests, 5500 seen before).  Each turn: every session's
+    request goes through the cache (lookup, then the missed prompt tokens are
+    appended and indexed), then 100 decode steps append one token to every
+    session at once; the turn's requests then finish.  Times are of the
+    library calls alone (token buffers built beforehand).  The same stream is
+    replayed with 8 tokens of per-request content after the first block (an
+    unstable template, §5.3) for its hit fraction.  The pool holds 1.1x the
+    last turn's live blocks."""
+    import ctypes
+    import numpy as np
+
+    import paged_kv_cache_160_amd as pkv
+    import workloads as wl
+    from paged_kv_cache_160_amd import _lib
+
+    lib = _lib.lib()
+    res = {}
+    for label, dyn in (("stable", 0), ("dynamic_head", 8)):
+        turns = wl.agent_sessions(2024, dynamic_head=dyn, **PREFIX_SHAPE)
+        last = max(len(t.prompt) + len(t.output) for t in turns)
+        nb = int(1.1 * PREFIX_SHAPE["n_sessions"] * -(-last // 16))
+        mbps = -(-last // 16) + 1
+        a = pkv.BlockAllocator(nb, mbps)
+        a.enable_prefix_cache(model_key=1)
+        h = a._h
+        slots = np.empty(last, np.int64)
+        pair = np.empty(2, np.int32)
+        bslots = np.empty(PREFIX_SHAPE["n_sessions"], np.int64)
+        bpairs = np.empty(2 * PREFIX_SHAPE["n_sessions"], np.int32)
+        ncow = ctypes.c_int()
+        got = ctypes.c_int()
+        P32, P64 = _lib.P_i32, _lib.P_i64
+        row = np.empty(PREFIX_SHAPE["n_sessions"], np.int32)
+        p_got, p_ncow = ctypes.byref(got), ctypes.byref(ncow)
+        p_slots, p_pair = slots.ctypes.data_as(P64), pair.ctypes.data_as(P32)
+        t_lookup = t_append = t_step = 0.0
+        n_req = n_steps = 0
+        prompt_tok = hit_tok = 0
+        late_prompt = late_hit = 0
+        for turn in range(PREFIX_SHAPE["turns"]):
+            group = [t for t in turns if t.turn == turn]
+            ids = np.array([1000 * turn + t.session for t in group], np.int64)
+            prompts = [np.asarray(t.prompt, np.int32) for t in group]
+            outs = np.stack([np.asarray(t.output, np.int32) for t in group], axis=1)   # [steps, sessions]
+            # ctypes pointers are built before timing: making one costs more
+            # than a whole batch step of the library
+            p_ids, p_row, p_bs, p_bp = (ids.ctypes.data_as(P64), row.ctypes.data_as(P32),
+                                        bslots.ctypes.data_as(P64), bpairs.ctypes.data_as(P32))
+            p_prompts = [p.ctypes.data_as(P32) for p in prompts]
+            for sid, p, pp in zip(ids, prompts, p_prompts):
+                t0 = time.perf_counter()
+                rc = lib.pkv_seq_create_cached(h, int(sid), pp, p.size, p_got)
+                t1 = time.perf_counter()
+                n = got.value
+                p_rest = ctypes.cast(ctypes.addressof(pp.contents) + 4 * n, P32)
+                t2 = time.perf_counter()
+                rc |= lib.pkv_seq_append_tokens(h, int(sid), p_rest, p.size - n, p_slots, p_pair, p_ncow)
+                t3 = time.perf_counter()
+                if rc:
+                    raise RuntimeError(f"allocator error {rc}")
+                t_lookup += t1 - t0
+                t_append += t3 - t2
+                n_req += 1
+                prompt_tok += p.size
+                hit_tok += n
+                if turn == PREFIX_SHAPE["turns"] - 1:
+                    late_prompt += p.size
+                    late_hit += n
+            for j in range(outs.shape[0]):
+                row[:] = outs[j]
+                t0 = time.perf_counter()
+                rc = lib.pkv_batch_append_tokens(h, p_ids, p_row, ids.size, p_bs, p_bp, p_ncow)
+                t_step += time.perf_counter() - t0
+                if rc:
+                    raise RuntimeError(f"allocator error {rc}")
+                n_steps += 1
+            for sid in ids:
+                a.free(int(sid))
+        st = a.prefix_stats()
+        res[label] = {
+            "hit_fraction_all_turns": hit_tok / prompt_tok,
+            "hit_fraction_last_turn": late_hit / late_prompt,
+            "last_turn_prompt_tokens": late_prompt // len(ids),
+            "last_turn_cached_tokens": late_hit // len(ids),
+            "lookup_us_per_request": 1e6 * t_lookup / n_req,
+            "append_us_per_request": 1e6 * t_append / n_req,
+            "batch_step_us": 1e6 * t_step / n_steps,
+            "pool_blocks": nb, **st,
+        }
+        log(f"[prefix] {label}: {json.dumps(res[label])}")
+    s = res["stable"]
+    rec = {
+        "metric": "prefix cache: fraction of prompt tokens served from cache (agent sessions, last turn)",
+        "value": s["hit_fraction_last_turn"], "unit": "fraction", "higher_is_better": True,
+        "n_gpus": 0, "data": "synthetic", "dtype": "int32 token ids",
+        "config": {"workload": "agent sessions 32 x 11 turns, system 1000 + 400 user + 100 out per turn",
+                   **PREFIX_SHAPE},
+        "stable": s, "dynamic_head": res["dynamic_head"],
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = prefix_cpu_baseline(args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def prefix_cpu_baseline(budget_s: float):
+    """The prefix-cache model (test infrastructure) replaying the first turns
+    of the same stream until the budget is spent: requests per second."""
+    import workloads as wl
+    from oracle.allocator import PrefixCachingAllocatorModel
+
+    turns = wl.agent_sessions(2024, dynamic_head=0, **PREFIX_SHAPE)
+    last = max(len(t.prompt) + len(t.output) for t in turns)
+    m = PrefixCachingAllocatorModel(int(1.1 * PREFIX_SHAPE["n_sessions"] * -(-last // 16)), -(-last // 16) + 1,
+                                    model_key=1)
+    t0 = time.perf_counter()
+    n_req = 0
+    for turn in range(PREFIX_SHAPE["turns"]):
+        group = [t for t in turns if t.turn == turn]
+        ids = [1000 * turn + t.session for t in group]
+        for sid, t in zip(ids, group):
+            n = m.create_cached(sid, t.prompt)
+            m.append_tokens(sid, t.prompt[n:])
+            n_req += 1
+        for j in range(len(group[0].output)):
+            m.batch_append_tokens(ids, [t.output[j] for t in group])
+        for sid in ids:
+            m.free_seq(sid)
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    wall = time.perf_counter() - t0
+    return {"value": n_req / wall, "unit": "requests/s (with their decode steps)", "cores": 1, "kind": "oracle",
+            "sample": f"first {turn + 1} turns ({n_req} requests) of the same stream, pure Python, one thread"}
 
 
 if __name__ == "__main__":

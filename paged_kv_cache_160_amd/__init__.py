@@ -13,6 +13,7 @@ import ctypes
 import math
 from typing import Iterable, List, Optional, Sequence, Tuple
 
+import numpy as np
 import torch
 
 from . import _lib
@@ -229,6 +230,11 @@ def paged_attention_merge_partials(out: torch.Tensor, context_lens: torch.Tensor
     return out
 
 
+def _int32_array(tokens) -> np.ndarray:
+    arr = np.ascontiguousarray(tokens, dtype=np.int32).reshape(-1)
+    return arr if arr.size else np.zeros(1, np.int32)[:0]
+
+
 class BlockAllocator:
     """Host block allocator (refcounts, fork, copy-on-write planning and,
     once ``enable_prefix_cache`` is called, prefix caching)."""
@@ -289,24 +295,24 @@ class BlockAllocator:
         _check(self._lib.pkv_prefix_cache_enable(self._h, int(model_key) & (2 ** 64 - 1), hash_bits),
                "pkv_prefix_cache_enable")
 
-    def create_cached(self, seq_id: int, tokens: Sequence[int]) -> int:
-        """New sequence holding the longest cached prefix of ``tokens``; returns
-        its length (the number of prompt tokens whose K/V is already cached)."""
-        n = len(tokens)
-        toks = (ctypes.c_int32 * max(n, 1))(*[int(t) for t in tokens])
+    def create_cached(self, seq_id: int, tokens) -> int:
+        """New sequence holding the longest cached prefix of ``tokens`` (a
+        sequence of ints or an int32 array); returns its length (the number of
+        prompt tokens whose K/V is already cached)."""
+        toks = _int32_array(tokens)
         got = ctypes.c_int()
-        _check(self._lib.pkv_seq_create_cached(self._h, seq_id, toks, n, ctypes.byref(got)),
-               "pkv_seq_create_cached")
+        _check(self._lib.pkv_seq_create_cached(self._h, seq_id, toks.ctypes.data_as(_lib.P_i32), toks.size,
+                                               ctypes.byref(got)), "pkv_seq_create_cached")
         return got.value
 
-    def append_tokens(self, seq_id: int, tokens: Sequence[int]) -> Tuple[List[int], List[Tuple[int, int]]]:
-        n = len(tokens)
-        toks = (ctypes.c_int32 * max(n, 1))(*[int(t) for t in tokens])
+    def append_tokens(self, seq_id: int, tokens) -> Tuple[List[int], List[Tuple[int, int]]]:
+        toks = _int32_array(tokens)
+        n = int(toks.size)
         slots = (ctypes.c_int64 * max(n, 1))()
         pair = (ctypes.c_int32 * 2)()
         ncow = ctypes.c_int()
-        _check(self._lib.pkv_seq_append_tokens(self._h, seq_id, toks, n, slots, pair, ctypes.byref(ncow)),
-               "pkv_seq_append_tokens")
+        _check(self._lib.pkv_seq_append_tokens(self._h, seq_id, toks.ctypes.data_as(_lib.P_i32), n, slots, pair,
+                                               ctypes.byref(ncow)), "pkv_seq_append_tokens")
         return list(slots[:n]), ([(pair[0], pair[1])] if ncow.value else [])
 
     def batch_append_tokens(self, seq_ids: Sequence[int], tokens: Sequence[int]

@@ -24,6 +24,7 @@ The five workloads follow the shapes of the pages' examples:
 """
 from __future__ import annotations
 
+import hashlib
 import math
 from dataclasses import dataclass, field
 from typing import List, Optional, Tuple
@@ -41,6 +42,9 @@ _TAG_PLACE = 5
 _TAG_CHURN = 6
 _TAG_PREFIX_K = 7
 _TAG_PREFIX_V = 8
+_TAG_TOKENS = 9
+_TAG_CTX_K = 10
+_TAG_CTX_V = 11
 
 DTYPES = ("f32", "f16", "bf16", "fp8_e4m3")
 
@@ -270,3 +274,68 @@ def setup_ops(w: Workload, share_prefix: bool = True) -> list:
     for b in range(w.num_seqs):
         ops.append(("append", b, w.context_lens[b]))
     return ops
+
+
+# ----------------------------------------------------------------------------
+# Token streams (prefix caching)
+# ----------------------------------------------------------------------------
+
+def token_digests(seed: int, tokens) -> List[int]:
+    """One 63-bit digest per position: position t's digest stands for tokens
+    0..t, chained (blake2b of the previous digest and the token).  Used only
+    to seed per-position rows, so that equal prefixes get equal K/V rows the
+    way a model's would; it is not the cache's own hash."""
+    out = []
+    h = hashlib.blake2b(f"{int(seed)}".encode(), digest_size=8).digest()
+    for t in tokens:
+        h = hashlib.blake2b(h + int(t).to_bytes(4, "little", signed=True), digest_size=8).digest()
+        out.append(int.from_bytes(h, "little") >> 1)
+    return out
+
+
+def context_rows(seed: int, tokens, start: int, stop: int, num_kv_heads: int, head_dim: int,
+                 which: str, dtype: str) -> np.ndarray:
+    """K or V rows [stop-start][Hkv][D] (float32, values in ``dtype``) for
+    positions start..stop-1 of a token stream: each position's row is drawn
+    from a stream keyed by the digest of the prefix it ends."""
+    tag = _TAG_CTX_K if which == "k" else _TAG_CTX_V
+    digs = token_digests(seed, list(tokens)[:stop])
+    rows = np.empty((max(stop - start, 0), num_kv_heads, head_dim), np.float32)
+    for i, t in enumerate(range(start, stop)):
+        rows[i] = _normal(_rng(seed, tag, digs[t]), (num_kv_heads, head_dim))
+    return round_to_dtype(rows, dtype)
+
+
+@dataclass
+class Turn:
+    session: int
+    turn: int
+    prompt: List[int]          # the request's full prompt
+    output: List[int]          # the tokens the turn generates
+
+
+def agent_sessions(seed: int, n_sessions: int, turns: int, system_len: int, user_len: int,
+                   output_len: int, vocab: int = 32000, dynamic_head: int = 0) -> List[Turn]:
+    """Multi-turn sessions in the shape of "KV Cache优化实战" §5.1: every
+    session starts from one fixed system prompt; each turn's prompt is the
+    previous turn's prompt and output plus ``user_len`` new tokens, so
+    almost all of a late turn's prompt was seen before.  ``dynamic_head``
+    tokens of per-request content (a time stamp, a user id) placed right
+    after the first system block reproduce the unstable template of
+    §5.3.  Turns are listed round-robin over sessions, turn by turn."""
+    rng = _rng(seed, _TAG_TOKENS)
+    system = [int(t) for t in rng.integers(0, vocab, size=system_len)]
+    history = [list(system) for _ in range(n_sessions)]
+    out: List[Turn] = []
+    for turn in range(turns):
+        for s in range(n_sessions):
+            user = [int(t) for t in rng.integers(0, vocab, size=user_len)]
+            prompt = history[s] + user
+            if dynamic_head:
+                head = [int(t) for t in rng.integers(0, vocab, size=dynamic_head)]
+                cut = min(BLOCK_TOKENS, len(prompt))
+                prompt = prompt[:cut] + head + prompt[cut:]
+            gen = [int(t) for t in rng.integers(0, vocab, size=output_len)]
+            out.append(Turn(s, turn, prompt, gen))
+            history[s] = history[s] + user + gen
+    return out
