@@ -5,17 +5,19 @@ wrong fp8 exponent bias, a scale from the mean instead of the max, an
 off-by-one position, a reversed free order, a copy-on-write that skips the
 copy, a prefix cache that evicts by plain recency, keys a block by its own
 tokens only, lets a lookup cover the last prompt token or forgets released
-blocks - must make at least one of the pins fail.  This shows the pins are
+blocks, a prefill mask that hides the diagonal or a chunk placed at the
+start of the sequence - must make at least one of the pins fail.  This shows the pins are
 sharp enough to catch the mistakes they are meant to catch."""
 import numpy as np
 import pytest
 
 from oracle import allocator as alloc_mod
-from oracle import attention, cache, fp8_e4m3
+from oracle import attention, cache, fp8_e4m3, prefill
 from oracle.allocator import BLOCK_TOKENS as BLOCK
 from tests import test_oracle_allocator as pins_alloc
 from tests import test_oracle_attention as pins_attn
 from tests import test_oracle_fp8 as pins_fp8
+from tests import test_oracle_prefill as pins_prefill
 from tests import test_oracle_prefix_cache as pins_prefix
 
 
@@ -189,3 +191,23 @@ def test_forgetting_released_blocks_is_caught(monkeypatch):
             self.free.append(blk)
     monkeypatch.setattr(PCM, "_release", forget)
     _fails(pins_prefix.test_hits_equal_brute_force_longest_shared_prefix, 0)
+
+
+# ---- prefill mutants --------------------------------------------------------------------
+
+def _prefill_with(q, K, V, scale, first_key_hidden=False, chunk_at_start=False):
+    q = np.asarray(q, np.float64)
+    n, L = q.shape[0], K.shape[0]
+    out = np.zeros(q.shape)
+    for i in range(n):
+        p = i if chunk_at_start else L - n + i
+        stop = p if first_key_hidden and p > 0 else p + 1       # k < p instead of k <= p
+        out[i] = attention.attend(q[i], K[:stop], V[:stop], scale)
+    return out
+
+
+@pytest.mark.parametrize("kw", [{"first_key_hidden": True}, {"chunk_at_start": True}],
+                         ids=["mask-hides-diagonal", "chunk-at-start"])
+def test_prefill_mutants_are_caught(monkeypatch, kw):
+    monkeypatch.setattr(prefill, "prefill_rows", lambda q, K, V, s: _prefill_with(q, K, V, s, **kw))
+    _fails(pins_prefill.test_matches_torch_sdpa_with_shifted_causal_mask, 4, 2, 64, 40, 7)

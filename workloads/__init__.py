@@ -45,6 +45,7 @@ _TAG_PREFIX_V = 8
 _TAG_TOKENS = 9
 _TAG_CTX_K = 10
 _TAG_CTX_V = 11
+_TAG_CHUNK = 12
 
 DTYPES = ("f32", "f16", "bf16", "fp8_e4m3")
 
@@ -274,6 +275,25 @@ def setup_ops(w: Workload, share_prefix: bool = True) -> list:
     for b in range(w.num_seqs):
         ops.append(("append", b, w.context_lens[b]))
     return ops
+
+
+def chunk_workload(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, cached: List[int],
+                   chunk: List[int], dtype: str = "bf16", cache_dtype: Optional[str] = None,
+                   q_dtype: Optional[str] = None, seed: int = 0, extra_blocks: int = 0) -> Workload:
+    """A chunked-prefill batch: sequence b holds ``cached[b]`` tokens and
+    appends a chunk of ``chunk[b]`` more; context_lens are the totals."""
+    lens = [int(c) + int(n) for c, n in zip(cached, chunk)]
+    w = custom_workload(num_seqs, num_q_heads, num_kv_heads, head_dim, lens, dtype=dtype,
+                        cache_dtype=cache_dtype, q_dtype=q_dtype, seed=seed, extra_blocks=extra_blocks)
+    w.extra["chunk"] = [int(n) for n in chunk]
+    return w
+
+
+def chunk_queries(w: Workload, step: int = 0) -> np.ndarray:
+    """q [T][Hq][D] for the chunks back to back (float32, values in ``w.q_dtype``)."""
+    T = int(sum(w.extra["chunk"]))
+    q = _normal(_rng(w.seed, _TAG_CHUNK, step), (T, w.num_q_heads, w.head_dim))
+    return round_to_dtype(q, w.q_dtype)
 
 
 # ----------------------------------------------------------------------------
