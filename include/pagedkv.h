@@ -42,6 +42,7 @@ extern "C" {
 #define PKV_BLOCK_SIZE 16   /* tokens per physical block ("KV Cache 和 vLLM" §3.1) */
 #define PKV_ABI_VERSION 1
 #define PKV_MAX_PARTITION_TOKENS 32768   /* largest decode partition (tokens) */
+#define PKV_MAX_PREFILL_CONTEXT 32768    /* longest context a prefill call reads (tokens) */
 
 typedef enum {
   PKV_F32 = 0,
@@ -242,6 +243,43 @@ int paged_attention_merge_partials(void* out, const int32_t* context_lens,
                                    int max_blocks_per_seq, int max_context_len, pkv_dtype q_dtype,
                                    int partition_size, void* workspace, size_t workspace_bytes,
                                    void* stream);
+
+/*
+ * paged_attention_prefill - chunked prefill: each sequence's chunk of new
+ * tokens attends over the sequence's cached K/V and causally over itself.
+ *
+ * Pages: in prefill every prompt token is processed at once and attends to
+ * the positions before it and to itself ("KV Cache 和 vLLM" §1.1;
+ * "企业官网建设流程全解析" §3.1-3.2); K/V of tokens already cached is reused
+ * rather than recomputed ("KV Cache优化实战" §5.2).
+ *
+ * The chunk's own K/V rows must already be in the pool (kv_cache_append
+ * takes any number of tokens; the allocator's append gives their slots).
+ *   out            device [num_tokens][num_q_heads][head_dim], q dtype
+ *   q              device [num_tokens][num_q_heads][head_dim]: the chunks back
+ *                  to back
+ *   query_start    device int32 [num_seqs + 1], query_start[0] = 0,
+ *                  non-decreasing, query_start[num_seqs] <= num_tokens:
+ *                  sequence b's chunk is q rows query_start[b] .. [b+1]-1
+ *   context_lens   device int32 [num_seqs]: cached tokens including the
+ *                  chunk, so chunk row i sits at position
+ *                  context_lens[b] - n_b + i and attends to positions 0 .. it
+ *   block_tables, pools, scales, scale: as paged_attention_decode
+ *   max_query_len  host: >= every chunk length (sizes the launch; a longer
+ *                  chunk, or one outside q, is skipped and its rows untouched)
+ *   max_context_len host: >= every context length, at most
+ *                  PKV_MAX_PREFILL_CONTEXT
+ * Dtype pairs (q / cache): f16/f16, bf16/bf16, bf16 or f16 / fp8_e4m3; f32
+ * and other head dims give PKV_ERR_UNSUPPORTED.  A sequence with an empty
+ * chunk is skipped; with context_lens[b] = 0 its chunk rows are zero.  No
+ * workspace; nothing is allocated; asynchronous on stream.
+ */
+int paged_attention_prefill(void* out, const void* q, const void* k_pool, const void* v_pool,
+                            const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                            const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+                            int num_tokens, int num_q_heads, int num_kv_heads, int head_dim, int num_blocks,
+                            int max_blocks_per_seq, int max_context_len, int max_query_len, float scale,
+                            pkv_dtype q_dtype, pkv_dtype cache_dtype, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Host block allocator.  Opaque handle, not thread-safe, no device memory.  */

@@ -159,6 +159,33 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
     return out
 
 
+def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                            block_tables: torch.Tensor, context_lens: torch.Tensor, query_start: torch.Tensor,
+                            max_context_len: int, max_query_len: int, scale: Optional[float] = None,
+                            k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
+                            stream=None) -> torch.Tensor:
+    """Chunked prefill: ``out[t, h]`` for chunk row t of sequence b (rows
+    ``query_start[b] .. query_start[b+1]-1``) attends over the first
+    ``context_lens[b] - n_b + i + 1`` cached tokens, i = t - query_start[b]."""
+    nb, hkv, d = _pool_geometry(k_pool)
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must be [T, Hq, D] of one dtype")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or query_start.dtype != torch.int32:
+        raise ValueError("block_tables, context_lens and query_start must be int32")
+    B = int(context_lens.numel())
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or query_start.numel() != B + 1:
+        raise ValueError("block_tables must be [B, max_blocks], query_start [B + 1]")
+    T, hq = int(q.shape[0]), int(q.shape[1])
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    _check(_lib.lib().paged_attention_prefill(
+        _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
+        _ptr(context_lens), _ptr(query_start), B, T, hq, hkv, d, nb, int(block_tables.shape[1]),
+        int(max_context_len), int(max_query_len), float(scale), dtype_code(q.dtype), dtype_code(k_pool.dtype),
+        _stream(stream)), "paged_attention_prefill")
+    return out
+
+
 def _decode_append_call(fn_name, out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables,
                         context_lens, max_context_len, scale, k_scale, v_scale, partition_size, workspace,
                         stream):

@@ -64,6 +64,9 @@ SIGNATURES = {
                                                        c_size_t, c_void_p]),
     "paged_attention_merge_partials": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
                                                c_int, c_int, c_void_p, c_size_t, c_void_p]),
+    "paged_attention_prefill": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
+                                        c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
+                                        c_int, c_float, c_int, c_int, c_void_p]),
     "pkv_alloc_create": (c_void_p, [c_int, c_int]),
     "pkv_alloc_destroy": (None, [c_void_p]),
     "pkv_alloc_set_free_order": (c_int, [c_void_p, P_i32, c_int]),

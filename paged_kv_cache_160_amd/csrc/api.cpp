@@ -304,4 +304,52 @@ int paged_attention_merge_partials(void* out, const int32_t* context_lens, int n
   return pkv::launch_decode(a, static_cast<hipStream_t>(stream), pkv::kStageMerge);
 }
 
+int paged_attention_prefill(void* out, const void* q, const void* k_pool, const void* v_pool,
+                            const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                            const int32_t* context_lens, const int32_t* query_start, int num_seqs, int num_tokens,
+                            int num_q_heads, int num_kv_heads, int head_dim, int num_blocks, int max_blocks_per_seq,
+                            int max_context_len, int max_query_len, float scale, pkv_dtype q_dtype,
+                            pkv_dtype cache_dtype, void* stream) {
+  if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
+  if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len))
+    return PKV_ERR_INVALID_ARG;
+  if (num_tokens < 0 || max_query_len < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+    return PKV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBlock)
+    return PKV_ERR_INVALID_ARG;
+  if (max_query_len > max_context_len || max_query_len > num_tokens) return PKV_ERR_INVALID_ARG;
+  if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
+  if (q_dtype == PKV_F32 || !decode_pair_ok(q_dtype, cache_dtype)) return PKV_ERR_UNSUPPORTED;
+  if (max_context_len > PKV_MAX_PREFILL_CONTEXT) return PKV_ERR_UNSUPPORTED;
+  if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
+    return PKV_ERR_INVALID_ARG;
+  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PKV_ERR_INVALID_ARG;
+
+  pkv::PrefillArgs a{};
+  a.out = out;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.k_scale = k_scale;
+  a.v_scale = v_scale;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.query_start = query_start;
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.head_dim = head_dim;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.max_query_len = max_query_len;
+  a.scale = scale;
+  a.q_dtype = q_dtype;
+  a.cache_dtype = cache_dtype;
+  return pkv::launch_prefill(a, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

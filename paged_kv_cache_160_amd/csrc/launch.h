@@ -53,6 +53,25 @@ enum DecodeStages { kStageAttend = 1, kStageMerge = 2, kStageBoth = 3 };
 
 int launch_decode(const DecodeArgs& a, hipStream_t stream, int stages);
 
+struct PrefillArgs {
+  void* out;                   // [num_tokens][num_q_heads][head_dim], q dtype
+  const void* q;               // [num_tokens][num_q_heads][head_dim]
+  const void* k_pool;
+  const void* v_pool;
+  const float* k_scale;
+  const float* v_scale;
+  const int32_t* block_tables;
+  const int32_t* context_lens; // [num_seqs]: cached length after the chunk's append
+  const int32_t* query_start;  // [num_seqs + 1]: chunk b = q rows query_start[b] .. query_start[b+1]-1
+  int num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim;
+  int num_blocks, max_blocks_per_seq, max_context_len, max_query_len;
+  float scale;
+  pkv_dtype q_dtype, cache_dtype;
+  int tiles_per_seq;           // set by the launcher
+};
+
+int launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
 // Automatic partition length for a decode launch (tokens, multiple of 16).
 int choose_partition_size(int num_seqs, int num_kv_heads, int max_context_len);
 

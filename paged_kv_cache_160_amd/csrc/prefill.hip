@@ -1,0 +1,471 @@
+// Chunked prefill attention over the paged cache for gfx950: a chunk of new
+// tokens of each sequence attends over the sequence's cached K/V (read
+// through the block table) and causally over its own tokens.
+//
+// Pages: in prefill every prompt token is processed at once, each position
+// attending to itself and the positions before it ("KV Cache 和 vLLM" §1.1;
+// "企业官网建设流程全解析" §3.1-3.2); the K/V of tokens already cached is
+// reused rather than recomputed ("KV Cache优化实战" §5.2); logical blocks map
+// to physical blocks through the block table ("KV Cache 和 vLLM" §3.2);
+// several query heads share one KV head ("企业官网建设流程全解析" §2.2).
+//
+// Unlike decode this is a dense contraction (each K/V element meets many
+// queries), so it is built for the matrix cores:
+//  * Workgroup = 4 waves owning 256 query rows of one (sequence, KV head);
+//    a row is a (chunk position, head of the GQA group) pair, so the whole
+//    group shares every K/V tile.  Each wave owns CTILES tiles of 16 rows.
+//  * K and V stream through LDS in stages of 64 keys (4 paged blocks): the
+//    workgroup loads a stage with 16-byte loads while computing the previous
+//    one from LDS; fp8 codes become 16-bit values exactly on the way in and
+//    their per-token scales go to LDS beside them.
+//      S^T = K (16 keys x D) * Q^T (D x 16 rows)       [16x16x32 MFMA]
+//      O  += P (16 rows x 32 keys) * V (32 keys x 16 d) [16x16x32 MFMA]
+//    The S^T accumulator (lane = row + 16*(key/4), reg = key%4) already is
+//    the P operand: the contraction index of an MFMA may be permuted freely
+//    when both operands use the same permutation, so each lane's 8 P values
+//    (keys 4j..4j+3 of two 16-key tiles) meet the V values of the same keys.
+//  * Online softmax in log2 units per row; the output rescale is skipped
+//    when no row's maximum moved.
+//  * The causal diagonal bounds each workgroup's key loop; stages entirely
+//    below it need no mask.
+//  * Workgroups of one (sequence, KV head) are placed on one XCD so they
+//    share its L2.
+
+#include <math.h>
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace pkv {
+namespace {
+
+constexpr int kPfWaves = 4;
+constexpr int kPfThreads = kPfWaves * kWave;
+constexpr int kPfKeys = 64;                                  // keys per stage
+constexpr int kPfMaxBlocks = PKV_MAX_PREFILL_CONTEXT / kBlockTokens;
+constexpr int kXcds = 8;
+constexpr float kLog2eP = 1.4426950408889634f;
+
+#ifndef PKV_PREFILL_CTILES
+#define PKV_PREFILL_CTILES 4   // 16-row query tiles per wave
+#endif
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int CTILES>
+struct PfShape {
+  static constexpr int rows_per_wave = 16 * CTILES;
+  static constexpr int rows = kPfWaves * rows_per_wave;     // query rows per workgroup
+};
+
+// 16-bit element type of the MFMA operands for query type QT.
+template <typename QT>
+__device__ __forceinline__ float4_t mfma32(u32x4 a, u32x4 b, float4_t c) {
+  if constexpr (std::is_same<QT, BF16>::value)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
+                                                   c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, a), __builtin_bit_cast(half8_t, b), c,
+                                                  0, 0, 0);
+}
+
+template <typename QT>
+__device__ __forceinline__ uint32_t pack_pair(float a, float b) {
+  if constexpr (std::is_same<QT, BF16>::value) {
+    bf16x2_t v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
+  } else {
+    half2_t v = {static_cast<_Float16>(a), static_cast<_Float16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+}
+
+// Eight fp8 codes (two words) -> eight 16-bit values of QT's type, exactly,
+// in element order.
+template <typename QT>
+__device__ __forceinline__ u32x4 fp8x8_to_16(uint32_t w0, uint32_t w1) {
+  u32x4 r;
+  if constexpr (std::is_same<QT, BF16>::value) {
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+  } else {
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true));
+  }
+  return r;
+}
+
+__device__ __forceinline__ float cmax4(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float csum4(float x) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+// Value of x held by lane src (0..63).
+__device__ __forceinline__ float lane_value(float x, int src) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+}
+
+// One stage's global -> register -> LDS traffic.  Thread t, round r moves
+// 16 bytes of the stage's K (and of V): stage byte (r*256 + t)*16.
+template <typename CT, int D>
+struct StageIO {
+  static constexpr int ces = CT::bytes;
+  static constexpr int row_bytes = D * ces;
+  static constexpr int rounds = kPfKeys * row_bytes / (kPfThreads * 16);
+  static constexpr int lds_row = D + 8;                      // 16-bit elements, padded
+  u32x4 k[rounds], v[rounds];
+  float ks;                                                  // fp8: thread t < 64 -> a K scale, < 128 -> a V scale
+};
+
+template <typename QT, typename CT, int D, int CTILES>
+__global__ void __launch_bounds__(kPfThreads, 1) paged_prefill_kernel(PrefillArgs a) {
+  using IO = StageIO<CT, D>;
+  using SH = PfShape<CTILES>;
+  constexpr bool kFp8 = std::is_same<CT, FP8>::value;
+  constexpr int DCH = D / 32;        // QK MFMAs per 16-key tile
+  constexpr int DT = D / 16;         // output column tiles
+  constexpr float kNegInf = -INFINITY;
+
+  __shared__ __attribute__((aligned(16))) uint16_t sm_k[kPfKeys * IO::lds_row];
+  __shared__ __attribute__((aligned(16))) uint16_t sm_v[kPfKeys * IO::lds_row];
+  __shared__ float sm_ks[kPfKeys];
+  __shared__ float sm_vs[kPfKeys];
+  __shared__ int sm_ids[kPfMaxBlocks];
+
+  // ---- which (sequence, KV head, row tile) this workgroup owns -------------
+  const int total = a.num_seqs * a.num_kv_heads * a.tiles_per_seq;
+  const int per_xcd = (total + kXcds - 1) / kXcds;
+  const int logical = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (logical >= total) return;
+  const int tile = logical % a.tiles_per_seq;
+  const int g = (logical / a.tiles_per_seq) % a.num_kv_heads;
+  const int b = logical / (a.tiles_per_seq * a.num_kv_heads);
+  const int group = a.num_q_heads / a.num_kv_heads;
+
+  const int qs = a.query_start[b];
+  const int n = a.query_start[b + 1] - qs;
+  // a chunk outside q, or longer than the launch was sized for, is skipped
+  if (qs < 0 || n <= 0 || n > a.max_query_len || qs + n > a.num_tokens) return;
+  const int rows_b = n * group;
+  const int r0 = tile * SH::rows;
+  if (r0 >= rows_b) return;
+  int L = a.context_lens[b];
+  L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * kBlockTokens)));
+  const int ctx = L - n;             // positions of the chunk: ctx .. L-1
+
+  const int tid = threadIdx.x;
+  const int wave = tid / kWave;
+  const int lane = tid % kWave;
+  const int c = lane & 15;
+  const int j = lane >> 4;
+
+  if (L == 0) {
+    // nothing cached: the chunk's rows are zero
+    const int r1 = min(rows_b, r0 + SH::rows);
+    for (int idx = tid; idx < (r1 - r0) * D; idx += kPfThreads) {
+      const int r = r0 + idx / D;
+      const int64_t o = (static_cast<int64_t>(qs + r / group) * a.num_q_heads + g * group + r % group) * D + idx % D;
+      store_from_f32<QT>(a.out, o, 0.0f);
+    }
+    return;
+  }
+
+  // key range: every row of the tile sees keys <= ctx + (its position)
+  const int i_first = r0 / group;
+  const int i_last = (min(rows_b, r0 + SH::rows) - 1) / group;
+  const int key_end = min(L, max(1, ctx + i_last + 1));       // exclusive
+  const int free_end = max(0, ctx + i_first + 1);             // keys < free_end are seen by every row
+  const int nstages = (key_end + kPfKeys - 1) / kPfKeys;
+  const int nblk = (key_end + kBlockTokens - 1) / kBlockTokens;
+
+  const int32_t* table = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq;
+  for (int i = tid; i < nblk; i += kPfThreads) sm_ids[i] = min(max(table[i], 0), a.num_blocks - 1);
+
+  // ---- query operands and per-row limits -------------------------------------
+  // Wave w, tile ct, column c: row r0 + w*16*CTILES + ct*16 + c.
+  u32x4 qop[CTILES][DCH];
+  int lim[CTILES];
+  const uint8_t* qbase = static_cast<const uint8_t*>(a.q);
+#pragma unroll
+  for (int ct = 0; ct < CTILES; ++ct) {
+    const int r = r0 + wave * SH::rows_per_wave + ct * 16 + c;
+    const bool valid = r < rows_b;
+    const int i = valid ? r / group : n - 1;
+    const int head = g * group + (valid ? r % group : 0);
+    lim[ct] = max(0, min(ctx + i, L - 1));
+    const uint8_t* qp = qbase + ((static_cast<int64_t>(qs + i) * a.num_q_heads + head) * D + 8 * j) * 2;
+#pragma unroll
+    for (int dc = 0; dc < DCH; ++dc) {
+      u32x4 v = *reinterpret_cast<const u32x4*>(qp + 64 * dc);
+      qop[ct][dc] = valid ? v : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __syncthreads();   // block ids staged
+
+  // ---- stage loader ------------------------------------------------------------
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool);
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool);
+  IO io;
+  auto load_stage = [&](int s) {
+    const int kb = s * kPfKeys;
+#pragma unroll
+    for (int r = 0; r < IO::rounds; ++r) {
+      const int byte = (r * kPfThreads + tid) * 16;
+      const int row = byte / IO::row_bytes;
+      const int col = byte % IO::row_bytes;
+      const int key = kb + row;
+      if (key < key_end) {
+        const int id = sm_ids[key / kBlockTokens];
+        const int64_t off = ((static_cast<int64_t>(id) * a.num_kv_heads + g) * kBlockTokens + key % kBlockTokens) *
+                                IO::row_bytes + col;
+        io.k[r] = *reinterpret_cast<const u32x4*>(kpool + off);
+        io.v[r] = *reinterpret_cast<const u32x4*>(vpool + off);
+      } else {
+        io.k[r] = u32x4{0u, 0u, 0u, 0u};
+        io.v[r] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    if constexpr (kFp8) {
+      io.ks = 0.0f;
+      if (tid < 2 * kPfKeys) {
+        const int key = kb + (tid % kPfKeys);
+        if (key < key_end) {
+          const int id = sm_ids[key / kBlockTokens];
+          const int64_t si = (static_cast<int64_t>(id) * a.num_kv_heads + g) * kBlockTokens + key % kBlockTokens;
+          io.ks = tid < kPfKeys ? a.k_scale[si] : a.v_scale[si];
+        }
+      }
+    }
+  };
+  auto store_stage = [&]() {
+#pragma unroll
+    for (int r = 0; r < IO::rounds; ++r) {
+      const int byte = (r * kPfThreads + tid) * 16;
+      const int row = byte / IO::row_bytes;
+      const int e = (byte % IO::row_bytes) / IO::ces;         // first element
+      uint16_t* kd = sm_k + row * IO::lds_row + e;
+      uint16_t* vd = sm_v + row * IO::lds_row + e;
+      if constexpr (kFp8) {
+        reinterpret_cast<u32x4*>(kd)[0] = fp8x8_to_16<QT>(io.k[r][0], io.k[r][1]);
+        reinterpret_cast<u32x4*>(kd)[1] = fp8x8_to_16<QT>(io.k[r][2], io.k[r][3]);
+        reinterpret_cast<u32x4*>(vd)[0] = fp8x8_to_16<QT>(io.v[r][0], io.v[r][1]);
+        reinterpret_cast<u32x4*>(vd)[1] = fp8x8_to_16<QT>(io.v[r][2], io.v[r][3]);
+      } else {
+        *reinterpret_cast<u32x4*>(kd) = io.k[r];
+        *reinterpret_cast<u32x4*>(vd) = io.v[r];
+      }
+    }
+    if constexpr (kFp8) {
+      if (tid < kPfKeys) sm_ks[tid] = io.ks;
+      else if (tid < 2 * kPfKeys) sm_vs[tid - kPfKeys] = io.ks;
+    }
+  };
+
+  // ---- main loop -------------------------------------------------------------------
+  float4_t o[CTILES][DT];
+  float m[CTILES], lsum[CTILES];
+#pragma unroll
+  for (int ct = 0; ct < CTILES; ++ct) {
+    m[ct] = kNegInf;
+    lsum[ct] = 0.0f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) o[ct][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  const float sl = a.scale * kLog2eP;
+
+  load_stage(0);
+  for (int s = 0; s < nstages; ++s) {
+    store_stage();
+    __syncthreads();
+    if (s + 1 < nstages) load_stage(s + 1);
+    const int kb = s * kPfKeys;
+    const bool masked = kb + kPfKeys > free_end;
+
+    // S^T tiles: [key tile][row tile]
+    float4_t st[4][CTILES];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+#pragma unroll
+      for (int ct = 0; ct < CTILES; ++ct) st[kt][ct] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int dc = 0; dc < DCH; ++dc) {
+        const u32x4 kop = *reinterpret_cast<const u32x4*>(sm_k + (kt * 16 + c) * IO::lds_row + 32 * dc + 8 * j);
+#pragma unroll
+        for (int ct = 0; ct < CTILES; ++ct) st[kt][ct] = mfma32<QT>(kop, qop[ct][dc], st[kt][ct]);
+      }
+    }
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const float4 ksc = *reinterpret_cast<const float4*>(sm_ks + kt * 16 + 4 * j);
+#pragma unroll
+        for (int ct = 0; ct < CTILES; ++ct) {
+          st[kt][ct][0] *= ksc.x;
+          st[kt][ct][1] *= ksc.y;
+          st[kt][ct][2] *= ksc.z;
+          st[kt][ct][3] *= ksc.w;
+        }
+      }
+    }
+    if (masked) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int ct = 0; ct < CTILES; ++ct)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            if (kb + kt * 16 + 4 * j + rr > lim[ct]) st[kt][ct][rr] = kNegInf;
+    }
+
+    // online softmax per row (column c of each row tile)
+    float alpha[CTILES];
+    bool moved = false;
+#pragma unroll
+    for (int ct = 0; ct < CTILES; ++ct) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, st[kt][ct][rr]);
+      mx = cmax4(mx) * sl;
+      const float mnew = fmaxf(m[ct], mx);
+      alpha[ct] = __builtin_amdgcn_exp2f(m[ct] - mnew);
+      moved |= mnew != m[ct];
+      m[ct] = mnew;
+      float ps = 0.0f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const float p = __builtin_amdgcn_exp2f(fmaf(st[kt][ct][rr], sl, -mnew));
+          st[kt][ct][rr] = p;
+          ps += p;
+        }
+      lsum[ct] = lsum[ct] * alpha[ct] + ps;
+    }
+    if (__any(moved)) {
+#pragma unroll
+      for (int ct = 0; ct < CTILES; ++ct) {
+        float ar[4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) ar[rr] = lane_value(alpha[ct], 4 * j + rr);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) o[ct][dt][rr] *= ar[rr];
+      }
+    }
+    if constexpr (kFp8) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const float4 vsc = *reinterpret_cast<const float4*>(sm_vs + kt * 16 + 4 * j);
+#pragma unroll
+        for (int ct = 0; ct < CTILES; ++ct) {
+          st[kt][ct][0] *= vsc.x;
+          st[kt][ct][1] *= vsc.y;
+          st[kt][ct][2] *= vsc.z;
+          st[kt][ct][3] *= vsc.w;
+        }
+      }
+    }
+
+    // O += P V over two 32-key halves
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv) {
+      u32x4 pop[CTILES];
+#pragma unroll
+      for (int ct = 0; ct < CTILES; ++ct) {
+        pop[ct][0] = pack_pair<QT>(st[2 * hv][ct][0], st[2 * hv][ct][1]);
+        pop[ct][1] = pack_pair<QT>(st[2 * hv][ct][2], st[2 * hv][ct][3]);
+        pop[ct][2] = pack_pair<QT>(st[2 * hv + 1][ct][0], st[2 * hv + 1][ct][1]);
+        pop[ct][3] = pack_pair<QT>(st[2 * hv + 1][ct][2], st[2 * hv + 1][ct][3]);
+      }
+      const uint16_t* v0 = sm_v + (32 * hv + 4 * j) * IO::lds_row + c;        // keys 4j .. 4j+3
+      const uint16_t* v1 = v0 + 16 * IO::lds_row;                               // keys 16+4j ..
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int d0 = 16 * dt;
+        u32x4 vop;
+        vop[0] = static_cast<uint32_t>(v0[d0]) | (static_cast<uint32_t>(v0[IO::lds_row + d0]) << 16);
+        vop[1] = static_cast<uint32_t>(v0[2 * IO::lds_row + d0]) |
+                 (static_cast<uint32_t>(v0[3 * IO::lds_row + d0]) << 16);
+        vop[2] = static_cast<uint32_t>(v1[d0]) | (static_cast<uint32_t>(v1[IO::lds_row + d0]) << 16);
+        vop[3] = static_cast<uint32_t>(v1[2 * IO::lds_row + d0]) |
+                 (static_cast<uint32_t>(v1[3 * IO::lds_row + d0]) << 16);
+#pragma unroll
+        for (int ct = 0; ct < CTILES; ++ct) o[ct][dt] = mfma32<QT>(pop[ct], vop, o[ct][dt]);
+      }
+    }
+    __syncthreads();   // every wave is done with this stage's LDS
+  }
+
+  // ---- normalise and store -------------------------------------------------------
+#pragma unroll
+  for (int ct = 0; ct < CTILES; ++ct) {
+    const float l = csum4(lsum[ct]);
+    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+    float ir[4];
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) ir[rr] = lane_value(inv, 4 * j + rr);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = r0 + wave * SH::rows_per_wave + ct * 16 + 4 * j + rr;
+      if (r >= rows_b) continue;
+      const int64_t orow = (static_cast<int64_t>(qs + r / group) * a.num_q_heads + g * group + r % group) * D;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) store_from_f32<QT>(a.out, orow + 16 * dt + c, o[ct][dt][rr] * ir[rr]);
+    }
+  }
+}
+
+template <typename QT, typename CT, int D>
+int launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
+  constexpr int kCt = PKV_PREFILL_CTILES;
+  PrefillArgs b = a;
+  const int group = a.num_q_heads / a.num_kv_heads;
+  const int64_t rows = static_cast<int64_t>(a.max_query_len) * group;
+  b.tiles_per_seq = static_cast<int>((rows + PfShape<kCt>::rows - 1) / PfShape<kCt>::rows);
+  const int64_t total = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * b.tiles_per_seq;
+  if (total == 0) return PKV_OK;
+  if (total > (int64_t{1} << 30)) return PKV_ERR_UNSUPPORTED;
+  const int64_t per_xcd = (total + kXcds - 1) / kXcds;
+  hipLaunchKernelGGL((paged_prefill_kernel<QT, CT, D, kCt>), dim3(static_cast<unsigned>(per_xcd * kXcds)),
+                     dim3(kPfThreads), 0, stream, b);
+  return check_launch();
+}
+
+template <typename QT, typename CT>
+int launch_prefill_dim(const PrefillArgs& a, hipStream_t stream) {
+  if (a.head_dim == 64) return launch_prefill_typed<QT, CT, 64>(a, stream);
+  if (a.head_dim == 128) return launch_prefill_typed<QT, CT, 128>(a, stream);
+  return PKV_ERR_UNSUPPORTED;
+}
+
+}  // namespace
+
+int launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+  if (a.cache_dtype == PKV_FP8_E4M3) {
+    if (a.q_dtype == PKV_BF16) return launch_prefill_dim<BF16, FP8>(a, stream);
+    if (a.q_dtype == PKV_F16) return launch_prefill_dim<F16, FP8>(a, stream);
+    return PKV_ERR_UNSUPPORTED;
+  }
+  if (a.q_dtype != a.cache_dtype) return PKV_ERR_UNSUPPORTED;
+  if (a.q_dtype == PKV_BF16) return launch_prefill_dim<BF16, BF16>(a, stream);
+  if (a.q_dtype == PKV_F16) return launch_prefill_dim<F16, F16>(a, stream);
+  return PKV_ERR_UNSUPPORTED;
+}
+
+}  // namespace pkv
