@@ -71,8 +71,11 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="write the step's rows with kv_cache_append, then attend (default: the write is fused "
                          "into the attention kernel)")
-    ap.add_argument("--row", choices=["decode", "prefix"], default="decode",
-                    help="decode (default): the hot path; prefix: host prefix-cache replay of agent sessions")
+    ap.add_argument("--row", choices=["decode", "prefix", "prefill"], default="decode",
+                    help="decode (default): the hot path; prefix: host prefix-cache replay of agent sessions; "
+                         "prefill: multi-token append + chunked prefill attention")
+    ap.add_argument("--cached", type=int, default=3584, help="prefill row: cached tokens per sequence")
+    ap.add_argument("--chunk", type=int, default=512, help="prefill row: chunk tokens per sequence")
     ap.add_argument("--one-call", action="store_true",
                     help="use the one-call paged_attention_decode_append (events then bracket both launches)")
     return ap.parse_args()
@@ -151,6 +154,9 @@ def main():
 
     if args.row == "prefix":
         run_prefix_row(args)
+        return
+    if args.row == "prefill":
+        run_prefill_row(args)
         return
 
     import numpy as np
@@ -466,6 +472,171 @@ def cpu_baseline(w, budget_s: float):
                    f"{w.name}; fp64 numpy; rows generated and dequantised before timing; "
                    f"{busy:.2f} cores busy on average, {allowed} allowed, BLAS threads {blas}"),
     }
+
+
+# ---- chunked prefill row ------------------------------------------------------------
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def prefill_flops(cached, chunk, hq, d):
+    """Algorithmic flops of one prefill call: query i of a chunk at position
+    p = cached + i meets p + 1 keys, 2*d flops each for q.k and for p*v."""
+    total = 0
+    for c, n in zip(cached, chunk):
+        keys = n * c + n * (n + 1) // 2
+        total += 4 * d * hq * keys
+    return total
+
+
+def run_prefill_row(args, lib=None):
+    """Multi-token append + chunked prefill on the Llama-3-8B layer shape
+    (32 query heads, 8 KV heads, D=128, bf16): 16 sequences, each holding
+    ``--cached`` tokens and appending a chunk of ``--chunk`` more (3584 + 512
+    = 4096 by default).  One step = for every layer: kv_cache_append of the
+    chunks' K/V rows (one multi-token append), then paged_attention_prefill.
+    Pools hold seeded device-generated N(0,1) rows; several layers rotate so
+    that K/V are read from HBM."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_160_amd as pkv
+    from paged_kv_cache_160_amd.cache import PagedKVCache
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = lib or pkv._lib.lib()
+    B, hq, hkv, D = 16, 32, 8, 128
+    cached, chunk = [args.cached] * B, [args.chunk] * B
+    L = args.cached + args.chunk
+    nb = int(math.ceil(1.1 * B * -(-L // 16)))
+    mb = -(-L // 16) + 1
+    layer_bytes = 2 * nb * hkv * 16 * D * 2
+    layers = args.layers or max(2, math.ceil(4 * MALL_BYTES / layer_bytes))
+    log(f"[prefill] B={B} cached={args.cached} chunk={args.chunk} Hq={hq} Hkv={hkv} D={D} bf16, "
+        f"{layers} layers x {layer_bytes / 2**30:.2f} GiB")
+    cache = PagedKVCache(layers, nb, hkv, D, torch.bfloat16, mb, device=dev)
+    cache.set_free_order(np.random.default_rng(2025).permutation(nb).astype(np.int32))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(99)
+    for l in range(layers):
+        cache.k[l].normal_(generator=gen)
+        cache.v[l].normal_(generator=gen)
+    chunk_slots = []
+    for b in range(B):
+        cache.create(b)
+        cache.alloc.append_slots(b, args.cached)            # the cached context (rows already in the pool)
+        slots, _ = cache.alloc.append_slots(b, args.chunk)  # the chunk: its rows are written every step
+        chunk_slots += slots
+    seqs = list(range(B))
+    tables, lens, max_len = cache.block_tables(seqs)
+    T = sum(chunk)
+    slot_t = torch.tensor(chunk_slots, dtype=torch.int64, device=dev)
+    qs_t = torch.tensor(np.concatenate([[0], np.cumsum(chunk)]), dtype=torch.int32, device=dev)
+    n_steps = args.warmup + args.steps
+    q = torch.randn((layers, T, hq, D), generator=gen, device=dev).to(torch.bfloat16)
+    knew = torch.randn((layers, T, hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+    vnew = torch.randn((layers, T, hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+    out = torch.empty((layers, T, hq, D), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    code = pkv.dtype_code(torch.bfloat16)
+    scale = 1.0 / math.sqrt(D)
+    flops = prefill_flops(cached, chunk, hq, D)
+    ev = {(s_, l): tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+          for s_ in range(args.warmup, n_steps) for l in range(layers)}
+
+    def step(s, timed):
+        for l in range(layers):
+            e = ev.get((s, l)) if timed else None
+            if e:
+                e[0].record(stream)
+            rc = lib.kv_cache_append(knew[l].data_ptr(), vnew[l].data_ptr(), cache.k[l].data_ptr(),
+                                     cache.v[l].data_ptr(), None, None, slot_t.data_ptr(), T, hkv, D, nb, code,
+                                     code, sp)
+            if rc:
+                raise pkv.PagedKVError(rc, "kv_cache_append")
+            if e:
+                e[1].record(stream)
+            rc = lib.paged_attention_prefill(out[l].data_ptr(), q[l].data_ptr(), cache.k[l].data_ptr(),
+                                             cache.v[l].data_ptr(), None, None, tables.data_ptr(), lens.data_ptr(),
+                                             qs_t.data_ptr(), B, T, hq, hkv, D, nb, mb, max_len, max(chunk), scale,
+                                             code, code, sp)
+            if rc:
+                raise pkv.PagedKVError(rc, "paged_attention_prefill")
+            if e:
+                e[2].record(stream)
+
+    for s in range(args.warmup):
+        step(s, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.warmup, n_steps):
+        step(s, True)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    app_s = sum(a.elapsed_time(b) for a, b, _ in ev.values()) / len(ev) / 1e3
+    pf_s = sum(b.elapsed_time(c) for _, b, c in ev.values()) / len(ev) / 1e3
+    calls = args.steps * layers
+    achieved = flops / pf_s / 1e12
+    value = flops * calls / elapsed / 1e12
+    kv_bytes = sum(L for _ in range(B)) * hkv * D * 2 * 2
+    log(f"[prefill] {args.steps} steps x {layers} layers in {elapsed * 1e3:.2f} ms; append {app_s * 1e6:.1f} us, "
+        f"prefill {pf_s * 1e6:.1f} us = {achieved:.1f} TFLOP/s ({100 * achieved / MFMA_BF16_PEAK_TFLOPS:.1f}% of "
+        f"bf16 MFMA peak); K/V read {kv_bytes / pf_s / 1e9:.0f} GB/s")
+    rec = {
+        "metric": "chunked prefill attention over the paged cache, TFLOP/s (algorithmic, causal), 1 GPU",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": elapsed * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) K/V/q)",
+        "config": {"workload": f"llama3-8b-shape chunked prefill: 16 x ({args.cached} cached + {args.chunk} new)",
+                   "q_heads": hq, "kv_heads": hkv, "head_dim": D, "block_size": 16, "layers_rotated": layers},
+        "append_us": app_s * 1e6, "prefill_kernel_us": pf_s * 1e6,
+        "chunk_tokens_per_s": T * calls / elapsed,
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": None, "kernel": "paged_prefill_kernel",
+                     "flops_per_launch": flops},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = prefill_cpu_baseline(args, hq, hkv, D, args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+    return rec
+
+
+def prefill_cpu_baseline(args, hq, hkv, D, budget_s):
+    """The fp64 oracle (test infrastructure): chunk rows of one sequence with
+    the same context length, timed until the budget is spent."""
+    import numpy as np
+
+    from oracle import prefill
+
+    import psutil
+
+    rng = np.random.default_rng(5)
+    L = args.cached + args.chunk
+    K = rng.standard_normal((L, hkv, D))
+    V = rng.standard_normal((L, hkv, D))
+    q = rng.standard_normal((args.chunk, hq, D))
+    proc = psutil.Process()
+    c0 = proc.cpu_times()
+    t0 = time.perf_counter()
+    done = flops = 0
+    step = 8
+    while True:
+        i0 = (done * step) % args.chunk
+        n = min(step, args.chunk - i0)
+        # rows i0 .. i0+n-1 of the chunk: pass the rows up to the last one's position
+        prefill.prefill_rows(q[i0:i0 + n], K[:args.cached + i0 + n], V[:args.cached + i0 + n], 1.0 / math.sqrt(D))
+        flops += prefill_flops([args.cached + i0], [n], hq, D)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    wall = time.perf_counter() - t0
+    c1 = proc.cpu_times()
+    busy = (c1.user - c0.user + c1.system - c0.system) / wall
+    return {"value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": max(1, round(busy)), "kind": "oracle",
+            "sample": f"{done} slices of {step} chunk rows (all {hq} heads, contexts {args.cached}..{L}), "
+                      f"fp64 numpy, {busy:.2f} cores busy on average"}
 
 
 # ---- prefix caching row --------------------------------------------------------------

@@ -49,10 +49,12 @@ constexpr int kXcds = 8;
 constexpr float kLog2eP = 1.4426950408889634f;
 
 #ifndef PKV_PREFILL_CTILES
-#define PKV_PREFILL_CTILES 4   // 16-row query tiles per wave
+#define PKV_PREFILL_CTILES 2   // 16-row query tiles per wave
 #endif
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+constexpr float kRebase = 8.0f;     // log2 headroom before the running max moves
 
 template <int CTILES>
 struct PfShape {
@@ -125,13 +127,17 @@ struct StageIO {
   static constexpr int ces = CT::bytes;
   static constexpr int row_bytes = D * ces;
   static constexpr int rounds = kPfKeys * row_bytes / (kPfThreads * 16);
-  static constexpr int lds_row = D + 8;                      // 16-bit elements, padded
+  // 16-bit elements per LDS row: D + 16 puts consecutive rows 32 bytes apart
+  // in bank space, so the 16 rows a transpose read or a K-operand read
+  // touches spread evenly over the banks
+  static constexpr int lds_row = D + 16;
+  static constexpr int tile_bytes = kBlockTokens * row_bytes;     // one (block, head) tile
   u32x4 k[rounds], v[rounds];
   float ks;                                                  // fp8: thread t < 64 -> a K scale, < 128 -> a V scale
 };
 
 template <typename QT, typename CT, int D, int CTILES>
-__global__ void __launch_bounds__(kPfThreads, 1) paged_prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill_kernel(PrefillArgs a) {
   using IO = StageIO<CT, D>;
   using SH = PfShape<CTILES>;
   constexpr bool kFp8 = std::is_same<CT, FP8>::value;
@@ -219,18 +225,23 @@ __global__ void __launch_bounds__(kPfThreads, 1) paged_prefill_kernel(PrefillArg
   const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool);
   const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool);
   IO io;
+  // round r of thread t moves stage bytes (r*256 + t)*16: a fixed row of the
+  // stage (so a fixed block of its 4 and row within it) and column
+  int thr_off[IO::rounds], thr_blk[IO::rounds], thr_row[IO::rounds];
+#pragma unroll
+  for (int r = 0; r < IO::rounds; ++r) {
+    const int byte = (r * kPfThreads + tid) * 16;
+    thr_row[r] = byte / IO::row_bytes;
+    thr_blk[r] = thr_row[r] / kBlockTokens;
+    thr_off[r] = (thr_row[r] % kBlockTokens) * IO::row_bytes + byte % IO::row_bytes;
+  }
   auto load_stage = [&](int s) {
     const int kb = s * kPfKeys;
 #pragma unroll
     for (int r = 0; r < IO::rounds; ++r) {
-      const int byte = (r * kPfThreads + tid) * 16;
-      const int row = byte / IO::row_bytes;
-      const int col = byte % IO::row_bytes;
-      const int key = kb + row;
-      if (key < key_end) {
-        const int id = sm_ids[key / kBlockTokens];
-        const int64_t off = ((static_cast<int64_t>(id) * a.num_kv_heads + g) * kBlockTokens + key % kBlockTokens) *
-                                IO::row_bytes + col;
+      if (kb + thr_row[r] < key_end) {
+        const int id = sm_ids[4 * s + thr_blk[r]];
+        const int64_t off = static_cast<int64_t>(id * a.num_kv_heads + g) * IO::tile_bytes + thr_off[r];
         io.k[r] = *reinterpret_cast<const u32x4*>(kpool + off);
         io.v[r] = *reinterpret_cast<const u32x4*>(vpool + off);
       } else {
@@ -244,7 +255,7 @@ __global__ void __launch_bounds__(kPfThreads, 1) paged_prefill_kernel(PrefillArg
         const int key = kb + (tid % kPfKeys);
         if (key < key_end) {
           const int id = sm_ids[key / kBlockTokens];
-          const int64_t si = (static_cast<int64_t>(id) * a.num_kv_heads + g) * kBlockTokens + key % kBlockTokens;
+          const int64_t si = static_cast<int64_t>(id * a.num_kv_heads + g) * kBlockTokens + key % kBlockTokens;
           io.ks = tid < kPfKeys ? a.k_scale[si] : a.v_scale[si];
         }
       }
@@ -291,120 +302,126 @@ __global__ void __launch_bounds__(kPfThreads, 1) paged_prefill_kernel(PrefillArg
     store_stage();
     __syncthreads();
     if (s + 1 < nstages) load_stage(s + 1);
-    const int kb = s * kPfKeys;
-    const bool masked = kb + kPfKeys > free_end;
-
-    // S^T tiles: [key tile][row tile]
-    float4_t st[4][CTILES];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int ct = 0; ct < CTILES; ++ct) st[kt][ct] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int dc = 0; dc < DCH; ++dc) {
-        const u32x4 kop = *reinterpret_cast<const u32x4*>(sm_k + (kt * 16 + c) * IO::lds_row + 32 * dc + 8 * j);
-#pragma unroll
-        for (int ct = 0; ct < CTILES; ++ct) st[kt][ct] = mfma32<QT>(kop, qop[ct][dc], st[kt][ct]);
-      }
-    }
-    if constexpr (kFp8) {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const float4 ksc = *reinterpret_cast<const float4*>(sm_ks + kt * 16 + 4 * j);
-#pragma unroll
-        for (int ct = 0; ct < CTILES; ++ct) {
-          st[kt][ct][0] *= ksc.x;
-          st[kt][ct][1] *= ksc.y;
-          st[kt][ct][2] *= ksc.z;
-          st[kt][ct][3] *= ksc.w;
-        }
-      }
-    }
-    if (masked) {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int ct = 0; ct < CTILES; ++ct)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            if (kb + kt * 16 + 4 * j + rr > lim[ct]) st[kt][ct][rr] = kNegInf;
-    }
-
-    // online softmax per row (column c of each row tile)
-    float alpha[CTILES];
-    bool moved = false;
-#pragma unroll
-    for (int ct = 0; ct < CTILES; ++ct) {
-      float mx = kNegInf;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, st[kt][ct][rr]);
-      mx = cmax4(mx) * sl;
-      const float mnew = fmaxf(m[ct], mx);
-      alpha[ct] = __builtin_amdgcn_exp2f(m[ct] - mnew);
-      moved |= mnew != m[ct];
-      m[ct] = mnew;
-      float ps = 0.0f;
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(st[kt][ct][rr], sl, -mnew));
-          st[kt][ct][rr] = p;
-          ps += p;
-        }
-      lsum[ct] = lsum[ct] * alpha[ct] + ps;
-    }
-    if (__any(moved)) {
-#pragma unroll
-      for (int ct = 0; ct < CTILES; ++ct) {
-        float ar[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) ar[rr] = lane_value(alpha[ct], 4 * j + rr);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) o[ct][dt][rr] *= ar[rr];
-      }
-    }
-    if constexpr (kFp8) {
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        const float4 vsc = *reinterpret_cast<const float4*>(sm_vs + kt * 16 + 4 * j);
-#pragma unroll
-        for (int ct = 0; ct < CTILES; ++ct) {
-          st[kt][ct][0] *= vsc.x;
-          st[kt][ct][1] *= vsc.y;
-          st[kt][ct][2] *= vsc.z;
-          st[kt][ct][3] *= vsc.w;
-        }
-      }
-    }
-
-    // O += P V over two 32-key halves
+    // the stage in two halves of 32 keys: S^T, softmax, then P V for each
 #pragma unroll
     for (int hv = 0; hv < 2; ++hv) {
+      const int kb = s * kPfKeys + 32 * hv;
+      const bool masked = kb + 32 > free_end;
+
+      // S^T tiles: [key tile of the half][row tile]
+      float4_t st[2][CTILES];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+        for (int ct = 0; ct < CTILES; ++ct) st[kt][ct] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int dc = 0; dc < DCH; ++dc) {
+          const u32x4 kop = *reinterpret_cast<const u32x4*>(sm_k + (32 * hv + kt * 16 + c) * IO::lds_row + 32 * dc +
+                                                            8 * j);
+#pragma unroll
+          for (int ct = 0; ct < CTILES; ++ct) st[kt][ct] = mfma32<QT>(kop, qop[ct][dc], st[kt][ct]);
+        }
+      }
+      if constexpr (kFp8) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+          const float4 ksc = *reinterpret_cast<const float4*>(sm_ks + 32 * hv + kt * 16 + 4 * j);
+#pragma unroll
+          for (int ct = 0; ct < CTILES; ++ct) {
+            st[kt][ct][0] *= ksc.x;
+            st[kt][ct][1] *= ksc.y;
+            st[kt][ct][2] *= ksc.z;
+            st[kt][ct][3] *= ksc.w;
+          }
+        }
+      }
+      if (masked) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int ct = 0; ct < CTILES; ++ct)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+              if (kb + kt * 16 + 4 * j + rr > lim[ct]) st[kt][ct][rr] = kNegInf;
+      }
+
+      // online softmax per row (column c of each row tile), in log2 units.
+      // The running maximum m only moves when a row's new maximum exceeds it
+      // by more than kRebase: probabilities exp2(s*sl - m) stay below
+      // 2^kRebase and the output and sum are rescaled far less often (the
+      // final division uses the same m for both, so the result is the same).
+      float mxs[CTILES];
+      bool need = false;
+#pragma unroll
+      for (int ct = 0; ct < CTILES; ++ct) {
+        float mx = kNegInf;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, st[kt][ct][rr]);
+        mxs[ct] = cmax4(mx) * sl;
+        need |= mxs[ct] > m[ct] + kRebase;
+      }
+      if (__any(need)) {
+#pragma unroll
+        for (int ct = 0; ct < CTILES; ++ct) {
+          const float mnew = mxs[ct] > m[ct] + kRebase ? mxs[ct] : m[ct];
+          const float alpha = __builtin_amdgcn_exp2f(m[ct] - mnew);     // 1 for rows that keep m
+          m[ct] = mnew;
+          lsum[ct] *= alpha;
+          float ar[4];
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) ar[rr] = lane_value(alpha, 4 * j + rr);
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) o[ct][dt][rr] *= ar[rr];
+        }
+      }
       u32x4 pop[CTILES];
 #pragma unroll
       for (int ct = 0; ct < CTILES; ++ct) {
-        pop[ct][0] = pack_pair<QT>(st[2 * hv][ct][0], st[2 * hv][ct][1]);
-        pop[ct][1] = pack_pair<QT>(st[2 * hv][ct][2], st[2 * hv][ct][3]);
-        pop[ct][2] = pack_pair<QT>(st[2 * hv + 1][ct][0], st[2 * hv + 1][ct][1]);
-        pop[ct][3] = pack_pair<QT>(st[2 * hv + 1][ct][2], st[2 * hv + 1][ct][3]);
+        float p[2][4];
+        float ps = 0.0f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) {
+            p[kt][rr] = __builtin_amdgcn_exp2f(fmaf(st[kt][ct][rr], sl, -m[ct]));
+            ps += p[kt][rr];
+          }
+        lsum[ct] += ps;
+        if constexpr (kFp8) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt) {
+            const float4 vsc = *reinterpret_cast<const float4*>(sm_vs + 32 * hv + kt * 16 + 4 * j);
+            p[kt][0] *= vsc.x;
+            p[kt][1] *= vsc.y;
+            p[kt][2] *= vsc.z;
+            p[kt][3] *= vsc.w;
+          }
+        }
+        pop[ct][0] = pack_pair<QT>(p[0][0], p[0][1]);
+        pop[ct][1] = pack_pair<QT>(p[0][2], p[0][3]);
+        pop[ct][2] = pack_pair<QT>(p[1][0], p[1][1]);
+        pop[ct][3] = pack_pair<QT>(p[1][2], p[1][3]);
       }
-      const uint16_t* v0 = sm_v + (32 * hv + 4 * j) * IO::lds_row + c;        // keys 4j .. 4j+3
-      const uint16_t* v1 = v0 + 16 * IO::lds_row;                               // keys 16+4j ..
+
+      // O += P V.  B operand (32 keys x 16 d) by transpose reads: lane c of
+      // group j points at V[key 4j + c/4 (+16)][d0 + 4(c%4) ..+3] and
+      // receives V[key 4j + e (+16)][d0 + c] for e = 0..3, the keys of its P
+      // slots.
+      const uint16_t* vrow0 = sm_v + (32 * hv + 4 * j + (c >> 2)) * IO::lds_row + 4 * (c & 3);
+      const uint16_t* vrow1 = vrow0 + 16 * IO::lds_row;
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int d0 = 16 * dt;
-        u32x4 vop;
-        vop[0] = static_cast<uint32_t>(v0[d0]) | (static_cast<uint32_t>(v0[IO::lds_row + d0]) << 16);
-        vop[1] = static_cast<uint32_t>(v0[2 * IO::lds_row + d0]) |
-                 (static_cast<uint32_t>(v0[3 * IO::lds_row + d0]) << 16);
-        vop[2] = static_cast<uint32_t>(v1[d0]) | (static_cast<uint32_t>(v1[IO::lds_row + d0]) << 16);
-        vop[3] = static_cast<uint32_t>(v1[2 * IO::lds_row + d0]) |
-                 (static_cast<uint32_t>(v1[3 * IO::lds_row + d0]) << 16);
+        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(vrow0 + 16 * dt));
+        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) short4_t*)(vrow1 + 16 * dt));
+        const u32x2_t wlo = __builtin_bit_cast(u32x2_t, lo);
+        const u32x2_t whi = __builtin_bit_cast(u32x2_t, hi);
+        const u32x4 vop = {wlo[0], wlo[1], whi[0], whi[1]};
 #pragma unroll
         for (int ct = 0; ct < CTILES; ++ct) o[ct][dt] = mfma32<QT>(pop[ct], vop, o[ct][dt]);
       }
