@@ -14,18 +14,23 @@
 //  * Workgroup = 4 waves owning 256 query rows of one (sequence, KV head);
 //    a row is a (chunk position, head of the GQA group) pair, so the whole
 //    group shares every K/V tile.  Each wave owns CTILES tiles of 16 rows.
-//  * K and V stream through LDS in stages of 64 keys (4 paged blocks): the
-//    workgroup loads a stage with 16-byte loads while computing the previous
-//    one from LDS; fp8 codes become 16-bit values exactly on the way in and
-//    their per-token scales go to LDS beside them.
+//  * K and V stream through LDS in stages of 64 keys (4 paged blocks).  For
+//    16-bit caches each wave moves one block of the next stage straight from
+//    HBM into the second of two LDS buffers (global_load_lds, no registers)
+//    while the workgroup computes the current one; rows are unpadded and
+//    their 16-byte chunks XOR-swizzled by row, so operand reads spread over
+//    the banks.  fp8 codes take a register path instead: they become 16-bit
+//    values exactly on the way into a padded buffer, and their per-token
+//    scales go to LDS beside them.
 //      S^T = K (16 keys x D) * Q^T (D x 16 rows)       [16x16x32 MFMA]
 //      O  += P (16 rows x 32 keys) * V (32 keys x 16 d) [16x16x32 MFMA]
 //    The S^T accumulator (lane = row + 16*(key/4), reg = key%4) already is
 //    the P operand: the contraction index of an MFMA may be permuted freely
 //    when both operands use the same permutation, so each lane's 8 P values
 //    (keys 4j..4j+3 of two 16-key tiles) meet the V values of the same keys.
-//  * Online softmax in log2 units per row; the output rescale is skipped
-//    when no row's maximum moved.
+//  * Online softmax in log2 units per row; the running maximum moves only
+//    when a row's maximum grows by more than 2^8, so output rescales are
+//    rare.  The matrix phases run at raised wave priority.
 //  * The causal diagonal bounds each workgroup's key loop; stages entirely
 //    below it need no mask.
 //  * Workgroups of one (sequence, KV head) are placed on one XCD so they
@@ -136,6 +141,18 @@ struct StageIO {
   float ks;                                                  // fp8: thread t < 64 -> a K scale, < 128 -> a V scale
 };
 
+// Swizzle of 16-byte chunk positions in an unpadded LDS row of D 16-bit
+// elements: consecutive rows (D = 128) or row pairs (D = 64, two rows per
+// 256-byte bank line) rotate their chunks, so the 16 rows one MFMA operand
+// read touches land on distinct banks.
+template <int D>
+struct LdsSwz {
+  static __device__ __forceinline__ int of(int r) {
+    if constexpr (D == 128) return r & 15;
+    else return (r >> 1) & 7;
+  }
+};
+
 template <typename QT, typename CT, int D, int CTILES>
 __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill_kernel(PrefillArgs a) {
   using IO = StageIO<CT, D>;
@@ -145,8 +162,14 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
   constexpr int DT = D / 16;         // output column tiles
   constexpr float kNegInf = -INFINITY;
 
-  __shared__ __attribute__((aligned(16))) uint16_t sm_k[kPfKeys * IO::lds_row];
-  __shared__ __attribute__((aligned(16))) uint16_t sm_v[kPfKeys * IO::lds_row];
+  // fp8 caches: one padded 16-bit stage buffer per tensor (and the scales);
+  // 16-bit caches: two unpadded, swizzled stage buffers per tensor
+  constexpr int kPadElems = kFp8 ? kPfKeys * IO::lds_row : 8;
+  constexpr int kDmaChunks = kFp8 ? 1 : kPfKeys * IO::row_bytes / 16;
+  __shared__ __attribute__((aligned(16))) uint16_t sm_k[kPadElems];
+  __shared__ __attribute__((aligned(16))) uint16_t sm_v[kPadElems];
+  __shared__ u32x4 sm_kd[2][kDmaChunks];
+  __shared__ u32x4 sm_vd[2][kDmaChunks];
   __shared__ float sm_ks[kPfKeys];
   __shared__ float sm_vs[kPfKeys];
   __shared__ int sm_ids[kPfMaxBlocks];
@@ -221,71 +244,7 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
   }
   __syncthreads();   // block ids staged
 
-  // ---- stage loader ------------------------------------------------------------
-  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool);
-  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool);
-  IO io;
-  // round r of thread t moves stage bytes (r*256 + t)*16: a fixed row of the
-  // stage (so a fixed block of its 4 and row within it) and column
-  int thr_off[IO::rounds], thr_blk[IO::rounds], thr_row[IO::rounds];
-#pragma unroll
-  for (int r = 0; r < IO::rounds; ++r) {
-    const int byte = (r * kPfThreads + tid) * 16;
-    thr_row[r] = byte / IO::row_bytes;
-    thr_blk[r] = thr_row[r] / kBlockTokens;
-    thr_off[r] = (thr_row[r] % kBlockTokens) * IO::row_bytes + byte % IO::row_bytes;
-  }
-  auto load_stage = [&](int s) {
-    const int kb = s * kPfKeys;
-#pragma unroll
-    for (int r = 0; r < IO::rounds; ++r) {
-      if (kb + thr_row[r] < key_end) {
-        const int id = sm_ids[4 * s + thr_blk[r]];
-        const int64_t off = static_cast<int64_t>(id * a.num_kv_heads + g) * IO::tile_bytes + thr_off[r];
-        io.k[r] = *reinterpret_cast<const u32x4*>(kpool + off);
-        io.v[r] = *reinterpret_cast<const u32x4*>(vpool + off);
-      } else {
-        io.k[r] = u32x4{0u, 0u, 0u, 0u};
-        io.v[r] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    if constexpr (kFp8) {
-      io.ks = 0.0f;
-      if (tid < 2 * kPfKeys) {
-        const int key = kb + (tid % kPfKeys);
-        if (key < key_end) {
-          const int id = sm_ids[key / kBlockTokens];
-          const int64_t si = static_cast<int64_t>(id * a.num_kv_heads + g) * kBlockTokens + key % kBlockTokens;
-          io.ks = tid < kPfKeys ? a.k_scale[si] : a.v_scale[si];
-        }
-      }
-    }
-  };
-  auto store_stage = [&]() {
-#pragma unroll
-    for (int r = 0; r < IO::rounds; ++r) {
-      const int byte = (r * kPfThreads + tid) * 16;
-      const int row = byte / IO::row_bytes;
-      const int e = (byte % IO::row_bytes) / IO::ces;         // first element
-      uint16_t* kd = sm_k + row * IO::lds_row + e;
-      uint16_t* vd = sm_v + row * IO::lds_row + e;
-      if constexpr (kFp8) {
-        reinterpret_cast<u32x4*>(kd)[0] = fp8x8_to_16<QT>(io.k[r][0], io.k[r][1]);
-        reinterpret_cast<u32x4*>(kd)[1] = fp8x8_to_16<QT>(io.k[r][2], io.k[r][3]);
-        reinterpret_cast<u32x4*>(vd)[0] = fp8x8_to_16<QT>(io.v[r][0], io.v[r][1]);
-        reinterpret_cast<u32x4*>(vd)[1] = fp8x8_to_16<QT>(io.v[r][2], io.v[r][3]);
-      } else {
-        *reinterpret_cast<u32x4*>(kd) = io.k[r];
-        *reinterpret_cast<u32x4*>(vd) = io.v[r];
-      }
-    }
-    if constexpr (kFp8) {
-      if (tid < kPfKeys) sm_ks[tid] = io.ks;
-      else if (tid < 2 * kPfKeys) sm_vs[tid - kPfKeys] = io.ks;
-    }
-  };
-
-  // ---- main loop -------------------------------------------------------------------
+  // ---- output state ----------------------------------------------------------------
   float4_t o[CTILES][DT];
   float m[CTILES], lsum[CTILES];
 #pragma unroll
@@ -296,137 +255,268 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
     for (int dt = 0; dt < DT; ++dt) o[ct][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
   const float sl = a.scale * kLog2eP;
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool);
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool);
 
-  load_stage(0);
-  for (int s = 0; s < nstages; ++s) {
-    store_stage();
-    __syncthreads();
-    if (s + 1 < nstages) load_stage(s + 1);
-    // the stage in two halves of 32 keys: S^T, softmax, then P V for each
-#pragma unroll
-    for (int hv = 0; hv < 2; ++hv) {
-      const int kb = s * kPfKeys + 32 * hv;
-      const bool masked = kb + 32 > free_end;
+  // Byte offset in a stage buffer of 16-byte chunk q (8 elements) of row r,
+  // and of its half h.  16-bit caches: unpadded rows whose chunk q sits at
+  // position q ^ swz(r); fp8 caches (converted on the way in): padded rows.
+  auto kaddr = [&](int r, int q) -> int {
+    if constexpr (kFp8) return (r * IO::lds_row + 8 * q) * 2;
+    else return r * IO::row_bytes + 16 * (q ^ LdsSwz<D>::of(r));
+  };
+  auto vaddr = [&](int r, int q, int h) -> int { return kaddr(r, q) + 8 * h; };
 
-      // S^T tiles: [key tile of the half][row tile]
-      float4_t st[2][CTILES];
+  // One stage (64 keys from s * 64) held in LDS at kbuf / vbuf.
+  auto compute = [&](const uint8_t* kbuf, const uint8_t* vbuf, int s) {
+      // the stage in two halves of 32 keys: S^T, softmax, then P V for each
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-        for (int ct = 0; ct < CTILES; ++ct) st[kt][ct] = float4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int dc = 0; dc < DCH; ++dc) {
-          const u32x4 kop = *reinterpret_cast<const u32x4*>(sm_k + (32 * hv + kt * 16 + c) * IO::lds_row + 32 * dc +
-                                                            8 * j);
-#pragma unroll
-          for (int ct = 0; ct < CTILES; ++ct) st[kt][ct] = mfma32<QT>(kop, qop[ct][dc], st[kt][ct]);
-        }
-      }
-      if constexpr (kFp8) {
+      for (int hv = 0; hv < 2; ++hv) {
+        const int kb = s * kPfKeys + 32 * hv;
+        const bool masked = kb + 32 > free_end;
+
+        // S^T tiles: [key tile of the half][row tile]
+        float4_t st[2][CTILES];
+        // matrix phases run at raised wave priority: of the two waves sharing
+        // a SIMD, the one with MFMA work issues first and the other's softmax
+        // fills the gaps
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) {
-          const float4 ksc = *reinterpret_cast<const float4*>(sm_ks + 32 * hv + kt * 16 + 4 * j);
 #pragma unroll
-          for (int ct = 0; ct < CTILES; ++ct) {
-            st[kt][ct][0] *= ksc.x;
-            st[kt][ct][1] *= ksc.y;
-            st[kt][ct][2] *= ksc.z;
-            st[kt][ct][3] *= ksc.w;
+          for (int ct = 0; ct < CTILES; ++ct) st[kt][ct] = float4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int dc = 0; dc < DCH; ++dc) {
+            const u32x4 kop = *reinterpret_cast<const u32x4*>(kbuf + kaddr(32 * hv + kt * 16 + c, 4 * dc + j));
+#pragma unroll
+            for (int ct = 0; ct < CTILES; ++ct) st[kt][ct] = mfma32<QT>(kop, qop[ct][dc], st[kt][ct]);
           }
         }
-      }
-      if (masked) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int ct = 0; ct < CTILES; ++ct)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr)
-              if (kb + kt * 16 + 4 * j + rr > lim[ct]) st[kt][ct][rr] = kNegInf;
-      }
-
-      // online softmax per row (column c of each row tile), in log2 units.
-      // The running maximum m only moves when a row's new maximum exceeds it
-      // by more than kRebase: probabilities exp2(s*sl - m) stay below
-      // 2^kRebase and the output and sum are rescaled far less often (the
-      // final division uses the same m for both, so the result is the same).
-      float mxs[CTILES];
-      bool need = false;
-#pragma unroll
-      for (int ct = 0; ct < CTILES; ++ct) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, st[kt][ct][rr]);
-        mxs[ct] = cmax4(mx) * sl;
-        need |= mxs[ct] > m[ct] + kRebase;
-      }
-      if (__any(need)) {
-#pragma unroll
-        for (int ct = 0; ct < CTILES; ++ct) {
-          const float mnew = mxs[ct] > m[ct] + kRebase ? mxs[ct] : m[ct];
-          const float alpha = __builtin_amdgcn_exp2f(m[ct] - mnew);     // 1 for rows that keep m
-          m[ct] = mnew;
-          lsum[ct] *= alpha;
-          float ar[4];
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) ar[rr] = lane_value(alpha, 4 * j + rr);
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) o[ct][dt][rr] *= ar[rr];
-        }
-      }
-      u32x4 pop[CTILES];
-#pragma unroll
-      for (int ct = 0; ct < CTILES; ++ct) {
-        float p[2][4];
-        float ps = 0.0f;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr) {
-            p[kt][rr] = __builtin_amdgcn_exp2f(fmaf(st[kt][ct][rr], sl, -m[ct]));
-            ps += p[kt][rr];
-          }
-        lsum[ct] += ps;
+        __builtin_amdgcn_s_setprio(0);
         if constexpr (kFp8) {
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt) {
-            const float4 vsc = *reinterpret_cast<const float4*>(sm_vs + 32 * hv + kt * 16 + 4 * j);
-            p[kt][0] *= vsc.x;
-            p[kt][1] *= vsc.y;
-            p[kt][2] *= vsc.z;
-            p[kt][3] *= vsc.w;
+            const float4 ksc = *reinterpret_cast<const float4*>(sm_ks + 32 * hv + kt * 16 + 4 * j);
+#pragma unroll
+            for (int ct = 0; ct < CTILES; ++ct) {
+              st[kt][ct][0] *= ksc.x;
+              st[kt][ct][1] *= ksc.y;
+              st[kt][ct][2] *= ksc.z;
+              st[kt][ct][3] *= ksc.w;
+            }
           }
         }
-        pop[ct][0] = pack_pair<QT>(p[0][0], p[0][1]);
-        pop[ct][1] = pack_pair<QT>(p[0][2], p[0][3]);
-        pop[ct][2] = pack_pair<QT>(p[1][0], p[1][1]);
-        pop[ct][3] = pack_pair<QT>(p[1][2], p[1][3]);
-      }
+        if (masked) {
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int ct = 0; ct < CTILES; ++ct)
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr)
+                if (kb + kt * 16 + 4 * j + rr > lim[ct]) st[kt][ct][rr] = kNegInf;
+        }
 
-      // O += P V.  B operand (32 keys x 16 d) by transpose reads: lane c of
-      // group j points at V[key 4j + c/4 (+16)][d0 + 4(c%4) ..+3] and
-      // receives V[key 4j + e (+16)][d0 + c] for e = 0..3, the keys of its P
-      // slots.
-      const uint16_t* vrow0 = sm_v + (32 * hv + 4 * j + (c >> 2)) * IO::lds_row + 4 * (c & 3);
-      const uint16_t* vrow1 = vrow0 + 16 * IO::lds_row;
+        // online softmax per row (column c of each row tile), in log2 units.
+        // The running maximum m only moves when a row's new maximum exceeds it
+        // by more than kRebase: probabilities exp2(s*sl - m) stay below
+        // 2^kRebase and the output and sum are rescaled far less often (the
+        // final division uses the same m for both, so the result is the same).
+        float mxs[CTILES];
+        bool need = false;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4_t*)(vrow0 + 16 * dt));
-        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) short4_t*)(vrow1 + 16 * dt));
-        const u32x2_t wlo = __builtin_bit_cast(u32x2_t, lo);
-        const u32x2_t whi = __builtin_bit_cast(u32x2_t, hi);
-        const u32x4 vop = {wlo[0], wlo[1], whi[0], whi[1]};
+        for (int ct = 0; ct < CTILES; ++ct) {
+          float mx = kNegInf;
 #pragma unroll
-        for (int ct = 0; ct < CTILES; ++ct) o[ct][dt] = mfma32<QT>(pop[ct], vop, o[ct][dt]);
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, st[kt][ct][rr]);
+          mxs[ct] = cmax4(mx) * sl;
+          need |= mxs[ct] > m[ct] + kRebase;
+        }
+        if (__any(need)) {
+#pragma unroll
+          for (int ct = 0; ct < CTILES; ++ct) {
+            const float mnew = mxs[ct] > m[ct] + kRebase ? mxs[ct] : m[ct];
+            const float alpha = __builtin_amdgcn_exp2f(m[ct] - mnew);     // 1 for rows that keep m
+            m[ct] = mnew;
+            lsum[ct] *= alpha;
+            float ar[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) ar[rr] = lane_value(alpha, 4 * j + rr);
+#pragma unroll
+            for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) o[ct][dt][rr] *= ar[rr];
+          }
+        }
+        u32x4 pop[CTILES];
+#pragma unroll
+        for (int ct = 0; ct < CTILES; ++ct) {
+          float p[2][4];
+          float ps = 0.0f;
+#pragma unroll
+          for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              p[kt][rr] = __builtin_amdgcn_exp2f(fmaf(st[kt][ct][rr], sl, -m[ct]));
+              ps += p[kt][rr];
+            }
+          lsum[ct] += ps;
+          if constexpr (kFp8) {
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+              const float4 vsc = *reinterpret_cast<const float4*>(sm_vs + 32 * hv + kt * 16 + 4 * j);
+              p[kt][0] *= vsc.x;
+              p[kt][1] *= vsc.y;
+              p[kt][2] *= vsc.z;
+              p[kt][3] *= vsc.w;
+            }
+          }
+          pop[ct][0] = pack_pair<QT>(p[0][0], p[0][1]);
+          pop[ct][1] = pack_pair<QT>(p[0][2], p[0][3]);
+          pop[ct][2] = pack_pair<QT>(p[1][0], p[1][1]);
+          pop[ct][3] = pack_pair<QT>(p[1][2], p[1][3]);
+        }
+
+        // O += P V.  B operand (32 keys x 16 d) by transpose reads: lane c of
+        // group j points at V[key 4j + c/4 (+16)][d0 + 4(c%4) ..+3] and
+        // receives V[key 4j + e (+16)][d0 + c] for e = 0..3, the keys of its P
+        // slots.
+        const int vr0 = 32 * hv + 4 * j + (c >> 2);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const int vq = 2 * dt + ((c & 3) >> 1);
+          const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4_t*)(vbuf + vaddr(vr0, vq, c & 1)));
+          const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) short4_t*)(vbuf + vaddr(vr0 + 16, vq, c & 1)));
+          const u32x2_t wlo = __builtin_bit_cast(u32x2_t, lo);
+          const u32x2_t whi = __builtin_bit_cast(u32x2_t, hi);
+          const u32x4 vop = {wlo[0], wlo[1], whi[0], whi[1]};
+#pragma unroll
+          for (int ct = 0; ct < CTILES; ++ct) o[ct][dt] = mfma32<QT>(pop[ct], vop, o[ct][dt]);
+        }
+        __builtin_amdgcn_s_setprio(0);
       }
+  };
+
+  if constexpr (kFp8) {
+    // ---- fp8: global -> registers -> (convert) -> LDS, one buffer ----------------
+    IO io;
+    // round r of thread t moves stage bytes (r*256 + t)*16: a fixed row of the
+    // stage (so a fixed block of its 4 and row within it) and column
+    int thr_off[IO::rounds], thr_blk[IO::rounds], thr_row[IO::rounds];
+#pragma unroll
+    for (int r = 0; r < IO::rounds; ++r) {
+      const int byte = (r * kPfThreads + tid) * 16;
+      thr_row[r] = byte / IO::row_bytes;
+      thr_blk[r] = thr_row[r] / kBlockTokens;
+      thr_off[r] = (thr_row[r] % kBlockTokens) * IO::row_bytes + byte % IO::row_bytes;
     }
-    __syncthreads();   // every wave is done with this stage's LDS
+    auto load_stage = [&](int s) {
+      const int kb = s * kPfKeys;
+#pragma unroll
+      for (int r = 0; r < IO::rounds; ++r) {
+        if (kb + thr_row[r] < key_end) {
+          const int id = sm_ids[4 * s + thr_blk[r]];
+          const int64_t off = static_cast<int64_t>(id * a.num_kv_heads + g) * IO::tile_bytes + thr_off[r];
+          io.k[r] = *reinterpret_cast<const u32x4*>(kpool + off);
+          io.v[r] = *reinterpret_cast<const u32x4*>(vpool + off);
+        } else {
+          io.k[r] = u32x4{0u, 0u, 0u, 0u};
+          io.v[r] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+      io.ks = 0.0f;
+      if (tid < 2 * kPfKeys) {
+        const int key = kb + (tid % kPfKeys);
+        if (key < key_end) {
+          const int id = sm_ids[key / kBlockTokens];
+          const int64_t si = static_cast<int64_t>(id * a.num_kv_heads + g) * kBlockTokens + key % kBlockTokens;
+          io.ks = tid < kPfKeys ? a.k_scale[si] : a.v_scale[si];
+        }
+      }
+    };
+    auto store_stage = [&]() {
+#pragma unroll
+      for (int r = 0; r < IO::rounds; ++r) {
+        const int byte = (r * kPfThreads + tid) * 16;
+        const int row = byte / IO::row_bytes;
+        const int e = byte % IO::row_bytes;                   // first element (one byte each)
+        uint16_t* kd = sm_k + row * IO::lds_row + e;
+        uint16_t* vd = sm_v + row * IO::lds_row + e;
+        reinterpret_cast<u32x4*>(kd)[0] = fp8x8_to_16<QT>(io.k[r][0], io.k[r][1]);
+        reinterpret_cast<u32x4*>(kd)[1] = fp8x8_to_16<QT>(io.k[r][2], io.k[r][3]);
+        reinterpret_cast<u32x4*>(vd)[0] = fp8x8_to_16<QT>(io.v[r][0], io.v[r][1]);
+        reinterpret_cast<u32x4*>(vd)[1] = fp8x8_to_16<QT>(io.v[r][2], io.v[r][3]);
+      }
+      if (tid < kPfKeys) sm_ks[tid] = io.ks;
+      else if (tid < 2 * kPfKeys) sm_vs[tid - kPfKeys] = io.ks;
+    };
+    load_stage(0);
+    for (int s = 0; s < nstages; ++s) {
+      store_stage();
+      __syncthreads();
+      if (s + 1 < nstages) load_stage(s + 1);
+      compute(reinterpret_cast<const uint8_t*>(sm_k), reinterpret_cast<const uint8_t*>(sm_v), s);
+      __syncthreads();   // every wave is done with this stage's LDS
+    }
+  } else {
+    // ---- 16-bit caches: global -> LDS directly, two buffers ----------------------
+    // Wave w moves block w of each stage (rows 16w .. 16w+15): kInsts
+    // instructions per tensor, lane i of instruction n filling stage chunk
+    // 64n + i, i.e. row (64n+i)/CH at swizzled position (64n+i)%CH.
+    constexpr int CH = IO::row_bytes / 16;                  // chunks per row
+    constexpr int kInsts = CH / 4;
+    static_assert(kPfKeys * CH == kPfWaves * kInsts * kWave, "one block per wave");
+    int lane_off[kInsts];
+#pragma unroll
+    for (int k = 0; k < kInsts; ++k) {
+      const int slot = (wave * kInsts + k) * kWave + lane;
+      const int r = slot / CH;
+      const int q = (slot % CH) ^ LdsSwz<D>::of(r);
+      lane_off[k] = (r % kBlockTokens) * IO::row_bytes + 16 * q;
+    }
+    auto dma = [&](uint8_t* kdst, uint8_t* vdst, int s) {
+      // rows past the context (last stage) read the sequence's last block
+      // and are zeroed after they land
+      const int id = sm_ids[min(4 * s + wave, nblk - 1)];
+      const int64_t base = static_cast<int64_t>(id * a.num_kv_heads + g) * IO::tile_bytes;
+#pragma unroll
+      for (int k = 0; k < kInsts; ++k) {
+        const int dst = (wave * kInsts + k) * kWave * 16;
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kpool + base + lane_off[k]),
+                                         (__attribute__((address_space(3))) void*)(kdst + dst), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vpool + base + lane_off[k]),
+                                         (__attribute__((address_space(3))) void*)(vdst + dst), 16, 0, 0);
+      }
+    };
+    // V rows at or past key_end of the last stage are zeroed by the wave that
+    // loaded them (after its own loads landed): P is 0 there, and 0 times a
+    // stale NaN would still be NaN.  K needs no care: those keys are masked.
+    auto zero_tail = [&](uint8_t* vdst, int s) {
+      const int first = max(key_end - s * kPfKeys, 16 * wave);
+      const int rows = 16 * wave + 16 - first;
+      for (int idx = lane; idx < max(rows, 0) * CH; idx += kWave)
+        *reinterpret_cast<u32x4*>(vdst + (first + idx / CH) * IO::row_bytes + 16 * (idx % CH)) = u32x4{0u, 0u, 0u, 0u};
+    };
+    auto step = [&](uint8_t* kc, uint8_t* vc, uint8_t* kn, uint8_t* vn, int s) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's loads of stage s landed
+      if (s == nstages - 1) zero_tail(vc, s);
+      __syncthreads();                                      // all of stage s is in LDS; stage s-1 is done
+      if (s + 1 < nstages) dma(kn, vn, s + 1);
+      compute(kc, vc, s);
+    };
+    uint8_t* k0 = reinterpret_cast<uint8_t*>(sm_kd[0]);
+    uint8_t* k1 = reinterpret_cast<uint8_t*>(sm_kd[1]);
+    uint8_t* v0 = reinterpret_cast<uint8_t*>(sm_vd[0]);
+    uint8_t* v1 = reinterpret_cast<uint8_t*>(sm_vd[1]);
+    dma(k0, v0, 0);
+    for (int s = 0; s < nstages; s += 2) {
+      step(k0, v0, k1, v1, s);
+      if (s + 1 < nstages) step(k1, v1, k0, v0, s + 1);
+    }
   }
 
   // ---- normalise and store -------------------------------------------------------
