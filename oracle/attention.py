@@ -22,7 +22,7 @@ import math
 
 import numpy as np
 
-from . import fp8_e4m3
+from . import kv_formats
 from .cache import Pool
 
 
@@ -67,13 +67,10 @@ def decode_paged(q: np.ndarray, pool: Pool, block_tables, context_lens, scale: f
 
 def rows_as_cached(k_rows: np.ndarray, v_rows: np.ndarray, cache_dtype: str):
     """The float64 values a cache of ``cache_dtype`` holds for token rows
-    ``[L][Hkv][D]``: the rows themselves, or for fp8 the dequantised codes
-    (each (token, head) row quantised with its own scale)."""
-    if cache_dtype == "fp8_e4m3":
-        kc, ks = fp8_e4m3.quantise_rows(k_rows)
-        vc, vs = fp8_e4m3.quantise_rows(v_rows)
-        return fp8_e4m3.dequantise(kc, ks), fp8_e4m3.dequantise(vc, vs)
-    return np.asarray(k_rows, dtype=np.float64), np.asarray(v_rows, dtype=np.float64)
+    ``[L][Hkv][D]``: the rows themselves, or for a quantised format the
+    dequantised codes (each (token, head) row quantised with its own scale)."""
+    k_elem, v_elem = kv_formats.FORMATS[cache_dtype]
+    return kv_formats.values_as_cached(k_rows, k_elem), kv_formats.values_as_cached(v_rows, v_elem)
 
 
 def partition_state(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float,

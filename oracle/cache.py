@@ -9,8 +9,9 @@ physical block that holds it.
 In-block layout (a reading; the pages fix only the 16-token block): for each
 physical block and each KV head, the 16 token rows of head_dim elements are
 contiguous, i.e. the pool is ``[num_blocks][num_kv_heads][16][head_dim]``.
-fp8 pools carry one float32 scale per (block, head, token) in
-``[num_blocks][num_kv_heads][16]``.
+Quantised pools carry one float32 scale per (block, head, token) in
+``[num_blocks][num_kv_heads][16]``; an INT4 pool holds two codes per byte,
+``[num_blocks][num_kv_heads][16][head_dim / 2]``.
 
 Test infrastructure: only tests, the smoke check and the CPU baseline leg of
 the benchmark use this module.
@@ -19,7 +20,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import fp8_e4m3
+from . import kv_formats
 
 BLOCK_TOKENS = 16
 
@@ -39,74 +40,98 @@ def slot_of(table_row, position: int) -> int:
 class Pool:
     """One layer's K and V pools.
 
-    Same-dtype pools keep float64 values (exact copies of the written rows) and
-    a written-mask; fp8 pools keep the e4m3 codes, the float32 scales and the
-    written-mask.  Unwritten slots are undefined in the GPU pool and are never
-    compared."""
+    Formats (``kv_formats.FORMATS``): unquantised pools keep float64 values
+    (exact copies of the written rows); quantised ones keep what the GPU
+    pool holds - the codes (int4: two per byte) and one float32 scale per
+    (block, head, token).  K and V may use different element formats.  A
+    written-mask marks filled slots; unwritten slots are undefined in the GPU
+    pool and are never compared."""
 
     def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, cache_dtype: str):
         self.num_blocks = num_blocks
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
         self.cache_dtype = cache_dtype
+        self.k_elem, self.v_elem = kv_formats.FORMATS[cache_dtype]
         shape = (num_blocks, num_kv_heads, BLOCK_TOKENS, head_dim)
         self.written = np.zeros((num_blocks, BLOCK_TOKENS), dtype=bool)
-        if cache_dtype == "fp8_e4m3":
-            self.k_codes = np.zeros(shape, dtype=np.uint8)
-            self.v_codes = np.zeros(shape, dtype=np.uint8)
-            self.k_scale = np.zeros(shape[:3], dtype=np.float32)
-            self.v_scale = np.zeros(shape[:3], dtype=np.float32)
-        else:
-            self.k = np.zeros(shape, dtype=np.float64)
-            self.v = np.zeros(shape, dtype=np.float64)
+        self.store = {}
+        for name, elem in (("k", self.k_elem), ("v", self.v_elem)):
+            if kv_formats.is_quantised(elem):
+                width = head_dim // 2 if elem == "i4" else head_dim
+                self.store[name] = (np.zeros(shape[:3] + (width,), dtype=np.uint8),
+                                    np.zeros(shape[:3], dtype=np.float32))
+            else:
+                self.store[name] = (np.zeros(shape, dtype=np.float64), None)
+
+    # the e4m3 attribute names used by tests that read codes and scales
+    @property
+    def k_codes(self):
+        return self.store["k"][0]
+
+    @property
+    def v_codes(self):
+        return self.store["v"][0]
+
+    @property
+    def k_scale(self):
+        return self.store["k"][1]
+
+    @property
+    def v_scale(self):
+        return self.store["v"][1]
+
+    @property
+    def k(self):
+        return self.store["k"][0]
+
+    @property
+    def v(self):
+        return self.store["v"][0]
 
     # -- writes -------------------------------------------------------------
     def append(self, k_rows: np.ndarray, v_rows: np.ndarray, slots) -> None:
         """Write token rows ``[n][Hkv][D]`` to their slots (a negative slot means
-        "skip this row").  Same dtype: an exact copy of the values.  fp8: each
-        (token, head) row is quantised with its own scale."""
+        "skip this row").  Unquantised: an exact copy of the values.  Quantised:
+        each (token, head) row is quantised with its own scale."""
         slots = np.asarray(slots, dtype=np.int64)
         keep = slots >= 0
         slots = slots[keep]
-        k_rows = np.asarray(k_rows)[keep]
-        v_rows = np.asarray(v_rows)[keep]
         blk = slots // BLOCK_TOKENS
         off = slots % BLOCK_TOKENS
         if np.any(blk >= self.num_blocks):
             raise IndexError("slot outside the pool")
-        if self.cache_dtype == "fp8_e4m3":
-            kc, ks = fp8_e4m3.quantise_rows(k_rows)
-            vc, vs = fp8_e4m3.quantise_rows(v_rows)
-            self.k_codes[blk, :, off, :] = kc
-            self.v_codes[blk, :, off, :] = vc
-            self.k_scale[blk, :, off] = ks
-            self.v_scale[blk, :, off] = vs
-        else:
-            self.k[blk, :, off, :] = k_rows
-            self.v[blk, :, off, :] = v_rows
+        for name, rows, elem in (("k", k_rows, self.k_elem), ("v", v_rows, self.v_elem)):
+            rows = np.asarray(rows)[keep]
+            data, scales = self.store[name]
+            if scales is None:
+                data[blk, :, off, :] = rows
+            else:
+                codes, sc = kv_formats.quantise(rows, elem)
+                data[blk, :, off, :] = codes
+                scales[blk, :, off] = sc
         self.written[blk, off] = True
 
     def copy_block(self, src: int, dst: int) -> None:
-        """Copy-on-write: the whole block (every head and slot, plus fp8 scales)."""
-        if self.cache_dtype == "fp8_e4m3":
-            self.k_codes[dst] = self.k_codes[src]
-            self.v_codes[dst] = self.v_codes[src]
-            self.k_scale[dst] = self.k_scale[src]
-            self.v_scale[dst] = self.v_scale[src]
-        else:
-            self.k[dst] = self.k[src]
-            self.v[dst] = self.v[src]
+        """Copy-on-write: the whole block (every head and slot, plus scales)."""
+        for data, scales in self.store.values():
+            data[dst] = data[src]
+            if scales is not None:
+                scales[dst] = scales[src]
         self.written[dst] = self.written[src]
 
     # -- reads --------------------------------------------------------------
     def read_slots(self, blocks, offsets):
         """float64 K and V rows ``[n][Hkv][D]`` stored at the given slots
-        (dequantised with their scales for fp8)."""
-        if self.cache_dtype == "fp8_e4m3":
-            k = fp8_e4m3.dequantise(self.k_codes[blocks, :, offsets, :], self.k_scale[blocks, :, offsets])
-            v = fp8_e4m3.dequantise(self.v_codes[blocks, :, offsets, :], self.v_scale[blocks, :, offsets])
-            return k, v
-        return self.k[blocks, :, offsets, :], self.v[blocks, :, offsets, :]
+        (dequantised with their scales for quantised formats)."""
+        out = []
+        for name, elem in (("k", self.k_elem), ("v", self.v_elem)):
+            data, scales = self.store[name]
+            if scales is None:
+                out.append(data[blocks, :, offsets, :])
+            else:
+                out.append(kv_formats.dequantise(data[blocks, :, offsets, :], scales[blocks, :, offsets], elem))
+        return out[0], out[1]
 
     def gather(self, table_row, length: int):
         """K, V ``[length][Hkv][D]`` float64 of one sequence, read through its

@@ -6,17 +6,19 @@ off-by-one position, a reversed free order, a copy-on-write that skips the
 copy, a prefix cache that evicts by plain recency, keys a block by its own
 tokens only, lets a lookup cover the last prompt token or forgets released
 blocks, a prefill mask that hides the diagonal or a chunk placed at the
-start of the sequence - must make at least one of the pins fail.  This shows the pins are
+start of the sequence, a wrong e5m2 bias, swapped int4 nibbles or integer
+rounding with ties up - must make at least one of the pins fail.  This shows the pins are
 sharp enough to catch the mistakes they are meant to catch."""
 import numpy as np
 import pytest
 
 from oracle import allocator as alloc_mod
-from oracle import attention, cache, fp8_e4m3, prefill
+from oracle import attention, cache, fp8_e4m3, kv_formats, prefill
 from oracle.allocator import BLOCK_TOKENS as BLOCK
 from tests import test_oracle_allocator as pins_alloc
 from tests import test_oracle_attention as pins_attn
 from tests import test_oracle_fp8 as pins_fp8
+from tests import test_oracle_kv_formats as pins_formats
 from tests import test_oracle_prefill as pins_prefill
 from tests import test_oracle_prefix_cache as pins_prefix
 
@@ -211,3 +213,29 @@ def _prefill_with(q, K, V, scale, first_key_hidden=False, chunk_at_start=False):
 def test_prefill_mutants_are_caught(monkeypatch, kw):
     monkeypatch.setattr(prefill, "prefill_rows", lambda q, K, V, s: _prefill_with(q, K, V, s, **kw))
     _fails(pins_prefill.test_matches_torch_sdpa_with_shifted_causal_mask, 4, 2, 64, 40, 7)
+
+
+# ---- cache-format mutants -------------------------------------------------------------------
+
+def test_wrong_e5m2_bias_is_caught(monkeypatch):
+    monkeypatch.setattr(kv_formats, "_E5M2_BIAS", 16)
+    _fails(pins_formats.test_e5m2_decode_matches_torch)
+
+
+def test_swapped_nibbles_are_caught(monkeypatch):
+    def swapped(codes):
+        c = np.asarray(codes, dtype=np.int16)
+        u = (c & 0xF).astype(np.uint8)
+        return (u[..., 1::2] | (u[..., 0::2] << 4)).astype(np.uint8)
+    monkeypatch.setattr(kv_formats, "pack_int4", swapped)
+    _fails(pins_formats.test_int4_packing_bytes)
+
+
+def test_int_ties_up_are_caught(monkeypatch):
+    def half_up(x, qmax):
+        x = np.asarray(x, dtype=np.float32)
+        s = kv_formats._row_scales(x, qmax)
+        y = np.clip((x / s[..., None]).astype(np.float32), -qmax, qmax)
+        return np.floor(y + np.float32(0.5)).astype(np.int8), s
+    monkeypatch.setattr(kv_formats, "quantise_int_rows", half_up)
+    _fails(pins_formats.test_int_codes_are_nearest_with_ties_to_even, 7)
