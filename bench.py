@@ -211,7 +211,7 @@ def main():
     log(f"[bench] workload {args.config} {w.name}: B={B} Hq={hq} Hkv={hkv} D={D} cache={w.cache_dtype} "
         f"layers={layers} pool={w.num_blocks} blocks/layer ({per_layer_bytes / 2**30:.2f} GiB/layer)")
 
-    cache = PagedKVCache(layers, w.num_blocks, hkv, D, TORCH_DTYPES[w.cache_dtype], w.max_blocks_per_seq,
+    cache = PagedKVCache(layers, w.num_blocks, hkv, D, w.cache_dtype, w.max_blocks_per_seq,
                          device=dev)
     gen = torch.Generator(device=dev)
     src_t = TORCH_DTYPES[w.src_dtype]
@@ -268,9 +268,9 @@ def main():
     d_slots = torch.zeros(B, dtype=torch.int64, device=dev)
     max_possible = max(w.context_lens) + n_steps
     ws = torch.zeros(max(1, pkv.workspace_size(B, hq, hkv, D, max_possible, args.partition_size,
-                                               pkv.dtype_code(cache.cache_dtype))), dtype=torch.uint8, device=dev)
+                                               cache.cache_code)), dtype=torch.uint8, device=dev)
     ps_used, np_used = pkv.decode_partition_size(B, hq, hkv, D, max(w.context_lens) + 1,
-                                                 pkv.dtype_code(cache.cache_dtype))
+                                                 cache.cache_code)
     if args.partition_size:
         ps_used = args.partition_size
     stream = torch.cuda.current_stream()
@@ -287,7 +287,7 @@ def main():
     lib = pkv._lib.lib()
     sp = stream.cuda_stream
     src_code = pkv.dtype_code(src_t)
-    cache_code = pkv.dtype_code(cache.cache_dtype)
+    cache_code = cache.cache_code
     q_code = pkv.dtype_code(qt)
     scale = 1.0 / math.sqrt(D)
     kv_stride = knew[0, 0].numel() * knew.element_size()

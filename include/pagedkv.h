@@ -12,7 +12,8 @@
  *     query attends over every cached token, itself included:
  *       out[h] = softmax(q[h] . K^T * scale) V,  scale = 1/sqrt(head_dim),
  *     with query head h reading KV head h / (Hq/Hkv) (grouped-query attention);
- *   - KV may be stored as fp8 e4m3 with one scale per token and per head.
+ *   - KV may be stored quantised (fp8 e4m3 or e5m2, or int8 keys with int4
+ *     values) with one scale per token and per head.
  *
  * Conventions for every call:
  *   - Return value: PKV_OK (0) or a negative PKV_ERR_* code; pkv_strerror()
@@ -48,7 +49,9 @@ typedef enum {
   PKV_F32 = 0,
   PKV_F16 = 1,
   PKV_BF16 = 2,
-  PKV_FP8_E4M3 = 3   /* OCP E4M3FN: bias 7, max 448, no infinities */
+  PKV_FP8_E4M3 = 3,  /* OCP E4M3FN: bias 7, max 448, no infinities */
+  PKV_FP8_E5M2 = 4,  /* OCP E5M2: bias 15, max 57344; stored codes are finite */
+  PKV_INT8_INT4 = 5  /* cache only: K int8 codes, V int4 codes (two per byte) */
 } pkv_dtype;
 
 enum {
@@ -70,7 +73,11 @@ const char* pkv_strerror(int code);
 /* ------------------------------------------------------------------------ */
 /* Device layouts (row-major, contiguous):                                   */
 /*   k_pool, v_pool   [num_blocks][num_kv_heads][16][head_dim] of cache dtype */
-/*   k_scale, v_scale [num_blocks][num_kv_heads][16] float32 (fp8 only)       */
+/*                    (one byte per code for fp8 and int8; PKV_INT8_INT4's V */
+/*                    pool is [num_blocks][num_kv_heads][16][head_dim / 2]   */
+/*                    bytes, element 2i in the low nibble of byte i)         */
+/*   k_scale, v_scale [num_blocks][num_kv_heads][16] float32 (quantised      */
+/*                    caches only: fp8 e4m3 / e5m2, int8 + int4)             */
 /*   slot = physical_block * 16 + (position % 16)                            */
 /* ------------------------------------------------------------------------ */
 
@@ -78,13 +85,14 @@ const char* pkv_strerror(int code);
  * kv_cache_append - write new K/V token rows into their slots.
  * Pages: "KV Cache 和 vLLM" §1.3 (each step computes the new token's K and V
  * and appends them to the layer's cache) and §3.1 (16-token blocks);
- * "KV Cache优化实战" §3.2-3.3 (fp8 KV with per-token / per-head scales).
+ * "KV Cache优化实战" §3.2-3.3 (fp8 KV with per-token / per-head scales;
+ * K and V tolerate quantisation differently, so K at int8 and V at int4).
  *
  *   k_new, v_new  device, [num_tokens][num_kv_heads][head_dim] of src_dtype
  *   k_pool, v_pool device pools (layout above) of cache_dtype
  *   k_scale, v_scale device [num_blocks][num_kv_heads][16] float32; required
- *                 when cache_dtype is PKV_FP8_E4M3, ignored (may be NULL)
- *                 otherwise
+ *                 for a quantised cache (PKV_FP8_E4M3, PKV_FP8_E5M2,
+ *                 PKV_INT8_INT4), ignored (may be NULL) otherwise
  *   slot_mapping  device int64 [num_tokens]: row i goes to slot_mapping[i];
  *                 a negative entry skips the row; entries >= 16*num_blocks
  *                 are skipped as well
@@ -94,6 +102,10 @@ const char* pkv_strerror(int code);
  *   e4m3 round-to-nearest-even of clamp(x / s, -448, 448) with x / s a
  *   correctly rounded fp32 division; codes go to the pool and s to the scale
  *   array at the same (block, head, offset).
+ * fp8 e5m2: the same with 57344 in place of 448 and e5m2 codes.
+ * int8 + int4: the same per row with 127 (K, int8 codes) and 7 (V, int4
+ *   codes), the nearest integer with ties to even; codes are two's
+ *   complement, int4 packed two per byte (even element in the low nibble).
  * Slots must be distinct within one call.  num_tokens == 0 is a no-op.
  * head_dim: 64 or 128.
  */
@@ -104,8 +116,8 @@ int kv_cache_append(const void* k_new, const void* v_new,
                     pkv_dtype src_dtype, pkv_dtype cache_dtype, void* stream);
 
 /*
- * pkv_copy_blocks - copy whole physical blocks (K, V and, for fp8, the
- * scales) from src to dst, for the copy-on-write of a shared block that one
+ * pkv_copy_blocks - copy whole physical blocks (K, V and, for a quantised
+ * cache, the scales) from src to dst, for the copy-on-write of a shared block that one
  * sequence is about to write ("KV Cache 和 vLLM" §3.3).
  *   pairs  device int32 [n_pairs][2] = {src, dst}; pairs with an entry
  *          outside [0, num_blocks) are skipped.  dst blocks must be distinct
@@ -145,7 +157,8 @@ size_t paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_
  *
  *   out           device [num_seqs][num_q_heads][head_dim] of q_dtype (written)
  *   q             device [num_seqs][num_q_heads][head_dim] of q_dtype
- *   k_pool, v_pool, k_scale, v_scale  as for kv_cache_append (scales: fp8 only)
+ *   k_pool, v_pool, k_scale, v_scale  as for kv_cache_append (scales: quantised
+ *                 caches only)
  *   block_tables  device int32 [num_seqs][max_blocks_per_seq]; entry i of row
  *                 b is the physical block of sequence b's logical block i
  *   context_lens  device int32 [num_seqs]; L_b, the tokens sequence b attends
@@ -169,8 +182,8 @@ size_t paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_
  * an all-zero output row.  Entries of the used part of a block-table row must
  * lie in [0, num_blocks); a block outside that range contributes no tokens.
  * Tokens at or beyond max_context_len (or 16*max_blocks_per_seq) are ignored.
- * dtype pairs (q / cache): f32/f32, f16/f16, bf16/bf16, bf16/fp8_e4m3,
- * f16/fp8_e4m3.  head_dim: 64 or 128.  num_q_heads/num_kv_heads: 1..16.
+ * dtype pairs (q / cache): f32/f32, f16/f16, bf16/bf16, and bf16 or f16 with
+ * fp8_e4m3, fp8_e5m2 or int8_int4.  head_dim: 64 or 128.  num_q_heads/num_kv_heads: 1..16.
  * Accumulation is fp32; the output is rounded to q_dtype (round to nearest
  * even).  The result for a given (sequence, head) depends only on the values
  * at its logical positions, not on where the blocks lie or who shares them.
@@ -200,7 +213,8 @@ int paged_attention_decode(void* out, const void* q,
  *                 position context_lens[b] - 1 (the slot the allocator handed
  *                 out for it); a negative entry writes nothing for b
  *   all other arguments as for paged_attention_decode; src_dtype as for
- *   kv_cache_append (equal to cache_dtype, or f32/f16/bf16 for an fp8 cache).
+ *   kv_cache_append (equal to cache_dtype, or f32/f16/bf16 for a quantised
+ *   cache).
  * The row of sequence b is written by the workgroup whose partition holds
  * position context_lens[b] - 1, before any K/V is read, so sequences with
  * context_lens[b] == 0 write nothing.

@@ -19,14 +19,15 @@ import torch
 from . import _lib
 
 __all__ = [
-    "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3", "BLOCK_SIZE", "PagedKVError",
+    "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3", "PKV_FP8_E5M2", "PKV_INT8_INT4", "BLOCK_SIZE",
+    "PagedKVError", "cache_code", "CACHE_FORMATS",
     "kv_cache_append", "copy_blocks", "paged_attention_decode", "paged_attention_decode_append",
     "paged_attention_decode_append_partials", "paged_attention_merge_partials",
     "workspace_size",
     "decode_partition_size", "BlockAllocator", "dtype_code", "abi_version",
 ]
 
-PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3 = 0, 1, 2, 3
+PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3, PKV_FP8_E5M2, PKV_INT8_INT4 = 0, 1, 2, 3, 4, 5
 BLOCK_SIZE = 16
 
 _TORCH_TO_CODE = {
@@ -35,6 +36,18 @@ _TORCH_TO_CODE = {
     torch.bfloat16: PKV_BF16,
     torch.float8_e4m3fn: PKV_FP8_E4M3,
     torch.uint8: PKV_FP8_E4M3,      # raw e4m3 codes
+    torch.float8_e5m2: PKV_FP8_E5M2,
+}
+
+# cache format name -> (library code, K pool torch dtype, V pool torch dtype,
+# V pool elements per K pool element)
+CACHE_FORMATS = {
+    "f32": (PKV_F32, torch.float32, torch.float32, 1),
+    "f16": (PKV_F16, torch.float16, torch.float16, 1),
+    "bf16": (PKV_BF16, torch.bfloat16, torch.bfloat16, 1),
+    "fp8_e4m3": (PKV_FP8_E4M3, torch.uint8, torch.uint8, 1),
+    "fp8_e5m2": (PKV_FP8_E5M2, torch.float8_e5m2, torch.float8_e5m2, 1),
+    "int8_int4": (PKV_INT8_INT4, torch.int8, torch.uint8, 2),   # V: two int4 codes per byte
 }
 
 
@@ -55,6 +68,19 @@ def dtype_code(t: torch.dtype) -> int:
         return _TORCH_TO_CODE[t]
     except KeyError:
         raise TypeError(f"unsupported dtype {t}") from None
+
+
+def cache_code(k_pool: torch.Tensor, v_pool: Optional[torch.Tensor] = None) -> int:
+    """Library code of the cache format the pools hold: their dtype, with an
+    int8 K pool meaning int8 keys and int4 values (V pool uint8, two codes per
+    byte, last dimension head_dim / 2)."""
+    if k_pool.dtype == torch.int8:
+        if v_pool is not None and (v_pool.dtype != torch.uint8 or v_pool.shape[-1] * 2 != k_pool.shape[-1]):
+            raise ValueError("an int8 K pool pairs with a uint8 V pool of head_dim / 2 bytes per row")
+        return PKV_INT8_INT4
+    if v_pool is not None and v_pool.dtype != k_pool.dtype:
+        raise ValueError("K and V pools must share a dtype (except int8 K with int4 V)")
+    return dtype_code(k_pool.dtype)
 
 
 def abi_version() -> int:
@@ -96,7 +122,7 @@ def kv_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tens
     _check(_lib.lib().kv_cache_append(
         _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
         _ptr(slot_mapping), int(k_new.shape[0]), hkv, d, nb, dtype_code(k_new.dtype),
-        dtype_code(k_pool.dtype), _stream(stream)), "kv_cache_append")
+        cache_code(k_pool, v_pool), _stream(stream)), "kv_cache_append")
 
 
 def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torch.Tensor,
@@ -108,7 +134,7 @@ def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torch.Tensor,
         raise ValueError("pairs must be int32 [n, 2]")
     _check(_lib.lib().pkv_copy_blocks(
         _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(pairs),
-        int(pairs.numel() // 2), hkv, d, nb, dtype_code(k_pool.dtype), _stream(stream)),
+        int(pairs.numel() // 2), hkv, d, nb, cache_code(k_pool, v_pool), _stream(stream)),
         "pkv_copy_blocks")
 
 
@@ -145,7 +171,7 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
         raise ValueError("block_tables must be [B, max_blocks], context_lens [B]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    cdt = dtype_code(k_pool.dtype)
+    cdt = cache_code(k_pool, v_pool)
     need = workspace_size(B, hq, hkv, d, max_context_len, partition_size, cdt)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         # zeroed once: the library keeps its counters zero between calls
@@ -181,7 +207,7 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Te
     _check(_lib.lib().paged_attention_prefill(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
         _ptr(context_lens), _ptr(query_start), B, T, hq, hkv, d, nb, int(block_tables.shape[1]),
-        int(max_context_len), int(max_query_len), float(scale), dtype_code(q.dtype), dtype_code(k_pool.dtype),
+        int(max_context_len), int(max_query_len), float(scale), dtype_code(q.dtype), cache_code(k_pool, v_pool),
         _stream(stream)), "paged_attention_prefill")
     return out
 
@@ -202,7 +228,7 @@ def _decode_append_call(fn_name, out, q, k_new, v_new, k_pool, v_pool, slot_mapp
         raise ValueError("block_tables and context_lens must be int32")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    cdt = dtype_code(k_pool.dtype)
+    cdt = cache_code(k_pool, v_pool)
     need = workspace_size(B, hq, hkv, d, max_context_len, partition_size, cdt)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)

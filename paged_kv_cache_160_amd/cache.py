@@ -10,8 +10,8 @@ from typing import List, Optional, Sequence, Union
 
 import torch
 
-from . import (BLOCK_SIZE, BlockAllocator, copy_blocks, kv_cache_append, paged_attention_decode,
-               paged_attention_decode_append, workspace_size, dtype_code)
+from . import (BLOCK_SIZE, CACHE_FORMATS, PKV_FP8_E4M3, PKV_FP8_E5M2, PKV_INT8_INT4, BlockAllocator, copy_blocks,
+               kv_cache_append, paged_attention_decode, paged_attention_decode_append, workspace_size)
 
 Rows = Union[torch.Tensor, Sequence[torch.Tensor]]
 
@@ -21,19 +21,30 @@ class PagedKVCache:
     table per sequence (every layer stores a token at the same slot)."""
 
     def __init__(self, num_layers: int, num_blocks: int, num_kv_heads: int, head_dim: int,
-                 cache_dtype: torch.dtype, max_blocks_per_seq: int, device="cuda"):
+                 cache_dtype, max_blocks_per_seq: int, device="cuda"):
+        """``cache_dtype``: a format name of ``CACHE_FORMATS`` ("bf16",
+        "fp8_e4m3", "fp8_e5m2", "int8_int4", ...) or a torch dtype (uint8
+        and float8_e4m3fn mean fp8 e4m3)."""
         self.num_layers = num_layers
         self.num_blocks = num_blocks
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
         self.max_blocks_per_seq = max_blocks_per_seq
         self.device = torch.device(device)
-        self.fp8 = cache_dtype in (torch.uint8, torch.float8_e4m3fn)
-        self.cache_dtype = torch.uint8 if self.fp8 else cache_dtype
+        if not isinstance(cache_dtype, str):
+            cache_dtype = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16",
+                           torch.uint8: "fp8_e4m3", torch.float8_e4m3fn: "fp8_e4m3",
+                           torch.float8_e5m2: "fp8_e5m2"}[cache_dtype]
+        self.format = cache_dtype
+        self.cache_code, k_dt, v_dt, v_per = CACHE_FORMATS[cache_dtype]
+        self.quantised = self.cache_code in (PKV_FP8_E4M3, PKV_FP8_E5M2, PKV_INT8_INT4)
+        self.fp8 = self.quantised
+        self.cache_dtype = k_dt
         shape = (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim)
-        self.k = [torch.empty(shape, dtype=self.cache_dtype, device=self.device) for _ in range(num_layers)]
-        self.v = [torch.empty(shape, dtype=self.cache_dtype, device=self.device) for _ in range(num_layers)]
-        if self.fp8:
+        vshape = (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim // v_per)
+        self.k = [torch.empty(shape, dtype=k_dt, device=self.device) for _ in range(num_layers)]
+        self.v = [torch.empty(vshape, dtype=v_dt, device=self.device) for _ in range(num_layers)]
+        if self.quantised:
             sshape = (num_blocks, num_kv_heads, BLOCK_SIZE)
             self.k_scale = [torch.empty(sshape, dtype=torch.float32, device=self.device) for _ in range(num_layers)]
             self.v_scale = [torch.empty(sshape, dtype=torch.float32, device=self.device) for _ in range(num_layers)]
@@ -117,7 +128,7 @@ class PagedKVCache:
         if out is None:
             out = torch.empty_like(q)
         need = workspace_size(q.shape[0], q.shape[1], self.num_kv_heads, self.head_dim, max_len,
-                              partition_size, dtype_code(self.cache_dtype))
+                              partition_size, self.cache_code)
         if need and (self._ws is None or self._ws.numel() < need):
             self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
         return paged_attention_decode(out, q, self.k[layer], self.v[layer], bt, lens, max_len,
@@ -140,7 +151,7 @@ class PagedKVCache:
             ql = self._layer_rows(q, layer)
             o = out[layer] if out is not None else torch.empty_like(ql)
             need = workspace_size(ql.shape[0], ql.shape[1], self.num_kv_heads, self.head_dim, max_len,
-                                  partition_size, dtype_code(self.cache_dtype))
+                                  partition_size, self.cache_code)
             if need and (self._ws is None or self._ws.numel() < need):
                 self._ws = torch.zeros(need, dtype=torch.uint8, device=self.device)
             paged_attention_decode_append(o, ql, self._layer_rows(k_rows, layer), self._layer_rows(v_rows, layer),

@@ -14,14 +14,20 @@ constexpr int kBlock = PKV_BLOCK_SIZE;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-bool valid_dtype(int d) { return d >= PKV_F32 && d <= PKV_FP8_E4M3; }
+bool valid_dtype(int d) { return d >= PKV_F32 && d <= PKV_INT8_INT4; }
+
+// Caches holding codes plus a float32 scale per (token, head).
+bool quantised(pkv_dtype c) { return c == PKV_FP8_E4M3 || c == PKV_FP8_E5M2 || c == PKV_INT8_INT4; }
+
+// dtypes K/V rows may arrive in (the cache write quantises them if needed).
+bool source_dtype(pkv_dtype d) { return d == PKV_F32 || d == PKV_F16 || d == PKV_BF16; }
 
 bool supported_head_dim(int d) { return d == 64 || d == 128; }
 
 // (q dtype, cache dtype) pairs the decode kernels are built for.
 bool decode_pair_ok(pkv_dtype q, pkv_dtype c) {
-  if (c == PKV_FP8_E4M3) return q == PKV_BF16 || q == PKV_F16;
-  return q == c;
+  if (quantised(c)) return q == PKV_BF16 || q == PKV_F16;
+  return q == c && source_dtype(q);
 }
 
 int resolve_partitions(int num_seqs, int num_kv_heads, int max_context_len, int partition_size,
@@ -88,11 +94,11 @@ int kv_cache_append(const void* k_new, const void* v_new, void* k_pool, void* v_
   if (!valid_dtype(src_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
   if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PKV_ERR_INVALID_ARG;
   if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
-  if (src_dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
-  if (cache_dtype != PKV_FP8_E4M3 && src_dtype != cache_dtype) return PKV_ERR_UNSUPPORTED;
+  if (!source_dtype(src_dtype)) return PKV_ERR_UNSUPPORTED;
+  if (!quantised(cache_dtype) && src_dtype != cache_dtype) return PKV_ERR_UNSUPPORTED;
   if (num_tokens == 0) return PKV_OK;
   if (!k_new || !v_new || !k_pool || !v_pool || !slot_mapping) return PKV_ERR_INVALID_ARG;
-  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  if (quantised(cache_dtype) && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
   if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pool) || !aligned16(v_pool))
     return PKV_ERR_INVALID_ARG;
   if (static_cast<int64_t>(num_tokens) * num_kv_heads > (static_cast<int64_t>(1) << 31))
@@ -110,7 +116,7 @@ int pkv_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
   if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
   if (n_pairs == 0) return PKV_OK;
   if (!k_pool || !v_pool || !pairs) return PKV_ERR_INVALID_ARG;
-  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  if (quantised(cache_dtype) && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
   if (!aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_INVALID_ARG;
   if (n_pairs > 65535 || num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
   return pkv::launch_copy_blocks(k_pool, v_pool, k_scale, v_scale, pairs, n_pairs, num_kv_heads,
@@ -159,18 +165,18 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new, 
   if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
   if (!decode_pair_ok(q_dtype, cache_dtype)) return PKV_ERR_UNSUPPORTED;
   if (slot_mapping) {
-    if (src_dtype == PKV_FP8_E4M3) return PKV_ERR_UNSUPPORTED;
-    if (cache_dtype != PKV_FP8_E4M3 && src_dtype != cache_dtype) return PKV_ERR_UNSUPPORTED;
+    if (!source_dtype(src_dtype)) return PKV_ERR_UNSUPPORTED;
+    if (!quantised(cache_dtype) && src_dtype != cache_dtype) return PKV_ERR_UNSUPPORTED;
   }
   if (num_q_heads / num_kv_heads > 16) return PKV_ERR_UNSUPPORTED;
   if (partition_size < 0 || partition_size % kBlock != 0 || partition_size > PKV_MAX_PARTITION_TOKENS)
     return PKV_ERR_INVALID_ARG;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_INVALID_ARG;
-  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  if (quantised(cache_dtype) && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out))
     return PKV_ERR_INVALID_ARG;
-  if (cache_dtype == PKV_FP8_E4M3 && (!aligned16(k_scale) || !aligned16(v_scale)))
+  if (quantised(cache_dtype) && (!aligned16(k_scale) || !aligned16(v_scale)))
     return PKV_ERR_INVALID_ARG;
   if (slot_mapping && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_INVALID_ARG;
 
@@ -266,7 +272,7 @@ int paged_attention_merge_partials(void* out, const int32_t* context_lens, int n
                                    int num_kv_heads, int head_dim, int max_blocks_per_seq, int max_context_len,
                                    pkv_dtype q_dtype, int partition_size, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-  if (!valid_dtype(q_dtype) || q_dtype == PKV_FP8_E4M3) return PKV_ERR_INVALID_ARG;
+  if (!valid_dtype(q_dtype) || !source_dtype(q_dtype)) return PKV_ERR_INVALID_ARG;
   if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len))
     return PKV_ERR_INVALID_ARG;
   if (max_blocks_per_seq <= 0 ||
@@ -320,11 +326,12 @@ int paged_attention_prefill(void* out, const void* q, const void* k_pool, const 
   if (max_query_len > max_context_len || max_query_len > num_tokens) return PKV_ERR_INVALID_ARG;
   if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
   if (q_dtype == PKV_F32 || !decode_pair_ok(q_dtype, cache_dtype)) return PKV_ERR_UNSUPPORTED;
+  if (cache_dtype == PKV_FP8_E5M2 || cache_dtype == PKV_INT8_INT4) return PKV_ERR_UNSUPPORTED;
   if (max_context_len > PKV_MAX_PREFILL_CONTEXT) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
     return PKV_ERR_INVALID_ARG;
-  if (cache_dtype == PKV_FP8_E4M3 && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
+  if (quantised(cache_dtype) && (!k_scale || !v_scale)) return PKV_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_pool) || !aligned16(v_pool) || !aligned16(out)) return PKV_ERR_INVALID_ARG;
 
   pkv::PrefillArgs a{};

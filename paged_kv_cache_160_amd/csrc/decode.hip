@@ -47,6 +47,15 @@ namespace pkv {
 #ifndef PKV_DECODE_WAVES
 #define PKV_DECODE_WAVES 4     // waves per workgroup
 #endif
+#ifndef PKV_DECODE_PIPE
+#define PKV_DECODE_PIPE 3      // blocks in flight per wave
+#endif
+#ifndef PKV_DECODE_NT
+#define PKV_DECODE_NT 0        // non-temporal K/V loads (measured slower: off)
+#endif
+#ifndef PKV_DECODE_MERGE
+#define PKV_DECODE_MERGE 0     // 0: merge kernel; 1: last workgroup merges (release fences)
+#endif
 constexpr int kWaves = PKV_DECODE_WAVES;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxGroup = 16;
@@ -107,76 +116,6 @@ __device__ __forceinline__ float col_sum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-// ---- per-flavour geometry -------------------------------------------------------
-//   QT: query/output type (F32, F16, BF16); CT: cache type (same, or FP8).
-template <typename QT, typename CT, int D>
-struct Geo {
-  static constexpr int ces = CT::bytes;
-  static constexpr int qes = QT::bytes;
-  static constexpr int kWords = D / 4 * ces / 4;    // K words per lane (1/4 of a row)
-  static constexpr int qWords = D / 4 * qes / 4;    // Q words per lane
-  static constexpr int DC = D / 16;                 // V columns per lane = P*V tiles
-  static constexpr int vWords = DC * ces / 4;       // V words per lane per row
-  static constexpr int tileBytes = kBlockTokens * D * ces;
-};
-
-template <typename QT, typename CT, int D>
-struct BlockRegs {
-  using G = Geo<QT, CT, D>;
-  Words<G::kWords> k;
-  Words<G::vWords> v[4];      // rows 4j..4j+3
-  float4 ks, vs;              // fp8 scales of tokens 4j..4j+3
-};
-
-// ---- QK^T on MFMA -----------------------------------------------------------------
-template <typename QT, typename CT, int D>
-__device__ __forceinline__ float4_t qk_tile(const Words<Geo<QT, CT, D>::kWords>& k,
-                                            const Words<Geo<QT, CT, D>::qWords>& q) {
-  float4_t s = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (std::is_same<CT, F32>::value) {
-#pragma unroll
-    for (int i = 0; i < D / 4; ++i)
-      s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.w[i]), __uint_as_float(q.w[i]), s, 0, 0, 0);
-  } else if constexpr (std::is_same<CT, FP8>::value) {
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      uint32_t a[4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint32_t src = k.w[2 * i + h];
-        if constexpr (std::is_same<QT, BF16>::value) {
-          a[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, false));
-          a[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, true));
-        } else {
-          a[2 * h] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, false));
-          a[2 * h + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, true));
-        }
-      }
-      uint4 av = make_uint4(a[0], a[1], a[2], a[3]);
-      uint4 bv = make_uint4(q.w[4 * i], q.w[4 * i + 1], q.w[4 * i + 2], q.w[4 * i + 3]);
-      if constexpr (std::is_same<QT, BF16>::value)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                    __builtin_bit_cast(bf16x8_t, bv), s, 0, 0, 0);
-      else
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av),
-                                                   __builtin_bit_cast(half8_t, bv), s, 0, 0, 0);
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < D / 32; ++i) {
-      uint4 av = make_uint4(k.w[4 * i], k.w[4 * i + 1], k.w[4 * i + 2], k.w[4 * i + 3]);
-      uint4 bv = make_uint4(q.w[4 * i], q.w[4 * i + 1], q.w[4 * i + 2], q.w[4 * i + 3]);
-      if constexpr (std::is_same<CT, BF16>::value)
-        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                    __builtin_bit_cast(bf16x8_t, bv), s, 0, 0, 0);
-      else
-        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av),
-                                                   __builtin_bit_cast(half8_t, bv), s, 0, 0, 0);
-    }
-  }
-  return s;
-}
-
 // Pack two fp32 values into a word of two 16-bit values of type QT (RNE).
 template <typename QT>
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
@@ -199,6 +138,116 @@ __device__ __forceinline__ float hi16_to_f32(uint32_t w) {
   else return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
 }
 
+// ---- per-flavour geometry -------------------------------------------------------
+//   QT: query/output type (F32, F16, BF16).  KT, VT: element types of the K
+//   and V pools - the query type itself, or a quantised format (FP8 e4m3,
+//   BF8 e5m2, I8, I4) with a float32 scale per (token, head).
+template <typename QT, typename KT, typename VT, int D>
+struct Geo {
+  static constexpr int qes = QT::bytes;
+  static constexpr int kRowBytes = D * KT::bits / 8;
+  static constexpr int vRowBytes = D * VT::bits / 8;
+  static constexpr int kLaneBytes = kRowBytes / 4;      // 1/4 of a K row per lane
+  static constexpr int kWords = kLaneBytes / 4;
+  static constexpr int qWords = D / 4 * qes / 4;        // Q words per lane
+  static constexpr int DC = D / 16;                     // V columns per lane = P*V tiles
+  static constexpr int vLaneBytes = DC * VT::bits / 8;  // one V row's share per lane (2..32 bytes)
+  static constexpr int vWords = vLaneBytes < 4 ? 1 : vLaneBytes / 4;
+  static constexpr int kTileBytes = kBlockTokens * kRowBytes;
+  static constexpr int vTileBytes = kBlockTokens * vRowBytes;
+};
+
+template <typename QT, typename KT, typename VT, int D>
+struct BlockRegs {
+  using G = Geo<QT, KT, VT, D>;
+  Words<G::kWords> k;
+  Words<G::vWords> v[4];      // rows 4j..4j+3
+  float4 ks, vs;              // scales of tokens 4j..4j+3 (quantised pools)
+};
+
+// One V row's share: vLaneBytes bytes (a 16-bit load for 2 bytes).
+template <int NB>
+__device__ __forceinline__ void load_vrow(Words<(NB < 4 ? 1 : NB / 4)>& dst, const uint8_t* p) {
+  if constexpr (NB == 2) dst.w[0] = *reinterpret_cast<const uint16_t*>(p);
+  else load_words<NB / 4, PKV_DECODE_NT != 0>(dst, p);
+}
+
+// ---- element conversions to the 16-bit MFMA operand type of QT ----------------
+// Four 8-bit codes (one word) -> two words of four 16-bit values, in element
+// order; every conversion is exact (e4m3, e5m2 and int8 values all fit).
+template <typename QT, typename ET>
+__device__ __forceinline__ uint2 conv8(uint32_t src) {
+  uint2 r;
+  if constexpr (std::is_same<ET, FP8>::value) {
+    if constexpr (std::is_same<QT, BF16>::value) {
+      r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, false));
+      r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, true));
+    } else {
+      r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, false));
+      r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, true));
+    }
+  } else if constexpr (std::is_same<ET, BF8>::value) {
+    if constexpr (std::is_same<QT, BF16>::value) {
+      r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(src, 1.0f, false));
+      r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(src, 1.0f, true));
+    } else {
+      r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(src, 1.0f, false));
+      r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(src, 1.0f, true));
+    }
+  } else {
+    static_assert(std::is_same<ET, I8>::value, "8-bit format");
+    const float f0 = static_cast<float>(static_cast<int8_t>(src & 0xffu));
+    const float f1 = static_cast<float>(static_cast<int8_t>((src >> 8) & 0xffu));
+    const float f2 = static_cast<float>(static_cast<int8_t>((src >> 16) & 0xffu));
+    const float f3 = static_cast<float>(static_cast<int8_t>(src >> 24));
+    r.x = pack2<QT>(f0, f1);
+    r.y = pack2<QT>(f2, f3);
+  }
+  return r;
+}
+
+// Nibble i of w (two's complement) as a float.
+__device__ __forceinline__ float nib(uint32_t w, int i) {
+  return static_cast<float>(static_cast<int32_t>(w << (28 - 4 * i)) >> 28);
+}
+
+// K operand words of MFMA i (8 contraction elements) from the lane's K words.
+template <typename QT, typename KT, int D>
+__device__ __forceinline__ uint4 k_operand(const Words<Geo<QT, KT, KT, D>::kWords>& k, int i) {
+  if constexpr (KT::bits == 16) {
+    return make_uint4(k.w[4 * i], k.w[4 * i + 1], k.w[4 * i + 2], k.w[4 * i + 3]);
+  } else {
+    const uint2 lo = conv8<QT, KT>(k.w[2 * i]);
+    const uint2 hi = conv8<QT, KT>(k.w[2 * i + 1]);
+    return make_uint4(lo.x, lo.y, hi.x, hi.y);
+  }
+}
+
+// ---- QK^T on MFMA -----------------------------------------------------------------
+template <typename QT, typename KT, int D>
+__device__ __forceinline__ float4_t qk_tile(const Words<Geo<QT, KT, KT, D>::kWords>& k,
+                                            const Words<Geo<QT, KT, KT, D>::qWords>& q) {
+  float4_t s = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (std::is_same<KT, F32>::value) {
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i)
+      s = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(k.w[i]), __uint_as_float(q.w[i]), s, 0, 0, 0);
+  } else {
+#pragma unroll
+    for (int i = 0; i < D / 32; ++i) {
+      const uint4 av = k_operand<QT, KT, D>(k, i);
+      const uint4 bv = make_uint4(q.w[4 * i], q.w[4 * i + 1], q.w[4 * i + 2], q.w[4 * i + 3]);
+      if constexpr (std::is_same<QT, BF16>::value)
+        s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
+                                                    __builtin_bit_cast(bf16x8_t, bv), s, 0, 0, 0);
+      else
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, av),
+                                                   __builtin_bit_cast(half8_t, bv), s, 0, 0, 0);
+    }
+  }
+  return s;
+}
+
 template <typename QT>
 __device__ __forceinline__ float4_t mfma16(uint2 a, uint2 b, float4_t c) {
   if constexpr (std::is_same<QT, BF16>::value)
@@ -210,12 +259,13 @@ __device__ __forceinline__ float4_t mfma16(uint2 a, uint2 b, float4_t c) {
 }
 
 // ---- P*V on MFMA -----------------------------------------------------------------
-// p[r]: probability (times the fp8 V scale) of token 4j+r for head column c.
-template <typename QT, typename CT, int D>
-__device__ __forceinline__ void pv_tile(const float (&p)[4], const Words<Geo<QT, CT, D>::vWords> (&v)[4],
+// p[r]: probability (times the V scale of a quantised pool) of token 4j+r for
+// head column c.
+template <typename QT, typename VT, int D>
+__device__ __forceinline__ void pv_tile(const float (&p)[4], const Words<Geo<QT, VT, VT, D>::vWords> (&v)[4],
                                         float4_t (&o)[D / 16]) {
-  using G = Geo<QT, CT, D>;
-  if constexpr (std::is_same<CT, F32>::value) {
+  using G = Geo<QT, VT, VT, D>;
+  if constexpr (std::is_same<VT, F32>::value) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -233,21 +283,20 @@ __device__ __forceinline__ void pv_tile(const float (&p)[4], const Words<Geo<QT,
     uint32_t w16[4][G::DC / 2];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if constexpr (std::is_same<CT, FP8>::value) {
-#pragma unroll
-        for (int i = 0; i < G::vWords; ++i) {
-          uint32_t src = v[e].w[i];
-          if constexpr (std::is_same<QT, BF16>::value) {
-            w16[e][2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, false));
-            w16[e][2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(src, 1.0f, true));
-          } else {
-            w16[e][2 * i] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, false));
-            w16[e][2 * i + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(src, 1.0f, true));
-          }
-        }
-      } else {
+      if constexpr (VT::bits == 16) {
 #pragma unroll
         for (int i = 0; i < G::vWords; ++i) w16[e][i] = v[e].w[i];
+      } else if constexpr (VT::bits == 8) {
+#pragma unroll
+        for (int i = 0; i < G::vWords; ++i) {
+          const uint2 c2 = conv8<QT, VT>(v[e].w[i]);
+          w16[e][2 * i] = c2.x;
+          w16[e][2 * i + 1] = c2.y;
+        }
+      } else {
+        static_assert(std::is_same<VT, I4>::value, "4-bit format");
+#pragma unroll
+        for (int i = 0; i < G::DC / 2; ++i) w16[e][i] = pack2<QT>(nib(v[e].w[0], 2 * i), nib(v[e].w[0], 2 * i + 1));
       }
     }
 #pragma unroll
@@ -265,20 +314,12 @@ __device__ __forceinline__ void pv_tile(const float (&p)[4], const Words<Geo<QT,
 
 // ---- the main kernel ------------------------------------------------------------
 
-#ifndef PKV_DECODE_PIPE
-#define PKV_DECODE_PIPE 3      // blocks in flight per wave
-#endif
-#ifndef PKV_DECODE_NT
-#define PKV_DECODE_NT 0        // non-temporal K/V loads (measured slower: off)
-#endif
-#ifndef PKV_DECODE_MERGE
-#define PKV_DECODE_MERGE 0     // 0: merge kernel; 1: last workgroup merges (release fences)
-#endif
 
-template <typename QT, typename CT, int D, int PIPE>
+template <typename QT, typename KT, typename VT, int D, int PIPE>
 __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a) {
-  using G = Geo<QT, CT, D>;
-  constexpr bool kFp8 = std::is_same<CT, FP8>::value;
+  using G = Geo<QT, KT, VT, D>;
+  constexpr bool kQK = KT::quantised;
+  constexpr bool kQV = VT::quantised;
   constexpr float kNegInf = -INFINITY;
 
   __shared__ float sm_m[kWaves][kMaxGroup];
@@ -334,8 +375,8 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
 
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k_pool);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v_pool);
-  const int64_t k_lane = static_cast<int64_t>(c * D + j * (D / 4)) * G::ces;
-  const int64_t v_lane = static_cast<int64_t>((4 * j) * D + G::DC * c) * G::ces;
+  const int64_t k_lane = static_cast<int64_t>(c) * G::kRowBytes + j * G::kLaneBytes;
+  const int64_t v_lane = static_cast<int64_t>(4 * j) * G::vRowBytes + c * G::vLaneBytes;
 
   // Fused cache write: the workgroup whose partition holds the sequence's
   // last position writes this step's K and V rows for its KV head (wave 0:
@@ -346,17 +387,21 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
     if (slot >= 0 && slot < static_cast<int64_t>(a.num_blocks) * kBlockTokens) {
       const int64_t dst_row = ((slot / kBlockTokens) * a.num_kv_heads + g) * kBlockTokens + slot % kBlockTokens;
       const int64_t src_row = static_cast<int64_t>(b) * a.num_kv_heads + g;
-      const void* src = wave == 0 ? a.k_new : a.v_new;
-      void* pool = const_cast<void*>(wave == 0 ? a.k_pool : a.v_pool);
-      if constexpr (kFp8) {
-        float* scales = const_cast<float*>(wave == 0 ? a.k_scale : a.v_scale);
-        auto* p8 = static_cast<uint8_t*>(pool);
-        if (a.src_dtype == PKV_F32) write_row_fp8<F32, D>(src, src_row, p8, scales, dst_row, lane);
-        else if (a.src_dtype == PKV_F16) write_row_fp8<F16, D>(src, src_row, p8, scales, dst_row, lane);
-        else write_row_fp8<BF16, D>(src, src_row, p8, scales, dst_row, lane);
-      } else {
-        write_row_copy(src, src_row, pool, dst_row, D * G::ces, lane);
-      }
+      auto write = [&](auto tag, const void* src, const void* pool_c, const float* scales_c) {
+        using T = decltype(tag);
+        void* pool = const_cast<void*>(pool_c);
+        if constexpr (T::quantised) {
+          float* scales = const_cast<float*>(scales_c);
+          auto* p8 = static_cast<uint8_t*>(pool);
+          if (a.src_dtype == PKV_F32) write_row_quant<F32, D, T>(src, src_row, p8, scales, dst_row, lane);
+          else if (a.src_dtype == PKV_F16) write_row_quant<F16, D, T>(src, src_row, p8, scales, dst_row, lane);
+          else write_row_quant<BF16, D, T>(src, src_row, p8, scales, dst_row, lane);
+        } else {
+          write_row_copy(src, src_row, pool, dst_row, D * T::bytes, lane);
+        }
+      };
+      if (wave == 0) write(KT{}, a.k_new, a.k_pool, a.k_scale);
+      else write(VT{}, a.v_new, a.v_pool, a.v_scale);
     }
   }
 
@@ -369,21 +414,18 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
 
   // Load one block's K/V (and scales) for this lane.  Blocks whose physical
   // id lies outside the pool are read from block 0 and fully masked.
-  auto load_block = [&](BlockRegs<QT, CT, D>& r, int i, bool& ok) {
+  auto load_block = [&](BlockRegs<QT, KT, VT, D>& r, int i, bool& ok) {
     int phys = __builtin_amdgcn_readfirstlane(sm_ids[i]);
     ok = phys >= 0 && phys < a.num_blocks;
     if (!ok) phys = 0;
     const int64_t tile = static_cast<int64_t>(phys) * a.num_kv_heads + g;
-    const uint8_t* kt = kbase + tile * G::tileBytes;
-    const uint8_t* vt = vbase + tile * G::tileBytes;
+    const uint8_t* kt = kbase + tile * G::kTileBytes;
+    const uint8_t* vt = vbase + tile * G::vTileBytes;
     load_words<G::kWords, PKV_DECODE_NT>(r.k, kt + k_lane);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      load_words<G::vWords, PKV_DECODE_NT>(r.v[e], vt + v_lane + static_cast<int64_t>(e) * D * G::ces);
-    if constexpr (kFp8) {
-      r.ks = *reinterpret_cast<const float4*>(a.k_scale + tile * kBlockTokens + 4 * j);
-      r.vs = *reinterpret_cast<const float4*>(a.v_scale + tile * kBlockTokens + 4 * j);
-    }
+    for (int e = 0; e < 4; ++e) load_vrow<G::vLaneBytes>(r.v[e], vt + v_lane + e * G::vRowBytes);
+    if constexpr (kQK) r.ks = *reinterpret_cast<const float4*>(a.k_scale + tile * kBlockTokens + 4 * j);
+    if constexpr (kQV) r.vs = *reinterpret_cast<const float4*>(a.v_scale + tile * kBlockTokens + 4 * j);
   };
 
   float m = kNegInf;          // running max of head column c (log2 units)
@@ -392,14 +434,16 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
 #pragma unroll
   for (int nt = 0; nt < G::DC; ++nt) o[nt] = {0.f, 0.f, 0.f, 0.f};
 
-  auto compute_block = [&](BlockRegs<QT, CT, D>& r, int i, bool ok) {
+  auto compute_block = [&](BlockRegs<QT, KT, VT, D>& r, int i, bool ok) {
     const int base = tok0 + i * kBlockTokens;   // logical position of the block's token 0
-    float4_t s = qk_tile<QT, CT, D>(r.k, qop);
+    float4_t s = qk_tile<QT, KT, D>(r.k, qop);
     float sc[4] = {s[0], s[1], s[2], s[3]};
     float ksc[4] = {1.f, 1.f, 1.f, 1.f};
     float vsc[4] = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (kFp8) {
+    if constexpr (kQK) {
       ksc[0] = r.ks.x; ksc[1] = r.ks.y; ksc[2] = r.ks.z; ksc[3] = r.ks.w;
+    }
+    if constexpr (kQV) {
       vsc[0] = r.vs.x; vsc[1] = r.vs.y; vsc[2] = r.vs.z; vsc[3] = r.vs.w;
     }
     bool valid[4];
@@ -453,7 +497,7 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
       o[nt][2] *= ar[2];
       o[nt][3] *= ar[3];
     }
-    pv_tile<QT, CT, D>(p, r.v, o);
+    pv_tile<QT, VT, D>(p, r.v, o);
   };
 
   // PIPE blocks in flight per wave: block i is computed while blocks
@@ -463,7 +507,7 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
   // order and each wait covers only the block about to be used.
   if (wave < nblk) {
     const int last = wave + kWaves * ((nblk - 1 - wave) / kWaves);
-    BlockRegs<QT, CT, D> r[PIPE];
+    BlockRegs<QT, KT, VT, D> r[PIPE];
     bool ok[PIPE];
 #pragma unroll
     for (int st = 0; st < PIPE; ++st) load_block(r[st], min(wave + st * kWaves, last), ok[st]);
@@ -642,15 +686,15 @@ int choose_partition_size(int num_seqs, int num_kv_heads, int max_context_len) {
   return static_cast<int>(blocks * kBlockTokens);
 }
 
-template <typename QT, typename CT, int D>
+template <typename QT, typename KT, typename VT, int D>
 static int launch_typed(const DecodeArgs& a, hipStream_t stream, int stages) {
   const int64_t grid = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.num_partitions;
   if (grid > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
   int rc = PKV_OK;
   if (stages & kStageAttend) {
     // fp32 tiles are twice as large: two in flight keep them in registers
-    constexpr int pipe = std::is_same<CT, F32>::value ? 2 : PKV_DECODE_PIPE;
-    hipLaunchKernelGGL((paged_decode_kernel<QT, CT, D, pipe>), dim3(static_cast<unsigned>(grid)),
+    constexpr int pipe = std::is_same<KT, F32>::value ? 2 : PKV_DECODE_PIPE;
+    hipLaunchKernelGGL((paged_decode_kernel<QT, KT, VT, D, pipe>), dim3(static_cast<unsigned>(grid)),
                        dim3(kThreads), 0, stream, a);
     rc = check_launch();
   }
@@ -659,20 +703,26 @@ static int launch_typed(const DecodeArgs& a, hipStream_t stream, int stages) {
   return check_launch();
 }
 
-template <typename QT, typename CT>
+template <typename QT, typename KT, typename VT>
 static int launch_dim(const DecodeArgs& a, hipStream_t stream, int stages) {
-  if (a.head_dim == 128) return launch_typed<QT, CT, 128>(a, stream, stages);
-  return launch_typed<QT, CT, 64>(a, stream, stages);
+  if (a.head_dim == 128) return launch_typed<QT, KT, VT, 128>(a, stream, stages);
+  return launch_typed<QT, KT, VT, 64>(a, stream, stages);
+}
+
+template <typename KT, typename VT>
+static int launch_quantised(const DecodeArgs& a, hipStream_t stream, int stages) {
+  if (a.q_dtype == PKV_BF16) return launch_dim<BF16, KT, VT>(a, stream, stages);
+  return launch_dim<F16, KT, VT>(a, stream, stages);
 }
 
 int launch_decode(const DecodeArgs& a, hipStream_t stream, int stages) {
   switch (a.cache_dtype) {
-    case PKV_F32: return launch_dim<F32, F32>(a, stream, stages);
-    case PKV_F16: return launch_dim<F16, F16>(a, stream, stages);
-    case PKV_BF16: return launch_dim<BF16, BF16>(a, stream, stages);
-    case PKV_FP8_E4M3:
-      if (a.q_dtype == PKV_BF16) return launch_dim<BF16, FP8>(a, stream, stages);
-      return launch_dim<F16, FP8>(a, stream, stages);
+    case PKV_F32: return launch_dim<F32, F32, F32>(a, stream, stages);
+    case PKV_F16: return launch_dim<F16, F16, F16>(a, stream, stages);
+    case PKV_BF16: return launch_dim<BF16, BF16, BF16>(a, stream, stages);
+    case PKV_FP8_E4M3: return launch_quantised<FP8, FP8>(a, stream, stages);
+    case PKV_FP8_E5M2: return launch_quantised<BF8, BF8>(a, stream, stages);
+    case PKV_INT8_INT4: return launch_quantised<I8, I4>(a, stream, stages);
   }
   return PKV_ERR_UNSUPPORTED;
 }

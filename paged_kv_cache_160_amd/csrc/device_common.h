@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pagedkv.h"
 
 namespace pkv {
@@ -12,21 +14,53 @@ constexpr int kBlockTokens = PKV_BLOCK_SIZE;
 constexpr int kWave = 64;
 
 // Storage tags.  Each names the element type a pool or a query holds.
+// Quantised tags (codes plus one float32 scale per (token, head) row) carry
+// qmax, the largest code magnitude the row's scale maps max|x| to.
 struct F32 {
   using storage = float;
   static constexpr int bytes = 4;
+  static constexpr int bits = 32;
+  static constexpr bool quantised = false;
 };
 struct F16 {
   using storage = uint16_t;
   static constexpr int bytes = 2;
+  static constexpr int bits = 16;
+  static constexpr bool quantised = false;
 };
 struct BF16 {
   using storage = uint16_t;
   static constexpr int bytes = 2;
+  static constexpr int bits = 16;
+  static constexpr bool quantised = false;
 };
-struct FP8 {
+struct FP8 {            // OCP e4m3 ("FN")
   using storage = uint8_t;
   static constexpr int bytes = 1;
+  static constexpr int bits = 8;
+  static constexpr bool quantised = true;
+  static constexpr float qmax = 448.0f;
+};
+struct BF8 {            // OCP e5m2
+  using storage = uint8_t;
+  static constexpr int bytes = 1;
+  static constexpr int bits = 8;
+  static constexpr bool quantised = true;
+  static constexpr float qmax = 57344.0f;
+};
+struct I8 {             // symmetric two's-complement int8
+  using storage = uint8_t;
+  static constexpr int bytes = 1;
+  static constexpr int bits = 8;
+  static constexpr bool quantised = true;
+  static constexpr float qmax = 127.0f;
+};
+struct I4 {             // symmetric two's-complement int4, two per byte (even element low)
+  using storage = uint8_t;
+  static constexpr int bytes = 1;   // per pair of elements
+  static constexpr int bits = 4;
+  static constexpr bool quantised = true;
+  static constexpr float qmax = 7.0f;
 };
 
 typedef short short4_t __attribute__((ext_vector_type(4)));
@@ -102,6 +136,40 @@ __device__ __forceinline__ uint32_t e4m3_encode_rne(float y) {
   return sign | mag;
 }
 
+// ---- OCP e5m2 encoding ---------------------------------------------------------
+// Round-to-nearest-even of a finite y with |y| <= 57344 to the E5M2 code
+// (1 sign, 5 exponent bits with bias 15, 2 mantissa bits).  Normal range
+// (|y| >= 2^-14): keep the fp32 exponent and round the mantissa to 2 bits
+// with ties to even (a carry bumps the exponent through the integer add).
+// Subnormal range: |y| * 2^16 rounded to an integer with ties to even (0..4;
+// 4 is the smallest normal code).  The sign bit copies y's sign.
+__device__ __forceinline__ uint32_t e5m2_encode_rne(float y) {
+  uint32_t bits = __float_as_uint(y);
+  uint32_t sign = (bits >> 24) & 0x80u;
+  float a = fabsf(y);
+  uint32_t mag;
+  if (a < 6.103515625e-05f) {                 // 2^-14
+    mag = static_cast<uint32_t>(__builtin_rintf(a * 65536.0f));
+  } else {
+    uint32_t abits = bits & 0x7fffffffu;
+    int32_t e = static_cast<int32_t>(abits >> 23) - 127;   // -14 .. 15
+    uint32_t m = abits & 0x7fffffu;
+    uint32_t rounded = (m + 0xfffffu + ((m >> 21) & 1u)) >> 21;   // 0 .. 4
+    mag = (static_cast<uint32_t>(e + 15) << 2) + rounded;
+  }
+  return sign | mag;
+}
+
+// Code of y (already divided by the row scale and clamped to +-qmax) in the
+// quantised format Q: an 8-bit pattern, or for I4 a nibble in the low bits.
+template <typename Q>
+__device__ __forceinline__ uint32_t quant_code(float y) {
+  if constexpr (std::is_same<Q, FP8>::value) return e4m3_encode_rne(y);
+  else if constexpr (std::is_same<Q, BF8>::value) return e5m2_encode_rne(y);
+  else if constexpr (std::is_same<Q, I8>::value) return static_cast<uint32_t>(static_cast<int32_t>(__builtin_rintf(y))) & 0xffu;
+  else return static_cast<uint32_t>(static_cast<int32_t>(__builtin_rintf(y))) & 0xfu;
+}
+
 // ---- wave reductions -----------------------------------------------------------
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -111,13 +179,15 @@ __device__ __forceinline__ float wave_max(float v) {
 
 // ---- cache-row writes ------------------------------------------------------------
 // One wave writes one (token, head) row of D elements to its pool row
-// (`dst_row` counts rows of D elements).  Same dtype: a bit copy in 16-byte
-// chunks.  fp8: a = max|x| over the row, s = a / 448 (s = 1 if a == 0),
-// codes = e4m3 RNE of clamp(x / s, -448, 448), with both divisions correctly
-// rounded in fp32; the scale goes to scales[dst_row].
-template <typename Src, int D>
-__device__ __forceinline__ void write_row_fp8(const void* src, int64_t src_row, uint8_t* pool,
-                                              float* scales, int64_t dst_row, int lane) {
+// (`dst_row` counts pool rows).  Same dtype: a bit copy in 16-byte chunks.
+// Quantised format Q: a = max|x| over the row, s = a / qmax (s = 1 if
+// a == 0), codes = quant_code(clamp(x / s, -qmax, qmax)), both divisions
+// correctly rounded in fp32; the scale goes to scales[dst_row].  Lane l holds
+// elements l*D/64 ..; I4 rows pack two codes per byte, the even element in
+// the low nibble (for D = 64 neighbouring lanes pair up).
+template <typename Src, int D, typename Q>
+__device__ __forceinline__ void write_row_quant(const void* src, int64_t src_row, uint8_t* pool,
+                                                float* scales, int64_t dst_row, int lane) {
   constexpr int kPer = D / kWave;   // 1 or 2 elements per lane
   float x[kPer];
   float amax = 0.0f;
@@ -127,22 +197,38 @@ __device__ __forceinline__ void write_row_fp8(const void* src, int64_t src_row, 
     amax = fmaxf(amax, fabsf(x[i]));
   }
   amax = wave_max(amax);
-  float s = __fdiv_rn(amax, 448.0f);
+  float s = __fdiv_rn(amax, Q::qmax);
   if (amax == 0.0f) s = 1.0f;
-  uint32_t packed = 0;
+  uint32_t code[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     float y = __fdiv_rn(x[i], s);
-    y = fminf(fmaxf(y, -448.0f), 448.0f);
-    packed |= e4m3_encode_rne(y) << (8 * i);
+    y = fminf(fmaxf(y, -Q::qmax), Q::qmax);
+    code[i] = quant_code<Q>(y);
   }
-  uint8_t* dst = pool + dst_row * D + lane * kPer;
-  if constexpr (kPer == 2) {
-    *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(packed);
+  if constexpr (std::is_same<Q, I4>::value) {
+    constexpr int row_bytes = D / 2;
+    if constexpr (kPer == 2) {
+      pool[dst_row * row_bytes + lane] = static_cast<uint8_t>(code[0] | (code[1] << 4));
+    } else {
+      const uint32_t other = static_cast<uint32_t>(__shfl_xor(static_cast<int>(code[0]), 1, kWave));
+      if ((lane & 1) == 0) pool[dst_row * row_bytes + lane / 2] = static_cast<uint8_t>(code[0] | (other << 4));
+    }
   } else {
-    *dst = static_cast<uint8_t>(packed);
+    uint8_t* dst = pool + dst_row * D + lane * kPer;
+    if constexpr (kPer == 2) {
+      *reinterpret_cast<uint16_t*>(dst) = static_cast<uint16_t>(code[0] | (code[1] << 8));
+    } else {
+      *dst = static_cast<uint8_t>(code[0]);
+    }
   }
   if (lane == 0) scales[dst_row] = s;
+}
+
+template <typename Src, int D>
+__device__ __forceinline__ void write_row_fp8(const void* src, int64_t src_row, uint8_t* pool,
+                                              float* scales, int64_t dst_row, int lane) {
+  write_row_quant<Src, D, FP8>(src, src_row, pool, scales, dst_row, lane);
 }
 
 __device__ __forceinline__ void write_row_copy(const void* src, int64_t src_row, void* pool, int64_t dst_row,

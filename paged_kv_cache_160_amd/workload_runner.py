@@ -16,7 +16,7 @@ import workloads as wl
 from .cache import PagedKVCache
 
 TORCH_DTYPES = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16,
-                "fp8_e4m3": torch.uint8}
+                "fp8_e4m3": torch.uint8}      # dtypes of rows and queries (cache formats: CACHE_FORMATS)
 
 
 def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -29,7 +29,7 @@ class GpuWorkload:
                  device="cuda"):
         self.w = w
         self.cache = PagedKVCache(num_layers, num_blocks or w.num_blocks, w.num_kv_heads, w.head_dim,
-                                  TORCH_DTYPES[w.cache_dtype], w.max_blocks_per_seq, device=device)
+                                  w.cache_dtype, w.max_blocks_per_seq, device=device)
         self.device = device
         self.trace: List[tuple] = []
         self._rows: Dict[int, tuple] = {}

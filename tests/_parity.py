@@ -9,11 +9,11 @@ import numpy as np
 import torch
 
 import workloads as wl
-from oracle import fp8_e4m3
+from oracle import kv_formats
 
 # Maximum absolute error of decode outputs against the fp64 oracle: 1e-5 for
 # fp32 inputs, 2e-2 for bf16 / f16 / fp8 inputs.
-TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2, "fp8_e4m3": 2e-2}
+TOL = {"f32": 1e-5, "f16": 2e-2, "bf16": 2e-2, "fp8_e4m3": 2e-2, "fp8_e5m2": 2e-2, "int8_int4": 2e-2}
 
 TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
 
@@ -51,16 +51,18 @@ def gather_gpu_rows(pool: torch.Tensor, slots: np.ndarray) -> torch.Tensor:
 def check_cache_rows(w: wl.Workload, cache, layer: int, seq: int, table_row, length: int) -> None:
     """Bit-exact: the GPU pool holds, at the slots the oracle's tables give for
     positions 0..L-1, the rows the oracle expects (copies, or e4m3 codes and
-    scales from the oracle's quantiser)."""
+    scales from the oracle's quantiser for quantised formats)."""
     slots = slots_for(table_row, length)
     k_rows = wl.kv_rows(w, seq, "k", length)
     v_rows = wl.kv_rows(w, seq, "v", length)
     gk = gather_gpu_rows(cache.k[layer], slots).cpu()
     gv = gather_gpu_rows(cache.v[layer], slots).cpu()
-    if w.cache_dtype == "fp8_e4m3":
-        for rows, got, scale_pool in ((k_rows, gk, cache.k_scale[layer]), (v_rows, gv, cache.v_scale[layer])):
-            codes, scales = fp8_e4m3.quantise_rows(rows)
-            assert np.array_equal(got.numpy(), codes), f"seq {seq}: fp8 codes differ"
+    k_elem, v_elem = kv_formats.FORMATS[w.cache_dtype]
+    if kv_formats.is_quantised(k_elem):
+        for rows, got, scale_pool, elem in ((k_rows, gk, cache.k_scale[layer], k_elem),
+                                            (v_rows, gv, cache.v_scale[layer], v_elem)):
+            codes, scales = kv_formats.quantise(rows, elem)
+            assert np.array_equal(got.view(torch.uint8).numpy(), codes), f"seq {seq}: {elem} codes differ"
             s = torch.from_numpy(slots).to(scale_pool.device)
             gs = scale_pool[s // 16, :, s % 16].cpu().numpy()
             assert np.array_equal(gs.view(np.uint32), scales.view(np.uint32)), f"seq {seq}: scales differ"

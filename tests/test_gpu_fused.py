@@ -23,6 +23,9 @@ CASES = [
     ([250, 31, 700], 16, 16, 128, "f16", None, None, 128),
     ([500, 17, 64], 32, 8, 128, "f32", "fp8_e4m3", "bf16", 0),
     ([500, 17, 64], 16, 4, 64, "bf16", "fp8_e4m3", "f16", 96),
+    ([500, 17, 64], 32, 8, 128, "f32", "fp8_e5m2", "bf16", 0),
+    ([500, 17, 64], 32, 8, 128, "bf16", "int8_int4", "bf16", 96),
+    ([300, 33], 16, 4, 64, "f32", "int8_int4", "f16", 0),
 ]
 
 

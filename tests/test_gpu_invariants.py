@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import workloads as wl
-from oracle import attention, fp8_e4m3, scenario
+from oracle import attention, fp8_e4m3, kv_formats, scenario
 import paged_kv_cache_160_amd as pkv
 from paged_kv_cache_160_amd.workload_runner import GpuWorkload, to_device
 from tests._parity import TOL, check_cache_rows, max_err, out_to_f64, say
@@ -112,6 +112,11 @@ CASES = [
     ([500, 17, 64], 32, 8, 64, "bf16", "fp8_e4m3", "bf16"),
     ([250, 99], 16, 2, 128, "f16", "fp8_e4m3", "f16"),
     ([250, 99], 8, 8, 64, "f32", "fp8_e4m3", "f16"),
+    ([500, 17, 64], 32, 8, 128, "f32", "fp8_e5m2", "bf16"),
+    ([250, 99], 8, 8, 64, "bf16", "fp8_e5m2", "f16"),
+    ([500, 17, 64], 32, 8, 128, "f32", "int8_int4", "bf16"),
+    ([300, 1, 47], 16, 2, 64, "bf16", "int8_int4", "bf16"),
+    ([250, 99], 16, 16, 128, "f16", "int8_int4", "f16"),
 ]
 
 
@@ -130,16 +135,17 @@ def test_dtype_and_shape_matrix(case):
         assert err <= TOL[w.cache_dtype]
 
 
-@pytest.mark.parametrize("cache", ["bf16", "fp8_e4m3"])
+@pytest.mark.parametrize("cache", ["bf16", "fp8_e4m3", "fp8_e5m2", "int8_int4"])
 def test_copy_blocks_copies_whole_blocks_only(cache):
     say(f"[cow] cache={cache}")
     w, g = _custom([64, 64], 8, 4, 128, "bf16" if cache == "bf16" else "f32", cache_dtype=cache,
                    q_dtype="bf16", seed=8)
     c = g.cache
     # compare storage bits: unwritten slots of a fresh pool may hold NaN patterns
-    bits = (lambda t: t.view(torch.int16)) if cache == "bf16" else (lambda t: t)
+    bits = (lambda t: t.view(torch.int16)) if cache == "bf16" else (lambda t: t.view(torch.uint8))
     k0, v0 = bits(c.k[0]).clone(), bits(c.v[0]).clone()
     ks0 = c.k_scale[0].view(torch.int32).clone() if c.fp8 else None
+    vs0 = c.v_scale[0].view(torch.int32).clone() if c.fp8 else None
     used = c.alloc.block_tables([0, 1])[0]
     src = [int(used[0, 0]), int(used[1, 2])]
     free_blocks = sorted(set(range(w.num_blocks)) - set(used.flatten().tolist()))
@@ -152,6 +158,7 @@ def test_copy_blocks_copies_whole_blocks_only(cache):
         assert torch.equal(k1[d_], k0[s]) and torch.equal(v1[d_], v0[s])
         if c.fp8:
             assert torch.equal(c.k_scale[0].view(torch.int32)[d_], ks0[s])
+            assert torch.equal(c.v_scale[0].view(torch.int32)[d_], vs0[s])
     others = [b for b in range(w.num_blocks) if b not in dst]
     assert torch.equal(k1[others], k0[others]) and torch.equal(v1[others], v0[others])
 
@@ -188,3 +195,37 @@ def test_fp8_quantiser_edge_rows():
     codes, scales = fp8_e4m3.quantise_rows(rows)
     assert np.array_equal(k_pool[0, 0, :6].cpu().numpy(), codes[:, 0])
     assert np.array_equal(ks[0, 0, :6].cpu().numpy().view(np.uint32), scales[:, 0].view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", ["fp8_e5m2", "int8_int4"])
+def test_quantiser_edge_rows_other_formats(fmt):
+    # zero rows, a lone spike, tiny values (e5m2 subnormals), exact integer
+    # grids with half-integer ties for the int formats, large values
+    say(f"[quant] edge rows {fmt}")
+    d = 128
+    rows = np.zeros((8, 1, d), dtype=np.float32)
+    rows[1, 0, 7] = 3.0
+    rows[2, 0] = np.linspace(-1e-3, 1e-3, d, dtype=np.float32)
+    rows[3, 0] = np.float32(57344.0) * np.linspace(-1, 1, d, dtype=np.float32)
+    rows[4, 0] = np.random.default_rng(4).standard_normal(d).astype(np.float32) * 1e4
+    rows[5, 0, :64] = -0.0
+    rows[5, 0, 64:] = 2.0 ** -20
+    # max 7 * 2^-3 -> s = 2^-3 for int4; entries on every half step
+    rows[6, 0, :15] = (np.arange(-7, 8) * 0.125).astype(np.float32)
+    rows[6, 0, 15:29] = ((np.arange(-7, 7) + 0.5) * 0.125).astype(np.float32)
+    rows[7, 0, :127] = ((np.arange(-63, 64) + 0.5) * 0.125).astype(np.float32)
+    rows[7, 0, 127] = np.float32(127 * 0.125)
+    k_elem, v_elem = kv_formats.FORMATS[fmt]
+    from paged_kv_cache_160_amd import CACHE_FORMATS
+    _, k_dt, v_dt, v_per = CACHE_FORMATS[fmt]
+    k_pool = torch.zeros((1, 1, 16, d), dtype=k_dt, device="cuda")
+    v_pool = torch.zeros((1, 1, 16, d // v_per), dtype=v_dt, device="cuda")
+    ks = torch.zeros((1, 1, 16), dtype=torch.float32, device="cuda")
+    vs = torch.zeros_like(ks)
+    x = torch.from_numpy(rows).cuda()
+    pkv.kv_cache_append(x, x, k_pool, v_pool, torch.arange(8, dtype=torch.int64, device="cuda"), ks, vs)
+    torch.cuda.synchronize()
+    for pool, sc, elem in ((k_pool, ks, k_elem), (v_pool, vs, v_elem)):
+        codes, scales = kv_formats.quantise(rows[:, 0], elem)
+        assert np.array_equal(pool[0, 0, :8].view(torch.uint8).cpu().numpy(), codes), elem
+        assert np.array_equal(sc[0, 0, :8].cpu().numpy().view(np.uint32), scales.view(np.uint32)), elem
