@@ -41,6 +41,9 @@ METRIC = "paged decode attention KV tokens/s and achieved HBM GB/s (% of peak), 
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 * 2 ** 20
 ES = {"f32": 4, "f16": 2, "bf16": 2, "fp8_e4m3": 1}
+# cache format -> (bytes per K element, bytes per V element, float32 scales per (token, head) and tensor)
+KV_BYTES = {"f32": (4, 4, 0), "f16": (2, 2, 0), "bf16": (2, 2, 0), "fp8_e4m3": (1, 1, 1), "fp8_e5m2": (1, 1, 1),
+            "int8_int4": (1, 0.5, 1)}
 
 
 def log(*a):
@@ -74,6 +77,9 @@ def parse():
     ap.add_argument("--row", choices=["decode", "prefix", "prefill"], default="decode",
                     help="decode (default): the hot path; prefix: host prefix-cache replay of agent sessions; "
                          "prefill: multi-token append + chunked prefill attention")
+    ap.add_argument("--cache", default=None,
+                    help="decode row: cache format to run the workload with instead of its own "
+                         "(fp8_e4m3, fp8_e5m2, int8_int4, ...; K/V rows stay in the workload's dtype)")
     ap.add_argument("--cached", type=int, default=3584, help="prefill row: cached tokens per sequence")
     ap.add_argument("--chunk", type=int, default=512, help="prefill row: chunk tokens per sequence")
     ap.add_argument("--one-call", action="store_true",
@@ -205,8 +211,17 @@ def main():
     torch.cuda.set_device(dev)
     w = wl.make_workload(args.config)
     B, hq, hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
-    ces = ES[w.cache_dtype]
-    per_layer_bytes = 2 * w.num_blocks * hkv * 16 * D * ces
+    if args.cache:
+        if args.cache not in KV_BYTES:
+            raise SystemExit(f"unknown cache format {args.cache}")
+        w.cache_dtype = args.cache
+        if args.cache not in ("f32", "f16", "bf16"):
+            w.q_dtype = "bf16" if w.q_dtype == "f32" else w.q_dtype
+        else:
+            w.src_dtype = w.q_dtype = args.cache
+        w.name = f"{w.name}-{args.cache}"
+    kb_el, vb_el, nscale = KV_BYTES[w.cache_dtype]
+    per_layer_bytes = int(w.num_blocks * hkv * 16 * (D * (kb_el + vb_el) + 8 * nscale))
     layers = args.layers or (32 if args.config == 2 else max(1, math.ceil(4 * MALL_BYTES / per_layer_bytes)))
     log(f"[bench] workload {args.config} {w.name}: B={B} Hq={hq} Hkv={hkv} D={D} cache={w.cache_dtype} "
         f"layers={layers} pool={w.num_blocks} blocks/layer ({per_layer_bytes / 2**30:.2f} GiB/layer)")
@@ -357,9 +372,7 @@ def main():
                 e[2].record(stream)
         if timed:
             tokens_timed += sum_l * layers
-            kv_bytes = sum_l * hkv * D * 2 * ces
-            if w.cache_dtype == "fp8_e4m3":
-                kv_bytes += sum_l * hkv * 2 * 4
+            kv_bytes = sum_l * hkv * (D * (kb_el + vb_el) + 8 * nscale)
             qo_bytes = 2 * B * hq * D * ES[w.q_dtype]
             table_bytes = sum(-(-L // 16) for L in lens) * 4 + B * 4
             # the fused call also reads the new rows and slots (its writes are
