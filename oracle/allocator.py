@@ -26,7 +26,13 @@ Readings (the pages leave these open):
     taken for each position p in [L, L+n) with p % 16 == 0, in position order;
   * a full shared block is never written and so never copied;
   * an append that needs more fresh blocks than are free, or that would
-    exceed ``max_blocks_per_seq``, changes nothing and reports an error.
+    exceed ``max_blocks_per_seq``, changes nothing and reports an error;
+  * swap ("KV Cache 和 vLLM" §6.2: under memory pressure blocks move out to
+    CPU memory and back): ``swap_out`` needs every block of the sequence
+    unshared (count 1), reports its blocks in logical order, releases them
+    in that order and keeps only the length; ``swap_in`` takes
+    ceil(length / 16) fresh blocks in order, all or nothing.  A swapped
+    sequence can only be swapped in, freed or asked its length.
 
 Test infrastructure: only tests, the smoke check and the CPU baseline leg of
 the benchmark use this module.
@@ -55,6 +61,7 @@ class BlockAllocatorModel:
         self.ref = [0] * num_blocks
         self.tables: Dict[int, List[int]] = {}
         self.lens: Dict[int, int] = {}
+        self.swapped: Dict[int, int] = {}          # swapped-out sequence -> length
         self.cow_copies = 0
 
     # -- free list ----------------------------------------------------------
@@ -80,16 +87,24 @@ class BlockAllocatorModel:
             self.free.append(blk)
 
     # -- sequences ----------------------------------------------------------
+    def _live(self, seq: int) -> bool:
+        return seq in self.tables or seq in self.swapped
+
+    def _resident(self, seq: int) -> None:
+        if seq in self.swapped:
+            raise AllocError("invalid_arg")
+        if seq not in self.tables:
+            raise AllocError("unknown_seq")
+
     def create(self, seq: int) -> None:
-        if seq in self.tables:
+        if self._live(seq):
             raise AllocError("invalid_arg")
         self.tables[seq] = []
         self.lens[seq] = 0
 
     def fork(self, parent: int, child: int) -> None:
-        if parent not in self.tables:
-            raise AllocError("unknown_seq")
-        if child in self.tables:
+        self._resident(parent)
+        if self._live(child):
             raise AllocError("invalid_arg")
         self.tables[child] = list(self.tables[parent])
         self.lens[child] = self.lens[parent]
@@ -97,17 +112,46 @@ class BlockAllocatorModel:
             self.ref[blk] += 1
 
     def free_seq(self, seq: int) -> None:
+        if seq in self.swapped:
+            del self.swapped[seq]
+            return
         if seq not in self.tables:
             raise AllocError("unknown_seq")
         for blk in self.tables.pop(seq):
             self._release(blk)
         del self.lens[seq]
 
+    def swap_out(self, seq: int) -> List[int]:
+        """Blocks of ``seq`` in logical order, released; the sequence keeps
+        only its length until ``swap_in``."""
+        self._resident(seq)
+        table = self.tables[seq]
+        if any(self.ref[b] != 1 for b in table):
+            raise AllocError("invalid_arg")
+        for blk in table:
+            self._release(blk)
+        del self.tables[seq]
+        self.swapped[seq] = self.lens.pop(seq)
+        return list(table)
+
+    def swap_in(self, seq: int) -> List[int]:
+        """Fresh blocks, in logical order, for the swapped sequence's length."""
+        if seq not in self.swapped:
+            raise AllocError("unknown_seq" if seq not in self.tables else "invalid_arg")
+        L = self.swapped[seq]
+        need = -(-L // BLOCK_TOKENS)
+        if need > self._available():
+            raise AllocError("no_free_blocks")
+        blocks = [self._take() for _ in range(need)]
+        del self.swapped[seq]
+        self.tables[seq] = blocks
+        self.lens[seq] = L
+        return list(blocks)
+
     def append_slots(self, seq: int, n: int) -> Tuple[List[int], List[Tuple[int, int]]]:
         """Slots for the next n positions of ``seq`` and the copy pairs the
         caller must apply (before writing) to keep shared blocks intact."""
-        if seq not in self.tables:
-            raise AllocError("unknown_seq")
+        self._resident(seq)
         if n < 0:
             raise AllocError("invalid_arg")
         table = self.tables[seq]
@@ -135,6 +179,8 @@ class BlockAllocatorModel:
         return slots, pairs
 
     def seq_len(self, seq: int) -> int:
+        if seq in self.swapped:
+            return self.swapped[seq]
         if seq not in self.lens:
             raise AllocError("unknown_seq")
         return self.lens[seq]
@@ -143,8 +189,7 @@ class BlockAllocatorModel:
         """Tables ``[n][max_blocks]`` (unused entries 0) and lengths ``[n]``."""
         tables, lens = [], []
         for s in seqs:
-            if s not in self.tables:
-                raise AllocError("unknown_seq")
+            self._resident(s)
             t = self.tables[s]
             if len(t) > max_blocks:
                 raise AllocError("invalid_arg")
@@ -260,7 +305,7 @@ class PrefixCachingAllocatorModel(BlockAllocatorModel):
     def create_cached(self, seq: int, tokens) -> int:
         """New tracked sequence holding the longest indexed prefix of
         ``tokens``; returns its length (a multiple of 16)."""
-        if seq in self.tables:
+        if self._live(seq):
             raise AllocError("invalid_arg")
         tokens = [int(t) for t in tokens]
         most = min(max(len(tokens) - 1, 0) // BLOCK_TOKENS, self.max_blocks_per_seq)
@@ -296,6 +341,11 @@ class PrefixCachingAllocatorModel(BlockAllocatorModel):
         if n > 0:
             self.tokens.pop(seq, None)
         return slots, pairs
+
+    def swap_out(self, seq: int):
+        blocks = super().swap_out(seq)
+        self.tokens.pop(seq, None)          # swapped-in copies are private: indexing stops
+        return blocks
 
     def append_tokens(self, seq: int, tokens):
         tokens = [int(t) for t in tokens]

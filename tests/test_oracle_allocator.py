@@ -145,3 +145,49 @@ def test_random_streams_keep_invariants(seed):
             for old, new in pairs:
                 assert a.ref[old] >= 1 and a.ref[new] == 1
         _check_invariants(a)
+
+
+# ---- swap ("KV Cache 和 vLLM" §6.2) ------------------------------------------------
+
+def test_hand_worked_swap_out_and_in():
+    # pool of 6, block 0 handed out first.  A = 40 tokens -> blocks 0,1,2;
+    # B = 20 tokens -> 3,4; free stack (top last) [5].  Swapping A out
+    # releases 0,1,2 in order -> [5,0,1,2]; C (33 tokens) takes 2,1,0.
+    # A cannot come back (3 needed, 1 free) until C is freed (released in
+    # logical order 2,1,0 -> [5,2,1,0]); then A takes 0,1,2 again.
+    m = BlockAllocatorModel(6, 8)
+    m.create(0)
+    m.append_slots(0, 40)
+    m.create(1)
+    m.append_slots(1, 20)
+    assert m.swap_out(0) == [0, 1, 2]
+    assert m.seq_len(0) == 40 and m.free == [5, 0, 1, 2]
+    for bad in (lambda: m.append_slots(0, 1), lambda: m.block_tables([0], 8), lambda: m.fork(0, 9),
+                lambda: m.swap_out(0), lambda: m.create(0)):
+        with pytest.raises(AllocError) as e:
+            bad()
+        assert e.value.kind == "invalid_arg"
+    m.create(2)
+    assert m.append_slots(2, 33)[0][:1] == [32] and m.tables[2] == [2, 1, 0]
+    with pytest.raises(AllocError) as e:
+        m.swap_in(0)
+    assert e.value.kind == "no_free_blocks" and m.seq_len(0) == 40
+    m.free_seq(2)
+    assert m.swap_in(0) == [0, 1, 2]
+    assert m.block_tables([0], 8)[1] == [40]
+    assert m.stats()["used_blocks"] == 5
+
+
+def test_swap_out_refuses_shared_blocks():
+    m = BlockAllocatorModel(8, 8)
+    m.create(0)
+    m.append_slots(0, 20)
+    m.fork(0, 1)
+    before = (dict(m.tables), list(m.free), list(m.ref))
+    with pytest.raises(AllocError):
+        m.swap_out(0)
+    assert (dict(m.tables), list(m.free), list(m.ref)) == before
+    m.free_seq(1)
+    assert m.swap_out(0) == [0, 1]
+    m.free_seq(0)                       # a swapped sequence can be dropped
+    assert m.swapped == {} and len(m.free) == 8
