@@ -295,6 +295,28 @@ int paged_attention_prefill(void* out, const void* q, const void* k_pool, const 
                             int max_blocks_per_seq, int max_context_len, int max_query_len, float scale,
                             pkv_dtype q_dtype, pkv_dtype cache_dtype, void* stream);
 
+/*
+ * pkv_gather_blocks / pkv_scatter_blocks - move whole physical blocks between
+ * one pool tensor and a contiguous staging buffer, for swapping sequences out
+ * to host memory and back ("KV Cache 和 vLLM" §6.2: under memory pressure
+ * blocks move out to CPU memory; the host link is slow, so one large copy
+ * of a contiguous staging buffer replaces per-block copies).
+ *   staging      device, n_blocks * block_bytes bytes; slot i holds blocks[i]
+ *   pool         a device pool tensor (K, V, or a scale array): block b is the
+ *                block_bytes bytes at b * block_bytes (all heads of it)
+ *   blocks       device int32 [n_blocks]; ids outside [0, num_blocks) are
+ *                skipped (their staging slot is not touched)
+ *   block_bytes  bytes of one block of this tensor, a multiple of 16:
+ *                num_kv_heads * 16 * head_dim * element size (int4 V: half a
+ *                byte per element; scales: num_kv_heads * 16 * 4)
+ * The caller moves the staging buffer to or from pinned host memory; nothing
+ * here touches host memory.  Asynchronous on stream.
+ */
+int pkv_gather_blocks(void* staging, const void* pool, const int32_t* blocks, int n_blocks,
+                      int64_t block_bytes, int num_blocks, void* stream);
+int pkv_scatter_blocks(void* pool, const void* staging, const int32_t* blocks, int n_blocks,
+                       int64_t block_bytes, int num_blocks, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host block allocator.  Opaque handle, not thread-safe, no device memory.  */
 /*                                                                          */
@@ -377,6 +399,25 @@ int pkv_build_block_tables(pkv_alloc* a, const int64_t* seq_ids, int n, int max_
                            int32_t* tables_out, int32_t* lens_out);
 
 int pkv_alloc_stats(pkv_alloc* a, pkv_alloc_stats_t* out);
+
+/*
+ * pkv_seq_swap_out - move a sequence out of the pool ("KV Cache 和 vLLM"
+ * §6.2).  Every block of the sequence must be unshared (count 1), else
+ * PKV_ERR_INVALID_ARG and nothing changes.  Writes its blocks in logical
+ * order to blocks_out (host int32, room for max_blocks_per_seq entries),
+ * their count to *n_out, and releases them in that order (prefix-indexed
+ * blocks stay cached and evictable).  The sequence keeps only its length;
+ * it stops being prefix-indexed.  The caller gathers those blocks (stream
+ * order keeps later writes to them behind the gather).
+ * pkv_seq_swap_in - bring a swapped sequence back: takes ceil(len / 16)
+ * fresh blocks, all or nothing (PKV_ERR_NO_FREE_BLOCKS), writes them in
+ * logical order to blocks_out for the caller to scatter into.
+ * A swapped sequence can only be swapped in, freed or asked its length;
+ * other calls naming it give PKV_ERR_INVALID_ARG.  Allocator statistics
+ * count resident sequences only.
+ */
+int pkv_seq_swap_out(pkv_alloc* a, int64_t seq_id, int32_t* blocks_out, int* n_out);
+int pkv_seq_swap_in(pkv_alloc* a, int64_t seq_id, int32_t* blocks_out, int* n_out);
 
 /* ------------------------------------------------------------------------ */
 /* Prefix caching.                                                          */

@@ -361,6 +361,8 @@ class PrefixCachingAllocatorModel(BlockAllocatorModel):
     def batch_append_tokens(self, seqs, tokens):
         """One token for each sequence, in order; all or nothing."""
         seqs = [int(s) for s in seqs]
+        for s in seqs:
+            self._resident(s)               # every sequence is checked before capacity
         if len(set(seqs)) != len(seqs):
             raise AllocError("invalid_arg")
         saved = copy.deepcopy(self.__dict__)

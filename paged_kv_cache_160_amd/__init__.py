@@ -24,7 +24,8 @@ __all__ = [
     "kv_cache_append", "copy_blocks", "paged_attention_decode", "paged_attention_decode_append",
     "paged_attention_decode_append_partials", "paged_attention_merge_partials",
     "workspace_size",
-    "decode_partition_size", "BlockAllocator", "dtype_code", "abi_version",
+    "decode_partition_size", "BlockAllocator", "dtype_code", "abi_version", "gather_blocks", "scatter_blocks",
+    "paged_attention_prefill",
 ]
 
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3, PKV_FP8_E5M2, PKV_INT8_INT4 = 0, 1, 2, 3, 4, 5
@@ -212,6 +213,30 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Te
     return out
 
 
+def _block_bytes(pool: torch.Tensor) -> int:
+    return pool[0].numel() * pool.element_size()
+
+
+def gather_blocks(staging: torch.Tensor, pool: torch.Tensor, blocks: torch.Tensor, stream=None) -> torch.Tensor:
+    """staging[i] = pool[blocks[i]] for whole blocks (all heads); ``staging``
+    is a device tensor shaped [n, *pool.shape[1:]] of pool's dtype."""
+    n = int(blocks.numel())
+    if blocks.dtype != torch.int32 or staging.shape != (n,) + tuple(pool.shape[1:]) or staging.dtype != pool.dtype:
+        raise ValueError("staging must be [n, *pool.shape[1:]] of the pool's dtype; blocks int32 [n]")
+    _check(_lib.lib().pkv_gather_blocks(_ptr(staging), _ptr(pool), _ptr(blocks), n, _block_bytes(pool),
+                                        int(pool.shape[0]), _stream(stream)), "pkv_gather_blocks")
+    return staging
+
+
+def scatter_blocks(pool: torch.Tensor, staging: torch.Tensor, blocks: torch.Tensor, stream=None) -> None:
+    """pool[blocks[i]] = staging[i] for whole blocks."""
+    n = int(blocks.numel())
+    if blocks.dtype != torch.int32 or staging.shape != (n,) + tuple(pool.shape[1:]) or staging.dtype != pool.dtype:
+        raise ValueError("staging must be [n, *pool.shape[1:]] of the pool's dtype; blocks int32 [n]")
+    _check(_lib.lib().pkv_scatter_blocks(_ptr(pool), _ptr(staging), _ptr(blocks), n, _block_bytes(pool),
+                                         int(pool.shape[0]), _stream(stream)), "pkv_scatter_blocks")
+
+
 def _decode_append_call(fn_name, out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables,
                         context_lens, max_context_len, scale, k_scale, v_scale, partition_size, workspace,
                         stream):
@@ -342,6 +367,22 @@ class BlockAllocator:
         _check(self._lib.pkv_batch_append_one(self._h, ids, n, slots, pairs, ctypes.byref(ncow)),
                "pkv_batch_append_one")
         return list(slots[:n]), [(pairs[2 * i], pairs[2 * i + 1]) for i in range(ncow.value)]
+
+    # -- swap ------------------------------------------------------------------
+    def swap_out(self, seq_id: int) -> List[int]:
+        """Release the sequence's (unshared) blocks, keeping its length; returns
+        them in logical order for the caller to gather."""
+        blocks = (ctypes.c_int32 * max(self.max_blocks_per_seq, 1))()
+        n = ctypes.c_int()
+        _check(self._lib.pkv_seq_swap_out(self._h, seq_id, blocks, ctypes.byref(n)), "pkv_seq_swap_out")
+        return list(blocks[:n.value])
+
+    def swap_in(self, seq_id: int) -> List[int]:
+        """Fresh blocks for a swapped sequence, in logical order (to scatter into)."""
+        blocks = (ctypes.c_int32 * max(self.max_blocks_per_seq, 1))()
+        n = ctypes.c_int()
+        _check(self._lib.pkv_seq_swap_in(self._h, seq_id, blocks, ctypes.byref(n)), "pkv_seq_swap_in")
+        return list(blocks[:n.value])
 
     # -- prefix caching --------------------------------------------------------
     def enable_prefix_cache(self, model_key: int = 0, hash_bits: int = 64) -> None:

@@ -78,6 +78,10 @@ SIGNATURES = {
     "pkv_batch_append_one": (c_int, [c_void_p, P_i64, c_int, P_i64, P_i32, P_int]),
     "pkv_build_block_tables": (c_int, [c_void_p, P_i64, c_int, c_int, P_i32, P_i32]),
     "pkv_alloc_stats": (c_int, [c_void_p, ctypes.POINTER(AllocStats)]),
+    "pkv_seq_swap_out": (c_int, [c_void_p, c_int64, P_i32, P_int]),
+    "pkv_seq_swap_in": (c_int, [c_void_p, c_int64, P_i32, P_int]),
+    "pkv_gather_blocks": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int64, c_int, c_void_p]),
+    "pkv_scatter_blocks": (c_int, [c_void_p, c_void_p, c_void_p, c_int, c_int64, c_int, c_void_p]),
     "pkv_prefix_cache_enable": (c_int, [c_void_p, ctypes.c_uint64, c_int]),
     "pkv_seq_create_cached": (c_int, [c_void_p, c_int64, P_i32, c_int, P_int]),
     "pkv_seq_append_tokens": (c_int, [c_void_p, c_int64, P_i32, c_int, P_i64, P_i32, P_int]),

@@ -11,7 +11,8 @@ from typing import List, Optional, Sequence, Union
 import torch
 
 from . import (BLOCK_SIZE, CACHE_FORMATS, PKV_FP8_E4M3, PKV_FP8_E5M2, PKV_INT8_INT4, BlockAllocator, copy_blocks,
-               kv_cache_append, paged_attention_decode, paged_attention_decode_append, workspace_size)
+               gather_blocks, kv_cache_append, paged_attention_decode, paged_attention_decode_append, scatter_blocks,
+               workspace_size)
 
 Rows = Union[torch.Tensor, Sequence[torch.Tensor]]
 
@@ -70,6 +71,44 @@ class PagedKVCache:
 
     def seq_len(self, seq_id: int) -> int:
         return self.alloc.seq_len(seq_id)
+
+    # -- swap -----------------------------------------------------------------
+    def _tensors(self):
+        """Every pool tensor, layer by layer (K, V and the scales if any)."""
+        out = []
+        for l in range(self.num_layers):
+            out += [self.k[l], self.v[l]]
+            if self.quantised:
+                out += [self.k_scale[l], self.v_scale[l]]
+        return out
+
+    def swap_out(self, seq_id: int) -> list:
+        """Move a sequence's blocks to pinned host memory ("KV Cache 和 vLLM"
+        §6.2): the allocator releases them, each pool tensor's blocks are
+        gathered into one device staging buffer and copied to the host in one
+        transfer.  Returns the host tensors (one per pool tensor); keep them
+        for swap_in.  The copies are asynchronous on the current stream."""
+        blocks = self.alloc.swap_out(seq_id)
+        bt = torch.tensor(blocks, dtype=torch.int32).to(self.device)
+        host = []
+        for t in self._tensors():
+            staging = torch.empty((len(blocks),) + tuple(t.shape[1:]), dtype=t.dtype, device=self.device)
+            gather_blocks(staging, t, bt)
+            h = torch.empty(staging.shape, dtype=t.dtype, pin_memory=True)
+            h.copy_(staging, non_blocking=True)
+            host.append(h)
+        return host
+
+    def swap_in(self, seq_id: int, host: list) -> List[int]:
+        """Bring a swapped sequence back into fresh blocks from the host tensors
+        swap_out returned; returns the new blocks."""
+        blocks = self.alloc.swap_in(seq_id)
+        bt = torch.tensor(blocks, dtype=torch.int32).to(self.device)
+        for t, h in zip(self._tensors(), host):
+            if h.shape[0] != len(blocks):
+                raise ValueError("host copy does not match the sequence's blocks")
+            scatter_blocks(t, h.to(self.device, non_blocking=True), bt)
+        return blocks
 
     # -- writes ---------------------------------------------------------------
     def _layer_rows(self, rows: Rows, layer: int) -> torch.Tensor:

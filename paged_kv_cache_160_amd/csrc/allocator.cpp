@@ -45,6 +45,7 @@ struct Seq {
   std::vector<int32_t> table;
   int64_t len = 0;
   bool tracked = false;              // token ids known for every position
+  bool swapped = false;              // blocks moved out: only len is kept
   std::vector<int32_t> pending;      // tokens of the unfinished last block
 };
 
@@ -284,6 +285,7 @@ int pkv_seq_fork(pkv_alloc* a, int64_t parent, int64_t child) {
   if (!a) return PKV_ERR_INVALID_ARG;
   auto it = a->seqs.find(parent);
   if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+  if (it->second.swapped) return PKV_ERR_INVALID_ARG;
   if (a->seqs.count(child)) return PKV_ERR_INVALID_ARG;
   Seq c = it->second;
   for (int32_t b : c.table) ++a->ref[b];
@@ -321,6 +323,7 @@ int append_impl(pkv_alloc* a, int64_t seq_id, int n, const int32_t* toks, int64_
     return PKV_ERR_INVALID_ARG;
   auto it = a->seqs.find(seq_id);
   if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+  if (it->second.swapped) return PKV_ERR_INVALID_ARG;
   Seq& s = it->second;
   bool cow;
   int64_t fresh;
@@ -348,6 +351,7 @@ int batch_impl(pkv_alloc* a, const int64_t* seq_ids, const int32_t* toks, int n,
   for (int i = 0; i < n; ++i) {
     auto it = a->seqs.find(seq_ids[i]);
     if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+    if (it->second.swapped) return PKV_ERR_INVALID_ARG;
     if (seen[seq_ids[i]]++) return PKV_ERR_INVALID_ARG;
     const Seq& s = it->second;
     int64_t fresh = blocks_for(s.len + 1) - blocks_for(s.len);
@@ -457,6 +461,7 @@ int pkv_build_block_tables(pkv_alloc* a, const int64_t* seq_ids, int n, int max_
   for (int i = 0; i < n; ++i) {
     auto it = a->seqs.find(seq_ids[i]);
     if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+    if (it->second.swapped) return PKV_ERR_INVALID_ARG;
     if (static_cast<int64_t>(it->second.table.size()) > max_blocks_per_seq)
       return PKV_ERR_INVALID_ARG;
   }
@@ -476,6 +481,7 @@ int pkv_alloc_stats(pkv_alloc* a, pkv_alloc_stats_t* out) {
   int64_t cached = 0;
   for (int64_t id : a->seq_order) {
     const Seq& s = a->seqs[id];
+    if (s.swapped) continue;
     cached += s.len;
     for (size_t i = 0; i < s.table.size(); ++i) {
       int64_t f = std::min<int64_t>(kBlock, s.len - static_cast<int64_t>(i) * kBlock);
@@ -496,6 +502,41 @@ int pkv_alloc_stats(pkv_alloc* a, pkv_alloc_stats_t* out) {
   out->cached_tokens = cached;
   out->stored_tokens = stored;
   out->utilisation = used ? static_cast<double>(stored) / (static_cast<double>(kBlock) * used) : 0.0;
+  return PKV_OK;
+}
+
+int pkv_seq_swap_out(pkv_alloc* a, int64_t seq_id, int32_t* blocks_out, int* n_out) {
+  if (!a || !n_out) return PKV_ERR_INVALID_ARG;
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+  Seq& s = it->second;
+  if (s.swapped) return PKV_ERR_INVALID_ARG;
+  if (!s.table.empty() && !blocks_out) return PKV_ERR_INVALID_ARG;
+  for (int32_t b : s.table)
+    if (a->ref[b] != 1) return PKV_ERR_INVALID_ARG;       // shared: its holders would lose it
+  std::copy(s.table.begin(), s.table.end(), blocks_out);
+  *n_out = static_cast<int>(s.table.size());
+  for (int32_t b : s.table) a->release(b);
+  s.table.clear();
+  s.swapped = true;
+  s.tracked = false;                                      // swapped-in copies are private
+  s.pending.clear();
+  return PKV_OK;
+}
+
+int pkv_seq_swap_in(pkv_alloc* a, int64_t seq_id, int32_t* blocks_out, int* n_out) {
+  if (!a || !n_out) return PKV_ERR_INVALID_ARG;
+  auto it = a->seqs.find(seq_id);
+  if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+  Seq& s = it->second;
+  if (!s.swapped) return PKV_ERR_INVALID_ARG;
+  const int64_t need = blocks_for(s.len);
+  if (need > 0 && !blocks_out) return PKV_ERR_INVALID_ARG;
+  if (need > a->available()) return PKV_ERR_NO_FREE_BLOCKS;
+  for (int64_t i = 0; i < need; ++i) s.table.push_back(a->take());
+  std::copy(s.table.begin(), s.table.end(), blocks_out);
+  *n_out = static_cast<int>(need);
+  s.swapped = false;
   return PKV_OK;
 }
 

@@ -360,3 +360,31 @@ int paged_attention_prefill(void* out, const void* q, const void* k_pool, const 
 }
 
 }  // extern "C"
+
+namespace {
+
+int swap_impl(void* staging, void* pool, const int32_t* blocks, int n_blocks, int64_t block_bytes, int num_blocks,
+              bool to_staging, void* stream) {
+  if (n_blocks < 0 || num_blocks <= 0 || block_bytes <= 0 || block_bytes % 16 != 0) return PKV_ERR_INVALID_ARG;
+  if (n_blocks == 0) return PKV_OK;
+  if (!staging || !pool || !blocks || !aligned16(staging) || !aligned16(pool)) return PKV_ERR_INVALID_ARG;
+  if (n_blocks > 0x7fffffff / 2) return PKV_ERR_UNSUPPORTED;
+  return pkv::launch_swap_blocks(staging, pool, blocks, n_blocks, block_bytes, num_blocks, to_staging,
+                                 static_cast<hipStream_t>(stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_gather_blocks(void* staging, const void* pool, const int32_t* blocks, int n_blocks, int64_t block_bytes,
+                      int num_blocks, void* stream) {
+  return swap_impl(staging, const_cast<void*>(pool), blocks, n_blocks, block_bytes, num_blocks, true, stream);
+}
+
+int pkv_scatter_blocks(void* pool, const void* staging, const int32_t* blocks, int n_blocks, int64_t block_bytes,
+                       int num_blocks, void* stream) {
+  return swap_impl(const_cast<void*>(staging), pool, blocks, n_blocks, block_bytes, num_blocks, false, stream);
+}
+
+}  // extern "C"

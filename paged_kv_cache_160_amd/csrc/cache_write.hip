@@ -12,6 +12,8 @@
 // launch-bound; they are written for exactness (bit copies, a bit-exact
 // quantiser) and coalesced 16-byte accesses, not for peak bandwidth.
 
+#include <algorithm>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -92,6 +94,25 @@ __global__ void __launch_bounds__(256) copy_blocks_kernel(
     scales[d_tile * kBlockTokens + threadIdx.x] = scales[s_tile * kBlockTokens + threadIdx.x];
 }
 
+// Swap staging: whole blocks (block_chunks 16-byte chunks each, every head)
+// between a pool and a contiguous staging buffer, slot i of the staging
+// buffer holding blocks[i].  to_staging: pool -> staging, else staging ->
+// pool.  Block ids outside [0, num_blocks) are skipped.
+__global__ void __launch_bounds__(256) swap_blocks_kernel(uint4* __restrict__ staging, uint4* __restrict__ pool,
+                                                          const int32_t* __restrict__ blocks, int64_t block_chunks,
+                                                          int num_blocks, int to_staging) {
+  const int i = blockIdx.x;
+  const int32_t blk = blocks[i];
+  if (blk < 0 || blk >= num_blocks) return;
+  uint4* p = pool + static_cast<int64_t>(blk) * block_chunks;
+  uint4* st = staging + static_cast<int64_t>(i) * block_chunks;
+  const int64_t step = static_cast<int64_t>(gridDim.y) * blockDim.x;
+  for (int64_t c = static_cast<int64_t>(blockIdx.y) * blockDim.x + threadIdx.x; c < block_chunks; c += step) {
+    if (to_staging) st[c] = p[c];
+    else p[c] = st[c];
+  }
+}
+
 // ---- launchers -------------------------------------------------------------------
 
 int launch_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
@@ -152,6 +173,17 @@ int launch_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scal
                      static_cast<uint4*>(k_pool), static_cast<uint4*>(v_pool),
                      quant ? k_scale : nullptr, quant ? v_scale : nullptr, pairs, num_kv_heads,
                      k_chunks, v_chunks, num_blocks);
+  return check_launch();
+}
+
+int launch_swap_blocks(void* staging, void* pool, const int32_t* blocks, int n_blocks, int64_t block_bytes,
+                       int num_blocks, bool to_staging, hipStream_t stream) {
+  const int64_t chunks = block_bytes / 16;
+  const int64_t per_wg = 256 * 8;                 // 8 chunks per thread per workgroup pass
+  const int64_t gy = std::min<int64_t>((chunks + per_wg - 1) / per_wg, 65535);
+  hipLaunchKernelGGL(swap_blocks_kernel, dim3(n_blocks, static_cast<unsigned>(gy)), dim3(256), 0, stream,
+                     static_cast<uint4*>(staging), static_cast<uint4*>(pool), blocks, chunks, num_blocks,
+                     to_staging ? 1 : 0);
   return check_launch();
 }
 

@@ -22,6 +22,9 @@ int launch_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scal
                        const int32_t* pairs, int n_pairs, int num_kv_heads, int head_dim,
                        int num_blocks, pkv_dtype cache_dtype, hipStream_t stream);
 
+int launch_swap_blocks(void* staging, void* pool, const int32_t* blocks, int n_blocks, int64_t block_bytes,
+                       int num_blocks, bool to_staging, hipStream_t stream);
+
 struct DecodeArgs {
   void* out;
   const void* q;

@@ -135,6 +135,7 @@ def test_allocator_random_streams_match_model(seed):
     model.set_free_order(order)
     native.set_free_order(order)
     live, nxt = [], 0
+    swapped = set()
     for _ in range(2000):
         r = rng.random()
         if r < 0.15 or not live:
@@ -142,12 +143,32 @@ def test_allocator_random_streams_match_model(seed):
         elif r < 0.3:
             s = live.pop(int(rng.integers(len(live))))
             model.free_seq(s); native.free(s)
+            swapped.discard(s)
         elif r < 0.4:
             p = live[int(rng.integers(len(live)))]
+            if p in swapped:
+                continue
             model.fork(p, nxt); native.fork(p, nxt); live.append(nxt); nxt += 1
+        elif r < 0.47:
+            s = live[int(rng.integers(len(live)))]
+            op = "swap_in" if s in swapped else "swap_out"
+            try:
+                exp = getattr(model, op)(s)
+            except AllocError as e:
+                with pytest.raises(pkv.PagedKVError) as got:
+                    getattr(native, op)(s)
+                assert got.value.code == {"no_free_blocks": -5, "invalid_arg": -1}[e.kind]
+                continue
+            assert getattr(native, op)(s) == exp
+            swapped.symmetric_difference_update({s})
         else:
             s = live[int(rng.integers(len(live)))]
             n = int(rng.integers(0, 40))
+            if s in swapped:
+                with pytest.raises(pkv.PagedKVError) as got:
+                    native.append_slots(s, n)
+                assert got.value.code == -1
+                continue
             try:
                 exp = model.append_slots(s, n)
             except AllocError as e:
@@ -244,3 +265,32 @@ def test_partition_plan_and_workspace():
         else:
             assert ws >= B * hq * npart * (128 + 2) * 4
     assert pkv.workspace_size(16, 32, 8, 128, 4096, 16, pkv.PKV_BF16) >= 16 * 32 * 256 * 130 * 4
+
+
+def test_swap_hand_worked_matches_model():
+    # the same sequence as the model's hand-worked swap pin
+    a = pkv.BlockAllocator(6, 8)
+    a.create(0)
+    a.append_slots(0, 40)
+    a.create(1)
+    a.append_slots(1, 20)
+    assert a.swap_out(0) == [0, 1, 2]
+    assert a.seq_len(0) == 40 and a.stats()["cached_tokens"] == 20
+    for bad in (lambda: a.append_slots(0, 1), lambda: a.block_tables([0]), lambda: a.fork(0, 9),
+                lambda: a.swap_out(0), lambda: a.create(0), lambda: a.batch_append_one([1, 0])):
+        with pytest.raises(pkv.PagedKVError) as e:
+            bad()
+        assert e.value.code == -1
+    a.create(2)
+    a.append_slots(2, 33)
+    assert a.block_tables([2])[0][0, :3].tolist() == [2, 1, 0]
+    with pytest.raises(pkv.PagedKVError) as e:
+        a.swap_in(0)
+    assert e.value.code == -5
+    a.free(2)
+    assert a.swap_in(0) == [0, 1, 2]
+    assert a.block_tables([0])[1].tolist() == [40]
+    a.fork(0, 3)
+    with pytest.raises(pkv.PagedKVError) as e:
+        a.swap_out(0)                    # shared blocks stay
+    assert e.value.code == -1

@@ -29,9 +29,9 @@ def test_hand_worked_example():
 
 
 @pytest.mark.parametrize("hash_bits", [64, 2])
-@pytest.mark.parametrize("seed", range(4))
+@pytest.mark.parametrize("seed", range(6))
 def test_random_streams_match_model(seed, hash_bits):
-    ops = list(_stream(seed, n_ops=800))
+    ops = list(_stream(seed, n_ops=800, shared=seed < 4))
     m = PrefixCachingAllocatorModel(40, 12, model_key=99)
     a = _native(40, 12, model_key=99, hash_bits=hash_bits)
     got, exp = [], []
@@ -42,7 +42,10 @@ def test_random_streams_match_model(seed, hash_bits):
         assert got == exp, i
         assert a.prefix_stats() == m.prefix_stats()
         assert a.stats() == pytest.approx(m.stats())
-    assert m.prefix_stats()["evictions"] > 20 and m.prefix_stats()["hit_blocks"] > 20
+    if seed < 4:
+        assert m.prefix_stats()["evictions"] > 20 and m.prefix_stats()["hit_blocks"] > 20
+    else:
+        assert sum(1 for r in exp if r[0] == "swap" and r[1] != "error") > 5
 
 
 def test_disabled_cache_keeps_plain_behaviour():
