@@ -74,9 +74,10 @@ def parse():
     ap.add_argument("--unfused", action="store_true",
                     help="write the step's rows with kv_cache_append, then attend (default: the write is fused "
                          "into the attention kernel)")
-    ap.add_argument("--row", choices=["decode", "prefix", "prefill"], default="decode",
+    ap.add_argument("--row", choices=["decode", "prefix", "prefill", "swap"], default="decode",
                     help="decode (default): the hot path; prefix: host prefix-cache replay of agent sessions; "
-                         "prefill: multi-token append + chunked prefill attention")
+                         "prefill: multi-token append + chunked prefill attention; swap: sequences to host "
+                         "memory and back")
     ap.add_argument("--cache", default=None,
                     help="decode row: cache format to run the workload with instead of its own "
                          "(fp8_e4m3, fp8_e5m2, int8_int4, ...; K/V rows stay in the workload's dtype)")
@@ -163,6 +164,9 @@ def main():
         return
     if args.row == "prefill":
         run_prefill_row(args)
+        return
+    if args.row == "swap":
+        run_swap_row(args)
         return
 
     import numpy as np
@@ -650,6 +654,146 @@ def prefill_cpu_baseline(args, hq, hkv, D, budget_s):
     return {"value": flops / wall / 1e12, "unit": "TFLOP/s", "cores": max(1, round(busy)), "kind": "oracle",
             "sample": f"{done} slices of {step} chunk rows (all {hq} heads, contexts {args.cached}..{L}), "
                       f"fp64 numpy, {busy:.2f} cores busy on average"}
+
+
+# ---- swap row --------------------------------------------------------------------------
+
+def run_swap_row(args):
+    """Sequence swap on the Llama-3-8B layer shape ("KV Cache 和 vLLM" §6.2):
+    32 layers of bf16 pools holding 16 sequences of 4096 tokens (the decode
+    workload's state); one step swaps 4 sequences out (per sequence: 64
+    gathers - 32 layers x K/V - into one device staging buffer, then one
+    device -> pinned-host copy) and back in (one host -> staging copy, 64
+    scatters into fresh blocks).  Each leg is timed with HIP events."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_160_amd as pkv
+    import workloads as wl
+    from paged_kv_cache_160_amd.cache import PagedKVCache
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = pkv._lib.lib()
+    w = wl.make_workload(2)
+    B, hkv, D = w.num_seqs, w.num_kv_heads, w.head_dim
+    layers = args.layers or 32
+    n_swap = 4
+    cache = PagedKVCache(layers, w.num_blocks, hkv, D, "bf16", w.max_blocks_per_seq, device=dev)
+    cache.set_free_order(w.free_order)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    for l in range(layers):
+        cache.k[l].normal_(generator=gen)
+        cache.v[l].normal_(generator=gen)
+    for b in range(B):
+        cache.create(b)
+        cache.alloc.append_slots(b, w.context_lens[b])
+    nblk = -(-w.context_lens[0] // 16)
+    tensors = cache._tensors()
+    block_bytes = tensors[0][0].numel() * tensors[0].element_size()
+    seq_bytes = nblk * block_bytes * len(tensors)
+    staging = torch.empty(seq_bytes, dtype=torch.uint8, device=dev)
+    host = [torch.empty(seq_bytes, dtype=torch.uint8, pin_memory=True) for _ in range(n_swap)]
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    log(f"[swap] {layers} layers, {B} x {w.context_lens[0]} tokens, swapping {n_swap} sequences of "
+        f"{seq_bytes / 2**20:.0f} MiB ({len(tensors)} pool tensors x {nblk} blocks x {block_bytes} B)")
+
+    def leg_out(b, h, ev):
+        blocks = cache.alloc.swap_out(b)
+        bt = torch.tensor(blocks, dtype=torch.int32).to(dev)
+        ev[0].record(stream)
+        for t_i, t in enumerate(tensors):
+            rc = lib.pkv_gather_blocks(staging.data_ptr() + t_i * nblk * block_bytes, t.data_ptr(), bt.data_ptr(),
+                                       nblk, block_bytes, w.num_blocks, sp)
+            if rc:
+                raise pkv.PagedKVError(rc, "pkv_gather_blocks")
+        ev[1].record(stream)
+        h.copy_(staging, non_blocking=True)
+        ev[2].record(stream)
+
+    def leg_in(b, h, ev):
+        blocks = cache.alloc.swap_in(b)
+        bt = torch.tensor(blocks, dtype=torch.int32).to(dev)
+        ev[0].record(stream)
+        staging.copy_(h, non_blocking=True)
+        ev[1].record(stream)
+        for t_i, t in enumerate(tensors):
+            rc = lib.pkv_scatter_blocks(t.data_ptr(), staging.data_ptr() + t_i * nblk * block_bytes, bt.data_ptr(),
+                                        nblk, block_bytes, w.num_blocks, sp)
+            if rc:
+                raise pkv.PagedKVError(rc, "pkv_scatter_blocks")
+        ev[2].record(stream)
+
+    n_steps = args.warmup + args.steps
+    evs = {(s_, i, d): tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
+           for s_ in range(n_steps) for i in range(n_swap) for d in (0, 1)}
+    t_start = None
+    for s_ in range(n_steps):
+        if s_ == args.warmup:
+            torch.cuda.synchronize()
+            t_start = time.perf_counter()
+        for i in range(n_swap):
+            leg_out(i, host[i], evs[(s_, i, 0)])
+            # the staging buffer is reused: the copy to the host must finish first
+            torch.cuda.current_stream().synchronize()
+        for i in range(n_swap):
+            leg_in(i, host[i], evs[(s_, i, 1)])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t_start
+    timed = [(s_, i) for s_ in range(args.warmup, n_steps) for i in range(n_swap)]
+    avg = lambda d, a, b: sum(evs[(s_, i, d)][a].elapsed_time(evs[(s_, i, d)][b]) for s_, i in timed) / len(timed) / 1e3
+    gather_s, d2h_s = avg(0, 0, 1), avg(0, 1, 2)
+    h2d_s, scatter_s = avg(1, 0, 1), avg(1, 1, 2)
+    gb = seq_bytes / 1e9
+    log(f"[swap] per sequence ({gb:.3f} GB): gather {gather_s * 1e3:.2f} ms ({2 * gb / gather_s:.0f} GB/s HBM), "
+        f"D2H {d2h_s * 1e3:.2f} ms ({gb / d2h_s:.1f} GB/s), H2D {h2d_s * 1e3:.2f} ms ({gb / h2d_s:.1f} GB/s), "
+        f"scatter {scatter_s * 1e3:.2f} ms ({2 * gb / scatter_s:.0f} GB/s HBM)")
+    swapped_tokens = args.steps * n_swap * w.context_lens[0]
+    rec = {
+        "metric": "sequence swap to host memory and back: KV tokens per second (round trip), 1 GPU",
+        "value": swapped_tokens / elapsed, "unit": "KV tokens/s (out + in)", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": elapsed * 1e3 / args.steps, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"llama3-8b-shape: {layers} layers x 16 x 4096 tokens, {n_swap} sequences "
+                               f"swapped per step", "bytes_per_sequence": seq_bytes},
+        "gather_ms": gather_s * 1e3, "d2h_ms": d2h_s * 1e3, "h2d_ms": h2d_s * 1e3, "scatter_ms": scatter_s * 1e3,
+        "gather_hbm_gbps": 2 * gb / gather_s, "scatter_hbm_gbps": 2 * gb / scatter_s,
+        "d2h_gbps": gb / d2h_s, "h2d_gbps": gb / h2d_s,
+        "roofline": {"bound": "hbm", "achieved": 2 * gb / gather_s, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": 2 * gb / gather_s / HBM_PEAK_GBPS, "traffic": None,
+                     "kernel": "swap_blocks_kernel (gather, 64 launches per sequence)",
+                     "bytes_per_launch": 2 * seq_bytes / len(tensors)},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = swap_cpu_baseline(args.cpu_seconds)
+    print(json.dumps(rec), flush=True)
+
+
+def swap_cpu_baseline(budget_s: float):
+    """The allocator model (test infrastructure) swapping the same sequences
+    out and in: swap operations per second (the model moves no data)."""
+    import workloads as wl
+    from oracle.allocator import BlockAllocatorModel
+
+    w = wl.make_workload(2)
+    m = BlockAllocatorModel(w.num_blocks, w.max_blocks_per_seq)
+    m.set_free_order(w.free_order)
+    for b in range(w.num_seqs):
+        m.create(b)
+        m.append_slots(b, w.context_lens[b])
+    t0 = time.perf_counter()
+    ops = 0
+    while time.perf_counter() - t0 < budget_s:
+        for b in range(4):
+            m.swap_out(b)
+        for b in range(4):
+            m.swap_in(b)
+        ops += 8
+    wall = time.perf_counter() - t0
+    return {"value": ops / wall, "unit": "swap operations/s (allocator state only)", "cores": 1, "kind": "oracle",
+            "sample": f"{ops} swap-outs and swap-ins of 4096-token sequences in the pure-Python allocator model"}
 
 
 # ---- prefix caching row --------------------------------------------------------------
