@@ -13,17 +13,21 @@ What the pages fix:
   * running out of cache memory must degrade (queue or recompute) rather than
     crash ("企业官网建设流程全解析" §6.4).
 
+Block size: 16 tokens, or 32 ("KV Cache 和 vLLM" §6.3: larger blocks shrink the
+block tables of long sequences at the cost of more internal fragmentation for
+short ones); every rule below counts positions in blocks of that size.
+
 Readings (the pages leave these open):
   * blocks carry a reference count; fork shares every block of the parent and
     increments each count; free decrements and returns a block at zero;
   * the free list is a stack: ``set_free_order(order)`` makes ``order[0]`` the
     next block handed out; a freed block goes on top (so it is reused first);
     a sequence's blocks are released in logical order 0, 1, 2, ...;
-  * an append of n tokens to a sequence of length L: if L % 16 != 0 and the
+  * an append of n tokens to a sequence of length L: if L % bs != 0 and the
     last block is shared (count > 1) that block is copied first - one fresh
     block is taken, the pair (old, new) is reported for copying, the old count
     is decremented and the table entry repointed; then one fresh block is
-    taken for each position p in [L, L+n) with p % 16 == 0, in position order;
+    taken for each position p in [L, L+n) with p % bs == 0, in position order;
   * a full shared block is never written and so never copied;
   * an append that needs more fresh blocks than are free, or that would
     exceed ``max_blocks_per_seq``, changes nothing and reports an error;
@@ -31,7 +35,7 @@ Readings (the pages leave these open):
     CPU memory and back): ``swap_out`` needs every block of the sequence
     unshared (count 1), reports its blocks in logical order, releases them
     in that order and keeps only the length; ``swap_in`` takes
-    ceil(length / 16) fresh blocks in order, all or nothing.  A swapped
+    ceil(length / bs) fresh blocks in order, all or nothing.  A swapped
     sequence can only be swapped in, freed or asked its length.
 
 Test infrastructure: only tests, the smoke check and the CPU baseline leg of
@@ -52,9 +56,10 @@ class AllocError(Exception):
 
 
 class BlockAllocatorModel:
-    def __init__(self, num_blocks: int, max_blocks_per_seq: int):
-        if num_blocks <= 0 or max_blocks_per_seq <= 0:
+    def __init__(self, num_blocks: int, max_blocks_per_seq: int, block_size: int = BLOCK_TOKENS):
+        if num_blocks <= 0 or max_blocks_per_seq <= 0 or block_size not in (16, 32):
             raise AllocError("invalid_arg")
+        self.bs = block_size
         self.num_blocks = num_blocks
         self.max_blocks_per_seq = max_blocks_per_seq
         self.free: List[int] = list(range(num_blocks - 1, -1, -1))   # top = end; block 0 first
@@ -139,7 +144,7 @@ class BlockAllocatorModel:
         if seq not in self.swapped:
             raise AllocError("unknown_seq" if seq not in self.tables else "invalid_arg")
         L = self.swapped[seq]
-        need = -(-L // BLOCK_TOKENS)
+        need = -(-L // self.bs)
         if need > self._available():
             raise AllocError("no_free_blocks")
         blocks = [self._take() for _ in range(need)]
@@ -156,8 +161,8 @@ class BlockAllocatorModel:
             raise AllocError("invalid_arg")
         table = self.tables[seq]
         L = self.lens[seq]
-        needs_cow = (n > 0 and L % BLOCK_TOKENS != 0 and self.ref[table[-1]] > 1)
-        new_blocks = -(-(L + n) // BLOCK_TOKENS) - -(-L // BLOCK_TOKENS)
+        needs_cow = (n > 0 and L % self.bs != 0 and self.ref[table[-1]] > 1)
+        new_blocks = -(-(L + n) // self.bs) - -(-L // self.bs)
         if len(table) + new_blocks > self.max_blocks_per_seq:
             raise AllocError("invalid_arg")
         if int(needs_cow) + new_blocks > self._available():
@@ -172,9 +177,9 @@ class BlockAllocatorModel:
             self.cow_copies += 1
         slots = []
         for p in range(L, L + n):
-            if p % BLOCK_TOKENS == 0:
+            if p % self.bs == 0:
                 table.append(self._take())
-            slots.append(BLOCK_TOKENS * table[p // BLOCK_TOKENS] + p % BLOCK_TOKENS)
+            slots.append(self.bs * table[p // self.bs] + p % self.bs)
         self.lens[seq] = L + n
         return slots, pairs
 
@@ -203,13 +208,13 @@ class BlockAllocatorModel:
 
         stored_tokens counts every filled physical slot once (a shared block's
         slot is filled if any holder has reached it); utilisation =
-        stored_tokens / (16 * used_blocks).  cached_tokens is the logical
+        stored_tokens / (bs * used_blocks).  cached_tokens is the logical
         total sum_b L_b."""
         filled: Dict[int, int] = {}
         for s, t in self.tables.items():
             L = self.lens[s]
             for i, blk in enumerate(t):
-                f = min(BLOCK_TOKENS, L - BLOCK_TOKENS * i)
+                f = min(self.bs, L - self.bs * i)
                 filled[blk] = max(filled.get(blk, 0), f)
         used = sum(1 for r in self.ref if r > 0)
         stored = sum(filled.values())
@@ -221,7 +226,7 @@ class BlockAllocatorModel:
             "cow_copies": self.cow_copies,
             "cached_tokens": sum(self.lens.values()),
             "stored_tokens": stored,
-            "utilisation": (stored / (BLOCK_TOKENS * used)) if used else 0.0,
+            "utilisation": (stored / (self.bs * used)) if used else 0.0,
         }
 
 
@@ -237,8 +242,8 @@ class PrefixCachingAllocatorModel(BlockAllocatorModel):
     plain access order.
 
     Readings (the pages leave these open):
-      * only full 16-token blocks are indexed; the key of a sequence's block i
-        is (model key, tokens 0 .. 16*i+15), the whole prefix it ends;
+      * only full blocks are indexed; the key of a sequence's block i is
+        (model key, tokens 0 .. bs*i+bs-1), the whole prefix it ends;
       * a block is indexed when an append that names its tokens fills it,
         unless its key is indexed already (the block then stays private), and
         for i > 0 only if the sequence's block i-1 is the one indexed under
@@ -246,7 +251,7 @@ class PrefixCachingAllocatorModel(BlockAllocatorModel):
       * ``create``, ``create_cached`` and ``fork`` of a tracked sequence give
         tracked sequences; an append without tokens (``append_slots``) stops
         tracking the sequence, since the keys of its later blocks are unknown;
-      * a lookup matches at most (n_tokens - 1) // 16 blocks, so the last
+      * a lookup matches at most (n_tokens - 1) // bs blocks, so the last
         prompt token is always computed, and takes a reference on each match;
       * an indexed block whose count drops to zero stays indexed and becomes
         evictable, stamped with a counter that rises at each such release;
@@ -257,8 +262,9 @@ class PrefixCachingAllocatorModel(BlockAllocatorModel):
       * capacity for an append counts free and evictable blocks.
     """
 
-    def __init__(self, num_blocks: int, max_blocks_per_seq: int, model_key: int = 0):
-        super().__init__(num_blocks, max_blocks_per_seq)
+    def __init__(self, num_blocks: int, max_blocks_per_seq: int, model_key: int = 0,
+                 block_size: int = BLOCK_TOKENS):
+        super().__init__(num_blocks, max_blocks_per_seq, block_size)
         self.model_key = int(model_key)
         self.index: Dict[tuple, int] = {}          # prefix key -> block
         self.key_of: Dict[int, tuple] = {}         # indexed block -> its key
@@ -268,11 +274,11 @@ class PrefixCachingAllocatorModel(BlockAllocatorModel):
         self.lookup_blocks = self.hit_blocks = self.evictions = 0
 
     def _key(self, toks, nblocks: int) -> tuple:
-        return (self.model_key,) + tuple(toks[:BLOCK_TOKENS * nblocks])
+        return (self.model_key,) + tuple(toks[:self.bs * nblocks])
 
     def _children(self, blk: int) -> int:
         key = self.key_of[blk]
-        return sum(1 for k in self.index if len(k) == len(key) + BLOCK_TOKENS and k[:len(key)] == key)
+        return sum(1 for k in self.index if len(k) == len(key) + self.bs and k[:len(key)] == key)
 
     # -- free list with eviction --------------------------------------------
     def _available(self) -> int:
@@ -304,11 +310,11 @@ class PrefixCachingAllocatorModel(BlockAllocatorModel):
 
     def create_cached(self, seq: int, tokens) -> int:
         """New tracked sequence holding the longest indexed prefix of
-        ``tokens``; returns its length (a multiple of 16)."""
+        ``tokens``; returns its length (a multiple of bs)."""
         if self._live(seq):
             raise AllocError("invalid_arg")
         tokens = [int(t) for t in tokens]
-        most = min(max(len(tokens) - 1, 0) // BLOCK_TOKENS, self.max_blocks_per_seq)
+        most = min(max(len(tokens) - 1, 0) // self.bs, self.max_blocks_per_seq)
         hits = []
         for i in range(most):
             blk = self.index.get(self._key(tokens, i + 1))
@@ -321,7 +327,7 @@ class PrefixCachingAllocatorModel(BlockAllocatorModel):
             if self.ref[blk] == 0:
                 del self.evictable[blk]
             self.ref[blk] += 1
-        n = BLOCK_TOKENS * len(hits)
+        n = self.bs * len(hits)
         self.tables[seq] = hits
         self.lens[seq] = n
         self.tokens[seq] = tokens[:n]
@@ -352,9 +358,9 @@ class PrefixCachingAllocatorModel(BlockAllocatorModel):
         slots, pairs = super().append_slots(seq, len(tokens))
         if seq in self.tokens:
             toks = self.tokens[seq]
-            done = len(toks) // BLOCK_TOKENS
+            done = len(toks) // self.bs
             toks.extend(tokens)
-            for i in range(done, len(toks) // BLOCK_TOKENS):
+            for i in range(done, len(toks) // self.bs):
                 self._index_block(seq, i)
         return slots, pairs
 
@@ -382,7 +388,7 @@ class PrefixCachingAllocatorModel(BlockAllocatorModel):
         if key in self.index:
             return
         table = self.tables[seq]
-        if i > 0 and self.index.get(key[:-BLOCK_TOKENS]) != table[i - 1]:
+        if i > 0 and self.index.get(key[:-self.bs]) != table[i - 1]:
             return
         self.index[key] = table[i]
         self.key_of[table[i]] = key

@@ -6,12 +6,14 @@ are logically contiguous (tokens 0-15 in logical block 0, 16-31 in logical
 block 1, ...) and a per-sequence block table maps each logical block to the
 physical block that holds it.
 
-In-block layout (a reading; the pages fix only the 16-token block): for each
-physical block and each KV head, the 16 token rows of head_dim elements are
-contiguous, i.e. the pool is ``[num_blocks][num_kv_heads][16][head_dim]``.
+In-block layout (a reading; the pages fix only the 16-token block, and 32 as
+the larger choice for long traffic, "KV Cache 和 vLLM" §6.3): for each
+physical block and each KV head, the block's token rows of head_dim elements
+are contiguous, i.e. the pool is ``[num_blocks][num_kv_heads][bs][head_dim]``
+with bs = 16 or 32 tokens per block.
 Quantised pools carry one float32 scale per (block, head, token) in
-``[num_blocks][num_kv_heads][16]``; an INT4 pool holds two codes per byte,
-``[num_blocks][num_kv_heads][16][head_dim / 2]``.
+``[num_blocks][num_kv_heads][bs]``; an INT4 pool holds two codes per byte,
+``[num_blocks][num_kv_heads][bs][head_dim / 2]``.
 
 Test infrastructure: only tests, the smoke check and the CPU baseline leg of
 the benchmark use this module.
@@ -25,16 +27,16 @@ from . import kv_formats
 BLOCK_TOKENS = 16
 
 
-def blocks_for(length: int) -> int:
-    """Blocks a sequence of ``length`` tokens owns: ceil(length / 16)."""
-    return -(-int(length) // BLOCK_TOKENS)
+def blocks_for(length: int, block_size: int = BLOCK_TOKENS) -> int:
+    """Blocks a sequence of ``length`` tokens owns: ceil(length / block_size)."""
+    return -(-int(length) // block_size)
 
 
-def slot_of(table_row, position: int) -> int:
+def slot_of(table_row, position: int, block_size: int = BLOCK_TOKENS) -> int:
     """Slot of logical position ``position`` given the sequence's block table
-    row: physical block ``table_row[position // 16]``, offset ``position % 16``;
-    slot = 16 * physical_block + offset."""
-    return BLOCK_TOKENS * int(table_row[position // BLOCK_TOKENS]) + position % BLOCK_TOKENS
+    row: physical block ``table_row[position // bs]``, offset ``position % bs``;
+    slot = bs * physical_block + offset (bs = 16, or 32)."""
+    return block_size * int(table_row[position // block_size]) + position % block_size
 
 
 class Pool:
@@ -47,14 +49,16 @@ class Pool:
     written-mask marks filled slots; unwritten slots are undefined in the GPU
     pool and are never compared."""
 
-    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, cache_dtype: str):
+    def __init__(self, num_blocks: int, num_kv_heads: int, head_dim: int, cache_dtype: str,
+                 block_size: int = BLOCK_TOKENS):
+        self.bs = block_size
         self.num_blocks = num_blocks
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
         self.cache_dtype = cache_dtype
         self.k_elem, self.v_elem = kv_formats.FORMATS[cache_dtype]
-        shape = (num_blocks, num_kv_heads, BLOCK_TOKENS, head_dim)
-        self.written = np.zeros((num_blocks, BLOCK_TOKENS), dtype=bool)
+        shape = (num_blocks, num_kv_heads, self.bs, head_dim)
+        self.written = np.zeros((num_blocks, self.bs), dtype=bool)
         self.store = {}
         for name, elem in (("k", self.k_elem), ("v", self.v_elem)):
             if kv_formats.is_quantised(elem):
@@ -97,8 +101,8 @@ class Pool:
         slots = np.asarray(slots, dtype=np.int64)
         keep = slots >= 0
         slots = slots[keep]
-        blk = slots // BLOCK_TOKENS
-        off = slots % BLOCK_TOKENS
+        blk = slots // self.bs
+        off = slots % self.bs
         if np.any(blk >= self.num_blocks):
             raise IndexError("slot outside the pool")
         for name, rows, elem in (("k", k_rows, self.k_elem), ("v", v_rows, self.v_elem)):
@@ -136,11 +140,11 @@ class Pool:
     def gather(self, table_row, length: int):
         """K, V ``[length][Hkv][D]`` float64 of one sequence, read through its
         block table in logical order: position t lives in physical block
-        ``table_row[t // 16]`` at offset ``t % 16``."""
+        ``table_row[t // bs]`` at offset ``t % bs``."""
         t = np.arange(int(length))
-        blocks = np.asarray(table_row, dtype=np.int64)[t // BLOCK_TOKENS]
+        blocks = np.asarray(table_row, dtype=np.int64)[t // self.bs]
         if length and (blocks.min() < 0 or blocks.max() >= self.num_blocks):
             raise IndexError("block table entry outside the pool")
-        if length and not np.all(self.written[blocks, t % BLOCK_TOKENS]):
+        if length and not np.all(self.written[blocks, t % self.bs]):
             raise ValueError("read of an unwritten slot")
-        return self.read_slots(blocks, t % BLOCK_TOKENS)
+        return self.read_slots(blocks, t % self.bs)

@@ -22,8 +22,8 @@ class OracleState:
     def __init__(self, w: wl.Workload, build_pool: bool = True, num_blocks: Optional[int] = None):
         self.w = w
         nb = num_blocks or w.num_blocks
-        self.alloc = BlockAllocatorModel(nb, w.max_blocks_per_seq)
-        self.pool = Pool(nb, w.num_kv_heads, w.head_dim, w.cache_dtype) if build_pool else None
+        self.alloc = BlockAllocatorModel(nb, w.max_blocks_per_seq, w.block_size)
+        self.pool = Pool(nb, w.num_kv_heads, w.head_dim, w.cache_dtype, w.block_size) if build_pool else None
         self.trace: List[tuple] = []          # (seq, slots, pairs) of every append
         self._rows: Dict[int, tuple] = {}
 

@@ -191,3 +191,85 @@ def test_swap_out_refuses_shared_blocks():
     assert m.swap_out(0) == [0, 1]
     m.free_seq(0)                       # a swapped sequence can be dropped
     assert m.swapped == {} and len(m.free) == 8
+
+
+# ---- 32-token blocks ("KV Cache 和 vLLM" §6.3) -----------------------------------------
+
+def test_hand_worked_32_token_blocks():
+    # free order 4,1,5,0,2,3.  s0: 1 token -> block 4; s1: 33 tokens -> 1, 5;
+    # s2: 32 tokens -> 0, then one more -> 2; fork s1 as s3 and append one
+    # token: 33 % 32 != 0 and block 5 is shared, so it is copied into 3.
+    a = BlockAllocatorModel(6, 4, block_size=32)
+    a.set_free_order([4, 1, 5, 0, 2, 3])
+    for s in range(3):
+        a.create(s)
+    assert a.append_slots(0, 1) == ([128], [])
+    assert a.append_slots(1, 33) == (list(range(32, 64)) + [160], [])
+    assert a.append_slots(2, 32) == (list(range(0, 32)), [])
+    assert a.append_slots(2, 1) == ([64], [])
+    assert a.block_tables(range(3), 4) == ([[4, 0, 0, 0], [1, 5, 0, 0], [0, 2, 0, 0]], [1, 33, 33])
+    a.fork(1, 3)
+    assert a.append_slots(3, 1) == ([97], [(5, 3)])
+    assert a.tables[3] == [1, 3] and a.ref[5] == 1 and a.ref[1] == 2
+    assert a.append_slots(0, 31) == (list(range(129, 160)), [])
+    with pytest.raises(AllocError) as e:
+        a.append_slots(0, 1)                          # position 32 needs a block; none free
+    assert e.value.kind == "no_free_blocks"
+    with pytest.raises(AllocError) as e:
+        a.append_slots(2, 100)                        # 133 tokens = 5 blocks > 4
+    assert e.value.kind == "invalid_arg"
+    assert a.append_slots(1, 31) == (list(range(161, 192)), [])   # block 5 is private again
+    st = a.stats()
+    assert st["used_blocks"] == 6 and st["shared_blocks"] == 1 and st["cow_copies"] == 1
+    assert st["cached_tokens"] == 32 + 64 + 33 + 34
+    assert st["stored_tokens"] == 32 + 32 + 32 + 32 + 1 + 2
+    assert st["utilisation"] == pytest.approx(131 / 192)
+    a.free_seq(1)                                     # block 1 -> count 1; block 5 freed
+    assert a.append_slots(0, 1) == ([160], []) and a.tables[0] == [4, 5]
+    assert a.swap_out(2) == [0, 2] and a.free == [0, 2]
+    assert a.swap_in(2) == [2, 0]
+
+
+def test_block_size_must_be_16_or_32():
+    for bad in (8, 24, 64):
+        with pytest.raises(AllocError):
+            BlockAllocatorModel(4, 4, block_size=bad)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_streams_with_32_token_blocks(seed):
+    rng = np.random.default_rng(100 + seed)
+    a = BlockAllocatorModel(40, 10, block_size=32)
+    a.set_free_order(rng.permutation(40))
+    live, nxt = [], 0
+    for _ in range(1200):
+        r = rng.random()
+        if r < 0.15 or not live:
+            a.create(nxt)
+            live.append(nxt)
+            nxt += 1
+        elif r < 0.3:
+            a.free_seq(live.pop(int(rng.integers(len(live)))))
+        elif r < 0.4:
+            a.fork(live[int(rng.integers(len(live)))], nxt)
+            live.append(nxt)
+            nxt += 1
+        else:
+            s = live[int(rng.integers(len(live)))]
+            n = int(rng.integers(0, 70))
+            try:
+                slots, pairs = a.append_slots(s, n)
+            except AllocError:
+                continue
+            L = a.lens[s]
+            for i, sl in enumerate(slots):
+                p = L - n + i
+                assert sl == 32 * a.tables[s][p // 32] + p % 32 and a.ref[sl // 32] == 1
+        counts = [0] * a.num_blocks
+        for t in a.tables.values():
+            for b in t:
+                counts[b] += 1
+        assert counts == a.ref
+        for s, t in a.tables.items():
+            assert len(t) == -(-a.lens[s] // 32)
+        assert len(a.free) + sum(1 for r in a.ref if r > 0) == a.num_blocks

@@ -116,11 +116,11 @@ def test_empty_context_is_zero():
     assert out.shape == (4, 64) and not out.any()
 
 
-def _build_paged(lengths, Hkv, D, num_blocks, order, seed, cache_dtype="f32"):
+def _build_paged(lengths, Hkv, D, num_blocks, order, seed, cache_dtype="f32", block_size=16):
     rng = np.random.default_rng(seed)
-    alloc = BlockAllocatorModel(num_blocks, 64)
+    alloc = BlockAllocatorModel(num_blocks, 64, block_size)
     alloc.set_free_order(order)
-    pool = cache.Pool(num_blocks, Hkv, D, cache_dtype)
+    pool = cache.Pool(num_blocks, Hkv, D, cache_dtype, block_size)
     rows = []
     for b, L in enumerate(lengths):
         alloc.create(b)
@@ -152,6 +152,30 @@ def test_paged_equals_contiguous_and_placement_invariant(cache_dtype):
         outs.append(out)
     # different physical placement, identical output (bitwise in fp64)
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+@pytest.mark.parametrize("cache_dtype", ["f32", "int8_int4"])
+def test_block_size_does_not_change_the_output(cache_dtype):
+    # the same rows in 16-token and in 32-token blocks, placed at random:
+    # reading through the tables gives the rows in logical order, so the
+    # outputs agree bit for bit, and each row sits at slot bs*table[p//bs] + p%bs
+    lengths = [1, 31, 32, 33, 64, 97]
+    Hq, Hkv, D = 4, 2, 64
+    q = np.random.default_rng(22).standard_normal((len(lengths), Hq, D))
+    outs = []
+    for bs, nb in ((16, 60), (32, 30)):
+        order = np.random.default_rng(bs).permutation(nb)
+        pool, tables, lens, rows = _build_paged(lengths, Hkv, D, nb, order, seed=6,
+                                                cache_dtype=cache_dtype, block_size=bs)
+        assert pool.k.shape[2] == bs
+        for b, (K, V) in enumerate(rows):
+            Kc, _ = attention.rows_as_cached(K, V, cache_dtype)
+            for p in (0, lengths[b] - 1):
+                sl = cache.slot_of(tables[b], p, bs)
+                assert sl == bs * tables[b][p // bs] + p % bs
+                assert np.array_equal(pool.read_slots([sl // bs], [sl % bs])[0][0], Kc[p])
+        outs.append(attention.decode_paged(q, pool, tables, lens, 1 / math.sqrt(D)))
+    assert np.array_equal(outs[0], outs[1])
 
 
 @pytest.mark.parametrize("P", [16, 64, 512, 4096])

@@ -6,8 +6,8 @@ off-by-one position, a reversed free order, a copy-on-write that skips the
 copy, a prefix cache that evicts by plain recency, keys a block by its own
 tokens only, lets a lookup cover the last prompt token or forgets released
 blocks, a prefill mask that hides the diagonal or a chunk placed at the
-start of the sequence, a wrong e5m2 bias, swapped int4 nibbles or integer
-rounding with ties up - must make at least one of the pins fail.  This shows the pins are
+start of the sequence, a wrong e5m2 bias, swapped int4 nibbles, integer
+rounding with ties up, or an allocator or pool that ignores the block size - must make at least one of the pins fail.  This shows the pins are
 sharp enough to catch the mistakes they are meant to catch."""
 import numpy as np
 import pytest
@@ -165,14 +165,14 @@ def test_plain_lru_eviction_is_caught(monkeypatch):
         self.ref[blk] = 1
         return blk
     monkeypatch.setattr(PCM, "_take", lru_take)
-    _fails(pins_prefix.test_hand_worked_leaf_first_eviction)
+    _fails(pins_prefix.test_hand_worked_leaf_first_eviction, 16)
 
 
 def test_block_only_key_is_caught(monkeypatch):
     # keying a block by its own 16 tokens, forgetting the prefix before it
     monkeypatch.setattr(PCM, "_key", lambda self, toks, nb: (self.model_key,) + tuple(
-        toks[BLOCK * (nb - 1):BLOCK * nb]))
-    _fails(pins_prefix.test_hits_hold_the_right_content_under_pressure, 0)
+        toks[self.bs * (nb - 1):self.bs * nb]))
+    _fails(pins_prefix.test_hits_hold_the_right_content_under_pressure, 0, 16)
 
 
 def test_lookup_bound_off_by_one_is_caught(monkeypatch):
@@ -192,7 +192,7 @@ def test_forgetting_released_blocks_is_caught(monkeypatch):
                 del self.index[self.key_of.pop(blk)]
             self.free.append(blk)
     monkeypatch.setattr(PCM, "_release", forget)
-    _fails(pins_prefix.test_hits_equal_brute_force_longest_shared_prefix, 0)
+    _fails(pins_prefix.test_hits_equal_brute_force_longest_shared_prefix, 0, 16)
 
 
 # ---- prefill mutants --------------------------------------------------------------------
@@ -239,3 +239,24 @@ def test_int_ties_up_are_caught(monkeypatch):
         return np.floor(y + np.float32(0.5)).astype(np.int8), s
     monkeypatch.setattr(kv_formats, "quantise_int_rows", half_up)
     _fails(pins_formats.test_int_codes_are_nearest_with_ties_to_even, 7)
+
+
+# ---- block-size mutants -------------------------------------------------------------------
+
+def test_allocator_ignoring_block_size_is_caught(monkeypatch):
+    init = alloc_mod.BlockAllocatorModel.__init__
+
+    def sixteen(self, *a, **kw):
+        init(self, *a, **kw)
+        self.bs = BLOCK
+    monkeypatch.setattr(alloc_mod.BlockAllocatorModel, "__init__", sixteen)
+    _fails(pins_alloc.test_hand_worked_32_token_blocks)
+
+
+def test_pool_ignoring_block_size_is_caught(monkeypatch):
+    init = cache.Pool.__init__
+
+    def sixteen(self, num_blocks, num_kv_heads, head_dim, cache_dtype, block_size=BLOCK):
+        init(self, num_blocks * block_size // BLOCK, num_kv_heads, head_dim, cache_dtype, BLOCK)
+    monkeypatch.setattr(cache.Pool, "__init__", sixteen)
+    _fails(pins_attn.test_block_size_does_not_change_the_output, "f32")

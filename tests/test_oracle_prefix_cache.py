@@ -23,15 +23,16 @@ from oracle.allocator import BLOCK_TOKENS, AllocError, PrefixCachingAllocatorMod
 B = BLOCK_TOKENS
 
 
-def blk(v):
-    return [v] * B
+def blk(v, bs=B):
+    return [v] * bs
 
 
 # ---- hand-worked example ------------------------------------------------------
 
-def hand_worked(alloc):
-    """Runs the paper example on ``alloc`` (model or native) and returns what
-    each step observed.  Pool of 5 blocks, block 0 handed out first.
+def hand_worked(alloc, bs=B):
+    """Runs the paper example on ``alloc`` (model or native, blocks of ``bs``
+    tokens) and returns what each step observed.  Pool of 5 blocks, block 0
+    handed out first; a, b, ... are blocks of bs equal tokens.
 
     r1 = a b c x: no hit; blocks 0,1,2 indexed (a, ab, abc), 3 partial.
     free r1: 0,1,2 evictable with stamps 1,2,3; 3 back on the free list.
@@ -44,7 +45,7 @@ def hand_worked(alloc):
     evicted 2 and then 0, the root both chains hang from.
     r4 = a b c w: abc is gone, a and ab remain -> 2 blocks hit.
     """
-    a, b, c, d, e, f = (blk(v) for v in (11, 12, 13, 14, 15, 16))
+    a, b, c, d, e, f = (blk(v, bs) for v in (11, 12, 13, 14, 15, 16))
     seen = {}
     p1 = a + b + c + [1]
     seen["r1_hit"] = alloc.create_cached(1, p1)
@@ -68,20 +69,25 @@ def hand_worked(alloc):
     return seen
 
 
-EXPECTED_HAND = {
-    "r1_hit": 0,
-    "r1_slots": list(range(0, 49)),                       # blocks 0,1,2,3
-    "r2_hit": 32,
-    "r2_slots": list(range(48, 64)) + [64],               # block 3 then block 4
-    "r3_slots": list(range(64, 80)) + list(range(32, 48)) + [48],   # blocks 4, 2, 3
-    "r4_hit": 32,
-}
+def expected_hand(bs=B):
+    return {
+        "r1_hit": 0,
+        "r1_slots": list(range(0, 3 * bs + 1)),                              # blocks 0,1,2,3
+        "r2_hit": 2 * bs,
+        "r2_slots": list(range(3 * bs, 4 * bs)) + [4 * bs],                  # block 3 then block 4
+        "r3_slots": list(range(4 * bs, 5 * bs)) + list(range(2 * bs, 3 * bs)) + [3 * bs],   # blocks 4, 2, 3
+        "r4_hit": 2 * bs,
+    }
 
 
-def test_hand_worked_leaf_first_eviction():
-    m = PrefixCachingAllocatorModel(5, 8)
-    seen = hand_worked(m)
-    for k, v in EXPECTED_HAND.items():
+EXPECTED_HAND = expected_hand()
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_hand_worked_leaf_first_eviction(bs):
+    m = PrefixCachingAllocatorModel(5, 8, block_size=bs)
+    seen = hand_worked(m, bs)
+    for k, v in expected_hand(bs).items():
         assert seen[k] == v, k
     assert seen["r3_refused"] == "no_free_blocks"
     assert m.tables[3] == [4, 2, 3] and m.tables[4] == [0, 1]
@@ -98,6 +104,19 @@ def test_lookup_never_covers_the_last_prompt_token():
     assert m.create_cached(2, p + [5]) == 32
     assert m.create_cached(3, blk(1)) == 0       # a one-block prompt never hits
     assert m.create_cached(4, []) == 0
+
+
+def test_lookup_bound_with_32_token_blocks():
+    # the same two 16-token runs form one 32-token block: a 32-token prompt
+    # never hits, a 33-token one hits the whole block
+    m = PrefixCachingAllocatorModel(8, 8, block_size=32)
+    p = blk(1) + blk(2)
+    m.create_cached(0, p + [3])
+    m.append_tokens(0, p + [3])
+    assert m.create_cached(1, p) == 0            # (32 - 1) // 32 = 0 blocks
+    assert m.create_cached(2, p + [5]) == 32
+    assert m.create_cached(3, blk(1) + blk(9) + [5]) == 0
+    assert len(m.index) == 1
 
 
 def test_model_key_separates_caches():
@@ -163,7 +182,8 @@ def _stream(seed, n_ops=600, pool=40, sys_prompts=3, vocab=3, shared=True):
 class Shadow:
     """slot -> the token prefix whose last position's K/V the slot holds."""
 
-    def __init__(self):
+    def __init__(self, bs=B):
+        self.bs = bs
         self.slot = {}
         self.stream = {}
 
@@ -174,10 +194,11 @@ class Shadow:
             self.slot[s] = tuple(toks[:base + i + 1])
 
     def copied(self, pairs):
+        bs = self.bs
         for src, dst in pairs:
-            for o in range(B):
-                if B * src + o in self.slot:
-                    self.slot[B * dst + o] = self.slot[B * src + o]
+            for o in range(bs):
+                if bs * src + o in self.slot:
+                    self.slot[bs * dst + o] = self.slot[bs * src + o]
 
 
 _CODES = {-1: "invalid_arg", -5: "no_free_blocks", -6: "unknown_seq"}
@@ -244,9 +265,9 @@ def replay(alloc, ops, shadow=None, check=None):
                     blocks = alloc.swap_in(s)
                     out_set.discard(s)
                     if shadow is not None:
-                        toks = shadow.stream[s]
+                        toks, bs = shadow.stream[s], shadow.bs
                         for p in range(len(toks)):
-                            shadow.slot[B * blocks[p // B] + p % B] = tuple(toks[:p + 1])
+                            shadow.slot[bs * blocks[p // bs] + p % bs] = tuple(toks[:p + 1])
                 else:
                     blocks = alloc.swap_out(s)
                     out_set.add(s)
@@ -268,10 +289,12 @@ def replay(alloc, ops, shadow=None, check=None):
 
 
 def _hit_check(shadow):
+    bs = shadow.bs
+
     def check(m, s, prompt, n):
-        assert n % B == 0 and n <= max(len(prompt) - 1, 0)
+        assert n % bs == 0 and n <= max(len(prompt) - 1, 0)
         for p in range(n):
-            slot = B * m.tables[s][p // B] + p % B
+            slot = bs * m.tables[s][p // bs] + p % bs
             assert shadow.slot.get(slot) == tuple(prompt[:p + 1]), (s, p)
     return check
 
@@ -279,23 +302,23 @@ def _hit_check(shadow):
 def _invariants(m):
     for key, b in m.index.items():
         assert m.key_of[b] == key
-        if len(key) > 1 + B:
-            assert key[:-B] in m.index                          # parents stay indexed
+        if len(key) > 1 + m.bs:
+            assert key[:-m.bs] in m.index                          # parents stay indexed
     for b in m.evictable:
         assert m.ref[b] == 0 and b in m.key_of
     assert len(m.free) + len(m.evictable) + sum(1 for r in m.ref if r > 0) == m.num_blocks
 
 
-@pytest.mark.parametrize("seed", range(6))
-def test_hits_hold_the_right_content_under_pressure(seed):
-    m = PrefixCachingAllocatorModel(40, 12)
-    shadow = Shadow()
+@pytest.mark.parametrize("seed,bs", [(s, 16) for s in range(6)] + [(s, 32) for s in (0, 1, 4)])
+def test_hits_hold_the_right_content_under_pressure(seed, bs):
+    m = PrefixCachingAllocatorModel(40 * 16 // bs, 12 * 16 // bs, block_size=bs)
+    shadow = Shadow(bs)
     ops = list(_stream(seed, shared=seed < 4))
     res = replay(m, ops, shadow, _hit_check(shadow))
     _invariants(m)
     st = m.prefix_stats()
     if seed < 4:
-        assert st["hit_blocks"] > 20 and st["evictions"] > 20, st   # the stream exercises both
+        assert st["hit_blocks"] > 20 and st["evictions"] > 320 // bs // (bs // 16), st   # exercises both
     else:
         assert sum(1 for r in res if r[0] == "swap" and r[1] != "error") > 5   # swaps go through
     assert any(r[1:2] == ("error",) for r in res)
@@ -303,10 +326,10 @@ def test_hits_hold_the_right_content_under_pressure(seed):
 
 # ---- brute force with no eviction ---------------------------------------------------
 
-@pytest.mark.parametrize("seed", range(4))
-def test_hits_equal_brute_force_longest_shared_prefix(seed):
+@pytest.mark.parametrize("seed,B", [(s, 16) for s in range(4)] + [(s, 32) for s in range(2)])
+def test_hits_equal_brute_force_longest_shared_prefix(seed, B):
     rng = np.random.default_rng(50 + seed)
-    m = PrefixCachingAllocatorModel(4096, 64)
+    m = PrefixCachingAllocatorModel(4096, 64, block_size=B)
     systems = [list(rng.integers(0, 4, size=int(rng.integers(10, 60)))) for _ in range(4)]
     done = []                                    # full token streams of finished requests
     for r in range(120):

@@ -71,6 +71,7 @@ class Workload:
     prefix_len: int = 0                       # shared-prefix length (workload 4)
     decode_appends: int = 0                   # extra single-token appends per sequence
     extra: dict = field(default_factory=dict)
+    block_size: int = BLOCK_TOKENS            # tokens per physical block (16 or 32)
 
     @property
     def group(self) -> int:
@@ -101,8 +102,8 @@ def _normal(rng: np.random.Generator, shape) -> np.ndarray:
 # Workload definitions
 # ----------------------------------------------------------------------------
 
-def _pool_for(lens: List[int], factor: float = 1.1) -> int:
-    demand = sum(-(-L // BLOCK_TOKENS) for L in lens)
+def _pool_for(lens: List[int], factor: float = 1.1, block_size: int = BLOCK_TOKENS) -> int:
+    demand = sum(-(-L // block_size) for L in lens)
     return int(math.ceil(factor * demand))
 
 
@@ -183,15 +184,30 @@ def make_workload(config_id: int, seed: Optional[int] = None) -> Workload:
 def custom_workload(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                     context_lens: List[int], dtype: str = "bf16", cache_dtype: Optional[str] = None,
                     q_dtype: Optional[str] = None, seed: int = 7, pool_factor: float = 1.25,
-                    extra_blocks: int = 4) -> Workload:
+                    extra_blocks: int = 4, block_size: int = BLOCK_TOKENS) -> Workload:
     """A free-form workload (edge cases and small parity sweeps)."""
     cache_dtype = cache_dtype or dtype
     q_dtype = q_dtype or ("bf16" if dtype == "f32" and cache_dtype == "fp8_e4m3" else dtype)
-    nb = max(1, _pool_for(context_lens, pool_factor) + extra_blocks)
-    mb = max(1, max([-(-L // BLOCK_TOKENS) for L in context_lens] + [1]) + 2)
+    nb = max(1, _pool_for(context_lens, pool_factor, block_size) + extra_blocks)
+    mb = max(1, max([-(-L // block_size) for L in context_lens] + [1]) + 2)
     return Workload(0, "custom", seed, num_seqs, num_q_heads, num_kv_heads, head_dim,
                     q_dtype, dtype, cache_dtype, list(context_lens), nb, mb,
-                    free_order=_rng(seed, _TAG_PLACE).permutation(nb).astype(np.int32))
+                    free_order=_rng(seed, _TAG_PLACE).permutation(nb).astype(np.int32), block_size=block_size)
+
+
+def with_block_size(w: Workload, block_size: int) -> Workload:
+    """The same workload (same rows, lengths and placement seed) on a pool of
+    ``block_size``-token blocks sized by the same rule."""
+    import dataclasses
+    if block_size == w.block_size:
+        return w
+    ratio = w.block_size / block_size
+    nb = max(1, int(math.ceil(w.num_blocks * ratio)) + 2)
+    mb = max(1, int(math.ceil(w.max_blocks_per_seq * ratio)) + 1)
+    out = dataclasses.replace(w, block_size=block_size, num_blocks=nb, max_blocks_per_seq=mb,
+                              free_order=_rng(w.seed, _TAG_PLACE, block_size).permutation(nb).astype(np.int32),
+                              churn_ops=None, churn_release=None, name=f"{w.name}-bs{block_size}")
+    return out
 
 
 # ----------------------------------------------------------------------------
