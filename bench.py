@@ -81,6 +81,8 @@ def parse():
     ap.add_argument("--cache", default=None,
                     help="decode row: cache format to run the workload with instead of its own "
                          "(fp8_e4m3, fp8_e5m2, int8_int4, ...; K/V rows stay in the workload's dtype)")
+    ap.add_argument("--block-size", type=int, choices=[16, 32], default=16,
+                    help="decode row: tokens per block (32: the same workload on 32-token blocks)")
     ap.add_argument("--cached", type=int, default=3584, help="prefill row: cached tokens per sequence")
     ap.add_argument("--chunk", type=int, default=512, help="prefill row: chunk tokens per sequence")
     ap.add_argument("--one-call", action="store_true",
@@ -213,7 +215,8 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = wl.make_workload(args.config)
+    w = wl.with_block_size(wl.make_workload(args.config), args.block_size)
+    bs = w.block_size
     B, hq, hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
     if args.cache:
         if args.cache not in KV_BYTES:
@@ -225,13 +228,13 @@ def main():
             w.src_dtype = w.q_dtype = args.cache
         w.name = f"{w.name}-{args.cache}"
     kb_el, vb_el, nscale = KV_BYTES[w.cache_dtype]
-    per_layer_bytes = int(w.num_blocks * hkv * 16 * (D * (kb_el + vb_el) + 8 * nscale))
+    per_layer_bytes = int(w.num_blocks * hkv * bs * (D * (kb_el + vb_el) + 8 * nscale))
     layers = args.layers or (32 if args.config == 2 else max(1, math.ceil(4 * MALL_BYTES / per_layer_bytes)))
     log(f"[bench] workload {args.config} {w.name}: B={B} Hq={hq} Hkv={hkv} D={D} cache={w.cache_dtype} "
         f"layers={layers} pool={w.num_blocks} blocks/layer ({per_layer_bytes / 2**30:.2f} GiB/layer)")
 
     cache = PagedKVCache(layers, w.num_blocks, hkv, D, w.cache_dtype, w.max_blocks_per_seq,
-                         device=dev)
+                         device=dev, block_size=bs)
     gen = torch.Generator(device=dev)
     src_t = TORCH_DTYPES[w.src_dtype]
 
@@ -337,8 +340,8 @@ def main():
             kp, vp, ksp, vsp = pools[l]
             kl, vl = kbase + l * kv_stride, vbase + l * kv_stride
             if args.unfused:
-                rc = lib.kv_cache_append(kl, vl, kp, vp, ksp, vsp, d_slots.data_ptr(), B, hkv, D, w.num_blocks,
-                                         src_code, cache_code, sp)
+                rc = lib.kv_cache_append_bs(kl, vl, kp, vp, ksp, vsp, d_slots.data_ptr(), B, hkv, D, w.num_blocks,
+                                            bs, src_code, cache_code, sp)
                 if rc:
                     raise pkv.PagedKVError(rc, "kv_cache_append")
             e = ev.get((s, l)) if timed else None
@@ -346,10 +349,11 @@ def main():
                 e[0].record(stream)
             o_ptr, q_ptr = outs.data_ptr() + l * out_stride, qbase + l * q_stride
             if args.one_call:
-                rc = lib.paged_attention_decode_append(o_ptr, q_ptr, kl, vl, kp, vp, ksp, vsp, d_slots.data_ptr(),
-                                                       d_tables.data_ptr(), d_lens.data_ptr(), B, hq, hkv, D,
-                                                       w.num_blocks, mb, max_len, scale, q_code, src_code,
-                                                       cache_code, args.partition_size, ws_ptr, ws_bytes, sp)
+                rc = lib.paged_attention_decode_append_bs(o_ptr, q_ptr, kl, vl, kp, vp, ksp, vsp,
+                                                          d_slots.data_ptr(), d_tables.data_ptr(), d_lens.data_ptr(),
+                                                          B, hq, hkv, D, w.num_blocks, bs, mb, max_len, scale,
+                                                          q_code, src_code, cache_code, args.partition_size,
+                                                          ws_ptr, ws_bytes, sp)
                 if rc:
                     raise pkv.PagedKVError(rc, "paged_attention_decode_append")
                 if e:
@@ -359,17 +363,17 @@ def main():
             # split form: the attention kernel (with the cache write fused in,
             # unless --unfused wrote it already), then the partition merge
             slot_ptr = None if args.unfused else d_slots.data_ptr()
-            rc = lib.paged_attention_decode_append_partials(o_ptr, q_ptr, kl, vl, kp, vp, ksp, vsp, slot_ptr,
-                                                            d_tables.data_ptr(), d_lens.data_ptr(), B, hq, hkv,
-                                                            D, w.num_blocks, mb, max_len, scale, q_code,
-                                                            src_code, cache_code, args.partition_size, ws_ptr,
-                                                            ws_bytes, sp)
+            rc = lib.paged_attention_decode_append_partials_bs(o_ptr, q_ptr, kl, vl, kp, vp, ksp, vsp, slot_ptr,
+                                                               d_tables.data_ptr(), d_lens.data_ptr(), B, hq, hkv,
+                                                               D, w.num_blocks, bs, mb, max_len, scale, q_code,
+                                                               src_code, cache_code, args.partition_size, ws_ptr,
+                                                               ws_bytes, sp)
             if rc:
                 raise pkv.PagedKVError(rc, "paged_attention_decode_append_partials")
             if e:
                 e[1].record(stream)
-            rc = lib.paged_attention_merge_partials(o_ptr, d_lens.data_ptr(), B, hq, hkv, D, mb, max_len, q_code,
-                                                    args.partition_size, ws_ptr, ws_bytes, sp)
+            rc = lib.paged_attention_merge_partials_bs(o_ptr, d_lens.data_ptr(), B, hq, hkv, D, bs, mb, max_len,
+                                                       q_code, args.partition_size, ws_ptr, ws_bytes, sp)
             if rc:
                 raise pkv.PagedKVError(rc, "paged_attention_merge_partials")
             if e:
@@ -378,7 +382,7 @@ def main():
             tokens_timed += sum_l * layers
             kv_bytes = sum_l * hkv * (D * (kb_el + vb_el) + 8 * nscale)
             qo_bytes = 2 * B * hq * D * ES[w.q_dtype]
-            table_bytes = sum(-(-L // 16) for L in lens) * 4 + B * 4
+            table_bytes = sum(-(-L // bs) for L in lens) * 4 + B * 4
             # the fused call also reads the new rows and slots (its writes are
             # inside the K/V bytes already counted)
             new_bytes = 0 if args.unfused else B * hkv * D * 2 * ES[w.src_dtype] + B * 8
@@ -423,7 +427,7 @@ def main():
         "config": {
             "workload": f"{w.name} (paged decode, one layer per call)",
             "batch": B, "context_len_first_timed_step": max(w.context_lens) + args.warmup + 1,
-            "q_heads": hq, "kv_heads": hkv, "head_dim": D, "block_size": 16, "kv_dtype": w.cache_dtype,
+            "q_heads": hq, "kv_heads": hkv, "head_dim": D, "block_size": bs, "kv_dtype": w.cache_dtype,
             "q_dtype": w.q_dtype, "layers_rotated": layers, "pool_blocks_per_layer": w.num_blocks,
             "partition_size": ps_used, "parallelism": "none (1 GPU)",
         },

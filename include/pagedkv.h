@@ -4,9 +4,11 @@
  *
  * The method (pages: "KV Cache 和 vLLM" §1.2-1.3, §3.1-3.3; "KV Cache优化实战"
  * §2.1, §3.2-3.3, §4.2; "企业官网建设流程全解析" §1.2-1.3, §2.2, §3.2):
- *   - each layer keeps its K and V in a pool of fixed 16-token physical blocks;
+ *   - each layer keeps its K and V in a pool of fixed 16-token physical blocks
+ *     (or 32-token ones, "KV Cache 和 vLLM" §6.3: fewer table entries for long
+ *     sequences, more unused slots for short ones);
  *   - each sequence has a block table mapping logical block i (tokens
- *     16i..16i+15) to a physical block, so a sequence is logically contiguous
+ *     bs*i..bs*i+bs-1, bs the block size) to a physical block, so a sequence is logically contiguous
  *     and physically scattered;
  *   - a decode step appends the new token's K and V to the cache, then the new
  *     query attends over every cached token, itself included:
@@ -40,7 +42,8 @@
 extern "C" {
 #endif
 
-#define PKV_BLOCK_SIZE 16   /* tokens per physical block ("KV Cache 和 vLLM" §3.1) */
+#define PKV_BLOCK_SIZE 16         /* tokens per physical block ("KV Cache 和 vLLM" §3.1) */
+#define PKV_BLOCK_SIZE_LARGE 32   /* the other block size the _bs calls take (§6.3 there) */
 #define PKV_ABI_VERSION 1
 #define PKV_MAX_PARTITION_TOKENS 32768   /* largest decode partition (tokens) */
 #define PKV_MAX_PREFILL_CONTEXT 32768    /* longest context a prefill call reads (tokens) */
@@ -71,14 +74,21 @@ int pkv_abi_version(void);
 const char* pkv_strerror(int code);
 
 /* ------------------------------------------------------------------------ */
-/* Device layouts (row-major, contiguous):                                   */
-/*   k_pool, v_pool   [num_blocks][num_kv_heads][16][head_dim] of cache dtype */
+/* Device layouts (row-major, contiguous), bs = block size (tokens):         */
+/*   k_pool, v_pool   [num_blocks][num_kv_heads][bs][head_dim] of cache dtype */
 /*                    (one byte per code for fp8 and int8; PKV_INT8_INT4's V */
-/*                    pool is [num_blocks][num_kv_heads][16][head_dim / 2]   */
+/*                    pool is [num_blocks][num_kv_heads][bs][head_dim / 2]   */
 /*                    bytes, element 2i in the low nibble of byte i)         */
-/*   k_scale, v_scale [num_blocks][num_kv_heads][16] float32 (quantised      */
+/*   k_scale, v_scale [num_blocks][num_kv_heads][bs] float32 (quantised      */
 /*                    caches only: fp8 e4m3 / e5m2, int8 + int4)             */
-/*   slot = physical_block * 16 + (position % 16)                            */
+/*   slot = physical_block * bs + (position % bs)                            */
+/* The plain calls use bs = PKV_BLOCK_SIZE (16).  Each call named _bs takes  */
+/* the same arguments plus `block_size` (16 or 32; anything else gives      */
+/* PKV_ERR_INVALID_ARG) right after num_blocks (after head_dim for the      */
+/* merge), and reads every "16" of the plain call's description as that     */
+/* block size - except partition sizes, which stay multiples of 16 tokens.  */
+/* A pool of 32-token blocks also needs num_blocks * num_kv_heads * 2 <     */
+/* 2^31 (else PKV_ERR_UNSUPPORTED from the decode and prefill calls).       */
 /* ------------------------------------------------------------------------ */
 
 /*
@@ -115,6 +125,12 @@ int kv_cache_append(const void* k_new, const void* v_new,
                     int num_tokens, int num_kv_heads, int head_dim, int num_blocks,
                     pkv_dtype src_dtype, pkv_dtype cache_dtype, void* stream);
 
+int kv_cache_append_bs(const void* k_new, const void* v_new,
+                       void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                       const int64_t* slot_mapping,
+                       int num_tokens, int num_kv_heads, int head_dim, int num_blocks, int block_size,
+                       pkv_dtype src_dtype, pkv_dtype cache_dtype, void* stream);
+
 /*
  * pkv_copy_blocks - copy whole physical blocks (K, V and, for a quantised
  * cache, the scales) from src to dst, for the copy-on-write of a shared block that one
@@ -127,6 +143,11 @@ int pkv_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
                     const int32_t* pairs, int n_pairs,
                     int num_kv_heads, int head_dim, int num_blocks, pkv_dtype cache_dtype,
                     void* stream);
+
+int pkv_copy_blocks_bs(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                       const int32_t* pairs, int n_pairs,
+                       int num_kv_heads, int head_dim, int num_blocks, int block_size,
+                       pkv_dtype cache_dtype, void* stream);
 
 /*
  * pkv_decode_partition_size - the partition length (tokens, a multiple of 16)
@@ -198,6 +219,16 @@ int paged_attention_decode(void* out, const void* q,
                            int partition_size, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+int paged_attention_decode_bs(void* out, const void* q,
+                              const void* k_pool, const void* v_pool,
+                              const float* k_scale, const float* v_scale,
+                              const int32_t* block_tables, const int32_t* context_lens,
+                              int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                              int num_blocks, int block_size, int max_blocks_per_seq, int max_context_len,
+                              float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                              int partition_size, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /*
  * paged_attention_decode_append - one decode step with its cache write fused
  * in: the same result, pool bytes and scales as kv_cache_append(k_new, v_new,
@@ -229,6 +260,16 @@ int paged_attention_decode_append(void* out, const void* q, const void* k_new, c
                                   pkv_dtype cache_dtype, int partition_size, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+int paged_attention_decode_append_bs(void* out, const void* q, const void* k_new, const void* v_new,
+                                     void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                     const int64_t* slot_mapping,
+                                     const int32_t* block_tables, const int32_t* context_lens,
+                                     int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                     int num_blocks, int block_size, int max_blocks_per_seq,
+                                     int max_context_len, float scale, pkv_dtype q_dtype,
+                                     pkv_dtype src_dtype, pkv_dtype cache_dtype, int partition_size,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Split form of paged_attention_decode_append, for callers that schedule or
  * time its two launches separately.  paged_attention_decode_append_partials
@@ -257,6 +298,22 @@ int paged_attention_merge_partials(void* out, const int32_t* context_lens,
                                    int max_blocks_per_seq, int max_context_len, pkv_dtype q_dtype,
                                    int partition_size, void* workspace, size_t workspace_bytes,
                                    void* stream);
+
+int paged_attention_decode_append_partials_bs(void* out, const void* q, const void* k_new, const void* v_new,
+                                              void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                              const int64_t* slot_mapping,
+                                              const int32_t* block_tables, const int32_t* context_lens,
+                                              int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                              int num_blocks, int block_size, int max_blocks_per_seq,
+                                              int max_context_len, float scale, pkv_dtype q_dtype,
+                                              pkv_dtype src_dtype, pkv_dtype cache_dtype, int partition_size,
+                                              void* workspace, size_t workspace_bytes, void* stream);
+
+int paged_attention_merge_partials_bs(void* out, const int32_t* context_lens,
+                                      int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                      int block_size, int max_blocks_per_seq, int max_context_len,
+                                      pkv_dtype q_dtype, int partition_size, void* workspace,
+                                      size_t workspace_bytes, void* stream);
 
 /*
  * paged_attention_prefill - chunked prefill: each sequence's chunk of new
@@ -295,6 +352,13 @@ int paged_attention_prefill(void* out, const void* q, const void* k_pool, const 
                             int max_blocks_per_seq, int max_context_len, int max_query_len, float scale,
                             pkv_dtype q_dtype, pkv_dtype cache_dtype, void* stream);
 
+int paged_attention_prefill_bs(void* out, const void* q, const void* k_pool, const void* v_pool,
+                               const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                               const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+                               int num_tokens, int num_q_heads, int num_kv_heads, int head_dim, int num_blocks,
+                               int block_size, int max_blocks_per_seq, int max_context_len, int max_query_len,
+                               float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, void* stream);
+
 /*
  * pkv_gather_blocks / pkv_scatter_blocks - move whole physical blocks between
  * one pool tensor and a contiguous staging buffer, for swapping sequences out
@@ -307,8 +371,9 @@ int paged_attention_prefill(void* out, const void* q, const void* k_pool, const 
  *   blocks       device int32 [n_blocks]; ids outside [0, num_blocks) are
  *                skipped (their staging slot is not touched)
  *   block_bytes  bytes of one block of this tensor, a multiple of 16:
- *                num_kv_heads * 16 * head_dim * element size (int4 V: half a
- *                byte per element; scales: num_kv_heads * 16 * 4)
+ *                num_kv_heads * bs * head_dim * element size (int4 V: half a
+ *                byte per element; scales: num_kv_heads * bs * 4), bs the
+ *                pool's block size
  * The caller moves the staging buffer to or from pinned host memory; nothing
  * here touches host memory.  Asynchronous on stream.
  */
@@ -348,12 +413,18 @@ typedef struct {
   int64_t cow_copies;      /* copy pairs reported so far */
   int64_t cached_tokens;   /* sum over live sequences of their length */
   int64_t stored_tokens;   /* filled physical slots, a shared slot counted once */
-  double utilisation;      /* stored_tokens / (16 * used_blocks), 0 if none used */
+  double utilisation;      /* stored_tokens / (bs * used_blocks), 0 if none used */
 } pkv_alloc_stats_t;
 
-/* New allocator with every block free (block 0 handed out first).
-   Returns NULL if num_blocks <= 0 or max_blocks_per_seq <= 0. */
+/* New allocator of 16-token blocks with every block free (block 0 handed
+   out first).  Returns NULL if num_blocks <= 0 or max_blocks_per_seq <= 0. */
 pkv_alloc* pkv_alloc_create(int num_blocks, int max_blocks_per_seq);
+/* The same with block_size tokens per block (16 or 32, else NULL): every
+   rule below counts positions in blocks of that size, and slots are
+   block * block_size + offset ("KV Cache 和 vLLM" §6.3). */
+pkv_alloc* pkv_alloc_create_bs(int num_blocks, int max_blocks_per_seq, int block_size);
+/* Tokens per block of an allocator (16 or 32), or PKV_ERR_INVALID_ARG. */
+int pkv_alloc_block_size(const pkv_alloc* a);
 void pkv_alloc_destroy(pkv_alloc* a);
 
 /* Reorder the free list of an idle allocator (no live sequence): order is a
@@ -409,7 +480,7 @@ int pkv_alloc_stats(pkv_alloc* a, pkv_alloc_stats_t* out);
  * blocks stay cached and evictable).  The sequence keeps only its length;
  * it stops being prefix-indexed.  The caller gathers those blocks (stream
  * order keeps later writes to them behind the gather).
- * pkv_seq_swap_in - bring a swapped sequence back: takes ceil(len / 16)
+ * pkv_seq_swap_in - bring a swapped sequence back: takes ceil(len / bs)
  * fresh blocks, all or nothing (PKV_ERR_NO_FREE_BLOCKS), writes them in
  * logical order to blocks_out for the caller to scatter into.
  * A swapped sequence can only be swapped in, freed or asked its length;

@@ -19,7 +19,7 @@ import torch
 from . import _lib
 
 __all__ = [
-    "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3", "PKV_FP8_E5M2", "PKV_INT8_INT4", "BLOCK_SIZE",
+    "PKV_F32", "PKV_F16", "PKV_BF16", "PKV_FP8_E4M3", "PKV_FP8_E5M2", "PKV_INT8_INT4", "BLOCK_SIZE", "BLOCK_SIZES",
     "PagedKVError", "cache_code", "CACHE_FORMATS",
     "kv_cache_append", "copy_blocks", "paged_attention_decode", "paged_attention_decode_append",
     "paged_attention_decode_append_partials", "paged_attention_merge_partials",
@@ -30,6 +30,7 @@ __all__ = [
 
 PKV_F32, PKV_F16, PKV_BF16, PKV_FP8_E4M3, PKV_FP8_E5M2, PKV_INT8_INT4 = 0, 1, 2, 3, 4, 5
 BLOCK_SIZE = 16
+BLOCK_SIZES = (16, 32)         # tokens per block the library takes
 
 _TORCH_TO_CODE = {
     torch.float32: PKV_F32,
@@ -104,10 +105,12 @@ def _stream(stream) -> Optional[int]:
     return int(stream)
 
 
-def _pool_geometry(k_pool: torch.Tensor) -> Tuple[int, int, int]:
-    if k_pool.dim() != 4 or k_pool.shape[2] != BLOCK_SIZE:
-        raise ValueError("pools are [num_blocks, num_kv_heads, 16, head_dim]")
-    return int(k_pool.shape[0]), int(k_pool.shape[1]), int(k_pool.shape[3])
+def _pool_geometry(k_pool: torch.Tensor) -> Tuple[int, int, int, int]:
+    """(num_blocks, num_kv_heads, head_dim, block_size) of a K pool
+    ``[num_blocks, num_kv_heads, block_size, head_dim]``, block_size 16 or 32."""
+    if k_pool.dim() != 4 or k_pool.shape[2] not in BLOCK_SIZES:
+        raise ValueError("pools are [num_blocks, num_kv_heads, block_size (16 or 32), head_dim]")
+    return int(k_pool.shape[0]), int(k_pool.shape[1]), int(k_pool.shape[3]), int(k_pool.shape[2])
 
 
 def kv_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tensor,
@@ -115,28 +118,28 @@ def kv_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tens
                     k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
                     stream=None) -> None:
     """Write rows ``k_new, v_new [T, Hkv, D]`` to ``slot_mapping [T]`` (int64) of the pools."""
-    nb, hkv, d = _pool_geometry(k_pool)
+    nb, hkv, d, bs = _pool_geometry(k_pool)
     if k_new.shape[1:] != (hkv, d) or v_new.shape != k_new.shape:
         raise ValueError("k_new/v_new must be [T, Hkv, D] matching the pool")
     if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != k_new.shape[0]:
         raise ValueError("slot_mapping must be int64 [T]")
-    _check(_lib.lib().kv_cache_append(
+    _check(_lib.lib().kv_cache_append_bs(
         _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
-        _ptr(slot_mapping), int(k_new.shape[0]), hkv, d, nb, dtype_code(k_new.dtype),
-        cache_code(k_pool, v_pool), _stream(stream)), "kv_cache_append")
+        _ptr(slot_mapping), int(k_new.shape[0]), hkv, d, nb, bs, dtype_code(k_new.dtype),
+        cache_code(k_pool, v_pool), _stream(stream)), "kv_cache_append_bs")
 
 
 def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torch.Tensor,
                 k_scale: Optional[torch.Tensor] = None, v_scale: Optional[torch.Tensor] = None,
                 stream=None) -> None:
     """Copy whole blocks ``pairs [n, 2] = (src, dst)`` (int32, device)."""
-    nb, hkv, d = _pool_geometry(k_pool)
+    nb, hkv, d, bs = _pool_geometry(k_pool)
     if pairs.dtype != torch.int32 or (pairs.numel() and pairs.shape[-1] != 2):
         raise ValueError("pairs must be int32 [n, 2]")
-    _check(_lib.lib().pkv_copy_blocks(
+    _check(_lib.lib().pkv_copy_blocks_bs(
         _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(pairs),
-        int(pairs.numel() // 2), hkv, d, nb, cache_code(k_pool, v_pool), _stream(stream)),
-        "pkv_copy_blocks")
+        int(pairs.numel() // 2), hkv, d, nb, bs, cache_code(k_pool, v_pool), _stream(stream)),
+        "pkv_copy_blocks_bs")
 
 
 def decode_partition_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
@@ -162,7 +165,7 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
                            workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """One decode step: ``out[b, h] = softmax(q[b, h] . K_b^T * scale) V_b`` over
     each sequence's first ``context_lens[b]`` cached tokens."""
-    nb, hkv, d = _pool_geometry(k_pool)
+    nb, hkv, d, bs = _pool_geometry(k_pool)
     if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q and out must be [B, Hq, D] of one dtype")
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
@@ -178,11 +181,11 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
         # zeroed once: the library keeps its counters zero between calls
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib.lib().paged_attention_decode(
+    _check(_lib.lib().paged_attention_decode_bs(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
-        _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb, int(block_tables.shape[1]),
+        _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb, bs, int(block_tables.shape[1]),
         int(max_context_len), float(scale), dtype_code(q.dtype), cdt, int(partition_size),
-        _ptr(workspace), ws_bytes, _stream(stream)), "paged_attention_decode")
+        _ptr(workspace), ws_bytes, _stream(stream)), "paged_attention_decode_bs")
     return out
 
 
@@ -194,7 +197,7 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Te
     """Chunked prefill: ``out[t, h]`` for chunk row t of sequence b (rows
     ``query_start[b] .. query_start[b+1]-1``) attends over the first
     ``context_lens[b] - n_b + i + 1`` cached tokens, i = t - query_start[b]."""
-    nb, hkv, d = _pool_geometry(k_pool)
+    nb, hkv, d, bs = _pool_geometry(k_pool)
     if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q and out must be [T, Hq, D] of one dtype")
     if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32 or query_start.dtype != torch.int32:
@@ -205,11 +208,11 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Te
     T, hq = int(q.shape[0]), int(q.shape[1])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    _check(_lib.lib().paged_attention_prefill(
+    _check(_lib.lib().paged_attention_prefill_bs(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
-        _ptr(context_lens), _ptr(query_start), B, T, hq, hkv, d, nb, int(block_tables.shape[1]),
+        _ptr(context_lens), _ptr(query_start), B, T, hq, hkv, d, nb, bs, int(block_tables.shape[1]),
         int(max_context_len), int(max_query_len), float(scale), dtype_code(q.dtype), cache_code(k_pool, v_pool),
-        _stream(stream)), "paged_attention_prefill")
+        _stream(stream)), "paged_attention_prefill_bs")
     return out
 
 
@@ -240,7 +243,7 @@ def scatter_blocks(pool: torch.Tensor, staging: torch.Tensor, blocks: torch.Tens
 def _decode_append_call(fn_name, out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables,
                         context_lens, max_context_len, scale, k_scale, v_scale, partition_size, workspace,
                         stream):
-    nb, hkv, d = _pool_geometry(k_pool)
+    nb, hkv, d, bs = _pool_geometry(k_pool)
     if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape or out.dtype != q.dtype:
         raise ValueError("q and out must be [B, Hq, D] of one dtype")
     B, hq = int(q.shape[0]), int(q.shape[1])
@@ -259,9 +262,9 @@ def _decode_append_call(fn_name, out, q, k_new, v_new, k_pool, v_pool, slot_mapp
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     src_code = dtype_code(k_new.dtype) if k_new is not None else dtype_code(q.dtype)
-    _check(getattr(_lib.lib(), fn_name)(
+    _check(getattr(_lib.lib(), fn_name + "_bs")(
         _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
-        _ptr(v_scale), _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb,
+        _ptr(v_scale), _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb, bs,
         int(block_tables.shape[1]), int(max_context_len), float(scale), dtype_code(q.dtype),
         src_code, cdt, int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)), fn_name)
     return out, workspace
@@ -297,14 +300,16 @@ def paged_attention_decode_append_partials(out, q, k_new, v_new, k_pool, v_pool,
 
 def paged_attention_merge_partials(out: torch.Tensor, context_lens: torch.Tensor, num_kv_heads: int,
                                    max_blocks_per_seq: int, max_context_len: int, partition_size: int = 0,
-                                   workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """Second launch of the split form: merge the partition states."""
+                                   workspace: Optional[torch.Tensor] = None, stream=None,
+                                   block_size: int = BLOCK_SIZE) -> torch.Tensor:
+    """Second launch of the split form: merge the partition states
+    (``block_size``: that of the pool the first launch read)."""
     B, hq, d = (int(x) for x in out.shape)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(_lib.lib().paged_attention_merge_partials(
-        _ptr(out), _ptr(context_lens), B, hq, num_kv_heads, d, max_blocks_per_seq, int(max_context_len),
-        dtype_code(out.dtype), int(partition_size), _ptr(workspace), ws_bytes, _stream(stream)),
-        "paged_attention_merge_partials")
+    _check(_lib.lib().paged_attention_merge_partials_bs(
+        _ptr(out), _ptr(context_lens), B, hq, num_kv_heads, d, int(block_size), max_blocks_per_seq,
+        int(max_context_len), dtype_code(out.dtype), int(partition_size), _ptr(workspace), ws_bytes,
+        _stream(stream)), "paged_attention_merge_partials_bs")
     return out
 
 
@@ -317,13 +322,14 @@ class BlockAllocator:
     """Host block allocator (refcounts, fork, copy-on-write planning and,
     once ``enable_prefix_cache`` is called, prefix caching)."""
 
-    def __init__(self, num_blocks: int, max_blocks_per_seq: int):
+    def __init__(self, num_blocks: int, max_blocks_per_seq: int, block_size: int = BLOCK_SIZE):
         self._lib = _lib.lib()
-        self._h = self._lib.pkv_alloc_create(num_blocks, max_blocks_per_seq)
+        self._h = self._lib.pkv_alloc_create_bs(num_blocks, max_blocks_per_seq, block_size)
         if not self._h:
-            raise PagedKVError(-1, "pkv_alloc_create")
+            raise PagedKVError(-1, "pkv_alloc_create_bs")
         self.num_blocks = num_blocks
         self.max_blocks_per_seq = max_blocks_per_seq
+        self.block_size = int(self._lib.pkv_alloc_block_size(self._h))
 
     def __del__(self):
         h = getattr(self, "_h", None)

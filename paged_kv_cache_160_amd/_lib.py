@@ -89,6 +89,23 @@ SIGNATURES = {
     "pkv_prefix_stats": (c_int, [c_void_p, ctypes.POINTER(PrefixStats)]),
 }
 
+# Block-size variants: the same arguments with block_size (int) inserted at
+# this position.
+_BS_INSERT = {
+    "kv_cache_append": 11,
+    "pkv_copy_blocks": 9,
+    "paged_attention_decode": 13,
+    "paged_attention_decode_append": 16,
+    "paged_attention_decode_append_partials": 16,
+    "paged_attention_merge_partials": 6,
+    "paged_attention_prefill": 15,
+}
+for _name, _pos in _BS_INSERT.items():
+    _res, _args = SIGNATURES[_name]
+    SIGNATURES[_name + "_bs"] = (_res, _args[:_pos] + [c_int] + _args[_pos:])
+SIGNATURES["pkv_alloc_create_bs"] = (c_void_p, [c_int, c_int, c_int])
+SIGNATURES["pkv_alloc_block_size"] = (c_int, [c_void_p])
+
 _lib = None
 
 

@@ -18,11 +18,12 @@ Rows = Union[torch.Tensor, Sequence[torch.Tensor]]
 
 
 class PagedKVCache:
-    """``num_layers`` pools of ``num_blocks`` 16-token blocks sharing one block
-    table per sequence (every layer stores a token at the same slot)."""
+    """``num_layers`` pools of ``num_blocks`` blocks of ``block_size`` tokens
+    (16 or 32) sharing one block table per sequence (every layer stores a
+    token at the same slot)."""
 
     def __init__(self, num_layers: int, num_blocks: int, num_kv_heads: int, head_dim: int,
-                 cache_dtype, max_blocks_per_seq: int, device="cuda"):
+                 cache_dtype, max_blocks_per_seq: int, device="cuda", block_size: int = BLOCK_SIZE):
         """``cache_dtype``: a format name of ``CACHE_FORMATS`` ("bf16",
         "fp8_e4m3", "fp8_e5m2", "int8_int4", ...) or a torch dtype (uint8
         and float8_e4m3fn mean fp8 e4m3)."""
@@ -31,6 +32,7 @@ class PagedKVCache:
         self.num_kv_heads = num_kv_heads
         self.head_dim = head_dim
         self.max_blocks_per_seq = max_blocks_per_seq
+        self.block_size = block_size
         self.device = torch.device(device)
         if not isinstance(cache_dtype, str):
             cache_dtype = {torch.float32: "f32", torch.float16: "f16", torch.bfloat16: "bf16",
@@ -41,18 +43,18 @@ class PagedKVCache:
         self.quantised = self.cache_code in (PKV_FP8_E4M3, PKV_FP8_E5M2, PKV_INT8_INT4)
         self.fp8 = self.quantised
         self.cache_dtype = k_dt
-        shape = (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim)
-        vshape = (num_blocks, num_kv_heads, BLOCK_SIZE, head_dim // v_per)
+        shape = (num_blocks, num_kv_heads, block_size, head_dim)
+        vshape = (num_blocks, num_kv_heads, block_size, head_dim // v_per)
         self.k = [torch.empty(shape, dtype=k_dt, device=self.device) for _ in range(num_layers)]
         self.v = [torch.empty(vshape, dtype=v_dt, device=self.device) for _ in range(num_layers)]
         if self.quantised:
-            sshape = (num_blocks, num_kv_heads, BLOCK_SIZE)
+            sshape = (num_blocks, num_kv_heads, block_size)
             self.k_scale = [torch.empty(sshape, dtype=torch.float32, device=self.device) for _ in range(num_layers)]
             self.v_scale = [torch.empty(sshape, dtype=torch.float32, device=self.device) for _ in range(num_layers)]
         else:
             self.k_scale = [None] * num_layers
             self.v_scale = [None] * num_layers
-        self.alloc = BlockAllocator(num_blocks, max_blocks_per_seq)
+        self.alloc = BlockAllocator(num_blocks, max_blocks_per_seq, block_size)
         self.cow_pairs_applied: List[tuple] = []
         self._ws: Optional[torch.Tensor] = None
 

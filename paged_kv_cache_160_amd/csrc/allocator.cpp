@@ -1,7 +1,7 @@
 // Host block allocator for the paged KV cache: free list, per-sequence block
 // tables, reference counts, fork and copy-on-write planning.
 //
-// Pages: blocks of 16 tokens are taken on demand when a sequence's current
+// Pages: blocks of 16 (or 32) tokens are taken on demand when a sequence's current
 // block is full ("KV Cache 和 vLLM" §3.1); finished sequences return their
 // blocks and later sequences reuse them wherever they lie ("KV Cache优化实战"
 // §4.2); sequences with a common prefix share physical blocks, and
@@ -16,7 +16,7 @@
 // §6.2-6.3): full blocks are indexed by their content - a hash chained from
 // the model key through every earlier block's tokens - and a new request
 // reuses the longest run of indexed blocks matching its prompt.  An index
-// entry is the exact pair (parent block, 16 token ids); the hash only picks
+// entry is the exact pair (parent block, the block's token ids); the hash only picks
 // the bucket and every candidate is compared in full, so a hash collision
 // costs a comparison, never a wrong match.  Because leaf-first eviction
 // never drops a block while an indexed child points at it, the pair names a
@@ -36,10 +36,8 @@
 
 namespace {
 
-constexpr int kBlock = PKV_BLOCK_SIZE;
+constexpr int kMaxBlock = 32;       // block sizes: 16 or 32 tokens
 constexpr int32_t kNoToken = 0;      // non-null stand-in for an empty token list
-
-inline int64_t blocks_for(int64_t len) { return (len + kBlock - 1) / kBlock; }
 
 struct Seq {
   std::vector<int32_t> table;
@@ -49,18 +47,18 @@ struct Seq {
   std::vector<int32_t> pending;      // tokens of the unfinished last block
 };
 
-using BlockTokens = std::array<int32_t, kBlock>;
+using BlockTokens = std::array<int32_t, kMaxBlock>;   // first bs entries used
 
 // 64-bit FNV-1a over the parent's hash (8 bytes, little-endian) and the
-// block's token ids (4 bytes each, little-endian).
-uint64_t chain_hash(uint64_t parent_hash, const int32_t* toks) {
+// block's bs token ids (4 bytes each, little-endian).
+uint64_t chain_hash(uint64_t parent_hash, const int32_t* toks, int bs) {
   uint64_t h = 0xcbf29ce484222325ull;
   auto mix = [&h](uint8_t byte) {
     h ^= byte;
     h *= 0x100000001b3ull;
   };
   for (int i = 0; i < 8; ++i) mix(static_cast<uint8_t>(parent_hash >> (8 * i)));
-  for (int t = 0; t < kBlock; ++t) {
+  for (int t = 0; t < bs; ++t) {
     uint32_t u = static_cast<uint32_t>(toks[t]);
     for (int i = 0; i < 4; ++i) mix(static_cast<uint8_t>(u >> (8 * i)));
   }
@@ -78,6 +76,7 @@ struct CacheEntry {
 
 struct PrefixCache {
   bool enabled = false;
+  int bs = PKV_BLOCK_SIZE;
   uint64_t model_key = 0;
   uint64_t mask = ~0ull;
   std::vector<CacheEntry> entry;                      // per physical block
@@ -89,14 +88,14 @@ struct PrefixCache {
   int64_t lookup_blocks = 0, hit_blocks = 0, evictions = 0;
 
   uint64_t hash_of(int32_t parent, const int32_t* toks) const {
-    return chain_hash(parent < 0 ? model_key : entry[parent].hash, toks);
+    return chain_hash(parent < 0 ? model_key : entry[parent].hash, toks, bs);
   }
   // The indexed block with this parent and these tokens, or -1.
   int32_t find(int32_t parent, const int32_t* toks, uint64_t h) const {
     auto range = index.equal_range(h & mask);
     for (auto it = range.first; it != range.second; ++it) {
       const CacheEntry& e = entry[it->second];
-      if (e.parent == parent && std::equal(toks, toks + kBlock, e.tokens.begin())) return it->second;
+      if (e.parent == parent && std::equal(toks, toks + bs, e.tokens.begin())) return it->second;
     }
     return -1;
   }
@@ -107,12 +106,15 @@ struct PrefixCache {
 struct pkv_alloc {
   int32_t num_blocks = 0;
   int32_t max_blocks_per_seq = 0;
+  int32_t bs = PKV_BLOCK_SIZE;       // tokens per block: 16 or 32
   std::vector<int32_t> free_stack;   // back() is handed out next
   std::vector<int32_t> ref;
   std::unordered_map<int64_t, Seq> seqs;
   std::vector<int64_t> seq_order;    // creation order, for deterministic stats walks
   int64_t cow_copies = 0;
   PrefixCache pc;
+
+  int64_t blocks_for(int64_t len) const { return (len + bs - 1) / bs; }
 
   // Blocks an append may take: free ones and, with prefix caching, the
   // evictable ones (indexed, no holder).
@@ -187,8 +189,8 @@ struct pkv_alloc {
     for (int64_t i = 0; i < n; ++i) {
       s.pending.push_back(toks[i]);
       int64_t p = first + i;
-      if (p % kBlock == kBlock - 1) {
-        index_block(s, p / kBlock);
+      if (p % bs == bs - 1) {
+        index_block(s, p / bs);
         s.pending.clear();
       }
     }
@@ -216,14 +218,14 @@ struct pkv_alloc {
 
   // Fresh blocks an append of n tokens needs, and whether it copies first.
   void plan(const Seq& s, int64_t n, bool* cow, int64_t* fresh) const {
-    *cow = n > 0 && (s.len % kBlock) != 0 && ref[s.table.back()] > 1;
+    *cow = n > 0 && (s.len % bs) != 0 && ref[s.table.back()] > 1;
     *fresh = blocks_for(s.len + n) - blocks_for(s.len);
   }
 
   // Apply a planned append; capacity was checked by the caller.
   void apply(Seq& s, int64_t n, int64_t* slots, int32_t* pair, int* n_cow) {
     *n_cow = 0;
-    if (n > 0 && (s.len % kBlock) != 0 && ref[s.table.back()] > 1) {
+    if (n > 0 && (s.len % bs) != 0 && ref[s.table.back()] > 1) {
       int32_t old_b = s.table.back();
       int32_t new_b = take();
       --ref[old_b];                    // another sequence still holds it
@@ -235,8 +237,8 @@ struct pkv_alloc {
     }
     for (int64_t i = 0; i < n; ++i) {
       int64_t p = s.len + i;
-      if (p % kBlock == 0) s.table.push_back(take());
-      slots[i] = static_cast<int64_t>(s.table[p / kBlock]) * kBlock + p % kBlock;
+      if (p % bs == 0) s.table.push_back(take());
+      slots[i] = static_cast<int64_t>(s.table[p / bs]) * bs + p % bs;
     }
     s.len += n;
   }
@@ -244,10 +246,12 @@ struct pkv_alloc {
 
 extern "C" {
 
-pkv_alloc* pkv_alloc_create(int num_blocks, int max_blocks_per_seq) {
-  if (num_blocks <= 0 || max_blocks_per_seq <= 0) return nullptr;
+pkv_alloc* pkv_alloc_create_bs(int num_blocks, int max_blocks_per_seq, int block_size) {
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0 || (block_size != PKV_BLOCK_SIZE && block_size != PKV_BLOCK_SIZE_LARGE)) return nullptr;
   pkv_alloc* a = new (std::nothrow) pkv_alloc();
   if (!a) return nullptr;
+  a->bs = block_size;
+  a->pc.bs = block_size;
   a->num_blocks = num_blocks;
   a->max_blocks_per_seq = max_blocks_per_seq;
   a->ref.assign(num_blocks, 0);
@@ -255,6 +259,12 @@ pkv_alloc* pkv_alloc_create(int num_blocks, int max_blocks_per_seq) {
   for (int i = 0; i < num_blocks; ++i) a->free_stack[i] = num_blocks - 1 - i;
   return a;
 }
+
+pkv_alloc* pkv_alloc_create(int num_blocks, int max_blocks_per_seq) {
+  return pkv_alloc_create_bs(num_blocks, max_blocks_per_seq, PKV_BLOCK_SIZE);
+}
+
+int pkv_alloc_block_size(const pkv_alloc* a) { return a ? a->bs : PKV_ERR_INVALID_ARG; }
 
 void pkv_alloc_destroy(pkv_alloc* a) { delete a; }
 
@@ -354,9 +364,9 @@ int batch_impl(pkv_alloc* a, const int64_t* seq_ids, const int32_t* toks, int n,
     if (it->second.swapped) return PKV_ERR_INVALID_ARG;
     if (seen[seq_ids[i]]++) return PKV_ERR_INVALID_ARG;
     const Seq& s = it->second;
-    int64_t fresh = blocks_for(s.len + 1) - blocks_for(s.len);
+    int64_t fresh = a->blocks_for(s.len + 1) - a->blocks_for(s.len);
     bool cow = false;
-    if (s.len % kBlock != 0) {
+    if (s.len % a->bs != 0) {
       int32_t last = s.table.back();
       cow = a->ref[last] - dropped[last] > 1;
       if (cow) ++dropped[last];
@@ -422,20 +432,21 @@ int pkv_seq_create_cached(pkv_alloc* a, int64_t seq_id, const int32_t* tokens, i
     return PKV_ERR_INVALID_ARG;
   if (a->seqs.count(seq_id)) return PKV_ERR_INVALID_ARG;
   PrefixCache& pc = a->pc;
-  // at most (n - 1) / 16 blocks, so the last prompt token is always computed
-  int64_t most = std::min<int64_t>(n_tokens > 0 ? (n_tokens - 1) / kBlock : 0, a->max_blocks_per_seq);
+  // at most (n - 1) / bs blocks, so the last prompt token is always computed
+  const int bs = a->bs;
+  int64_t most = std::min<int64_t>(n_tokens > 0 ? (n_tokens - 1) / bs : 0, a->max_blocks_per_seq);
   Seq s;
   s.tracked = true;
   int32_t parent = -1;
   for (int64_t i = 0; i < most; ++i) {
-    const int32_t* t = tokens + i * kBlock;
+    const int32_t* t = tokens + i * bs;
     int32_t b = pc.find(parent, t, pc.hash_of(parent, t));
     if (b < 0) break;
     s.table.push_back(b);
     parent = b;
   }
   for (int32_t b : s.table) a->hold(b);
-  s.len = static_cast<int64_t>(s.table.size()) * kBlock;
+  s.len = static_cast<int64_t>(s.table.size()) * bs;
   pc.lookup_blocks += most;
   pc.hit_blocks += static_cast<int64_t>(s.table.size());
   *n_cached_out = static_cast<int>(s.len);
@@ -484,7 +495,7 @@ int pkv_alloc_stats(pkv_alloc* a, pkv_alloc_stats_t* out) {
     if (s.swapped) continue;
     cached += s.len;
     for (size_t i = 0; i < s.table.size(); ++i) {
-      int64_t f = std::min<int64_t>(kBlock, s.len - static_cast<int64_t>(i) * kBlock);
+      int64_t f = std::min<int64_t>(a->bs, s.len - static_cast<int64_t>(i) * a->bs);
       filled[s.table[i]] = std::max<int32_t>(filled[s.table[i]], static_cast<int32_t>(f));
     }
   }
@@ -501,7 +512,7 @@ int pkv_alloc_stats(pkv_alloc* a, pkv_alloc_stats_t* out) {
   out->cow_copies = a->cow_copies;
   out->cached_tokens = cached;
   out->stored_tokens = stored;
-  out->utilisation = used ? static_cast<double>(stored) / (static_cast<double>(kBlock) * used) : 0.0;
+  out->utilisation = used ? static_cast<double>(stored) / (static_cast<double>(a->bs) * used) : 0.0;
   return PKV_OK;
 }
 
@@ -530,7 +541,7 @@ int pkv_seq_swap_in(pkv_alloc* a, int64_t seq_id, int32_t* blocks_out, int* n_ou
   if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
   Seq& s = it->second;
   if (!s.swapped) return PKV_ERR_INVALID_ARG;
-  const int64_t need = blocks_for(s.len);
+  const int64_t need = a->blocks_for(s.len);
   if (need > 0 && !blocks_out) return PKV_ERR_INVALID_ARG;
   if (need > a->available()) return PKV_ERR_NO_FREE_BLOCKS;
   for (int64_t i = 0; i < need; ++i) s.table.push_back(a->take());

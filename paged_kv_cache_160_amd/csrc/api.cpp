@@ -10,7 +10,15 @@
 
 namespace {
 
-constexpr int kBlock = PKV_BLOCK_SIZE;
+constexpr int kTile = 16;     // partitions are whole 16-token tiles
+
+bool block_size_ok(int bs) { return bs == PKV_BLOCK_SIZE || bs == PKV_BLOCK_SIZE_LARGE; }
+
+// Kernels index 16-row tiles with int32: (num_blocks * num_kv_heads) tiles
+// per 16 tokens of block must fit.
+bool tiles_fit(int num_blocks, int num_kv_heads, int block_size) {
+  return static_cast<int64_t>(num_blocks) * num_kv_heads * (block_size / kTile) < (static_cast<int64_t>(1) << 31);
+}
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -34,7 +42,7 @@ int resolve_partitions(int num_seqs, int num_kv_heads, int max_context_len, int 
                        int* ps_out, int* np_out) {
   int ps = partition_size;
   if (ps == 0) ps = pkv::choose_partition_size(num_seqs, num_kv_heads, max_context_len);
-  if (ps <= 0 || ps % kBlock != 0 || ps > PKV_MAX_PARTITION_TOKENS) return PKV_ERR_INVALID_ARG;
+  if (ps <= 0 || ps % kTile != 0 || ps > PKV_MAX_PARTITION_TOKENS) return PKV_ERR_INVALID_ARG;
   int64_t np = (static_cast<int64_t>(max_context_len) + ps - 1) / ps;
   if (np < 1) np = 1;
   if (np > (1 << 20)) return PKV_ERR_UNSUPPORTED;
@@ -87,12 +95,13 @@ const char* pkv_strerror(int code) {
   }
 }
 
-int kv_cache_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
-                    float* k_scale, float* v_scale, const int64_t* slot_mapping, int num_tokens,
-                    int num_kv_heads, int head_dim, int num_blocks, pkv_dtype src_dtype,
-                    pkv_dtype cache_dtype, void* stream) {
+int kv_cache_append_bs(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                       float* k_scale, float* v_scale, const int64_t* slot_mapping, int num_tokens,
+                       int num_kv_heads, int head_dim, int num_blocks, int block_size, pkv_dtype src_dtype,
+                       pkv_dtype cache_dtype, void* stream) {
   if (!valid_dtype(src_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
-  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0) return PKV_ERR_INVALID_ARG;
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0 || !block_size_ok(block_size))
+    return PKV_ERR_INVALID_ARG;
   if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
   if (!source_dtype(src_dtype)) return PKV_ERR_UNSUPPORTED;
   if (!quantised(cache_dtype) && src_dtype != cache_dtype) return PKV_ERR_UNSUPPORTED;
@@ -104,14 +113,23 @@ int kv_cache_append(const void* k_new, const void* v_new, void* k_pool, void* v_
   if (static_cast<int64_t>(num_tokens) * num_kv_heads > (static_cast<int64_t>(1) << 31))
     return PKV_ERR_UNSUPPORTED;
   return pkv::launch_append(k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, num_tokens,
-                            num_kv_heads, head_dim, num_blocks, src_dtype, cache_dtype,
+                            num_kv_heads, head_dim, num_blocks, block_size, src_dtype, cache_dtype,
                             static_cast<hipStream_t>(stream));
 }
 
-int pkv_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
-                    const int32_t* pairs, int n_pairs, int num_kv_heads, int head_dim,
-                    int num_blocks, pkv_dtype cache_dtype, void* stream) {
-  if (!valid_dtype(cache_dtype) || n_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0)
+int kv_cache_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                    float* k_scale, float* v_scale, const int64_t* slot_mapping, int num_tokens,
+                    int num_kv_heads, int head_dim, int num_blocks, pkv_dtype src_dtype,
+                    pkv_dtype cache_dtype, void* stream) {
+  return kv_cache_append_bs(k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, num_tokens,
+                            num_kv_heads, head_dim, num_blocks, PKV_BLOCK_SIZE, src_dtype, cache_dtype, stream);
+}
+
+int pkv_copy_blocks_bs(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                       const int32_t* pairs, int n_pairs, int num_kv_heads, int head_dim,
+                       int num_blocks, int block_size, pkv_dtype cache_dtype, void* stream) {
+  if (!valid_dtype(cache_dtype) || n_pairs < 0 || num_kv_heads <= 0 || num_blocks <= 0 ||
+      !block_size_ok(block_size))
     return PKV_ERR_INVALID_ARG;
   if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
   if (n_pairs == 0) return PKV_OK;
@@ -120,7 +138,14 @@ int pkv_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
   if (!aligned16(k_pool) || !aligned16(v_pool)) return PKV_ERR_INVALID_ARG;
   if (n_pairs > 65535 || num_kv_heads > 65535) return PKV_ERR_UNSUPPORTED;
   return pkv::launch_copy_blocks(k_pool, v_pool, k_scale, v_scale, pairs, n_pairs, num_kv_heads,
-                                 head_dim, num_blocks, cache_dtype, static_cast<hipStream_t>(stream));
+                                 head_dim, num_blocks, block_size, cache_dtype, static_cast<hipStream_t>(stream));
+}
+
+int pkv_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                    const int32_t* pairs, int n_pairs, int num_kv_heads, int head_dim,
+                    int num_blocks, pkv_dtype cache_dtype, void* stream) {
+  return pkv_copy_blocks_bs(k_pool, v_pool, k_scale, v_scale, pairs, n_pairs, num_kv_heads, head_dim,
+                            num_blocks, PKV_BLOCK_SIZE, cache_dtype, stream);
 }
 
 int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
@@ -153,23 +178,24 @@ namespace {
 int decode_impl(void* out, const void* q, const void* k_new, const void* v_new, const void* k_pool,
                 const void* v_pool, const float* k_scale, const float* v_scale, const int64_t* slot_mapping,
                 const int32_t* block_tables, const int32_t* context_lens, int num_seqs, int num_q_heads,
-                int num_kv_heads, int head_dim, int num_blocks, int max_blocks_per_seq, int max_context_len,
-                float scale, pkv_dtype q_dtype, pkv_dtype src_dtype, pkv_dtype cache_dtype, int partition_size,
-                void* workspace, size_t workspace_bytes, void* stream, int stages) {
+                int num_kv_heads, int head_dim, int num_blocks, int block_size, int max_blocks_per_seq,
+                int max_context_len, float scale, pkv_dtype q_dtype, pkv_dtype src_dtype, pkv_dtype cache_dtype,
+                int partition_size, void* workspace, size_t workspace_bytes, void* stream, int stages) {
   if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype) || !valid_dtype(src_dtype)) return PKV_ERR_INVALID_ARG;
   if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len))
     return PKV_ERR_INVALID_ARG;
-  if (num_blocks <= 0 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBlock)
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0 || !block_size_ok(block_size)) return PKV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
     return PKV_ERR_INVALID_ARG;
   if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
   if (!decode_pair_ok(q_dtype, cache_dtype)) return PKV_ERR_UNSUPPORTED;
+  if (!tiles_fit(num_blocks, num_kv_heads, block_size)) return PKV_ERR_UNSUPPORTED;
   if (slot_mapping) {
     if (!source_dtype(src_dtype)) return PKV_ERR_UNSUPPORTED;
     if (!quantised(cache_dtype) && src_dtype != cache_dtype) return PKV_ERR_UNSUPPORTED;
   }
   if (num_q_heads / num_kv_heads > 16) return PKV_ERR_UNSUPPORTED;
-  if (partition_size < 0 || partition_size % kBlock != 0 || partition_size > PKV_MAX_PARTITION_TOKENS)
+  if (partition_size < 0 || partition_size % kTile != 0 || partition_size > PKV_MAX_PARTITION_TOKENS)
     return PKV_ERR_INVALID_ARG;
   if (num_seqs == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens) return PKV_ERR_INVALID_ARG;
@@ -201,6 +227,7 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new, 
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
   a.num_blocks = num_blocks;
+  a.block_size = block_size;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_context_len = max_context_len;
   a.scale = scale;
@@ -225,6 +252,19 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new, 
 
 extern "C" {
 
+int paged_attention_decode_bs(void* out, const void* q, const void* k_pool, const void* v_pool,
+                              const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                              const int32_t* context_lens, int num_seqs, int num_q_heads,
+                              int num_kv_heads, int head_dim, int num_blocks, int block_size,
+                              int max_blocks_per_seq, int max_context_len, float scale, pkv_dtype q_dtype,
+                              pkv_dtype cache_dtype, int partition_size, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return decode_impl(out, q, nullptr, nullptr, k_pool, v_pool, k_scale, v_scale, nullptr, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                     max_blocks_per_seq, max_context_len, scale, q_dtype, q_dtype, cache_dtype,
+                     partition_size, workspace, workspace_bytes, stream, pkv::kStageBoth);
+}
+
 int paged_attention_decode(void* out, const void* q, const void* k_pool, const void* v_pool,
                            const float* k_scale, const float* v_scale, const int32_t* block_tables,
                            const int32_t* context_lens, int num_seqs, int num_q_heads,
@@ -232,9 +272,24 @@ int paged_attention_decode(void* out, const void* q, const void* k_pool, const v
                            int max_context_len, float scale, pkv_dtype q_dtype,
                            pkv_dtype cache_dtype, int partition_size, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  return decode_impl(out, q, nullptr, nullptr, k_pool, v_pool, k_scale, v_scale, nullptr, block_tables,
-                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
-                     max_blocks_per_seq, max_context_len, scale, q_dtype, q_dtype, cache_dtype,
+  return paged_attention_decode_bs(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens,
+                                   num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, PKV_BLOCK_SIZE,
+                                   max_blocks_per_seq, max_context_len, scale, q_dtype, cache_dtype,
+                                   partition_size, workspace, workspace_bytes, stream);
+}
+
+int paged_attention_decode_append_bs(void* out, const void* q, const void* k_new, const void* v_new,
+                                     void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                     const int64_t* slot_mapping, const int32_t* block_tables,
+                                     const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                     int num_kv_heads, int head_dim, int num_blocks, int block_size,
+                                     int max_blocks_per_seq, int max_context_len, float scale, pkv_dtype q_dtype,
+                                     pkv_dtype src_dtype, pkv_dtype cache_dtype, int partition_size,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!slot_mapping) return PKV_ERR_INVALID_ARG;
+  return decode_impl(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                     max_blocks_per_seq, max_context_len, scale, q_dtype, src_dtype, cache_dtype,
                      partition_size, workspace, workspace_bytes, stream, pkv::kStageBoth);
 }
 
@@ -246,11 +301,26 @@ int paged_attention_decode_append(void* out, const void* q, const void* k_new, c
                                   int max_context_len, float scale, pkv_dtype q_dtype, pkv_dtype src_dtype,
                                   pkv_dtype cache_dtype, int partition_size, void* workspace,
                                   size_t workspace_bytes, void* stream) {
-  if (!slot_mapping) return PKV_ERR_INVALID_ARG;
+  return paged_attention_decode_append_bs(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping,
+                                          block_tables, context_lens, num_seqs, num_q_heads, num_kv_heads,
+                                          head_dim, num_blocks, PKV_BLOCK_SIZE, max_blocks_per_seq,
+                                          max_context_len, scale, q_dtype, src_dtype, cache_dtype, partition_size,
+                                          workspace, workspace_bytes, stream);
+}
+
+int paged_attention_decode_append_partials_bs(void* out, const void* q, const void* k_new, const void* v_new,
+                                              void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                              const int64_t* slot_mapping, const int32_t* block_tables,
+                                              const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                              int num_kv_heads, int head_dim, int num_blocks, int block_size,
+                                              int max_blocks_per_seq, int max_context_len, float scale,
+                                              pkv_dtype q_dtype, pkv_dtype src_dtype, pkv_dtype cache_dtype,
+                                              int partition_size, void* workspace, size_t workspace_bytes,
+                                              void* stream) {
   return decode_impl(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, block_tables,
-                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
                      max_blocks_per_seq, max_context_len, scale, q_dtype, src_dtype, cache_dtype,
-                     partition_size, workspace, workspace_bytes, stream, pkv::kStageBoth);
+                     partition_size, workspace, workspace_bytes, stream, pkv::kStageAttend);
 }
 
 int paged_attention_decode_append_partials(void* out, const void* q, const void* k_new, const void* v_new,
@@ -262,24 +332,24 @@ int paged_attention_decode_append_partials(void* out, const void* q, const void*
                                            pkv_dtype q_dtype, pkv_dtype src_dtype, pkv_dtype cache_dtype,
                                            int partition_size, void* workspace, size_t workspace_bytes,
                                            void* stream) {
-  return decode_impl(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, block_tables,
-                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks,
-                     max_blocks_per_seq, max_context_len, scale, q_dtype, src_dtype, cache_dtype,
-                     partition_size, workspace, workspace_bytes, stream, pkv::kStageAttend);
+  return paged_attention_decode_append_partials_bs(
+      out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, block_tables, context_lens, num_seqs,
+      num_q_heads, num_kv_heads, head_dim, num_blocks, PKV_BLOCK_SIZE, max_blocks_per_seq, max_context_len, scale,
+      q_dtype, src_dtype, cache_dtype, partition_size, workspace, workspace_bytes, stream);
 }
 
-int paged_attention_merge_partials(void* out, const int32_t* context_lens, int num_seqs, int num_q_heads,
-                                   int num_kv_heads, int head_dim, int max_blocks_per_seq, int max_context_len,
-                                   pkv_dtype q_dtype, int partition_size, void* workspace,
-                                   size_t workspace_bytes, void* stream) {
+int paged_attention_merge_partials_bs(void* out, const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                      int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
+                                      int max_context_len, pkv_dtype q_dtype, int partition_size, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
   if (!valid_dtype(q_dtype) || !source_dtype(q_dtype)) return PKV_ERR_INVALID_ARG;
   if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len))
     return PKV_ERR_INVALID_ARG;
-  if (max_blocks_per_seq <= 0 ||
-      static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBlock)
+  if (max_blocks_per_seq <= 0 || !block_size_ok(block_size) ||
+      static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
     return PKV_ERR_INVALID_ARG;
   if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
-  if (partition_size < 0 || partition_size % kBlock != 0 || partition_size > PKV_MAX_PARTITION_TOKENS)
+  if (partition_size < 0 || partition_size % kTile != 0 || partition_size > PKV_MAX_PARTITION_TOKENS)
     return PKV_ERR_INVALID_ARG;
   int ps, np;
   int rc = resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, &ps, &np);
@@ -295,6 +365,7 @@ int paged_attention_merge_partials(void* out, const int32_t* context_lens, int n
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
+  a.block_size = block_size;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_context_len = max_context_len;
   a.q_dtype = q_dtype;
@@ -310,24 +381,35 @@ int paged_attention_merge_partials(void* out, const int32_t* context_lens, int n
   return pkv::launch_decode(a, static_cast<hipStream_t>(stream), pkv::kStageMerge);
 }
 
-int paged_attention_prefill(void* out, const void* q, const void* k_pool, const void* v_pool,
-                            const float* k_scale, const float* v_scale, const int32_t* block_tables,
-                            const int32_t* context_lens, const int32_t* query_start, int num_seqs, int num_tokens,
-                            int num_q_heads, int num_kv_heads, int head_dim, int num_blocks, int max_blocks_per_seq,
-                            int max_context_len, int max_query_len, float scale, pkv_dtype q_dtype,
-                            pkv_dtype cache_dtype, void* stream) {
+int paged_attention_merge_partials(void* out, const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                   int num_kv_heads, int head_dim, int max_blocks_per_seq, int max_context_len,
+                                   pkv_dtype q_dtype, int partition_size, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  return paged_attention_merge_partials_bs(out, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                           PKV_BLOCK_SIZE, max_blocks_per_seq, max_context_len, q_dtype,
+                                           partition_size, workspace, workspace_bytes, stream);
+}
+
+int paged_attention_prefill_bs(void* out, const void* q, const void* k_pool, const void* v_pool,
+                               const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                               const int32_t* context_lens, const int32_t* query_start, int num_seqs,
+                               int num_tokens, int num_q_heads, int num_kv_heads, int head_dim, int num_blocks,
+                               int block_size, int max_blocks_per_seq, int max_context_len, int max_query_len,
+                               float scale, pkv_dtype q_dtype, pkv_dtype cache_dtype, void* stream) {
   if (!valid_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
   if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len))
     return PKV_ERR_INVALID_ARG;
-  if (num_tokens < 0 || max_query_len < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0)
+  if (num_tokens < 0 || max_query_len < 0 || num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+      !block_size_ok(block_size))
     return PKV_ERR_INVALID_ARG;
-  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * kBlock)
+  if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
     return PKV_ERR_INVALID_ARG;
   if (max_query_len > max_context_len || max_query_len > num_tokens) return PKV_ERR_INVALID_ARG;
   if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
   if (q_dtype == PKV_F32 || !decode_pair_ok(q_dtype, cache_dtype)) return PKV_ERR_UNSUPPORTED;
   if (cache_dtype == PKV_FP8_E5M2 || cache_dtype == PKV_INT8_INT4) return PKV_ERR_UNSUPPORTED;
   if (max_context_len > PKV_MAX_PREFILL_CONTEXT) return PKV_ERR_UNSUPPORTED;
+  if (!tiles_fit(num_blocks, num_kv_heads, block_size)) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_tokens == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens || !query_start)
     return PKV_ERR_INVALID_ARG;
@@ -350,6 +432,7 @@ int paged_attention_prefill(void* out, const void* q, const void* k_pool, const 
   a.num_kv_heads = num_kv_heads;
   a.head_dim = head_dim;
   a.num_blocks = num_blocks;
+  a.block_size = block_size;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_context_len = max_context_len;
   a.max_query_len = max_query_len;
@@ -357,6 +440,18 @@ int paged_attention_prefill(void* out, const void* q, const void* k_pool, const 
   a.q_dtype = q_dtype;
   a.cache_dtype = cache_dtype;
   return pkv::launch_prefill(a, static_cast<hipStream_t>(stream));
+}
+
+int paged_attention_prefill(void* out, const void* q, const void* k_pool, const void* v_pool,
+                            const float* k_scale, const float* v_scale, const int32_t* block_tables,
+                            const int32_t* context_lens, const int32_t* query_start, int num_seqs, int num_tokens,
+                            int num_q_heads, int num_kv_heads, int head_dim, int num_blocks, int max_blocks_per_seq,
+                            int max_context_len, int max_query_len, float scale, pkv_dtype q_dtype,
+                            pkv_dtype cache_dtype, void* stream) {
+  return paged_attention_prefill_bs(out, q, k_pool, v_pool, k_scale, v_scale, block_tables, context_lens,
+                                    query_start, num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim,
+                                    num_blocks, PKV_BLOCK_SIZE, max_blocks_per_seq, max_context_len, max_query_len,
+                                    scale, q_dtype, cache_dtype, stream);
 }
 
 }  // extern "C"

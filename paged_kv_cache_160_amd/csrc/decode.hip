@@ -59,7 +59,7 @@ namespace pkv {
 constexpr int kWaves = PKV_DECODE_WAVES;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxGroup = 16;
-constexpr int kMaxPartitionBlocks = PKV_MAX_PARTITION_TOKENS / kBlockTokens;
+constexpr int kMaxPartitionBlocks = PKV_MAX_PARTITION_TOKENS / kTileTokens;
 constexpr float kLog2e = 1.4426950408889634f;
 
 // ---- raw register loads -------------------------------------------------------
@@ -153,8 +153,8 @@ struct Geo {
   static constexpr int DC = D / 16;                     // V columns per lane = P*V tiles
   static constexpr int vLaneBytes = DC * VT::bits / 8;  // one V row's share per lane (2..32 bytes)
   static constexpr int vWords = vLaneBytes < 4 ? 1 : vLaneBytes / 4;
-  static constexpr int kTileBytes = kBlockTokens * kRowBytes;
-  static constexpr int vTileBytes = kBlockTokens * vRowBytes;
+  static constexpr int kTileBytes = kTileTokens * kRowBytes;
+  static constexpr int vTileBytes = kTileTokens * vRowBytes;
 };
 
 template <typename QT, typename KT, typename VT, int D>
@@ -340,7 +340,7 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
   const int j = lane >> 4;
 
   int L = a.context_lens[b];
-  L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * kBlockTokens)));
+  L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * a.block_size)));
   const int PS = a.partition_size;
   const int np_b = (L + PS - 1) / PS;         // non-empty partitions of this sequence
   const int tok0 = part * PS;
@@ -355,9 +355,10 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
   }
   if (part >= np_b) return;
   const int tok1 = min(L, tok0 + PS);
-  const int blk0 = tok0 / kBlockTokens;
-  const int nblk = (tok1 - tok0 + kBlockTokens - 1) / kBlockTokens;
-  const int32_t* table = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq + blk0;
+  const int blk0 = tok0 / kTileTokens;       // first 16-token unit of the partition
+  const int nblk = (tok1 - tok0 + kTileTokens - 1) / kTileTokens;
+  const int32_t* table = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq;
+  const int rs = block_shift(a.block_size);
 
   // Q^T operand: lane (head column c, k-group j) holds q[head c][j*D/4 ...).
   Words<G::qWords> qop;
@@ -384,8 +385,8 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
   // visible to every wave of the workgroup.
   if (a.slot_mapping != nullptr && part == (L - 1) / PS && wave < 2) {
     const int64_t slot = a.slot_mapping[b];
-    if (slot >= 0 && slot < static_cast<int64_t>(a.num_blocks) * kBlockTokens) {
-      const int64_t dst_row = ((slot / kBlockTokens) * a.num_kv_heads + g) * kBlockTokens + slot % kBlockTokens;
+    if (slot >= 0 && slot < static_cast<int64_t>(a.num_blocks) * a.block_size) {
+      const int64_t dst_row = slot_row(slot, a.block_size, a.num_kv_heads, g);
       const int64_t src_row = static_cast<int64_t>(b) * a.num_kv_heads + g;
       auto write = [&](auto tag, const void* src, const void* pool_c, const float* scales_c) {
         using T = decltype(tag);
@@ -405,27 +406,34 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
     }
   }
 
-  // The partition's physical block ids, staged in LDS once: a per-block
-  // table read from global memory in front of the K/V loads would make the
-  // wave wait for every load already in flight (vmcnt is in order), while
-  // LDS reads are counted separately.
-  for (int i = tid; i < nblk; i += kThreads) sm_ids[i] = table[i];
+  // The partition's tiles, staged in LDS once: a per-block table read from
+  // global memory in front of the K/V loads would make the wave wait for
+  // every load already in flight (vmcnt is in order), while LDS reads are
+  // counted separately.  Unit u's entry is its tile index at KV head 0,
+  // ((phys * Hkv) << rs) + (u & (2^rs - 1)), or -1 when the table names a
+  // block outside the pool.
+  for (int i = tid; i < nblk; i += kThreads) {
+    const int u = blk0 + i;
+    const int phys = table[u >> rs];
+    sm_ids[i] = (phys >= 0 && phys < a.num_blocks) ? ((phys * a.num_kv_heads) << rs) + (u & ((1 << rs) - 1)) : -1;
+  }
+  const int g_tile = g << rs;
   __syncthreads();
 
-  // Load one block's K/V (and scales) for this lane.  Blocks whose physical
-  // id lies outside the pool are read from block 0 and fully masked.
+  // Load one tile's K/V (and scales) for this lane.  Tiles of blocks outside
+  // the pool are read from tile 0 and fully masked.
   auto load_block = [&](BlockRegs<QT, KT, VT, D>& r, int i, bool& ok) {
-    int phys = __builtin_amdgcn_readfirstlane(sm_ids[i]);
-    ok = phys >= 0 && phys < a.num_blocks;
-    if (!ok) phys = 0;
-    const int64_t tile = static_cast<int64_t>(phys) * a.num_kv_heads + g;
+    int t0 = __builtin_amdgcn_readfirstlane(sm_ids[i]);
+    ok = t0 >= 0;
+    if (!ok) t0 = -g_tile;
+    const int64_t tile = static_cast<int64_t>(t0) + g_tile;
     const uint8_t* kt = kbase + tile * G::kTileBytes;
     const uint8_t* vt = vbase + tile * G::vTileBytes;
     load_words<G::kWords, PKV_DECODE_NT>(r.k, kt + k_lane);
 #pragma unroll
     for (int e = 0; e < 4; ++e) load_vrow<G::vLaneBytes>(r.v[e], vt + v_lane + e * G::vRowBytes);
-    if constexpr (kQK) r.ks = *reinterpret_cast<const float4*>(a.k_scale + tile * kBlockTokens + 4 * j);
-    if constexpr (kQV) r.vs = *reinterpret_cast<const float4*>(a.v_scale + tile * kBlockTokens + 4 * j);
+    if constexpr (kQK) r.ks = *reinterpret_cast<const float4*>(a.k_scale + tile * kTileTokens + 4 * j);
+    if constexpr (kQV) r.vs = *reinterpret_cast<const float4*>(a.v_scale + tile * kTileTokens + 4 * j);
   };
 
   float m = kNegInf;          // running max of head column c (log2 units)
@@ -435,7 +443,7 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
   for (int nt = 0; nt < G::DC; ++nt) o[nt] = {0.f, 0.f, 0.f, 0.f};
 
   auto compute_block = [&](BlockRegs<QT, KT, VT, D>& r, int i, bool ok) {
-    const int base = tok0 + i * kBlockTokens;   // logical position of the block's token 0
+    const int base = tok0 + i * kTileTokens;   // logical position of the block's token 0
     float4_t s = qk_tile<QT, KT, D>(r.k, qop);
     float sc[4] = {s[0], s[1], s[2], s[3]};
     float ksc[4] = {1.f, 1.f, 1.f, 1.f};
@@ -447,7 +455,7 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
       vsc[0] = r.vs.x; vsc[1] = r.vs.y; vsc[2] = r.vs.z; vsc[3] = r.vs.w;
     }
     bool valid[4];
-    const bool partial = !ok || base + kBlockTokens > tok1;
+    const bool partial = !ok || base + kTileTokens > tok1;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       valid[t] = ok && (base + 4 * j + t < tok1);
@@ -616,7 +624,7 @@ __global__ void __launch_bounds__(D) partition_merge_kernel(DecodeArgs a) {
   const int d = threadIdx.x;
   const int P = a.num_partitions;
   int L = a.context_lens[b];
-  L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * kBlockTokens)));
+  L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * a.block_size)));
   const int np = (L + a.partition_size - 1) / a.partition_size;
   if (np <= 1) return;
   const float* ml = a.part_ml + static_cast<int64_t>(row) * P * 2;
@@ -667,8 +675,8 @@ int choose_partition_size(int num_seqs, int num_kv_heads, int max_context_len) {
   // allows.
   constexpr int64_t kCUs = 256;
   const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads;
-  const int64_t seq_blocks = (static_cast<int64_t>(max_context_len) + kBlockTokens - 1) / kBlockTokens;
-  if (seq_blocks <= 0 || units <= 0) return kBlockTokens;
+  const int64_t seq_blocks = (static_cast<int64_t>(max_context_len) + kTileTokens - 1) / kTileTokens;
+  if (seq_blocks <= 0 || units <= 0) return kTileTokens;
   const int64_t np_min = (seq_blocks + kMaxPartitionBlocks - 1) / kMaxPartitionBlocks;
   int64_t np_max = seq_blocks / (4 * kWaves);
   if (np_max < np_min) np_max = np_min;
@@ -683,7 +691,7 @@ int choose_partition_size(int num_seqs, int num_kv_heads, int max_context_len) {
   }
   if (np < 1) np = 1;
   const int64_t blocks = (seq_blocks + np - 1) / np;
-  return static_cast<int>(blocks * kBlockTokens);
+  return static_cast<int>(blocks * kTileTokens);
 }
 
 template <typename QT, typename KT, typename VT, int D>

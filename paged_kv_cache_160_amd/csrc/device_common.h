@@ -10,8 +10,22 @@
 
 namespace pkv {
 
-constexpr int kBlockTokens = PKV_BLOCK_SIZE;
+// Kernels walk the pool in tiles of 16 token rows of one (block, KV head): a
+// 16-token block is one tile per head, a 32-token block two consecutive ones.
+// Tile index of a sequence's 16-token unit u (tokens 16u .. 16u+15) at KV head
+// g, with rs = log2(block_size / 16) and phys the block holding the unit:
+//   ((phys * num_kv_heads + g) << rs) + (u & ((1 << rs) - 1)),
+// and the tile's rows start at row tile * 16 of the pool (scales likewise).
+constexpr int kTileTokens = 16;
 constexpr int kWave = 64;
+
+// log2(block_size / 16): 0 for 16-token blocks, 1 for 32-token blocks.
+__host__ __device__ inline int block_shift(int block_size) { return block_size == 32 ? 1 : 0; }
+
+// Pool row of slot = phys * block_size + offset at KV head g.
+__host__ __device__ inline int64_t slot_row(int64_t slot, int block_size, int num_kv_heads, int g) {
+  return ((slot / block_size) * num_kv_heads + g) * block_size + slot % block_size;
+}
 
 // Storage tags.  Each names the element type a pool or a query holds.
 // Quantised tags (codes plus one float32 scale per (token, head) row) carry

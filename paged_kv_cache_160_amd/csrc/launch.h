@@ -15,12 +15,12 @@ inline int check_launch() {
 
 int launch_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
                   float* k_scale, float* v_scale, const int64_t* slot_mapping, int num_tokens,
-                  int num_kv_heads, int head_dim, int num_blocks, pkv_dtype src_dtype,
+                  int num_kv_heads, int head_dim, int num_blocks, int block_size, pkv_dtype src_dtype,
                   pkv_dtype cache_dtype, hipStream_t stream);
 
 int launch_copy_blocks(void* k_pool, void* v_pool, float* k_scale, float* v_scale,
                        const int32_t* pairs, int n_pairs, int num_kv_heads, int head_dim,
-                       int num_blocks, pkv_dtype cache_dtype, hipStream_t stream);
+                       int num_blocks, int block_size, pkv_dtype cache_dtype, hipStream_t stream);
 
 int launch_swap_blocks(void* staging, void* pool, const int32_t* blocks, int n_blocks, int64_t block_bytes,
                        int num_blocks, bool to_staging, hipStream_t stream);
@@ -36,6 +36,7 @@ struct DecodeArgs {
   const int32_t* context_lens;
   int num_seqs, num_q_heads, num_kv_heads, head_dim;
   int num_blocks, max_blocks_per_seq, max_context_len;
+  int block_size;          // tokens per block: 16 or 32
   float scale;
   pkv_dtype q_dtype, cache_dtype;
   int partition_size;      // tokens, multiple of 16 (resolved, never 0)
@@ -68,6 +69,7 @@ struct PrefillArgs {
   const int32_t* query_start;  // [num_seqs + 1]: chunk b = q rows query_start[b] .. query_start[b+1]-1
   int num_seqs, num_tokens, num_q_heads, num_kv_heads, head_dim;
   int num_blocks, max_blocks_per_seq, max_context_len, max_query_len;
+  int block_size;              // tokens per block: 16 or 32
   float scale;
   pkv_dtype q_dtype, cache_dtype;
   int tiles_per_seq;           // set by the launcher

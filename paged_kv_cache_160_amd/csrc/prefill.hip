@@ -49,7 +49,7 @@ namespace {
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfKeys = 64;                                  // keys per stage
-constexpr int kPfMaxBlocks = PKV_MAX_PREFILL_CONTEXT / kBlockTokens;
+constexpr int kPfMaxBlocks = PKV_MAX_PREFILL_CONTEXT / kTileTokens;
 constexpr int kXcds = 8;
 constexpr float kLog2eP = 1.4426950408889634f;
 
@@ -136,7 +136,7 @@ struct StageIO {
   // in bank space, so the 16 rows a transpose read or a K-operand read
   // touches spread evenly over the banks
   static constexpr int lds_row = D + 16;
-  static constexpr int tile_bytes = kBlockTokens * row_bytes;     // one (block, head) tile
+  static constexpr int tile_bytes = kTileTokens * row_bytes;     // one 16-row tile
   u32x4 k[rounds], v[rounds];
   float ks;                                                  // fp8: thread t < 64 -> a K scale, < 128 -> a V scale
 };
@@ -192,7 +192,7 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
   const int r0 = tile * SH::rows;
   if (r0 >= rows_b) return;
   int L = a.context_lens[b];
-  L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * kBlockTokens)));
+  L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * a.block_size)));
   const int ctx = L - n;             // positions of the chunk: ctx .. L-1
 
   const int tid = threadIdx.x;
@@ -218,10 +218,16 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
   const int key_end = min(L, max(1, ctx + i_last + 1));       // exclusive
   const int free_end = max(0, ctx + i_first + 1);             // keys < free_end are seen by every row
   const int nstages = (key_end + kPfKeys - 1) / kPfKeys;
-  const int nblk = (key_end + kBlockTokens - 1) / kBlockTokens;
+  const int nblk = (key_end + kTileTokens - 1) / kTileTokens;
 
+  // Unit u (tokens 16u .. 16u+15) staged as its tile index at KV head 0,
+  // ((phys * Hkv) << rs) + (u & (2^rs - 1)); the table entry is clamped into
+  // the pool (the positions it stands for are the caller's to keep valid).
   const int32_t* table = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq;
-  for (int i = tid; i < nblk; i += kPfThreads) sm_ids[i] = min(max(table[i], 0), a.num_blocks - 1);
+  const int rs = block_shift(a.block_size);
+  for (int u = tid; u < nblk; u += kPfThreads)
+    sm_ids[u] = ((min(max(table[u >> rs], 0), a.num_blocks - 1) * a.num_kv_heads) << rs) + (u & ((1 << rs) - 1));
+  const int g_tile = g << rs;
 
   // ---- query operands and per-row limits -------------------------------------
   // Wave w, tile ct, column c: row r0 + w*16*CTILES + ct*16 + c.
@@ -411,8 +417,8 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
     for (int r = 0; r < IO::rounds; ++r) {
       const int byte = (r * kPfThreads + tid) * 16;
       thr_row[r] = byte / IO::row_bytes;
-      thr_blk[r] = thr_row[r] / kBlockTokens;
-      thr_off[r] = (thr_row[r] % kBlockTokens) * IO::row_bytes + byte % IO::row_bytes;
+      thr_blk[r] = thr_row[r] / kTileTokens;
+      thr_off[r] = (thr_row[r] % kTileTokens) * IO::row_bytes + byte % IO::row_bytes;
     }
     auto load_stage = [&](int s) {
       const int kb = s * kPfKeys;
@@ -420,7 +426,7 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
       for (int r = 0; r < IO::rounds; ++r) {
         if (kb + thr_row[r] < key_end) {
           const int id = sm_ids[4 * s + thr_blk[r]];
-          const int64_t off = static_cast<int64_t>(id * a.num_kv_heads + g) * IO::tile_bytes + thr_off[r];
+          const int64_t off = static_cast<int64_t>(id + g_tile) * IO::tile_bytes + thr_off[r];
           io.k[r] = *reinterpret_cast<const u32x4*>(kpool + off);
           io.v[r] = *reinterpret_cast<const u32x4*>(vpool + off);
         } else {
@@ -432,8 +438,8 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
       if (tid < 2 * kPfKeys) {
         const int key = kb + (tid % kPfKeys);
         if (key < key_end) {
-          const int id = sm_ids[key / kBlockTokens];
-          const int64_t si = static_cast<int64_t>(id * a.num_kv_heads + g) * kBlockTokens + key % kBlockTokens;
+          const int id = sm_ids[key / kTileTokens];
+          const int64_t si = static_cast<int64_t>(id + g_tile) * kTileTokens + key % kTileTokens;
           io.ks = tid < kPfKeys ? a.k_scale[si] : a.v_scale[si];
         }
       }
@@ -476,13 +482,13 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
       const int slot = (wave * kInsts + k) * kWave + lane;
       const int r = slot / CH;
       const int q = (slot % CH) ^ LdsSwz<D>::of(r);
-      lane_off[k] = (r % kBlockTokens) * IO::row_bytes + 16 * q;
+      lane_off[k] = (r % kTileTokens) * IO::row_bytes + 16 * q;
     }
     auto dma = [&](uint8_t* kdst, uint8_t* vdst, int s) {
       // rows past the context (last stage) read the sequence's last block
       // and are zeroed after they land
       const int id = sm_ids[min(4 * s + wave, nblk - 1)];
-      const int64_t base = static_cast<int64_t>(id * a.num_kv_heads + g) * IO::tile_bytes;
+      const int64_t base = static_cast<int64_t>(id + g_tile) * IO::tile_bytes;
 #pragma unroll
       for (int k = 0; k < kInsts; ++k) {
         const int dst = (wave * kInsts + k) * kWave * 16;

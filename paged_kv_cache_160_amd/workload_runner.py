@@ -29,7 +29,7 @@ class GpuWorkload:
                  device="cuda"):
         self.w = w
         self.cache = PagedKVCache(num_layers, num_blocks or w.num_blocks, w.num_kv_heads, w.head_dim,
-                                  w.cache_dtype, w.max_blocks_per_seq, device=device)
+                                  w.cache_dtype, w.max_blocks_per_seq, device=device, block_size=w.block_size)
         self.device = device
         self.trace: List[tuple] = []
         self._rows: Dict[int, tuple] = {}

@@ -37,22 +37,24 @@ def bits_of_values(vals: np.ndarray, dtype: str) -> np.ndarray:
     return t.view(torch.int32 if dtype == "f32" else torch.int16).numpy()
 
 
-def slots_for(table_row, length: int) -> np.ndarray:
+def slots_for(table_row, length: int, bs: int = 16) -> np.ndarray:
     t = np.arange(length)
-    return np.asarray(table_row, dtype=np.int64)[t // 16] * 16 + t % 16
+    return np.asarray(table_row, dtype=np.int64)[t // bs] * bs + t % bs
 
 
 def gather_gpu_rows(pool: torch.Tensor, slots: np.ndarray) -> torch.Tensor:
-    """Rows [n, Hkv, D] stored at the given slots of a device pool (raw dtype)."""
+    """Rows [n, Hkv, D] stored at the given slots of a device pool
+    ``[num_blocks, Hkv, bs, D]`` (raw dtype)."""
+    bs = pool.shape[2]
     s = torch.from_numpy(slots).to(pool.device)
-    return pool[s // 16, :, s % 16, :]
+    return pool[s // bs, :, s % bs, :]
 
 
 def check_cache_rows(w: wl.Workload, cache, layer: int, seq: int, table_row, length: int) -> None:
     """Bit-exact: the GPU pool holds, at the slots the oracle's tables give for
     positions 0..L-1, the rows the oracle expects (copies, or e4m3 codes and
     scales from the oracle's quantiser for quantised formats)."""
-    slots = slots_for(table_row, length)
+    slots = slots_for(table_row, length, w.block_size)
     k_rows = wl.kv_rows(w, seq, "k", length)
     v_rows = wl.kv_rows(w, seq, "v", length)
     gk = gather_gpu_rows(cache.k[layer], slots).cpu()
@@ -64,7 +66,7 @@ def check_cache_rows(w: wl.Workload, cache, layer: int, seq: int, table_row, len
             codes, scales = kv_formats.quantise(rows, elem)
             assert np.array_equal(got.view(torch.uint8).numpy(), codes), f"seq {seq}: {elem} codes differ"
             s = torch.from_numpy(slots).to(scale_pool.device)
-            gs = scale_pool[s // 16, :, s % 16].cpu().numpy()
+            gs = scale_pool[s // w.block_size, :, s % w.block_size].cpu().numpy()
             assert np.array_equal(gs.view(np.uint32), scales.view(np.uint32)), f"seq {seq}: scales differ"
     else:
         view = torch.int32 if w.cache_dtype == "f32" else torch.int16

@@ -36,10 +36,10 @@ def _ids(c):
     return f"hq{c[0]}-hkv{c[1]}-d{c[2]}-{c[6] or c[5]}-n{sum(c[4])}"
 
 
-def _run(case, seed=11):
+def _run(case, seed=11, bs=16):
     hq, hkv, d, cached, chunk, dtype, cache, qd = case
     w = wl.chunk_workload(len(cached), hq, hkv, d, cached, chunk, dtype=dtype, cache_dtype=cache, q_dtype=qd,
-                          seed=seed, extra_blocks=8)
+                          seed=seed, extra_blocks=8, block_size=bs)
     ops = [("free_order", w.free_order)]
     for b in range(w.num_seqs):
         ops.append(("create", b))
@@ -68,9 +68,9 @@ def pkv_dtype(name):
 
 
 @pytest.mark.parametrize("case", CASES, ids=[_ids(c) for c in CASES])
-def test_prefill_matches_oracle(case):
-    say(f"[prefill] {case}")
-    w, g, q_np, got = _run(case)
+def test_prefill_matches_oracle(case, bs=16):
+    say(f"[prefill] {case} block size {bs}")
+    w, g, q_np, got = _run(case, bs=bs)
     scale = 1.0 / math.sqrt(w.head_dim)
     chunk = w.extra["chunk"]
     qs = np.concatenate([[0], np.cumsum(chunk)])

@@ -15,26 +15,27 @@ from tests._parity import check_cache_rows, say
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("cache,src,qd,d", [("bf16", "bf16", None, 128), ("fp8_e4m3", "f32", "bf16", 128),
-                                            ("int8_int4", "bf16", "bf16", 64)])
-def test_swap_round_trip(cache, src, qd, d):
-    say(f"[swap] {cache} D={d}")
+@pytest.mark.parametrize("cache,src,qd,d,bs", [("bf16", "bf16", None, 128, 16), ("fp8_e4m3", "f32", "bf16", 128, 16),
+                                               ("int8_int4", "bf16", "bf16", 64, 16), ("bf16", "bf16", None, 128, 32),
+                                               ("int8_int4", "bf16", "bf16", 64, 32)])
+def test_swap_round_trip(cache, src, qd, d, bs):
+    say(f"[swap] {cache} D={d} block size {bs}")
     lens = [300, 517, 45]
     w = wl.custom_workload(len(lens), 16, 4, d, lens, dtype=src, cache_dtype=cache, q_dtype=qd, seed=21,
-                           pool_factor=1.0, extra_blocks=40)
+                           pool_factor=1.0, extra_blocks=40 * 16 // bs, block_size=bs)
     g = GpuWorkload(w, num_layers=2).run(wl.setup_ops(w))
     c = g.cache
     seqs = [0, 1, 2]
     q = to_device(wl.queries(w, 0), w.q_dtype)
     before = [c.decode(q, layer, seq_ids=seqs).clone() for layer in range(2)]
-    old_blocks = c.alloc.block_tables([1])[0][0, :(lens[1] + 15) // 16].tolist()
+    old_blocks = c.alloc.block_tables([1])[0][0, :(lens[1] + bs - 1) // bs].tolist()
 
     host = c.swap_out(1)
     torch.cuda.synchronize()
     assert c.alloc.seq_len(1) == lens[1]
     # a new sequence takes the freed blocks and writes other rows into them
     c.create(99)
-    n_new = 16 * len(old_blocks)
+    n_new = bs * len(old_blocks)
     rows = torch.randn((n_new, 4, d), device="cuda").to(TORCH_DTYPES[src])
     c.append(99, rows, rows)
     reused = set(c.alloc.block_tables([99])[0][0].tolist()) & set(old_blocks)

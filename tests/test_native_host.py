@@ -50,8 +50,8 @@ def test_strerror_and_version():
 # ---- allocator: C++ vs the oracle model ------------------------------------------
 
 def _run_both(w, ops):
-    model = BlockAllocatorModel(w.num_blocks, w.max_blocks_per_seq)
-    native = pkv.BlockAllocator(w.num_blocks, w.max_blocks_per_seq)
+    model = BlockAllocatorModel(w.num_blocks, w.max_blocks_per_seq, w.block_size)
+    native = pkv.BlockAllocator(w.num_blocks, w.max_blocks_per_seq, w.block_size)
     for op in ops:
         kind = op[0]
         if kind == "free_order":
@@ -70,9 +70,9 @@ def _run_both(w, ops):
     return model, native
 
 
-@pytest.mark.parametrize("cid", [1, 2, 3, 4, 5])
-def test_allocator_matches_model_on_workload_setup(cid):
-    w = wl.make_workload(cid)
+@pytest.mark.parametrize("cid,bs", [(c, 16) for c in (1, 2, 3, 4, 5)] + [(c, 32) for c in (1, 2, 4, 5)])
+def test_allocator_matches_model_on_workload_setup(cid, bs):
+    w = wl.with_block_size(wl.make_workload(cid), bs)
     model, native = _run_both(w, wl.setup_ops(w))
     seqs = list(range(w.num_seqs))
     mt, ml = model.block_tables(seqs, w.max_blocks_per_seq)
@@ -125,12 +125,13 @@ def test_batch_append_shared_block_counts_exact():
     assert [s % 16 for s in slots] == [5, 5, 5, 5]
 
 
-@pytest.mark.parametrize("seed", range(4))
-def test_allocator_random_streams_match_model(seed):
-    rng = np.random.default_rng(100 + seed)
-    nb, mb = 48, 12
-    model = BlockAllocatorModel(nb, mb)
-    native = pkv.BlockAllocator(nb, mb)
+@pytest.mark.parametrize("seed,bs", [(s, 16) for s in range(4)] + [(s, 32) for s in range(3)])
+def test_allocator_random_streams_match_model(seed, bs):
+    rng = np.random.default_rng(100 + seed + bs)
+    nb, mb = 48 * 16 // bs, 12 * 16 // bs
+    model = BlockAllocatorModel(nb, mb, bs)
+    native = pkv.BlockAllocator(nb, mb, bs)
+    assert native.block_size == bs
     order = rng.permutation(nb)
     model.set_free_order(order)
     native.set_free_order(order)
@@ -294,3 +295,26 @@ def test_swap_hand_worked_matches_model():
     with pytest.raises(pkv.PagedKVError) as e:
         a.swap_out(0)                    # shared blocks stay
     assert e.value.code == -1
+
+
+def test_block_size_is_16_or_32():
+    for bad in (0, 8, 24, 64):
+        with pytest.raises(pkv.PagedKVError):
+            pkv.BlockAllocator(4, 4, block_size=bad)
+    lib = pkv._lib.lib()
+    assert lib.pkv_alloc_block_size(None) == -1
+    # device calls check the block size on the host before anything else runs
+    assert lib.kv_cache_append_bs(None, None, None, None, None, None, None, 1, 1, 64, 4, 24,
+                                  pkv.PKV_BF16, pkv.PKV_BF16, None) == -1
+    assert lib.pkv_copy_blocks_bs(None, None, None, None, None, 1, 1, 64, 4, 64, pkv.PKV_BF16, None) == -1
+    assert lib.paged_attention_decode_bs(None, None, None, None, None, None, None, None, 1, 4, 1, 64, 4, 8,
+                                         4, 64, 0.125, pkv.PKV_BF16, pkv.PKV_BF16, 0, None, 0, None) == -1
+    assert lib.paged_attention_merge_partials_bs(None, None, 1, 4, 1, 64, 48, 4, 64, pkv.PKV_BF16, 0, None, 0,
+                                                 None) == -1
+    assert lib.paged_attention_prefill_bs(None, None, None, None, None, None, None, None, None, 1, 1, 4, 1, 64, 4,
+                                          8, 4, 64, 1, 0.125, pkv.PKV_BF16, pkv.PKV_BF16, None) == -1
+    # 32-token blocks: max_context_len may reach 32 * max_blocks_per_seq, not more
+    assert lib.paged_attention_decode_bs(None, None, None, None, None, None, None, None, 0, 4, 1, 64, 4, 32,
+                                         4, 128, 0.125, pkv.PKV_BF16, pkv.PKV_BF16, 0, None, 0, None) == 0
+    assert lib.paged_attention_decode_bs(None, None, None, None, None, None, None, None, 0, 4, 1, 64, 4, 32,
+                                         4, 129, 0.125, pkv.PKV_BF16, pkv.PKV_BF16, 0, None, 0, None) == -1

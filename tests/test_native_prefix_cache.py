@@ -7,11 +7,11 @@ import pytest
 
 import paged_kv_cache_160_amd as pkv
 from oracle.allocator import PrefixCachingAllocatorModel
-from tests.test_oracle_prefix_cache import EXPECTED_HAND, _stream, hand_worked, replay
+from tests.test_oracle_prefix_cache import EXPECTED_HAND, _stream, expected_hand, hand_worked, replay
 
 
-def _native(nb, mb, model_key=0, hash_bits=64):
-    a = pkv.BlockAllocator(nb, mb)
+def _native(nb, mb, model_key=0, hash_bits=64, bs=16):
+    a = pkv.BlockAllocator(nb, mb, bs)
     a.enable_prefix_cache(model_key, hash_bits)
     return a
 
@@ -28,12 +28,21 @@ def test_hand_worked_example():
                               "hit_blocks": 4, "evictions": 2}
 
 
-@pytest.mark.parametrize("hash_bits", [64, 2])
-@pytest.mark.parametrize("seed", range(6))
-def test_random_streams_match_model(seed, hash_bits):
+def test_hand_worked_example_32_token_blocks():
+    a = _native(5, 8, bs=32)
+    seen = hand_worked(a, 32)
+    for k, v in expected_hand(32).items():
+        assert seen[k] == v, k
+    assert seen["r3_refused"] == -5
+
+
+@pytest.mark.parametrize("seed,hash_bits,bs", [(s, h, 16) for s in range(6) for h in (64, 2)] +
+                         [(s, h, 32) for s in (0, 1, 4) for h in (64, 2)])
+def test_random_streams_match_model(seed, hash_bits, bs):
     ops = list(_stream(seed, n_ops=800, shared=seed < 4))
-    m = PrefixCachingAllocatorModel(40, 12, model_key=99)
-    a = _native(40, 12, model_key=99, hash_bits=hash_bits)
+    nb, mb = 40 * 16 // bs, 12 * 16 // bs
+    m = PrefixCachingAllocatorModel(nb, mb, model_key=99, block_size=bs)
+    a = _native(nb, mb, model_key=99, hash_bits=hash_bits, bs=bs)
     got, exp = [], []
     for i in range(0, len(ops), 50):
         chunk = ops[i:i + 50]
@@ -43,7 +52,7 @@ def test_random_streams_match_model(seed, hash_bits):
         assert a.prefix_stats() == m.prefix_stats()
         assert a.stats() == pytest.approx(m.stats())
     if seed < 4:
-        assert m.prefix_stats()["evictions"] > 20 and m.prefix_stats()["hit_blocks"] > 20
+        assert m.prefix_stats()["evictions"] > 20 * 16 // bs // (bs // 16) and m.prefix_stats()["hit_blocks"] > 20
     else:
         assert sum(1 for r in exp if r[0] == "swap" and r[1] != "error") > 5
 

@@ -271,7 +271,7 @@ def setup_ops(w: Workload, share_prefix: bool = True) -> list:
         for op, arg in w.churn_ops:
             if op == "alloc":
                 ops.append(("create", nxt))
-                ops.append(("append", nxt, BLOCK_TOKENS * arg))
+                ops.append(("append", nxt, w.block_size * arg))
                 live.append(nxt)
                 nxt += 1
             else:
@@ -295,12 +295,14 @@ def setup_ops(w: Workload, share_prefix: bool = True) -> list:
 
 def chunk_workload(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int, cached: List[int],
                    chunk: List[int], dtype: str = "bf16", cache_dtype: Optional[str] = None,
-                   q_dtype: Optional[str] = None, seed: int = 0, extra_blocks: int = 0) -> Workload:
+                   q_dtype: Optional[str] = None, seed: int = 0, extra_blocks: int = 0,
+                   block_size: int = BLOCK_TOKENS) -> Workload:
     """A chunked-prefill batch: sequence b holds ``cached[b]`` tokens and
     appends a chunk of ``chunk[b]`` more; context_lens are the totals."""
     lens = [int(c) + int(n) for c, n in zip(cached, chunk)]
     w = custom_workload(num_seqs, num_q_heads, num_kv_heads, head_dim, lens, dtype=dtype,
-                        cache_dtype=cache_dtype, q_dtype=q_dtype, seed=seed, extra_blocks=extra_blocks)
+                        cache_dtype=cache_dtype, q_dtype=q_dtype, seed=seed, extra_blocks=extra_blocks,
+                        block_size=block_size)
     w.extra["chunk"] = [int(n) for n in chunk]
     return w
 
