@@ -315,12 +315,18 @@ __device__ __forceinline__ void pv_tile(const float (&p)[4], const Words<Geo<QT,
 // ---- the main kernel ------------------------------------------------------------
 
 
+// Quantised pools keep three waves per SIMD (their tiles are half as large,
+// so the registers fit); 16-bit and fp32 pools take two.
+template <typename KT>
+constexpr int decode_min_blocks() { return KT::quantised ? 3 : 2; }
+
 template <typename QT, typename KT, typename VT, int D, int PIPE>
-__global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a) {
+__global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decode_kernel(DecodeArgs a) {
   using G = Geo<QT, KT, VT, D>;
   constexpr bool kQK = KT::quantised;
   constexpr bool kQV = VT::quantised;
   constexpr float kNegInf = -INFINITY;
+  constexpr float kRebase = 8.0f;          // lazy-rescale threshold (log2 units)
 
   __shared__ float sm_m[kWaves][kMaxGroup];
   __shared__ float sm_l[kWaves][kMaxGroup];
@@ -473,38 +479,47 @@ __global__ void __launch_bounds__(kThreads, 2) paged_decode_kernel(DecodeArgs a)
         }
       }
     }
+    // Lazy rescale: the running max m of a head only moves when the tile's
+    // max exceeds it by more than kRebase (log2 units), so p = 2^(s - m)
+    // stays below 2^kRebase and O and l are rescaled only then - for random
+    // scores about once per wave.  O and l always share one m, so the final
+    // O / l is the same function of the scores.
     const float bm = col_max4(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
-    const float m_new = fmaxf(m, bm);
-    const float alpha = (m_new == kNegInf) ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
+    const bool grow = bm > m + kRebase;       // also true for the first valid tile (m = -inf)
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float m_new = grow ? bm : m;
+      const float alpha = (m_new == kNegInf || !grow) ? 1.0f : __builtin_amdgcn_exp2f(m - m_new);
+      l *= alpha;
+      m = m_new;
+      // rescale O: lane (c, j) reg r holds head row 4j+r; alpha of head h
+      // sits in lane h (all lanes of column h agree).  With at most 4 heads
+      // per group only rows 0..3 (lanes j == 0) matter, and the four factors
+      // are wave-uniform: read them into scalar registers.
+      float ar[4];
+      if (group <= 4) {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) ar[rr] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(alpha), rr));
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) ar[rr] = __shfl(alpha, 4 * j + rr, kWave);
+      }
+#pragma unroll
+      for (int nt = 0; nt < G::DC; ++nt) {
+        o[nt][0] *= ar[0];
+        o[nt][1] *= ar[1];
+        o[nt][2] *= ar[2];
+        o[nt][3] *= ar[3];
+      }
+    }
     float p[4];
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      float e = valid[t] ? __builtin_amdgcn_exp2f(sc[t] - m_new) : 0.0f;
+      float e = valid[t] ? __builtin_amdgcn_exp2f(sc[t] - m) : 0.0f;
       psum += e;
       p[t] = e * vsc[t];
     }
-    l = l * alpha + psum;
-    m = m_new;
-    // rescale O: lane (c, j) reg r holds head row 4j+r; alpha of head h sits
-    // in lane h (all lanes of column h agree).  With at most 4 heads per
-    // group only rows 0..3 (lanes j == 0) matter, and the four factors are
-    // wave-uniform: read them into scalar registers.
-    float ar[4];
-    if (group <= 4) {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) ar[rr] = __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(alpha), rr));
-    } else {
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) ar[rr] = __shfl(alpha, 4 * j + rr, kWave);
-    }
-#pragma unroll
-    for (int nt = 0; nt < G::DC; ++nt) {
-      o[nt][0] *= ar[0];
-      o[nt][1] *= ar[1];
-      o[nt][2] *= ar[2];
-      o[nt][3] *= ar[3];
-    }
+    l += psum;
     pv_tile<QT, VT, D>(p, r.v, o);
   };
 
