@@ -206,11 +206,6 @@ __device__ __forceinline__ uint2 conv8(uint32_t src) {
   return r;
 }
 
-// Nibble i of w (two's complement) as a float.
-__device__ __forceinline__ float nib(uint32_t w, int i) {
-  return static_cast<float>(static_cast<int32_t>(w << (28 - 4 * i)) >> 28);
-}
-
 // K operand words of MFMA i (8 contraction elements) from the lane's K words.
 template <typename QT, typename KT, int D>
 __device__ __forceinline__ uint4 k_operand(const Words<Geo<QT, KT, KT, D>::kWords>& k, int i) {
@@ -261,9 +256,22 @@ __device__ __forceinline__ float4_t mfma16(uint2 a, uint2 b, float4_t c) {
 // ---- P*V on MFMA -----------------------------------------------------------------
 // p[r]: probability (times the V scale of a quantised pool) of token 4j+r for
 // head column c.
+// INT4 values enter the MFMA with an offset: the code x (two's complement,
+// |x| <= 8) becomes the 16-bit value MAGIC + (x + 8) by one AND-OR of its
+// nibble into the mantissa of MAGIC (128 in bf16, 1024 in f16, where the
+// 16-bit format steps by 1), so a word of 8 codes takes 8 instructions
+// instead of an integer-to-float conversion per code.  The offset is taken
+// back by a second accumulator fed the same probabilities against the
+// constant MAGIC + 8: O = P (V + off) - P off.
+template <typename QT>
+struct I4Magic {
+  static constexpr uint32_t pair = std::is_same<QT, BF16>::value ? 0x43004300u : 0x64006400u;   // MAGIC, MAGIC
+  static constexpr uint32_t off = std::is_same<QT, BF16>::value ? 0x43084308u : 0x64086408u;    // MAGIC + 8
+};
+
 template <typename QT, typename VT, int D>
 __device__ __forceinline__ void pv_tile(const float (&p)[4], const Words<Geo<QT, VT, VT, D>::vWords> (&v)[4],
-                                        float4_t (&o)[D / 16]) {
+                                        float4_t (&o)[D / 16], float4_t& ocorr) {
   using G = Geo<QT, VT, VT, D>;
   if constexpr (std::is_same<VT, F32>::value) {
 #pragma unroll
@@ -295,19 +303,39 @@ __device__ __forceinline__ void pv_tile(const float (&p)[4], const Words<Geo<QT,
         }
       } else {
         static_assert(std::is_same<VT, I4>::value, "4-bit format");
+        // word k: columns k (low half) and k + DC/2 (high half), offset by
+        // MAGIC + 8; x ^ 8 is x + 8 for a 4-bit two's complement code
+        const uint32_t u = v[e].w[0] ^ (G::DC == 8 ? 0x88888888u : 0x00008888u);   // DC = 4: one 16-bit row
+        const uint32_t s = G::DC == 8 ? u : (u | (u << 8));   // DC = 4: codes 2, 3 move to bits 16..23
 #pragma unroll
-        for (int i = 0; i < G::DC / 2; ++i) w16[e][i] = pack2<QT>(nib(v[e].w[0], 2 * i), nib(v[e].w[0], 2 * i + 1));
+        for (int k = 0; k < G::DC / 2; ++k) w16[e][k] = ((s >> (4 * k)) & 0x000F000Fu) | I4Magic<QT>::pair;
       }
     }
+    if constexpr (std::is_same<VT, I4>::value) {
 #pragma unroll
-    for (int nt = 0; nt < G::DC; ++nt) {
-      const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
-      const int wi = nt >> 1;
-      uint2 b;
-      b.x = __builtin_amdgcn_perm(w16[1][wi], w16[0][wi], sel);
-      b.y = __builtin_amdgcn_perm(w16[3][wi], w16[2][wi], sel);
-      o[nt] = mfma16<QT>(phi, b, o[nt]);
-      o[nt] = mfma16<QT>(plo, b, o[nt]);
+      for (int nt = 0; nt < G::DC; ++nt) {
+        const uint32_t sel = (nt >= G::DC / 2) ? 0x07060302u : 0x05040100u;
+        const int wi = nt % (G::DC / 2);
+        uint2 b;
+        b.x = __builtin_amdgcn_perm(w16[1][wi], w16[0][wi], sel);
+        b.y = __builtin_amdgcn_perm(w16[3][wi], w16[2][wi], sel);
+        o[nt] = mfma16<QT>(phi, b, o[nt]);
+        o[nt] = mfma16<QT>(plo, b, o[nt]);
+      }
+      const uint2 boff = make_uint2(I4Magic<QT>::off, I4Magic<QT>::off);
+      ocorr = mfma16<QT>(phi, boff, ocorr);
+      ocorr = mfma16<QT>(plo, boff, ocorr);
+    } else {
+#pragma unroll
+      for (int nt = 0; nt < G::DC; ++nt) {
+        const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
+        const int wi = nt >> 1;
+        uint2 b;
+        b.x = __builtin_amdgcn_perm(w16[1][wi], w16[0][wi], sel);
+        b.y = __builtin_amdgcn_perm(w16[3][wi], w16[2][wi], sel);
+        o[nt] = mfma16<QT>(phi, b, o[nt]);
+        o[nt] = mfma16<QT>(plo, b, o[nt]);
+      }
     }
   }
 }
@@ -447,6 +475,7 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   float4_t o[G::DC];
 #pragma unroll
   for (int nt = 0; nt < G::DC; ++nt) o[nt] = {0.f, 0.f, 0.f, 0.f};
+  float4_t ocorr = {0.f, 0.f, 0.f, 0.f};     // INT4 V: P times the operand offset
 
   auto compute_block = [&](BlockRegs<QT, KT, VT, D>& r, int i, bool ok) {
     const int base = tok0 + i * kTileTokens;   // logical position of the block's token 0
@@ -510,6 +539,12 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
         o[nt][2] *= ar[2];
         o[nt][3] *= ar[3];
       }
+      if constexpr (std::is_same<VT, I4>::value) {
+        ocorr[0] *= ar[0];
+        ocorr[1] *= ar[1];
+        ocorr[2] *= ar[2];
+        ocorr[3] *= ar[3];
+      }
     }
     float p[4];
     float psum = 0.f;
@@ -520,7 +555,7 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
       p[t] = e * vsc[t];
     }
     l += psum;
-    pv_tile<QT, VT, D>(p, r.v, o);
+    pv_tile<QT, VT, D>(p, r.v, o, ocorr);
   };
 
   // PIPE blocks in flight per wave: block i is computed while blocks
@@ -541,6 +576,17 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
         if (blk < nblk) compute_block(r[st], blk, ok[st]);
         load_block(r[st], min(blk + PIPE * kWaves, last), ok[st]);
       }
+    }
+  }
+
+  if constexpr (std::is_same<VT, I4>::value) {
+    // every column of a head row carries the same offset term
+#pragma unroll
+    for (int nt = 0; nt < G::DC; ++nt) {
+      o[nt][0] -= ocorr[0];
+      o[nt][1] -= ocorr[1];
+      o[nt][2] -= ocorr[2];
+      o[nt][3] -= ocorr[3];
     }
   }
 

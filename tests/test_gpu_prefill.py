@@ -121,3 +121,27 @@ def test_rows_outside_chunks_untouched_and_bad_args_rejected():
         kp = torch.zeros((4, hkv, 16, d), dtype=torch.float32, device="cuda")
         pkv.paged_attention_prefill(qf.clone(), qf, kp, kp, tables, lens, qs, max_len, 10)
     assert e.value.code == -2
+
+
+def test_prefill_bench_shape_sampled():
+    # the benchmarked shape: 16 sequences x (3584 cached + 512 new tokens),
+    # Llama-3-8B layer (Hq 32, Hkv 8, D 128), bf16.  Every output row must be
+    # finite; sampled rows (first, last and interior chunk positions of three
+    # sequences) are compared with the oracle one by one.
+    case = (32, 8, 128, [3584] * 16, [512] * 16, "bf16", None, None)
+    say("[prefill] bench shape 16 x (3584 + 512)")
+    w, g, q_np, got = _run(case, seed=19)
+    assert np.isfinite(got).all()
+    scale = 1.0 / math.sqrt(w.head_dim)
+    qs = np.concatenate([[0], np.cumsum(w.extra["chunk"])])
+    worst = 0.0
+    for b in (0, 7, 15):
+        L = w.context_lens[b]
+        K, V = attention.rows_as_cached(wl.kv_rows(w, b, "k", L), wl.kv_rows(w, b, "v", L), w.cache_dtype)
+        for i in (0, 1, 63, 64, 255, 510, 511):
+            p = L - 512 + i
+            exp = attention.attend(q_np[qs[b] + i], K[:p + 1], V[:p + 1], scale)
+            err = max_err(got[qs[b] + i], exp)
+            worst = max(worst, err)
+            assert err <= TOL["bf16"], (b, i, err)
+    say(f"[prefill] bench shape sampled max err {worst:.3e}")

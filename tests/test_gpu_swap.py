@@ -56,3 +56,34 @@ def test_swap_round_trip(cache, src, qd, d, bs):
     for layer in range(2):
         assert torch.equal(before[layer].cpu(), after[layer].cpu()), f"layer {layer}"
     say(f"[swap] old blocks {old_blocks[:4]}.. new {new_blocks[:4]}..")
+
+
+def test_swap_bench_shape():
+    # one layer of the benchmarked swap row: 16 x 4096 tokens, Hq 32, Hkv 8,
+    # D 128, bf16; sequences 0-3 go out, four new sequences take their
+    # blocks and overwrite them, and they come back into other blocks
+    lens = [4096] * 16
+    w = wl.custom_workload(16, 32, 8, 128, lens, dtype="bf16", seed=23, pool_factor=1.0, extra_blocks=4 * 256 + 8)
+    say("[swap] bench shape 16 x 4096, 4 sequences out and in")
+    g = GpuWorkload(w).run(wl.setup_ops(w))
+    c = g.cache
+    seqs = list(range(16))
+    q = to_device(wl.queries(w, 0), w.q_dtype)
+    before = c.decode(q, 0, seq_ids=seqs).clone()
+    hosts = {s: c.swap_out(s) for s in range(4)}
+    torch.cuda.synchronize()
+    rows = torch.randn((4096, 8, 128), device="cuda").to(torch.bfloat16)
+    for s in range(4):
+        c.create(100 + s)
+        c.append(100 + s, rows, rows)
+    for s in range(4):
+        c.swap_in(s, hosts[s])
+    torch.cuda.synchronize()
+    for s in range(4):
+        c.free(100 + s)
+    tables, lengths = c.alloc.block_tables(seqs)
+    for b in range(4):
+        check_cache_rows(w, c, 0, b, tables[b].numpy(), int(lengths[b]))
+    after = c.decode(q, 0, seq_ids=seqs)
+    torch.cuda.synchronize()
+    assert torch.equal(before.cpu(), after.cpu())
