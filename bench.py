@@ -56,7 +56,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--config", type=int, default=2, help="workload 1..5 (default 2: Llama-3-8B shape, bf16)")
-    ap.add_argument("--layers", type=int, default=0, help="pools to rotate (0 = 32, or enough for 4x the MALL)")
+    ap.add_argument("--layers", type=int, default=0, help="pools to rotate (0 = 32, or at least 4 and enough for 4x the MALL)")
     ap.add_argument("--partition-size", type=int, default=0)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="budget of the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -229,7 +229,7 @@ def main():
         w.name = f"{w.name}-{args.cache}"
     kb_el, vb_el, nscale = KV_BYTES[w.cache_dtype]
     per_layer_bytes = int(w.num_blocks * hkv * bs * (D * (kb_el + vb_el) + 8 * nscale))
-    layers = args.layers or (32 if args.config == 2 else max(1, math.ceil(4 * MALL_BYTES / per_layer_bytes)))
+    layers = args.layers or (32 if args.config == 2 else max(4, math.ceil(4 * MALL_BYTES / per_layer_bytes)))
     log(f"[bench] workload {args.config} {w.name}: B={B} Hq={hq} Hkv={hkv} D={D} cache={w.cache_dtype} "
         f"layers={layers} pool={w.num_blocks} blocks/layer ({per_layer_bytes / 2**30:.2f} GiB/layer)")
 
