@@ -79,7 +79,7 @@ def parse():
                          "prefill: multi-token append + chunked prefill attention; swap: sequences to host "
                          "memory and back")
     ap.add_argument("--cache", default=None,
-                    help="decode row: cache format to run the workload with instead of its own "
+                    help="decode and prefill rows: cache format to run with instead of the workload's own "
                          "(fp8_e4m3, fp8_e5m2, int8_int4, ...; K/V rows stay in the workload's dtype)")
     ap.add_argument("--block-size", type=int, choices=[16, 32], default=16,
                     help="decode row: tokens per block (32: the same workload on 32-token blocks)")
@@ -528,27 +528,37 @@ def run_prefill_row(args, lib=None):
     torch.cuda.set_device(dev)
     lib = lib or pkv._lib.lib()
     B, hq, hkv, D = 16, 32, 8, 128
+    fmt = args.cache or "bf16"
+    if fmt not in KV_BYTES or fmt in ("f32", "f16"):
+        raise SystemExit(f"prefill row: cache format {fmt} not taken (bf16 queries)")
+    kb_el, vb_el, nscale = KV_BYTES[fmt]
     cached, chunk = [args.cached] * B, [args.chunk] * B
     L = args.cached + args.chunk
     nb = int(math.ceil(1.1 * B * -(-L // 16)))
     mb = -(-L // 16) + 1
-    layer_bytes = 2 * nb * hkv * 16 * D * 2
+    layer_bytes = int(nb * hkv * 16 * (D * (kb_el + vb_el) + 8 * nscale))
     layers = args.layers or max(2, math.ceil(4 * MALL_BYTES / layer_bytes))
-    log(f"[prefill] B={B} cached={args.cached} chunk={args.chunk} Hq={hq} Hkv={hkv} D={D} bf16, "
+    log(f"[prefill] B={B} cached={args.cached} chunk={args.chunk} Hq={hq} Hkv={hkv} D={D} q bf16, cache {fmt}, "
         f"{layers} layers x {layer_bytes / 2**30:.2f} GiB")
-    cache = PagedKVCache(layers, nb, hkv, D, torch.bfloat16, mb, device=dev)
+    cache = PagedKVCache(layers, nb, hkv, D, fmt, mb, device=dev)
     cache.set_free_order(np.random.default_rng(2025).permutation(nb).astype(np.int32))
     gen = torch.Generator(device=dev)
     gen.manual_seed(99)
-    for l in range(layers):
-        cache.k[l].normal_(generator=gen)
-        cache.v[l].normal_(generator=gen)
-    chunk_slots = []
+    ctx_slots, chunk_slots = [], []
     for b in range(B):
         cache.create(b)
-        cache.alloc.append_slots(b, args.cached)            # the cached context (rows already in the pool)
+        slots, _ = cache.alloc.append_slots(b, args.cached)  # the cached context, written once below
+        ctx_slots += slots
         slots, _ = cache.alloc.append_slots(b, args.chunk)  # the chunk: its rows are written every step
         chunk_slots += slots
+    # the cached context: seeded N(0,1) rows through the cache write (quantised for quantised formats)
+    ctx_t = torch.tensor(ctx_slots, dtype=torch.int64, device=dev)
+    for l in range(layers):
+        krow = torch.randn((len(ctx_slots), hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+        vrow = torch.randn((len(ctx_slots), hkv, D), generator=gen, device=dev).to(torch.bfloat16)
+        pkv.kv_cache_append(krow, vrow, cache.k[l], cache.v[l], ctx_t, cache.k_scale[l], cache.v_scale[l])
+        del krow, vrow
+    torch.cuda.synchronize()
     seqs = list(range(B))
     tables, lens, max_len = cache.block_tables(seqs)
     T = sum(chunk)
@@ -562,6 +572,8 @@ def run_prefill_row(args, lib=None):
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     code = pkv.dtype_code(torch.bfloat16)
+    ccode = cache.cache_code
+    ptr = lambda t: None if t is None else t.data_ptr()
     scale = 1.0 / math.sqrt(D)
     flops = prefill_flops(cached, chunk, hq, D)
     ev = {(s_, l): tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
@@ -573,16 +585,16 @@ def run_prefill_row(args, lib=None):
             if e:
                 e[0].record(stream)
             rc = lib.kv_cache_append(knew[l].data_ptr(), vnew[l].data_ptr(), cache.k[l].data_ptr(),
-                                     cache.v[l].data_ptr(), None, None, slot_t.data_ptr(), T, hkv, D, nb, code,
-                                     code, sp)
+                                     cache.v[l].data_ptr(), ptr(cache.k_scale[l]), ptr(cache.v_scale[l]),
+                                     slot_t.data_ptr(), T, hkv, D, nb, code, ccode, sp)
             if rc:
                 raise pkv.PagedKVError(rc, "kv_cache_append")
             if e:
                 e[1].record(stream)
             rc = lib.paged_attention_prefill(out[l].data_ptr(), q[l].data_ptr(), cache.k[l].data_ptr(),
-                                             cache.v[l].data_ptr(), None, None, tables.data_ptr(), lens.data_ptr(),
-                                             qs_t.data_ptr(), B, T, hq, hkv, D, nb, mb, max_len, max(chunk), scale,
-                                             code, code, sp)
+                                             cache.v[l].data_ptr(), ptr(cache.k_scale[l]), ptr(cache.v_scale[l]),
+                                             tables.data_ptr(), lens.data_ptr(), qs_t.data_ptr(), B, T, hq, hkv, D,
+                                             nb, mb, max_len, max(chunk), scale, code, ccode, sp)
             if rc:
                 raise pkv.PagedKVError(rc, "paged_attention_prefill")
             if e:
@@ -601,7 +613,7 @@ def run_prefill_row(args, lib=None):
     calls = args.steps * layers
     achieved = flops / pf_s / 1e12
     value = flops * calls / elapsed / 1e12
-    kv_bytes = sum(L for _ in range(B)) * hkv * D * 2 * 2
+    kv_bytes = B * L * hkv * (D * (kb_el + vb_el) + 8 * nscale)
     log(f"[prefill] {args.steps} steps x {layers} layers in {elapsed * 1e3:.2f} ms; append {app_s * 1e6:.1f} us, "
         f"prefill {pf_s * 1e6:.1f} us = {achieved:.1f} TFLOP/s ({100 * achieved / MFMA_BF16_PEAK_TFLOPS:.1f}% of "
         f"bf16 MFMA peak); K/V read {kv_bytes / pf_s / 1e9:.0f} GB/s")
@@ -609,8 +621,9 @@ def run_prefill_row(args, lib=None):
         "metric": "chunked prefill attention over the paged cache, TFLOP/s (algorithmic, causal), 1 GPU",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": elapsed * 1e3 / args.steps, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) K/V/q)",
-        "config": {"workload": f"llama3-8b-shape chunked prefill: 16 x ({args.cached} cached + {args.chunk} new)",
+        "vs_baseline": None, "dtype": fmt, "data": "synthetic (seeded N(0,1) K/V/q)",
+        "config": {"workload": f"llama3-8b-shape chunked prefill: 16 x ({args.cached} cached + {args.chunk} new)"
+                               + ("" if fmt == "bf16" else f", {fmt} cache"),
                    "q_heads": hq, "kv_heads": hkv, "head_dim": D, "block_size": 16, "layers_rotated": layers},
         "append_us": app_s * 1e6, "prefill_kernel_us": pf_s * 1e6,
         "chunk_tokens_per_s": T * calls / elapsed,

@@ -340,7 +340,9 @@ int paged_attention_merge_partials_bs(void* out, const int32_t* context_lens,
  *                  chunk, or one outside q, is skipped and its rows untouched)
  *   max_context_len host: >= every context length, at most
  *                  PKV_MAX_PREFILL_CONTEXT
- * Dtype pairs (q / cache): f16/f16, bf16/bf16, bf16 or f16 / fp8_e4m3; f32
+ * Dtype pairs (q / cache): f16/f16, bf16/bf16, and bf16 or f16 with
+ * fp8_e4m3, fp8_e5m2 or int8_int4 (codes converted exactly to 16-bit values
+ * on their way into LDS, scales applied to scores and probabilities); f32
  * and other head dims give PKV_ERR_UNSUPPORTED.  A sequence with an empty
  * chunk is skipped; with context_lens[b] = 0 its chunk rows are zero.  No
  * workspace; nothing is allocated; asynchronous on stream.

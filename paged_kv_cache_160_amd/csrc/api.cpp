@@ -407,7 +407,6 @@ int paged_attention_prefill_bs(void* out, const void* q, const void* k_pool, con
   if (max_query_len > max_context_len || max_query_len > num_tokens) return PKV_ERR_INVALID_ARG;
   if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
   if (q_dtype == PKV_F32 || !decode_pair_ok(q_dtype, cache_dtype)) return PKV_ERR_UNSUPPORTED;
-  if (cache_dtype == PKV_FP8_E5M2 || cache_dtype == PKV_INT8_INT4) return PKV_ERR_UNSUPPORTED;
   if (max_context_len > PKV_MAX_PREFILL_CONTEXT) return PKV_ERR_UNSUPPORTED;
   if (!tiles_fit(num_blocks, num_kv_heads, block_size)) return PKV_ERR_UNSUPPORTED;
   if (num_seqs == 0 || num_tokens == 0) return PKV_OK;

@@ -89,23 +89,66 @@ __device__ __forceinline__ uint32_t pack_pair(float a, float b) {
   }
 }
 
-// Eight fp8 codes (two words) -> eight 16-bit values of QT's type, exactly,
-// in element order.
-template <typename QT>
-__device__ __forceinline__ u32x4 fp8x8_to_16(uint32_t w0, uint32_t w1) {
-  u32x4 r;
-  if constexpr (std::is_same<QT, BF16>::value) {
-    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false));
-    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true));
-    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false));
-    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true));
+// Four 8-bit codes (one word) of format ET -> four 16-bit values of QT's
+// type (two words), exactly, in element order: e4m3, e5m2 and int8 values
+// all fit.
+template <typename QT, typename ET>
+__device__ __forceinline__ u32x2_t codes8_to_16(uint32_t w) {
+  constexpr bool kBf = std::is_same<QT, BF16>::value;
+  u32x2_t r;
+  if constexpr (std::is_same<ET, FP8>::value) {
+    if constexpr (kBf) {
+      r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+      r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true));
+    } else {
+      r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+      r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true));
+    }
+  } else if constexpr (std::is_same<ET, BF8>::value) {
+    if constexpr (kBf) {
+      r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, false));
+      r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, true));
+    } else {
+      r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, false));
+      r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.0f, true));
+    }
   } else {
-    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false));
-    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true));
-    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false));
-    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true));
+    static_assert(std::is_same<ET, I8>::value, "8-bit format");
+    r[0] = pack_pair<QT>(static_cast<float>(static_cast<int8_t>(w & 0xffu)),
+                         static_cast<float>(static_cast<int8_t>((w >> 8) & 0xffu)));
+    r[1] = pack_pair<QT>(static_cast<float>(static_cast<int8_t>((w >> 16) & 0xffu)),
+                         static_cast<float>(static_cast<int8_t>(w >> 24)));
   }
   return r;
+}
+
+// 16 bytes of codes of format ET -> their values as 16-bit elements of QT's
+// type at dst (16 values for 8-bit codes, 32 for 4-bit ones), exactly.
+// INT4: two's complement nibbles, element 2i in the low nibble of byte i.
+template <typename QT, typename ET>
+__device__ __forceinline__ void codes_to_lds(const u32x4& src, uint16_t* dst) {
+  if constexpr (ET::bits == 8) {
+    const u32x2_t w0 = codes8_to_16<QT, ET>(src[0]);
+    const u32x2_t w1 = codes8_to_16<QT, ET>(src[1]);
+    const u32x2_t w2 = codes8_to_16<QT, ET>(src[2]);
+    const u32x2_t w3 = codes8_to_16<QT, ET>(src[3]);
+    reinterpret_cast<u32x4*>(dst)[0] = u32x4{w0[0], w0[1], w1[0], w1[1]};
+    reinterpret_cast<u32x4*>(dst)[1] = u32x4{w2[0], w2[1], w3[0], w3[1]};
+  } else {
+    static_assert(std::is_same<ET, I4>::value, "4-bit format");
+#pragma unroll
+    for (int wd = 0; wd < 4; ++wd) {
+      u32x4 r;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int32_t x = static_cast<int32_t>(src[wd]);
+        const float e0 = static_cast<float>((x << (28 - 8 * k)) >> 28);
+        const float e1 = static_cast<float>((x << (24 - 8 * k)) >> 28);
+        r[k] = pack_pair<QT>(e0, e1);
+      }
+      reinterpret_cast<u32x4*>(dst)[wd] = r;
+    }
+  }
 }
 
 __device__ __forceinline__ float cmax4(float x) {
@@ -125,20 +168,29 @@ __device__ __forceinline__ float lane_value(float x, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
 }
 
-// One stage's global -> register -> LDS traffic.  Thread t, round r moves
-// 16 bytes of the stage's K (and of V): stage byte (r*256 + t)*16.
-template <typename CT, int D>
+// One stage's global -> LDS traffic.  16-bit pools (KT = VT = the query
+// type) go straight to LDS by row (row_bytes, tile_bytes).  Quantised pools
+// go through registers: thread t, round r moves the 16-byte chunk r*256 + t
+// of the stage's K rows (and of its V rows, which are shorter for INT4), and
+// the chunks are converted to 16-bit values on the way into LDS.
+template <typename KT, typename VT, int D>
 struct StageIO {
-  static constexpr int ces = CT::bytes;
-  static constexpr int row_bytes = D * ces;
-  static constexpr int rounds = kPfKeys * row_bytes / (kPfThreads * 16);
+  static constexpr int k_row_bytes = D * KT::bits / 8;
+  static constexpr int v_row_bytes = D * VT::bits / 8;
+  static constexpr int row_bytes = k_row_bytes;              // 16-bit pools: K and V alike
+  static constexpr int tile_bytes = kTileTokens * row_bytes;
+  static constexpr int k_tile_bytes = kTileTokens * k_row_bytes;
+  static constexpr int v_tile_bytes = kTileTokens * v_row_bytes;
+  static constexpr int k_chunks = kPfKeys * k_row_bytes / 16;
+  static constexpr int v_chunks = kPfKeys * v_row_bytes / 16;
+  static constexpr int k_rounds = (k_chunks + kPfThreads - 1) / kPfThreads;
+  static constexpr int v_rounds = (v_chunks + kPfThreads - 1) / kPfThreads;
   // 16-bit elements per LDS row: D + 16 puts consecutive rows 32 bytes apart
   // in bank space, so the 16 rows a transpose read or a K-operand read
   // touches spread evenly over the banks
   static constexpr int lds_row = D + 16;
-  static constexpr int tile_bytes = kTileTokens * row_bytes;     // one 16-row tile
-  u32x4 k[rounds], v[rounds];
-  float ks;                                                  // fp8: thread t < 64 -> a K scale, < 128 -> a V scale
+  u32x4 k[k_rounds], v[v_rounds];
+  float ks;                                                  // thread t < 64 -> a K scale, < 128 -> a V scale
 };
 
 // Swizzle of 16-byte chunk positions in an unpadded LDS row of D 16-bit
@@ -153,19 +205,19 @@ struct LdsSwz {
   }
 };
 
-template <typename QT, typename CT, int D, int CTILES>
+template <typename QT, typename KT, typename VT, int D, int CTILES>
 __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill_kernel(PrefillArgs a) {
-  using IO = StageIO<CT, D>;
+  using IO = StageIO<KT, VT, D>;
   using SH = PfShape<CTILES>;
-  constexpr bool kFp8 = std::is_same<CT, FP8>::value;
+  constexpr bool kConv = KT::quantised;      // codes converted on the way into LDS
   constexpr int DCH = D / 32;        // QK MFMAs per 16-key tile
   constexpr int DT = D / 16;         // output column tiles
   constexpr float kNegInf = -INFINITY;
 
-  // fp8 caches: one padded 16-bit stage buffer per tensor (and the scales);
-  // 16-bit caches: two unpadded, swizzled stage buffers per tensor
-  constexpr int kPadElems = kFp8 ? kPfKeys * IO::lds_row : 8;
-  constexpr int kDmaChunks = kFp8 ? 1 : kPfKeys * IO::row_bytes / 16;
+  // quantised caches: one padded 16-bit stage buffer per tensor (and the
+  // scales); 16-bit caches: two unpadded, swizzled stage buffers per tensor
+  constexpr int kPadElems = kConv ? kPfKeys * IO::lds_row : 8;
+  constexpr int kDmaChunks = kConv ? 1 : kPfKeys * IO::row_bytes / 16;
   __shared__ __attribute__((aligned(16))) uint16_t sm_k[kPadElems];
   __shared__ __attribute__((aligned(16))) uint16_t sm_v[kPadElems];
   __shared__ u32x4 sm_kd[2][kDmaChunks];
@@ -268,7 +320,7 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
   // and of its half h.  16-bit caches: unpadded rows whose chunk q sits at
   // position q ^ swz(r); fp8 caches (converted on the way in): padded rows.
   auto kaddr = [&](int r, int q) -> int {
-    if constexpr (kFp8) return (r * IO::lds_row + 8 * q) * 2;
+    if constexpr (kConv) return (r * IO::lds_row + 8 * q) * 2;
     else return r * IO::row_bytes + 16 * (q ^ LdsSwz<D>::of(r));
   };
   auto vaddr = [&](int r, int q, int h) -> int { return kaddr(r, q) + 8 * h; };
@@ -299,7 +351,7 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
           }
         }
         __builtin_amdgcn_s_setprio(0);
-        if constexpr (kFp8) {
+        if constexpr (kConv) {
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt) {
             const float4 ksc = *reinterpret_cast<const float4*>(sm_ks + 32 * hv + kt * 16 + 4 * j);
@@ -368,7 +420,7 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
               ps += p[kt][rr];
             }
           lsum[ct] += ps;
-          if constexpr (kFp8) {
+          if constexpr (kConv) {
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
               const float4 vsc = *reinterpret_cast<const float4*>(sm_vs + 32 * hv + kt * 16 + 4 * j);
@@ -407,34 +459,32 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
       }
   };
 
-  if constexpr (kFp8) {
-    // ---- fp8: global -> registers -> (convert) -> LDS, one buffer ----------------
+  if constexpr (kConv) {
+    // ---- quantised: global -> registers -> (convert) -> LDS, one buffer ---------
     IO io;
-    // round r of thread t moves stage bytes (r*256 + t)*16: a fixed row of the
-    // stage (so a fixed block of its 4 and row within it) and column
-    int thr_off[IO::rounds], thr_blk[IO::rounds], thr_row[IO::rounds];
-#pragma unroll
-    for (int r = 0; r < IO::rounds; ++r) {
-      const int byte = (r * kPfThreads + tid) * 16;
-      thr_row[r] = byte / IO::row_bytes;
-      thr_blk[r] = thr_row[r] / kTileTokens;
-      thr_off[r] = (thr_row[r] % kTileTokens) * IO::row_bytes + byte % IO::row_bytes;
-    }
-    auto load_stage = [&](int s) {
+    // round r of thread t moves the stage's 16-byte chunk r*256 + t of K and
+    // of V: a fixed row of the stage (so a fixed tile of its 4 and row within
+    // it) and column
+    auto load_rows = [&](u32x4* dst, const uint8_t* pool, int row_bytes, int tile_bytes, int chunks, int rounds,
+                         int s) {
       const int kb = s * kPfKeys;
-#pragma unroll
-      for (int r = 0; r < IO::rounds; ++r) {
-        if (kb + thr_row[r] < key_end) {
-          const int id = sm_ids[4 * s + thr_blk[r]];
-          const int64_t off = static_cast<int64_t>(id + g_tile) * IO::tile_bytes + thr_off[r];
-          io.k[r] = *reinterpret_cast<const u32x4*>(kpool + off);
-          io.v[r] = *reinterpret_cast<const u32x4*>(vpool + off);
-        } else {
-          io.k[r] = u32x4{0u, 0u, 0u, 0u};
-          io.v[r] = u32x4{0u, 0u, 0u, 0u};
+      for (int r = 0; r < rounds; ++r) {
+        const int chunk = r * kPfThreads + tid;
+        const int row = chunk * 16 / row_bytes;
+        dst[r] = u32x4{0u, 0u, 0u, 0u};
+        if (chunk < chunks && kb + row < key_end) {
+          const int id = sm_ids[4 * s + row / kTileTokens];
+          const int64_t off = static_cast<int64_t>(id + g_tile) * tile_bytes +
+                              (row % kTileTokens) * row_bytes + (chunk * 16) % row_bytes;
+          dst[r] = *reinterpret_cast<const u32x4*>(pool + off);
         }
       }
+    };
+    auto load_stage = [&](int s) {
+      load_rows(io.k, kpool, IO::k_row_bytes, IO::k_tile_bytes, IO::k_chunks, IO::k_rounds, s);
+      load_rows(io.v, vpool, IO::v_row_bytes, IO::v_tile_bytes, IO::v_chunks, IO::v_rounds, s);
       io.ks = 0.0f;
+      const int kb = s * kPfKeys;
       if (tid < 2 * kPfKeys) {
         const int key = kb + (tid % kPfKeys);
         if (key < key_end) {
@@ -446,16 +496,22 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
     };
     auto store_stage = [&]() {
 #pragma unroll
-      for (int r = 0; r < IO::rounds; ++r) {
-        const int byte = (r * kPfThreads + tid) * 16;
-        const int row = byte / IO::row_bytes;
-        const int e = byte % IO::row_bytes;                   // first element (one byte each)
-        uint16_t* kd = sm_k + row * IO::lds_row + e;
-        uint16_t* vd = sm_v + row * IO::lds_row + e;
-        reinterpret_cast<u32x4*>(kd)[0] = fp8x8_to_16<QT>(io.k[r][0], io.k[r][1]);
-        reinterpret_cast<u32x4*>(kd)[1] = fp8x8_to_16<QT>(io.k[r][2], io.k[r][3]);
-        reinterpret_cast<u32x4*>(vd)[0] = fp8x8_to_16<QT>(io.v[r][0], io.v[r][1]);
-        reinterpret_cast<u32x4*>(vd)[1] = fp8x8_to_16<QT>(io.v[r][2], io.v[r][3]);
+      for (int r = 0; r < IO::k_rounds; ++r) {
+        const int chunk = r * kPfThreads + tid;
+        if (chunk < IO::k_chunks) {
+          const int row = chunk * 16 / IO::k_row_bytes;
+          const int e = (chunk * 16) % IO::k_row_bytes * 8 / KT::bits;   // first element of the chunk
+          codes_to_lds<QT, KT>(io.k[r], sm_k + row * IO::lds_row + e);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < IO::v_rounds; ++r) {
+        const int chunk = r * kPfThreads + tid;
+        if (chunk < IO::v_chunks) {
+          const int row = chunk * 16 / IO::v_row_bytes;
+          const int e = (chunk * 16) % IO::v_row_bytes * 8 / VT::bits;
+          codes_to_lds<QT, VT>(io.v[r], sm_v + row * IO::lds_row + e);
+        }
       }
       if (tid < kPfKeys) sm_ks[tid] = io.ks;
       else if (tid < 2 * kPfKeys) sm_vs[tid - kPfKeys] = io.ks;
@@ -544,7 +600,7 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
   }
 }
 
-template <typename QT, typename CT, int D>
+template <typename QT, typename KT, typename VT, int D>
 int launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
   constexpr int kCt = PKV_PREFILL_CTILES;
   PrefillArgs b = a;
@@ -555,29 +611,37 @@ int launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
   if (total == 0) return PKV_OK;
   if (total > (int64_t{1} << 30)) return PKV_ERR_UNSUPPORTED;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL((paged_prefill_kernel<QT, CT, D, kCt>), dim3(static_cast<unsigned>(per_xcd * kXcds)),
+  hipLaunchKernelGGL((paged_prefill_kernel<QT, KT, VT, D, kCt>), dim3(static_cast<unsigned>(per_xcd * kXcds)),
                      dim3(kPfThreads), 0, stream, b);
   return check_launch();
 }
 
-template <typename QT, typename CT>
+template <typename QT, typename KT, typename VT>
 int launch_prefill_dim(const PrefillArgs& a, hipStream_t stream) {
-  if (a.head_dim == 64) return launch_prefill_typed<QT, CT, 64>(a, stream);
-  if (a.head_dim == 128) return launch_prefill_typed<QT, CT, 128>(a, stream);
+  if (a.head_dim == 64) return launch_prefill_typed<QT, KT, VT, 64>(a, stream);
+  if (a.head_dim == 128) return launch_prefill_typed<QT, KT, VT, 128>(a, stream);
+  return PKV_ERR_UNSUPPORTED;
+}
+
+template <typename KT, typename VT>
+int launch_prefill_quantised(const PrefillArgs& a, hipStream_t stream) {
+  if (a.q_dtype == PKV_BF16) return launch_prefill_dim<BF16, KT, VT>(a, stream);
+  if (a.q_dtype == PKV_F16) return launch_prefill_dim<F16, KT, VT>(a, stream);
   return PKV_ERR_UNSUPPORTED;
 }
 
 }  // namespace
 
 int launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-  if (a.cache_dtype == PKV_FP8_E4M3) {
-    if (a.q_dtype == PKV_BF16) return launch_prefill_dim<BF16, FP8>(a, stream);
-    if (a.q_dtype == PKV_F16) return launch_prefill_dim<F16, FP8>(a, stream);
-    return PKV_ERR_UNSUPPORTED;
+  switch (a.cache_dtype) {
+    case PKV_FP8_E4M3: return launch_prefill_quantised<FP8, FP8>(a, stream);
+    case PKV_FP8_E5M2: return launch_prefill_quantised<BF8, BF8>(a, stream);
+    case PKV_INT8_INT4: return launch_prefill_quantised<I8, I4>(a, stream);
+    default: break;
   }
   if (a.q_dtype != a.cache_dtype) return PKV_ERR_UNSUPPORTED;
-  if (a.q_dtype == PKV_BF16) return launch_prefill_dim<BF16, BF16>(a, stream);
-  if (a.q_dtype == PKV_F16) return launch_prefill_dim<F16, F16>(a, stream);
+  if (a.q_dtype == PKV_BF16) return launch_prefill_dim<BF16, BF16, BF16>(a, stream);
+  if (a.q_dtype == PKV_F16) return launch_prefill_dim<F16, F16, F16>(a, stream);
   return PKV_ERR_UNSUPPORTED;
 }
 

@@ -29,6 +29,10 @@ CASES = [
     (32, 4, 64, [500], [130], "bf16", None, None),
     (16, 2, 128, [1000, 17], [700, 3], "f32", "fp8_e4m3", "f16"),
     (32, 8, 128, [2048, 0, 77, 333], [0, 513, 64, 1], "bf16", None, None),
+    (16, 4, 128, [64, 200], [100, 7], "f32", "fp8_e5m2", "bf16"),
+    (8, 2, 64, [300, 31], [65, 17], "f32", "fp8_e5m2", "f16"),
+    (32, 8, 128, [500, 0, 129], [130, 70, 1], "f32", "int8_int4", "bf16"),
+    (16, 2, 64, [1000, 17], [300, 3], "bf16", "int8_int4", "f16"),
 ]
 
 
