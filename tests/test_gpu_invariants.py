@@ -91,6 +91,16 @@ def test_partition_size_independence(ps):
     assert max_err(out, exp) <= TOL["bf16"]
 
 
+def test_largest_partition():
+    # partitions of PKV_MAX_PARTITION_TOKENS = 32768 tokens (the LDS table of
+    # a workgroup full): a 32808-token sequence is one full partition plus 40
+    # tokens, merged; a short one fits the first
+    say("[I8] partition_size=32768")
+    w, g = _custom([32808, 100], 8, 2, 128, "bf16", seed=43)
+    out, exp = _decode_and_compare(w, g, partition_size=32768)
+    assert max_err(out, exp) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("ps", [0, 64])
 def test_empty_context_gives_zeros(ps):
     say(f"[L=0] partition_size={ps}")

@@ -149,3 +149,24 @@ def test_prefill_bench_shape_sampled():
             worst = max(worst, err)
             assert err <= TOL["bf16"], (b, i, err)
     say(f"[prefill] bench shape sampled max err {worst:.3e}")
+
+
+def test_prefill_max_context():
+    # the longest context a prefill call takes (PKV_MAX_PREFILL_CONTEXT = 32768
+    # tokens): one sequence with 32256 cached tokens and a 512-token chunk,
+    # plus a short one; sampled rows against the oracle
+    case = (8, 2, 128, [32768 - 512, 40], [512, 9], "bf16", None, None)
+    say("[prefill] max context 32768")
+    w, g, q_np, got = _run(case, seed=41)
+    assert w.context_lens[0] == 32768          # the header's PKV_MAX_PREFILL_CONTEXT
+    assert np.isfinite(got).all()
+    scale = 1.0 / math.sqrt(w.head_dim)
+    qs = np.concatenate([[0], np.cumsum(w.extra["chunk"])])
+    for b, rows in ((0, (0, 255, 511)), (1, (0, 8))):
+        L = w.context_lens[b]
+        K, V = attention.rows_as_cached(wl.kv_rows(w, b, "k", L), wl.kv_rows(w, b, "v", L), w.cache_dtype)
+        n = w.extra["chunk"][b]
+        for i in rows:
+            p = L - n + i
+            exp = attention.attend(q_np[qs[b] + i], K[:p + 1], V[:p + 1], scale)
+            assert max_err(got[qs[b] + i], exp) <= TOL["bf16"], (b, i)
