@@ -91,10 +91,15 @@ def parse():
 
 
 def source_digest() -> str:
+    """Digest of the decode kernel's code (line comments and blank lines
+    dropped, so that editing a comment keeps a counter record valid)."""
     h = hashlib.sha256()
     for name in ("decode.hip", "device_common.h", "launch.h"):
-        with open(os.path.join(ROOT, "paged_kv_cache_160_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_160_amd", "csrc", name), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].strip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -11,10 +11,12 @@
 //
 // Design (MI355X / CDNA4):
 //  * Workgroup = 4 waves for one (sequence, KV head, partition).  A partition
-//    is a run of logical positions; wave w takes the partition's blocks w,
-//    w+4, w+8, ...  Each wave streams its blocks straight from HBM into
-//    registers with 16-byte loads, several blocks in flight, and keeps its own
-//    online-softmax state; the 4 states merge through LDS at the end.
+//    is a run of logical positions; wave w takes the partition's 16-token
+//    tiles w, w+4, w+8, ... (a tile is 16 rows of one (block, KV head): a
+//    16-token block is one tile, a 32-token block two).  Each wave streams
+//    its tiles straight from HBM into registers with 16-byte loads, several
+//    tiles in flight, and keeps its own online-softmax state; the 4 states
+//    merge through LDS at the end.
 //  * The whole GQA group is served from one read of each K/V tile: the
 //    group's query heads are the 16 columns of an MFMA tile (columns >= G are
 //    zero), so one 16x16 MFMA output holds 16 tokens x 16 heads.
@@ -25,15 +27,20 @@
 //    contraction index of each MFMA may be permuted freely as long as both
 //    operands use the same permutation: each lane loads a contiguous 1/4 of
 //    a K row, and 4 V rows x D/16 contiguous columns.
-//  * fp8 e4m3 codes convert exactly to bf16/f16 in hardware; the per-token
-//    scales multiply the scores (k) and the probabilities (v), never each
-//    element.
+//  * Quantised codes: e4m3 and e5m2 convert exactly to bf16/f16 in
+//    hardware, int8 through float; int4 enters the MFMA as MAGIC + x + 8 and
+//    a second accumulator removes the offset.  The per-token scales multiply
+//    the scores (k) and the probabilities (v), never each element.
+//  * The running maximum of a head moves only when a tile's maximum exceeds
+//    it by more than 2^8, so the output is rescaled about once per wave.
 //  * Probabilities enter the P*V MFMA as a hi + lo pair of 16-bit values, so
 //    P carries ~16 significant bits while the MFMA still accumulates in fp32.
 //  * Long sequences split into partitions; each partition's (max, sum,
-//    unnormalised output) goes to the workspace, and the workgroup that
-//    finishes last for a (sequence, KV head) merges them with the
-//    log-sum-exp formula in the same launch.
+//    unnormalised output) goes to the workspace and a second launch merges
+//    them with the log-sum-exp formula (a variant that merges in the
+//    workgroup of a (sequence, KV head) that finishes last, behind
+//    PKV_DECODE_MERGE, was measured slower: its device-scope fences write
+//    back L2).
 
 #include <math.h>
 

@@ -11,17 +11,18 @@
 //
 // Unlike decode this is a dense contraction (each K/V element meets many
 // queries), so it is built for the matrix cores:
-//  * Workgroup = 4 waves owning 256 query rows of one (sequence, KV head);
+//  * Workgroup = 4 waves owning 4 * 16 * CTILES (128) query rows of one
+//    (sequence, KV head);
 //    a row is a (chunk position, head of the GQA group) pair, so the whole
 //    group shares every K/V tile.  Each wave owns CTILES tiles of 16 rows.
-//  * K and V stream through LDS in stages of 64 keys (4 paged blocks).  For
-//    16-bit caches each wave moves one block of the next stage straight from
+//  * K and V stream through LDS in stages of 64 keys (4 tiles of 16).  For
+//    16-bit caches each wave moves one tile of the next stage straight from
 //    HBM into the second of two LDS buffers (global_load_lds, no registers)
 //    while the workgroup computes the current one; rows are unpadded and
 //    their 16-byte chunks XOR-swizzled by row, so operand reads spread over
-//    the banks.  fp8 codes take a register path instead: they become 16-bit
-//    values exactly on the way into a padded buffer, and their per-token
-//    scales go to LDS beside them.
+//    the banks.  Quantised codes (e4m3, e5m2, int8 K, int4 V) take a
+//    register path instead: they become 16-bit values exactly on the way
+//    into a padded buffer, and their per-token scales go to LDS beside them.
 //      S^T = K (16 keys x D) * Q^T (D x 16 rows)       [16x16x32 MFMA]
 //      O  += P (16 rows x 32 keys) * V (32 keys x 16 d) [16x16x32 MFMA]
 //    The S^T accumulator (lane = row + 16*(key/4), reg = key%4) already is
@@ -318,7 +319,7 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
 
   // Byte offset in a stage buffer of 16-byte chunk q (8 elements) of row r,
   // and of its half h.  16-bit caches: unpadded rows whose chunk q sits at
-  // position q ^ swz(r); fp8 caches (converted on the way in): padded rows.
+  // position q ^ swz(r); quantised caches (converted on the way in): padded rows.
   auto kaddr = [&](int r, int q) -> int {
     if constexpr (kConv) return (r * IO::lds_row + 8 * q) * 2;
     else return r * IO::row_bytes + 16 * (q ^ LdsSwz<D>::of(r));
