@@ -105,14 +105,15 @@ def test_fused_step_with_copy_on_write():
     assert max_err(out, exp) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("ps", [0, 64])
-def test_split_form_equals_one_call(ps):
+@pytest.mark.parametrize("ps,bs", [(0, 16), (64, 16), (0, 32), (64, 32)])
+def test_split_form_equals_one_call(ps, bs):
     # paged_attention_decode_append_partials + paged_attention_merge_partials
     # gives the bytes of paged_attention_decode_append (split and unsplit rows)
     import paged_kv_cache_160_amd as pkv
     case = ([700, 9, 1300, 64], 32, 8, 128, "bf16", None, None, ps)
-    say(f"[split] ps={ps}")
-    w = _make(case, seed=23)
+    say(f"[split] ps={ps} block size {bs}")
+    w = wl.with_block_size(_make(case, seed=23), bs)
+    w.decode_appends = STEPS
     ops = wl.setup_ops(w)
     one = GpuWorkload(w).run(ops)
     two = GpuWorkload(w).run(ops)
@@ -130,7 +131,7 @@ def test_split_form_equals_one_call(ps):
         out_b, ws = pkv.paged_attention_decode_append_partials(out_b, q, kd, vd, c.k[0], c.v[0], slot_t, bt, lens,
                                                                max_len, partition_size=ps)
         pkv.paged_attention_merge_partials(out_b, lens, w.num_kv_heads, w.max_blocks_per_seq, max_len,
-                                           partition_size=ps, workspace=ws)
+                                           partition_size=ps, workspace=ws, block_size=bs)
         torch.cuda.synchronize()
         assert torch.equal(out_a.cpu(), out_b.cpu()), f"step {step}"
     for b in seqs:
