@@ -10,9 +10,9 @@ from typing import List, Optional, Sequence, Union
 
 import torch
 
-from . import (BLOCK_SIZE, CACHE_FORMATS, PKV_FP8_E4M3, PKV_FP8_E5M2, PKV_INT8_INT4, BlockAllocator, copy_blocks,
-               gather_blocks, kv_cache_append, paged_attention_decode, paged_attention_decode_append, scatter_blocks,
-               workspace_size)
+from . import (BLOCK_SIZE, CACHE_FORMATS, PKV_FP8_E4M3, PKV_FP8_E5M2, PKV_INT8_INT4, BlockAllocator, PagedKVError,
+               _lib, copy_blocks, gather_blocks, kv_cache_append, paged_attention_decode, paged_attention_decode_append,
+               scatter_blocks, workspace_size)
 
 Rows = Union[torch.Tensor, Sequence[torch.Tensor]]
 
@@ -111,6 +111,104 @@ class PagedKVCache:
                 raise ValueError("host copy does not match the sequence's blocks")
             scatter_blocks(t, h.to(self.device, non_blocking=True), bt)
         return blocks
+
+    def swap(self, out_seqs: Sequence[int], back_in: Optional[dict] = None, out_host: Optional[dict] = None) -> dict:
+        """Swap ``out_seqs`` out and the sequences of ``back_in`` in, with the
+        two directions of the host link overlapped ("KV Cache 和 vLLM" §6.2:
+        the link is what swapping costs; it carries both directions at once).
+
+        ``back_in`` maps each sequence to the buffer an earlier ``swap`` call
+        returned for it.  The allocator releases the blocks of ``out_seqs``
+        first and then gives each ``back_in`` sequence fresh blocks, which may
+        be blocks just released: their scatters wait for the gathers.  A
+        sequence travels as one pinned host buffer: every pool tensor's blocks
+        are gathered into one device staging buffer and copied at once.
+        Device -> host copies run on the current stream, host -> device copies
+        on a second stream; the current stream waits for both before this
+        returns (nothing here synchronises the host).  The device staging
+        buffers stay allocated between calls (per direction, one per
+        sequence of the largest call so far).  Returns
+        ``{seq: (pinned uint8 buffer, n_blocks)}`` for ``out_seqs``.
+        ``out_host`` may map outgoing sequences to pinned uint8 buffers to
+        fill (large enough; reusing them avoids pinning new memory on every
+        call, which costs more than the copies): a buffer handed back in
+        through ``back_in`` may be reused by a later call, since the current
+        stream has waited for its copy.  An allocator error raises after the
+        swaps already made."""
+        back_in = back_in or {}
+        tensors = self._tensors()
+        bb = [t[0].numel() * t.element_size() for t in tensors]      # bytes of one block of each tensor
+        outs = {s_: self.alloc.swap_out(s_) for s_ in out_seqs}
+        ins = {s_: self.alloc.swap_in(s_) for s_ in back_in}
+        for s_, blocks in ins.items():
+            if back_in[s_][1] != len(blocks):
+                raise ValueError(f"host buffer of sequence {s_} does not match its blocks")
+        lib = _lib.lib()
+        cur = torch.cuda.current_stream(self.device)
+        if getattr(self, "_side", None) is None:
+            self._side = torch.cuda.Stream(self.device)
+        side = self._side
+        if getattr(self, "_swap_done", None) is not None:
+            cur.wait_event(self._swap_done)      # the staging buffers' last use, whatever stream that was on
+
+        def move(staging, blocks_t, n, gather, stream):
+            off = 0
+            for t, b_ in zip(tensors, bb):
+                fn = lib.pkv_gather_blocks if gather else lib.pkv_scatter_blocks
+                args = ((staging.data_ptr() + off, t.data_ptr()) if gather else (t.data_ptr(), staging.data_ptr() + off))
+                rc = fn(*args, blocks_t.data_ptr(), n, b_, self.num_blocks, stream.cuda_stream)
+                if rc:
+                    raise PagedKVError(rc, "pkv_gather_blocks" if gather else "pkv_scatter_blocks")
+                off += n * b_
+
+        # device staging buffers are kept between calls; each is used on one
+        # stream only, so that stream orders its reuse
+        if getattr(self, "_stage", None) is None:
+            self._stage = {"out": [], "in": []}
+
+        def stage(kind, i, nbytes, stream):
+            bufs = self._stage[kind]
+            while len(bufs) <= i:
+                bufs.append(None)
+            if bufs[i] is None or bufs[i].numel() < nbytes:
+                with torch.cuda.stream(stream):
+                    bufs[i] = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+            return bufs[i][:nbytes]
+
+        result, staged = {}, []
+        for i, (s_, blocks) in enumerate(outs.items()):
+            n = len(blocks)
+            staging = stage("out", i, n * sum(bb), cur)
+            bt = torch.tensor(blocks, dtype=torch.int32).to(self.device, non_blocking=True)
+            if n:
+                move(staging, bt, n, True, cur)
+            staged.append((s_, staging, n))
+        gathered = torch.cuda.Event()
+        gathered.record(cur)
+        for s_, staging, n in staged:
+            host = (out_host or {}).get(s_)
+            if host is None:
+                host = torch.empty(staging.numel(), dtype=torch.uint8, pin_memory=True)
+            elif host.dtype != torch.uint8 or not host.is_pinned() or host.numel() < staging.numel():
+                raise ValueError(f"host buffer for sequence {s_} must be pinned uint8 of >= {staging.numel()} bytes")
+            host[:staging.numel()].copy_(staging, non_blocking=True)
+            result[s_] = (host, n)
+        with torch.cuda.stream(side):
+            pending = []
+            for i, (s_, blocks) in enumerate(ins.items()):
+                host, n = back_in[s_]
+                staging = stage("in", i, n * sum(bb), side)
+                staging.copy_(host[:staging.numel()], non_blocking=True)
+                bt = torch.tensor(blocks, dtype=torch.int32).to(self.device, non_blocking=True)
+                pending.append((staging, bt, n))
+            side.wait_event(gathered)            # reused blocks are read before they are written
+            for staging, bt, n in pending:
+                if n:
+                    move(staging, bt, n, False, side)
+        cur.wait_stream(side)
+        self._swap_done = torch.cuda.Event()
+        self._swap_done.record(cur)
+        return result
 
     # -- writes ---------------------------------------------------------------
     def _layer_rows(self, rows: Rows, layer: int) -> torch.Tensor:

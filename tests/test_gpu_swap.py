@@ -87,3 +87,38 @@ def test_swap_bench_shape():
     after = c.decode(q, 0, seq_ids=seqs)
     torch.cuda.synchronize()
     assert torch.equal(before.cpu(), after.cpu())
+
+
+@pytest.mark.parametrize("cache,src,qd,d", [("bf16", "bf16", None, 128), ("int8_int4", "bf16", "bf16", 64)])
+def test_overlapped_swap_reuses_released_blocks(cache, src, qd, d):
+    # PagedKVCache.swap moves one sequence out while another comes back in,
+    # the two copies on different streams.  The incoming sequence takes the
+    # blocks the outgoing one just released (the free list is a stack), so
+    # its scatters must wait for the outgoing gathers: both sequences'
+    # contents are checked after the round trip.
+    say(f"[swap] overlapped {cache} D={d}")
+    lens = [300, 517, 45]
+    w = wl.custom_workload(len(lens), 16, 4, d, lens, dtype=src, cache_dtype=cache, q_dtype=qd, seed=27,
+                           pool_factor=1.0, extra_blocks=2)
+    g = GpuWorkload(w, num_layers=2).run(wl.setup_ops(w))
+    c = g.cache
+    seqs = [0, 1, 2]
+    q = to_device(wl.queries(w, 0), w.q_dtype)
+    before = [c.decode(q, layer, seq_ids=seqs).clone() for layer in range(2)]
+    blocks0 = set(c.alloc.block_tables([0])[0][0, :(lens[0] + 15) // 16].tolist())
+
+    out1 = c.swap([1])                                   # sequence 1 out
+    out0 = c.swap([0], {1: out1[1]})                     # 0 out while 1 comes back in
+    t1 = c.alloc.block_tables([1])[0][0, :(lens[1] + 15) // 16].tolist()
+    assert blocks0 <= set(t1), "sequence 1 did not take sequence 0's released blocks"
+    c.swap([], {0: out0[0]})                             # 0 back in
+    torch.cuda.synchronize()
+
+    tables, lengths = c.alloc.block_tables(seqs)
+    assert lengths.tolist() == lens
+    for b in seqs:
+        check_cache_rows(w, c, 0, b, tables[b].numpy(), int(lengths[b]))
+    after = [c.decode(q, layer, seq_ids=seqs) for layer in range(2)]
+    torch.cuda.synchronize()
+    for layer in range(2):
+        assert torch.equal(before[layer].cpu(), after[layer].cpu()), f"layer {layer}"
