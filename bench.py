@@ -165,7 +165,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
-              "(sharding by sequence or KV head needs no exchange; see DESIGN.md)", file=sys.stderr)
+              "(sharding by sequence or KV head needs no exchange between GPUs)", file=sys.stderr)
         sys.exit(2)
 
     if args.row == "prefix":

@@ -189,10 +189,10 @@ size_t paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_
  *   scale         the caller passes 1/sqrt(head_dim)
  *   partition_size 0 = automatic; else tokens per partition, a multiple of 16
  *                 and at most PKV_MAX_PARTITION_TOKENS.
- *                 Sequences longer than one partition are split; the
- *                 partitions are merged exactly (log-sum-exp) in the same
- *                 launch by whichever workgroup of a (sequence, KV head)
- *                 finishes last.
+ *                 When some sequence is longer than one partition, every
+ *                 sequence's partition states go to the workspace and a
+ *                 second kernel of the same call merges them exactly
+ *                 (log-sum-exp) into the output.
  *   workspace     device scratch of at least paged_attention_workspace_size()
  *                 bytes (may be NULL when that is 0).  Its first part holds
  *                 arrival counters: the whole workspace must be zero before
@@ -274,10 +274,11 @@ int paged_attention_decode_append_bs(void* out, const void* q, const void* k_new
  * Split form of paged_attention_decode_append, for callers that schedule or
  * time its two launches separately.  paged_attention_decode_append_partials
  * takes the same arguments (slot_mapping may be NULL: no cache write, as in
- * paged_attention_decode) and launches only the attention kernel: it writes
- * the output rows of sequences that fit in one partition and the partition
- * states of the others into the workspace.  paged_attention_merge_partials
- * then merges those states into the remaining output rows (log-sum-exp); it
+ * paged_attention_decode) and launches only the attention kernel: when
+ * some sequence is longer than one partition it writes every sequence's
+ * partition states (empty partitions included) into the workspace, else the
+ * output rows.  paged_attention_merge_partials then merges those states
+ * into the output rows (log-sum-exp); it
  * must get the same num_seqs, head counts, head_dim, max_context_len,
  * partition_size and workspace, on the same stream.  The pair gives exactly
  * the bytes of the one-call form.  When nothing is split, the merge call

@@ -36,8 +36,8 @@
 //  * Probabilities enter the P*V MFMA as a hi + lo pair of 16-bit values, so
 //    P carries ~16 significant bits while the MFMA still accumulates in fp32.
 //  * Long sequences split into partitions; each partition's (max, sum,
-//    unnormalised output) goes to the workspace and a second launch merges
-//    them with the log-sum-exp formula (a variant that merges in the
+//    unnormalised output) goes to the workspace (an empty one writes max
+//    -inf) and a second launch merges them with the log-sum-exp formula (a variant that merges in the
 //    workgroup of a (sequence, KV head) that finishes last, behind
 //    PKV_DECODE_MERGE, was measured slower: its device-scope fences write
 //    back L2).
@@ -380,26 +380,19 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   const int c = lane & 15;
   const int j = lane >> 4;
 
-  int L = a.context_lens[b];
-  L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * a.block_size)));
   const int PS = a.partition_size;
-  const int np_b = (L + PS - 1) / PS;         // non-empty partitions of this sequence
   const int tok0 = part * PS;
-  const int64_t out_row0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(g) * group;
-
-  if (L == 0) {
-    // an empty context gives a zero output row (written once)
-    if (part == 0) {
-      for (int i = tid; i < group * D; i += kThreads) store_from_f32<QT>(a.out, out_row0 * D + i, 0.0f);
-    }
-    return;
-  }
-  if (part >= np_b) return;
-  const int tok1 = min(L, tok0 + PS);
   const int blk0 = tok0 / kTileTokens;       // first 16-token unit of the partition
-  const int nblk = (tok1 - tok0 + kTileTokens - 1) / kTileTokens;
+  const int pblk = PS / kTileTokens;         // units of a full partition
+  const int64_t out_row0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(g) * group;
   const int32_t* table = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq;
   const int rs = block_shift(a.block_size);
+
+  // The workgroup's first loads do not depend on each other and are issued
+  // together: the context length, the query, and the block-table entries of
+  // a full partition (read before the length is known; entries past the
+  // sequence's end lie inside its table row and are never used).
+  int L = a.context_lens[b];
 
   // Q^T operand: lane (head column c, k-group j) holds q[head c][j*D/4 ...).
   Words<G::qWords> qop;
@@ -413,6 +406,52 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
       for (int i = 0; i < G::qWords; ++i) qop.w[i] = 0u;
     }
   }
+
+  // The partition's tiles, staged in LDS once: a per-block table read from
+  // global memory in front of the K/V loads would make the wave wait for
+  // every load already in flight (vmcnt is in order), while LDS reads are
+  // counted separately.  Unit u's entry is its tile index at KV head 0,
+  // ((phys * Hkv) << rs) + (u & (2^rs - 1)), or -1 when the table names a
+  // block outside the pool.
+  {
+    constexpr int kLoads = (kMaxPartitionBlocks + kThreads - 1) / kThreads;
+    const int max_units = a.max_blocks_per_seq << rs;
+    int phys[kLoads];
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int u = blk0 + tid + k * kThreads;
+      phys[k] = (tid + k * kThreads < pblk && u < max_units) ? table[u >> rs] : -1;
+    }
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int i = tid + k * kThreads;
+      const int u = blk0 + i;
+      if (i < pblk)
+        sm_ids[i] = (phys[k] >= 0 && phys[k] < a.num_blocks)
+                        ? ((phys[k] * a.num_kv_heads) << rs) + (u & ((1 << rs) - 1))
+                        : -1;
+    }
+  }
+
+  L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * a.block_size)));
+  const int np_b = (L + PS - 1) / PS;         // non-empty partitions of this sequence
+  if (part >= np_b) {
+    if (P == 1 || PKV_DECODE_MERGE != 0) {
+      // an empty context gives a zero output row (written once)
+      if (part == 0)
+        for (int i = tid; i < group * D; i += kThreads) store_from_f32<QT>(a.out, out_row0 * D + i, 0.0f);
+    } else {
+      // the merge reads every partition slot: mark this one empty
+      for (int h = tid; h < group; h += kThreads) {
+        const int64_t prow = (out_row0 + h) * P + part;
+        a.part_ml[2 * prow] = kNegInf;
+        a.part_ml[2 * prow + 1] = 0.0f;
+      }
+    }
+    return;
+  }
+  const int tok1 = min(L, tok0 + PS);
+  const int nblk = (tok1 - tok0 + kTileTokens - 1) / kTileTokens;
   const float qk_scale = a.scale * kLog2e;   // scores in log2 units
 
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k_pool);
@@ -445,18 +484,6 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
       if (wave == 0) write(KT{}, a.k_new, a.k_pool, a.k_scale);
       else write(VT{}, a.v_new, a.v_pool, a.v_scale);
     }
-  }
-
-  // The partition's tiles, staged in LDS once: a per-block table read from
-  // global memory in front of the K/V loads would make the wave wait for
-  // every load already in flight (vmcnt is in order), while LDS reads are
-  // counted separately.  Unit u's entry is its tile index at KV head 0,
-  // ((phys * Hkv) << rs) + (u & (2^rs - 1)), or -1 when the table names a
-  // block outside the pool.
-  for (int i = tid; i < nblk; i += kThreads) {
-    const int u = blk0 + i;
-    const int phys = table[u >> rs];
-    sm_ids[i] = (phys >= 0 && phys < a.num_blocks) ? ((phys * a.num_kv_heads) << rs) + (u & ((1 << rs) - 1)) : -1;
   }
   const int g_tile = g << rs;
   __syncthreads();
@@ -613,7 +640,7 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   }
   __syncthreads();
 
-  const bool single = np_b == 1;
+  const bool single = P == 1;                // else the merge kernel writes the output
   for (int idx = tid; idx < group * D; idx += kThreads) {
     const int h = idx / D;
     const int d = idx % D;
@@ -682,29 +709,26 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
 }
 
 // ---- log-sum-exp merge of partitions (second launch) --------------------------------
-// One workgroup of D threads per (sequence, query head); rows whose sequence
-// fit in one partition (or was empty) were written by the main kernel.
+// One workgroup of D threads per (sequence, query head).  The main kernel
+// wrote a state into every partition slot (an empty partition has max -inf),
+// so the merge needs no context length and issues all of its loads at once.
 template <typename QT, int D>
 __global__ void __launch_bounds__(D) partition_merge_kernel(DecodeArgs a) {
   constexpr int kChunk = 8;                   // partitions whose loads are in flight together
   const int row = blockIdx.x;                 // b * Hq + h
-  const int b = row / a.num_q_heads;
   const int d = threadIdx.x;
   const int P = a.num_partitions;
-  int L = a.context_lens[b];
-  L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * a.block_size)));
-  const int np = (L + a.partition_size - 1) / a.partition_size;
-  if (np <= 1) return;
   const float* ml = a.part_ml + static_cast<int64_t>(row) * P * 2;
   const float* acc = a.part_acc + static_cast<int64_t>(row) * P * D;
   // Running merge over chunks of partitions; within a chunk every load is
-  // issued before any of them is used.
+  // issued before any of them is used.  The output slot of an empty
+  // partition holds stale values and is never used.
   float M = -INFINITY, num = 0.f, den = 0.f;
-  for (int p0 = 0; p0 < np; p0 += kChunk) {
+  for (int p0 = 0; p0 < P; p0 += kChunk) {
     float mp[kChunk], lp[kChunk], ap[kChunk];
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
-      const int p = min(p0 + i, np - 1);
+      const int p = min(p0 + i, P - 1);
       mp[i] = ml[2 * p];
       lp[i] = ml[2 * p + 1];
       ap[i] = acc[static_cast<int64_t>(p) * D + d];
@@ -712,7 +736,7 @@ __global__ void __launch_bounds__(D) partition_merge_kernel(DecodeArgs a) {
     float cm = -INFINITY;
 #pragma unroll
     for (int i = 0; i < kChunk; ++i)
-      if (p0 + i < np) cm = fmaxf(cm, mp[i]);
+      if (p0 + i < P) cm = fmaxf(cm, mp[i]);
     const float M_new = fmaxf(M, cm);
     if (M_new == -INFINITY) continue;
     const float r = __builtin_amdgcn_exp2f(M - M_new);   // 0 while M is still -inf
@@ -720,7 +744,7 @@ __global__ void __launch_bounds__(D) partition_merge_kernel(DecodeArgs a) {
     den *= r;
 #pragma unroll
     for (int i = 0; i < kChunk; ++i) {
-      if (p0 + i < np && mp[i] != -INFINITY) {
+      if (p0 + i < P && mp[i] != -INFINITY) {
         const float f = __builtin_amdgcn_exp2f(mp[i] - M_new);
         num += f * ap[i];
         den += f * lp[i];
