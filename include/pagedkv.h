@@ -336,7 +336,8 @@ int paged_attention_merge_partials_bs(void* out, const int32_t* context_lens,
  *   context_lens   device int32 [num_seqs]: cached tokens including the
  *                  chunk, so chunk row i sits at position
  *                  context_lens[b] - n_b + i and attends to positions 0 .. it
- *   block_tables, pools, scales, scale: as paged_attention_decode
+ *   block_tables, pools, scales, scale: as paged_attention_decode; scale
+ *                  must be positive and finite (else PKV_ERR_INVALID_ARG)
  *   max_query_len  host: >= every chunk length (sizes the launch; a longer
  *                  chunk, or one outside q, is skipped and its rows untouched)
  *   max_context_len host: >= every context length, at most

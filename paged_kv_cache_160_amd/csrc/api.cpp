@@ -3,6 +3,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 
 #include "launch.h"
@@ -405,6 +406,8 @@ int paged_attention_prefill_bs(void* out, const void* q, const void* k_pool, con
   if (static_cast<int64_t>(max_context_len) > static_cast<int64_t>(max_blocks_per_seq) * block_size)
     return PKV_ERR_INVALID_ARG;
   if (max_query_len > max_context_len || max_query_len > num_tokens) return PKV_ERR_INVALID_ARG;
+  // the kernel takes row maxima of raw scores: the scale must be positive
+  if (!(scale > 0.0f) || !std::isfinite(scale)) return PKV_ERR_INVALID_ARG;
   if (!supported_head_dim(head_dim)) return PKV_ERR_UNSUPPORTED;
   if (q_dtype == PKV_F32 || !decode_pair_ok(q_dtype, cache_dtype)) return PKV_ERR_UNSUPPORTED;
   if (max_context_len > PKV_MAX_PREFILL_CONTEXT) return PKV_ERR_UNSUPPORTED;

@@ -30,8 +30,17 @@
 //    when both operands use the same permutation, so each lane's 8 P values
 //    (keys 4j..4j+3 of two 16-key tiles) meet the V values of the same keys.
 //  * Online softmax in log2 units per row; the running maximum moves only
-//    when a row's maximum grows by more than 2^8, so output rescales are
-//    rare.  The matrix phases run at raised wave priority.
+//    when a row's maximum grows by more than 2^8.  Each lane compares its own
+//    raw scores with a raw threshold, so the cross-lane maximum is only taken
+//    when some score passes it.  The stage loop runs in a fast form that
+//    never rescales the output (a row's first maximum is set while its output
+//    is still zero); a wave whose row maximum grows past the threshold
+//    leaves it and finishes its keys in a second form that rescales.  The
+//    fast loop then carries no conditional update of the accumulators, which
+//    the register allocator otherwise pays for with copies on every stage.
+//  * Row sums of P (16-bit caches) come from the matrix cores: one extra
+//    MFMA per half-stage multiplies P by a column of ones.
+//  * The matrix phases run at raised wave priority.
 //  * The causal diagonal bounds each workgroup's key loop; stages entirely
 //    below it need no mask.
 //  * Workgroups of one (sequence, KV head) are placed on one XCD so they
@@ -305,15 +314,23 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
 
   // ---- output state ----------------------------------------------------------------
   float4_t o[CTILES][DT];
-  float m[CTILES], lsum[CTILES];
+  // Row sums of P: 16-bit caches add them on the matrix cores, as P times a
+  // column of ones (osum: lane (c, j) register rr holds row 4j + rr, as in o,
+  // and sums the 16-bit P that meets V); quantised caches, whose P operand
+  // carries the V scales, add the fp32 values in lsum (a lane's share of row c).
+  float4_t osum[CTILES];
+  float m[CTILES], lsum[CTILES], rt[CTILES];
 #pragma unroll
   for (int ct = 0; ct < CTILES; ++ct) {
     m[ct] = kNegInf;
+    rt[ct] = kNegInf;
     lsum[ct] = 0.0f;
+    osum[ct] = float4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) o[ct][dt] = float4_t{0.f, 0.f, 0.f, 0.f};
   }
-  const float sl = a.scale * kLog2eP;
+  const float sl = a.scale * kLog2eP;       // > 0: the host refuses other scales
+  const float inv_sl = 1.0f / sl;
   const uint8_t* kpool = static_cast<const uint8_t*>(a.k_pool);
   const uint8_t* vpool = static_cast<const uint8_t*>(a.v_pool);
 
@@ -327,10 +344,18 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
   auto vaddr = [&](int r, int q, int h) -> int { return kaddr(r, q) + 8 * h; };
 
   // One stage (64 keys from s * 64) held in LDS at kbuf / vbuf.
-  auto compute = [&](const uint8_t* kbuf, const uint8_t* vbuf, int s) {
+  // One stage from half hv0 on.  The fast form (kSlow false) never rescales
+  // the output: when a row that already holds output needs a new maximum it
+  // returns the half it stopped at, before changing anything for that half,
+  // and the caller finishes the work with the slow form, which rescales.
+  // Returns -1 when the stage is done.
+  auto compute = [&](auto slow_tag, const uint8_t* kbuf, const uint8_t* vbuf, int s, int hv0)
+                     __attribute__((always_inline)) -> int {
+      constexpr bool kSlow = decltype(slow_tag)::value;
       // the stage in two halves of 32 keys: S^T, softmax, then P V for each
 #pragma unroll
       for (int hv = 0; hv < 2; ++hv) {
+        if (hv < hv0) continue;
         const int kb = s * kPfKeys + 32 * hv;
         const bool masked = kb + 32 > free_end;
 
@@ -380,7 +405,10 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
         // by more than kRebase: probabilities exp2(s*sl - m) stay below
         // 2^kRebase and the output and sum are rescaled far less often (the
         // final division uses the same m for both, so the result is the same).
-        float mxs[CTILES];
+        // A row's scores are spread over 4 lanes; each lane compares its own
+        // raw scores with rt = (m + kRebase) / sl (sl > 0), and only when one
+        // of them is above it does the wave take row maxima across lanes.
+        float mxr[CTILES];
         bool need = false;
 #pragma unroll
         for (int ct = 0; ct < CTILES; ++ct) {
@@ -389,39 +417,56 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, st[kt][ct][rr]);
-          mxs[ct] = cmax4(mx) * sl;
-          need |= mxs[ct] > m[ct] + kRebase;
+          mxr[ct] = mx;
+          need |= mx > rt[ct];
         }
         if (__any(need)) {
+          if constexpr (!kSlow) {
+            // a row with a finite maximum holds output: that needs a rescale
+            bool held = false;
 #pragma unroll
-          for (int ct = 0; ct < CTILES; ++ct) {
-            const float mnew = mxs[ct] > m[ct] + kRebase ? mxs[ct] : m[ct];
-            const float alpha = __builtin_amdgcn_exp2f(m[ct] - mnew);     // 1 for rows that keep m
-            m[ct] = mnew;
-            lsum[ct] *= alpha;
-            float ar[4];
+            for (int ct = 0; ct < CTILES; ++ct) held |= mxr[ct] > rt[ct] && m[ct] != kNegInf;
+            if (__any(held)) return hv;
+            // first keys of rows with nothing yet (output and sum are zero):
+            // only the maximum is set
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) ar[rr] = lane_value(alpha, 4 * j + rr);
+            for (int ct = 0; ct < CTILES; ++ct) {
+              const float mxs = cmax4(mxr[ct]) * sl;
+              const float mnew = mxs > m[ct] + kRebase ? mxs : m[ct];
+              m[ct] = mnew;
+              rt[ct] = (mnew + kRebase) * inv_sl;
+            }
+          } else {
 #pragma unroll
-            for (int dt = 0; dt < DT; ++dt)
+            for (int ct = 0; ct < CTILES; ++ct) {
+              const float mxs = cmax4(mxr[ct]) * sl;
+              const float mnew = mxs > m[ct] + kRebase ? mxs : m[ct];
+              const float alpha = mnew == m[ct] ? 1.0f : __builtin_amdgcn_exp2f(m[ct] - mnew);
+              m[ct] = mnew;
+              rt[ct] = (mnew + kRebase) * inv_sl;
+              lsum[ct] *= alpha;
+              float ar[4];
 #pragma unroll
-              for (int rr = 0; rr < 4; ++rr) o[ct][dt][rr] *= ar[rr];
+              for (int rr = 0; rr < 4; ++rr) ar[rr] = lane_value(alpha, 4 * j + rr);
+#pragma unroll
+              for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) o[ct][dt][rr] *= ar[rr];
+#pragma unroll
+              for (int rr = 0; rr < 4; ++rr) osum[ct][rr] *= ar[rr];
+            }
           }
         }
         u32x4 pop[CTILES];
 #pragma unroll
         for (int ct = 0; ct < CTILES; ++ct) {
           float p[2][4];
-          float ps = 0.0f;
 #pragma unroll
           for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-              p[kt][rr] = __builtin_amdgcn_exp2f(fmaf(st[kt][ct][rr], sl, -m[ct]));
-              ps += p[kt][rr];
-            }
-          lsum[ct] += ps;
+            for (int rr = 0; rr < 4; ++rr) p[kt][rr] = __builtin_amdgcn_exp2f(fmaf(st[kt][ct][rr], sl, -m[ct]));
           if constexpr (kConv) {
+            lsum[ct] += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) + ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
               const float4 vsc = *reinterpret_cast<const float4*>(sm_vs + 32 * hv + kt * 16 + 4 * j);
@@ -456,8 +501,14 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
 #pragma unroll
           for (int ct = 0; ct < CTILES; ++ct) o[ct][dt] = mfma32<QT>(pop[ct], vop, o[ct][dt]);
         }
+        if constexpr (!kConv) {
+          constexpr uint32_t kOnes = std::is_same<QT, BF16>::value ? 0x3F803F80u : 0x3C003C00u;   // 1.0, 1.0
+#pragma unroll
+          for (int ct = 0; ct < CTILES; ++ct) osum[ct] = mfma32<QT>(pop[ct], u32x4{kOnes, kOnes, kOnes, kOnes}, osum[ct]);
+        }
         __builtin_amdgcn_s_setprio(0);
       }
+      return -1;
   };
 
   if constexpr (kConv) {
@@ -517,13 +568,29 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
       if (tid < kPfKeys) sm_ks[tid] = io.ks;
       else if (tid < 2 * kPfKeys) sm_vs[tid - kPfKeys] = io.ks;
     };
+    const uint8_t* kb8 = reinterpret_cast<const uint8_t*>(sm_k);
+    const uint8_t* vb8 = reinterpret_cast<const uint8_t*>(sm_v);
     load_stage(0);
-    for (int s = 0; s < nstages; ++s) {
+    int s = 0, hv = -1;
+    for (; s < nstages; ++s) {
       store_stage();
       __syncthreads();
       if (s + 1 < nstages) load_stage(s + 1);
-      compute(reinterpret_cast<const uint8_t*>(sm_k), reinterpret_cast<const uint8_t*>(sm_v), s);
+      hv = compute(std::false_type{}, kb8, vb8, s, 0);
+      if (hv >= 0) break;
       __syncthreads();   // every wave is done with this stage's LDS
+    }
+    if (hv >= 0) {
+      // a row's maximum grew: the rest of the keys with rescaling
+      compute(std::true_type{}, kb8, vb8, s, hv);
+      __syncthreads();
+      for (++s; s < nstages; ++s) {
+        store_stage();
+        __syncthreads();
+        if (s + 1 < nstages) load_stage(s + 1);
+        compute(std::true_type{}, kb8, vb8, s, 0);
+        __syncthreads();
+      }
     }
   } else {
     // ---- 16-bit caches: global -> LDS directly, two buffers ----------------------
@@ -564,32 +631,56 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
       for (int idx = lane; idx < max(rows, 0) * CH; idx += kWave)
         *reinterpret_cast<u32x4*>(vdst + (first + idx / CH) * IO::row_bytes + 16 * (idx % CH)) = u32x4{0u, 0u, 0u, 0u};
     };
-    auto step = [&](uint8_t* kc, uint8_t* vc, uint8_t* kn, uint8_t* vn, int s) {
+    auto step = [&](auto slow_tag, uint8_t* kc, uint8_t* vc, uint8_t* kn, uint8_t* vn, int s)
+                    __attribute__((always_inline)) -> int {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's loads of stage s landed
       if (s == nstages - 1) zero_tail(vc, s);
       __syncthreads();                                      // all of stage s is in LDS; stage s-1 is done
       if (s + 1 < nstages) dma(kn, vn, s + 1);
-      compute(kc, vc, s);
+      return compute(slow_tag, kc, vc, s, 0);
     };
     uint8_t* k0 = reinterpret_cast<uint8_t*>(sm_kd[0]);
     uint8_t* k1 = reinterpret_cast<uint8_t*>(sm_kd[1]);
     uint8_t* v0 = reinterpret_cast<uint8_t*>(sm_vd[0]);
     uint8_t* v1 = reinterpret_cast<uint8_t*>(sm_vd[1]);
     dma(k0, v0, 0);
-    for (int s = 0; s < nstages; s += 2) {
-      step(k0, v0, k1, v1, s);
-      if (s + 1 < nstages) step(k1, v1, k0, v0, s + 1);
+    int s = 0, hv = -1;
+    for (; s < nstages; s += 2) {
+      hv = step(std::false_type{}, k0, v0, k1, v1, s);
+      if (hv >= 0) break;
+      if (s + 1 < nstages) {
+        hv = step(std::false_type{}, k1, v1, k0, v0, s + 1);
+        if (hv >= 0) {
+          ++s;
+          break;
+        }
+      }
+    }
+    if (hv >= 0) {
+      // a row's maximum grew: finish stage s from half hv, then the rest of
+      // the keys with rescaling (same barriers per stage as above)
+      if (s & 1) compute(std::true_type{}, k1, v1, s, hv);
+      else compute(std::true_type{}, k0, v0, s, hv);
+      for (++s; s < nstages; ++s) {
+        if (s & 1) step(std::true_type{}, k1, v1, k0, v0, s);
+        else step(std::true_type{}, k0, v0, k1, v1, s);
+      }
     }
   }
 
   // ---- normalise and store -------------------------------------------------------
 #pragma unroll
   for (int ct = 0; ct < CTILES; ++ct) {
-    const float l = csum4(lsum[ct]);
-    const float inv = l > 0.0f ? 1.0f / l : 0.0f;
     float ir[4];
+    if constexpr (kConv) {
+      const float l = csum4(lsum[ct]);
+      const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
-    for (int rr = 0; rr < 4; ++rr) ir[rr] = lane_value(inv, 4 * j + rr);
+      for (int rr = 0; rr < 4; ++rr) ir[rr] = lane_value(inv, 4 * j + rr);
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) ir[rr] = osum[ct][rr] > 0.0f ? 1.0f / osum[ct][rr] : 0.0f;
+    }
 #pragma unroll
     for (int rr = 0; rr < 4; ++rr) {
       const int r = r0 + wave * SH::rows_per_wave + ct * 16 + 4 * j + rr;

@@ -318,3 +318,15 @@ def test_block_size_is_16_or_32():
                                          4, 128, 0.125, pkv.PKV_BF16, pkv.PKV_BF16, 0, None, 0, None) == 0
     assert lib.paged_attention_decode_bs(None, None, None, None, None, None, None, None, 0, 4, 1, 64, 4, 32,
                                          4, 129, 0.125, pkv.PKV_BF16, pkv.PKV_BF16, 0, None, 0, None) == -1
+
+
+def test_prefill_refuses_non_positive_scale():
+    # the prefill kernel compares raw scores against a threshold scaled by
+    # 1/scale, so the host refuses a scale that is not positive and finite
+    # (a valid call with no tokens returns 0 before any launch)
+    lib = pkv._lib.lib()
+    args = lambda scale: (None, None, None, None, None, None, None, None, None, 0, 0, 4, 1, 64, 4, 16, 4, 64, 0,
+                          scale, pkv.PKV_BF16, pkv.PKV_BF16, None)
+    assert lib.paged_attention_prefill_bs(*args(0.125)) == 0
+    for bad in (0.0, -0.125, float("inf"), float("nan")):
+        assert lib.paged_attention_prefill_bs(*args(bad)) == -1
