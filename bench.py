@@ -66,8 +66,8 @@ def parse():
                     help="from rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE counter CSVs of this bench and of "
                          "--calibrate-copy, write profiles/decode_<workload>_traffic.json and exit")
     ap.add_argument("--probe-read", action="store_true",
-                    help="only measure a cold read-bandwidth reference (a torch sum over 256 MiB per launch, "
-                         "rotating through 4 GiB) and exit")
+                    help="only measure a cold HBM reference (device-to-device copies of 128 MiB, 256 MiB of "
+                         "traffic per launch, rotating through 16 slices of a 2 GiB source) and exit")
     ap.add_argument("--event-every", type=int, default=8,
                     help="bracket every Nth layer's decode call with HIP events (default 8: each event pair "
                          "adds a few microseconds of GPU time, so the calls in between run undisturbed)")
