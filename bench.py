@@ -380,7 +380,8 @@ def main():
             if e:
                 e[1].record(stream)
             rc = lib.paged_attention_merge_partials_bs(o_ptr, d_lens.data_ptr(), B, hq, hkv, D, bs, mb, max_len,
-                                                       q_code, args.partition_size, ws_ptr, ws_bytes, sp)
+                                                       q_code, cache_code, args.partition_size, ws_ptr, ws_bytes,
+                                                       sp)
             if rc:
                 raise pkv.PagedKVError(rc, "paged_attention_merge_partials")
             if e:

@@ -152,7 +152,10 @@ int pkv_copy_blocks_bs(void* k_pool, void* v_pool, float* k_scale, float* v_scal
 /*
  * pkv_decode_partition_size - the partition length (tokens, a multiple of 16)
  * paged_attention_decode uses when called with partition_size == 0, and the
- * resulting partitions per sequence for max_context_len.  Host only.
+ * resulting partitions per sequence for max_context_len.  The plan fills
+ * the 256 CUs with at least one workgroup each (two for int8 K + int4 V
+ * caches, whose decoding is heaviest per byte) and at most 64 blocks per
+ * wave.  Host only.
  */
 int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                               int max_context_len, pkv_dtype cache_dtype,
@@ -280,7 +283,8 @@ int paged_attention_decode_append_bs(void* out, const void* q, const void* k_new
  * output rows.  paged_attention_merge_partials then merges those states
  * into the output rows (log-sum-exp); it
  * must get the same num_seqs, head counts, head_dim, max_context_len,
- * partition_size and workspace, on the same stream.  The pair gives exactly
+ * cache_dtype, partition_size and workspace, on the same stream (the
+ * automatic partition plan depends on the cache format).  The pair gives exactly
  * the bytes of the one-call form.  When nothing is split, the merge call
  * does nothing.
  */
@@ -297,8 +301,8 @@ int paged_attention_decode_append_partials(void* out, const void* q, const void*
 int paged_attention_merge_partials(void* out, const int32_t* context_lens,
                                    int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                    int max_blocks_per_seq, int max_context_len, pkv_dtype q_dtype,
-                                   int partition_size, void* workspace, size_t workspace_bytes,
-                                   void* stream);
+                                   pkv_dtype cache_dtype, int partition_size, void* workspace,
+                                   size_t workspace_bytes, void* stream);
 
 int paged_attention_decode_append_partials_bs(void* out, const void* q, const void* k_new, const void* v_new,
                                               void* k_pool, void* v_pool, float* k_scale, float* v_scale,
@@ -313,8 +317,8 @@ int paged_attention_decode_append_partials_bs(void* out, const void* q, const vo
 int paged_attention_merge_partials_bs(void* out, const int32_t* context_lens,
                                       int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                                       int block_size, int max_blocks_per_seq, int max_context_len,
-                                      pkv_dtype q_dtype, int partition_size, void* workspace,
-                                      size_t workspace_bytes, void* stream);
+                                      pkv_dtype q_dtype, pkv_dtype cache_dtype, int partition_size,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * paged_attention_prefill - chunked prefill: each sequence's chunk of new

@@ -299,17 +299,18 @@ def paged_attention_decode_append_partials(out, q, k_new, v_new, k_pool, v_pool,
 
 
 def paged_attention_merge_partials(out: torch.Tensor, context_lens: torch.Tensor, num_kv_heads: int,
-                                   max_blocks_per_seq: int, max_context_len: int, partition_size: int = 0,
-                                   workspace: Optional[torch.Tensor] = None, stream=None,
-                                   block_size: int = BLOCK_SIZE) -> torch.Tensor:
+                                   max_blocks_per_seq: int, max_context_len: int, cache_dtype: int,
+                                   partition_size: int = 0, workspace: Optional[torch.Tensor] = None,
+                                   stream=None, block_size: int = BLOCK_SIZE) -> torch.Tensor:
     """Second launch of the split form: merge the partition states
-    (``block_size``: that of the pool the first launch read)."""
+    (``block_size`` and ``cache_dtype``, a library format code such as
+    :func:`cache_code` returns: those of the pool the first launch read)."""
     B, hq, d = (int(x) for x in out.shape)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.lib().paged_attention_merge_partials_bs(
         _ptr(out), _ptr(context_lens), B, hq, num_kv_heads, d, int(block_size), max_blocks_per_seq,
-        int(max_context_len), dtype_code(out.dtype), int(partition_size), _ptr(workspace), ws_bytes,
-        _stream(stream)), "paged_attention_merge_partials_bs")
+        int(max_context_len), dtype_code(out.dtype), int(cache_dtype), int(partition_size), _ptr(workspace),
+        ws_bytes, _stream(stream)), "paged_attention_merge_partials_bs")
     return out
 
 

@@ -63,7 +63,7 @@ SIGNATURES = {
                                                        c_int, c_float, c_int, c_int, c_int, c_int, c_void_p,
                                                        c_size_t, c_void_p]),
     "paged_attention_merge_partials": (c_int, [c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int,
-                                               c_int, c_int, c_void_p, c_size_t, c_void_p]),
+                                               c_int, c_int, c_int, c_void_p, c_size_t, c_void_p]),
     "paged_attention_prefill": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p,
                                         c_void_p, c_void_p, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int,
                                         c_int, c_float, c_int, c_int, c_void_p]),

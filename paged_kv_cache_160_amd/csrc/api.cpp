@@ -40,9 +40,9 @@ bool decode_pair_ok(pkv_dtype q, pkv_dtype c) {
 }
 
 int resolve_partitions(int num_seqs, int num_kv_heads, int max_context_len, int partition_size,
-                       int* ps_out, int* np_out) {
+                       pkv_dtype cache_dtype, int* ps_out, int* np_out) {
   int ps = partition_size;
-  if (ps == 0) ps = pkv::choose_partition_size(num_seqs, num_kv_heads, max_context_len);
+  if (ps == 0) ps = pkv::choose_partition_size(num_seqs, num_kv_heads, max_context_len, cache_dtype);
   if (ps <= 0 || ps % kTile != 0 || ps > PKV_MAX_PARTITION_TOKENS) return PKV_ERR_INVALID_ARG;
   int64_t np = (static_cast<int64_t>(max_context_len) + ps - 1) / ps;
   if (np < 1) np = 1;
@@ -153,21 +153,21 @@ int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, i
                               int max_context_len, pkv_dtype cache_dtype, int* partition_size_out,
                               int* num_partitions_out) {
   (void)head_dim;
-  (void)cache_dtype;
-  if (!partition_size_out || !num_partitions_out) return PKV_ERR_INVALID_ARG;
+  if (!partition_size_out || !num_partitions_out || !valid_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
   if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, 64, max_context_len))
     return PKV_ERR_INVALID_ARG;
-  return resolve_partitions(num_seqs, num_kv_heads, max_context_len, 0, partition_size_out,
+  return resolve_partitions(num_seqs, num_kv_heads, max_context_len, 0, cache_dtype, partition_size_out,
                             num_partitions_out);
 }
 
 size_t paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
                                       int head_dim, int max_context_len, int partition_size,
                                       pkv_dtype cache_dtype) {
-  (void)cache_dtype;
+  if (!valid_dtype(cache_dtype)) return 0;
   if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len)) return 0;
   int ps, np;
-  if (resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, &ps, &np) != PKV_OK)
+  if (resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, cache_dtype, &ps, &np) !=
+      PKV_OK)
     return 0;
   return workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, np).total;
 }
@@ -208,7 +208,7 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new, 
   if (slot_mapping && (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new))) return PKV_ERR_INVALID_ARG;
 
   int ps, np;
-  int rc = resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, &ps, &np);
+  int rc = resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, cache_dtype, &ps, &np);
   if (rc != PKV_OK) return rc;
   const WorkspaceLayout ws = workspace_layout(num_seqs, num_q_heads, num_kv_heads, head_dim, np);
   if (ws.total > 0 && (!workspace || workspace_bytes < ws.total || !aligned16(workspace)))
@@ -341,9 +341,10 @@ int paged_attention_decode_append_partials(void* out, const void* q, const void*
 
 int paged_attention_merge_partials_bs(void* out, const int32_t* context_lens, int num_seqs, int num_q_heads,
                                       int num_kv_heads, int head_dim, int block_size, int max_blocks_per_seq,
-                                      int max_context_len, pkv_dtype q_dtype, int partition_size, void* workspace,
-                                      size_t workspace_bytes, void* stream) {
-  if (!valid_dtype(q_dtype) || !source_dtype(q_dtype)) return PKV_ERR_INVALID_ARG;
+                                      int max_context_len, pkv_dtype q_dtype, pkv_dtype cache_dtype,
+                                      int partition_size, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (!valid_dtype(q_dtype) || !source_dtype(q_dtype) || !valid_dtype(cache_dtype)) return PKV_ERR_INVALID_ARG;
   if (!decode_sizes_ok(num_seqs, num_q_heads, num_kv_heads, head_dim, max_context_len))
     return PKV_ERR_INVALID_ARG;
   if (max_blocks_per_seq <= 0 || !block_size_ok(block_size) ||
@@ -353,7 +354,7 @@ int paged_attention_merge_partials_bs(void* out, const int32_t* context_lens, in
   if (partition_size < 0 || partition_size % kTile != 0 || partition_size > PKV_MAX_PARTITION_TOKENS)
     return PKV_ERR_INVALID_ARG;
   int ps, np;
-  int rc = resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, &ps, &np);
+  int rc = resolve_partitions(num_seqs, num_kv_heads, max_context_len, partition_size, cache_dtype, &ps, &np);
   if (rc != PKV_OK) return rc;
   if (num_seqs == 0 || np == 1) return PKV_OK;       // nothing was split
   if (!out || !context_lens || !aligned16(out)) return PKV_ERR_INVALID_ARG;
@@ -384,11 +385,11 @@ int paged_attention_merge_partials_bs(void* out, const int32_t* context_lens, in
 
 int paged_attention_merge_partials(void* out, const int32_t* context_lens, int num_seqs, int num_q_heads,
                                    int num_kv_heads, int head_dim, int max_blocks_per_seq, int max_context_len,
-                                   pkv_dtype q_dtype, int partition_size, void* workspace,
+                                   pkv_dtype q_dtype, pkv_dtype cache_dtype, int partition_size, void* workspace,
                                    size_t workspace_bytes, void* stream) {
   return paged_attention_merge_partials_bs(out, context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                            PKV_BLOCK_SIZE, max_blocks_per_seq, max_context_len, q_dtype,
-                                           partition_size, workspace, workspace_bytes, stream);
+                                           cache_dtype, partition_size, workspace, workspace_bytes, stream);
 }
 
 int paged_attention_prefill_bs(void* out, const void* q, const void* k_pool, const void* v_pool,

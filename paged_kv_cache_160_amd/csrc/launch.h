@@ -78,6 +78,6 @@ struct PrefillArgs {
 int launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
 // Automatic partition length for a decode launch (tokens, multiple of 16).
-int choose_partition_size(int num_seqs, int num_kv_heads, int max_context_len);
+int choose_partition_size(int num_seqs, int num_kv_heads, int max_context_len, pkv_dtype cache_dtype);
 
 }  // namespace pkv

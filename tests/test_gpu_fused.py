@@ -105,13 +105,26 @@ def test_fused_step_with_copy_on_write():
     assert max_err(out, exp) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("ps,bs", [(0, 16), (64, 16), (0, 32), (64, 32)])
-def test_split_form_equals_one_call(ps, bs):
+SPLIT = [(0, 16, None), (64, 16, None), (0, 32, None), (64, 32, None), (0, 16, "int8_int4")]
+
+
+@pytest.mark.parametrize("ps,bs,cache", SPLIT, ids=[f"ps{c[0]}-bs{c[1]}-{c[2] or 'bf16'}" for c in SPLIT])
+def test_split_form_equals_one_call(ps, bs, cache):
     # paged_attention_decode_append_partials + paged_attention_merge_partials
-    # gives the bytes of paged_attention_decode_append (split and unsplit rows)
+    # gives the bytes of paged_attention_decode_append (split and unsplit
+    # rows).  The int8 + int4 case is sized so that the automatic plan of
+    # that format (two workgroups per CU) differs from a 16-bit cache's: the
+    # merge must resolve it from the cache format it is given.
     import paged_kv_cache_160_amd as pkv
-    case = ([700, 9, 1300, 64], 32, 8, 128, "bf16", None, None, ps)
-    say(f"[split] ps={ps} block size {bs}")
+    if cache is None:
+        case = ([700, 9, 1300, 64], 32, 8, 128, "bf16", None, None, ps)
+    else:
+        lens = [4100, 17, 4000, 2600, 4100, 300, 3900, 4096]
+        case = (lens, 32, 8, 128, "f32", cache, "bf16", ps)
+        plan_q = pkv.decode_partition_size(8, 32, 8, 128, 4100 + STEPS, pkv.PKV_BF16)
+        plan_c = pkv.decode_partition_size(8, 32, 8, 128, 4100 + STEPS, pkv.PKV_INT8_INT4)
+        assert plan_q[1] < plan_c[1], (plan_q, plan_c)
+    say(f"[split] ps={ps} block size {bs} cache {cache or 'bf16'}")
     w = wl.with_block_size(_make(case, seed=23), bs)
     w.decode_appends = STEPS
     ops = wl.setup_ops(w)
@@ -129,9 +142,10 @@ def test_split_form_equals_one_call(ps, bs):
         q = two.queries(step)
         out_b = torch.empty_like(q)
         out_b, ws = pkv.paged_attention_decode_append_partials(out_b, q, kd, vd, c.k[0], c.v[0], slot_t, bt, lens,
-                                                               max_len, partition_size=ps)
+                                                               max_len, k_scale=c.k_scale[0], v_scale=c.v_scale[0],
+                                                               partition_size=ps)
         pkv.paged_attention_merge_partials(out_b, lens, w.num_kv_heads, w.max_blocks_per_seq, max_len,
-                                           partition_size=ps, workspace=ws, block_size=bs)
+                                           c.cache_code, partition_size=ps, workspace=ws, block_size=bs)
         torch.cuda.synchronize()
         assert torch.equal(out_a.cpu(), out_b.cpu()), f"step {step}"
     for b in seqs:

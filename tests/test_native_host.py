@@ -309,8 +309,8 @@ def test_block_size_is_16_or_32():
     assert lib.pkv_copy_blocks_bs(None, None, None, None, None, 1, 1, 64, 4, 64, pkv.PKV_BF16, None) == -1
     assert lib.paged_attention_decode_bs(None, None, None, None, None, None, None, None, 1, 4, 1, 64, 4, 8,
                                          4, 64, 0.125, pkv.PKV_BF16, pkv.PKV_BF16, 0, None, 0, None) == -1
-    assert lib.paged_attention_merge_partials_bs(None, None, 1, 4, 1, 64, 48, 4, 64, pkv.PKV_BF16, 0, None, 0,
-                                                 None) == -1
+    assert lib.paged_attention_merge_partials_bs(None, None, 1, 4, 1, 64, 48, 4, 64, pkv.PKV_BF16, pkv.PKV_BF16, 0,
+                                                 None, 0, None) == -1
     assert lib.paged_attention_prefill_bs(None, None, None, None, None, None, None, None, None, 1, 1, 4, 1, 64, 4,
                                           8, 4, 64, 1, 0.125, pkv.PKV_BF16, pkv.PKV_BF16, None) == -1
     # 32-token blocks: max_context_len may reach 32 * max_blocks_per_seq, not more
