@@ -18,7 +18,9 @@ Score magnitudes stay near 30 log2 units (the spike aside, whose weight is
 fp32 tolerance.
 Each is decoded with one and with several partitions (the log-sum-exp merge
 then meets partition maxima hundreds of units apart), on every cache format,
-and prefilled on every format but f32 (which prefill does not take).
+and prefilled on every format but f32 (which prefill does not take).  A last
+prefill case puts waves of one workgroup in both forms of the kernel's stage
+loop (the fast one without rescales and the rescaling one).
 """
 import math
 
@@ -121,4 +123,36 @@ def test_prefill_adversarial_scores(fmt, src, qt):
     assert np.isfinite(got).all()
     err = max_err(got, exp)
     say(f"[softmax] prefill {fmt} max abs err {err:.3e}")
+    assert err <= TOL[fmt]
+
+
+@pytest.mark.parametrize("fmt,src,qt", [FORMATS[2], FORMATS[3]], ids=["bf16", "fp8_e4m3"])
+def test_prefill_waves_in_both_loop_forms(fmt, src, qt):
+    # A prefill workgroup holds 128 query rows, 32 per wave.  Here each
+    # workgroup's first wave (chunk positions 32k .. 32k+7 with 4 heads per
+    # KV head) gets the one-hot queries whose row maxima keep growing, so it
+    # leaves the kernel's fast stage loop for the rescaling one; every other
+    # row gets a zero query (all scores 0, the maximum never moves), so its
+    # wave stays in the fast loop.  Both kinds of wave meet at the same
+    # barriers; the result still matches the oracle.
+    L, n = 700, 100
+    say(f"[softmax] prefill mixed loop forms {fmt}")
+    K, V = _rows(L, seed=41)
+    cache, Kc, Vc = _cache(fmt, K, V, src)
+    qf = _queries(n, torch.float32)
+    rows_per_wave = 32 // G                       # chunk positions per wave
+    keep = np.array([(p % (4 * rows_per_wave)) < rows_per_wave for p in range(n)])
+    qf[torch.from_numpy(~keep)] = 0.0
+    q = qf.to(qt).to("cuda")
+    out = torch.full_like(q, float("nan"))
+    tables, lens, max_len = cache.block_tables([0])
+    qs = torch.tensor([0, n], dtype=torch.int32, device="cuda")
+    pkv.paged_attention_prefill(out, q, cache.k[0], cache.v[0], tables, lens, qs, max_len, n,
+                                k_scale=cache.k_scale[0], v_scale=cache.v_scale[0])
+    torch.cuda.synchronize()
+    got = out_to_f64(out)
+    exp = prefill.prefill_rows(q.float().cpu().numpy(), Kc, Vc, 1.0 / math.sqrt(D))
+    assert np.isfinite(got).all()
+    err = max_err(got, exp)
+    say(f"[softmax] prefill mixed {fmt} max abs err {err:.3e}")
     assert err <= TOL[fmt]
