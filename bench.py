@@ -105,6 +105,12 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
+def percentiles(times_us):
+    t = sorted(times_us)
+    n = len(t)
+    return {"median_us": t[n // 2], "p10_us": t[n // 10], "p90_us": t[min(n - 1, (9 * n) // 10)], "n": n}
+
+
 def load_traffic(workload_name: str):
     """HBM bytes per decode launch from a committed rocprofv3 counter summary,
     if it was taken on the current kernel source (else None)."""
@@ -413,7 +419,43 @@ def main():
     log(f"[bench] {args.steps} steps in {elapsed * 1e3:.2f} ms; attention kernel avg {kern_s * 1e6:.2f} us "
         f"({achieved:.0f} GB/s algorithmic); whole decode call {call_s * 1e6:.2f} us "
         f"({bytes_per_call / call_s / 1e9:.0f} GB/s); {value / 1e9:.3f} G KV tokens/s")
+    kern_pct = percentiles([a.elapsed_time(b) * 1e3 for a, b, _ in ev.values()])
+    log(f"[bench] attention kernel (events) median {kern_pct['median_us']:.2f} us, p10 {kern_pct['p10_us']:.2f}, "
+        f"p90 {kern_pct['p90_us']:.2f} over {len(ev)} sampled calls")
     traffic = load_traffic(w.name)
+
+    # Side measurements after the timed region (not part of the value): the
+    # decode step's cache write on its own (B rows into layer 0, the slots of
+    # the last step) and a copy-on-write copy of 8 whole blocks of sequence 0
+    # into free blocks, 100 calls each, HIP events around every call.
+    def time_calls(fn, n=100):
+        evs_ = []
+        for _ in range(n):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc_ = fn()
+            e1.record(stream)
+            if rc_:
+                raise pkv.PagedKVError(rc_, "side measurement")
+            evs_.append((e0, e1))
+        torch.cuda.synchronize()
+        return percentiles([a.elapsed_time(b) * 1e3 for a, b in evs_])
+
+    kp0, vp0, ksp0, vsp0 = pools[0]
+    side = {"append_b_rows": time_calls(lambda: lib.kv_cache_append_bs(
+        knew.data_ptr(), vnew.data_ptr(), kp0, vp0, ksp0, vsp0, d_slots.data_ptr(), B, hkv, D, w.num_blocks, bs,
+        src_code, cache_code, sp))}
+    used_tables, _ = cache.alloc.block_tables(seqs, mb)
+    used = set(int(x) for x in used_tables.flatten().tolist() if x >= 0)
+    free_blocks = [blk for blk in range(w.num_blocks) if blk not in used][:8]
+    if len(free_blocks) == 8:
+        pairs_t = torch.tensor([[int(used_tables[0, i]), free_blocks[i]] for i in range(8)], dtype=torch.int32,
+                               device=dev)
+        side["cow_copy_8_blocks"] = time_calls(lambda: lib.pkv_copy_blocks_bs(
+            kp0, vp0, ksp0, vsp0, pairs_t.data_ptr(), 8, hkv, D, w.num_blocks, bs, cache_code, sp))
+    for k_, v_ in side.items():
+        log(f"[bench] {k_}: median {v_['median_us']:.2f} us (p10 {v_['p10_us']:.2f}, p90 {v_['p90_us']:.2f}), "
+            f"events around each call")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -442,7 +484,9 @@ def main():
         "achieved_hbm_gbps": achieved,
         "pct_of_peak": 100.0 * achieved / HBM_PEAK_GBPS,
         "attention_kernel_us": kern_s * 1e6,
+        "attention_kernel_us_percentiles": kern_pct,
         "decode_call_us": call_s * 1e6,
+        "side_kernels_us": side,
         "decode_call_hbm_gbps": bytes_per_call / call_s / 1e9,
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -493,6 +537,19 @@ def cpu_baseline(w, budget_s: float):
     allowed = len(os.sched_getaffinity(0))
     log(f"[cpu] oracle: {seqs_done} sequence decodes, {tokens} KV tokens in {wall:.1f}s "
         f"({tokens / wall / 1e6:.2f} M KV tokens/s), {busy:.1f} cores busy on average")
+    # the same loop on one thread, for a short sample
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        t1 = time.perf_counter()
+        tokens1 = 0
+        done1 = 0
+        while time.perf_counter() - t1 < min(3.0, budget_s) or done1 < 1:
+            b, K, V = pre[done1 % n_pre]
+            attention.attend(q[b], K, V, scale)
+            tokens1 += K.shape[0]
+            done1 += 1
+        wall1 = time.perf_counter() - t1
+    log(f"[cpu] oracle on one thread: {done1} sequence decodes, {tokens1 / wall1 / 1e6:.2f} M KV tokens/s")
     return {
         "value": tokens / wall, "unit": "KV tokens/s", "cores": max(1, round(busy)),
         "kind": "oracle",
@@ -500,6 +557,8 @@ def cpu_baseline(w, budget_s: float):
                    f"L={w.context_lens[0]}) cycling over the first {n_pre} sequences of layer 0 of "
                    f"{w.name}; fp64 numpy; rows generated and dequantised before timing; "
                    f"{busy:.2f} cores busy on average, {allowed} allowed, BLAS threads {blas}"),
+        "single_thread_value": tokens1 / wall1,
+        "single_thread_sample": f"{done1} of the same decodes with BLAS limited to one thread",
     }
 
 
