@@ -56,7 +56,14 @@
 namespace pkv {
 namespace {
 
-constexpr int kPfWaves = 4;
+#ifndef PKV_PREFILL_WAVES
+#define PKV_PREFILL_WAVES 4    // waves per workgroup (4 or 8)
+#endif
+constexpr int kPfWaves = PKV_PREFILL_WAVES;
+#ifndef PKV_PREFILL_BUFFERS
+#define PKV_PREFILL_BUFFERS (PKV_PREFILL_WAVES == 8 ? 3 : 2)   // K/V stage buffers (16-bit caches)
+#endif
+constexpr int kPfBufs = PKV_PREFILL_BUFFERS;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kPfKeys = 64;                                  // keys per stage
 constexpr int kPfMaxBlocks = PKV_MAX_PREFILL_CONTEXT / kTileTokens;
@@ -216,7 +223,8 @@ struct LdsSwz {
 };
 
 template <typename QT, typename KT, typename VT, int D, int CTILES>
-__global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2 : 1)
+    paged_prefill_kernel(PrefillArgs a) {
   using IO = StageIO<KT, VT, D>;
   using SH = PfShape<CTILES>;
   constexpr bool kConv = KT::quantised;      // codes converted on the way into LDS
@@ -230,8 +238,8 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
   constexpr int kDmaChunks = kConv ? 1 : kPfKeys * IO::row_bytes / 16;
   __shared__ __attribute__((aligned(16))) uint16_t sm_k[kPadElems];
   __shared__ __attribute__((aligned(16))) uint16_t sm_v[kPadElems];
-  __shared__ u32x4 sm_kd[2][kDmaChunks];
-  __shared__ u32x4 sm_vd[2][kDmaChunks];
+  __shared__ u32x4 sm_kd[kPfBufs][kDmaChunks];
+  __shared__ u32x4 sm_vd[kPfBufs][kDmaChunks];
   __shared__ float sm_ks[kPfKeys];
   __shared__ float sm_vs[kPfKeys];
   __shared__ int sm_ids[kPfMaxBlocks];
@@ -594,12 +602,13 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
     }
   } else {
     // ---- 16-bit caches: global -> LDS directly, two buffers ----------------------
-    // Wave w moves block w of each stage (rows 16w .. 16w+15): kInsts
-    // instructions per tensor, lane i of instruction n filling stage chunk
-    // 64n + i, i.e. row (64n+i)/CH at swizzled position (64n+i)%CH.
+    // Wave w moves rows kPfKeys/kPfWaves * w ... of each stage (a whole
+    // block with 4 waves, half a block with 8): kInsts instructions per
+    // tensor, lane i of instruction n filling stage chunk 64n + i, i.e. row
+    // (64n+i)/CH at swizzled position (64n+i)%CH.
     constexpr int CH = IO::row_bytes / 16;                  // chunks per row
-    constexpr int kInsts = CH / 4;
-    static_assert(kPfKeys * CH == kPfWaves * kInsts * kWave, "one block per wave");
+    constexpr int kInsts = kPfKeys * CH / (kPfWaves * kWave);
+    static_assert(kPfKeys * CH == kPfWaves * kInsts * kWave, "a stage splits evenly over the waves");
     int lane_off[kInsts];
 #pragma unroll
     for (int k = 0; k < kInsts; ++k) {
@@ -611,7 +620,7 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
     auto dma = [&](uint8_t* kdst, uint8_t* vdst, int s) {
       // rows past the context (last stage) read the sequence's last block
       // and are zeroed after they land
-      const int id = sm_ids[min(4 * s + wave, nblk - 1)];
+      const int id = sm_ids[min(4 * s + wave * 4 / kPfWaves, nblk - 1)];
       const int64_t base = static_cast<int64_t>(id + g_tile) * IO::tile_bytes;
 #pragma unroll
       for (int k = 0; k < kInsts; ++k) {
@@ -626,45 +635,55 @@ __global__ void __launch_bounds__(kPfThreads, CTILES <= 2 ? 2 : 1) paged_prefill
     // loaded them (after its own loads landed): P is 0 there, and 0 times a
     // stale NaN would still be NaN.  K needs no care: those keys are masked.
     auto zero_tail = [&](uint8_t* vdst, int s) {
-      const int first = max(key_end - s * kPfKeys, 16 * wave);
-      const int rows = 16 * wave + 16 - first;
+      constexpr int kRowsPerWave = kPfKeys / kPfWaves;        // stage rows this wave loaded
+      const int first = max(key_end - s * kPfKeys, kRowsPerWave * wave);
+      const int rows = kRowsPerWave * wave + kRowsPerWave - first;
       for (int idx = lane; idx < max(rows, 0) * CH; idx += kWave)
         *reinterpret_cast<u32x4*>(vdst + (first + idx / CH) * IO::row_bytes + 16 * (idx % CH)) = u32x4{0u, 0u, 0u, 0u};
     };
-    auto step = [&](auto slow_tag, uint8_t* kc, uint8_t* vc, uint8_t* kn, uint8_t* vn, int s)
-                    __attribute__((always_inline)) -> int {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's loads of stage s landed
-      if (s == nstages - 1) zero_tail(vc, s);
+    // kPfBufs stage buffers: the loads of stage s + kPfBufs - 1 go out after
+    // the barrier that ends stage s - 1, into the buffer that stage used.
+    constexpr int kLoads = 2 * kInsts;                      // this wave's loads per stage
+    auto kbuf = [&](int i) { return reinterpret_cast<uint8_t*>(sm_kd[i]); };
+    auto vbuf = [&](int i) { return reinterpret_cast<uint8_t*>(sm_vd[i]); };
+    auto step = [&](auto slow_tag, int s, int cur) __attribute__((always_inline)) -> int {
+      // this wave's loads of stage s landed (those of later stages may fly)
+      if (kPfBufs == 3 && s + 1 < nstages) {
+        static_assert(kPfBufs == 2 || kLoads == 2 || kLoads == 4 || kLoads == 8, "wait count");
+        if constexpr (kLoads == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        else if constexpr (kLoads == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      } else {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      if (s == nstages - 1) zero_tail(vbuf(cur), s);
       __syncthreads();                                      // all of stage s is in LDS; stage s-1 is done
-      if (s + 1 < nstages) dma(kn, vn, s + 1);
-      return compute(slow_tag, kc, vc, s, 0);
+      if (s + kPfBufs - 1 < nstages) {
+        const int nb = (cur + kPfBufs - 1) % kPfBufs;
+        dma(kbuf(nb), vbuf(nb), s + kPfBufs - 1);
+      }
+      return compute(slow_tag, kbuf(cur), vbuf(cur), s, 0);
     };
-    uint8_t* k0 = reinterpret_cast<uint8_t*>(sm_kd[0]);
-    uint8_t* k1 = reinterpret_cast<uint8_t*>(sm_kd[1]);
-    uint8_t* v0 = reinterpret_cast<uint8_t*>(sm_vd[0]);
-    uint8_t* v1 = reinterpret_cast<uint8_t*>(sm_vd[1]);
-    dma(k0, v0, 0);
+#pragma unroll
+    for (int i = 0; i + 1 < kPfBufs; ++i)
+      if (i < nstages) dma(kbuf(i), vbuf(i), i);
     int s = 0, hv = -1;
-    for (; s < nstages; s += 2) {
-      hv = step(std::false_type{}, k0, v0, k1, v1, s);
-      if (hv >= 0) break;
-      if (s + 1 < nstages) {
-        hv = step(std::false_type{}, k1, v1, k0, v0, s + 1);
-        if (hv >= 0) {
+    while (s < nstages) {
+#pragma unroll
+      for (int u = 0; u < kPfBufs; ++u) {                   // stage s uses buffer u = s % kPfBufs
+        if (s < nstages) {
+          hv = step(std::false_type{}, s, u);
+          if (hv >= 0) break;
           ++s;
-          break;
         }
       }
+      if (hv >= 0) break;
     }
     if (hv >= 0) {
       // a row's maximum grew: finish stage s from half hv, then the rest of
       // the keys with rescaling (same barriers per stage as above)
-      if (s & 1) compute(std::true_type{}, k1, v1, s, hv);
-      else compute(std::true_type{}, k0, v0, s, hv);
-      for (++s; s < nstages; ++s) {
-        if (s & 1) step(std::true_type{}, k1, v1, k0, v0, s);
-        else step(std::true_type{}, k0, v0, k1, v1, s);
-      }
+      compute(std::true_type{}, kbuf(s % kPfBufs), vbuf(s % kPfBufs), s, hv);
+      for (++s; s < nstages; ++s) step(std::true_type{}, s, s % kPfBufs);
     }
   }
 
