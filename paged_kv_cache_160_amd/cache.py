@@ -133,16 +133,28 @@ class PagedKVCache:
         fill (large enough; reusing them avoids pinning new memory on every
         call, which costs more than the copies): a buffer handed back in
         through ``back_in`` may be reused by a later call, since the current
-        stream has waited for its copy.  An allocator error raises after the
-        swaps already made."""
+        stream has waited for its copy.  Host buffers (type, pinning, size,
+        block count) are checked before anything changes; an allocator error
+        raises after the swaps already made."""
         back_in = back_in or {}
+        out_host = out_host or {}
         tensors = self._tensors()
         bb = [t[0].numel() * t.element_size() for t in tensors]      # bytes of one block of each tensor
+
+        # host buffers are checked before the allocator changes anything
+        def check_host(s_, host, n):
+            if host.dtype != torch.uint8 or not host.is_pinned() or host.numel() < n * sum(bb):
+                raise ValueError(f"host buffer of sequence {s_} must be pinned uint8 of >= {n * sum(bb)} bytes")
+
+        for s_, (host, n) in back_in.items():
+            if n != -(-self.alloc.seq_len(s_) // self.block_size):
+                raise ValueError(f"host buffer of sequence {s_} does not match its length")
+            check_host(s_, host, n)
+        for s_, host in out_host.items():
+            if s_ in out_seqs:
+                check_host(s_, host, -(-self.alloc.seq_len(s_) // self.block_size))
         outs = {s_: self.alloc.swap_out(s_) for s_ in out_seqs}
         ins = {s_: self.alloc.swap_in(s_) for s_ in back_in}
-        for s_, blocks in ins.items():
-            if back_in[s_][1] != len(blocks):
-                raise ValueError(f"host buffer of sequence {s_} does not match its blocks")
         lib = _lib.lib()
         cur = torch.cuda.current_stream(self.device)
         if getattr(self, "_side", None) is None:
@@ -186,11 +198,9 @@ class PagedKVCache:
         gathered = torch.cuda.Event()
         gathered.record(cur)
         for s_, staging, n in staged:
-            host = (out_host or {}).get(s_)
+            host = out_host.get(s_)
             if host is None:
                 host = torch.empty(staging.numel(), dtype=torch.uint8, pin_memory=True)
-            elif host.dtype != torch.uint8 or not host.is_pinned() or host.numel() < staging.numel():
-                raise ValueError(f"host buffer for sequence {s_} must be pinned uint8 of >= {staging.numel()} bytes")
             host[:staging.numel()].copy_(staging, non_blocking=True)
             result[s_] = (host, n)
         with torch.cuda.stream(side):

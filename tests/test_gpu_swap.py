@@ -122,3 +122,32 @@ def test_overlapped_swap_reuses_released_blocks(cache, src, qd, d):
     torch.cuda.synchronize()
     for layer in range(2):
         assert torch.equal(before[layer].cpu(), after[layer].cpu()), f"layer {layer}"
+
+
+def test_overlapped_swap_refuses_bad_host_buffers_before_moving_anything():
+    # a host buffer that is too small, not pinned, or stands for another
+    # block count is refused before the allocator changes: the sequence
+    # stays swapped out and comes back intact with the right buffer
+    lens = [300, 517]
+    w = wl.custom_workload(len(lens), 16, 4, 128, lens, dtype="bf16", seed=31, pool_factor=1.0, extra_blocks=2)
+    g = GpuWorkload(w, num_layers=2).run(wl.setup_ops(w))
+    c = g.cache
+    q = to_device(wl.queries(w, 0), w.q_dtype)
+    before = c.decode(q, 0, seq_ids=[0, 1]).clone()
+    out = c.swap([1])
+    host, n = out[1]
+    stats = c.alloc.stats()
+    small = torch.empty(host.numel() // 2, dtype=torch.uint8, pin_memory=True)
+    with pytest.raises(ValueError):
+        c.swap([], {1: (small, n)})
+    with pytest.raises(ValueError):
+        c.swap([], {1: (host.clone(), n)})                  # pageable copy
+    with pytest.raises(ValueError):
+        c.swap([], {1: (host, n - 1)})
+    with pytest.raises(ValueError):
+        c.swap([0], out_host={0: small})
+    assert c.alloc.stats() == stats
+    c.swap([], {1: (host, n)})
+    after = c.decode(q, 0, seq_ids=[0, 1])
+    torch.cuda.synchronize()
+    assert torch.equal(before.cpu(), after.cpu())
