@@ -90,8 +90,12 @@ def abi_version() -> int:
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    """Device address of a tensor for a device entry point: it must be a
+    contiguous GPU tensor (a host address would reach a kernel)."""
     if t is None:
         return None
+    if t.device.type != "cuda":
+        raise ValueError("tensors passed to libpagedkv's device calls must be on the GPU")
     if not t.is_contiguous():
         raise ValueError("tensors passed to libpagedkv must be contiguous")
     return t.data_ptr()
