@@ -85,6 +85,28 @@ def cache_code(k_pool: torch.Tensor, v_pool: Optional[torch.Tensor] = None) -> i
     return dtype_code(k_pool.dtype)
 
 
+_QUANTISED = (PKV_FP8_E4M3, PKV_FP8_E5M2, PKV_INT8_INT4)
+
+
+def _pool_code(k_pool: torch.Tensor, v_pool: torch.Tensor, k_scale: Optional[torch.Tensor],
+               v_scale: Optional[torch.Tensor]) -> int:
+    """cache_code, with the shapes the kernels index checked on the host: the
+    V pool matches the K pool's blocks, heads and block size, and a quantised
+    format has float32 scales [num_blocks, num_kv_heads, block_size] for K
+    and V."""
+    code = cache_code(k_pool, v_pool)
+    if tuple(v_pool.shape[:3]) != tuple(k_pool.shape[:3]):
+        raise ValueError("K and V pools must have the same blocks, heads and block size")
+    if code != PKV_INT8_INT4 and v_pool.shape[3] != k_pool.shape[3]:
+        raise ValueError("K and V pools must have the same head_dim")
+    if code in _QUANTISED:
+        for sc in (k_scale, v_scale):
+            if sc is None or sc.dtype != torch.float32 or tuple(sc.shape) != tuple(k_pool.shape[:3]):
+                raise ValueError("a quantised cache needs float32 K and V scales [num_blocks, num_kv_heads, "
+                                 "block_size]")
+    return code
+
+
 def abi_version() -> int:
     return _lib.lib().pkv_abi_version()
 
@@ -130,7 +152,7 @@ def kv_cache_append(k_new: torch.Tensor, v_new: torch.Tensor, k_pool: torch.Tens
     _check(_lib.lib().kv_cache_append_bs(
         _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
         _ptr(slot_mapping), int(k_new.shape[0]), hkv, d, nb, bs, dtype_code(k_new.dtype),
-        cache_code(k_pool, v_pool), _stream(stream)), "kv_cache_append_bs")
+        _pool_code(k_pool, v_pool, k_scale, v_scale), _stream(stream)), "kv_cache_append_bs")
 
 
 def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torch.Tensor,
@@ -140,10 +162,10 @@ def copy_blocks(k_pool: torch.Tensor, v_pool: torch.Tensor, pairs: torch.Tensor,
     nb, hkv, d, bs = _pool_geometry(k_pool)
     if pairs.dtype != torch.int32 or (pairs.numel() and pairs.shape[-1] != 2):
         raise ValueError("pairs must be int32 [n, 2]")
+    code = _pool_code(k_pool, v_pool, k_scale, v_scale)
     _check(_lib.lib().pkv_copy_blocks_bs(
         _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(pairs),
-        int(pairs.numel() // 2), hkv, d, nb, bs, cache_code(k_pool, v_pool), _stream(stream)),
-        "pkv_copy_blocks_bs")
+        int(pairs.numel() // 2), hkv, d, nb, bs, code, _stream(stream)), "pkv_copy_blocks_bs")
 
 
 def decode_partition_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
@@ -179,7 +201,7 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
         raise ValueError("block_tables must be [B, max_blocks], context_lens [B]")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    cdt = cache_code(k_pool, v_pool)
+    cdt = _pool_code(k_pool, v_pool, k_scale, v_scale)
     need = workspace_size(B, hq, hkv, d, max_context_len, partition_size, cdt)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         # zeroed once: the library keeps its counters zero between calls
@@ -212,10 +234,11 @@ def paged_attention_prefill(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Te
     T, hq = int(q.shape[0]), int(q.shape[1])
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    code = _pool_code(k_pool, v_pool, k_scale, v_scale)
     _check(_lib.lib().paged_attention_prefill_bs(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale), _ptr(block_tables),
         _ptr(context_lens), _ptr(query_start), B, T, hq, hkv, d, nb, bs, int(block_tables.shape[1]),
-        int(max_context_len), int(max_query_len), float(scale), dtype_code(q.dtype), cache_code(k_pool, v_pool),
+        int(max_context_len), int(max_query_len), float(scale), dtype_code(q.dtype), code,
         _stream(stream)), "paged_attention_prefill_bs")
     return out
 
@@ -260,7 +283,7 @@ def _decode_append_call(fn_name, out, q, k_new, v_new, k_pool, v_pool, slot_mapp
         raise ValueError("block_tables and context_lens must be int32")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    cdt = cache_code(k_pool, v_pool)
+    cdt = _pool_code(k_pool, v_pool, k_scale, v_scale)
     need = workspace_size(B, hq, hkv, d, max_context_len, partition_size, cdt)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)

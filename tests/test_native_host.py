@@ -346,3 +346,28 @@ def test_device_calls_refuse_host_tensors():
     lens = torch.ones(1, dtype=torch.int32)
     with pytest.raises(ValueError, match="GPU"):
         pkv.paged_attention_decode(torch.empty_like(q), q, pool, pool, tables, lens, 1, partition_size=16)
+
+
+def test_binding_checks_pool_shapes_and_scales_on_the_host():
+    # shapes the kernels index are checked before any call: V pool against K
+    # pool, and float32 scales [num_blocks, num_kv_heads, block_size] for a
+    # quantised cache (the checks come before the device checks, so host
+    # tensors suffice here)
+    k = torch.zeros((8, 2, 16, 64), dtype=torch.uint8)
+    sc = torch.ones((8, 2, 16), dtype=torch.float32)
+    assert pkv._pool_code(k, k, sc, sc) == pkv.PKV_FP8_E4M3
+    with pytest.raises(ValueError, match="scales"):
+        pkv._pool_code(k, k, None, sc)
+    with pytest.raises(ValueError, match="scales"):
+        pkv._pool_code(k, k, sc, sc.reshape(-1))
+    with pytest.raises(ValueError, match="scales"):
+        pkv._pool_code(k, k, sc, sc.double())
+    with pytest.raises(ValueError, match="blocks"):
+        pkv._pool_code(k, k[:4], sc, sc)
+    b = torch.zeros((8, 2, 16, 64), dtype=torch.bfloat16)
+    assert pkv._pool_code(b, b, None, None) == pkv.PKV_BF16
+    with pytest.raises(ValueError, match="head_dim"):
+        pkv._pool_code(b, torch.zeros((8, 2, 16, 32), dtype=torch.bfloat16), None, None)
+    k8 = torch.zeros((8, 2, 16, 64), dtype=torch.int8)
+    v4 = torch.zeros((8, 2, 16, 32), dtype=torch.uint8)
+    assert pkv._pool_code(k8, v4, sc, sc) == pkv.PKV_INT8_INT4
