@@ -197,11 +197,10 @@ size_t paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_
  *                 second kernel of the same call merges them exactly
  *                 (log-sum-exp) into the output.
  *   workspace     device scratch of at least paged_attention_workspace_size()
- *                 bytes (may be NULL when that is 0).  Its first part holds
- *                 arrival counters: the whole workspace must be zero before
- *                 its first use (for example allocated with torch.zeros), and
- *                 every call leaves the counters zero again.  Calls that may
- *                 run concurrently must not share a workspace.
+ *                 bytes (may be NULL when that is 0): the partition states of
+ *                 the call.  It needs no initialisation (every value a call
+ *                 uses is written by that call).  Calls that may run
+ *                 concurrently must not share a workspace.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).  L_b == 0 gives
  * an all-zero output row.  Entries of the used part of a block-table row must
  * lie in [0, num_blocks); a block outside that range contributes no tokens.

@@ -204,7 +204,6 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
     cdt = _pool_code(k_pool, v_pool, k_scale, v_scale)
     need = workspace_size(B, hq, hkv, d, max_context_len, partition_size, cdt)
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        # zeroed once: the library keeps its counters zero between calls
         workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.lib().paged_attention_decode_bs(

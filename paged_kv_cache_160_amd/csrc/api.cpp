@@ -52,11 +52,10 @@ int resolve_partitions(int num_seqs, int num_kv_heads, int max_context_len, int 
   return PKV_OK;
 }
 
-// Workspace layout: per (sequence, KV head) arrival counters (int32), then
-// per (sequence, query head, partition) (m, l) pairs, then the unnormalised
-// partition outputs; each part starts on a 256-byte boundary.
+// Workspace layout: per (sequence, query head, partition) (m, l) pairs, then
+// the unnormalised partition outputs (256-byte aligned).
 struct WorkspaceLayout {
-  size_t counters = 0, ml = 0, acc = 0, total = 0;
+  size_t ml = 0, acc = 0, total = 0;
 };
 
 WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int np) {
@@ -64,9 +63,9 @@ WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads
   if (np <= 1) return w;
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * np;
-  w.counters = 0;
-  w.ml = up(static_cast<size_t>(num_seqs) * num_kv_heads * sizeof(int32_t));
-  w.acc = w.ml + up(rows * 2 * sizeof(float));
+  (void)num_kv_heads;
+  w.ml = 0;
+  w.acc = up(rows * 2 * sizeof(float));
   w.total = w.acc + rows * head_dim * sizeof(float);
   return w;
 }
@@ -242,8 +241,7 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new, 
   a.src_dtype = src_dtype;
   if (np > 1) {
     char* base = static_cast<char*>(workspace);
-    a.counters = reinterpret_cast<int*>(base + ws.counters);
-    a.part_ml = reinterpret_cast<float*>(base + ws.ml);
+      a.part_ml = reinterpret_cast<float*>(base + ws.ml);
     a.part_acc = reinterpret_cast<float*>(base + ws.acc);
   }
   return pkv::launch_decode(a, static_cast<hipStream_t>(stream), stages);
@@ -377,7 +375,6 @@ int paged_attention_merge_partials_bs(void* out, const int32_t* context_lens, in
   a.partition_size = ps;
   a.num_partitions = np;
   char* base = static_cast<char*>(workspace);
-  a.counters = reinterpret_cast<int*>(base + ws.counters);
   a.part_ml = reinterpret_cast<float*>(base + ws.ml);
   a.part_acc = reinterpret_cast<float*>(base + ws.acc);
   return pkv::launch_decode(a, static_cast<hipStream_t>(stream), pkv::kStageMerge);

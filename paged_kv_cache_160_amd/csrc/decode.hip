@@ -37,10 +37,10 @@
 //    P carries ~16 significant bits while the MFMA still accumulates in fp32.
 //  * Long sequences split into partitions; each partition's (max, sum,
 //    unnormalised output) goes to the workspace (an empty one writes max
-//    -inf) and a second launch merges them with the log-sum-exp formula (a variant that merges in the
-//    workgroup of a (sequence, KV head) that finishes last, behind
-//    PKV_DECODE_MERGE, was measured slower: its device-scope fences write
-//    back L2).
+//    -inf) and a second launch merges them with the log-sum-exp formula.
+//    Merging inside this kernel, in the workgroup of a (sequence, KV head)
+//    that finishes last, was measured slower: the device-scope fences it
+//    needs write back L2.
 
 #include <math.h>
 
@@ -59,9 +59,6 @@ namespace pkv {
 #endif
 #ifndef PKV_DECODE_NT
 #define PKV_DECODE_NT 0        // non-temporal K/V loads (measured slower: off)
-#endif
-#ifndef PKV_DECODE_MERGE
-#define PKV_DECODE_MERGE 0     // 0: merge kernel; 1: last workgroup merges (release fences)
 #endif
 constexpr int kWaves = PKV_DECODE_WAVES;
 constexpr int kThreads = kWaves * kWave;
@@ -366,7 +363,6 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   __shared__ float sm_m[kWaves][kMaxGroup];
   __shared__ float sm_l[kWaves][kMaxGroup];
   __shared__ float sm_o[kWaves][kMaxGroup][D];
-  __shared__ int sm_last;
   __shared__ int sm_ids[kMaxPartitionBlocks];
 
   const int P = a.num_partitions;
@@ -436,10 +432,9 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * a.block_size)));
   const int np_b = (L + PS - 1) / PS;         // non-empty partitions of this sequence
   if (part >= np_b) {
-    if (P == 1 || PKV_DECODE_MERGE != 0) {
-      // an empty context gives a zero output row (written once)
-      if (part == 0)
-        for (int i = tid; i < group * D; i += kThreads) store_from_f32<QT>(a.out, out_row0 * D + i, 0.0f);
+    if (P == 1) {
+      // an empty context gives a zero output row
+      for (int i = tid; i < group * D; i += kThreads) store_from_f32<QT>(a.out, out_row0 * D + i, 0.0f);
     } else {
       // the merge reads every partition slot: mark this one empty
       for (int h = tid; h < group; h += kThreads) {
@@ -671,41 +666,6 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
       }
     }
   }
-  if (single || PKV_DECODE_MERGE == 0) return;
-
-  // ---- log-sum-exp merge of the sequence's partitions, by the workgroup of
-  // this (sequence, KV head) that finishes last.  Each workgroup releases its
-  // partials device-wide (every XCD's L2) before counting in; the last
-  // arriver acquires before reading them and resets the count, so the
-  // counters stay zero between calls.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  __syncthreads();
-  int* counter = a.counters + static_cast<int64_t>(b) * a.num_kv_heads + g;
-  if (tid == 0) sm_last = (atomicAdd(counter, 1) == np_b - 1);
-  __syncthreads();
-  if (!sm_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  for (int idx = tid; idx < group * D; idx += kThreads) {
-    const int h = idx / D;
-    const int d = idx % D;
-    const int64_t row = out_row0 + h;
-    const float* ml = a.part_ml + row * P * 2;
-    const float* acc = a.part_acc + row * P * D;
-    float M = kNegInf;
-    for (int pp = 0; pp < np_b; ++pp) M = fmaxf(M, ml[2 * pp]);
-    float num = 0.f, den = 0.f;
-    if (M != kNegInf) {
-      for (int pp = 0; pp < np_b; ++pp) {
-        const float mp = ml[2 * pp];
-        if (mp == kNegInf) continue;
-        const float f = __builtin_amdgcn_exp2f(mp - M);
-        num += f * acc[static_cast<int64_t>(pp) * D + d];
-        den += f * ml[2 * pp + 1];
-      }
-    }
-    store_from_f32<QT>(a.out, row * D + d, den > 0.f ? num / den : 0.f);
-  }
-  if (tid == 0) atomicExch(counter, 0);
 }
 
 // ---- log-sum-exp merge of partitions (second launch) --------------------------------
@@ -802,7 +762,7 @@ static int launch_typed(const DecodeArgs& a, hipStream_t stream, int stages) {
                        dim3(kThreads), 0, stream, a);
     rc = check_launch();
   }
-  if (rc != PKV_OK || !(stages & kStageMerge) || PKV_DECODE_MERGE != 0 || a.num_partitions == 1) return rc;
+  if (rc != PKV_OK || !(stages & kStageMerge) || a.num_partitions == 1) return rc;
   hipLaunchKernelGGL((partition_merge_kernel<QT, D>), dim3(a.num_seqs * a.num_q_heads), dim3(D), 0, stream, a);
   return check_launch();
 }

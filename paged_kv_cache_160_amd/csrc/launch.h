@@ -46,7 +46,6 @@ struct DecodeArgs {
   const void* v_new;
   const int64_t* slot_mapping;   // [num_seqs]: slot of position context_lens[b] - 1
   pkv_dtype src_dtype;
-  int* counters;           // [num_seqs][num_kv_heads], zero between calls
   float* part_ml;          // [num_seqs][num_q_heads][num_partitions][2]  (m, l)
   float* part_acc;         // [num_seqs][num_q_heads][num_partitions][head_dim]
 };

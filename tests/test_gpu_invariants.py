@@ -101,6 +101,31 @@ def test_largest_partition():
     assert max_err(out, exp) <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("cache", [None, "int8_int4"])
+def test_workspace_needs_no_initialisation(cache):
+    # a ragged batch split into 64-token partitions leaves empty partition
+    # slots (their output rows are never written); a workspace full of NaN
+    # bytes gives the same output bits as a zeroed one
+    lens = [700, 1, 0, 130, 64, 2000]
+    w, g = _custom(lens, 16, 4, 128, "bf16" if cache is None else "f32", cache_dtype=cache,
+                   q_dtype=None if cache is None else "bf16")
+    seqs = list(range(w.num_seqs))
+    tables = g.cache.block_tables(seqs)
+    q = g.queries(0)
+    c = g.cache
+    need = pkv.workspace_size(len(seqs), 16, 4, 128, tables[2], 64, c.cache_code)
+    outs = []
+    for fill in (0, 0xFF):
+        ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(q)
+        pkv.paged_attention_decode(out, q, c.k[0], c.v[0], tables[0], tables[1], tables[2],
+                                   k_scale=c.k_scale[0], v_scale=c.v_scale[0], partition_size=64, workspace=ws)
+        outs.append(out.cpu())
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs[1].float()).all()
+    assert torch.equal(outs[0], outs[1])
+
+
 @pytest.mark.parametrize("ps", [0, 64])
 def test_empty_context_gives_zeros(ps):
     say(f"[L=0] partition_size={ps}")
