@@ -72,8 +72,9 @@ WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads
 
 bool decode_sizes_ok(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
                      int max_context_len) {
+  // (sequence, query head) rows index the merge grid and the workspace
   return num_seqs >= 0 && num_kv_heads > 0 && num_q_heads > 0 && num_q_heads % num_kv_heads == 0 &&
-         max_context_len >= 0 && head_dim > 0;
+         max_context_len >= 0 && head_dim > 0 && static_cast<int64_t>(num_seqs) * num_q_heads <= 0x7fffffff;
 }
 
 }  // namespace

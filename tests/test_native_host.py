@@ -371,3 +371,13 @@ def test_binding_checks_pool_shapes_and_scales_on_the_host():
     k8 = torch.zeros((8, 2, 16, 64), dtype=torch.int8)
     v4 = torch.zeros((8, 2, 16, 32), dtype=torch.uint8)
     assert pkv._pool_code(k8, v4, sc, sc) == pkv.PKV_INT8_INT4
+
+
+def test_sizes_past_the_grid_limit_are_refused():
+    # (sequence, query head) rows beyond 2^31 - 1 would overflow the merge
+    # grid and the workspace size: refused on the host
+    lib = pkv._lib.lib()
+    assert lib.paged_attention_workspace_size(1 << 20, 1 << 12, 1 << 8, 128, 4096, 0, pkv.PKV_BF16) == 0
+    assert lib.paged_attention_decode_bs(None, None, None, None, None, None, None, None, 1 << 20, 1 << 12, 1 << 8,
+                                         128, 4, 16, 256, 4096, 0.125, pkv.PKV_BF16, pkv.PKV_BF16, 0, None, 0,
+                                         None) == -1
