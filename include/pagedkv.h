@@ -64,7 +64,9 @@ enum {
   PKV_ERR_WORKSPACE = -3,      /* workspace missing or smaller than required */
   PKV_ERR_HIP = -4,            /* the HIP runtime reported an error */
   PKV_ERR_NO_FREE_BLOCKS = -5, /* allocator: not enough free blocks; nothing changed */
-  PKV_ERR_UNKNOWN_SEQ = -6     /* allocator: no such sequence id */
+  PKV_ERR_UNKNOWN_SEQ = -6,    /* allocator: no such sequence id */
+  PKV_ERR_HOST_MEMORY = -7     /* allocator: host memory ran out during the call; its state
+                                  may be partly updated, so destroy it */
 };
 
 /* Library ABI version (PKV_ABI_VERSION). */

@@ -244,19 +244,28 @@ struct pkv_alloc {
   }
 };
 
+// Exported calls that may allocate host memory catch what the standard
+// containers throw: no exception crosses the C boundary.
 extern "C" {
 
 pkv_alloc* pkv_alloc_create_bs(int num_blocks, int max_blocks_per_seq, int block_size) {
-  if (num_blocks <= 0 || max_blocks_per_seq <= 0 || (block_size != PKV_BLOCK_SIZE && block_size != PKV_BLOCK_SIZE_LARGE)) return nullptr;
+  if (num_blocks <= 0 || max_blocks_per_seq <= 0 ||
+      (block_size != PKV_BLOCK_SIZE && block_size != PKV_BLOCK_SIZE_LARGE))
+    return nullptr;
   pkv_alloc* a = new (std::nothrow) pkv_alloc();
   if (!a) return nullptr;
-  a->bs = block_size;
-  a->pc.bs = block_size;
-  a->num_blocks = num_blocks;
-  a->max_blocks_per_seq = max_blocks_per_seq;
-  a->ref.assign(num_blocks, 0);
-  a->free_stack.resize(num_blocks);
-  for (int i = 0; i < num_blocks; ++i) a->free_stack[i] = num_blocks - 1 - i;
+  try {
+      a->bs = block_size;
+      a->pc.bs = block_size;
+      a->num_blocks = num_blocks;
+      a->max_blocks_per_seq = max_blocks_per_seq;
+      a->ref.assign(num_blocks, 0);
+      a->free_stack.resize(num_blocks);
+      for (int i = 0; i < num_blocks; ++i) a->free_stack[i] = num_blocks - 1 - i;
+  } catch (...) {
+    delete a;
+    return nullptr;
+  }
   return a;
 }
 
@@ -269,49 +278,65 @@ int pkv_alloc_block_size(const pkv_alloc* a) { return a ? a->bs : PKV_ERR_INVALI
 void pkv_alloc_destroy(pkv_alloc* a) { delete a; }
 
 int pkv_alloc_set_free_order(pkv_alloc* a, const int32_t* order, int n) {
-  if (!a || !order || n != a->num_blocks) return PKV_ERR_INVALID_ARG;
-  if (!a->seqs.empty() || static_cast<int>(a->free_stack.size()) != a->num_blocks)
-    return PKV_ERR_INVALID_ARG;
-  std::vector<char> seen(n, 0);
-  for (int i = 0; i < n; ++i) {
-    if (order[i] < 0 || order[i] >= n || seen[order[i]]) return PKV_ERR_INVALID_ARG;
-    seen[order[i]] = 1;
+  try {
+    if (!a || !order || n != a->num_blocks) return PKV_ERR_INVALID_ARG;
+    if (!a->seqs.empty() || static_cast<int>(a->free_stack.size()) != a->num_blocks)
+      return PKV_ERR_INVALID_ARG;
+    std::vector<char> seen(n, 0);
+    for (int i = 0; i < n; ++i) {
+      if (order[i] < 0 || order[i] >= n || seen[order[i]]) return PKV_ERR_INVALID_ARG;
+      seen[order[i]] = 1;
+    }
+    for (int i = 0; i < n; ++i) a->free_stack[i] = order[n - 1 - i];
+    return PKV_OK;
+  } catch (...) {
+    return PKV_ERR_HOST_MEMORY;
   }
-  for (int i = 0; i < n; ++i) a->free_stack[i] = order[n - 1 - i];
-  return PKV_OK;
 }
 
 int pkv_seq_create(pkv_alloc* a, int64_t seq_id) {
-  if (!a) return PKV_ERR_INVALID_ARG;
-  if (a->seqs.count(seq_id)) return PKV_ERR_INVALID_ARG;
-  Seq s;
-  s.tracked = a->pc.enabled;
-  a->seqs.emplace(seq_id, std::move(s));
-  a->seq_order.push_back(seq_id);
-  return PKV_OK;
+  try {
+    if (!a) return PKV_ERR_INVALID_ARG;
+    if (a->seqs.count(seq_id)) return PKV_ERR_INVALID_ARG;
+    Seq s;
+    s.tracked = a->pc.enabled;
+    a->seqs.emplace(seq_id, std::move(s));
+    a->seq_order.push_back(seq_id);
+    return PKV_OK;
+  } catch (...) {
+    return PKV_ERR_HOST_MEMORY;
+  }
 }
 
 int pkv_seq_fork(pkv_alloc* a, int64_t parent, int64_t child) {
-  if (!a) return PKV_ERR_INVALID_ARG;
-  auto it = a->seqs.find(parent);
-  if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
-  if (it->second.swapped) return PKV_ERR_INVALID_ARG;
-  if (a->seqs.count(child)) return PKV_ERR_INVALID_ARG;
-  Seq c = it->second;
-  for (int32_t b : c.table) ++a->ref[b];
-  a->seqs.emplace(child, std::move(c));
-  a->seq_order.push_back(child);
-  return PKV_OK;
+  try {
+    if (!a) return PKV_ERR_INVALID_ARG;
+    auto it = a->seqs.find(parent);
+    if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+    if (it->second.swapped) return PKV_ERR_INVALID_ARG;
+    if (a->seqs.count(child)) return PKV_ERR_INVALID_ARG;
+    Seq c = it->second;
+    for (int32_t b : c.table) ++a->ref[b];
+    a->seqs.emplace(child, std::move(c));
+    a->seq_order.push_back(child);
+    return PKV_OK;
+  } catch (...) {
+    return PKV_ERR_HOST_MEMORY;
+  }
 }
 
 int pkv_seq_free(pkv_alloc* a, int64_t seq_id) {
-  if (!a) return PKV_ERR_INVALID_ARG;
-  auto it = a->seqs.find(seq_id);
-  if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
-  for (int32_t b : it->second.table) a->release(b);
-  a->seqs.erase(it);
-  a->seq_order.erase(std::find(a->seq_order.begin(), a->seq_order.end(), seq_id));
-  return PKV_OK;
+  try {
+    if (!a) return PKV_ERR_INVALID_ARG;
+    auto it = a->seqs.find(seq_id);
+    if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+    for (int32_t b : it->second.table) a->release(b);
+    a->seqs.erase(it);
+    a->seq_order.erase(std::find(a->seq_order.begin(), a->seq_order.end(), seq_id));
+    return PKV_OK;
+  } catch (...) {
+    return PKV_ERR_HOST_MEMORY;
+  }
 }
 
 int pkv_seq_len(pkv_alloc* a, int64_t seq_id) {
@@ -394,65 +419,89 @@ extern "C" {
 
 int pkv_seq_append_slots(pkv_alloc* a, int64_t seq_id, int n_tokens, int64_t* slots_out,
                          int32_t* cow_pairs_out, int* n_cow_out) {
-  return append_impl(a, seq_id, n_tokens, nullptr, slots_out, cow_pairs_out, n_cow_out);
+  try {
+    return append_impl(a, seq_id, n_tokens, nullptr, slots_out, cow_pairs_out, n_cow_out);
+  } catch (...) {
+    return PKV_ERR_HOST_MEMORY;
+  }
 }
 
 int pkv_seq_append_tokens(pkv_alloc* a, int64_t seq_id, const int32_t* tokens, int n_tokens,
                           int64_t* slots_out, int32_t* cow_pairs_out, int* n_cow_out) {
-  if (n_tokens > 0 && !tokens) return PKV_ERR_INVALID_ARG;
-  return append_impl(a, seq_id, n_tokens, tokens ? tokens : &kNoToken, slots_out, cow_pairs_out,
-                     n_cow_out);
+  try {
+    if (n_tokens > 0 && !tokens) return PKV_ERR_INVALID_ARG;
+    return append_impl(a, seq_id, n_tokens, tokens ? tokens : &kNoToken, slots_out, cow_pairs_out,
+                       n_cow_out);
+  } catch (...) {
+    return PKV_ERR_HOST_MEMORY;
+  }
 }
 
 int pkv_batch_append_one(pkv_alloc* a, const int64_t* seq_ids, int n, int64_t* slots_out,
                          int32_t* cow_pairs_out, int* n_cow_out) {
-  return batch_impl(a, seq_ids, nullptr, n, slots_out, cow_pairs_out, n_cow_out);
+  try {
+    return batch_impl(a, seq_ids, nullptr, n, slots_out, cow_pairs_out, n_cow_out);
+  } catch (...) {
+    return PKV_ERR_HOST_MEMORY;
+  }
 }
 
 int pkv_batch_append_tokens(pkv_alloc* a, const int64_t* seq_ids, const int32_t* tokens, int n,
                             int64_t* slots_out, int32_t* cow_pairs_out, int* n_cow_out) {
-  if (n > 0 && !tokens) return PKV_ERR_INVALID_ARG;
-  return batch_impl(a, seq_ids, tokens ? tokens : &kNoToken, n, slots_out, cow_pairs_out, n_cow_out);
+  try {
+    if (n > 0 && !tokens) return PKV_ERR_INVALID_ARG;
+    return batch_impl(a, seq_ids, tokens ? tokens : &kNoToken, n, slots_out, cow_pairs_out, n_cow_out);
+  } catch (...) {
+    return PKV_ERR_HOST_MEMORY;
+  }
 }
 
 int pkv_prefix_cache_enable(pkv_alloc* a, uint64_t model_key, int hash_bits) {
-  if (!a || hash_bits < 1 || hash_bits > 64 || a->pc.enabled) return PKV_ERR_INVALID_ARG;
-  if (!a->seqs.empty() || static_cast<int>(a->free_stack.size()) != a->num_blocks)
-    return PKV_ERR_INVALID_ARG;
-  a->pc.enabled = true;
-  a->pc.model_key = model_key;
-  a->pc.mask = hash_bits == 64 ? ~0ull : ((1ull << hash_bits) - 1);
-  a->pc.entry.assign(a->num_blocks, CacheEntry{});
-  return PKV_OK;
+  try {
+    if (!a || hash_bits < 1 || hash_bits > 64 || a->pc.enabled) return PKV_ERR_INVALID_ARG;
+    if (!a->seqs.empty() || static_cast<int>(a->free_stack.size()) != a->num_blocks)
+      return PKV_ERR_INVALID_ARG;
+    a->pc.enabled = true;
+    a->pc.model_key = model_key;
+    a->pc.mask = hash_bits == 64 ? ~0ull : ((1ull << hash_bits) - 1);
+    a->pc.entry.assign(a->num_blocks, CacheEntry{});
+    return PKV_OK;
+  } catch (...) {
+    return PKV_ERR_HOST_MEMORY;
+  }
 }
 
 int pkv_seq_create_cached(pkv_alloc* a, int64_t seq_id, const int32_t* tokens, int n_tokens,
                           int* n_cached_out) {
-  if (!a || !a->pc.enabled || n_tokens < 0 || !n_cached_out || (n_tokens > 0 && !tokens))
-    return PKV_ERR_INVALID_ARG;
-  if (a->seqs.count(seq_id)) return PKV_ERR_INVALID_ARG;
-  PrefixCache& pc = a->pc;
-  // at most (n - 1) / bs blocks, so the last prompt token is always computed
-  const int bs = a->bs;
-  int64_t most = std::min<int64_t>(n_tokens > 0 ? (n_tokens - 1) / bs : 0, a->max_blocks_per_seq);
-  Seq s;
-  s.tracked = true;
-  int32_t parent = -1;
-  for (int64_t i = 0; i < most; ++i) {
-    const int32_t* t = tokens + i * bs;
-    int32_t b = pc.find(parent, t, pc.hash_of(parent, t));
-    if (b < 0) break;
-    s.table.push_back(b);
-    parent = b;
+  try {
+    if (!a || !a->pc.enabled || n_tokens < 0 || !n_cached_out || (n_tokens > 0 && !tokens))
+      return PKV_ERR_INVALID_ARG;
+    if (a->seqs.count(seq_id)) return PKV_ERR_INVALID_ARG;
+    PrefixCache& pc = a->pc;
+    // at most (n - 1) / bs blocks, so the last prompt token is always computed
+    const int bs = a->bs;
+    int64_t most = std::min<int64_t>(n_tokens > 0 ? (n_tokens - 1) / bs : 0, a->max_blocks_per_seq);
+    Seq s;
+    s.tracked = true;
+    int32_t parent = -1;
+    for (int64_t i = 0; i < most; ++i) {
+      const int32_t* t = tokens + i * bs;
+      int32_t b = pc.find(parent, t, pc.hash_of(parent, t));
+      if (b < 0) break;
+      s.table.push_back(b);
+      parent = b;
+    }
+    for (int32_t b : s.table) a->hold(b);
+    s.len = static_cast<int64_t>(s.table.size()) * bs;
+    pc.lookup_blocks += most;
+    pc.hit_blocks += static_cast<int64_t>(s.table.size());
+    *n_cached_out = static_cast<int>(s.len);
+    a->seqs.emplace(seq_id, std::move(s));
+    a->seq_order.push_back(seq_id);
+    return PKV_OK;
+  } catch (...) {
+    return PKV_ERR_HOST_MEMORY;
   }
-  for (int32_t b : s.table) a->hold(b);
-  s.len = static_cast<int64_t>(s.table.size()) * bs;
-  pc.lookup_blocks += most;
-  pc.hit_blocks += static_cast<int64_t>(s.table.size());
-  *n_cached_out = static_cast<int>(s.len);
-  a->seqs.emplace(seq_id, std::move(s));
-  a->seq_order.push_back(seq_id);
-  return PKV_OK;
 }
 
 int pkv_prefix_stats(pkv_alloc* a, pkv_prefix_stats_t* out) {
@@ -467,23 +516,27 @@ int pkv_prefix_stats(pkv_alloc* a, pkv_prefix_stats_t* out) {
 
 int pkv_build_block_tables(pkv_alloc* a, const int64_t* seq_ids, int n, int max_blocks_per_seq,
                            int32_t* tables_out, int32_t* lens_out) {
-  if (!a || n < 0 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
-  if (n > 0 && (!seq_ids || !tables_out || !lens_out)) return PKV_ERR_INVALID_ARG;
-  for (int i = 0; i < n; ++i) {
-    auto it = a->seqs.find(seq_ids[i]);
-    if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
-    if (it->second.swapped) return PKV_ERR_INVALID_ARG;
-    if (static_cast<int64_t>(it->second.table.size()) > max_blocks_per_seq)
-      return PKV_ERR_INVALID_ARG;
+  try {
+    if (!a || n < 0 || max_blocks_per_seq <= 0) return PKV_ERR_INVALID_ARG;
+    if (n > 0 && (!seq_ids || !tables_out || !lens_out)) return PKV_ERR_INVALID_ARG;
+    for (int i = 0; i < n; ++i) {
+      auto it = a->seqs.find(seq_ids[i]);
+      if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+      if (it->second.swapped) return PKV_ERR_INVALID_ARG;
+      if (static_cast<int64_t>(it->second.table.size()) > max_blocks_per_seq)
+        return PKV_ERR_INVALID_ARG;
+    }
+    for (int i = 0; i < n; ++i) {
+      const Seq& s = a->seqs[seq_ids[i]];
+      int32_t* row = tables_out + static_cast<int64_t>(i) * max_blocks_per_seq;
+      std::fill(row, row + max_blocks_per_seq, 0);
+      std::copy(s.table.begin(), s.table.end(), row);
+      lens_out[i] = static_cast<int32_t>(s.len);
+    }
+    return PKV_OK;
+  } catch (...) {
+    return PKV_ERR_HOST_MEMORY;
   }
-  for (int i = 0; i < n; ++i) {
-    const Seq& s = a->seqs[seq_ids[i]];
-    int32_t* row = tables_out + static_cast<int64_t>(i) * max_blocks_per_seq;
-    std::fill(row, row + max_blocks_per_seq, 0);
-    std::copy(s.table.begin(), s.table.end(), row);
-    lens_out[i] = static_cast<int32_t>(s.len);
-  }
-  return PKV_OK;
 }
 
 int pkv_alloc_stats(pkv_alloc* a, pkv_alloc_stats_t* out) {
@@ -517,38 +570,46 @@ int pkv_alloc_stats(pkv_alloc* a, pkv_alloc_stats_t* out) {
 }
 
 int pkv_seq_swap_out(pkv_alloc* a, int64_t seq_id, int32_t* blocks_out, int* n_out) {
-  if (!a || !n_out) return PKV_ERR_INVALID_ARG;
-  auto it = a->seqs.find(seq_id);
-  if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
-  Seq& s = it->second;
-  if (s.swapped) return PKV_ERR_INVALID_ARG;
-  if (!s.table.empty() && !blocks_out) return PKV_ERR_INVALID_ARG;
-  for (int32_t b : s.table)
-    if (a->ref[b] != 1) return PKV_ERR_INVALID_ARG;       // shared: its holders would lose it
-  std::copy(s.table.begin(), s.table.end(), blocks_out);
-  *n_out = static_cast<int>(s.table.size());
-  for (int32_t b : s.table) a->release(b);
-  s.table.clear();
-  s.swapped = true;
-  s.tracked = false;                                      // swapped-in copies are private
-  s.pending.clear();
-  return PKV_OK;
+  try {
+    if (!a || !n_out) return PKV_ERR_INVALID_ARG;
+    auto it = a->seqs.find(seq_id);
+    if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+    Seq& s = it->second;
+    if (s.swapped) return PKV_ERR_INVALID_ARG;
+    if (!s.table.empty() && !blocks_out) return PKV_ERR_INVALID_ARG;
+    for (int32_t b : s.table)
+      if (a->ref[b] != 1) return PKV_ERR_INVALID_ARG;       // shared: its holders would lose it
+    std::copy(s.table.begin(), s.table.end(), blocks_out);
+    *n_out = static_cast<int>(s.table.size());
+    for (int32_t b : s.table) a->release(b);
+    s.table.clear();
+    s.swapped = true;
+    s.tracked = false;                                      // swapped-in copies are private
+    s.pending.clear();
+    return PKV_OK;
+  } catch (...) {
+    return PKV_ERR_HOST_MEMORY;
+  }
 }
 
 int pkv_seq_swap_in(pkv_alloc* a, int64_t seq_id, int32_t* blocks_out, int* n_out) {
-  if (!a || !n_out) return PKV_ERR_INVALID_ARG;
-  auto it = a->seqs.find(seq_id);
-  if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
-  Seq& s = it->second;
-  if (!s.swapped) return PKV_ERR_INVALID_ARG;
-  const int64_t need = a->blocks_for(s.len);
-  if (need > 0 && !blocks_out) return PKV_ERR_INVALID_ARG;
-  if (need > a->available()) return PKV_ERR_NO_FREE_BLOCKS;
-  for (int64_t i = 0; i < need; ++i) s.table.push_back(a->take());
-  std::copy(s.table.begin(), s.table.end(), blocks_out);
-  *n_out = static_cast<int>(need);
-  s.swapped = false;
-  return PKV_OK;
+  try {
+    if (!a || !n_out) return PKV_ERR_INVALID_ARG;
+    auto it = a->seqs.find(seq_id);
+    if (it == a->seqs.end()) return PKV_ERR_UNKNOWN_SEQ;
+    Seq& s = it->second;
+    if (!s.swapped) return PKV_ERR_INVALID_ARG;
+    const int64_t need = a->blocks_for(s.len);
+    if (need > 0 && !blocks_out) return PKV_ERR_INVALID_ARG;
+    if (need > a->available()) return PKV_ERR_NO_FREE_BLOCKS;
+    for (int64_t i = 0; i < need; ++i) s.table.push_back(a->take());
+    std::copy(s.table.begin(), s.table.end(), blocks_out);
+    *n_out = static_cast<int>(need);
+    s.swapped = false;
+    return PKV_OK;
+  } catch (...) {
+    return PKV_ERR_HOST_MEMORY;
+  }
 }
 
 }  // extern "C"

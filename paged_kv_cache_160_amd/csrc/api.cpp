@@ -92,6 +92,7 @@ const char* pkv_strerror(int code) {
     case PKV_ERR_HIP: return "HIP runtime error";
     case PKV_ERR_NO_FREE_BLOCKS: return "no free blocks";
     case PKV_ERR_UNKNOWN_SEQ: return "unknown sequence id";
+    case PKV_ERR_HOST_MEMORY: return "host memory exhausted (allocator state may be partly updated)";
     default: return "unknown error code";
   }
 }

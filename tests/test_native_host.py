@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 def test_strerror_and_version():
     lib = _lib.lib()
     assert lib.pkv_abi_version() == 1
-    for code in (0, -1, -2, -3, -4, -5, -6):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert lib.pkv_strerror(code)
     assert lib.pkv_strerror(-99) == b"unknown error code"
 
