@@ -426,8 +426,8 @@ def main():
 
     # Side measurements after the timed region (not part of the value): the
     # decode step's cache write on its own (B rows into layer 0, the slots of
-    # the last step) and a copy-on-write copy of 8 whole blocks of sequence 0
-    # into free blocks, 100 calls each, HIP events around every call.
+    # the last step) and a copy-on-write copy of up to 8 used blocks into
+    # free blocks, 100 calls each, HIP events around every call.
     def time_calls(fn, n=100):
         evs_ = []
         for _ in range(n):
@@ -445,14 +445,14 @@ def main():
     side = {"append_b_rows": time_calls(lambda: lib.kv_cache_append_bs(
         knew.data_ptr(), vnew.data_ptr(), kp0, vp0, ksp0, vsp0, d_slots.data_ptr(), B, hkv, D, w.num_blocks, bs,
         src_code, cache_code, sp))}
-    used_tables, _ = cache.alloc.block_tables(seqs, mb)
-    used = set(int(x) for x in used_tables.flatten().tolist() if x >= 0)
-    free_blocks = [blk for blk in range(w.num_blocks) if blk not in used][:8]
-    if len(free_blocks) == 8:
-        pairs_t = torch.tensor([[int(used_tables[0, i]), free_blocks[i]] for i in range(8)], dtype=torch.int32,
-                               device=dev)
-        side["cow_copy_8_blocks"] = time_calls(lambda: lib.pkv_copy_blocks_bs(
-            kp0, vp0, ksp0, vsp0, pairs_t.data_ptr(), 8, hkv, D, w.num_blocks, bs, cache_code, sp))
+    used_tables, used_lens = cache.alloc.block_tables(seqs, mb)
+    used = sorted(set(int(used_tables[b_, i]) for b_ in range(B) for i in range(-(-int(used_lens[b_]) // bs))))
+    free_blocks = [blk for blk in range(w.num_blocks) if blk not in set(used)]
+    n_pairs = min(8, len(used), len(free_blocks))
+    if n_pairs:
+        pairs_t = torch.tensor([[used[i], free_blocks[i]] for i in range(n_pairs)], dtype=torch.int32, device=dev)
+        side[f"cow_copy_{n_pairs}_blocks"] = time_calls(lambda: lib.pkv_copy_blocks_bs(
+            kp0, vp0, ksp0, vsp0, pairs_t.data_ptr(), n_pairs, hkv, D, w.num_blocks, bs, cache_code, sp))
     for k_, v_ in side.items():
         log(f"[bench] {k_}: median {v_['median_us']:.2f} us (p10 {v_['p10_us']:.2f}, p90 {v_['p90_us']:.2f}), "
             f"events around each call")
