@@ -65,9 +65,20 @@ constexpr int kPfWaves = PKV_PREFILL_WAVES;
 #endif
 constexpr int kPfBufs = PKV_PREFILL_BUFFERS;
 constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kPfKeys = 64;                                  // keys per stage
+#ifndef PKV_PREFILL_KEYS
+#define PKV_PREFILL_KEYS 64    // keys per stage (32 or 64)
+#endif
+constexpr int kPfKeys = PKV_PREFILL_KEYS;
+constexpr int kPfStageTiles = kPfKeys / kTileTokens;          // 16-token units per stage
 constexpr int kPfMaxBlocks = PKV_MAX_PREFILL_CONTEXT / kTileTokens;
 constexpr int kXcds = 8;
+
+// s_waitcnt on vector memory only: at most N of this wave's loads in flight
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 constexpr float kLog2eP = 1.4426950408889634f;
 
 #ifndef PKV_PREFILL_CTILES
@@ -351,7 +362,7 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
   };
   auto vaddr = [&](int r, int q, int h) -> int { return kaddr(r, q) + 8 * h; };
 
-  // One stage (64 keys from s * 64) held in LDS at kbuf / vbuf.
+  // One stage (kPfKeys keys from s * kPfKeys) held in LDS at kbuf / vbuf.
   // One stage from half hv0 on.  The fast form (kSlow false) never rescales
   // the output: when a row that already holds output needs a new maximum it
   // returns the half it stopped at, before changing anything for that half,
@@ -360,9 +371,9 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
   auto compute = [&](auto slow_tag, const uint8_t* kbuf, const uint8_t* vbuf, int s, int hv0)
                      __attribute__((always_inline)) -> int {
       constexpr bool kSlow = decltype(slow_tag)::value;
-      // the stage in two halves of 32 keys: S^T, softmax, then P V for each
+      // the stage in halves of 32 keys: S^T, softmax, then P V for each
 #pragma unroll
-      for (int hv = 0; hv < 2; ++hv) {
+      for (int hv = 0; hv < kPfKeys / 32; ++hv) {
         if (hv < hv0) continue;
         const int kb = s * kPfKeys + 32 * hv;
         const bool masked = kb + 32 > free_end;
@@ -533,7 +544,7 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
         const int row = chunk * 16 / row_bytes;
         dst[r] = u32x4{0u, 0u, 0u, 0u};
         if (chunk < chunks && kb + row < key_end) {
-          const int id = sm_ids[4 * s + row / kTileTokens];
+          const int id = sm_ids[kPfStageTiles * s + row / kTileTokens];
           const int64_t off = static_cast<int64_t>(id + g_tile) * tile_bytes +
                               (row % kTileTokens) * row_bytes + (chunk * 16) % row_bytes;
           dst[r] = *reinterpret_cast<const u32x4*>(pool + off);
@@ -620,7 +631,7 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
     auto dma = [&](uint8_t* kdst, uint8_t* vdst, int s) {
       // rows past the context (last stage) read the sequence's last block
       // and are zeroed after they land
-      const int id = sm_ids[min(4 * s + wave * 4 / kPfWaves, nblk - 1)];
+      const int id = sm_ids[min(kPfStageTiles * s + wave * kPfStageTiles / kPfWaves, nblk - 1)];
       const int64_t base = static_cast<int64_t>(id + g_tile) * IO::tile_bytes;
 #pragma unroll
       for (int k = 0; k < kInsts; ++k) {
@@ -647,15 +658,10 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
     auto kbuf = [&](int i) { return reinterpret_cast<uint8_t*>(sm_kd[i]); };
     auto vbuf = [&](int i) { return reinterpret_cast<uint8_t*>(sm_vd[i]); };
     auto step = [&](auto slow_tag, int s, int cur) __attribute__((always_inline)) -> int {
-      // this wave's loads of stage s landed (those of later stages may fly)
-      if (kPfBufs == 3 && s + 1 < nstages) {
-        static_assert(kPfBufs == 2 || kLoads == 2 || kLoads == 4 || kLoads == 8, "wait count");
-        if constexpr (kLoads == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-        else if constexpr (kLoads == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      } else {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      }
+      // this wave's loads of stage s landed (those of the kPfBufs - 2 later
+      // stages already issued may fly; near the end, wait for all)
+      if (kPfBufs > 2 && s + kPfBufs - 2 < nstages) wait_vmcnt<(kPfBufs - 2) * kLoads>();
+      else wait_vmcnt<0>();
       if (s == nstages - 1) zero_tail(vbuf(cur), s);
       __syncthreads();                                      // all of stage s is in LDS; stage s-1 is done
       if (s + kPfBufs - 1 < nstages) {
