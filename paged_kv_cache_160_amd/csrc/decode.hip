@@ -42,6 +42,7 @@
 //    that finishes last, was measured slower: the device-scope fences it
 //    needs write back L2.
 
+#include <limits.h>
 #include <math.h>
 
 #include <type_traits>
@@ -60,9 +61,14 @@ namespace pkv {
 #ifndef PKV_DECODE_NT
 #define PKV_DECODE_NT 0        // non-temporal K/V loads (measured slower: off)
 #endif
+#ifndef PKV_DECODE_ORDER
+#define PKV_DECODE_ORDER 1     // longest-first order for many single-partition workgroups
+#endif
 constexpr int kWaves = PKV_DECODE_WAVES;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxGroup = 16;
+constexpr int kMaxOrderSeqs = 256;   // longest-first order: batches of at most this many sequences
+static_assert(kMaxOrderSeqs <= PKV_DECODE_WAVES * 64, "one ranking thread per sequence");
 constexpr int kMaxPartitionBlocks = PKV_MAX_PARTITION_TOKENS / kTileTokens;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -347,6 +353,49 @@ __device__ __forceinline__ void pv_tile(const float (&p)[4], const Words<Geo<QT,
 // ---- the main kernel ------------------------------------------------------------
 
 
+// Index of the sequence at position r of the longest-first order of the
+// batch (ties: lower index first), which is a permutation of 0..num_seqs-1
+// for any length values.  Every thread of the workgroup calls it;
+// num_seqs <= kMaxOrderSeqs.
+__device__ __forceinline__ int seq_of_rank(const int32_t* context_lens, int num_seqs, int r, int tid,
+                                           int* sm_len, int* sm_part, int* sm_pick) {
+  // slots past num_seqs (to a multiple of 4) hold INT_MIN at index >= num_seqs:
+  // never longer than a real entry, and never tied with a lower index
+  const int padded = (num_seqs + 3) & ~3;
+  for (int t = tid; t < padded; t += kThreads) sm_len[t] = t < num_seqs ? context_lens[t] : INT_MIN;
+  __syncthreads();
+  // a batch already longest first (equal lengths included) is its own order
+  int unsorted = 0;
+  for (int t = tid; t + 1 < num_seqs; t += kThreads) unsorted |= sm_len[t] < sm_len[t + 1] ? 1 : 0;
+  if (!__syncthreads_or(unsorted)) return r;
+  // rank of sequence t = entries before it in the order; thread (k, t)
+  // counts over the k-th of nk slices of the batch
+  const int nk = num_seqs <= kThreads / 4 ? 4 : (num_seqs <= kThreads / 2 ? 2 : 1);
+  const int slice = ((padded / nk) + 3) & ~3;
+  if (tid < nk * num_seqs) {
+    const int t = tid % num_seqs;
+    const int k = tid / num_seqs;
+    const int lt = sm_len[t];
+    int rank = 0;
+    for (int u = k * slice; u < min(padded, (k + 1) * slice); u += 4) {
+      const int4 lu = *reinterpret_cast<const int4*>(sm_len + u);
+      rank += (lu.x > lt || (lu.x == lt && u < t)) ? 1 : 0;
+      rank += (lu.y > lt || (lu.y == lt && u + 1 < t)) ? 1 : 0;
+      rank += (lu.z > lt || (lu.z == lt && u + 2 < t)) ? 1 : 0;
+      rank += (lu.w > lt || (lu.w == lt && u + 3 < t)) ? 1 : 0;
+    }
+    sm_part[tid] = rank;
+  }
+  __syncthreads();
+  if (tid < num_seqs) {
+    int rank = 0;
+    for (int k = 0; k < nk; ++k) rank += sm_part[k * num_seqs + tid];
+    if (rank == r) *sm_pick = tid;
+  }
+  __syncthreads();
+  return *sm_pick;
+}
+
 // Quantised pools keep three waves per SIMD (their tiles are half as large,
 // so the registers fit); 16-bit and fp32 pools take two.
 template <typename KT>
@@ -368,9 +417,8 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   const int P = a.num_partitions;
   const int part = blockIdx.x % P;
   const int g = (blockIdx.x / P) % a.num_kv_heads;
-  const int b = blockIdx.x / (P * a.num_kv_heads);
-  const int group = a.num_q_heads / a.num_kv_heads;
   const int tid = threadIdx.x;
+  const int group = a.num_q_heads / a.num_kv_heads;
   const int wave = tid / kWave;
   const int lane = tid % kWave;
   const int c = lane & 15;
@@ -380,28 +428,56 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   const int tok0 = part * PS;
   const int blk0 = tok0 / kTileTokens;       // first 16-token unit of the partition
   const int pblk = PS / kTileTokens;         // units of a full partition
-  const int64_t out_row0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(g) * group;
-  const int32_t* table = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq;
   const int rs = block_shift(a.block_size);
+  const int max_units = a.max_blocks_per_seq << rs;
+  constexpr int kLoads = (kMaxPartitionBlocks + kThreads - 1) / kThreads;
 
   // The workgroup's first loads do not depend on each other and are issued
   // together: the context length, the query, and the block-table entries of
   // a full partition (read before the length is known; entries past the
   // sequence's end lie inside its table row and are never used).
-  int L = a.context_lens[b];
-
   // Q^T operand: lane (head column c, k-group j) holds q[head c][j*D/4 ...).
   Words<G::qWords> qop;
-  {
+  int phys[kLoads];
+  auto first_loads = [&](int bb) {
     const bool valid = c < group;
-    const uint8_t* qp = static_cast<const uint8_t*>(a.q) +
-                        ((out_row0 + (valid ? c : 0)) * D + j * (D / 4)) * G::qes;
+    const int64_t row0 = static_cast<int64_t>(bb) * a.num_q_heads + static_cast<int64_t>(g) * group;
+    const uint8_t* qp = static_cast<const uint8_t*>(a.q) + ((row0 + (valid ? c : 0)) * D + j * (D / 4)) * G::qes;
     load_words<G::qWords, false>(qop, qp);
     if (!valid) {
 #pragma unroll
       for (int i = 0; i < G::qWords; ++i) qop.w[i] = 0u;
     }
+    const int32_t* table = a.block_tables + static_cast<int64_t>(bb) * a.max_blocks_per_seq;
+#pragma unroll
+    for (int k = 0; k < kLoads; ++k) {
+      const int u = blk0 + tid + k * kThreads;
+      phys[k] = (tid + k * kThreads < pblk && u < max_units) ? table[u >> rs] : -1;
+    }
+  };
+
+  // Workgroups are dispatched in index order.  When many of them share the
+  // chip in turns (one partition per sequence), index r takes the r-th
+  // longest sequence, so long sequences start first and none starts last.
+  // The loads for sequence r go out first; they are repeated for the
+  // sequence the order names only when it is another one.
+  int b = blockIdx.x / (P * a.num_kv_heads);
+  int L = a.context_lens[b];
+  first_loads(b);
+#if PKV_DECODE_ORDER
+  if (a.order_by_length) {
+    __shared__ __attribute__((aligned(16))) int sm_len[kMaxOrderSeqs];
+    __shared__ int sm_part[kThreads];
+    __shared__ int sm_pick;
+    const int pick = seq_of_rank(a.context_lens, a.num_seqs, b, tid, sm_len, sm_part, &sm_pick);
+    if (pick != b) {
+      b = pick;
+      L = sm_len[b];
+      first_loads(b);
+    }
   }
+#endif
+  const int64_t out_row0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(g) * group;
 
   // The partition's tiles, staged in LDS once: a per-block table read from
   // global memory in front of the K/V loads would make the wave wait for
@@ -409,24 +485,14 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   // counted separately.  Unit u's entry is its tile index at KV head 0,
   // ((phys * Hkv) << rs) + (u & (2^rs - 1)), or -1 when the table names a
   // block outside the pool.
-  {
-    constexpr int kLoads = (kMaxPartitionBlocks + kThreads - 1) / kThreads;
-    const int max_units = a.max_blocks_per_seq << rs;
-    int phys[kLoads];
 #pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-      const int u = blk0 + tid + k * kThreads;
-      phys[k] = (tid + k * kThreads < pblk && u < max_units) ? table[u >> rs] : -1;
-    }
-#pragma unroll
-    for (int k = 0; k < kLoads; ++k) {
-      const int i = tid + k * kThreads;
-      const int u = blk0 + i;
-      if (i < pblk)
-        sm_ids[i] = (phys[k] >= 0 && phys[k] < a.num_blocks)
-                        ? ((phys[k] * a.num_kv_heads) << rs) + (u & ((1 << rs) - 1))
-                        : -1;
-    }
+  for (int k = 0; k < kLoads; ++k) {
+    const int i = tid + k * kThreads;
+    const int u = blk0 + i;
+    if (i < pblk)
+      sm_ids[i] = (phys[k] >= 0 && phys[k] < a.num_blocks)
+                      ? ((phys[k] * a.num_kv_heads) << rs) + (u & ((1 << rs) - 1))
+                      : -1;
   }
 
   L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * a.block_size)));
@@ -758,8 +824,12 @@ static int launch_typed(const DecodeArgs& a, hipStream_t stream, int stages) {
   if (stages & kStageAttend) {
     // fp32 tiles are twice as large: two in flight keep them in registers
     constexpr int pipe = std::is_same<KT, F32>::value ? 2 : PKV_DECODE_PIPE;
+    // longest first where the dispatcher hands out workgroups in turns
+    DecodeArgs la = a;
+    la.order_by_length = PKV_DECODE_ORDER && a.num_partitions == 1 && a.num_seqs >= 2 &&
+                         a.num_seqs <= kMaxOrderSeqs && grid >= 4 * 256;
     hipLaunchKernelGGL((paged_decode_kernel<QT, KT, VT, D, pipe>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kThreads), 0, stream, a);
+                       dim3(kThreads), 0, stream, la);
     rc = check_launch();
   }
   if (rc != PKV_OK || !(stages & kStageMerge) || a.num_partitions == 1) return rc;
