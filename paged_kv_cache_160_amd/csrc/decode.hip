@@ -824,7 +824,9 @@ static int launch_typed(const DecodeArgs& a, hipStream_t stream, int stages) {
   if (stages & kStageAttend) {
     // fp32 tiles are twice as large: two in flight keep them in registers
     constexpr int pipe = std::is_same<KT, F32>::value ? 2 : PKV_DECODE_PIPE;
-    // longest first where the dispatcher hands out workgroups in turns
+    // longest first where the dispatcher hands out workgroups in turns and
+    // each holds a whole sequence (split sequences already have workgroups of
+    // at most one partition each: the order measured no faster there)
     DecodeArgs la = a;
     la.order_by_length = PKV_DECODE_ORDER && a.num_partitions == 1 && a.num_seqs >= 2 &&
                          a.num_seqs <= kMaxOrderSeqs && grid >= 4 * 256;

@@ -24,9 +24,9 @@ from tests._parity import TOL, check_cache_rows, max_err, out_to_f64, say
 pytestmark = pytest.mark.gpu
 
 
-def _lens(kind: str, n: int, seed: int):
+def _lens(kind: str, n: int, seed: int, lmax: int):
     rng = np.random.default_rng(seed)
-    lens = rng.integers(1, 400, n)
+    lens = rng.integers(1, lmax, n)
     lens[3] = 0                                  # an empty sequence
     lens[5] = lens[9] = lens[n - 1] = lens[7]    # ties
     if kind == "sorted":
@@ -34,17 +34,17 @@ def _lens(kind: str, n: int, seed: int):
     return [int(x) for x in lens]
 
 
-CASES = [  # (kind, num_seqs, hq, hkv, head_dim, dtype)
-    ("ragged", 40, 32, 32, 64, "bf16"),
-    ("ragged", 100, 32, 16, 64, "f16"),
-    ("ragged", 200, 8, 8, 64, "bf16"),
-    ("sorted", 64, 16, 16, 128, "bf16"),
+CASES = [  # (kind, num_seqs, hq, hkv, head_dim, dtype, longest context + 1)
+    ("ragged", 40, 32, 32, 64, "bf16", 400),
+    ("ragged", 100, 32, 16, 64, "f16", 400),
+    ("ragged", 200, 8, 8, 64, "bf16", 400),
+    ("sorted", 64, 16, 16, 128, "bf16", 400),
 ]
 
 
 def _workload(case, seed=23):
-    kind, n, hq, hkv, d, dtype = case
-    return wl.custom_workload(n, hq, hkv, d, _lens(kind, n, seed), dtype=dtype, seed=seed,
+    kind, n, hq, hkv, d, dtype, lmax = case
+    return wl.custom_workload(n, hq, hkv, d, _lens(kind, n, seed, lmax), dtype=dtype, seed=seed,
                               extra_blocks=4 * n + 8)
 
 
