@@ -7,9 +7,10 @@ output row must still be its own sequence's attention ("KV Cache 和 vLLM"
 §1.2-1.3: out = softmax(q K^T / sqrt(d)) V over the sequence's cached
 tokens).  Batches in that regime - ragged with ties and an empty sequence,
 for each of the ranking's three slicings (up to 64, 128 and 256 sequences),
-and one already longest first (the kernel's shortcut) - are checked against
-the fp64 oracle; the fused step, which writes the step's K/V row through the
-same sequence index, is checked bit for bit against append-then-decode.
+one already longest first (the kernel's shortcut), and fp8 and int8 + int4
+caches - are checked against the fp64 oracle; the fused step, which writes
+the step's K/V row through the same sequence index, is checked bit for bit
+against append-then-decode.
 """
 import numpy as np
 import pytest
@@ -34,21 +35,24 @@ def _lens(kind: str, n: int, seed: int, lmax: int):
     return [int(x) for x in lens]
 
 
-CASES = [  # (kind, num_seqs, hq, hkv, head_dim, dtype, longest context + 1)
-    ("ragged", 40, 32, 32, 64, "bf16", 400),
-    ("ragged", 100, 32, 16, 64, "f16", 400),
-    ("ragged", 200, 8, 8, 64, "bf16", 400),
-    ("sorted", 64, 16, 16, 128, "bf16", 400),
+CASES = [  # (kind, num_seqs, hq, hkv, head_dim, source dtype, longest context + 1, cache dtype)
+    ("ragged", 40, 32, 32, 64, "bf16", 400, None),
+    ("ragged", 100, 32, 16, 64, "f16", 400, None),
+    ("ragged", 200, 8, 8, 64, "bf16", 400, None),
+    ("sorted", 64, 16, 16, 128, "bf16", 400, None),
+    ("ragged", 48, 32, 32, 128, "f32", 400, "fp8_e4m3"),
+    ("ragged", 48, 32, 32, 64, "f32", 400, "int8_int4"),
 ]
 
 
 def _workload(case, seed=23):
-    kind, n, hq, hkv, d, dtype, lmax = case
-    return wl.custom_workload(n, hq, hkv, d, _lens(kind, n, seed, lmax), dtype=dtype, seed=seed,
+    kind, n, hq, hkv, d, dtype, lmax, cache = case
+    return wl.custom_workload(n, hq, hkv, d, _lens(kind, n, seed, lmax), dtype=dtype, cache_dtype=cache,
+                              q_dtype="bf16" if cache else None, seed=seed,
                               extra_blocks=4 * n + 8)
 
 
-@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-{c[1]}x{c[3]}" for c in CASES])
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-{c[1]}x{c[3]}-{c[7] or c[5]}" for c in CASES])
 def test_longest_first_rows_match_oracle(case):
     w = _workload(case)
     ops = wl.setup_ops(w)
