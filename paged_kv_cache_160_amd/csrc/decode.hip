@@ -401,7 +401,9 @@ __device__ __forceinline__ int seq_of_rank(const int32_t* context_lens, int num_
 template <typename KT>
 constexpr int decode_min_blocks() { return KT::quantised ? 3 : 2; }
 
-template <typename QT, typename KT, typename VT, int D, int PIPE>
+// ORDER: workgroups take sequences longest first (a separate instance, so
+// launches without the order carry none of its code or registers).
+template <typename QT, typename KT, typename VT, int D, int PIPE, bool ORDER>
 __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decode_kernel(DecodeArgs a) {
   using G = Geo<QT, KT, VT, D>;
   constexpr bool kQK = KT::quantised;
@@ -464,8 +466,7 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   int b = blockIdx.x / (P * a.num_kv_heads);
   int L = a.context_lens[b];
   first_loads(b);
-#if PKV_DECODE_ORDER
-  if (a.order_by_length) {
+  if constexpr (ORDER) {
     __shared__ __attribute__((aligned(16))) int sm_len[kMaxOrderSeqs];
     __shared__ int sm_part[kThreads];
     __shared__ int sm_pick;
@@ -476,7 +477,6 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
       first_loads(b);
     }
   }
-#endif
   const int64_t out_row0 = static_cast<int64_t>(b) * a.num_q_heads + static_cast<int64_t>(g) * group;
 
   // The partition's tiles, staged in LDS once: a per-block table read from
@@ -827,11 +827,14 @@ static int launch_typed(const DecodeArgs& a, hipStream_t stream, int stages) {
     // longest first where the dispatcher hands out workgroups in turns and
     // each holds a whole sequence (split sequences already have workgroups of
     // at most one partition each: the order measured no faster there)
-    DecodeArgs la = a;
-    la.order_by_length = PKV_DECODE_ORDER && a.num_partitions == 1 && a.num_seqs >= 2 &&
-                         a.num_seqs <= kMaxOrderSeqs && grid >= 4 * 256;
-    hipLaunchKernelGGL((paged_decode_kernel<QT, KT, VT, D, pipe>), dim3(static_cast<unsigned>(grid)),
-                       dim3(kThreads), 0, stream, la);
+    const bool order = PKV_DECODE_ORDER && a.num_partitions == 1 && a.num_seqs >= 2 &&
+                       a.num_seqs <= kMaxOrderSeqs && grid >= 4 * 256;
+    if (order)
+      hipLaunchKernelGGL((paged_decode_kernel<QT, KT, VT, D, pipe, true>), dim3(static_cast<unsigned>(grid)),
+                         dim3(kThreads), 0, stream, a);
+    else
+      hipLaunchKernelGGL((paged_decode_kernel<QT, KT, VT, D, pipe, false>), dim3(static_cast<unsigned>(grid)),
+                         dim3(kThreads), 0, stream, a);
     rc = check_launch();
   }
   if (rc != PKV_OK || !(stages & kStageMerge) || a.num_partitions == 1) return rc;

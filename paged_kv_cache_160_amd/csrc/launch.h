@@ -48,8 +48,6 @@ struct DecodeArgs {
   pkv_dtype src_dtype;
   float* part_ml;          // [num_seqs][num_q_heads][num_partitions][2]  (m, l)
   float* part_acc;         // [num_seqs][num_q_heads][num_partitions][head_dim]
-  // set by the launcher: workgroups take sequences longest first
-  int order_by_length;
 };
 
 // What a decode call launches: the attention kernel and, when sequences are
