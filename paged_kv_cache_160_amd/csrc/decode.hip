@@ -56,7 +56,10 @@ namespace pkv {
 #define PKV_DECODE_WAVES 4     // waves per workgroup
 #endif
 #ifndef PKV_DECODE_PIPE
-#define PKV_DECODE_PIPE 3      // blocks in flight per wave
+#define PKV_DECODE_PIPE 2      // blocks in flight per wave, 16-bit caches
+#endif
+#ifndef PKV_DECODE_PIPE_Q
+#define PKV_DECODE_PIPE_Q 3    // blocks in flight per wave, quantised caches
 #endif
 #ifndef PKV_DECODE_NT
 #define PKV_DECODE_NT 0        // non-temporal K/V loads (measured slower: off)
@@ -822,8 +825,11 @@ static int launch_typed(const DecodeArgs& a, hipStream_t stream, int stages) {
   if (grid > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
   int rc = PKV_OK;
   if (stages & kStageAttend) {
-    // fp32 tiles are twice as large: two in flight keep them in registers
-    constexpr int pipe = std::is_same<KT, F32>::value ? 2 : PKV_DECODE_PIPE;
+    // fp32 tiles are twice as large: two in flight keep them in registers.
+    // 16-bit caches: two (interleaved A/B: 1.3% faster than three on the
+    // Llama-3-8B layer shape, 5% on the shared-prefix batch); quantised
+    // caches, whose tiles are half as large: three.
+    constexpr int pipe = std::is_same<KT, F32>::value ? 2 : (KT::quantised ? PKV_DECODE_PIPE_Q : PKV_DECODE_PIPE);
     // longest first where the dispatcher hands out workgroups in turns and
     // each holds a whole sequence (split sequences already have workgroups of
     // at most one partition each: the order measured no faster there)
