@@ -19,8 +19,12 @@ from .cache import Pool
 
 
 class OracleState:
-    def __init__(self, w: wl.Workload, build_pool: bool = True, num_blocks: Optional[int] = None):
+    def __init__(self, w: wl.Workload, build_pool: bool = True, num_blocks: Optional[int] = None,
+                 pool_seqs: Optional[set] = None):
+        """``pool_seqs``: write rows into the pool for these sequences only
+        (None: all); the allocator still runs every operation."""
         self.w = w
+        self.pool_seqs = pool_seqs
         nb = num_blocks or w.num_blocks
         self.alloc = BlockAllocatorModel(nb, w.max_blocks_per_seq, w.block_size)
         self.pool = Pool(nb, w.num_kv_heads, w.head_dim, w.cache_dtype, w.block_size) if build_pool else None
@@ -50,7 +54,7 @@ class OracleState:
             if self.pool is not None:
                 for src, dst in pairs:
                     self.pool.copy_block(src, dst)
-                if seq < wl.CHURN_ID_BASE and n:
+                if seq < wl.CHURN_ID_BASE and n and (self.pool_seqs is None or seq in self.pool_seqs):
                     k, v = self.rows(seq)
                     self.pool.append(k[start:start + n], v[start:start + n], slots)
         else:

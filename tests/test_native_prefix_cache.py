@@ -85,3 +85,28 @@ def test_enable_rules():
     with pytest.raises(pkv.PagedKVError) as e:
         a.create_cached(1, [1])                         # live id
     assert e.value.code == -1
+
+
+def test_batch_error_precedence_matches_model():
+    # a failing batch decode-step append reports the error of the first
+    # sequence (in the order the batch names them) that is unknown, swapped
+    # out or named again, and changes nothing
+    from oracle.allocator import AllocError
+    codes = {"unknown_seq": -6, "invalid_arg": -1}
+    for batch in ([1, 1, 99], [1, 99, 1], [99, 1, 1], [1, 2, 2], [2, 3, 1, 3, 99]):
+        for lib_like in (True, False):
+            a = _native(16, 8) if lib_like else PrefixCachingAllocatorModel(16, 8)
+            for s in (1, 2, 3):
+                a.create(s)
+                a.append_tokens(s, list(range(20)))
+            if lib_like:
+                with pytest.raises(pkv.PagedKVError) as e:
+                    a.batch_append_tokens(batch, [7] * len(batch))
+                got_lib = e.value.code
+                assert a.stats()["used_blocks"] == 6 and [a.seq_len(s) for s in (1, 2, 3)] == [20] * 3
+            else:
+                with pytest.raises(AllocError) as e:
+                    a.batch_append_tokens(batch, [7] * len(batch))
+                got_model = codes[e.value.kind]
+        first_bad = next(s for i, s in enumerate(batch) if s == 99 or s in batch[:i])
+        assert got_lib == got_model == (codes["unknown_seq"] if first_bad == 99 else codes["invalid_arg"]), batch

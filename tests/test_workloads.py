@@ -62,3 +62,20 @@ def test_churn_script_respects_capacity():
         else:
             used -= live.pop(arg)
     assert len(w.churn_release) == len(live)
+
+
+def test_workload5_golden_matches_generator():
+    # the stored expectations of the long fp8 workload were written by
+    # tests/golden/make_workload5_expected.py from these very inputs
+    import json
+    import os
+    from tests.golden.make_workload5_expected import input_fingerprint
+    here = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+    with open(os.path.join(here, "workload5_expected.json")) as f:
+        rec = json.load(f)
+    w = workloads.make_workload(5)
+    assert rec["input_fingerprint"] == input_fingerprint(w)
+    out = np.load(os.path.join(here, "workload5_expected.npz"))["out"]
+    assert out.shape == (w.num_seqs, w.num_q_heads, w.head_dim) and np.all(np.isfinite(out))
+    assert [s["seq"] for s in rec["sequences"]] == list(range(w.num_seqs))
+    assert all(s["context_len"] == L for s, L in zip(rec["sequences"], w.context_lens))
