@@ -367,10 +367,14 @@ class PrefixCachingAllocatorModel(BlockAllocatorModel):
     def batch_append_tokens(self, seqs, tokens):
         """One token for each sequence, in order; all or nothing."""
         seqs = [int(s) for s in seqs]
+        # the batch is checked in order before any block is taken: the first
+        # sequence that is unknown, swapped out or named again decides the error
+        seen = set()
         for s in seqs:
-            self._resident(s)               # every sequence is checked before capacity
-        if len(set(seqs)) != len(seqs):
-            raise AllocError("invalid_arg")
+            self._resident(s)
+            if s in seen:
+                raise AllocError("invalid_arg")
+            seen.add(s)
         saved = copy.deepcopy(self.__dict__)
         slots, pairs = [], []
         try:
