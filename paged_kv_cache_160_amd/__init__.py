@@ -131,6 +131,21 @@ def _stream(stream) -> Optional[int]:
     return int(stream)
 
 
+def _workspace_for(need: int, workspace: Optional[torch.Tensor], device, stream) -> Optional[torch.Tensor]:
+    """The caller's workspace if it holds ``need`` bytes, else a new one.  A
+    new workspace is allocated on the stream the kernels run on, so that
+    PyTorch's caching allocator hands its memory to no other stream's
+    allocation while those kernels may still use it (the tensor may be
+    dropped as soon as the call returns)."""
+    if not need or (workspace is not None and workspace.numel() * workspace.element_size() >= need):
+        return workspace
+    if stream is None:
+        return torch.zeros(need, dtype=torch.uint8, device=device)
+    s = stream if isinstance(stream, torch.cuda.Stream) else torch.cuda.ExternalStream(int(stream), device=device)
+    with torch.cuda.stream(s):
+        return torch.zeros(need, dtype=torch.uint8, device=device)
+
+
 def _pool_geometry(k_pool: torch.Tensor) -> Tuple[int, int, int, int]:
     """(num_blocks, num_kv_heads, head_dim, block_size) of a K pool
     ``[num_blocks, num_kv_heads, block_size, head_dim]``, block_size 16 or 32."""
@@ -203,8 +218,7 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Ten
         scale = 1.0 / math.sqrt(d)
     cdt = _pool_code(k_pool, v_pool, k_scale, v_scale)
     need = workspace_size(B, hq, hkv, d, max_context_len, partition_size, cdt)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace_for(need, workspace, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(_lib.lib().paged_attention_decode_bs(
         _ptr(out), _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale), _ptr(v_scale),
@@ -284,8 +298,7 @@ def _decode_append_call(fn_name, out, q, k_new, v_new, k_pool, v_pool, slot_mapp
         scale = 1.0 / math.sqrt(d)
     cdt = _pool_code(k_pool, v_pool, k_scale, v_scale)
     need = workspace_size(B, hq, hkv, d, max_context_len, partition_size, cdt)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.zeros(need, dtype=torch.uint8, device=q.device)
+    workspace = _workspace_for(need, workspace, q.device, stream)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     src_code = dtype_code(k_new.dtype) if k_new is not None else dtype_code(q.dtype)
     _check(getattr(_lib.lib(), fn_name + "_bs")(
