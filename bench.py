@@ -15,11 +15,14 @@ value    = KV tokens attended per second = sum over timed steps and layers of
            sum_b L_b, divided by the timed wall time.
 roofline = the decode call's algorithmic bytes (K/V [+ fp8 scales] of every
            attended token, q, out, block-table entries, lengths, and the
-           appended K/V row) divided by the attention kernel's average
-           duration from HIP events on the launch stream (every 8th layer by
-           default); the whole call (with the merge) is reported beside it.
+           appended K/V row) divided by the whole call's average duration
+           (attention kernel + partition merge), from HIP events on the launch
+           stream around each step's run of consecutive layer calls; the
+           attention kernel alone is reported beside it.
 cpu_baseline = the fp64 oracle (test infrastructure) timed on the host over a
-           bounded sample of the same workload.
+           bounded sample of the same workload: single-sequence decodes
+           through the oracle's paged pool, block-table gather and widening
+           to fp64 inside the timed region.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -68,9 +71,6 @@ def parse():
     ap.add_argument("--probe-read", action="store_true",
                     help="only measure a cold HBM reference (device-to-device copies of 128 MiB, 256 MiB of "
                          "traffic per launch, rotating through 16 slices of a 2 GiB source) and exit")
-    ap.add_argument("--event-every", type=int, default=8,
-                    help="bracket every Nth layer's decode call with HIP events (default 8: each event pair "
-                         "adds a few microseconds of GPU time, so the calls in between run undisturbed)")
     ap.add_argument("--unfused", action="store_true",
                     help="write the step's rows with kv_cache_append, then attend (default: the write is fused "
                          "into the attention kernel)")
@@ -309,11 +309,11 @@ def main():
     if args.partition_size:
         ps_used = args.partition_size
     stream = torch.cuda.current_stream()
-    timed_layers = [l for l in range(layers) if l % max(1, args.event_every) == 0]
-    # per sampled call: before the attention kernel, after it (= before the
-    # merge kernel), after the merge
-    ev = {(s_, l): tuple(torch.cuda.Event(enable_timing=True) for _ in range(3))
-          for s_ in range(args.warmup, n_steps) for l in timed_layers}
+    # One event pair per timed step, around its run of `layers` consecutive
+    # decode calls: per-call times are the span divided by the calls in it,
+    # so no event sits between two calls of the run.
+    step_ev = {s_: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for s_ in range(args.warmup, n_steps)}
     tokens_timed = 0
     bytes_timed = 0
 
@@ -333,6 +333,42 @@ def main():
              for l in range(layers)]
     ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
 
+    def attend(s, l, max_len):
+        """Layer l's attention kernel of step s (cache write fused unless
+        --unfused wrote it already)."""
+        kp, vp, ksp, vsp = pools[l]
+        kl = knew.data_ptr() + (s * layers + l) * kv_stride
+        vl = vnew.data_ptr() + (s * layers + l) * kv_stride
+        o_ptr = outs.data_ptr() + l * out_stride
+        q_ptr = qs.data_ptr() + (s * layers + l) * q_stride
+        if args.one_call:
+            rc = lib.paged_attention_decode_append_bs(o_ptr, q_ptr, kl, vl, kp, vp, ksp, vsp,
+                                                      d_slots.data_ptr(), d_tables.data_ptr(), d_lens.data_ptr(),
+                                                      B, hq, hkv, D, w.num_blocks, bs, mb, max_len, scale,
+                                                      q_code, src_code, cache_code, args.partition_size,
+                                                      ws_ptr, ws_bytes, sp)
+            if rc:
+                raise pkv.PagedKVError(rc, "paged_attention_decode_append")
+            return
+        slot_ptr = None if args.unfused else d_slots.data_ptr()
+        rc = lib.paged_attention_decode_append_partials_bs(o_ptr, q_ptr, kl, vl, kp, vp, ksp, vsp, slot_ptr,
+                                                           d_tables.data_ptr(), d_lens.data_ptr(), B, hq, hkv,
+                                                           D, w.num_blocks, bs, mb, max_len, scale, q_code,
+                                                           src_code, cache_code, args.partition_size, ws_ptr,
+                                                           ws_bytes, sp)
+        if rc:
+            raise pkv.PagedKVError(rc, "paged_attention_decode_append_partials")
+
+    def merge(l, max_len):
+        """Layer l's partition merge (nothing is launched when no sequence is split)."""
+        if args.one_call:
+            return
+        o_ptr = outs.data_ptr() + l * out_stride
+        rc = lib.paged_attention_merge_partials_bs(o_ptr, d_lens.data_ptr(), B, hq, hkv, D, bs, mb, max_len,
+                                                   q_code, cache_code, args.partition_size, ws_ptr, ws_bytes, sp)
+        if rc:
+            raise pkv.PagedKVError(rc, "paged_attention_merge_partials")
+
     def step(s, timed):
         nonlocal tokens_timed, bytes_timed
         slots, pairs = cache.alloc.batch_append_one(seqs)
@@ -346,52 +382,23 @@ def main():
         lens = h_lens[s].tolist()
         max_len = max(lens)
         sum_l = sum(lens)
-        kbase = knew.data_ptr() + s * layers * kv_stride
-        vbase = vnew.data_ptr() + s * layers * kv_stride
-        qbase = qs.data_ptr() + s * layers * q_stride
-        for l in range(layers):
-            kp, vp, ksp, vsp = pools[l]
-            kl, vl = kbase + l * kv_stride, vbase + l * kv_stride
-            if args.unfused:
-                rc = lib.kv_cache_append_bs(kl, vl, kp, vp, ksp, vsp, d_slots.data_ptr(), B, hkv, D, w.num_blocks,
-                                            bs, src_code, cache_code, sp)
+        if args.unfused:
+            for l in range(layers):
+                kp, vp, ksp, vsp = pools[l]
+                kl = knew.data_ptr() + (s * layers + l) * kv_stride
+                vl = vnew.data_ptr() + (s * layers + l) * kv_stride
+                rc = lib.kv_cache_append_bs(kl, vl, kp, vp, ksp, vsp, d_slots.data_ptr(), B, hkv, D,
+                                            w.num_blocks, bs, src_code, cache_code, sp)
                 if rc:
                     raise pkv.PagedKVError(rc, "kv_cache_append")
-            e = ev.get((s, l)) if timed else None
-            if e:
-                e[0].record(stream)
-            o_ptr, q_ptr = outs.data_ptr() + l * out_stride, qbase + l * q_stride
-            if args.one_call:
-                rc = lib.paged_attention_decode_append_bs(o_ptr, q_ptr, kl, vl, kp, vp, ksp, vsp,
-                                                          d_slots.data_ptr(), d_tables.data_ptr(), d_lens.data_ptr(),
-                                                          B, hq, hkv, D, w.num_blocks, bs, mb, max_len, scale,
-                                                          q_code, src_code, cache_code, args.partition_size,
-                                                          ws_ptr, ws_bytes, sp)
-                if rc:
-                    raise pkv.PagedKVError(rc, "paged_attention_decode_append")
-                if e:
-                    e[1].record(stream)
-                    e[2].record(stream)
-                continue
-            # split form: the attention kernel (with the cache write fused in,
-            # unless --unfused wrote it already), then the partition merge
-            slot_ptr = None if args.unfused else d_slots.data_ptr()
-            rc = lib.paged_attention_decode_append_partials_bs(o_ptr, q_ptr, kl, vl, kp, vp, ksp, vsp, slot_ptr,
-                                                               d_tables.data_ptr(), d_lens.data_ptr(), B, hq, hkv,
-                                                               D, w.num_blocks, bs, mb, max_len, scale, q_code,
-                                                               src_code, cache_code, args.partition_size, ws_ptr,
-                                                               ws_bytes, sp)
-            if rc:
-                raise pkv.PagedKVError(rc, "paged_attention_decode_append_partials")
-            if e:
-                e[1].record(stream)
-            rc = lib.paged_attention_merge_partials_bs(o_ptr, d_lens.data_ptr(), B, hq, hkv, D, bs, mb, max_len,
-                                                       q_code, cache_code, args.partition_size, ws_ptr, ws_bytes,
-                                                       sp)
-            if rc:
-                raise pkv.PagedKVError(rc, "paged_attention_merge_partials")
-            if e:
-                e[2].record(stream)
+        e = step_ev.get(s) if timed else None
+        if e:
+            e[0].record(stream)
+        for l in range(layers):
+            attend(s, l, max_len)
+            merge(l, max_len)
+        if e:
+            e[1].record(stream)
         if timed:
             tokens_timed += sum_l * layers
             kv_bytes = sum_l * hkv * (D * (kb_el + vb_el) + 8 * nscale)
@@ -401,27 +408,50 @@ def main():
             # inside the K/V bytes already counted)
             new_bytes = 0 if args.unfused else B * hkv * D * 2 * ES[w.src_dtype] + B * 8
             bytes_timed += (kv_bytes + qo_bytes + table_bytes + new_bytes) * layers
+        return max_len
 
     for s in range(args.warmup):
         step(s, False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.warmup, n_steps):
-        step(s, True)
+        last_max_len = step(s, True)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    kern_s = sum(a.elapsed_time(b) for a, b, _ in ev.values()) / len(ev) / 1e3
-    call_s = sum(a.elapsed_time(c) for a, _, c in ev.values()) / len(ev) / 1e3
+    per_call_us = [a.elapsed_time(b) * 1e3 / layers for a, b in step_ev.values()]
+    call_s = sum(per_call_us) / len(per_call_us) / 1e6
     calls = args.steps * layers
     bytes_per_call = bytes_timed / calls
-    achieved = bytes_per_call / kern_s / 1e9
+    achieved = bytes_per_call / call_s / 1e9
     value = tokens_timed / elapsed
-    log(f"[bench] {args.steps} steps in {elapsed * 1e3:.2f} ms; attention kernel avg {kern_s * 1e6:.2f} us "
-        f"({achieved:.0f} GB/s algorithmic); whole decode call {call_s * 1e6:.2f} us "
-        f"({bytes_per_call / call_s / 1e9:.0f} GB/s); {value / 1e9:.3f} G KV tokens/s")
-    kern_pct = percentiles([a.elapsed_time(b) * 1e3 for a, b, _ in ev.values()])
-    log(f"[bench] attention kernel (events) median {kern_pct['median_us']:.2f} us, p10 {kern_pct['p10_us']:.2f}, "
-        f"p90 {kern_pct['p90_us']:.2f} over {len(ev)} sampled calls")
+    call_pct = percentiles(per_call_us)
+    log(f"[bench] {args.steps} steps in {elapsed * 1e3:.2f} ms; whole decode call {call_s * 1e6:.2f} us "
+        f"(runs of {layers} consecutive calls, {achieved:.0f} GB/s algorithmic, "
+        f"{100 * achieved / HBM_PEAK_GBPS:.1f}% of peak); {value / 1e9:.3f} G KV tokens/s")
+
+    # The two kernels of the call apart (after the timed region, last step's
+    # arguments): runs of `layers` consecutive attention kernels, then of
+    # merges, one event pair around each run.
+    def time_runs(fn, reps=10):
+        spans = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for l in range(layers):
+                fn(l)
+            e1.record(stream)
+            spans.append((e0, e1))
+        torch.cuda.synchronize()
+        return percentiles([a.elapsed_time(b) * 1e3 / layers for a, b in spans])
+
+    last_s = n_steps - 1
+    kern_pct = time_runs(lambda l: attend(last_s, l, last_max_len))
+    split = not args.one_call and ps_used < last_max_len
+    merge_pct = time_runs(lambda l: merge(l, last_max_len)) if split else None
+    kern_s = kern_pct["median_us"] / 1e6
+    log(f"[bench] attention kernel alone: median {kern_pct['median_us']:.2f} us per call "
+        f"({bytes_per_call / kern_s / 1e9:.0f} GB/s)"
+        + (f"; merge kernel alone: median {merge_pct['median_us']:.2f} us" if merge_pct else ""))
     traffic = load_traffic(w.name)
 
     # Side measurements after the timed region (not part of the value): the
@@ -483,17 +513,22 @@ def main():
         },
         "achieved_hbm_gbps": achieved,
         "pct_of_peak": 100.0 * achieved / HBM_PEAK_GBPS,
-        "attention_kernel_us": kern_s * 1e6,
-        "attention_kernel_us_percentiles": kern_pct,
         "decode_call_us": call_s * 1e6,
+        "decode_call_us_percentiles": call_pct,
+        "attention_kernel_us_percentiles": kern_pct,
+        "attention_kernel_hbm_gbps": bytes_per_call / kern_s / 1e9,
+        "merge_kernel_us_percentiles": merge_pct,
         "side_kernels_us": side,
-        "decode_call_hbm_gbps": bytes_per_call / call_s / 1e9,
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
-            "kernel": "paged_decode_kernel" + ("" if args.unfused else " (cache write fused)")
-                      + ("; timed with the partition merge (one call)" if args.one_call else ""),
+            "kernel": ("whole decode call: paged_decode_kernel" + ("" if args.unfused else " (cache write fused)")
+                       + (" + partition_merge_kernel" if split else "")),
+            "timing": f"HIP events around runs of {layers} consecutive calls on the launch stream, "
+                      f"{args.steps} runs; per-call time = span / {layers}",
             "bytes_per_launch": bytes_per_call,
+            "attention_kernel_alone": {"us": kern_s * 1e6, "achieved": bytes_per_call / kern_s / 1e9,
+                                       "frac": bytes_per_call / kern_s / 1e9 / HBM_PEAK_GBPS},
         },
         "cpu_baseline": cpu,
     }
@@ -501,61 +536,64 @@ def main():
 
 
 def cpu_baseline(w, budget_s: float):
-    """The fp64 oracle on the host: whole sequences of layer 0, rows generated
-    beforehand (not timed), attention timed until the budget is spent."""
+    """The fp64 oracle on the host, decoding through its own paged pool: the
+    workload's setup script builds the oracle's allocator and pool (not
+    timed); then single-sequence decodes of layer 0, cycling over the batch,
+    are timed until the budget is spent.  Each decode gathers the sequence's
+    K/V through its block table, widens (dequantises) them to fp64 and
+    attends - the paged work the GPU call does."""
     import numpy as np
     import psutil
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import workloads as wl
-    from oracle import attention
+    from oracle import attention, scenario
 
     scale = 1.0 / math.sqrt(w.head_dim)
     q = wl.queries(w, 0)
-    n_pre = min(w.num_seqs, 4)
-    pre = []
-    for b in range(n_pre):
-        L = w.context_lens[b]
-        K, V = attention.rows_as_cached(wl.kv_rows(w, b, "k", L), wl.kv_rows(w, b, "v", L), w.cache_dtype)
-        pre.append((b, K, V))
+    # the sample: the first sequences up to 65536 tokens (32768 for quantised
+    # caches, whose rows the oracle quantises one by one while building)
+    cap = 32768 if w.cache_dtype not in ("f32", "f16", "bf16") else 65536
+    seqs = []
+    for b in range(w.num_seqs):
+        if seqs and sum(w.context_lens[x] for x in seqs) + w.context_lens[b] > cap:
+            break
+        seqs.append(b)
+    t_setup = time.perf_counter()
+    st = scenario.OracleState(w, build_pool=True, pool_seqs=set(seqs)).run(wl.setup_ops(w))
+    tables, lens = st.tables(seqs)
+    log(f"[cpu] oracle pool built in {time.perf_counter() - t_setup:.1f}s (not timed)")
+
+    def run(limit_s):
+        t0_ = time.perf_counter()
+        tokens_, done_ = 0, 0
+        while True:
+            i = done_ % len(seqs)
+            b = seqs[i]
+            attention.decode_paged(q[b:b + 1], st.pool, tables[i:i + 1], lens[i:i + 1], scale)
+            tokens_ += int(lens[i])
+            done_ += 1
+            if time.perf_counter() - t0_ >= limit_s and done_ >= 1:
+                return tokens_, done_, time.perf_counter() - t0_
+
     proc = psutil.Process()
     c0 = proc.cpu_times()
-    t0 = time.perf_counter()
-    tokens = 0
-    seqs_done = 0
-    while True:
-        b, K, V = pre[seqs_done % n_pre]
-        attention.attend(q[b], K, V, scale)
-        tokens += K.shape[0]
-        seqs_done += 1
-        if time.perf_counter() - t0 >= budget_s and seqs_done >= n_pre:
-            break
-    wall = time.perf_counter() - t0
+    tokens, seqs_done, wall = run(budget_s)
     c1 = proc.cpu_times()
     busy = (c1.user - c0.user + c1.system - c0.system) / wall
     blas = [i.get("num_threads") for i in threadpool_info() if i.get("user_api") == "blas"]
     allowed = len(os.sched_getaffinity(0))
     log(f"[cpu] oracle: {seqs_done} sequence decodes, {tokens} KV tokens in {wall:.1f}s "
         f"({tokens / wall / 1e6:.2f} M KV tokens/s), {busy:.1f} cores busy on average")
-    # the same loop on one thread, for a short sample
-    from threadpoolctl import threadpool_limits
     with threadpool_limits(limits=1):
-        t1 = time.perf_counter()
-        tokens1 = 0
-        done1 = 0
-        while time.perf_counter() - t1 < min(3.0, budget_s) or done1 < 1:
-            b, K, V = pre[done1 % n_pre]
-            attention.attend(q[b], K, V, scale)
-            tokens1 += K.shape[0]
-            done1 += 1
-        wall1 = time.perf_counter() - t1
+        tokens1, done1, wall1 = run(min(3.0, budget_s))
     log(f"[cpu] oracle on one thread: {done1} sequence decodes, {tokens1 / wall1 / 1e6:.2f} M KV tokens/s")
     return {
         "value": tokens / wall, "unit": "KV tokens/s", "cores": max(1, round(busy)),
         "kind": "oracle",
-        "sample": (f"{seqs_done} single-sequence decodes (all {w.num_q_heads} query heads, "
-                   f"L={w.context_lens[0]}) cycling over the first {n_pre} sequences of layer 0 of "
-                   f"{w.name}; fp64 numpy; rows generated and dequantised before timing; "
+        "sample": (f"{seqs_done} single-sequence decodes (all {w.num_q_heads} query heads) of layer 0 of "
+                   f"{w.name}, cycling over its first {len(seqs)} sequences ({sum(int(x) for x in lens)} tokens), through the oracle's paged pool: "
+                   f"block-table gather, widening to fp64 and attention timed; fp64 numpy; "
                    f"{busy:.2f} cores busy on average, {allowed} allowed, BLAS threads {blas}"),
         "single_thread_value": tokens1 / wall1,
         "single_thread_sample": f"{done1} of the same decodes with BLAS limited to one thread",
