@@ -87,8 +87,10 @@ def parse():
                     help="swap row: out and in on two streams at once (PagedKVCache.swap), or one after the other")
     ap.add_argument("--cached", type=int, default=3584, help="prefill row: cached tokens per sequence")
     ap.add_argument("--chunk", type=int, default=512, help="prefill row: chunk tokens per sequence")
-    ap.add_argument("--one-call", action="store_true",
-                    help="use the one-call paged_attention_decode_append (events then bracket both launches)")
+    ap.add_argument("--split", action="store_true",
+                    help="time the split form (paged_attention_decode_append_partials, then "
+                         "paged_attention_merge_partials: the merge as a second launch) instead of the one-call "
+                         "paged_attention_decode_append (one launch; the last partition of a sequence merges)")
     return ap.parse_args()
 
 
@@ -334,14 +336,16 @@ def main():
     ws_ptr, ws_bytes = ws.data_ptr(), ws.numel()
 
     def attend(s, l, max_len):
-        """Layer l's attention kernel of step s (cache write fused unless
-        --unfused wrote it already)."""
+        """Layer l's attention kernel of step s: the one-call form (cache write
+        fused, partitions merged in the same launch) by default; the split
+        form's first launch with --split, without the cache write with
+        --unfused (kv_cache_append wrote the rows already)."""
         kp, vp, ksp, vsp = pools[l]
         kl = knew.data_ptr() + (s * layers + l) * kv_stride
         vl = vnew.data_ptr() + (s * layers + l) * kv_stride
         o_ptr = outs.data_ptr() + l * out_stride
         q_ptr = qs.data_ptr() + (s * layers + l) * q_stride
-        if args.one_call:
+        if not args.split and not args.unfused:
             rc = lib.paged_attention_decode_append_bs(o_ptr, q_ptr, kl, vl, kp, vp, ksp, vsp,
                                                       d_slots.data_ptr(), d_tables.data_ptr(), d_lens.data_ptr(),
                                                       B, hq, hkv, D, w.num_blocks, bs, mb, max_len, scale,
@@ -360,8 +364,9 @@ def main():
             raise pkv.PagedKVError(rc, "paged_attention_decode_append_partials")
 
     def merge(l, max_len):
-        """Layer l's partition merge (nothing is launched when no sequence is split)."""
-        if args.one_call:
+        """Layer l's partition merge, split form only (nothing is launched when
+        no sequence is split)."""
+        if not args.split and not args.unfused:
             return
         o_ptr = outs.data_ptr() + l * out_stride
         rc = lib.paged_attention_merge_partials_bs(o_ptr, d_lens.data_ptr(), B, hq, hkv, D, bs, mb, max_len,
@@ -446,7 +451,7 @@ def main():
 
     last_s = n_steps - 1
     kern_pct = time_runs(lambda l: attend(last_s, l, last_max_len))
-    split = not args.one_call and ps_used < last_max_len
+    split = (args.split or args.unfused) and ps_used < last_max_len
     merge_pct = time_runs(lambda l: merge(l, last_max_len)) if split else None
     kern_s = kern_pct["median_us"] / 1e6
     log(f"[bench] attention kernel alone: median {kern_pct['median_us']:.2f} us per call "
@@ -523,7 +528,8 @@ def main():
             "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
             "kernel": ("whole decode call: paged_decode_kernel" + ("" if args.unfused else " (cache write fused)")
-                       + (" + partition_merge_kernel" if split else "")),
+                       + (" + partition_merge_kernel" if split else
+                          (", partitions merged in the same launch" if ps_used < last_max_len else ""))),
             "timing": f"HIP events around runs of {layers} consecutive calls on the launch stream, "
                       f"{args.steps} runs; per-call time = span / {layers}",
             "bytes_per_launch": bytes_per_call,

@@ -46,6 +46,15 @@ extern "C" {
 #define PKV_BLOCK_SIZE_LARGE 32   /* the other block size the _bs calls take (§6.3 there) */
 #define PKV_ABI_VERSION 1
 #define PKV_MAX_PARTITION_TOKENS 32768   /* largest decode partition (tokens) */
+/* A decode workspace (when one is needed) starts with PKV_WS_COUNTER_BYTES of
+   counters: two int32 for each of up to PKV_WS_COUNTER_UNITS (sequence, KV
+   head) pairs, used by the one-call decode forms to find the last partition
+   of a sequence to finish.  They must be zero before a workspace's first
+   use (a zero-filled workspace is) and every call leaves them zero; the
+   area's size does not depend on the call, so a workspace may serve calls
+   of any size.  The rest of a workspace needs no initialisation. */
+#define PKV_WS_COUNTER_UNITS 32768
+#define PKV_WS_COUNTER_BYTES (PKV_WS_COUNTER_UNITS * 8)
 #define PKV_MAX_PREFILL_CONTEXT 32768    /* longest context a prefill call reads (tokens) */
 
 typedef enum {
@@ -174,6 +183,7 @@ size_t paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_
                                       int head_dim, int max_context_len, int partition_size,
                                       pkv_dtype cache_dtype);
 
+
 /*
  * paged_attention_decode - one decode step of attention for a batch.
  * Pages: "企业官网建设流程全解析" §1.2 (softmax(Q K^T / sqrt(d_k)) V), §2.2
@@ -194,15 +204,20 @@ size_t paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_
  *   scale         the caller passes 1/sqrt(head_dim)
  *   partition_size 0 = automatic; else tokens per partition, a multiple of 16
  *                 and at most PKV_MAX_PARTITION_TOKENS.
- *                 When some sequence is longer than one partition, every
- *                 sequence's partition states go to the workspace and a
- *                 second kernel of the same call merges them exactly
- *                 (log-sum-exp) into the output.
+ *                 When a sequence is longer than one partition, its
+ *                 partitions' states are merged exactly (log-sum-exp) into
+ *                 the output inside the same launch: the workgroup of the
+ *                 sequence's last partition to finish reads the others'
+ *                 states from the workspace and writes the output row.
  *   workspace     device scratch of at least paged_attention_workspace_size()
- *                 bytes (may be NULL when that is 0): the partition states of
- *                 the call.  It needs no initialisation (every value a call
- *                 uses is written by that call).  Calls that may run
- *                 concurrently must not share a workspace.
+ *                 bytes (may be NULL when that is 0): arrival counters (the
+ *                 first PKV_WS_COUNTER_BYTES: zero before the workspace's
+ *                 first use, left zero by every call), then the partition
+ *                 states of the call, which need no initialisation.  With
+ *                 more than PKV_WS_COUNTER_UNITS (sequence, KV head) pairs
+ *                 the merge runs as a second kernel of the same call instead
+ *                 (same bits).  Calls that may run concurrently must not
+ *                 share a workspace.
  * Query head h reads KV head h / (num_q_heads / num_kv_heads).  L_b == 0 gives
  * an all-zero output row.  Entries of the used part of a block-table row must
  * lie in [0, num_blocks); a block outside that range contributes no tokens.
@@ -237,8 +252,8 @@ int paged_attention_decode_bs(void* out, const void* q,
  * paged_attention_decode_append - one decode step with its cache write fused
  * in: the same result, pool bytes and scales as kv_cache_append(k_new, v_new,
  * ..., slot_mapping, num_tokens = num_seqs) followed by
- * paged_attention_decode(...), in one launch (plus the partition merge when a
- * sequence spans several partitions).  Pages: the new token's K and V are
+ * paged_attention_decode(...), in one launch (partition states merged in it
+ * as in paged_attention_decode).  Pages: the new token's K and V are
  * appended to the cache and the new query then attends over the whole cache,
  * itself included ("KV Cache 和 vLLM" §1.2-1.3; "企业官网建设流程全解析" §3.2).
  *
@@ -275,14 +290,16 @@ int paged_attention_decode_append_bs(void* out, const void* q, const void* k_new
                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
- * Split form of paged_attention_decode_append, for callers that schedule or
- * time its two launches separately.  paged_attention_decode_append_partials
- * takes the same arguments (slot_mapping may be NULL: no cache write, as in
- * paged_attention_decode) and launches only the attention kernel: when
- * some sequence is longer than one partition it writes every sequence's
- * partition states (empty partitions included) into the workspace, else the
- * output rows.  paged_attention_merge_partials then merges those states
- * into the output rows (log-sum-exp); it
+ * Split form of paged_attention_decode_append, in two launches, for callers
+ * that schedule or time the merge separately.
+ * paged_attention_decode_append_partials takes the same arguments
+ * (slot_mapping may be NULL: no cache write, as in paged_attention_decode)
+ * and launches only the attention kernel: when some sequence is longer than
+ * one partition it writes every sequence's partition states (empty
+ * partitions included) into the workspace, else the output rows; it does not
+ * use the workspace's counters.  paged_attention_merge_partials then merges
+ * those states into the output rows (log-sum-exp, the same arithmetic in the
+ * same order as the one-call form, so the output bits are equal); it
  * must get the same num_seqs, head counts, head_dim, max_context_len,
  * cache_dtype, partition_size and workspace, on the same stream (the
  * automatic partition plan depends on the cache format).  The pair gives exactly

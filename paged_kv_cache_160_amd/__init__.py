@@ -23,7 +23,7 @@ __all__ = [
     "PagedKVError", "cache_code", "CACHE_FORMATS",
     "kv_cache_append", "copy_blocks", "paged_attention_decode", "paged_attention_decode_append",
     "paged_attention_decode_append_partials", "paged_attention_merge_partials",
-    "workspace_size",
+    "workspace_size", "WS_COUNTER_BYTES",
     "decode_partition_size", "BlockAllocator", "dtype_code", "abi_version", "gather_blocks", "scatter_blocks",
     "paged_attention_prefill",
 ]
@@ -196,6 +196,12 @@ def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim:
                    max_context_len: int, partition_size: int = 0, cache_dtype: int = PKV_BF16) -> int:
     return int(_lib.lib().paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
                                                          max_context_len, partition_size, cache_dtype))
+
+
+# Bytes at the start of a decode workspace that hold the one-call form's
+# counters (PKV_WS_COUNTER_BYTES): zero before a workspace's first use, left
+# zero by every call.
+WS_COUNTER_BYTES = 32768 * 8
 
 
 def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,

@@ -52,20 +52,27 @@ int resolve_partitions(int num_seqs, int num_kv_heads, int max_context_len, int 
   return PKV_OK;
 }
 
-// Workspace layout: per (sequence, query head, partition) (m, l) pairs, then
-// the unnormalised partition outputs (256-byte aligned).
+// Workspace layout: the one-call form's counters (two int32 for each of up
+// to PKV_WS_COUNTER_UNITS (sequence, KV head) pairs, zero between calls; a
+// fixed size, so that no call of any size ever writes states where another
+// call keeps counters), then per (sequence, query head, partition) (m, l)
+// pairs, then the unnormalised partition outputs; each part 256-byte aligned.
 struct WorkspaceLayout {
-  size_t ml = 0, acc = 0, total = 0;
+  size_t counters = 0, ml = 0, acc = 0, total = 0;
 };
 
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+constexpr size_t kCounterBytes = static_cast<size_t>(PKV_WS_COUNTER_UNITS) * 2 * sizeof(int32_t);
+
 WorkspaceLayout workspace_layout(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim, int np) {
+  (void)num_kv_heads;
   WorkspaceLayout w;
   if (np <= 1) return w;
-  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   const size_t rows = static_cast<size_t>(num_seqs) * num_q_heads * np;
-  (void)num_kv_heads;
-  w.ml = 0;
-  w.acc = up(rows * 2 * sizeof(float));
+  w.counters = 0;
+  w.ml = kCounterBytes;
+  w.acc = w.ml + align256(rows * 2 * sizeof(float));
   w.total = w.acc + rows * head_dim * sizeof(float);
   return w;
 }
@@ -161,6 +168,7 @@ int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, i
                             num_partitions_out);
 }
 
+
 size_t paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_heads,
                                       int head_dim, int max_context_len, int partition_size,
                                       pkv_dtype cache_dtype) {
@@ -243,8 +251,14 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new, 
   a.src_dtype = src_dtype;
   if (np > 1) {
     char* base = static_cast<char*>(workspace);
-      a.part_ml = reinterpret_cast<float*>(base + ws.ml);
+    a.part_ml = reinterpret_cast<float*>(base + ws.ml);
     a.part_acc = reinterpret_cast<float*>(base + ws.acc);
+    // the one-call form merges inside the attention kernel (up to
+    // PKV_WS_COUNTER_UNITS (sequence, KV head) pairs; beyond, a merge kernel
+    // follows, as in the split form)
+    if (stages == pkv::kStageBoth &&
+        static_cast<int64_t>(num_seqs) * num_kv_heads <= static_cast<int64_t>(PKV_WS_COUNTER_UNITS))
+      a.counters = reinterpret_cast<int*>(base + ws.counters);
   }
   return pkv::launch_decode(a, static_cast<hipStream_t>(stream), stages);
 }

@@ -353,6 +353,77 @@ __device__ __forceinline__ void pv_tile(const float (&p)[4], const Words<Geo<QT,
   }
 }
 
+// ---- log-sum-exp merge of partition states ------------------------------------
+// A partition's state is (m, l, acc): its maximum score (log2 units), the
+// sum of 2^(s - m) over its tokens and the unnormalised output
+// sum 2^(s - m) V.  The merged output is sum_p 2^(m_p - M) acc_p /
+// sum_p 2^(m_p - M) l_p with M = max_p m_p ("企业官网建设流程全解析" §1.2:
+// the softmax over the whole context, regrouped by partition).  States are
+// taken in partition order, up to 8 at a time, with a running maximum.  Both
+// places that merge - the merge kernel of the split form and the last
+// partition of a sequence to finish in the one-call form - go through this
+// function, so the two forms give the same bits.
+template <int N>
+struct MergeState {
+  float M;
+  float den;
+  float num[N];
+};
+
+template <int N>
+__device__ __forceinline__ MergeState<N> merge_begin() {
+  MergeState<N> s;
+  s.M = -INFINITY;
+  s.den = 0.f;
+#pragma unroll
+  for (int e = 0; e < N; ++e) s.num[e] = 0.f;
+  return s;
+}
+
+// n (<= 8) states of consecutive partitions; empty ones have m = -inf.
+template <int N>
+__device__ __forceinline__ void merge_chunk(MergeState<N>& s, const float (&mp)[8], const float (&lp)[8],
+                                            const float (&ap)[8][N], int n) {
+  float cm = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if (i < n) cm = fmaxf(cm, mp[i]);
+  const float M_new = fmaxf(s.M, cm);
+  if (M_new == -INFINITY) return;
+  const float r = __builtin_amdgcn_exp2f(s.M - M_new);   // 0 while s.M is still -inf
+  s.den *= r;
+#pragma unroll
+  for (int e = 0; e < N; ++e) s.num[e] *= r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    if (i < n && mp[i] != -INFINITY) {
+      const float f = __builtin_amdgcn_exp2f(mp[i] - M_new);
+#pragma unroll
+      for (int e = 0; e < N; ++e) s.num[e] = __builtin_fmaf(f, ap[i][e], s.num[e]);
+      s.den = __builtin_fmaf(f, lp[i], s.den);
+    }
+  }
+  s.M = M_new;
+}
+
+template <int N>
+__device__ __forceinline__ float merge_result(const MergeState<N>& s, int e) {
+  return s.den > 0.f ? s.num[e] / s.den : 0.f;
+}
+
+// Partition states written for another workgroup to read go straight to
+// memory (agent-scope stores write through the XCD's L2) and are read back
+// past the reader's caches (agent-scope loads), so the workgroups of one
+// sequence may run on any XCDs.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_agent2(const float* p) {
+  const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(static_cast<uint32_t>(u)), __uint_as_float(static_cast<uint32_t>(u >> 32)));
+}
+
 // ---- the main kernel ------------------------------------------------------------
 
 
@@ -501,16 +572,18 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * a.block_size)));
   const int np_b = (L + PS - 1) / PS;         // non-empty partitions of this sequence
   if (part >= np_b) {
-    if (P == 1) {
-      // an empty context gives a zero output row
-      for (int i = tid; i < group * D; i += kThreads) store_from_f32<QT>(a.out, out_row0 * D + i, 0.0f);
-    } else {
-      // the merge reads every partition slot: mark this one empty
+    if (P > 1 && a.counters == nullptr) {
+      // split form: the merge kernel reads every partition slot, so mark
+      // this one empty
       for (int h = tid; h < group; h += kThreads) {
         const int64_t prow = (out_row0 + h) * P + part;
         a.part_ml[2 * prow] = kNegInf;
         a.part_ml[2 * prow + 1] = 0.0f;
       }
+    } else if (part == 0) {
+      // an empty context gives a zero output row (merged in this launch, a
+      // sequence's states come from its non-empty partitions only)
+      for (int i = tid; i < group * D; i += kThreads) store_from_f32<QT>(a.out, out_row0 * D + i, 0.0f);
     }
     return;
   }
@@ -689,6 +762,14 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   }
 
   // ---- merge the waves' states ----
+  // A sequence split over several partitions and merged in this launch: its
+  // workgroups count their arrival on the sequence's (KV head's) counter;
+  // the request goes out now and its reply is read after the wave merge.
+  const bool merge_here = P > 1 && np_b > 1 && a.counters != nullptr;
+  int* const cnt = merge_here ? a.counters + 2 * (static_cast<int64_t>(b) * a.num_kv_heads + g) : nullptr;
+  int arrival = 0;
+  if (merge_here && tid == 0) arrival = atomicAdd(cnt, 1);
+
   l = col_sum4(l);
   if (j == 0 && c < group) {
     sm_m[wave][c] = m;
@@ -704,36 +785,157 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   }
   __syncthreads();
 
-  const bool single = P == 1;                // else the merge kernel writes the output
-  for (int idx = tid; idx < group * D; idx += kThreads) {
-    const int h = idx / D;
-    const int d = idx % D;
-    float M = kNegInf;
+  // This workgroup's state, two adjacent output columns (h, d..d+1) per
+  // step: kPairs steps cover the largest group.
+  constexpr int kPairs = (kMaxGroup * D / 2 + kThreads - 1) / kThreads;
+  const int n_pairs = group * D / 2;
+  float st_m[kPairs], st_l[kPairs], st_a[kPairs][2];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
-    float acc = 0.f, lsum = 0.f;
-    if (M != kNegInf) {
+  for (int k = 0; k < kPairs; ++k) {
+    const int pi = tid + k * kThreads;
+    st_m[k] = kNegInf;
+    st_l[k] = 0.f;
+    st_a[k][0] = st_a[k][1] = 0.f;
+    if (pi < n_pairs) {
+      const int h = pi / (D / 2);
+      const int d = 2 * (pi % (D / 2));
+      float M = kNegInf;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = sm_m[w][h];
-        if (mw != kNegInf) {
-          const float f = __builtin_amdgcn_exp2f(mw - M);
-          acc += f * sm_o[w][h][d];
-          lsum += f * sm_l[w][h];
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+      float acc0 = 0.f, acc1 = 0.f, lsum = 0.f;
+      if (M != kNegInf) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float mw = sm_m[w][h];
+          if (mw != kNegInf) {
+            const float f = __builtin_amdgcn_exp2f(mw - M);
+            acc0 += f * sm_o[w][h][d];
+            acc1 += f * sm_o[w][h][d + 1];
+            lsum += f * sm_l[w][h];
+          }
+        }
+      }
+      st_m[k] = M;
+      st_l[k] = lsum;
+      st_a[k][0] = acc0;
+      st_a[k][1] = acc1;
+    }
+  }
+
+  if (P == 1 || (np_b == 1 && a.counters != nullptr)) {
+    // the workgroup holds the whole sequence: its state is the output (the
+    // merge of one state gives the same bits)
+#pragma unroll
+    for (int k = 0; k < kPairs; ++k) {
+      const int pi = tid + k * kThreads;
+      if (pi < n_pairs) {
+        const int64_t i = (out_row0 + pi / (D / 2)) * D + 2 * (pi % (D / 2));
+        store_from_f32<QT>(a.out, i, st_l[k] > 0.f ? st_a[k][0] / st_l[k] : 0.f);
+        store_from_f32<QT>(a.out, i + 1, st_l[k] > 0.f ? st_a[k][1] / st_l[k] : 0.f);
+      }
+    }
+    return;
+  }
+
+  if (!merge_here) {
+    // split form: every partition's state goes to the workspace for the
+    // merge kernel
+#pragma unroll
+    for (int k = 0; k < kPairs; ++k) {
+      const int pi = tid + k * kThreads;
+      if (pi < n_pairs) {
+        const int d = 2 * (pi % (D / 2));
+        const int64_t prow = (out_row0 + pi / (D / 2)) * P + part;
+        a.part_acc[prow * D + d] = st_a[k][0];
+        a.part_acc[prow * D + d + 1] = st_a[k][1];
+        if (d == 0) {
+          a.part_ml[2 * prow] = st_m[k];
+          a.part_ml[2 * prow + 1] = st_l[k];
         }
       }
     }
-    const int64_t row = out_row0 + h;
-    if (single) {
-      store_from_f32<QT>(a.out, row * D + d, lsum > 0.f ? acc / lsum : 0.f);
-    } else {
-      const int64_t prow = row * P + part;
-      a.part_acc[prow * D + d] = acc;
-      if (d == 0) {
-        a.part_ml[2 * prow] = M;
-        a.part_ml[2 * prow + 1] = lsum;
+    return;
+  }
+
+  // One-call form.  Every workgroup but the last to arrive publishes its
+  // state (stored through to memory, then counted on the second counter);
+  // the last one waits until the others have published - they have all
+  // arrived, so only their stores are outstanding - merges every state in
+  // partition order and writes the output, then zeroes both counters for
+  // the next call.  The wait is bounded; if it ever ran out the output row
+  // would be NaN rather than the kernel hanging.
+  __shared__ int sm_arrival;
+  if (tid == 0) sm_arrival = arrival;
+  __syncthreads();
+  const bool last = sm_arrival == np_b - 1;
+  if (!last) {
+#pragma unroll
+    for (int k = 0; k < kPairs; ++k) {
+      const int pi = tid + k * kThreads;
+      if (pi < n_pairs) {
+        const int d = 2 * (pi % (D / 2));
+        const int64_t prow = (out_row0 + pi / (D / 2)) * P + part;
+        store_agent(a.part_acc + prow * D + d, st_a[k][0]);
+        store_agent(a.part_acc + prow * D + d + 1, st_a[k][1]);
+        if (d == 0) {
+          store_agent(a.part_ml + 2 * prow, st_m[k]);
+          store_agent(a.part_ml + 2 * prow + 1, st_l[k]);
+        }
       }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // every store of this thread acknowledged
+    __syncthreads();
+    if (tid == 0) atomicAdd(cnt + 1, 1);
+    return;
+  }
+  if (tid == 0) {
+    constexpr int kMaxSpins = 1 << 20;
+    int spins = 0;
+    while (__hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < np_b - 1 &&
+           spins < kMaxSpins) {
+      __builtin_amdgcn_s_sleep(1);
+      ++spins;
+    }
+    sm_arrival = spins < kMaxSpins ? 1 : 0;
+  }
+  __syncthreads();
+  const bool published = sm_arrival != 0;
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k) {
+    const int pi = tid + k * kThreads;
+    if (pi >= n_pairs) continue;
+    const int d = 2 * (pi % (D / 2));
+    const int64_t row = out_row0 + pi / (D / 2);
+    MergeState<2> ms = merge_begin<2>();
+    for (int p0 = 0; p0 < np_b; p0 += 8) {
+      float mp[8], lp[8], ap[8][2];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int p = min(p0 + i, np_b - 1);
+        const int64_t prow = row * P + p;
+        if (p == part) {
+          mp[i] = st_m[k];
+          lp[i] = st_l[k];
+          ap[i][0] = st_a[k][0];
+          ap[i][1] = st_a[k][1];
+        } else {
+          const float2 ml = load_agent2(a.part_ml + 2 * prow);
+          const float2 av = load_agent2(a.part_acc + prow * D + d);
+          mp[i] = ml.x;
+          lp[i] = ml.y;
+          ap[i][0] = av.x;
+          ap[i][1] = av.y;
+        }
+      }
+      merge_chunk<2>(ms, mp, lp, ap, min(8, np_b - p0));
+    }
+    const float nan = __builtin_nanf("");
+    store_from_f32<QT>(a.out, row * D + d, published ? merge_result<2>(ms, 0) : nan);
+    store_from_f32<QT>(a.out, row * D + d + 1, published ? merge_result<2>(ms, 1) : nan);
+  }
+  if (tid == 0) {
+    __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(cnt + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -743,45 +945,26 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
 // so the merge needs no context length and issues all of its loads at once.
 template <typename QT, int D>
 __global__ void __launch_bounds__(D) partition_merge_kernel(DecodeArgs a) {
-  constexpr int kChunk = 8;                   // partitions whose loads are in flight together
   const int row = blockIdx.x;                 // b * Hq + h
   const int d = threadIdx.x;
   const int P = a.num_partitions;
   const float* ml = a.part_ml + static_cast<int64_t>(row) * P * 2;
   const float* acc = a.part_acc + static_cast<int64_t>(row) * P * D;
-  // Running merge over chunks of partitions; within a chunk every load is
-  // issued before any of them is used.  The output slot of an empty
-  // partition holds stale values and is never used.
-  float M = -INFINITY, num = 0.f, den = 0.f;
-  for (int p0 = 0; p0 < P; p0 += kChunk) {
-    float mp[kChunk], lp[kChunk], ap[kChunk];
+  // Within a chunk every load is issued before any is used.  The output
+  // slot of an empty partition holds stale values and is never used.
+  MergeState<1> ms = merge_begin<1>();
+  for (int p0 = 0; p0 < P; p0 += 8) {
+    float mp[8], lp[8], ap[8][1];
 #pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
+    for (int i = 0; i < 8; ++i) {
       const int p = min(p0 + i, P - 1);
       mp[i] = ml[2 * p];
       lp[i] = ml[2 * p + 1];
-      ap[i] = acc[static_cast<int64_t>(p) * D + d];
+      ap[i][0] = acc[static_cast<int64_t>(p) * D + d];
     }
-    float cm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i)
-      if (p0 + i < P) cm = fmaxf(cm, mp[i]);
-    const float M_new = fmaxf(M, cm);
-    if (M_new == -INFINITY) continue;
-    const float r = __builtin_amdgcn_exp2f(M - M_new);   // 0 while M is still -inf
-    num *= r;
-    den *= r;
-#pragma unroll
-    for (int i = 0; i < kChunk; ++i) {
-      if (p0 + i < P && mp[i] != -INFINITY) {
-        const float f = __builtin_amdgcn_exp2f(mp[i] - M_new);
-        num += f * ap[i];
-        den += f * lp[i];
-      }
-    }
-    M = M_new;
+    merge_chunk<1>(ms, mp, lp, ap, min(8, P - p0));
   }
-  store_from_f32<QT>(a.out, static_cast<int64_t>(row) * D + d, den > 0.f ? num / den : 0.f);
+  store_from_f32<QT>(a.out, static_cast<int64_t>(row) * D + d, merge_result<1>(ms, 0));
 }
 
 // ---- host side -------------------------------------------------------------------------
@@ -843,7 +1026,8 @@ static int launch_typed(const DecodeArgs& a, hipStream_t stream, int stages) {
                          dim3(kThreads), 0, stream, a);
     rc = check_launch();
   }
-  if (rc != PKV_OK || !(stages & kStageMerge) || a.num_partitions == 1) return rc;
+  // one-call launches with counters merge inside the attention kernel
+  if (rc != PKV_OK || !(stages & kStageMerge) || a.num_partitions == 1 || a.counters != nullptr) return rc;
   hipLaunchKernelGGL((partition_merge_kernel<QT, D>), dim3(a.num_seqs * a.num_q_heads), dim3(D), 0, stream, a);
   return check_launch();
 }

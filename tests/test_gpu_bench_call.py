@@ -3,13 +3,15 @@ oracle.
 
 Llama-3-8B layer shape (16 sequences x 4096 cached tokens, 32 query / 8 KV
 heads, head_dim 128, bf16): each step the native allocator hands out one
-slot per sequence, then the same two C-ABI calls the benchmark makes run on
-the same arguments - paged_attention_decode_append_partials with the slot
-mapping (cache write fused into the attention kernel, automatic partition
-plan) and paged_attention_merge_partials - with one workspace reused across
-steps.  After each of several steps: every output row against the fp64
-oracle over the rows appended so far, and the pool bits of every sequence
-(positions 0..L-1, the new rows included) against the oracle's rows.
+slot per sequence, then the C-ABI call the benchmark times runs on the same
+arguments - paged_attention_decode_append with the slot mapping (cache write
+fused into the attention kernel, automatic partition plan, partitions merged
+in the same launch) - with one workspace reused across steps.  After each of
+several steps: every output row against the fp64 oracle over the rows
+appended so far, the pool bits of every sequence (positions 0..L-1, the new
+rows included) against the oracle's rows, the workspace's counters back at
+zero, and the split form (attention kernel, then the merge kernel) over the
+same cache giving the same output bits.
 Pages: "KV Cache 和 vLLM" §1.2-1.3 (append, then attend over the whole
 cache); "企业官网建设流程全解析" §1.2 (the attention).
 """
@@ -30,7 +32,7 @@ pytestmark = pytest.mark.gpu
 STEPS = 4
 
 
-def test_benched_split_call_at_full_size():
+def test_benched_call_at_full_size():
     w = wl.make_workload(2)
     w.decode_appends = STEPS
     ops = wl.setup_ops(w)
@@ -42,8 +44,12 @@ def test_benched_split_call_at_full_size():
     lib = pkv._lib.lib()
     sp = torch.cuda.current_stream().cuda_stream
     max_possible = max(w.context_lens) + STEPS
-    ws = torch.full((pkv.workspace_size(B, hq, hkv, D, max_possible, 0, c.cache_code),), 0xFF,
-                    dtype=torch.uint8, device="cuda")     # NaN bits: nothing may depend on old contents
+    need = pkv.workspace_size(B, hq, hkv, D, max_possible, 0, c.cache_code)
+    n_cnt = pkv.WS_COUNTER_BYTES
+    # counters zero, states NaN bits: nothing may depend on old state values
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    ws[:n_cnt] = 0
+    ws2 = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
     ps, npart = pkv.decode_partition_size(B, hq, hkv, D, max(w.context_lens) + 1, c.cache_code)
     say(f"[bench-call] automatic plan: {npart} partitions of {ps} tokens")
     assert npart > 1, "the benched call at this size spans several partitions"
@@ -62,16 +68,26 @@ def test_benched_split_call_at_full_size():
         max_len = int(lens.max())
         q = g.queries(step)
         out = torch.empty_like(q)
-        rc = lib.paged_attention_decode_append_partials_bs(
+        rc = lib.paged_attention_decode_append_bs(
             out.data_ptr(), q.data_ptr(), kd.data_ptr(), vd.data_ptr(), c.k[0].data_ptr(), c.v[0].data_ptr(),
             None, None, d_slots.data_ptr(), d_tables.data_ptr(), d_lens.data_ptr(), B, hq, hkv, D, w.num_blocks,
             w.block_size, w.max_blocks_per_seq, max_len, 1.0 / math.sqrt(D), code_q, code_q, c.cache_code, 0,
             ws.data_ptr(), ws.numel(), sp)
         assert rc == 0, rc
-        rc = lib.paged_attention_merge_partials_bs(
-            out.data_ptr(), d_lens.data_ptr(), B, hq, hkv, D, w.block_size, w.max_blocks_per_seq, max_len,
-            code_q, c.cache_code, 0, ws.data_ptr(), ws.numel(), sp)
+        # the split form over the cache as the call left it (rows written)
+        out2 = torch.empty_like(q)
+        rc = lib.paged_attention_decode_append_partials_bs(
+            out2.data_ptr(), q.data_ptr(), None, None, c.k[0].data_ptr(), c.v[0].data_ptr(), None, None, None,
+            d_tables.data_ptr(), d_lens.data_ptr(), B, hq, hkv, D, w.num_blocks, w.block_size,
+            w.max_blocks_per_seq, max_len, 1.0 / math.sqrt(D), code_q, code_q, c.cache_code, 0, ws2.data_ptr(),
+            ws2.numel(), sp)
         assert rc == 0, rc
+        rc = lib.paged_attention_merge_partials_bs(
+            out2.data_ptr(), d_lens.data_ptr(), B, hq, hkv, D, w.block_size, w.max_blocks_per_seq, max_len,
+            code_q, c.cache_code, 0, ws2.data_ptr(), ws2.numel(), sp)
+        assert rc == 0, rc
+        assert torch.equal(out.cpu(), out2.cpu()), "split form differs from the one-call form"
+        assert int(ws[:n_cnt].count_nonzero()) == 0, "counters not left at zero"
         got = out_to_f64(out)
         torch.cuda.synchronize()
         L = [int(x) for x in lens]

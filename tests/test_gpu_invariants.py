@@ -102,10 +102,12 @@ def test_largest_partition():
 
 
 @pytest.mark.parametrize("cache", [None, "int8_int4"])
-def test_workspace_needs_no_initialisation(cache):
-    # a ragged batch split into 64-token partitions leaves empty partition
-    # slots (their output rows are never written); a workspace full of NaN
-    # bytes gives the same output bits as a zeroed one
+def test_workspace_needs_only_zero_counters(cache):
+    # a ragged batch split into 64-token partitions (empty partition slots
+    # included): a workspace whose counter area is zero and whose state area
+    # is full of NaN bytes gives the same output bits as a zeroed one, leaves
+    # the counters zero, and the split form (whose merge kernel reads every
+    # slot and never the counters) gives the same bits from a NaN workspace
     lens = [700, 1, 0, 130, 64, 2000]
     w, g = _custom(lens, 16, 4, 128, "bf16" if cache is None else "f32", cache_dtype=cache,
                    q_dtype=None if cache is None else "bf16")
@@ -114,16 +116,29 @@ def test_workspace_needs_no_initialisation(cache):
     q = g.queries(0)
     c = g.cache
     need = pkv.workspace_size(len(seqs), 16, 4, 128, tables[2], 64, c.cache_code)
+    n_cnt = pkv.WS_COUNTER_BYTES
+    assert 0 < n_cnt < need
     outs = []
     for fill in (0, 0xFF):
         ws = torch.full((need,), fill, dtype=torch.uint8, device="cuda")
+        ws[:n_cnt] = 0
         out = torch.empty_like(q)
         pkv.paged_attention_decode(out, q, c.k[0], c.v[0], tables[0], tables[1], tables[2],
                                    k_scale=c.k_scale[0], v_scale=c.v_scale[0], partition_size=64, workspace=ws)
         outs.append(out.cpu())
+        assert int(ws[:n_cnt].count_nonzero()) == 0
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    pkv.paged_attention_decode_append_partials(out, q, None, None, c.k[0], c.v[0], None, tables[0], tables[1],
+                                               tables[2], k_scale=c.k_scale[0], v_scale=c.v_scale[0],
+                                               partition_size=64, workspace=ws)
+    pkv.paged_attention_merge_partials(out, tables[1], 4, w.max_blocks_per_seq, tables[2], c.cache_code,
+                                       partition_size=64, workspace=ws)
+    outs.append(out.cpu())
     torch.cuda.synchronize()
     assert torch.isfinite(outs[1].float()).all()
     assert torch.equal(outs[0], outs[1])
+    assert torch.equal(outs[0], outs[2])
 
 
 @pytest.mark.parametrize("ps", [0, 64])
@@ -264,3 +279,56 @@ def test_quantiser_edge_rows_other_formats(fmt):
         codes, scales = kv_formats.quantise(rows[:, 0], elem)
         assert np.array_equal(pool[0, 0, :8].view(torch.uint8).cpu().numpy(), codes), elem
         assert np.array_equal(sc[0, 0, :8].cpu().numpy().view(np.uint32), scales.view(np.uint32)), elem
+
+
+def test_one_workspace_serves_calls_of_any_size():
+    # one zero-filled workspace used by one-call decodes of growing and
+    # shrinking batches and partition counts (so states of one call lie where
+    # a differently sized call keeps nothing but states): every output equals
+    # the output with a fresh workspace, and the counters stay zero
+    lens = [900, 40, 2000, 1, 300, 1500, 64, 1200]
+    w, g = _custom(lens, 16, 4, 128, "bf16", seed=29)
+    c = g.cache
+    q = g.queries(0)
+    big = torch.zeros(pkv.workspace_size(len(lens), 16, 4, 128, 2000, 16, c.cache_code), dtype=torch.uint8,
+                      device="cuda")
+    for n, ps in ((2, 64), (8, 16), (3, 128), (8, 0), (5, 16), (1, 16), (8, 64)):
+        seqs = list(range(n))
+        tables = c.block_tables(seqs)
+        say(f"[workspace] {n} sequences, partition size {ps}")
+        shared = torch.empty_like(q[:n])
+        pkv.paged_attention_decode(shared, q[:n].contiguous(), c.k[0], c.v[0], tables[0], tables[1], tables[2],
+                                   partition_size=ps, workspace=big)
+        fresh = torch.empty_like(q[:n])
+        pkv.paged_attention_decode(fresh, q[:n].contiguous(), c.k[0], c.v[0], tables[0], tables[1], tables[2],
+                                   partition_size=ps)
+        torch.cuda.synchronize()
+        assert torch.equal(shared.cpu(), fresh.cpu())
+        assert int(big[:pkv.WS_COUNTER_BYTES].count_nonzero()) == 0
+
+
+def test_more_sequence_heads_than_counters_use_the_merge_kernel():
+    # beyond PKV_WS_COUNTER_UNITS (sequence, KV head) pairs the one-call form
+    # merges in a second kernel: same bits as the split form, and the oracle
+    B, hkv = 2112, 16                      # 33792 pairs > 32768
+    rng = np.random.default_rng(5)
+    lens = [int(x) for x in rng.integers(1, 49, size=B)]
+    lens[0] = 48
+    w, g = _custom(lens, 16, hkv, 64, "bf16", seed=31)
+    c = g.cache
+    seqs = list(range(B))
+    tables = c.block_tables(seqs)
+    q = g.queries(0)
+    say(f"[workspace] {B} sequences x {hkv} KV heads, 16-token partitions")
+    one = torch.empty_like(q)
+    pkv.paged_attention_decode(one, q, c.k[0], c.v[0], tables[0], tables[1], tables[2], partition_size=16)
+    two = torch.empty_like(q)
+    _, ws = pkv.paged_attention_decode_append_partials(two, q, None, None, c.k[0], c.v[0], None, tables[0],
+                                                       tables[1], tables[2], partition_size=16)
+    pkv.paged_attention_merge_partials(two, tables[1], hkv, w.max_blocks_per_seq, tables[2], c.cache_code,
+                                       partition_size=16, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(one.cpu(), two.cpu())
+    sample = [0, 1, 700, B - 1]
+    exp = scenario.expected_decode_rows(w, wl.queries(w, 0)[sample], sample, [lens[b] for b in sample])
+    assert max_err(out_to_f64(one)[sample], exp) <= TOL["bf16"]

@@ -265,8 +265,17 @@ def test_partition_plan_and_workspace():
         if npart == 1:
             assert ws == 0
         else:
-            assert ws >= B * hq * npart * (128 + 2) * 4
+            assert ws >= pkv.WS_COUNTER_BYTES + B * hq * npart * (128 + 2) * 4
     assert pkv.workspace_size(16, 32, 8, 128, 4096, 16, pkv.PKV_BF16) >= 16 * 32 * 256 * 130 * 4
+
+
+def test_counter_area_size_matches_header():
+    # the binding's constant is the header's PKV_WS_COUNTER_BYTES
+    with open(HEADER, encoding="utf-8") as f:
+        text = f.read()
+    units = int(re.search(r"#define PKV_WS_COUNTER_UNITS (\d+)", text).group(1))
+    assert re.search(r"#define PKV_WS_COUNTER_BYTES \(PKV_WS_COUNTER_UNITS \* 8\)", text)
+    assert pkv.WS_COUNTER_BYTES == units * 8
 
 
 def test_swap_hand_worked_matches_model():
