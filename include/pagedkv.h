@@ -55,6 +55,8 @@ extern "C" {
    of any size.  The rest of a workspace needs no initialisation. */
 #define PKV_WS_COUNTER_UNITS 32768
 #define PKV_WS_COUNTER_BYTES (PKV_WS_COUNTER_UNITS * 8)
+/* Device scratch the library keeps per GPU for paged_attention_decode_append_noalloc. */
+#define PKV_SCRATCH_BYTES (16 * 1024 * 1024)
 #define PKV_MAX_PREFILL_CONTEXT 32768    /* longest context a prefill call reads (tokens) */
 
 typedef enum {
@@ -74,8 +76,10 @@ enum {
   PKV_ERR_HIP = -4,            /* the HIP runtime reported an error */
   PKV_ERR_NO_FREE_BLOCKS = -5, /* allocator: not enough free blocks; nothing changed */
   PKV_ERR_UNKNOWN_SEQ = -6,    /* allocator: no such sequence id */
-  PKV_ERR_HOST_MEMORY = -7     /* allocator: host memory ran out during the call; its state
+  PKV_ERR_HOST_MEMORY = -7,    /* allocator: host memory ran out during the call; its state
                                   may be partly updated, so destroy it */
+  PKV_ERR_SCRATCH = -8         /* the call needs more than the library's fixed scratch
+                                  (PKV_SCRATCH_BYTES); use the form that takes a workspace */
 };
 
 /* Library ABI version (PKV_ABI_VERSION). */
@@ -288,6 +292,33 @@ int paged_attention_decode_append_bs(void* out, const void* q, const void* k_new
                                      int max_context_len, float scale, pkv_dtype q_dtype,
                                      pkv_dtype src_dtype, pkv_dtype cache_dtype, int partition_size,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attention_decode_append_noalloc - paged_attention_decode_append
+ * (block_size 16 or 32, as the _bs form) that allocates nothing and takes no
+ * workspace, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The partition states and counters a split sequence needs live in a
+ * device array of PKV_SCRATCH_BYTES (16 MiB) that the library holds on
+ * each GPU it runs on until the process ends; the first call on a device
+ * looks up the array's address and clears its counters (a fill kernel on the
+ * call's stream).  Every call on a GPU shares that GPU's array, so calls
+ * that may overlap on one GPU (other streams, other threads) race and must
+ * not be issued.  Same arguments, result and bytes as
+ * paged_attention_decode_append_bs without workspace and workspace_bytes.
+ * Returns PKV_ERR_SCRATCH, before touching the device, when the call would
+ * need more than PKV_SCRATCH_BYTES (paged_attention_workspace_size() of its
+ * sizes); calls no hipMalloc, hipFree or allocating library routine.
+ */
+int paged_attention_decode_append_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                                          void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                          const int64_t* slot_mapping,
+                                          const int32_t* block_tables, const int32_t* context_lens,
+                                          int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,
+                                          int num_blocks, int block_size, int max_blocks_per_seq,
+                                          int max_context_len, float scale, pkv_dtype q_dtype,
+                                          pkv_dtype src_dtype, pkv_dtype cache_dtype, int partition_size,
+                                          void* stream);
 
 /*
  * Split form of paged_attention_decode_append, in two launches, for callers

@@ -23,6 +23,7 @@ __all__ = [
     "PagedKVError", "cache_code", "CACHE_FORMATS",
     "kv_cache_append", "copy_blocks", "paged_attention_decode", "paged_attention_decode_append",
     "paged_attention_decode_append_partials", "paged_attention_merge_partials",
+    "paged_attention_decode_append_noalloc", "SCRATCH_BYTES",
     "workspace_size", "WS_COUNTER_BYTES",
     "decode_partition_size", "BlockAllocator", "dtype_code", "abi_version", "gather_blocks", "scatter_blocks",
     "paged_attention_prefill",
@@ -202,6 +203,9 @@ def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim:
 # counters (PKV_WS_COUNTER_BYTES): zero before a workspace's first use, left
 # zero by every call.
 WS_COUNTER_BYTES = 32768 * 8
+# The library's fixed device scratch per GPU (PKV_SCRATCH_BYTES), used by
+# paged_attention_decode_append_noalloc.
+SCRATCH_BYTES = 16 * 1024 * 1024
 
 
 def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, k_pool: torch.Tensor,
@@ -330,6 +334,37 @@ def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, k_new: tor
     return _decode_append_call("paged_attention_decode_append", out, q, k_new, v_new, k_pool, v_pool,
                                slot_mapping, block_tables, context_lens, max_context_len, scale, k_scale,
                                v_scale, partition_size, workspace, stream)[0]
+
+
+def paged_attention_decode_append_noalloc(out: torch.Tensor, q: torch.Tensor, k_new: torch.Tensor,
+                                          v_new: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                          slot_mapping: torch.Tensor, block_tables: torch.Tensor,
+                                          context_lens: torch.Tensor, max_context_len: int,
+                                          scale: Optional[float] = None, k_scale: Optional[torch.Tensor] = None,
+                                          v_scale: Optional[torch.Tensor] = None, partition_size: int = 0,
+                                          stream=None) -> torch.Tensor:
+    """:func:`paged_attention_decode_append` without a workspace: the library's
+    fixed device scratch holds the partition states (nothing is allocated;
+    calls that overlap on one GPU must not be issued)."""
+    nb, hkv, d, bs = _pool_geometry(k_pool)
+    if q.dim() != 3 or q.shape[2] != d or out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("q and out must be [B, Hq, D] of one dtype")
+    B, hq = int(q.shape[0]), int(q.shape[1])
+    if k_new.shape != (B, hkv, d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new/v_new must be [B, Hkv, D]")
+    if slot_mapping.dtype != torch.int64 or slot_mapping.numel() != B:
+        raise ValueError("slot_mapping must be int64 [B]")
+    if block_tables.dtype != torch.int32 or context_lens.dtype != torch.int32:
+        raise ValueError("block_tables and context_lens must be int32")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    cdt = _pool_code(k_pool, v_pool, k_scale, v_scale)
+    _check(_lib.lib().paged_attention_decode_append_noalloc(
+        _ptr(out), _ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pool), _ptr(v_pool), _ptr(k_scale),
+        _ptr(v_scale), _ptr(slot_mapping), _ptr(block_tables), _ptr(context_lens), B, hq, hkv, d, nb, bs,
+        int(block_tables.shape[1]), int(max_context_len), float(scale), dtype_code(q.dtype),
+        dtype_code(k_new.dtype), cdt, int(partition_size), _stream(stream)), "paged_attention_decode_append_noalloc")
+    return out
 
 
 def paged_attention_decode_append_partials(out, q, k_new, v_new, k_pool, v_pool, slot_mapping, block_tables,

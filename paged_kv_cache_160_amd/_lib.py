@@ -103,6 +103,9 @@ _BS_INSERT = {
 for _name, _pos in _BS_INSERT.items():
     _res, _args = SIGNATURES[_name]
     SIGNATURES[_name + "_bs"] = (_res, _args[:_pos] + [c_int] + _args[_pos:])
+# the decode step without a workspace: the _bs decode-append arguments minus workspace and its size
+SIGNATURES["paged_attention_decode_append_noalloc"] = (
+    c_int, SIGNATURES["paged_attention_decode_append_bs"][1][:-3] + [c_void_p])
 SIGNATURES["pkv_alloc_create_bs"] = (c_void_p, [c_int, c_int, c_int])
 SIGNATURES["pkv_alloc_block_size"] = (c_int, [c_void_p])
 

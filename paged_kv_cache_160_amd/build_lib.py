@@ -16,7 +16,7 @@ INCLUDE = os.path.join(REPO, "include")
 LIB_NAME = "libpagedkv.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 
-SOURCES = ["api.cpp", "allocator.cpp", "cache_write.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "allocator.cpp", "cache_write.hip", "decode.hip", "prefill.hip", "noalloc.hip"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

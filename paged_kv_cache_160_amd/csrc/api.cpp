@@ -100,6 +100,7 @@ const char* pkv_strerror(int code) {
     case PKV_ERR_NO_FREE_BLOCKS: return "no free blocks";
     case PKV_ERR_UNKNOWN_SEQ: return "unknown sequence id";
     case PKV_ERR_HOST_MEMORY: return "host memory exhausted (allocator state may be partly updated)";
+    case PKV_ERR_SCRATCH: return "decode sizes need more than the library's fixed scratch (PKV_SCRATCH_BYTES)";
     default: return "unknown error code";
   }
 }
@@ -306,6 +307,31 @@ int paged_attention_decode_append_bs(void* out, const void* q, const void* k_new
                      context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
                      max_blocks_per_seq, max_context_len, scale, q_dtype, src_dtype, cache_dtype,
                      partition_size, workspace, workspace_bytes, stream, pkv::kStageBoth);
+}
+
+int paged_attention_decode_append_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                                          void* k_pool, void* v_pool, float* k_scale, float* v_scale,
+                                          const int64_t* slot_mapping, const int32_t* block_tables,
+                                          const int32_t* context_lens, int num_seqs, int num_q_heads,
+                                          int num_kv_heads, int head_dim, int num_blocks, int block_size,
+                                          int max_blocks_per_seq, int max_context_len, float scale,
+                                          pkv_dtype q_dtype, pkv_dtype src_dtype, pkv_dtype cache_dtype,
+                                          int partition_size, void* stream) {
+  if (!slot_mapping) return PKV_ERR_INVALID_ARG;
+  // invalid sizes give 0 here and are reported by decode_impl
+  const size_t need = paged_attention_workspace_size(num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                                     max_context_len, partition_size, cache_dtype);
+  if (need > static_cast<size_t>(PKV_SCRATCH_BYTES)) return PKV_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (need > 0) {
+    const int rc = pkv::scratch_workspace(static_cast<hipStream_t>(stream), &scratch);
+    if (rc != PKV_OK) return rc;
+  }
+  return decode_impl(out, q, k_new, v_new, k_pool, v_pool, k_scale, v_scale, slot_mapping, block_tables,
+                     context_lens, num_seqs, num_q_heads, num_kv_heads, head_dim, num_blocks, block_size,
+                     max_blocks_per_seq, max_context_len, scale, q_dtype, src_dtype, cache_dtype,
+                     partition_size, scratch, need > 0 ? static_cast<size_t>(PKV_SCRATCH_BYTES) : 0, stream,
+                     pkv::kStageBoth);
 }
 
 int paged_attention_decode_append(void* out, const void* q, const void* k_new, const void* v_new,

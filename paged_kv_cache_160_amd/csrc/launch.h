@@ -81,6 +81,10 @@ struct PrefillArgs {
 
 int launch_prefill(const PrefillArgs& a, hipStream_t stream);
 
+// The library's fixed device scratch on the current GPU (PKV_SCRATCH_BYTES,
+// counters cleared on first use on the given stream).
+int scratch_workspace(hipStream_t stream, void** ptr);
+
 // Automatic partition length for a decode launch (tokens, multiple of 16).
 int choose_partition_size(int num_seqs, int num_kv_heads, int max_context_len, pkv_dtype cache_dtype);
 

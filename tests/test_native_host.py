@@ -3,6 +3,7 @@ is exported, the C++ allocator matches the oracle's allocator model
 bit-exactly on every workload's setup and on random operation streams, and
 invalid arguments are rejected on the host before anything is enqueued."""
 import ctypes
+import math
 import os
 import re
 
@@ -390,3 +391,19 @@ def test_sizes_past_the_grid_limit_are_refused():
     assert lib.paged_attention_decode_bs(None, None, None, None, None, None, None, None, 1 << 20, 1 << 12, 1 << 8,
                                          128, 4, 16, 256, 4096, 0.125, pkv.PKV_BF16, pkv.PKV_BF16, 0, None, 0,
                                          None) == -1
+
+
+def test_noalloc_decode_refuses_sizes_beyond_its_scratch():
+    # the decode step without a workspace checks its scratch need on the host
+    # before any device call (no GPU here: a device call would fail with a
+    # HIP error instead)
+    lib = pkv._lib.lib()
+    B, hq, hkv, D, L, ps = 2, 8, 2, 128, 32768 * 4, 16
+    need = pkv.workspace_size(B, hq, hkv, D, L, ps, pkv.PKV_BF16)
+    assert need > pkv.SCRATCH_BYTES
+    fake = 1 << 20          # never dereferenced
+    rc = lib.paged_attention_decode_append_noalloc(fake, fake, fake, fake, fake, fake, None, None, fake, fake, fake,
+                                                   B, hq, hkv, D, 64, 16, L // 16, L, 1.0 / math.sqrt(D),
+                                                   pkv.PKV_BF16, pkv.PKV_BF16, pkv.PKV_BF16, ps, None)
+    assert rc == -8
+    assert "scratch" in lib.pkv_strerror(rc).decode()
