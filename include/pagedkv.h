@@ -53,6 +53,12 @@ extern "C" {
    use (a zero-filled workspace is) and every call leaves them zero; the
    area's size does not depend on the call, so a workspace may serve calls
    of any size.  The rest of a workspace needs no initialisation. */
+/* Single-partition decode launches of at least 1024 workgroups over batches
+   of 2 .. PKV_MAX_ORDER_SEQS sequences take the sequences longest first.  For
+   more than 256 sequences the order (one int32 per sequence) is computed by
+   the call into its workspace, after the counter area (without a workspace of
+   paged_attention_workspace_size() bytes such a launch runs in index order). */
+#define PKV_MAX_ORDER_SEQS 8192
 #define PKV_WS_COUNTER_UNITS 32768
 #define PKV_WS_COUNTER_BYTES (PKV_WS_COUNTER_UNITS * 8)
 /* Device scratch the library keeps per GPU for paged_attention_decode_append_noalloc. */
@@ -210,14 +216,17 @@ size_t paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_
  *                 and at most PKV_MAX_PARTITION_TOKENS.
  *                 When a sequence is longer than one partition, its
  *                 partitions' states are merged exactly (log-sum-exp) into
- *                 the output inside the same launch: the workgroup of the
- *                 sequence's last partition to finish reads the others'
- *                 states from the workspace and writes the output row.
+ *                 the output: for up to two partitions per sequence inside
+ *                 the same launch (the workgroup of the sequence's last
+ *                 partition to finish reads the other's state from the
+ *                 workspace and writes the output row), for more by a second
+ *                 kernel of the call; the bits are the same either way.
  *   workspace     device scratch of at least paged_attention_workspace_size()
  *                 bytes (may be NULL when that is 0): arrival counters (the
  *                 first PKV_WS_COUNTER_BYTES: zero before the workspace's
- *                 first use, left zero by every call), then the partition
- *                 states of the call, which need no initialisation.  With
+ *                 first use, left zero by every call), then the call's
+ *                 longest-first order or its partition states, which need
+ *                 no initialisation.  With
  *                 more than PKV_WS_COUNTER_UNITS (sequence, KV head) pairs
  *                 the merge runs as a second kernel of the same call instead
  *                 (same bits).  Calls that may run concurrently must not

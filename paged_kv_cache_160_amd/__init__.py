@@ -23,7 +23,7 @@ __all__ = [
     "PagedKVError", "cache_code", "CACHE_FORMATS",
     "kv_cache_append", "copy_blocks", "paged_attention_decode", "paged_attention_decode_append",
     "paged_attention_decode_append_partials", "paged_attention_merge_partials",
-    "paged_attention_decode_append_noalloc", "SCRATCH_BYTES",
+    "paged_attention_decode_append_noalloc", "SCRATCH_BYTES", "MAX_ORDER_SEQS",
     "workspace_size", "WS_COUNTER_BYTES",
     "decode_partition_size", "BlockAllocator", "dtype_code", "abi_version", "gather_blocks", "scatter_blocks",
     "paged_attention_prefill",
@@ -203,6 +203,9 @@ def workspace_size(num_seqs: int, num_q_heads: int, num_kv_heads: int, head_dim:
 # counters (PKV_WS_COUNTER_BYTES): zero before a workspace's first use, left
 # zero by every call.
 WS_COUNTER_BYTES = 32768 * 8
+# Largest batch whose single-partition decode launches take sequences
+# longest first (PKV_MAX_ORDER_SEQS).
+MAX_ORDER_SEQS = 8192
 # The library's fixed device scratch per GPU (PKV_SCRATCH_BYTES), used by
 # paged_attention_decode_append_noalloc.
 SCRATCH_BYTES = 16 * 1024 * 1024

@@ -113,15 +113,20 @@ _lib = None
 
 
 def lib() -> ctypes.CDLL:
-    """The loaded library; raises if it has not been built."""
+    """The loaded library; raises if it has not been built.  PKV_LIB names
+    another build of the same sources (a build-option variant made with
+    ``build_lib --define ... --out PATH``) to load instead."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
+        path = os.environ.get("PKV_LIB", LIB_PATH)
+        if not os.path.exists(path):
             raise RuntimeError(
-                f"{LIB_PATH} is missing: build it with `python -m paged_kv_cache_160_amd.build_lib` "
+                f"{path} is missing: build it with `python -m paged_kv_cache_160_amd.build_lib` "
                 "(or __graft_entry__.build()). There is no fallback path.")
-        handle = ctypes.CDLL(LIB_PATH)
+        handle = ctypes.CDLL(path)
         for name, (res, args) in SIGNATURES.items():
+            if path != LIB_PATH and not hasattr(handle, name):
+                continue          # a variant build may predate an entry point; calling it then fails
             fn = getattr(handle, name)
             fn.restype = res
             fn.argtypes = args

@@ -39,10 +39,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every source into LIB_PATH (always recompiles)."""
+def build(verbose: bool = False, extra_flags=None, out: str = LIB_PATH) -> str:
+    """Compile every source into ``out`` (LIB_PATH by default; always
+    recompiles).  ``extra_flags`` such as ``-DPKV_DECODE_QK_VALU=1`` select
+    the measured alternatives the kernels keep as build options."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
+    tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -54,9 +56,16 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    import argparse
+    ap = argparse.ArgumentParser(description="build libpagedkv.so for gfx950")
+    ap.add_argument("-v", action="store_true", help="print the hipcc command")
+    ap.add_argument("--define", action="append", default=[], metavar="NAME=VALUE",
+                    help="a kernel build option, e.g. PKV_DECODE_QK_VALU=1 (a variant library; use --out)")
+    ap.add_argument("--out", default=LIB_PATH, help="library path (default: the package's libpagedkv.so)")
+    args = ap.parse_args()
+    print(build(verbose=args.v, extra_flags=[f"-D{d}" for d in args.define], out=os.path.abspath(args.out)))

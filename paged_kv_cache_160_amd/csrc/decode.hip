@@ -64,14 +64,21 @@ namespace pkv {
 #ifndef PKV_DECODE_NT
 #define PKV_DECODE_NT 0        // non-temporal K/V loads (measured slower: off)
 #endif
-#ifndef PKV_DECODE_ORDER
-#define PKV_DECODE_ORDER 1     // longest-first order for many single-partition workgroups
+#ifndef PKV_DECODE_LDS
+#define PKV_DECODE_LDS 0       // K/V tiles staged in LDS by direct loads (measured against registers: off)
+#endif
+#ifndef PKV_DECODE_LDS_BUFS
+#define PKV_DECODE_LDS_BUFS 3  // tiles in flight per wave when staged in LDS
+#endif
+#ifndef PKV_DECODE_QK_VALU
+#define PKV_DECODE_QK_VALU 0   // Q.K^T on vector ALU dot products (measured against MFMA: off)
 #endif
 constexpr int kWaves = PKV_DECODE_WAVES;
 constexpr int kThreads = kWaves * kWave;
 constexpr int kMaxGroup = 16;
-constexpr int kMaxOrderSeqs = 256;   // longest-first order: batches of at most this many sequences
-static_assert(kMaxOrderSeqs <= PKV_DECODE_WAVES * 64, "one ranking thread per sequence");
+constexpr int kMaxOrderSeqs = PKV_MAX_ORDER_SEQS;   // longest-first order: batches of at most this many
+constexpr int kOrderThreads = 1024;
+static_assert(kMaxRankSeqs <= kThreads, "one ranking thread per sequence");
 constexpr int kMaxPartitionBlocks = PKV_MAX_PARTITION_TOKENS / kTileTokens;
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -256,6 +263,64 @@ __device__ __forceinline__ float4_t qk_tile(const Words<Geo<QT, KT, KT, D>::kWor
   return s;
 }
 
+// ---- Q.K^T on the vector ALU (build option PKV_DECODE_QK_VALU) -------------
+// For groups of up to 4 heads: lane (c, j) holds row c, quarter j of the K
+// tile and the same quarter of each head's query; it forms the 4 partial dot
+// products with packed 16-bit dot instructions, the 4 lanes of a row sum them
+// with row-swap permutes, and the wave's LDS scratch turns "token c, all
+// heads" into the MFMA output layout (lane = head + 16 * (token / 4), value r
+// = token 4j + r) that the softmax and P.V steps take.
+template <typename QT>
+__device__ __forceinline__ float dot2acc(uint32_t a, uint32_t b, float c) {
+  if constexpr (std::is_same<QT, BF16>::value)
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+  else
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), c, false);
+}
+
+template <typename QT, typename KT, int D>
+__device__ __forceinline__ float4_t qk_tile_valu(const Words<Geo<QT, KT, KT, D>::kWords>& k,
+                                                 const uint32_t (&qv)[4][D / 8], float* sm_st, int c, int j) {
+  uint32_t kw[D / 8];                       // this lane's 32 K elements as 16-bit pairs, in order
+  if constexpr (KT::bits == 16) {
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) kw[i] = k.w[i];
+  } else {
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m) {
+      const uint2 c2 = conv8<QT, KT>(k.w[m]);
+      kw[2 * m] = c2.x;
+      kw[2 * m + 1] = c2.y;
+    }
+  }
+  float acc[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) {
+    acc[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 8; ++i) acc[h] = dot2acc<QT>(kw[i], qv[h][i], acc[h]);
+    acc[h] = col_sum4(acc[h]);
+  }
+  if (j == 0) {
+#pragma unroll
+    for (int h = 0; h < 4; ++h) sm_st[h * 16 + c] = acc[h];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  float4_t s = {0.f, 0.f, 0.f, 0.f};
+  if (c < 4) {
+    const float4 v = *reinterpret_cast<const float4*>(sm_st + c * 16 + 4 * j);
+    s[0] = v.x;
+    s[1] = v.y;
+    s[2] = v.z;
+    s[3] = v.w;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();           // the next tile's writes follow these reads
+  return s;
+}
+
 template <typename QT>
 __device__ __forceinline__ float4_t mfma16(uint2 a, uint2 b, float4_t c) {
   if constexpr (std::is_same<QT, BF16>::value)
@@ -427,10 +492,49 @@ __device__ __forceinline__ float2 load_agent2(const float* p) {
 // ---- the main kernel ------------------------------------------------------------
 
 
+// ---- longest-first order of a batch (once per call) ----------------------------
+// order[r] = the sequence at position r when the batch is sorted by context
+// length, longest first, ties by lower index: a permutation of
+// 0..num_seqs-1 for any length values.  One workgroup sorts 64-bit keys
+// (length above, complement of the index below) in LDS with a bitonic
+// network; num_seqs <= kMaxOrderSeqs.
+__global__ void __launch_bounds__(kOrderThreads) order_kernel(const int32_t* context_lens, int num_seqs,
+                                                              int32_t* order) {
+  __shared__ uint64_t key[kMaxOrderSeqs];
+  int n = 1;
+  while (n < num_seqs) n <<= 1;
+  for (int t = threadIdx.x; t < n; t += kOrderThreads) {
+    // padding sorts last: every real key is at least 2^32 - kMaxOrderSeqs
+    key[t] = t < num_seqs ? (static_cast<uint64_t>(static_cast<uint32_t>(max(context_lens[t], 0))) << 32) |
+                                (0xffffffffu - static_cast<uint32_t>(t))
+                          : 0ull;
+  }
+  __syncthreads();
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int jj = k >> 1; jj > 0; jj >>= 1) {
+      for (int t = threadIdx.x; t < n; t += kOrderThreads) {
+        const int u = t ^ jj;
+        if (u > t) {
+          const uint64_t x = key[t], y = key[u];
+          // descending within blocks whose bit k is clear, ascending otherwise
+          const bool desc = (t & k) == 0;
+          if (desc ? x < y : x > y) {
+            key[t] = y;
+            key[u] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  for (int r = threadIdx.x; r < num_seqs; r += kOrderThreads)
+    order[r] = static_cast<int32_t>(0xffffffffu - static_cast<uint32_t>(key[r]));
+}
+
 // Index of the sequence at position r of the longest-first order of the
 // batch (ties: lower index first), which is a permutation of 0..num_seqs-1
 // for any length values.  Every thread of the workgroup calls it;
-// num_seqs <= kMaxOrderSeqs.
+// num_seqs <= kMaxRankSeqs.
 __device__ __forceinline__ int seq_of_rank(const int32_t* context_lens, int num_seqs, int r, int tid,
                                            int* sm_len, int* sm_part, int* sm_pick) {
   // slots past num_seqs (to a multiple of 4) hold INT_MIN at index >= num_seqs:
@@ -473,7 +577,7 @@ __device__ __forceinline__ int seq_of_rank(const int32_t* context_lens, int num_
 // Quantised pools keep three waves per SIMD (their tiles are half as large,
 // so the registers fit); 16-bit and fp32 pools take two.
 template <typename KT>
-constexpr int decode_min_blocks() { return KT::quantised ? 3 : 2; }
+constexpr int decode_min_blocks() { return KT::quantised && !PKV_DECODE_QK_VALU ? 3 : 2; }
 
 // ORDER: workgroups take sequences longest first (a separate instance, so
 // launches without the order carry none of its code or registers).
@@ -489,6 +593,10 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   __shared__ float sm_l[kWaves][kMaxGroup];
   __shared__ float sm_o[kWaves][kMaxGroup][D];
   __shared__ int sm_ids[kMaxPartitionBlocks];
+  __shared__ __attribute__((aligned(16))) float sm_st[kWaves][PKV_DECODE_QK_VALU ? 64 : 1];   // vector-ALU Q.K^T
+  constexpr bool kLdsStage = PKV_DECODE_LDS && KT::bits == 16 && VT::bits == 16 && D == 128;
+  __shared__ __attribute__((aligned(16))) uint8_t
+      sm_ring[kLdsStage ? kWaves * PKV_DECODE_LDS_BUFS * 2 * Geo<QT, KT, VT, D>::kTileBytes : 16];
 
   const int P = a.num_partitions;
   const int part = blockIdx.x % P;
@@ -514,6 +622,9 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   // sequence's end lie inside its table row and are never used).
   // Q^T operand: lane (head column c, k-group j) holds q[head c][j*D/4 ...).
   Words<G::qWords> qop;
+  constexpr bool kValuQK = PKV_DECODE_QK_VALU && !std::is_same<KT, F32>::value;
+  // vector-ALU form: quarter j of each of the group's (up to 4) queries
+  uint32_t qv[4][D / 8];
   int phys[kLoads];
   auto first_loads = [&](int bb) {
     const bool valid = c < group;
@@ -523,6 +634,16 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
     if (!valid) {
 #pragma unroll
       for (int i = 0; i < G::qWords; ++i) qop.w[i] = 0u;
+    }
+    if constexpr (kValuQK) {
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        Words<D / 8> w;
+        const uint8_t* qh = static_cast<const uint8_t*>(a.q) + ((row0 + min(h, group - 1)) * D + j * (D / 4)) * 2;
+        load_words<D / 8, false>(w, qh);
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) qv[h][i] = h < group ? w.w[i] : 0u;
+      }
     }
     const int32_t* table = a.block_tables + static_cast<int64_t>(bb) * a.max_blocks_per_seq;
 #pragma unroll
@@ -534,20 +655,27 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
 
   // Workgroups are dispatched in index order.  When many of them share the
   // chip in turns (one partition per sequence), index r takes the r-th
-  // longest sequence, so long sequences start first and none starts last.
-  // The loads for sequence r go out first; they are repeated for the
-  // sequence the order names only when it is another one.
+  // longest sequence (the order kernel launched before this one wrote the
+  // permutation), so long sequences start first and none starts last.  The
+  // loads for sequence r go out together with the read of the order; they
+  // are repeated for the sequence the order names only when it is another.
   int b = blockIdx.x / (P * a.num_kv_heads);
   int L = a.context_lens[b];
   first_loads(b);
   if constexpr (ORDER) {
-    __shared__ __attribute__((aligned(16))) int sm_len[kMaxOrderSeqs];
+    __shared__ __attribute__((aligned(16))) int sm_len[kMaxRankSeqs];
     __shared__ int sm_part[kThreads];
     __shared__ int sm_pick;
-    const int pick = seq_of_rank(a.context_lens, a.num_seqs, b, tid, sm_len, sm_part, &sm_pick);
+    int pick;
+    if (a.num_seqs <= kMaxRankSeqs) {
+      pick = seq_of_rank(a.context_lens, a.num_seqs, b, tid, sm_len, sm_part, &sm_pick);
+    } else {
+      pick = a.seq_order[b];
+      if (pick < 0 || pick >= a.num_seqs) pick = b;   // (never: the order is a permutation)
+    }
     if (pick != b) {
       b = pick;
-      L = sm_len[b];
+      L = a.context_lens[b];
       first_loads(b);
     }
   }
@@ -650,7 +778,13 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
 
   auto compute_block = [&](BlockRegs<QT, KT, VT, D>& r, int i, bool ok) {
     const int base = tok0 + i * kTileTokens;   // logical position of the block's token 0
-    float4_t s = qk_tile<QT, KT, D>(r.k, qop);
+    float4_t s;
+    if constexpr (kValuQK) {
+      if (group <= 4) s = qk_tile_valu<QT, KT, D>(r.k, qv, &sm_st[wave][0], c, j);
+      else s = qk_tile<QT, KT, D>(r.k, qop);
+    } else {
+      s = qk_tile<QT, KT, D>(r.k, qop);
+    }
     float sc[4] = {s[0], s[1], s[2], s[3]};
     float ksc[4] = {1.f, 1.f, 1.f, 1.f};
     float vsc[4] = {1.f, 1.f, 1.f, 1.f};
@@ -734,7 +868,75 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   // unconditionally (past the end it re-reads the wave's last block, an L2
   // hit) so that all paths through the loop carry the same loads in the same
   // order and each wait covers only the block about to be used.
-  if (wave < nblk) {
+  if constexpr (kLdsStage) {
+    // Build option PKV_DECODE_LDS (16-bit caches, head_dim 128): each wave
+    // streams its tiles into a ring of kBufs LDS slots with direct loads
+    // (global_load_lds, no registers held for the tiles in flight), then reads
+    // its MFMA operands from LDS.  Within a tile row the 16-byte chunks are
+    // XOR-swizzled by the row so that the operand reads (16 rows at one
+    // column, or one row's 4 columns) touch distinct banks.
+    constexpr int kBufs = PKV_DECODE_LDS_BUFS;
+    constexpr int kCh = 16;                                   // 16-byte chunks per 256-byte row
+    constexpr int kInsts = kTileTokens * kCh / kWave;         // direct loads per tile (K or V): 4
+    uint8_t* ring = sm_ring + wave * kBufs * 2 * G::kTileBytes;
+    int lane_off[kInsts];
+#pragma unroll
+    for (int t = 0; t < kInsts; ++t) {
+      const int pos = t * kWave + lane;                       // chunk position in the LDS tile
+      const int row = pos / kCh;
+      lane_off[t] = row * G::kRowBytes + 16 * ((pos % kCh) ^ (row & 15));
+    }
+    auto dma = [&](int slot, int i) {
+      int t0 = __builtin_amdgcn_readfirstlane(sm_ids[i]);
+      if (t0 < 0) t0 = -g_tile;
+      const int64_t tile = static_cast<int64_t>(t0) + g_tile;
+      uint8_t* kd = ring + slot * 2 * G::kTileBytes;
+      uint8_t* vd = kd + G::kTileBytes;
+#pragma unroll
+      for (int t = 0; t < kInsts; ++t) {
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(kbase + tile * G::kTileBytes + lane_off[t]),
+            (__attribute__((address_space(3))) void*)(kd + t * kWave * 16), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(
+            (const __attribute__((address_space(1))) void*)(vbase + tile * G::vTileBytes + lane_off[t]),
+            (__attribute__((address_space(3))) void*)(vd + t * kWave * 16), 16, 0, 0);
+      }
+    };
+    auto chunk = [&](const uint8_t* base, int row, int col) {
+      return *reinterpret_cast<const u32x4_t*>(base + row * G::kRowBytes + 16 * (col ^ (row & 15)));
+    };
+    if (wave < nblk) {
+      const int last = wave + kWaves * ((nblk - 1 - wave) / kWaves);
+#pragma unroll
+      for (int st = 0; st < kBufs - 1; ++st) dma(st, min(wave + st * kWaves, last));
+      int slot = 0;
+      for (int i = wave; i < nblk; i += kWaves) {
+        dma((slot + kBufs - 1) % kBufs, min(i + (kBufs - 1) * kWaves, last));
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kBufs - 1) * 2 * kInsts) : "memory");
+        const uint8_t* kd = ring + slot * 2 * G::kTileBytes;
+        const uint8_t* vd = kd + G::kTileBytes;
+        BlockRegs<QT, KT, VT, D> r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const u32x4_t x = chunk(kd, c, 4 * j + q);          // K row c, quarter j
+          r.k.w[4 * q] = x[0];
+          r.k.w[4 * q + 1] = x[1];
+          r.k.w[4 * q + 2] = x[2];
+          r.k.w[4 * q + 3] = x[3];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const u32x4_t x = chunk(vd, 4 * j + e, c);          // V row 4j+e, columns 8c..8c+7
+          r.v[e].w[0] = x[0];
+          r.v[e].w[1] = x[1];
+          r.v[e].w[2] = x[2];
+          r.v[e].w[3] = x[3];
+        }
+        compute_block(r, i, __builtin_amdgcn_readfirstlane(sm_ids[i]) >= 0);
+        slot = slot + 1 == kBufs ? 0 : slot + 1;
+      }
+    }
+  } else if (wave < nblk) {
     const int last = wave + kWaves * ((nblk - 1 - wave) / kWaves);
     BlockRegs<QT, KT, VT, D> r[PIPE];
     bool ok[PIPE];
@@ -762,13 +964,22 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   }
 
   // ---- merge the waves' states ----
+  // The pipeline's last loads (re-reads of the wave's last block, an L2 hit)
+  // are drained here, so that no later instruction waits on them - the wait
+  // counter is in order, and a wait for them would also wait for whatever
+  // was issued after them.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // A sequence split over several partitions and merged in this launch: its
   // workgroups count their arrival on the sequence's (KV head's) counter;
   // the request goes out now and its reply is read after the wave merge.
   const bool merge_here = P > 1 && np_b > 1 && a.counters != nullptr;
   int* const cnt = merge_here ? a.counters + 2 * (static_cast<int64_t>(b) * a.num_kv_heads + g) : nullptr;
+  // (an increment the compiler leaves as one atomic: an add would go
+  // through its wave-level combining, whose result it waits for at once)
   int arrival = 0;
-  if (merge_here && tid == 0) arrival = atomicAdd(cnt, 1);
+  if (merge_here && tid == 0)
+    arrival = static_cast<int>(__builtin_amdgcn_atomic_inc32(reinterpret_cast<unsigned*>(cnt), 0xffffffffu,
+                                                             __ATOMIC_RELAXED, "agent"));
 
   l = col_sum4(l);
   if (j == 0 && c < group) {
@@ -1016,11 +1227,19 @@ static int launch_typed(const DecodeArgs& a, hipStream_t stream, int stages) {
     // longest first where the dispatcher hands out workgroups in turns and
     // each holds a whole sequence (split sequences already have workgroups of
     // at most one partition each: the order measured no faster there)
-    const bool order = PKV_DECODE_ORDER && a.num_partitions == 1 && a.num_seqs >= 2 &&
-                       a.num_seqs <= kMaxOrderSeqs && grid >= 4 * 256;
-    if (order)
+    if (a.seq_order != nullptr ||
+        (decode_uses_order(a.num_seqs, a.num_kv_heads, a.num_partitions) && a.num_seqs <= kMaxRankSeqs)) {
+      // small batches: every workgroup ranks in its prologue (measured faster
+      // than a sort launch ahead of the kernel); larger ones: sorted once
+      if (a.num_seqs > kMaxRankSeqs) {
+        hipLaunchKernelGGL(order_kernel, dim3(1), dim3(kOrderThreads), 0, stream, a.context_lens, a.num_seqs,
+                           const_cast<int32_t*>(a.seq_order));
+        rc = check_launch();
+        if (rc != PKV_OK) return rc;
+      }
       hipLaunchKernelGGL((paged_decode_kernel<QT, KT, VT, D, pipe, true>), dim3(static_cast<unsigned>(grid)),
                          dim3(kThreads), 0, stream, a);
+    }
     else
       hipLaunchKernelGGL((paged_decode_kernel<QT, KT, VT, D, pipe, false>), dim3(static_cast<unsigned>(grid)),
                          dim3(kThreads), 0, stream, a);

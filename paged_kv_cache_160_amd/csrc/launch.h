@@ -5,6 +5,10 @@
 
 #include "pagedkv.h"
 
+#ifndef PKV_DECODE_ORDER
+#define PKV_DECODE_ORDER 1     // longest-first order for many single-partition workgroups
+#endif
+
 namespace pkv {
 
 // Map the runtime's last error after a launch to a return code.
@@ -51,6 +55,10 @@ struct DecodeArgs {
   // nullptr: the attention kernel writes every partition state and a merge
   // kernel combines them (split form).
   int* counters;           // [num_seqs][num_kv_heads][2]
+  // Longest-first order (single-partition launches of many workgroups,
+  // decode_uses_order): workgroup r takes sequence seq_order[r], which an
+  // order kernel launched just before writes; nullptr: index order.
+  const int32_t* seq_order;   // [num_seqs]
   float* part_ml;          // [num_seqs][num_q_heads][num_partitions][2]  (m, l)
   float* part_acc;         // [num_seqs][num_q_heads][num_partitions][head_dim]
 };
@@ -84,6 +92,23 @@ int launch_prefill(const PrefillArgs& a, hipStream_t stream);
 // The library's fixed device scratch on the current GPU (PKV_SCRATCH_BYTES,
 // counters cleared on first use on the given stream).
 int scratch_workspace(hipStream_t stream, void** ptr);
+
+// Whether a decode launch takes sequences longest first: single-partition
+// launches of at least four workgroups per CU (the dispatcher then hands
+// them out in turns; split sequences already have workgroups of at most one
+// partition each, and the order measured no faster there), for batches of
+// 2 .. PKV_MAX_ORDER_SEQS sequences.
+inline bool decode_uses_order(int num_seqs, int num_kv_heads, int num_partitions) {
+  return PKV_DECODE_ORDER && num_partitions == 1 && num_seqs >= 2 && num_seqs <= PKV_MAX_ORDER_SEQS &&
+         static_cast<int64_t>(num_seqs) * num_kv_heads >= 4 * 256;
+}
+
+// Up to this many sequences every workgroup of an ordered launch ranks the
+// batch itself; larger batches are sorted once per call into the workspace.
+constexpr int kMaxRankSeqs = 256;
+inline bool decode_order_in_workspace(int num_seqs, int num_kv_heads, int num_partitions) {
+  return decode_uses_order(num_seqs, num_kv_heads, num_partitions) && num_seqs > kMaxRankSeqs;
+}
 
 // Automatic partition length for a decode launch (tokens, multiple of 16).
 int choose_partition_size(int num_seqs, int num_kv_heads, int max_context_len, pkv_dtype cache_dtype);

@@ -332,3 +332,33 @@ def test_more_sequence_heads_than_counters_use_the_merge_kernel():
     sample = [0, 1, 700, B - 1]
     exp = scenario.expected_decode_rows(w, wl.queries(w, 0)[sample], sample, [lens[b] for b in sample])
     assert max_err(out_to_f64(one)[sample], exp) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("cache", [None, "fp8_e4m3"])
+def test_two_partition_merge_in_kernel_equals_split_form(cache):
+    # sequences of one and of two partitions in one launch of two partitions
+    # per sequence (merged inside the attention kernel by the one-call form):
+    # the same bits as the split form's merge kernel, and the oracle
+    lens = [3000, 1500, 10, 2900, 1504, 1505, 0, 2999]
+    w, g = _custom(lens, 16, 4, 128, "bf16" if cache is None else "f32", cache_dtype=cache,
+                   q_dtype=None if cache is None else "bf16", seed=37)
+    c = g.cache
+    seqs = list(range(w.num_seqs))
+    tables = c.block_tables(seqs)
+    q = g.queries(0)
+    ps = 1504
+    assert -(-max(lens) // ps) == 2
+    say(f"[merge] two partitions of {ps} tokens, cache {cache or 'bf16'}")
+    one = torch.empty_like(q)
+    pkv.paged_attention_decode(one, q, c.k[0], c.v[0], tables[0], tables[1], tables[2], k_scale=c.k_scale[0],
+                               v_scale=c.v_scale[0], partition_size=ps)
+    two = torch.empty_like(q)
+    _, ws = pkv.paged_attention_decode_append_partials(two, q, None, None, c.k[0], c.v[0], None, tables[0],
+                                                       tables[1], tables[2], k_scale=c.k_scale[0],
+                                                       v_scale=c.v_scale[0], partition_size=ps)
+    pkv.paged_attention_merge_partials(two, tables[1], 4, w.max_blocks_per_seq, tables[2], c.cache_code,
+                                       partition_size=ps, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(one.cpu(), two.cpu())
+    exp = scenario.expected_decode_rows(w, wl.queries(w, 0), seqs, lens)
+    assert max_err(out_to_f64(one), exp) <= TOL[w.cache_dtype]

@@ -2,16 +2,19 @@
 
 When every sequence of a batch fits one partition and the launch has at
 least four workgroups per CU (the dispatcher then hands them out in turns),
-workgroup r takes the r-th longest sequence, ties to the lower index.  Each
-output row must still be its own sequence's attention ("KV Cache 和 vLLM"
-§1.2-1.3: out = softmax(q K^T / sqrt(d)) V over the sequence's cached
-tokens).  Batches in that regime - ragged with ties and an empty sequence,
-for each of the ranking's three slicings (up to 64, 128 and 256 sequences),
-one already longest first (the kernel's shortcut), and fp8 and int8 + int4
-caches - are checked against the fp64 oracle; the fused step, which writes
-the step's K/V row through the same sequence index, is checked bit for bit
-against append-then-decode.
+workgroup r takes the r-th longest sequence, ties to the lower index (up to
+256 sequences every workgroup ranks the batch; larger batches are sorted
+once per call, by a one-workgroup sort kernel, into the call's workspace).  Each output row must still be its own sequence's
+attention ("KV Cache 和 vLLM" §1.2-1.3: out = softmax(q K^T / sqrt(d)) V over
+the sequence's cached tokens).  Batches in that regime - ragged with ties
+and an empty sequence, from 40 to 3000 sequences, one already longest first,
+and fp8 and int8 + int4 caches - are checked against the fp64 oracle; the
+order changes no output bit (a call without a workspace runs in index order);
+the fused step, which writes the step's K/V row through the same sequence
+index, is checked bit for bit against append-then-decode.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -42,6 +45,8 @@ CASES = [  # (kind, num_seqs, hq, hkv, head_dim, source dtype, longest context +
     ("sorted", 64, 16, 16, 128, "bf16", 400, None),
     ("ragged", 48, 32, 32, 128, "f32", 400, "fp8_e4m3"),
     ("ragged", 48, 32, 32, 64, "f32", 400, "int8_int4"),
+    ("ragged", 600, 8, 2, 64, "bf16", 200, None),
+    ("ragged", 3000, 4, 1, 64, "bf16", 80, None),
 ]
 
 
@@ -97,3 +102,37 @@ def test_longest_first_fused_step_equals_append_then_decode():
     assert torch.equal(ta, tb) and torch.equal(la, lb)
     for b in seqs:
         check_cache_rows(w, fus.cache, 0, b, tb[b].numpy(), int(lb[b]))
+
+
+@pytest.mark.parametrize("case", [CASES[6], CASES[7]], ids=["600x2", "3000x1"])
+def test_order_changes_no_output_bit(case):
+    # the same call with the sorted order (workspace given) and in index
+    # order (no workspace): every workgroup computes its row the same way
+    w = _workload(case)
+    g = GpuWorkload(w).run(wl.setup_ops(w))
+    c = g.cache
+    seqs = list(range(w.num_seqs))
+    bt, lens, max_len = c.block_tables(seqs)
+    q = g.queries(0)
+    B, hq, hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
+    need = pkv.workspace_size(B, hq, hkv, D, max_len, 0, c.cache_code)
+    assert need > pkv.WS_COUNTER_BYTES          # the launch takes the order
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    lib = pkv._lib.lib()
+    sp = torch.cuda.current_stream().cuda_stream
+    outs = []
+    for wp, wb in ((ws.data_ptr(), need), (None, 0)):
+        out = torch.empty_like(q)
+        rc = lib.paged_attention_decode_bs(out.data_ptr(), q.data_ptr(), c.k[0].data_ptr(), c.v[0].data_ptr(),
+                                           None, None, bt.data_ptr(), lens.data_ptr(), B, hq, hkv, D,
+                                           w.num_blocks, w.block_size, w.max_blocks_per_seq, max_len,
+                                           1.0 / math.sqrt(D), pkv.dtype_code(q.dtype), c.cache_code, 0, wp, wb, sp)
+        assert rc == 0
+        outs.append(out.cpu())
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    # the order the kernel wrote is the longest-first permutation
+    order = ws[pkv.WS_COUNTER_BYTES:pkv.WS_COUNTER_BYTES + 4 * B].view(torch.int32).cpu().numpy()
+    ln = lens.cpu().numpy()
+    expect = sorted(range(B), key=lambda b: (-int(ln[b]), b))
+    assert order.tolist() == expect

@@ -264,7 +264,11 @@ def test_partition_plan_and_workspace():
         assert ps % 16 == 0 and ps > 0 and npart == -(-L // ps)
         ws = pkv.workspace_size(B, hq, hkv, 128, L, 0, pkv.PKV_BF16)
         if npart == 1:
-            assert ws == 0
+            # a workspace only for the longest-first order of launches of
+            # >= 1024 workgroups over more than 256 sequences: after the
+            # counter area, one int32 per sequence
+            ordered = 256 < B <= pkv.MAX_ORDER_SEQS and B * hkv >= 1024
+            assert ws == (pkv.WS_COUNTER_BYTES + -(-4 * B // 256) * 256 if ordered else 0), (B, hkv, L, ws)
         else:
             assert ws >= pkv.WS_COUNTER_BYTES + B * hq * npart * (128 + 2) * 4
     assert pkv.workspace_size(16, 32, 8, 128, 4096, 16, pkv.PKV_BF16) >= 16 * 32 * 256 * 130 * 4
@@ -277,6 +281,7 @@ def test_counter_area_size_matches_header():
     units = int(re.search(r"#define PKV_WS_COUNTER_UNITS (\d+)", text).group(1))
     assert re.search(r"#define PKV_WS_COUNTER_BYTES \(PKV_WS_COUNTER_UNITS \* 8\)", text)
     assert pkv.WS_COUNTER_BYTES == units * 8
+    assert pkv.MAX_ORDER_SEQS == int(re.search(r"#define PKV_MAX_ORDER_SEQS (\d+)", text).group(1))
 
 
 def test_swap_hand_worked_matches_model():
