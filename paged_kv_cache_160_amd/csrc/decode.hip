@@ -35,12 +35,18 @@
 //    it by more than 2^8, so the output is rescaled about once per wave.
 //  * Probabilities enter the P*V MFMA as a hi + lo pair of 16-bit values, so
 //    P carries ~16 significant bits while the MFMA still accumulates in fp32.
-//  * Long sequences split into partitions; each partition's (max, sum,
-//    unnormalised output) goes to the workspace (an empty one writes max
-//    -inf) and a second launch merges them with the log-sum-exp formula.
-//    Merging inside this kernel, in the workgroup of a (sequence, KV head)
-//    that finishes last, was measured slower: the device-scope fences it
-//    needs write back L2.
+//    With a quantised V pool every code converts exactly to f16, and P
+//    rounded once to f16 (11 significant bits) takes one MFMA per column
+//    tile instead of two.
+//  * Long sequences split into partitions, each with its state (max, sum,
+//    unnormalised output), merged with the log-sum-exp formula.  Up to two
+//    partitions per sequence the merge happens in this launch: the last
+//    workgroup of a (sequence, KV head) to finish, told so by an arrival
+//    counter, reads the other's state (stored and loaded at device scope,
+//    past the XCD caches - no fences) and writes the output.  With more
+//    partitions, or in the split form, every state goes to the workspace
+//    (an empty partition writes max -inf) and a second launch merges them;
+//    the two places share one merge routine and give the same bits.
 
 #include <limits.h>
 #include <math.h>
@@ -69,6 +75,12 @@ namespace pkv {
 #endif
 #ifndef PKV_DECODE_LDS_BUFS
 #define PKV_DECODE_LDS_BUFS 3  // tiles in flight per wave when staged in LDS
+#endif
+#ifndef PKV_DECODE_PV_X32
+#define PKV_DECODE_PV_X32 0    // hi and lo probabilities in one 16x16x32 MFMA (measured no faster: off)
+#endif
+#ifndef PKV_DECODE_PV_F16Q
+#define PKV_DECODE_PV_F16Q 1   // quantised V: P rounded once to f16, one MFMA per column tile
 #endif
 #ifndef PKV_DECODE_QK_VALU
 #define PKV_DECODE_QK_VALU 0   // Q.K^T on vector ALU dot products (measured against MFMA: off)
@@ -331,6 +343,21 @@ __device__ __forceinline__ float4_t mfma16(uint2 a, uint2 b, float4_t c) {
                                                  __builtin_bit_cast(half4_t, b), c, 0, 0, 0);
 }
 
+// Build option PKV_DECODE_PV_X32: the hi and lo halves of the probabilities
+// in one 16x16x32 MFMA (A = hi and lo of tokens 4j..4j+3, B = the same 4 V
+// values twice) instead of two 16x16x16 ones; on gfx950 the one takes as long
+// as each of the two, but the repeated B operand costs two register copies.
+template <typename QT>
+__device__ __forceinline__ float4_t mfma_hilo(uint4 p_hilo, uint2 b, float4_t c) {
+  const uint4 bb = make_uint4(b.x, b.y, b.x, b.y);
+  if constexpr (std::is_same<QT, BF16>::value)
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, p_hilo),
+                                                   __builtin_bit_cast(bf16x8_t, bb), c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, p_hilo),
+                                                  __builtin_bit_cast(half8_t, bb), c, 0, 0, 0);
+}
+
 // ---- P*V on MFMA -----------------------------------------------------------------
 // p[r]: probability (times the V scale of a quantised pool) of token 4j+r for
 // head column c.
@@ -358,38 +385,42 @@ __device__ __forceinline__ void pv_tile(const float (&p)[4], const Words<Geo<QT,
       for (int nt = 0; nt < G::DC; ++nt)
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(p[r], __uint_as_float(v[r].w[nt]), o[nt], 0, 0, 0);
   } else {
-    // hi/lo split of the probabilities
-    uint32_t h01 = pack2<QT>(p[0], p[1]);
-    uint32_t h23 = pack2<QT>(p[2], p[3]);
-    uint32_t l01 = pack2<QT>(p[0] - lo16_to_f32<QT>(h01), p[1] - hi16_to_f32<QT>(h01));
-    uint32_t l23 = pack2<QT>(p[2] - lo16_to_f32<QT>(h23), p[3] - hi16_to_f32<QT>(h23));
+    // PT: the 16-bit type of the P*V operands.  Probabilities are split in a
+    // hi and a lo half (P keeps ~16 significant bits), except for quantised
+    // V (build option PKV_DECODE_PV_F16Q, on): every code converts exactly
+    // to f16, and P rounded once to f16 keeps 11 bits in one MFMA per column
+    // tile.
+    constexpr bool kOne = PKV_DECODE_PV_F16Q && VT::quantised;
+    using PT = typename std::conditional<kOne, F16, QT>::type;
+    const uint32_t h01 = pack2<PT>(p[0], p[1]);
+    const uint32_t h23 = pack2<PT>(p[2], p[3]);
+    const uint32_t l01 = kOne ? 0u : pack2<PT>(p[0] - lo16_to_f32<PT>(h01), p[1] - hi16_to_f32<PT>(h01));
+    const uint32_t l23 = kOne ? 0u : pack2<PT>(p[2] - lo16_to_f32<PT>(h23), p[3] - hi16_to_f32<PT>(h23));
     const uint2 phi = make_uint2(h01, h23);
     const uint2 plo = make_uint2(l01, l23);
-    // 16-bit words of the 4 V rows: element nt of row e sits in word nt/2.
-    uint32_t w16[4][G::DC / 2];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if constexpr (VT::bits == 16) {
-#pragma unroll
-        for (int i = 0; i < G::vWords; ++i) w16[e][i] = v[e].w[i];
-      } else if constexpr (VT::bits == 8) {
-#pragma unroll
-        for (int i = 0; i < G::vWords; ++i) {
-          const uint2 c2 = conv8<QT, VT>(v[e].w[i]);
-          w16[e][2 * i] = c2.x;
-          w16[e][2 * i + 1] = c2.y;
-        }
+    const uint4 phl = make_uint4(h01, h23, l01, l23);
+    auto acc = [&](float4_t& o_, uint2 b_) {
+      if constexpr (kOne) {
+        o_ = mfma16<PT>(phi, b_, o_);
+      } else if constexpr (PKV_DECODE_PV_X32) {
+        o_ = mfma_hilo<PT>(phl, b_, o_);
       } else {
-        static_assert(std::is_same<VT, I4>::value, "4-bit format");
-        // word k: columns k (low half) and k + DC/2 (high half), offset by
-        // MAGIC + 8; x ^ 8 is x + 8 for a 4-bit two's complement code
+        o_ = mfma16<PT>(phi, b_, o_);
+        o_ = mfma16<PT>(plo, b_, o_);
+      }
+    };
+    static_assert(VT::bits == 16 || VT::bits == 8 || std::is_same<VT, I4>::value, "V format");
+    if constexpr (std::is_same<VT, I4>::value) {
+      // word k of row e: columns k (low half) and k + DC/2 (high half),
+      // offset by MAGIC + 8; x ^ 8 is x + 8 for a 4-bit two's complement code
+      uint32_t w16[4][G::DC / 2];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
         const uint32_t u = v[e].w[0] ^ (G::DC == 8 ? 0x88888888u : 0x00008888u);   // DC = 4: one 16-bit row
         const uint32_t s = G::DC == 8 ? u : (u | (u << 8));   // DC = 4: codes 2, 3 move to bits 16..23
 #pragma unroll
-        for (int k = 0; k < G::DC / 2; ++k) w16[e][k] = ((s >> (4 * k)) & 0x000F000Fu) | I4Magic<QT>::pair;
+        for (int k = 0; k < G::DC / 2; ++k) w16[e][k] = ((s >> (4 * k)) & 0x000F000Fu) | I4Magic<PT>::pair;
       }
-    }
-    if constexpr (std::is_same<VT, I4>::value) {
 #pragma unroll
       for (int nt = 0; nt < G::DC; ++nt) {
         const uint32_t sel = (nt >= G::DC / 2) ? 0x07060302u : 0x05040100u;
@@ -397,13 +428,42 @@ __device__ __forceinline__ void pv_tile(const float (&p)[4], const Words<Geo<QT,
         uint2 b;
         b.x = __builtin_amdgcn_perm(w16[1][wi], w16[0][wi], sel);
         b.y = __builtin_amdgcn_perm(w16[3][wi], w16[2][wi], sel);
-        o[nt] = mfma16<QT>(phi, b, o[nt]);
-        o[nt] = mfma16<QT>(plo, b, o[nt]);
+        acc(o[nt], b);
       }
-      const uint2 boff = make_uint2(I4Magic<QT>::off, I4Magic<QT>::off);
-      ocorr = mfma16<QT>(phi, boff, ocorr);
-      ocorr = mfma16<QT>(plo, boff, ocorr);
+      acc(ocorr, make_uint2(I4Magic<PT>::off, I4Magic<PT>::off));
+    } else if constexpr (VT::bits == 8 && !std::is_same<VT, I8>::value) {
+      // fp8 codes: the bytes of rows (0, 1) and (2, 3) are interleaved first
+      // - one byte permute per two columns - so that each pair conversion
+      // gives an operand word (row 2r, row 2r + 1 of one column) directly
+#pragma unroll
+      for (int i = 0; i < G::vWords; ++i) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const uint32_t sel = half ? 0x07030602u : 0x05010400u;
+          const uint2 c01 = conv8<PT, VT>(__builtin_amdgcn_perm(v[1].w[i], v[0].w[i], sel));
+          const uint2 c23 = conv8<PT, VT>(__builtin_amdgcn_perm(v[3].w[i], v[2].w[i], sel));
+          const int nt = 4 * i + 2 * half;
+          acc(o[nt], make_uint2(c01.x, c23.x));
+          acc(o[nt + 1], make_uint2(c01.y, c23.y));
+        }
+      }
     } else {
+      // 16-bit words of the 4 V rows (int8 codes converted): element nt of
+      // row e sits in word nt/2
+      uint32_t w16[4][G::DC / 2];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+#pragma unroll
+        for (int i = 0; i < G::vWords; ++i) {
+          if constexpr (VT::bits == 16) {
+            w16[e][i] = v[e].w[i];
+          } else {
+            const uint2 c2 = conv8<PT, VT>(v[e].w[i]);
+            w16[e][2 * i] = c2.x;
+            w16[e][2 * i + 1] = c2.y;
+          }
+        }
+      }
 #pragma unroll
       for (int nt = 0; nt < G::DC; ++nt) {
         const uint32_t sel = (nt & 1) ? 0x07060302u : 0x05040100u;
@@ -411,8 +471,7 @@ __device__ __forceinline__ void pv_tile(const float (&p)[4], const Words<Geo<QT,
         uint2 b;
         b.x = __builtin_amdgcn_perm(w16[1][wi], w16[0][wi], sel);
         b.y = __builtin_amdgcn_perm(w16[3][wi], w16[2][wi], sel);
-        o[nt] = mfma16<QT>(phi, b, o[nt]);
-        o[nt] = mfma16<QT>(plo, b, o[nt]);
+        acc(o[nt], b);
       }
     }
   }
@@ -480,8 +539,9 @@ __device__ __forceinline__ float merge_result(const MergeState<N>& s, int e) {
 // memory (agent-scope stores write through the XCD's L2) and are read back
 // past the reader's caches (agent-scope loads), so the workgroups of one
 // sequence may run on any XCDs.
-__device__ __forceinline__ void store_agent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void store_agent2(float* p, float v0, float v1) {
+  const uint64_t u = static_cast<uint64_t>(__float_as_uint(v0)) | (static_cast<uint64_t>(__float_as_uint(v1)) << 32);
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ float2 load_agent2(const float* p) {
   const uint64_t u = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
@@ -964,15 +1024,15 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   }
 
   // ---- merge the waves' states ----
-  // The pipeline's last loads (re-reads of the wave's last block, an L2 hit)
-  // are drained here, so that no later instruction waits on them - the wait
-  // counter is in order, and a wait for them would also wait for whatever
-  // was issued after them.
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   // A sequence split over several partitions and merged in this launch: its
   // workgroups count their arrival on the sequence's (KV head's) counter;
   // the request goes out now and its reply is read after the wave merge.
+  // The pipeline's last loads (re-reads of the wave's last block, an L2 hit)
+  // are drained first, so that no later instruction waits on them - the wait
+  // counter is in order, and a wait for them would also wait for whatever
+  // was issued after them, the arrival reply among it.
   const bool merge_here = P > 1 && np_b > 1 && a.counters != nullptr;
+  if (merge_here) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   int* const cnt = merge_here ? a.counters + 2 * (static_cast<int64_t>(b) * a.num_kv_heads + g) : nullptr;
   // (an increment the compiler leaves as one atomic: an add would go
   // through its wave-level combining, whose result it waits for at once)
@@ -1041,8 +1101,8 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
       const int pi = tid + k * kThreads;
       if (pi < n_pairs) {
         const int64_t i = (out_row0 + pi / (D / 2)) * D + 2 * (pi % (D / 2));
-        store_from_f32<QT>(a.out, i, st_l[k] > 0.f ? st_a[k][0] / st_l[k] : 0.f);
-        store_from_f32<QT>(a.out, i + 1, st_l[k] > 0.f ? st_a[k][1] / st_l[k] : 0.f);
+        store2_from_f32<QT>(a.out, i, st_l[k] > 0.f ? st_a[k][0] / st_l[k] : 0.f,
+                            st_l[k] > 0.f ? st_a[k][1] / st_l[k] : 0.f);
       }
     }
     return;
@@ -1057,8 +1117,7 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
       if (pi < n_pairs) {
         const int d = 2 * (pi % (D / 2));
         const int64_t prow = (out_row0 + pi / (D / 2)) * P + part;
-        a.part_acc[prow * D + d] = st_a[k][0];
-        a.part_acc[prow * D + d + 1] = st_a[k][1];
+        *reinterpret_cast<float2*>(a.part_acc + prow * D + d) = make_float2(st_a[k][0], st_a[k][1]);
         if (d == 0) {
           a.part_ml[2 * prow] = st_m[k];
           a.part_ml[2 * prow + 1] = st_l[k];
@@ -1086,12 +1145,8 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
       if (pi < n_pairs) {
         const int d = 2 * (pi % (D / 2));
         const int64_t prow = (out_row0 + pi / (D / 2)) * P + part;
-        store_agent(a.part_acc + prow * D + d, st_a[k][0]);
-        store_agent(a.part_acc + prow * D + d + 1, st_a[k][1]);
-        if (d == 0) {
-          store_agent(a.part_ml + 2 * prow, st_m[k]);
-          store_agent(a.part_ml + 2 * prow + 1, st_l[k]);
-        }
+        store_agent2(a.part_acc + prow * D + d, st_a[k][0], st_a[k][1]);
+        if (d == 0) store_agent2(a.part_ml + 2 * prow, st_m[k], st_l[k]);
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // every store of this thread acknowledged
@@ -1141,8 +1196,8 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
       merge_chunk<2>(ms, mp, lp, ap, min(8, np_b - p0));
     }
     const float nan = __builtin_nanf("");
-    store_from_f32<QT>(a.out, row * D + d, published ? merge_result<2>(ms, 0) : nan);
-    store_from_f32<QT>(a.out, row * D + d + 1, published ? merge_result<2>(ms, 1) : nan);
+    store2_from_f32<QT>(a.out, row * D + d, published ? merge_result<2>(ms, 0) : nan,
+                        published ? merge_result<2>(ms, 1) : nan);
   }
   if (tid == 0) {
     __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

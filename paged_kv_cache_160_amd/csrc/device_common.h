@@ -124,6 +124,19 @@ template <> __device__ __forceinline__ void store_from_f32<F16>(void* p, int64_t
 template <> __device__ __forceinline__ void store_from_f32<BF16>(void* p, int64_t i, float v) {
   static_cast<uint16_t*>(p)[i] = f32_to_bf16_bits(v);
 }
+// Elements i and i + 1 (i even) in one store.
+template <typename T> __device__ __forceinline__ void store2_from_f32(void* p, int64_t i, float v0, float v1);
+template <> __device__ __forceinline__ void store2_from_f32<F32>(void* p, int64_t i, float v0, float v1) {
+  *reinterpret_cast<float2*>(static_cast<float*>(p) + i) = make_float2(v0, v1);
+}
+template <> __device__ __forceinline__ void store2_from_f32<F16>(void* p, int64_t i, float v0, float v1) {
+  *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p) + i) =
+      static_cast<uint32_t>(f32_to_f16_bits(v0)) | (static_cast<uint32_t>(f32_to_f16_bits(v1)) << 16);
+}
+template <> __device__ __forceinline__ void store2_from_f32<BF16>(void* p, int64_t i, float v0, float v1) {
+  *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p) + i) =
+      static_cast<uint32_t>(f32_to_bf16_bits(v0)) | (static_cast<uint32_t>(f32_to_bf16_bits(v1)) << 16);
+}
 
 // ---- OCP e4m3 encoding ---------------------------------------------------------
 // Round-to-nearest-even of a finite y with |y| <= 448 to the E4M3FN code
