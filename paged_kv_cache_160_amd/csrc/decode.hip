@@ -82,6 +82,9 @@ namespace pkv {
 #ifndef PKV_DECODE_PV_F16Q
 #define PKV_DECODE_PV_F16Q 1   // quantised V: P rounded once to f16, one MFMA per column tile
 #endif
+#ifndef PKV_DECODE_I8_MFMA
+#define PKV_DECODE_I8_MFMA 1   // int8 K: Q.K^T on int8 MFMA against two digit planes of the query
+#endif
 #ifndef PKV_DECODE_QK_VALU
 #define PKV_DECODE_QK_VALU 0   // Q.K^T on vector ALU dot products (measured against MFMA: off)
 #endif
@@ -272,6 +275,80 @@ __device__ __forceinline__ float4_t qk_tile(const Words<Geo<QT, KT, KT, D>::kWor
                                                    __builtin_bit_cast(half8_t, bv), s, 0, 0, 0);
     }
   }
+  return s;
+}
+
+// ---- Q.K^T on int8 MFMA (int8 K pools) ----------------------------------------------
+// The query of each head is taken as a 15-bit fixed-point integer v = q times
+// 2^(14 - e), where |q| < 2^e over the head's D values, written in two signed
+// base-256 digits, v = 256 d1 + d0.  A 16-bit query value is exact there when
+// it is at least 2^-7 (bf16) or 2^-4 (f16) of the head's largest; smaller ones
+// are rounded, by at most 2^-15 of the largest.  Each digit plane meets the
+// int8 codes of the K tile in exact int32 MFMAs, so the codes need no
+// conversion, and the two dot products combine exactly in int32.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct QDigits {
+  static constexpr int kWords = D / 16;    // a lane's quarter of a head: D/4 bytes
+  uint32_t w[2][kWords];                   // planes d0, d1
+};
+
+// Digits of this lane's D/4 query values (16-bit words of QT, two per word);
+// returns the factor 2^(e - 14) that takes the integer dot product back to
+// q.K, or NaN when the head's query is not finite.
+template <typename QT, int D, int QW>
+__device__ __forceinline__ float q_digits(const Words<QW>& q, QDigits<D>& qd) {
+  static_assert(QW * 2 == D / 4, "two query values per word");
+  float qf[D / 4];
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < QW; ++i) {
+    qf[2 * i] = lo16_to_f32<QT>(q.w[i]);
+    qf[2 * i + 1] = hi16_to_f32<QT>(q.w[i]);
+    mx = fmaxf(mx, fmaxf(fabsf(qf[2 * i]), fabsf(qf[2 * i + 1])));
+  }
+  mx = col_max4(mx);                       // the head's largest |q| (4 lanes hold it)
+  const bool finite = mx <= 3.0e38f;
+  int e = 0;
+  if (mx > 0.f && finite) frexpf(mx, &e);  // mx = f 2^e, f in [0.5, 1)
+  const float up = ldexpf(1.f, 14 - e);
+#pragma unroll
+  for (int w = 0; w < D / 16; ++w) {
+    uint32_t p0 = 0u, p1 = 0u;
+#pragma unroll
+    for (int bt = 0; bt < 4; ++bt) {
+      const int v = finite ? static_cast<int>(rintf(qf[4 * w + bt] * up)) : 0;   // |v| <= 2^14
+      const int d0 = ((v + 128) & 255) - 128;
+      const int d1 = (v - d0) >> 8;                                              // |d1| <= 64
+      p0 |= static_cast<uint32_t>(d0 & 255) << (8 * bt);
+      p1 |= static_cast<uint32_t>(d1 & 255) << (8 * bt);
+    }
+    qd.w[0][w] = p0;
+    qd.w[1][w] = p1;
+  }
+  return finite ? ldexpf(1.f, e - 14) : __builtin_nanf("");
+}
+
+template <int D, int KW>
+__device__ __forceinline__ float4_t qk_tile_i8(const Words<KW>& k, const QDigits<D>& qd) {
+  static_assert(KW == D / 16, "a lane's quarter of an int8 K row");
+  i32x4_t acc[2];
+#pragma unroll
+  for (int pl = 0; pl < 2; ++pl) {
+    acc[pl] = i32x4_t{0, 0, 0, 0};
+#pragma unroll
+    for (int m = 0; m < KW / 4; ++m) {
+      const i32x4_t kv = {static_cast<int>(k.w[4 * m]), static_cast<int>(k.w[4 * m + 1]),
+                          static_cast<int>(k.w[4 * m + 2]), static_cast<int>(k.w[4 * m + 3])};
+      const i32x4_t qv = {static_cast<int>(qd.w[pl][4 * m]), static_cast<int>(qd.w[pl][4 * m + 1]),
+                          static_cast<int>(qd.w[pl][4 * m + 2]), static_cast<int>(qd.w[pl][4 * m + 3])};
+      acc[pl] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kv, qv, acc[pl], 0, 0, 0);
+    }
+  }
+  float4_t s;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s[r] = static_cast<float>(acc[1][r] * 256 + acc[0][r]);   // |.| < 2^29
   return s;
 }
 
@@ -777,7 +854,10 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   }
   const int tok1 = min(L, tok0 + PS);
   const int nblk = (tok1 - tok0 + kTileTokens - 1) / kTileTokens;
-  const float qk_scale = a.scale * kLog2e;   // scores in log2 units
+  float qk_scale = a.scale * kLog2e;   // scores in log2 units
+  constexpr bool kIntQK = PKV_DECODE_I8_MFMA && std::is_same<KT, I8>::value && D % 64 == 0;
+  QDigits<kIntQK ? D : 64> qd;
+  if constexpr (kIntQK) qk_scale *= q_digits<QT, D>(qop, qd);
 
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k_pool);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v_pool);
@@ -842,6 +922,8 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
     if constexpr (kValuQK) {
       if (group <= 4) s = qk_tile_valu<QT, KT, D>(r.k, qv, &sm_st[wave][0], c, j);
       else s = qk_tile<QT, KT, D>(r.k, qop);
+    } else if constexpr (kIntQK) {
+      s = qk_tile_i8<D>(r.k, qd);
     } else {
       s = qk_tile<QT, KT, D>(r.k, qop);
     }
