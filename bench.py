@@ -85,6 +85,9 @@ def parse():
                     help="decode row: tokens per block (32: the same workload on 32-token blocks)")
     ap.add_argument("--swap-mode", choices=["overlapped", "sequential"], default="overlapped",
                     help="swap row: out and in on two streams at once (PagedKVCache.swap), or one after the other")
+    ap.add_argument("--swap-ahead", type=int, default=1,
+                    help="swap row, overlapped mode: the host waits for the GPU after every N steps (default 1: "
+                         "after each step, as a scheduler does; 0: never inside the timed loop)")
     ap.add_argument("--cached", type=int, default=3584, help="prefill row: cached tokens per sequence")
     ap.add_argument("--chunk", type=int, default=512, help="prefill row: chunk tokens per sequence")
     ap.add_argument("--split", action="store_true",
@@ -932,10 +935,12 @@ def run_swap_overlapped(args, cache, w, n_swap, seq_bytes, layers):
         outs = {x: free_bufs.pop() for x in groups[s_ % len(groups)]}
         held.update(cache.swap(groups[s_ % len(groups)], back, out_host=outs))
         e1.record(stream)
-        # a scheduler step ends when its swaps are done; letting the host
-        # queue many steps ahead (512 launches and 8 copies each) gives
-        # steps of 170-240 ms instead of ~47 ms on the runtime's queues
-        stream.synchronize()
+        # a scheduler step ends when its swaps are done (--swap-ahead N: the
+        # host waits only after every N steps; a pinned buffer handed back is
+        # reused only after the current stream has passed its copy, which
+        # the stream order guarantees)
+        if args.swap_ahead > 0 and (s_ + 1) % args.swap_ahead == 0:
+            stream.synchronize()
         free_bufs += [buf for buf, _ in back.values()]
         if s_ >= args.warmup:
             evs.append((e0, e1))
