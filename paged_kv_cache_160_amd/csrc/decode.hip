@@ -282,8 +282,8 @@ __device__ __forceinline__ float4_t qk_tile(const Words<Geo<QT, KT, KT, D>::kWor
 // The query of each head is taken as a 15-bit fixed-point integer v = q times
 // 2^(14 - e), where |q| < 2^e over the head's D values, written in two signed
 // base-256 digits, v = 256 d1 + d0.  A 16-bit query value is exact there when
-// it is at least 2^-7 (bf16) or 2^-4 (f16) of the head's largest; smaller ones
-// are rounded, by at most 2^-15 of the largest.  Each digit plane meets the
+// it is at least 2^-6 (bf16) or 2^-3 (f16) of the head's largest; smaller ones
+// are rounded, by at most 2^-14 of the largest.  Each digit plane meets the
 // int8 codes of the K tile in exact int32 MFMAs, so the codes need no
 // conversion, and the two dot products combine exactly in int32.
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
