@@ -334,21 +334,23 @@ def test_more_sequence_heads_than_counters_use_the_merge_kernel():
     assert max_err(out_to_f64(one)[sample], exp) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("cache", [None, "fp8_e4m3"])
-def test_two_partition_merge_in_kernel_equals_split_form(cache):
-    # sequences of one and of two partitions in one launch of two partitions
-    # per sequence (merged inside the attention kernel by the one-call form):
-    # the same bits as the split form's merge kernel, and the oracle
-    lens = [3000, 1500, 10, 2900, 1504, 1505, 0, 2999]
+@pytest.mark.parametrize("cache,ps", [(None, 1504), ("fp8_e4m3", 1504), (None, 1008), ("int8_int4", 752)],
+                         ids=["bf16-2", "fp8-2", "bf16-3", "int8int4-4"])
+def test_in_kernel_merge_equals_split_form(cache, ps):
+    # sequences of one to four partitions in one launch of two to four
+    # partitions per sequence (merged inside the attention kernel by the
+    # one-call form): the same bits as the split form's merge kernel, and the
+    # oracle
+    lens = [3000, 1500, 10, 2900, 1504, 1505, 0, 2999, 2256, 752, 753]
     w, g = _custom(lens, 16, 4, 128, "bf16" if cache is None else "f32", cache_dtype=cache,
                    q_dtype=None if cache is None else "bf16", seed=37)
     c = g.cache
     seqs = list(range(w.num_seqs))
     tables = c.block_tables(seqs)
     q = g.queries(0)
-    ps = 1504
-    assert -(-max(lens) // ps) == 2
-    say(f"[merge] two partitions of {ps} tokens, cache {cache or 'bf16'}")
+    n_parts = -(-max(lens) // ps)
+    assert 2 <= n_parts <= 4
+    say(f"[merge] {n_parts} partitions of {ps} tokens, cache {cache or 'bf16'}")
     one = torch.empty_like(q)
     pkv.paged_attention_decode(one, q, c.k[0], c.v[0], tables[0], tables[1], tables[2], k_scale=c.k_scale[0],
                                v_scale=c.v_scale[0], partition_size=ps)
