@@ -718,7 +718,12 @@ constexpr int decode_min_blocks() { return KT::quantised && !PKV_DECODE_QK_VALU 
 
 // ORDER: workgroups take sequences longest first (a separate instance, so
 // launches without the order carry none of its code or registers).
-template <typename QT, typename KT, typename VT, int D, int PIPE, bool ORDER>
+// MERGE: the instance of one-call launches that merge split sequences in the
+// launch (counters given, more than one partition); the others - single
+// partitions, the split form - are built without that code, which measured
+// 3% faster on long split launches (the register allocation of the whole
+// kernel changes with it).
+template <typename QT, typename KT, typename VT, int D, int PIPE, bool ORDER, bool MERGE>
 __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decode_kernel(DecodeArgs a) {
   using G = Geo<QT, KT, VT, D>;
   constexpr bool kQK = KT::quantised;
@@ -1113,7 +1118,7 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   // are drained first, so that no later instruction waits on them - the wait
   // counter is in order, and a wait for them would also wait for whatever
   // was issued after them, the arrival reply among it.
-  const bool merge_here = P > 1 && np_b > 1 && a.counters != nullptr;
+  const bool merge_here = MERGE && np_b > 1;
   if (merge_here) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   int* const cnt = merge_here ? a.counters + 2 * (static_cast<int64_t>(b) * a.num_kv_heads + g) : nullptr;
   // (an increment the compiler leaves as one atomic: an add would go
@@ -1138,8 +1143,47 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   }
   __syncthreads();
 
-  // This workgroup's state, two adjacent output columns (h, d..d+1) per
-  // step: kPairs steps cover the largest group.
+  if constexpr (!MERGE) {
+    // One element (h, d) per thread and step: the output when the workgroup
+    // holds the whole sequence, else the partition's state for the merge
+    // kernel.
+    const bool single = P == 1;
+    for (int idx = tid; idx < group * D; idx += kThreads) {
+      const int h = idx / D;
+      const int d = idx % D;
+      float M = kNegInf;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+      float acc = 0.f, lsum = 0.f;
+      if (M != kNegInf) {
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+          const float mw = sm_m[w][h];
+          if (mw != kNegInf) {
+            const float f = __builtin_amdgcn_exp2f(mw - M);
+            acc += f * sm_o[w][h][d];
+            lsum += f * sm_l[w][h];
+          }
+        }
+      }
+      const int64_t row = out_row0 + h;
+      if (single) {
+        store_from_f32<QT>(a.out, row * D + d, lsum > 0.f ? acc / lsum : 0.f);
+      } else {
+        const int64_t prow = row * P + part;
+        a.part_acc[prow * D + d] = acc;
+        if (d == 0) {
+          a.part_ml[2 * prow] = M;
+          a.part_ml[2 * prow + 1] = lsum;
+        }
+      }
+    }
+    return;
+  }
+
+  // Merging instance.  This workgroup's state, two adjacent output columns
+  // (h, d..d+1) per step (the same sums as above, so the split form's states
+  // carry the same bits): kPairs steps cover the largest group.
   constexpr int kPairs = (kMaxGroup * D / 2 + kThreads - 1) / kThreads;
   const int n_pairs = group * D / 2;
   float st_m[kPairs], st_l[kPairs], st_a[kPairs][2];
@@ -1175,7 +1219,7 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
     }
   }
 
-  if (P == 1 || (np_b == 1 && a.counters != nullptr)) {
+  if (np_b == 1) {
     // the workgroup holds the whole sequence: its state is the output (the
     // merge of one state gives the same bits)
 #pragma unroll
@@ -1190,24 +1234,6 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
     return;
   }
 
-  if (!merge_here) {
-    // split form: every partition's state goes to the workspace for the
-    // merge kernel
-#pragma unroll
-    for (int k = 0; k < kPairs; ++k) {
-      const int pi = tid + k * kThreads;
-      if (pi < n_pairs) {
-        const int d = 2 * (pi % (D / 2));
-        const int64_t prow = (out_row0 + pi / (D / 2)) * P + part;
-        *reinterpret_cast<float2*>(a.part_acc + prow * D + d) = make_float2(st_a[k][0], st_a[k][1]);
-        if (d == 0) {
-          a.part_ml[2 * prow] = st_m[k];
-          a.part_ml[2 * prow + 1] = st_l[k];
-        }
-      }
-    }
-    return;
-  }
 
   // One-call form.  Every workgroup but the last to arrive publishes its
   // state (stored through to memory, then counted on the second counter);
@@ -1374,12 +1400,15 @@ static int launch_typed(const DecodeArgs& a, hipStream_t stream, int stages) {
         rc = check_launch();
         if (rc != PKV_OK) return rc;
       }
-      hipLaunchKernelGGL((paged_decode_kernel<QT, KT, VT, D, pipe, true>), dim3(static_cast<unsigned>(grid)),
+      hipLaunchKernelGGL((paged_decode_kernel<QT, KT, VT, D, pipe, true, false>), dim3(static_cast<unsigned>(grid)),
                          dim3(kThreads), 0, stream, a);
+    } else if (a.counters != nullptr && a.num_partitions > 1) {
+      hipLaunchKernelGGL((paged_decode_kernel<QT, KT, VT, D, pipe, false, true>),
+                         dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((paged_decode_kernel<QT, KT, VT, D, pipe, false, false>),
+                         dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, stream, a);
     }
-    else
-      hipLaunchKernelGGL((paged_decode_kernel<QT, KT, VT, D, pipe, false>), dim3(static_cast<unsigned>(grid)),
-                         dim3(kThreads), 0, stream, a);
     rc = check_launch();
   }
   // one-call launches with counters merge inside the attention kernel
