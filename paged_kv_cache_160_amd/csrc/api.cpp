@@ -10,7 +10,7 @@
 #include "pagedkv.h"
 
 #ifndef PKV_DECODE_MERGE_HERE_MAX
-#define PKV_DECODE_MERGE_HERE_MAX 4   // most partitions a one-call decode merges inside its attention kernel
+#define PKV_DECODE_MERGE_HERE_MAX 2   // most partitions a one-call decode merges inside its attention kernel
 #endif
 
 namespace {

@@ -336,11 +336,11 @@ def test_more_sequence_heads_than_counters_use_the_merge_kernel():
 
 @pytest.mark.parametrize("cache,ps", [(None, 1504), ("fp8_e4m3", 1504), (None, 1008), ("int8_int4", 752)],
                          ids=["bf16-2", "fp8-2", "bf16-3", "int8int4-4"])
-def test_in_kernel_merge_equals_split_form(cache, ps):
+def test_one_call_merge_equals_split_form(cache, ps):
     # sequences of one to four partitions in one launch of two to four
-    # partitions per sequence (merged inside the attention kernel by the
-    # one-call form): the same bits as the split form's merge kernel, and the
-    # oracle
+    # partitions per sequence: the one-call form (merged inside the
+    # attention kernel for two partitions, by the merge kernel beyond) gives
+    # the same bits as the split form's merge kernel, and the oracle
     lens = [3000, 1500, 10, 2900, 1504, 1505, 0, 2999, 2256, 752, 753]
     w, g = _custom(lens, 16, 4, 128, "bf16" if cache is None else "f32", cache_dtype=cache,
                    q_dtype=None if cache is None else "bf16", seed=37)
