@@ -1158,10 +1158,10 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   // A sequence split over several partitions and merged in this launch: its
   // workgroups count their arrival on the sequence's (KV head's) counter;
   // the request goes out now and its reply is read after the wave merge.
-  // The pipeline's last loads (re-reads of the wave's last block, an L2 hit)
-  // are drained first, so that no later instruction waits on them - the wait
-  // counter is in order, and a wait for them would also wait for whatever
-  // was issued after them, the arrival reply among it.
+  // Loads still in flight (a quantised pipeline's re-reads of the wave's
+  // last block) are drained first: the wait counter is in order, and a wait
+  // for them would also wait for whatever was issued after them, the
+  // arrival reply among it.
   const bool merge_here = MERGE && np_b > 1;
   if (merge_here) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   int* const cnt = merge_here ? a.counters + 2 * (static_cast<int64_t>(b) * a.num_kv_heads + g) : nullptr;
@@ -1279,17 +1279,21 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   }
 
 
-  // One-call form.  Every workgroup but the last to arrive publishes its
-  // state (stored through to memory, then counted on the second counter);
-  // the last one waits until the others have published - they have all
-  // arrived, so only their stores are outstanding - merges every state in
-  // partition order and writes the output, then zeroes both counters for
-  // the next call.  The wait is bounded; if it ever ran out the output row
-  // would be NaN rather than the kernel hanging.
+  // One-call form.  The counter holds arrivals in its low 16 bits and
+  // publications above them.  Every workgroup but the last to arrive
+  // publishes its state (stored through to memory, then counted as
+  // published once the stores are acknowledged); the reply to the last
+  // one's arrival usually shows every other state published already, and
+  // otherwise it waits until they are - they have all arrived, so only their
+  // stores are outstanding.  It merges every state in partition order,
+  // writes the output and zeroes the counter for the next call.  The wait
+  // is bounded; if it ever ran out the output row would be NaN rather than
+  // the kernel hanging.
+  constexpr int kPub = 1 << 16;
   __shared__ int sm_arrival;
   if (tid == 0) sm_arrival = arrival;
   __syncthreads();
-  const bool last = sm_arrival == np_b - 1;
+  const bool last = (sm_arrival & (kPub - 1)) == np_b - 1;
   if (!last) {
 #pragma unroll
     for (int k = 0; k < kPairs; ++k) {
@@ -1303,18 +1307,19 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // every store of this thread acknowledged
     __syncthreads();
-    if (tid == 0) atomicAdd(cnt + 1, 1);
+    if (tid == 0) atomicAdd(cnt, kPub);
     return;
   }
   if (tid == 0) {
     constexpr int kMaxSpins = 1 << 20;
     int spins = 0;
-    while (__hip_atomic_load(cnt + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < np_b - 1 &&
-           spins < kMaxSpins) {
+    int seen = sm_arrival;
+    while ((seen >> 16) < np_b - 1 && spins < kMaxSpins) {
       __builtin_amdgcn_s_sleep(1);
       ++spins;
+      seen = __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    sm_arrival = spins < kMaxSpins ? 1 : 0;
+    sm_arrival = (seen >> 16) >= np_b - 1 ? 1 : 0;
   }
   __syncthreads();
   const bool published = sm_arrival != 0;
@@ -1357,10 +1362,7 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
     store2_from_f32<QT>(a.out, row * D + d, published ? merge_result<2>(ms, 0) : nan,
                         published ? merge_result<2>(ms, 1) : nan);
   }
-  if (tid == 0) {
-    __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(cnt + 1, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---- log-sum-exp merge of partitions (second launch) --------------------------------

@@ -50,8 +50,9 @@ struct DecodeArgs {
   const void* v_new;
   const int64_t* slot_mapping;   // [num_seqs]: slot of position context_lens[b] - 1
   pkv_dtype src_dtype;
-  // One-call form: per (sequence, KV head) an arrival and a published count,
-  // zero between calls; the last partition of a sequence to finish merges.
+  // One-call form: per (sequence, KV head) two words, zero between calls;
+  // the first counts arrivals (low 16 bits) and published states (above),
+  // the second is unused.  The last partition of a sequence to finish merges.
   // nullptr: the attention kernel writes every partition state and a merge
   // kernel combines them (split form).
   int* counters;           // [num_seqs][num_kv_heads][2]
