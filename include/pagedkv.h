@@ -175,7 +175,7 @@ int pkv_copy_blocks_bs(void* k_pool, void* v_pool, float* k_scale, float* v_scal
  * paged_attention_decode uses when called with partition_size == 0, and the
  * resulting partitions per sequence for max_context_len.  The plan fills
  * the 256 CUs with at least one workgroup each (two for int8 K + int4 V
- * caches, whose decoding is heaviest per byte) and at most 64 blocks per
+ * caches, whose decoding is heaviest per byte) and at most 72 blocks per
  * wave.  Host only.
  */
 int pkv_decode_partition_size(int num_seqs, int num_q_heads, int num_kv_heads, int head_dim,

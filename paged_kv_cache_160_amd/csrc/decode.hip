@@ -1398,15 +1398,20 @@ __global__ void __launch_bounds__(D) partition_merge_kernel(DecodeArgs a) {
 int choose_partition_size(int num_seqs, int num_kv_heads, int max_context_len, pkv_dtype cache_dtype) {
   // Pick the number of partitions per sequence, np, as the smallest value
   // for which the launch fills the chip evenly and no wave streams more than
-  // 64 blocks: units * np workgroups should be at least min_wgs and either a
+  // kMaxWaveTiles blocks: units * np workgroups should be at least min_wgs and either a
   // whole number of 256-CU rounds or at least four rounds (then the
   // dispatcher balances the remainder).  min_wgs is one workgroup per CU,
   // except for int8 K + int4 V caches, whose decoding takes the most vector
   // instructions per byte: two resident workgroups per CU hide it (16 x 4096
   // at 8 KV heads: 31.0 us against 37.3 us with one).  Each partition keeps
   // >= 4 blocks per wave.  Partitions of one sequence are made as even as a
-  // 16-token granule allows.
+  // 16-token granule allows.  kMaxWaveTiles = 72 lets 32 x 32768 tokens at
+  // 8 KV heads run in 8 partitions (65 blocks per wave, 2048 workgroups):
+  // fp8 386.5-387.2 us and int8 K + int4 V 300.2-301.0 us per whole call
+  // against 390.2-391.0 and 302.4-303.5 us with the 9 that a cap of 64
+  // gave; 6 and 7 partitions measured within 1% of 8.
   constexpr int64_t kCUs = 256;
+  constexpr int64_t kMaxWaveTiles = 72;
   const int64_t min_wgs = cache_dtype == PKV_INT8_INT4 ? 2 * kCUs : kCUs;
   const int64_t units = static_cast<int64_t>(num_seqs) * num_kv_heads;
   const int64_t seq_blocks = (static_cast<int64_t>(max_context_len) + kTileTokens - 1) / kTileTokens;
@@ -1418,7 +1423,7 @@ int choose_partition_size(int num_seqs, int num_kv_heads, int max_context_len, p
   for (int64_t cand = np_min; cand <= np_max; ++cand) {
     const int64_t wgs = units * cand;
     const int64_t per_wave = (seq_blocks + cand * kWaves - 1) / (cand * kWaves);
-    if (per_wave <= 64 && wgs >= min_wgs && (wgs % kCUs == 0 || wgs >= 4 * kCUs)) {
+    if (per_wave <= kMaxWaveTiles && wgs >= min_wgs && (wgs % kCUs == 0 || wgs >= 4 * kCUs)) {
       np = cand;
       break;
     }

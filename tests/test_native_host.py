@@ -274,6 +274,17 @@ def test_partition_plan_and_workspace():
     assert pkv.workspace_size(16, 32, 8, 128, 4096, 16, pkv.PKV_BF16) >= 16 * 32 * 256 * 130 * 4
 
 
+def test_partition_plan_of_the_benched_workloads():
+    # the Llama-3-8B layer shape after the bench's first appends: two
+    # partitions, 256 workgroups; 32 x 32768 tokens: eight partitions of
+    # 4112 tokens (65 blocks per wave, 2048 workgroups) in every cache format
+    assert pkv.decode_partition_size(16, 32, 8, 128, 4100, pkv.PKV_BF16) == (2064, 2)
+    for cache in (pkv.PKV_BF16, pkv.PKV_FP8_E4M3, pkv.PKV_INT8_INT4):
+        assert pkv.decode_partition_size(32, 32, 8, 128, 32769, cache) == (4112, 8)
+    # int8 K + int4 V asks for two workgroups per CU: four partitions here
+    assert pkv.decode_partition_size(16, 32, 8, 128, 4100, pkv.PKV_INT8_INT4) == (1040, 4)
+
+
 def test_counter_area_size_matches_header():
     # the binding's constant is the header's PKV_WS_COUNTER_BYTES
     with open(HEADER, encoding="utf-8") as f:
