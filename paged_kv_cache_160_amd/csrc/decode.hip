@@ -65,7 +65,7 @@ namespace pkv {
 #define PKV_DECODE_PIPE 2      // blocks in flight per wave, 16-bit caches
 #endif
 #ifndef PKV_DECODE_PIPE_Q
-#define PKV_DECODE_PIPE_Q 3    // blocks in flight per wave, quantised caches
+#define PKV_DECODE_PIPE_Q 2    // blocks in flight per wave, quantised caches
 #endif
 #ifndef PKV_DECODE_NT
 #define PKV_DECODE_NT 0        // non-temporal K/V loads (measured slower: off)
@@ -730,10 +730,6 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   constexpr bool kQV = VT::quantised;
   constexpr float kNegInf = -INFINITY;
   constexpr float kRebase = 8.0f;          // lazy-rescale threshold (log2 units)
-  // 16-bit and fp32 caches end each wave's pipeline without loads past its
-  // last tile (measured 1.3% faster on the Llama-3-8B layer shape); quantised
-  // caches keep the uniform loop
-  constexpr bool kPeel = !KT::quantised;
 
   __shared__ float sm_m[kWaves][kMaxGroup];
   __shared__ float sm_l[kWaves][kMaxGroup];
@@ -1015,10 +1011,7 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   };
 
   // PIPE blocks in flight per wave: block i is computed while blocks
-  // i+4, ..., i+4*(PIPE-1) are being loaded.  Every stage issues its load
-  // unconditionally (past the end it re-reads the wave's last block, an L2
-  // hit) so that all paths through the loop carry the same loads in the same
-  // order and each wait covers only the block about to be used.
+  // i+4, ..., i+4*(PIPE-1) are being loaded.
   if constexpr (kLdsStage) {
     // Build option PKV_DECODE_LDS (16-bit caches, head_dim 128): each wave
     // streams its tiles into a ring of kBufs LDS slots with direct loads
@@ -1087,7 +1080,7 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
         slot = slot + 1 == kBufs ? 0 : slot + 1;
       }
     }
-  } else if (kPeel && wave < nblk) {
+  } else if (wave < nblk) {
     // The wave's tiles are wave + k * kWaves, k < n; tile k lives in slot
     // k % PIPE.  Full rounds load only real tiles; the last 1 .. 2*PIPE-1
     // tiles run as straight-line code for their count, so no load goes past
@@ -1124,23 +1117,6 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
       case 5: if constexpr (PIPE >= 3) finish(std::integral_constant<int, 5>{}); break;
       default: break;
     }
-  } else if (wave < nblk) {
-    // Quantised caches (three tiles in flight, registers at their limit):
-    // one loop whose every stage loads, past the wave's last tile a re-read
-    // of it (the straight-line tail of the form above adds spills there).
-    const int last = wave + kWaves * ((nblk - 1 - wave) / kWaves);
-    BlockRegs<QT, KT, VT, D> r[PIPE];
-    bool ok[PIPE];
-#pragma unroll
-    for (int st = 0; st < PIPE; ++st) load_block(r[st], min(wave + st * kWaves, last), ok[st]);
-    for (int i = wave; i < nblk; i += PIPE * kWaves) {
-#pragma unroll
-      for (int st = 0; st < PIPE; ++st) {
-        const int blk = i + st * kWaves;
-        if (blk < nblk) compute_block(r[st], blk, ok[st]);
-        load_block(r[st], min(blk + PIPE * kWaves, last), ok[st]);
-      }
-    }
   }
 
   if constexpr (std::is_same<VT, I4>::value) {
@@ -1158,10 +1134,10 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   // A sequence split over several partitions and merged in this launch: its
   // workgroups count their arrival on the sequence's (KV head's) counter;
   // the request goes out now and its reply is read after the wave merge.
-  // Loads still in flight (a quantised pipeline's re-reads of the wave's
-  // last block) are drained first: the wait counter is in order, and a wait
-  // for them would also wait for whatever was issued after them, the
-  // arrival reply among it.
+  // Loads still in flight (the LDS-staged build's, or a short partition's
+  // repeated first loads) are drained first: the wait counter is in order,
+  // and a wait for them would also wait for whatever was issued after them,
+  // the arrival reply among it.
   const bool merge_here = MERGE && np_b > 1;
   if (merge_here) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   int* const cnt = merge_here ? a.counters + 2 * (static_cast<int64_t>(b) * a.num_kv_heads + g) : nullptr;
@@ -1439,10 +1415,13 @@ static int launch_typed(const DecodeArgs& a, hipStream_t stream, int stages) {
   if (grid > 0x7fffffff) return PKV_ERR_UNSUPPORTED;
   int rc = PKV_OK;
   if (stages & kStageAttend) {
-    // fp32 tiles are twice as large: two in flight keep them in registers.
-    // 16-bit caches: two (interleaved A/B: 1.3% faster than three on the
-    // Llama-3-8B layer shape, 5% on the shared-prefix batch); quantised
-    // caches, whose tiles are half as large: three.
+    // Two tiles in flight per wave for every format.  16-bit caches:
+    // interleaved A/B 1.3% faster than three on the Llama-3-8B layer shape,
+    // 5% on the shared-prefix batch.  Quantised caches (tiles half as large)
+    // took three while each wave ended with re-reads of its last tile; with
+    // the straight-line tail two are faster (fp8 on the Llama-3-8B shape
+    // 30.2-30.4 against 34.2-34.4 us, 32 x 32768 fp8 377.5 against 386.7 us)
+    // and three would spill.
     constexpr int pipe = std::is_same<KT, F32>::value ? 2 : (KT::quantised ? PKV_DECODE_PIPE_Q : PKV_DECODE_PIPE);
     // longest first where the dispatcher hands out workgroups in turns and
     // each holds a whole sequence (split sequences already have workgroups of
