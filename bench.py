@@ -930,17 +930,21 @@ def run_swap_overlapped(args, cache, w, n_swap, seq_bytes, layers):
     n_steps = args.warmup + args.steps
     stream = torch.cuda.current_stream()
     evs = []
+    host_ms = []        # host time to queue each timed step (the runtime may block the caller)
     t_start = None
     for s_ in range(n_steps):
         if s_ == args.warmup:
             torch.cuda.synchronize()
             t_start = time.perf_counter()
+        t_q = time.perf_counter()
         back = {x: held.pop(x) for x in groups[(s_ - 1) % len(groups)]} if s_ > 0 else {}
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         outs = {x: free_bufs.pop() for x in groups[s_ % len(groups)]}
         held.update(cache.swap(groups[s_ % len(groups)], back, out_host=outs))
         e1.record(stream)
+        if s_ >= args.warmup:
+            host_ms.append((time.perf_counter() - t_q) * 1e3)
         # a scheduler step ends when its swaps are done (--swap-ahead N: the
         # host waits only after every N steps; a pinned buffer handed back is
         # reused only after the current stream has passed its copy, which
@@ -954,6 +958,7 @@ def run_swap_overlapped(args, cache, w, n_swap, seq_bytes, layers):
     elapsed = time.perf_counter() - t_start
     step_s = sum(a.elapsed_time(b) for a, b in evs) / len(evs) / 1e3
     log("[swap] step times (ms): " + " ".join(f"{a.elapsed_time(b):.1f}" for a, b in evs))
+    log("[swap] host time to queue each step (ms): " + " ".join(f"{t:.1f}" for t in host_ms))
     gb = seq_bytes / 1e9
     link = 2 * n_swap * gb / step_s             # bytes over the host link per second, both directions
     log(f"[swap] overlapped: {args.steps} steps in {elapsed * 1e3:.1f} ms; per step {n_swap} sequences out and "

@@ -173,6 +173,12 @@ class PagedKVCache:
                     raise PagedKVError(rc, "pkv_gather_blocks" if gather else "pkv_scatter_blocks")
                 off += n * b_
 
+        def ids_on_device(blocks):
+            # block ids go up from pinned memory: an asynchronous copy from
+            # pageable memory is staged by the runtime, which blocks the caller
+            # once its staging buffers are taken by copies still queued
+            return torch.tensor(blocks, dtype=torch.int32).pin_memory().to(self.device, non_blocking=True)
+
         # device staging buffers are kept between calls; each is used on one
         # stream only, so that stream orders its reuse
         if getattr(self, "_stage", None) is None:
@@ -191,7 +197,7 @@ class PagedKVCache:
         for i, (s_, blocks) in enumerate(outs.items()):
             n = len(blocks)
             staging = stage("out", i, n * sum(bb), cur)
-            bt = torch.tensor(blocks, dtype=torch.int32).to(self.device, non_blocking=True)
+            bt = ids_on_device(blocks)
             if n:
                 move(staging, bt, n, True, cur)
             staged.append((s_, staging, n))
@@ -209,7 +215,7 @@ class PagedKVCache:
                 host, n = back_in[s_]
                 staging = stage("in", i, n * sum(bb), side)
                 staging.copy_(host[:staging.numel()], non_blocking=True)
-                bt = torch.tensor(blocks, dtype=torch.int32).to(self.device, non_blocking=True)
+                bt = ids_on_device(blocks)
                 pending.append((staging, bt, n))
             side.wait_event(gathered)            # reused blocks are read before they are written
             for staging, bt, n in pending:
