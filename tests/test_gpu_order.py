@@ -47,6 +47,9 @@ CASES = [  # (kind, num_seqs, hq, hkv, head_dim, source dtype, longest context +
     ("ragged", 48, 32, 32, 64, "f32", 400, "int8_int4"),
     ("ragged", 600, 8, 2, 64, "bf16", 200, None),
     ("ragged", 3000, 4, 1, 64, "bf16", 80, None),
+    # the largest batch the order kernel sorts, and one more (index order)
+    ("ragged", 8192, 4, 1, 64, "bf16", 40, None),
+    ("ragged", 8193, 4, 1, 64, "bf16", 40, None),
 ]
 
 
@@ -104,7 +107,7 @@ def test_longest_first_fused_step_equals_append_then_decode():
         check_cache_rows(w, fus.cache, 0, b, tb[b].numpy(), int(lb[b]))
 
 
-@pytest.mark.parametrize("case", [CASES[6], CASES[7]], ids=["600x2", "3000x1"])
+@pytest.mark.parametrize("case", [CASES[6], CASES[7], CASES[8]], ids=["600x2", "3000x1", "8192x1"])
 def test_order_changes_no_output_bit(case):
     # the same call with the sorted order (workspace given) and in index
     # order (no workspace): every workgroup computes its row the same way
