@@ -18,8 +18,9 @@
 //    tiles in flight, and keeps its own online-softmax state; the 4 states
 //    merge through LDS at the end.
 //  * The whole GQA group is served from one read of each K/V tile: the
-//    group's query heads are the 16 columns of an MFMA tile (columns >= G are
-//    zero), so one 16x16 MFMA output holds 16 tokens x 16 heads.
+//    group's query heads are the 16 columns of an MFMA tile (columns >= G
+//    repeat the first head and are discarded), so one 16x16 MFMA output
+//    holds 16 tokens x 16 heads.
 //      S^T = K_tile (16 tok x D) * Q^T (D x 16 heads)    [16x16x32 MFMA]
 //      O  += P (16 heads x 16 tok) * V_tile (16 tok x D) [16x16x16 MFMA]
 //    The S^T accumulator layout (lane = head + 16*(token/4), reg = token%4)
@@ -769,14 +770,14 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   uint32_t qv[4][D / 8];
   int phys[kLoads];
   auto first_loads = [&](int bb) {
+    // Columns c >= group of the MFMA tile take a copy of the group's first
+    // query: their scores, probabilities and output rows repeat column 0's
+    // and are never stored.  (Zeroing them instead would make the wave wait
+    // for the query loads before it issues the table loads.)
     const bool valid = c < group;
     const int64_t row0 = static_cast<int64_t>(bb) * a.num_q_heads + static_cast<int64_t>(g) * group;
     const uint8_t* qp = static_cast<const uint8_t*>(a.q) + ((row0 + (valid ? c : 0)) * D + j * (D / 4)) * G::qes;
     load_words<G::qWords, false>(qop, qp);
-    if (!valid) {
-#pragma unroll
-      for (int i = 0; i < G::qWords; ++i) qop.w[i] = 0u;
-    }
     if constexpr (kValuQK) {
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
