@@ -760,15 +760,17 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   constexpr int kLoads = (kMaxPartitionBlocks + kThreads - 1) / kThreads;
 
   // The workgroup's first loads do not depend on each other and are issued
-  // together: the context length, the query, and the block-table entries of
-  // a full partition (read before the length is known; entries past the
-  // sequence's end lie inside its table row and are never used).
+  // together: the context length, the query, the block-table entries of a
+  // full partition (read before the length is known; entries past the
+  // sequence's end lie inside its table row and are never used) and the
+  // fused write's slot.
   // Q^T operand: lane (head column c, k-group j) holds q[head c][j*D/4 ...).
   Words<G::qWords> qop;
   constexpr bool kValuQK = PKV_DECODE_QK_VALU && !std::is_same<KT, F32>::value;
   // vector-ALU form: quarter j of each of the group's (up to 4) queries
   uint32_t qv[4][D / 8];
   int phys[kLoads];
+  int64_t new_slot = -1;   // fused cache write: the slot of this step's row
   auto first_loads = [&](int bb) {
     // Columns c >= group of the MFMA tile take a copy of the group's first
     // query: their scores, probabilities and output rows repeat column 0's
@@ -794,6 +796,9 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
       const int u = blk0 + tid + k * kThreads;
       phys[k] = (tid + k * kThreads < pblk && u < max_units) ? table[u >> rs] : -1;
     }
+    // (a scalar load, issued with the others: the workgroup that writes the
+    // row then waits for one round trip fewer)
+    if (a.slot_mapping != nullptr) new_slot = a.slot_mapping[bb];
   };
 
   // Workgroups are dispatched in index order.  When many of them share the
@@ -875,7 +880,7 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   // K, wave 1: V) before anything is read; the barrier below makes the rows
   // visible to every wave of the workgroup.
   if (a.slot_mapping != nullptr && part == (L - 1) / PS && wave < 2) {
-    const int64_t slot = a.slot_mapping[b];
+    const int64_t slot = new_slot;
     if (slot >= 0 && slot < static_cast<int64_t>(a.num_blocks) * a.block_size) {
       const int64_t dst_row = slot_row(slot, a.block_size, a.num_kv_heads, g);
       const int64_t src_row = static_cast<int64_t>(b) * a.num_kv_heads + g;
