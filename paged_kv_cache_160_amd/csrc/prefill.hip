@@ -267,12 +267,12 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
 
   const int qs = a.query_start[b];
   const int n = a.query_start[b + 1] - qs;
+  int L = a.context_lens[b];
   // a chunk outside q, or longer than the launch was sized for, is skipped
   if (qs < 0 || n <= 0 || n > a.max_query_len || qs + n > a.num_tokens) return;
   const int rows_b = n * group;
   const int r0 = tile * SH::rows;
   if (r0 >= rows_b) return;
-  int L = a.context_lens[b];
   L = max(0, min(L, min(a.max_context_len, a.max_blocks_per_seq * a.block_size)));
   const int ctx = L - n;             // positions of the chunk: ctx .. L-1
 
@@ -301,17 +301,11 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
   const int nstages = (key_end + kPfKeys - 1) / kPfKeys;
   const int nblk = (key_end + kTileTokens - 1) / kTileTokens;
 
-  // Unit u (tokens 16u .. 16u+15) staged as its tile index at KV head 0,
-  // ((phys * Hkv) << rs) + (u & (2^rs - 1)); the table entry is clamped into
-  // the pool (the positions it stands for are the caller's to keep valid).
-  const int32_t* table = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq;
-  const int rs = block_shift(a.block_size);
-  for (int u = tid; u < nblk; u += kPfThreads)
-    sm_ids[u] = ((min(max(table[u >> rs], 0), a.num_blocks - 1) * a.num_kv_heads) << rs) + (u & ((1 << rs) - 1));
-  const int g_tile = g << rs;
-
   // ---- query operands and per-row limits -------------------------------------
-  // Wave w, tile ct, column c: row r0 + w*16*CTILES + ct*16 + c.
+  // Wave w, tile ct, column c: row r0 + w*16*CTILES + ct*16 + c.  Rows past
+  // the chunk take a copy of its last row (their output is never stored):
+  // no register a load still fills is overwritten, so the query loads and
+  // the block-table loads below are in flight together.
   u32x4 qop[CTILES][DCH];
   int lim[CTILES];
   const uint8_t* qbase = static_cast<const uint8_t*>(a.q);
@@ -324,11 +318,17 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
     lim[ct] = max(0, min(ctx + i, L - 1));
     const uint8_t* qp = qbase + ((static_cast<int64_t>(qs + i) * a.num_q_heads + head) * D + 8 * j) * 2;
 #pragma unroll
-    for (int dc = 0; dc < DCH; ++dc) {
-      u32x4 v = *reinterpret_cast<const u32x4*>(qp + 64 * dc);
-      qop[ct][dc] = valid ? v : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int dc = 0; dc < DCH; ++dc) qop[ct][dc] = *reinterpret_cast<const u32x4*>(qp + 64 * dc);
   }
+  // Unit u (tokens 16u .. 16u+15) staged as its tile index at KV head 0,
+  // ((phys * Hkv) << rs) + (u & (2^rs - 1)); the table entry is clamped into
+  // the pool (the positions it stands for are the caller's to keep valid).
+  const int32_t* table = a.block_tables + static_cast<int64_t>(b) * a.max_blocks_per_seq;
+  const int rs = block_shift(a.block_size);
+  for (int u = tid; u < nblk; u += kPfThreads)
+    sm_ids[u] = ((min(max(table[u >> rs], 0), a.num_blocks - 1) * a.num_kv_heads) << rs) + (u & ((1 << rs) - 1));
+  const int g_tile = g << rs;
+
   __syncthreads();   // block ids staged
 
   // ---- output state ----------------------------------------------------------------
