@@ -216,9 +216,11 @@ size_t paged_attention_workspace_size(int num_seqs, int num_q_heads, int num_kv_
  *                 and at most PKV_MAX_PARTITION_TOKENS.
  *                 When a sequence is longer than one partition, its
  *                 partitions' states are merged exactly (log-sum-exp) into
- *                 the output: for up to two partitions per sequence inside
- *                 the same launch (the workgroup of the sequence's last
- *                 partition to finish reads the other's state from the
+ *                 the output: for up to two partitions per sequence (up to
+ *                 four when the launch has at most 512 workgroups, i.e.
+ *                 num_seqs * num_kv_heads * partitions <= 512) inside the
+ *                 same launch (the workgroup of the sequence's last
+ *                 partition to finish reads the others' states from the
  *                 workspace and writes the output row), for more by a second
  *                 kernel of the call; the bits are the same either way.
  *   workspace     device scratch of at least paged_attention_workspace_size()

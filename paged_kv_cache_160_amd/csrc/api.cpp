@@ -10,7 +10,10 @@
 #include "pagedkv.h"
 
 #ifndef PKV_DECODE_MERGE_HERE_MAX
-#define PKV_DECODE_MERGE_HERE_MAX 2   // most partitions a one-call decode merges inside its attention kernel
+#define PKV_DECODE_MERGE_HERE_MAX 4   // most partitions a one-call decode merges inside its attention kernel
+#endif
+#ifndef PKV_DECODE_MERGE_HERE_WGS
+#define PKV_DECODE_MERGE_HERE_WGS 512 // ... more than two only in launches of at most this many workgroups
 #endif
 
 namespace {
@@ -269,14 +272,20 @@ int decode_impl(void* out, const void* q, const void* k_new, const void* v_new, 
     char* base = static_cast<char*>(workspace);
     a.part_ml = reinterpret_cast<float*>(base + ws.ml);
     a.part_acc = reinterpret_cast<float*>(base + ws.acc);
-    // the one-call form merges inside the attention kernel for up to
-    // PKV_DECODE_MERGE_HERE_MAX partitions and PKV_WS_COUNTER_UNITS
+    // the one-call form merges inside the attention kernel for up to two
+    // partitions, and for three or four when the launch has at most
+    // PKV_DECODE_MERGE_HERE_WGS workgroups, with at most PKV_WS_COUNTER_UNITS
     // (sequence, KV head) pairs; otherwise a merge kernel follows, as in the
-    // split form (same bits).  Long contexts split into many partitions merge
-    // faster in a kernel of their own: there the last partition to finish
-    // reads many states back through memory while other workgroups wait for
-    // its CU slot (32 x 32768 fp8 tokens in 9 partitions: 421 against 429 us)
-    if (stages == pkv::kStageBoth && np <= PKV_DECODE_MERGE_HERE_MAX &&
+    // split form (same bits).  Interleaved A/B: the shared-prefix batch (4
+    // partitions, 256 workgroups) 13.95 against 14.25 us, int8 K + int4 V on
+    // the Llama-3-8B shape (4 partitions, 512 workgroups) 26.9 against
+    // 27.45 us; 32 x 32768 fp8 tokens in 8 partitions (2048 workgroups)
+    // 389 against 377 us - there the last partition to finish reads many
+    // states back while other workgroups wait for its CU slot, and the
+    // merging instance's registers cost the long launch.
+    const int64_t wgs = static_cast<int64_t>(num_seqs) * num_kv_heads * np;
+    const bool here = np <= 2 || (np <= PKV_DECODE_MERGE_HERE_MAX && wgs <= PKV_DECODE_MERGE_HERE_WGS);
+    if (stages == pkv::kStageBoth && here &&
         static_cast<int64_t>(num_seqs) * num_kv_heads <= static_cast<int64_t>(PKV_WS_COUNTER_UNITS)) {
       a.counters = reinterpret_cast<int*>(base + ws.counters);
     }

@@ -41,11 +41,12 @@
 //    tile instead of two.
 //  * Long sequences split into partitions, each with its state (max, sum,
 //    unnormalised output), merged with the log-sum-exp formula.  Up to two
-//    partitions per sequence the merge happens in this launch: the last
-//    workgroup of a (sequence, KV head) to finish, told so by an arrival
-//    counter, reads the other's state (stored and loaded at device scope,
-//    past the XCD caches - no fences) and writes the output.  With more
-//    partitions, or in the split form, every state goes to the workspace
+//    partitions per sequence (four in launches of at most 512 workgroups)
+//    the merge happens in this launch: the last workgroup of a (sequence,
+//    KV head) to finish, told so by an arrival counter, reads the others'
+//    states (stored and loaded at device scope, past the XCD caches - no
+//    fences) and writes the output.  With more partitions, or in the split
+//    form, every state goes to the workspace
 //    (an empty partition writes max -inf) and a second launch merges them;
 //    the two places share one merge routine and give the same bits.
 

@@ -334,14 +334,17 @@ def test_more_sequence_heads_than_counters_use_the_merge_kernel():
     assert max_err(out_to_f64(one)[sample], exp) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("cache,ps", [(None, 1504), ("fp8_e4m3", 1504), (None, 1008), ("int8_int4", 752)],
-                         ids=["bf16-2", "fp8-2", "bf16-3", "int8int4-4"])
-def test_one_call_merge_equals_split_form(cache, ps):
+@pytest.mark.parametrize("cache,ps,copies", [(None, 1504, 1), ("fp8_e4m3", 1504, 1), (None, 1008, 1),
+                                              ("int8_int4", 752, 1), (None, 1008, 4), ("int8_int4", 752, 4)],
+                         ids=["bf16-2", "fp8-2", "bf16-3", "int8int4-4", "bf16-3-528wg", "int8int4-4-704wg"])
+def test_one_call_merge_equals_split_form(cache, ps, copies):
     # sequences of one to four partitions in one launch of two to four
     # partitions per sequence: the one-call form (merged inside the
-    # attention kernel for two partitions, by the merge kernel beyond) gives
-    # the same bits as the split form's merge kernel, and the oracle
-    lens = [3000, 1500, 10, 2900, 1504, 1505, 0, 2999, 2256, 752, 753]
+    # attention kernel: up to four partitions in a launch of at most 512
+    # workgroups) gives the same bits as the split form's merge kernel, and
+    # the oracle; with ``copies`` the batch repeats until the launch has more
+    # than 512 workgroups and three or four partitions go to the merge kernel
+    lens = [3000, 1500, 10, 2900, 1504, 1505, 0, 2999, 2256, 752, 753] * copies
     w, g = _custom(lens, 16, 4, 128, "bf16" if cache is None else "f32", cache_dtype=cache,
                    q_dtype=None if cache is None else "bf16", seed=37)
     c = g.cache
