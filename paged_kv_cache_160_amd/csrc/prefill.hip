@@ -249,8 +249,12 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
   constexpr int kDmaChunks = kConv ? 1 : kPfKeys * IO::row_bytes / 16;
   __shared__ __attribute__((aligned(16))) uint16_t sm_k[kPadElems];
   __shared__ __attribute__((aligned(16))) uint16_t sm_v[kPadElems];
-  __shared__ u32x4 sm_kd[kPfBufs][kDmaChunks];
-  __shared__ u32x4 sm_vd[kPfBufs][kDmaChunks];
+  // one variable per stage buffer: the compiler gives each its own alias
+  // scope, so it can tell that the reads of one buffer do not touch another
+  // that direct loads are filling
+  constexpr int kDma3 = kPfBufs > 2 ? kDmaChunks : 1;
+  __shared__ u32x4 sm_k0[kDmaChunks], sm_k1[kDmaChunks], sm_k2[kDma3];
+  __shared__ u32x4 sm_v0[kDmaChunks], sm_v1[kDmaChunks], sm_v2[kDma3];
   __shared__ float sm_ks[kPfKeys];
   __shared__ float sm_vs[kPfKeys];
   __shared__ int sm_ids[kPfMaxBlocks];
@@ -628,7 +632,8 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
       const int q = (slot % CH) ^ LdsSwz<D>::of(r);
       lane_off[k] = (r % kTileTokens) * IO::row_bytes + 16 * q;
     }
-    auto dma = [&](uint8_t* kdst, uint8_t* vdst, int s) {
+    auto dma = [&](const uint8_t* kp, const uint8_t* vp, uint8_t* kdst, uint8_t* vdst, int s)
+                   __attribute__((always_inline)) {
       // rows past the context (last stage) read the sequence's last block
       // and are zeroed after they land
       const int id = sm_ids[min(kPfStageTiles * s + wave * kPfStageTiles / kPfWaves, nblk - 1)];
@@ -636,11 +641,23 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
 #pragma unroll
       for (int k = 0; k < kInsts; ++k) {
         const int dst = (wave * kInsts + k) * kWave * 16;
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kpool + base + lane_off[k]),
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kp + base + lane_off[k]),
                                          (__attribute__((address_space(3))) void*)(kdst + dst), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vpool + base + lane_off[k]),
+        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vp + base + lane_off[k]),
                                          (__attribute__((address_space(3))) void*)(vdst + dst), 16, 0, 0);
       }
+    };
+    // A stage's compute and the loads that fill a later stage's buffers go
+    // through the restrict-qualified pointers of one inlined call.  The
+    // compiler then knows that the operand reads of the current buffers do
+    // not touch the buffers being filled, and does not wait for those loads
+    // before each read (which would expose their whole latency in every
+    // stage); the waits for the current stage's own loads are explicit.
+    auto run = [&](auto slow_tag, const uint8_t* __restrict__ ck, const uint8_t* __restrict__ cv,
+                   uint8_t* __restrict__ nk, uint8_t* __restrict__ nv, const uint8_t* __restrict__ kp,
+                   const uint8_t* __restrict__ vp, int s, bool issue) __attribute__((always_inline)) -> int {
+      if (issue) dma(kp, vp, nk, nv, s + kPfBufs - 1);
+      return compute(slow_tag, ck, cv, s, 0);
     };
     // V rows at or past key_end of the last stage are zeroed by the wave that
     // loaded them (after its own loads landed): P is 0 there, and 0 times a
@@ -655,8 +672,9 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
     // kPfBufs stage buffers: the loads of stage s + kPfBufs - 1 go out after
     // the barrier that ends stage s - 1, into the buffer that stage used.
     constexpr int kLoads = 2 * kInsts;                      // this wave's loads per stage
-    auto kbuf = [&](int i) { return reinterpret_cast<uint8_t*>(sm_kd[i]); };
-    auto vbuf = [&](int i) { return reinterpret_cast<uint8_t*>(sm_vd[i]); };
+    static_assert(kPfBufs <= 3, "three stage buffers at most");
+    auto kbuf = [&](int i) { return reinterpret_cast<uint8_t*>(i == 0 ? sm_k0 : i == 1 ? sm_k1 : sm_k2); };
+    auto vbuf = [&](int i) { return reinterpret_cast<uint8_t*>(i == 0 ? sm_v0 : i == 1 ? sm_v1 : sm_v2); };
     auto step = [&](auto slow_tag, int s, int cur) __attribute__((always_inline)) -> int {
       // this wave's loads of stage s landed (those of the kPfBufs - 2 later
       // stages already issued may fly; near the end, wait for all)
@@ -664,15 +682,12 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
       else wait_vmcnt<0>();
       if (s == nstages - 1) zero_tail(vbuf(cur), s);
       __syncthreads();                                      // all of stage s is in LDS; stage s-1 is done
-      if (s + kPfBufs - 1 < nstages) {
-        const int nb = (cur + kPfBufs - 1) % kPfBufs;
-        dma(kbuf(nb), vbuf(nb), s + kPfBufs - 1);
-      }
-      return compute(slow_tag, kbuf(cur), vbuf(cur), s, 0);
+      const int nb = (cur + kPfBufs - 1) % kPfBufs;
+      return run(slow_tag, kbuf(cur), vbuf(cur), kbuf(nb), vbuf(nb), kpool, vpool, s, s + kPfBufs - 1 < nstages);
     };
 #pragma unroll
     for (int i = 0; i + 1 < kPfBufs; ++i)
-      if (i < nstages) dma(kbuf(i), vbuf(i), i);
+      if (i < nstages) dma(kpool, vpool, kbuf(i), vbuf(i), i);
     int s = 0, hv = -1;
     while (s < nstages) {
 #pragma unroll
