@@ -19,8 +19,10 @@
 //    16-bit caches each wave moves one tile of the next stage straight from
 //    HBM into the second of two LDS buffers (global_load_lds, no registers)
 //    while the workgroup computes the current one; rows are unpadded and
-//    their 16-byte chunks XOR-swizzled by row, so operand reads spread over
-//    the banks.  Quantised codes (e4m3, e5m2, int8 K, int4 V) take a
+//    their 16-byte chunks XOR-swizzled by row, so the K operand reads meet
+//    no bank conflicts (the transposed V reads meet two-way ones, which
+//    cost nothing measurable, while a map free of both needed registers
+//    the stage loop does not have).  Quantised codes (e4m3, e5m2, int8 K, int4 V) take a
 //    register path instead: they become 16-bit values exactly on the way
 //    into a padded buffer, and their per-token scales go to LDS beside them.
 //      S^T = K (16 keys x D) * Q^T (D x 16 rows)       [16x16x32 MFMA]
@@ -223,8 +225,9 @@ struct StageIO {
 
 // Swizzle of 16-byte chunk positions in an unpadded LDS row of D 16-bit
 // elements: consecutive rows (D = 128) or row pairs (D = 64, two rows per
-// 256-byte bank line) rotate their chunks, so the 16 rows one MFMA operand
-// read touches land on distinct banks.
+// 256-byte bank line) rotate their chunks, so the 16 rows of one K operand
+// read land on distinct banks (the LDS serves 16 lanes of a 16-byte read
+// per pass).
 template <int D>
 struct LdsSwz {
   static __device__ __forceinline__ int of(int r) {
