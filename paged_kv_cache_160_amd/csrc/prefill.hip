@@ -42,7 +42,9 @@
 //    the register allocator otherwise pays for with copies on every stage.
 //  * Row sums of P (16-bit caches) come from the matrix cores: one extra
 //    MFMA per half-stage multiplies P by a column of ones.
-//  * The matrix phases run at raised wave priority.
+//  * The matrix phases run at raised wave priority, and each issues all of
+//    its LDS operand reads before its first MFMA (a scheduling hint): one
+//    LDS round trip per phase instead of one per group of four reads.
 //  * The causal diagonal bounds each workgroup's key loop; stages entirely
 //    below it need no mask.
 //  * Workgroups of one (sequence, KV head) are placed on one XCD so they
@@ -402,6 +404,11 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
             for (int ct = 0; ct < CTILES; ++ct) st[kt][ct] = mfma32<QT>(kop, qop[ct][dc], st[kt][ct]);
           }
         }
+        // every operand read of the phase goes out before its first MFMA
+        // (left to itself the scheduler splits them into groups, each a full
+        // LDS round trip in front of its MFMAs)
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * DCH, 0);          // LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * DCH * CTILES, 0);  // MFMA
         __builtin_amdgcn_s_setprio(0);
         if constexpr (kConv) {
 #pragma unroll
@@ -532,6 +539,9 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
 #pragma unroll
           for (int ct = 0; ct < CTILES; ++ct) osum[ct] = mfma32<QT>(pop[ct], u32x4{kOnes, kOnes, kOnes, kOnes}, osum[ct]);
         }
+        // as for S^T: every V operand read, then the MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, DT * CTILES + (kConv ? 0 : CTILES), 0);
         __builtin_amdgcn_s_setprio(0);
       }
       return -1;
