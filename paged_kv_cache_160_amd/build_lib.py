@@ -29,6 +29,9 @@ HIPCC_FLAGS = [
     # packed fp32 arithmetic stays off for all device code on this hardware
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-fno-gpu-flush-denormals-to-zero",
+    # every symbol resolved at link time: a kernel whose host-side launch stub
+    # the compiler failed to emit is a build error, not a load-time one
+    "-Wl,-z,defs",
 ]
 
 

@@ -85,6 +85,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 constexpr float kLog2eP = 1.4426950408889634f;
 
+#ifndef PKV_PREFILL_BUFLDS
+#define PKV_PREFILL_BUFLDS 0   // stage loads as buffer loads into LDS
+#endif
 #ifndef PKV_PREFILL_CTILES
 #define PKV_PREFILL_CTILES 2   // 16-row query tiles per wave
 #endif
@@ -198,6 +201,16 @@ __device__ __forceinline__ float csum4(float x) {
 // Value of x held by lane src (0..63).
 __device__ __forceinline__ float lane_value(float x, int src) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+}
+
+// 16 bytes of a K/V tile (at byte lane_off of it) for each lane of the wave,
+// into LDS at lds + 16 * lane, by a buffer load through a descriptor of the
+// tile (so the hardware also bounds every lane's offset by the tile).
+__device__ __forceinline__ void tile_chunk_to_lds(const uint8_t* tile, int tile_bytes, uint8_t* lds, int lane_off) {
+  constexpr int kRaw32 = 0x00020000;   // descriptor word 3: 32-bit data, untyped
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(tile), 0, tile_bytes, kRaw32);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)lds, 16, lane_off, 0, 0, 0);
 }
 
 // One stage's global -> LDS traffic.  16-bit pools (KT = VT = the query
@@ -651,6 +664,17 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
       // and are zeroed after they land
       const int id = sm_ids[min(kPfStageTiles * s + wave * kPfStageTiles / kPfWaves, nblk - 1)];
       const int64_t base = static_cast<int64_t>(id + g_tile) * IO::tile_bytes;
+#if PKV_PREFILL_BUFLDS
+      // buffer loads into LDS (not the flat-encoded global form: while one of
+      // those is in flight the compiler makes every LDS read wait for all
+      // earlier ones)
+#pragma unroll
+      for (int k = 0; k < kInsts; ++k) {
+        const int dst = (wave * kInsts + k) * kWave * 16;
+        tile_chunk_to_lds(kp + base, IO::tile_bytes, kdst + dst, lane_off[k]);
+        tile_chunk_to_lds(vp + base, IO::tile_bytes, vdst + dst, lane_off[k]);
+      }
+#else
 #pragma unroll
       for (int k = 0; k < kInsts; ++k) {
         const int dst = (wave * kInsts + k) * kWave * 16;
@@ -659,6 +683,7 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
         __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vp + base + lane_off[k]),
                                          (__attribute__((address_space(3))) void*)(vdst + dst), 16, 0, 0);
       }
+#endif
     };
     // A stage's compute and the loads that fill a later stage's buffers go
     // through the restrict-qualified pointers of one inlined call.  The
