@@ -60,15 +60,19 @@
 namespace pkv {
 namespace {
 
-#ifndef PKV_PREFILL_WAVES
-#define PKV_PREFILL_WAVES 4    // waves per workgroup (4 or 8)
+// Waves per workgroup (4 or 8): 16-bit caches stage K/V straight into LDS
+// and share each stage among 8 waves (256 query rows); quantised caches,
+// which convert the codes on their way into LDS, run 4.
+#ifndef PKV_PREFILL_WAVES_16
+#define PKV_PREFILL_WAVES_16 8
 #endif
-constexpr int kPfWaves = PKV_PREFILL_WAVES;
+#ifndef PKV_PREFILL_WAVES_Q
+#define PKV_PREFILL_WAVES_Q 4
+#endif
 #ifndef PKV_PREFILL_BUFFERS
-#define PKV_PREFILL_BUFFERS (PKV_PREFILL_WAVES == 8 ? 3 : 2)   // K/V stage buffers (16-bit caches)
+#define PKV_PREFILL_BUFFERS 2   // K/V stage buffers (16-bit caches)
 #endif
 constexpr int kPfBufs = PKV_PREFILL_BUFFERS;
-constexpr int kPfThreads = kPfWaves * kWave;
 #ifndef PKV_PREFILL_KEYS
 #define PKV_PREFILL_KEYS 64    // keys per stage (32 or 64)
 #endif
@@ -96,10 +100,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 constexpr float kRebase = 8.0f;     // log2 headroom before the running max moves
 
-template <int CTILES>
+template <int CTILES, int W>
 struct PfShape {
   static constexpr int rows_per_wave = 16 * CTILES;
-  static constexpr int rows = kPfWaves * rows_per_wave;     // query rows per workgroup
+  static constexpr int rows = W * rows_per_wave;            // query rows per workgroup
 };
 
 // 16-bit element type of the MFMA operands for query type QT.
@@ -218,8 +222,9 @@ __device__ __forceinline__ void tile_chunk_to_lds(const uint8_t* tile, int tile_
 // go through registers: thread t, round r moves the 16-byte chunk r*256 + t
 // of the stage's K rows (and of its V rows, which are shorter for INT4), and
 // the chunks are converted to 16-bit values on the way into LDS.
-template <typename KT, typename VT, int D>
+template <typename KT, typename VT, int D, int W>
 struct StageIO {
+  static constexpr int threads = W * kWave;
   static constexpr int k_row_bytes = D * KT::bits / 8;
   static constexpr int v_row_bytes = D * VT::bits / 8;
   static constexpr int row_bytes = k_row_bytes;              // 16-bit pools: K and V alike
@@ -228,8 +233,8 @@ struct StageIO {
   static constexpr int v_tile_bytes = kTileTokens * v_row_bytes;
   static constexpr int k_chunks = kPfKeys * k_row_bytes / 16;
   static constexpr int v_chunks = kPfKeys * v_row_bytes / 16;
-  static constexpr int k_rounds = (k_chunks + kPfThreads - 1) / kPfThreads;
-  static constexpr int v_rounds = (v_chunks + kPfThreads - 1) / kPfThreads;
+  static constexpr int k_rounds = (k_chunks + threads - 1) / threads;
+  static constexpr int v_rounds = (v_chunks + threads - 1) / threads;
   // 16-bit elements per LDS row: D + 16 puts consecutive rows 32 bytes apart
   // in bank space, so the 16 rows a transpose read or a K-operand read
   // touches spread evenly over the banks
@@ -251,11 +256,13 @@ struct LdsSwz {
   }
 };
 
-template <typename QT, typename KT, typename VT, int D, int CTILES>
-__global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2 : 1)
+template <typename QT, typename KT, typename VT, int D, int CTILES, int W>
+__global__ void __launch_bounds__(W * kWave, (CTILES <= 2 && W == 4) ? 2 : 1)
     paged_prefill_kernel(PrefillArgs a) {
-  using IO = StageIO<KT, VT, D>;
-  using SH = PfShape<CTILES>;
+  constexpr int kPfWaves = W;
+  constexpr int kPfThreads = W * kWave;
+  using IO = StageIO<KT, VT, D, W>;
+  using SH = PfShape<CTILES, W>;
   constexpr bool kConv = KT::quantised;      // codes converted on the way into LDS
   constexpr int DCH = D / 32;        // QK MFMAs per 16-key tile
   constexpr int DT = D / 16;         // output column tiles
@@ -773,16 +780,18 @@ __global__ void __launch_bounds__(kPfThreads, (CTILES <= 2 && kPfWaves == 4) ? 2
 template <typename QT, typename KT, typename VT, int D>
 int launch_prefill_typed(const PrefillArgs& a, hipStream_t stream) {
   constexpr int kCt = PKV_PREFILL_CTILES;
+  constexpr int kW = KT::quantised ? PKV_PREFILL_WAVES_Q : PKV_PREFILL_WAVES_16;
+  using SH = PfShape<kCt, kW>;
   PrefillArgs b = a;
   const int group = a.num_q_heads / a.num_kv_heads;
   const int64_t rows = static_cast<int64_t>(a.max_query_len) * group;
-  b.tiles_per_seq = static_cast<int>((rows + PfShape<kCt>::rows - 1) / PfShape<kCt>::rows);
+  b.tiles_per_seq = static_cast<int>((rows + SH::rows - 1) / SH::rows);
   const int64_t total = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * b.tiles_per_seq;
   if (total == 0) return PKV_OK;
   if (total > (int64_t{1} << 30)) return PKV_ERR_UNSUPPORTED;
   const int64_t per_xcd = (total + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL((paged_prefill_kernel<QT, KT, VT, D, kCt>), dim3(static_cast<unsigned>(per_xcd * kXcds)),
-                     dim3(kPfThreads), 0, stream, b);
+  hipLaunchKernelGGL((paged_prefill_kernel<QT, KT, VT, D, kCt, kW>), dim3(static_cast<unsigned>(per_xcd * kXcds)),
+                     dim3(kW * kWave), 0, stream, b);
   return check_launch();
 }
 
