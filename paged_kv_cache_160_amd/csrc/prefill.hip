@@ -11,12 +11,13 @@
 //
 // Unlike decode this is a dense contraction (each K/V element meets many
 // queries), so it is built for the matrix cores:
-//  * Workgroup = 4 waves owning 4 * 16 * CTILES (128) query rows of one
-//    (sequence, KV head);
-//    a row is a (chunk position, head of the GQA group) pair, so the whole
-//    group shares every K/V tile.  Each wave owns CTILES tiles of 16 rows.
+//  * Workgroup = W waves owning W * 16 * CTILES query rows of one (sequence,
+//    KV head): 8 waves (256 rows) for 16-bit caches, 4 (128 rows) for
+//    quantised ones; a row is a (chunk position, head of the GQA group)
+//    pair, so the whole group shares every K/V tile.  Each wave owns CTILES
+//    tiles of 16 rows.
 //  * K and V stream through LDS in stages of 64 keys (4 tiles of 16).  For
-//    16-bit caches each wave moves one tile of the next stage straight from
+//    16-bit caches each wave moves its share of the next stage straight from
 //    HBM into the second of two LDS buffers (global_load_lds, no registers)
 //    while the workgroup computes the current one; rows are unpadded and
 //    their 16-byte chunks XOR-swizzled by row, so the K operand reads meet
