@@ -60,6 +60,9 @@
 
 namespace pkv {
 
+#ifndef PKV_DECODE_NATK
+#define PKV_DECODE_NATK 1     // 16-bit K in the MFMA's contraction order (0: permuted)
+#endif
 #ifndef PKV_DECODE_WAVES
 #define PKV_DECODE_WAVES 4     // waves per workgroup
 #endif
@@ -768,6 +771,12 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
   // Q^T operand: lane (head column c, k-group j) holds q[head c][j*D/4 ...).
   Words<G::qWords> qop;
   constexpr bool kValuQK = PKV_DECODE_QK_VALU && !std::is_same<KT, F32>::value;
+  // 16-bit K meets the query in the MFMA's own contraction order: lane (c, j)
+  // takes bytes 64i + 16j .. +15 of K row c for MFMA i (and the same elements
+  // of its query), so each load instruction reads 64 contiguous bytes of each
+  // of the tile's 16 rows.  The other formats take a contiguous quarter row
+  // per lane, the contraction index permuted alike on both operands.
+  constexpr bool kNatK = KT::bits == 16 && !kValuQK && !kLdsStage && PKV_DECODE_NATK;
   // vector-ALU form: quarter j of each of the group's (up to 4) queries
   uint32_t qv[4][D / 8];
   int phys[kLoads];
@@ -779,8 +788,22 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
     // for the query loads before it issues the table loads.)
     const bool valid = c < group;
     const int64_t row0 = static_cast<int64_t>(bb) * a.num_q_heads + static_cast<int64_t>(g) * group;
-    const uint8_t* qp = static_cast<const uint8_t*>(a.q) + ((row0 + (valid ? c : 0)) * D + j * (D / 4)) * G::qes;
-    load_words<G::qWords, false>(qop, qp);
+    if constexpr (kNatK) {
+      static_assert(G::qes == 2 && G::qWords == 4 * (D / 32), "16-bit query words, four per MFMA");
+      const uint8_t* qr = static_cast<const uint8_t*>(a.q) + (row0 + (valid ? c : 0)) * D * G::qes + 16 * j;
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) {
+        const u32x4_t v = load_vec<u32x4_t, false>(qr + 64 * i);
+        qop.w[4 * i + 0] = v[0];
+        qop.w[4 * i + 1] = v[1];
+        qop.w[4 * i + 2] = v[2];
+        qop.w[4 * i + 3] = v[3];
+      }
+    } else {
+      const uint8_t* qp =
+          static_cast<const uint8_t*>(a.q) + ((row0 + (valid ? c : 0)) * D + j * (D / 4)) * G::qes;
+      load_words<G::qWords, false>(qop, qp);
+    }
     if constexpr (kValuQK) {
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
@@ -873,7 +896,7 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
 
   const uint8_t* kbase = static_cast<const uint8_t*>(a.k_pool);
   const uint8_t* vbase = static_cast<const uint8_t*>(a.v_pool);
-  const int64_t k_lane = static_cast<int64_t>(c) * G::kRowBytes + j * G::kLaneBytes;
+  const int64_t k_lane = static_cast<int64_t>(c) * G::kRowBytes + j * (kNatK ? 16 : G::kLaneBytes);
   const int64_t v_lane = static_cast<int64_t>(4 * j) * G::vRowBytes + c * G::vLaneBytes;
 
   // Fused cache write: the workgroup whose partition holds the sequence's
@@ -914,7 +937,18 @@ __global__ void __launch_bounds__(kThreads, decode_min_blocks<KT>()) paged_decod
     const int64_t tile = static_cast<int64_t>(t0) + g_tile;
     const uint8_t* kt = kbase + tile * G::kTileBytes;
     const uint8_t* vt = vbase + tile * G::vTileBytes;
-    load_words<G::kWords, PKV_DECODE_NT>(r.k, kt + k_lane);
+    if constexpr (kNatK) {
+#pragma unroll
+      for (int i = 0; i < D / 32; ++i) {
+        const u32x4_t v = load_vec<u32x4_t, PKV_DECODE_NT != 0>(kt + k_lane + 64 * i);
+        r.k.w[4 * i + 0] = v[0];
+        r.k.w[4 * i + 1] = v[1];
+        r.k.w[4 * i + 2] = v[2];
+        r.k.w[4 * i + 3] = v[3];
+      }
+    } else {
+      load_words<G::kWords, PKV_DECODE_NT>(r.k, kt + k_lane);
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) load_vrow<G::vLaneBytes>(r.v[e], vt + v_lane + e * G::vRowBytes);
     if constexpr (kQK) r.ks = *reinterpret_cast<const float4*>(a.k_scale + tile * kTileTokens + 4 * j);
